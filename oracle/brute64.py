@@ -1,0 +1,133 @@
+"""Float64 brute force of the selective state update, for tiny shapes.
+
+TEST INFRASTRUCTURE ONLY (see oracle/__init__.py). It exists to pin the C
+oracle: it is written separately (Python over rows and heads, NumPy over the
+[dim, dstate] tile, float64 arithmetic), from the same pages:
+  - MATE docs, "Mamba / SSU", table "SSU at a glance" (layouts, slot rules,
+    variable-length and MTP decode) and the API reference's argument list;
+  - ReplaySSM article (lpnh.cn), section "三个瓶颈其实来自同一个动作": the
+    step S_t = a_t S_{t-1} + dt_t x_t B_t^T with the readout y_t = S_t C_t.
+Same readings as the C oracle (R1..R12 in its header). Rounding happens only
+where the method stores a value: the carried/stored state in the state dtype
+and y in the io dtype. Library routines do the dtype casts (NumPy for half,
+PyTorch for bfloat16).
+"""
+import numpy as np
+import torch
+
+
+def to_f64(a, dtype):
+    a = np.asarray(a)
+    if dtype == "f32":
+        return a.astype(np.float64)
+    if dtype == "f16":
+        return a.view(np.float16).astype(np.float64)
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def from_f64(v, dtype):
+    v = np.asarray(v, dtype=np.float64)
+    if dtype == "f32":
+        return v.astype(np.float32)
+    if dtype == "f16":
+        return v.astype(np.float16).view(np.uint16)
+    t = torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _rows_of_sequences(case, R):
+    """[(first row, length)] per sequence, from the call's layout."""
+    x = np.asarray(case["x"])
+    cu = case.get("cu_seqlens")
+    if cu is not None:
+        cu = [int(v) for v in np.asarray(cu)]
+        return [(cu[i], cu[i + 1] - cu[i]) for i in range(len(cu) - 1)]
+    if x.ndim == 4:
+        T = x.shape[1]
+        return [(b * T, T) for b in range(x.shape[0])]
+    return [(r, 1) for r in range(R)]
+
+
+def _lookup(table, b, first_row, t):
+    """Slot named by sequence b's position t (1-D tables are row-indexed)."""
+    if hasattr(table, "base") and not isinstance(table, np.ndarray):
+        base = np.asarray(table.base).ravel()
+        if len(table.shape) == 1:
+            return int(base[first_row + t])
+        return int(base[b * table.strides[0] + t * table.strides[1]])
+    table = np.asarray(table)
+    if table.ndim == 1:
+        return int(table[first_row + t])
+    return int(table[b, t])
+
+
+def run(case):
+    sd, io = case["state_dtype"], case["io_dtype"]
+    dtd = case.get("dt_dtype", io)
+    pool = np.asarray(case["state"])
+    slots, H, P, N = pool.shape
+    x = np.asarray(case["x"])
+    R = x.shape[0] * (x.shape[1] if x.ndim == 4 else 1)
+    X = to_f64(x, io).reshape(R, H, P)
+    dt = np.asarray(case["dt"])
+    if dt.ndim == x.ndim - 1:  # one value per head, broadcast over dim
+        DT = np.repeat(to_f64(dt, dtd).reshape(R, H, 1), P, axis=2)
+    else:
+        DT = to_f64(dt, dtd).reshape(R, H, P)
+    G = np.asarray(case["B"]).shape[-2]
+    Bm = to_f64(case["B"], io).reshape(R, G, N)
+    Cm = to_f64(case["C"], io).reshape(R, G, N)
+    Z = None if case.get("z") is None else to_f64(case["z"], io).reshape(R, H, P)
+    A = np.asarray(case["A"], dtype=np.float64)
+    Dv = None if case.get("D") is None else np.asarray(case["D"], dtype=np.float64)
+    bias = None if case.get("dt_bias") is None else np.asarray(case["dt_bias"], dtype=np.float64)
+    pad = int(case.get("pad_slot_id", -1))
+    disable = bool(case.get("disable_state_update", False))
+    rtab = case.get("state_batch_indices")
+    wtab = case.get("dst_state_batch_indices")
+    acc = case.get("num_accepted_tokens")
+
+    new_pool = pool.copy()
+    Y = np.zeros((R, H, P), dtype=np.float64)
+    written = np.zeros(slots, dtype=bool)
+    per_group = H // G
+    for b, (first, length) in enumerate(_rows_of_sequences(case, R)):
+        if length == 0:
+            continue
+        start = 0 if acc is None else max(int(np.asarray(acc)[b]) - 1, 0)
+        src = b if rtab is None else _lookup(rtab, b, first, start)
+        for h in range(H):
+            g = h // per_group
+            if src == pad:
+                S = np.zeros((P, N))
+            else:
+                S = to_f64(pool[src, h], sd)
+            for t in range(length):
+                r = first + t
+                step = DT[r, h].copy()
+                if bias is not None:
+                    step = step + bias[h]
+                if case.get("dt_softplus", False):
+                    step = np.where(step > 20.0, step, np.log1p(np.exp(np.minimum(step, 20.0))))
+                S = S * np.exp(step * A[h])[:, None] + np.outer(step * X[r, h], Bm[r, g])
+                y = S @ Cm[r, g]
+                if Dv is not None:
+                    y = y + Dv[h] * X[r, h]
+                if Z is not None:
+                    y = y * (Z[r, h] / (1.0 + np.exp(-Z[r, h])))
+                Y[r, h] = y
+                S = to_f64(from_f64(S, sd), sd)
+                if disable:
+                    continue
+                if wtab is not None:
+                    dst = _lookup(wtab, b, first, t)
+                elif rtab is not None:
+                    dst = _lookup(rtab, b, first, t)
+                else:
+                    dst = b
+                if dst == pad:
+                    continue
+                new_pool[dst, h] = from_f64(S, sd)
+                written[dst] = True
+    y = from_f64(Y, io).reshape(x.shape)
+    return {"y": y, "y64": Y.reshape(x.shape), "state": new_pool, "written": written}

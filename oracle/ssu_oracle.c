@@ -1,0 +1,473 @@
+/*
+ * ssu_oracle.c -- plain, slow CPU reference of the Mamba-2 selective state
+ * update (SSU) decode step.
+ *
+ * TEST INFRASTRUCTURE ONLY. The test suite, the package entry's smoke check
+ * and the benchmark's CPU-baseline leg are the only code that loads this
+ * library. The GPU library never calls it and shares no source with it: the
+ * dtype codes, the half/bfloat16 conversions and every formula below are
+ * written here on their own.
+ *
+ * What it computes (the pages it follows):
+ *  - MATE docs, "Mamba / SSU": the table "SSU at a glance" fixes the state
+ *    pool [slots, heads, dim, dstate] updated in place through destination
+ *    slots; A / D / dt_bias per head in fp32; B / C [rows, groups, dstate] in
+ *    the x dtype with heads divisible by groups; the output [rows, heads, dim]
+ *    in the x dtype; the slot semantics (flat or 2-D tables, pad_slot_id reads
+ *    as a zero state and is never written, disable_state_update leaves the
+ *    pool unchanged); variable-length and MTP decode (cu_seqlens splits the
+ *    rows, num_accepted_tokens seeds the read slot at count-1 floored at 0,
+ *    every token publishes to its own destination entry, defaulting to its
+ *    own entry of the read table; empty sequences are skipped). The
+ *    "SSU toolchain requirements" list says the recurrence runs in fp32 and
+ *    the state is kept in the state dtype.
+ *  - ReplaySSM article (lpnh.cn), section "三个瓶颈其实来自同一个动作" (the
+ *    three bottlenecks): the Mamba-2 step S_t = a_t * S_{t-1} + D_t * v_t k_t^T
+ *    with the readout y_t = S_t q_t. With v = x, k = B, q = C, D_t = dt and
+ *    a_t = exp(dt * A[h]), one step on a [dim, dstate] tile is
+ *        S[d][n] = S[d][n] * exp(dt'[d] A[h]) + (dt'[d] x[d]) B[n]
+ *        y[d]    = sum_n S[d][n] C[n] + D[h] x[d],  times silu(z[d]) if z.
+ *
+ * Readings taken where the pages leave a step open (each one is listed with
+ * its justification in the design notes of the repository):
+ *  R1  a 1-D slot table is row-indexed: sequence b, position t names entry
+ *      bos(b) + t; a 2-D table is addressed by its strides, b*s0 + t*s1.
+ *      Both name the same entries for one sequence, as the MATE page says.
+ *  R2  head h uses group h / (heads / groups) (consecutive heads share one).
+ *  R3  dt' = softplus(dt + dt_bias): bias first, then softplus; no clamp.
+ *  R4  softplus(v) = log1p(exp(v)), and v itself for v > 20.
+ *  R5  y is computed from the fp32 updated state; the state carried to the
+ *      next token of a sequence is the value stored in the state dtype.
+ *  R6  y uses the post-update state, and is (C.S + D x) * silu(z).
+ *  R7  16-bit stores and outputs round to nearest even.
+ *  R8  without num_accepted_tokens the read position is 0.
+ *  R9  a row whose read slot is the pad id is computed from a zero state and
+ *      its y is written.
+ *  R10 a pad destination skips that store only; the carry goes on.
+ *  R11 with no read table the slot is the sequence index for the read and
+ *      for every write.
+ *  R12 a slot written by one sequence and read or written by another has no
+ *      defined result; this oracle refuses such inputs.
+ *
+ * Precision: every product and sum is rounded to fp32 on its own (the build
+ * uses -O2 -ffp-contract=off, no fast-math); the readout sums n in order.
+ *
+ * Parity pins: every function here is pinned by the CPU test suite against
+ * values the mathematics fixes (library conversions, closed forms, invariants
+ * and a float64 brute force). The one convention the pages do not fix at all
+ * is R2's head-to-group order: the code's implementation of R2 is pinned, the
+ * convention itself is parity unpinned.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2 };
+enum { OR_ONE_TOKEN = 0, OR_DENSE = 1, OR_CU = 2 };
+
+typedef struct {
+    const int64_t *data; /* NULL: no table */
+    int64_t len;         /* number of int64 elements data may be indexed at */
+    int32_t ndim;        /* 1 (row-indexed, R1) or 2 (strided) */
+    int64_t s0, s1;      /* element strides of a 2-D table */
+} oracle_table;
+
+typedef struct {
+    /* state pool [slots, H, P, N]: read from pool_in, stores go to pool_out
+     * (the caller initialises pool_out as a copy of pool_in) */
+    const void *pool_in;
+    void *pool_out;
+    int32_t state_dtype;
+    int64_t slots, H, P, N, G;
+    /* packed rows */
+    int64_t R;
+    int32_t io_dtype;   /* dtype of x, B, C, z and out */
+    const void *x;      /* [R, H, P] */
+    const void *dt;     /* [R, H, P], or [R, H] when dt_per_head */
+    int32_t dt_dtype;
+    int32_t dt_per_head;
+    const float *A;     /* [H] */
+    const void *B;      /* [R, G, N] */
+    const void *C;      /* [R, G, N] */
+    const float *D;     /* [H] or NULL */
+    const void *z;      /* [R, H, P] or NULL */
+    const float *dt_bias; /* [H] or NULL */
+    int32_t dt_softplus;
+    /* sequences */
+    int32_t layout;     /* OR_ONE_TOKEN, OR_DENSE, OR_CU */
+    int64_t steps;      /* OR_DENSE: tokens per sequence */
+    const int64_t *cu;  /* OR_CU: [nseq + 1] */
+    int64_t nseq;       /* OR_CU: number of sequences */
+    const int64_t *acc; /* [nseq] or NULL */
+    oracle_table rtab, wtab;
+    int64_t pad;
+    int32_t disable;
+    void *out;          /* [R, H, P] */
+    uint8_t *written;   /* [slots] or NULL: set to 1 for every slot stored */
+    int64_t *read_slot; /* [nseq] or NULL: resolved read slot (INT64_MIN if empty) */
+} oracle_args;
+
+/* ---- scalar formats (IEEE 754 binary16; bfloat16 = top half of binary32) */
+
+float oracle_f16_to_f32(uint16_t h)
+{
+    uint32_t sign = (uint32_t)(h >> 15) << 31;
+    uint32_t e = (h >> 10) & 0x1F;
+    uint32_t m = h & 0x3FF;
+    uint32_t u;
+    if (e == 0x1F) {
+        u = sign | 0x7F800000u | (m << 13); /* inf / nan, payload kept */
+    } else if (e != 0) {
+        u = sign | ((e - 15 + 127) << 23) | (m << 13);
+    } else if (m == 0) {
+        u = sign;
+    } else {
+        /* subnormal: value m * 2^-24, renormalise */
+        int k = 0;
+        while (!(m & 0x400)) { m <<= 1; k++; }
+        m &= 0x3FF;
+        u = sign | ((uint32_t)(127 - 15 + 1 - k) << 23) | (m << 13);
+    }
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+/* round q + rem / 2^shift to nearest, ties to even */
+static uint32_t round_shift(uint32_t v, int shift)
+{
+    uint32_t q = v >> shift;
+    uint32_t rem = v & ((1u << shift) - 1u);
+    uint32_t half = 1u << (shift - 1);
+    if (rem > half || (rem == half && (q & 1u)))
+        q++;
+    return q;
+}
+
+uint16_t oracle_f32_to_f16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    uint32_t sign = (u >> 16) & 0x8000u;
+    int32_t exp = (int32_t)((u >> 23) & 0xFF);
+    uint32_t man = u & 0x7FFFFFu;
+    if (exp == 0xFF) {
+        if (man == 0)
+            return (uint16_t)(sign | 0x7C00u);
+        return (uint16_t)(sign | 0x7E00u | (man >> 13)); /* quiet nan */
+    }
+    int32_t e = exp - 127 + 15; /* binary16 biased exponent */
+    if (e >= 31)
+        return (uint16_t)(sign | 0x7C00u);
+    if (e <= 0) {
+        /* subnormal result: value / 2^-24 = (man | 1<<23) * 2^(exp - 126) */
+        if (exp == 0)
+            return (uint16_t)sign; /* fp32 subnormals are far below 2^-25 */
+        int shift = 126 - exp;     /* >= 14 */
+        if (shift > 24)
+            return (uint16_t)sign;
+        return (uint16_t)(sign | round_shift(man | 0x800000u, shift));
+    }
+    /* normal: 10 mantissa bits kept, 13 rounded away; a carry may roll the
+     * exponent up, to infinity at the top, which is the right result */
+    uint32_t q = ((uint32_t)e << 10) | (man >> 13);
+    uint32_t rem = man & 0x1FFFu;
+    if (rem > 0x1000u || (rem == 0x1000u && (q & 1u)))
+        q++;
+    return (uint16_t)(sign | q);
+}
+
+float oracle_bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+uint16_t oracle_f32_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x7FFFFFu))
+        return (uint16_t)((u >> 16) | 0x40u); /* quiet nan, sign kept */
+    return (uint16_t)(round_shift(u, 16) & 0xFFFFu);
+}
+
+static float load_as_f32(const void *p, int32_t dtype, int64_t i)
+{
+    switch (dtype) {
+    case OR_F32: return ((const float *)p)[i];
+    case OR_F16: return oracle_f16_to_f32(((const uint16_t *)p)[i]);
+    default:     return oracle_bf16_to_f32(((const uint16_t *)p)[i]);
+    }
+}
+
+static void store_from_f32(void *p, int32_t dtype, int64_t i, float v)
+{
+    switch (dtype) {
+    case OR_F32: ((float *)p)[i] = v; break;
+    case OR_F16: ((uint16_t *)p)[i] = oracle_f32_to_f16(v); break;
+    default:     ((uint16_t *)p)[i] = oracle_f32_to_bf16(v); break;
+    }
+}
+
+/* value after a store in `dtype` and a load back (R5's carried state) */
+static float through_dtype(int32_t dtype, float v)
+{
+    switch (dtype) {
+    case OR_F32: return v;
+    case OR_F16: return oracle_f16_to_f32(oracle_f32_to_f16(v));
+    default:     return oracle_bf16_to_f32(oracle_f32_to_bf16(v));
+    }
+}
+
+/* R4 */
+float oracle_softplus(float v)
+{
+    if (v > 20.0f)
+        return v;
+    return log1pf(expf(v));
+}
+
+static float silu(float v) { return v / (1.0f + expf(-v)); }
+
+/* ---- sequences and slots */
+
+static void seq_span(const oracle_args *a, int64_t b, int64_t *bos, int64_t *len)
+{
+    if (a->layout == OR_ONE_TOKEN) {
+        *bos = b;
+        *len = 1;
+    } else if (a->layout == OR_DENSE) {
+        *bos = b * a->steps;
+        *len = a->steps;
+    } else {
+        *bos = a->cu[b];
+        *len = a->cu[b + 1] - a->cu[b];
+    }
+}
+
+static int64_t num_seqs(const oracle_args *a)
+{
+    if (a->layout == OR_ONE_TOKEN)
+        return a->R;
+    if (a->layout == OR_DENSE)
+        return a->steps > 0 ? a->R / a->steps : 0;
+    return a->nseq;
+}
+
+static void set_err(char *err, int errlen, const char *msg, long long v1, long long v2)
+{
+    if (err && errlen > 0)
+        snprintf(err, (size_t)errlen, msg, v1, v2);
+}
+
+/* resolve sequence b's read slot (R8, R11 and the count-1 floor); returns 0
+ * and the slot, or -1 when the entry lies outside the table */
+static int read_slot_of(const oracle_args *a, int64_t b, int64_t bos, int64_t *slot)
+{
+    int64_t pos0 = 0;
+    if (a->acc) {
+        pos0 = a->acc[b] - 1;
+        if (pos0 < 0)
+            pos0 = 0;
+    }
+    if (!a->rtab.data) {
+        *slot = b;
+        return 0;
+    }
+    int64_t i = a->rtab.ndim == 1 ? bos + pos0 : b * a->rtab.s0 + pos0 * a->rtab.s1;
+    if (i < 0 || i >= a->rtab.len)
+        return -1;
+    *slot = a->rtab.data[i];
+    return 0;
+}
+
+/* destination of sequence b's token t: its own entry of the destination
+ * table, else of the read table, else the sequence index (R11) */
+static int write_slot_of(const oracle_args *a, int64_t b, int64_t bos, int64_t t, int64_t *slot)
+{
+    const oracle_table *tb = a->wtab.data ? &a->wtab : (a->rtab.data ? &a->rtab : NULL);
+    if (!tb) {
+        *slot = b;
+        return 0;
+    }
+    int64_t i = tb->ndim == 1 ? bos + t : b * tb->s0 + t * tb->s1;
+    if (i < 0 || i >= tb->len)
+        return -1;
+    *slot = tb->data[i];
+    return 0;
+}
+
+/* checks the oracle makes so that a result it returns is well defined */
+static int check_inputs(const oracle_args *a, char *err, int errlen)
+{
+    if (a->H <= 0 || a->P <= 0 || a->N <= 0 || a->G <= 0 || a->H % a->G != 0) {
+        set_err(err, errlen, "bad heads/groups %lld/%lld", (long long)a->H, (long long)a->G);
+        return 1;
+    }
+    int64_t nseq = num_seqs(a);
+    if (a->layout == OR_DENSE && a->steps > 0 && a->R % a->steps != 0) {
+        set_err(err, errlen, "rows %lld not a multiple of steps %lld", (long long)a->R,
+                (long long)a->steps);
+        return 1;
+    }
+    if (a->layout == OR_CU) {
+        if (a->cu[0] != 0 || a->cu[nseq] != a->R) {
+            set_err(err, errlen, "cu_seqlens must run from 0 to rows (%lld), ends at %lld",
+                    (long long)a->R, (long long)a->cu[nseq]);
+            return 1;
+        }
+        for (int64_t b = 0; b < nseq; b++)
+            if (a->cu[b + 1] < a->cu[b]) {
+                set_err(err, errlen, "cu_seqlens decreases at %lld%lld", (long long)b, 0);
+                return 1;
+            }
+    }
+    int64_t *writer = (int64_t *)malloc((size_t)(a->slots > 0 ? a->slots : 1) * sizeof(int64_t));
+    for (int64_t s = 0; s < a->slots; s++)
+        writer[s] = -1;
+    int rc = 0;
+    /* every slot named must be the pad id or inside the pool; a slot written
+     * by one sequence must not be read or written by another (R12) */
+    for (int64_t b = 0; b < nseq && !rc; b++) {
+        int64_t bos, len, s;
+        seq_span(a, b, &bos, &len);
+        if (len == 0)
+            continue;
+        if (read_slot_of(a, b, bos, &s)) {
+            set_err(err, errlen, "read entry of sequence %lld outside the table%lld", (long long)b, 0);
+            rc = 1;
+            break;
+        }
+        if (s != a->pad && (s < 0 || s >= a->slots)) {
+            set_err(err, errlen, "read slot %lld of sequence %lld outside the pool", (long long)s,
+                    (long long)b);
+            rc = 1;
+            break;
+        }
+        if (a->disable)
+            continue;
+        for (int64_t t = 0; t < len; t++) {
+            if (write_slot_of(a, b, bos, t, &s)) {
+                set_err(err, errlen, "write entry of sequence %lld token %lld outside the table",
+                        (long long)b, (long long)t);
+                rc = 1;
+                break;
+            }
+            if (s == a->pad)
+                continue;
+            if (s < 0 || s >= a->slots) {
+                set_err(err, errlen, "write slot %lld of sequence %lld outside the pool",
+                        (long long)s, (long long)b);
+                rc = 1;
+                break;
+            }
+            if (writer[s] != -1 && writer[s] != b) {
+                set_err(err, errlen, "slot %lld written by two sequences (second: %lld)",
+                        (long long)s, (long long)b);
+                rc = 1;
+                break;
+            }
+            writer[s] = b;
+        }
+    }
+    for (int64_t b = 0; b < nseq && !rc; b++) {
+        int64_t bos, len, s;
+        seq_span(a, b, &bos, &len);
+        if (len == 0)
+            continue;
+        read_slot_of(a, b, bos, &s);
+        if (s != a->pad && writer[s] != -1 && writer[s] != b) {
+            set_err(err, errlen, "slot %lld read by sequence %lld and written by another",
+                    (long long)s, (long long)b);
+            rc = 1;
+        }
+    }
+    free(writer);
+    return rc;
+}
+
+/* ---- the update */
+
+int oracle_ssu(const oracle_args *a, char *err, int errlen)
+{
+    if (check_inputs(a, err, errlen))
+        return 1;
+    const int64_t H = a->H, P = a->P, N = a->N, G = a->G;
+    const int64_t heads_per_group = H / G;
+    const int64_t tile = P * N;
+    float *S = (float *)malloc((size_t)tile * sizeof(float));
+    const int64_t nseq = num_seqs(a);
+
+    for (int64_t b = 0; b < nseq; b++) {
+        int64_t bos, len;
+        seq_span(a, b, &bos, &len);
+        if (a->read_slot)
+            a->read_slot[b] = INT64_MIN;
+        if (len == 0)
+            continue; /* empty sequences are skipped */
+        int64_t rslot;
+        read_slot_of(a, b, bos, &rslot);
+        if (a->read_slot)
+            a->read_slot[b] = rslot;
+
+        for (int64_t h = 0; h < H; h++) {
+            const int64_t g = h / heads_per_group; /* R2 */
+            /* the tile this sequence starts from; the pad id reads as zeros */
+            for (int64_t e = 0; e < tile; e++)
+                S[e] = rslot == a->pad
+                           ? 0.0f
+                           : load_as_f32(a->pool_in, a->state_dtype, (rslot * H + h) * tile + e);
+
+            for (int64_t t = 0; t < len; t++) {
+                const int64_t r = bos + t;
+                for (int64_t d = 0; d < P; d++) {
+                    const int64_t xi = (r * H + h) * P + d;
+                    float v = a->dt_per_head ? load_as_f32(a->dt, a->dt_dtype, r * H + h)
+                                             : load_as_f32(a->dt, a->dt_dtype, xi);
+                    if (a->dt_bias)
+                        v = v + a->dt_bias[h]; /* R3 */
+                    if (a->dt_softplus)
+                        v = oracle_softplus(v);
+                    const float xv = load_as_f32(a->x, a->io_dtype, xi);
+                    const float decay = expf(v * a->A[h]);
+                    const float dtx = v * xv;
+                    float *Sd = S + d * N;
+                    for (int64_t n = 0; n < N; n++) {
+                        const float bn = load_as_f32(a->B, a->io_dtype, (r * G + g) * N + n);
+                        Sd[n] = Sd[n] * decay + dtx * bn;
+                    }
+                    float y = 0.0f;
+                    for (int64_t n = 0; n < N; n++) {
+                        const float cn = load_as_f32(a->C, a->io_dtype, (r * G + g) * N + n);
+                        y = y + Sd[n] * cn;
+                    }
+                    if (a->D)
+                        y = y + a->D[h] * xv;
+                    if (a->z)
+                        y = y * silu(load_as_f32(a->z, a->io_dtype, xi)); /* R6 */
+                    store_from_f32(a->out, a->io_dtype, xi, y);
+                }
+                /* R5: carry what the state dtype holds */
+                for (int64_t e = 0; e < tile; e++)
+                    S[e] = through_dtype(a->state_dtype, S[e]);
+                if (a->disable)
+                    continue;
+                int64_t wslot;
+                write_slot_of(a, b, bos, t, &wslot);
+                if (wslot == a->pad)
+                    continue; /* R10 */
+                for (int64_t e = 0; e < tile; e++)
+                    store_from_f32(a->pool_out, a->state_dtype, (wslot * H + h) * tile + e, S[e]);
+                if (a->written)
+                    a->written[wslot] = 1;
+            }
+        }
+    }
+    free(S);
+    return 0;
+}

@@ -1,0 +1,228 @@
+"""ctypes front end of the CPU oracle (oracle/ssu_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the package entry's smoke check and
+the benchmark's CPU-baseline leg are the only callers. The GPU package never
+imports this module.
+
+Input format (numpy, shared with the seeded workload generators): a dict with
+  state        [slots, H, P, N]; float32, or uint16 bit patterns for f16/bf16
+  state_dtype  'f32' | 'f16' | 'bf16'
+  io_dtype     dtype of x, B, C, z and of the output y
+  x            [R, H, P] (packed or one token per sequence) or [Bt, T, H, P]
+  dt           like x, or without the last axis (one value per head)
+  dt_dtype     'f32' or the io dtype
+  A            float32 [H];  D, dt_bias: float32 [H] or None
+  B, C         [R, G, N] or [Bt, T, G, N], io dtype
+  z            like x, or None
+  dt_softplus, disable_state_update: bool;  pad_slot_id: int
+  state_batch_indices, dst_state_batch_indices: None, an integer array
+               (1-D or 2-D), or an object with .base (1-D integer array),
+               .shape and .strides (element strides) describing a strided view
+  cu_seqlens, num_accepted_tokens: None or integer arrays
+Output: dict(y=..., state=new pool, written=bool[slots], read_slot=int64[nseq]).
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+DTYPES = {"f32": 0, "f16": 1, "bf16": 2}
+ONE_TOKEN, DENSE, CU = 0, 1, 2
+
+
+class _Table(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("len", ctypes.c_int64),
+                ("ndim", ctypes.c_int32), ("s0", ctypes.c_int64), ("s1", ctypes.c_int64)]
+
+
+class _Args(ctypes.Structure):
+    _fields_ = [
+        ("pool_in", ctypes.c_void_p), ("pool_out", ctypes.c_void_p),
+        ("state_dtype", ctypes.c_int32),
+        ("slots", ctypes.c_int64), ("H", ctypes.c_int64), ("P", ctypes.c_int64),
+        ("N", ctypes.c_int64), ("G", ctypes.c_int64),
+        ("R", ctypes.c_int64), ("io_dtype", ctypes.c_int32),
+        ("x", ctypes.c_void_p), ("dt", ctypes.c_void_p),
+        ("dt_dtype", ctypes.c_int32), ("dt_per_head", ctypes.c_int32),
+        ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("C", ctypes.c_void_p),
+        ("D", ctypes.c_void_p), ("z", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
+        ("dt_softplus", ctypes.c_int32),
+        ("layout", ctypes.c_int32), ("steps", ctypes.c_int64),
+        ("cu", ctypes.c_void_p), ("nseq", ctypes.c_int64), ("acc", ctypes.c_void_p),
+        ("rtab", _Table), ("wtab", _Table),
+        ("pad", ctypes.c_int64), ("disable", ctypes.c_int32),
+        ("out", ctypes.c_void_p), ("written", ctypes.c_void_p), ("read_slot", ctypes.c_void_p),
+    ]
+
+
+class OracleError(ValueError):
+    pass
+
+
+class Oracle:
+    """One loaded copy of the oracle library (tests may load a modified copy)."""
+
+    def __init__(self, path=None):
+        if path is None:
+            path = _build.LIB
+            if (not os.path.exists(path)
+                    or os.path.getmtime(path) < os.path.getmtime(_build.SRC)):
+                _build.build()
+        self.lib = ctypes.CDLL(path)
+        self.lib.oracle_ssu.argtypes = [ctypes.POINTER(_Args), ctypes.c_char_p, ctypes.c_int]
+        self.lib.oracle_ssu.restype = ctypes.c_int
+        self.lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
+        self.lib.oracle_f32_to_f16.restype = ctypes.c_uint16
+        self.lib.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
+        self.lib.oracle_f16_to_f32.restype = ctypes.c_float
+        self.lib.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+        self.lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
+        self.lib.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        self.lib.oracle_bf16_to_f32.restype = ctypes.c_float
+        self.lib.oracle_softplus.argtypes = [ctypes.c_float]
+        self.lib.oracle_softplus.restype = ctypes.c_float
+
+    # scalar helpers, exported for the pins
+    def f32_to_f16(self, v):
+        return self.lib.oracle_f32_to_f16(float(v))
+
+    def f16_to_f32(self, b):
+        return self.lib.oracle_f16_to_f32(int(b))
+
+    def f32_to_bf16(self, v):
+        return self.lib.oracle_f32_to_bf16(float(v))
+
+    def bf16_to_f32(self, b):
+        return self.lib.oracle_bf16_to_f32(int(b))
+
+    def softplus(self, v):
+        return self.lib.oracle_softplus(float(v))
+
+    def run(self, case):
+        return _run(self, case)
+
+
+_default = None
+
+
+def default():
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def run(case, oracle=None):
+    return (oracle or default()).run(case)
+
+
+def _np_dtype(name):
+    return np.float32 if name == "f32" else np.uint16
+
+
+def _arr(a, dtype):
+    a = np.ascontiguousarray(a)
+    if a.dtype != dtype:
+        raise OracleError("array of dtype %s where %s was expected" % (a.dtype, np.dtype(dtype)))
+    return a
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _table(t, keep):
+    if t is None:
+        return _Table(None, 0, 0, 0, 0)
+    if hasattr(t, "base") and hasattr(t, "strides") and not isinstance(t, np.ndarray):
+        base = np.ascontiguousarray(t.base, dtype=np.int64).ravel()
+        keep.append(base)
+        ndim = len(t.shape)
+        s0 = int(t.strides[0])
+        s1 = int(t.strides[1]) if ndim == 2 else 0
+        return _Table(base.ctypes.data, base.size, ndim, s0, s1)
+    t = np.asarray(t)
+    if t.ndim not in (1, 2):
+        raise OracleError("slot tables are 1-D or 2-D")
+    flat = np.ascontiguousarray(t, dtype=np.int64).ravel()
+    keep.append(flat)
+    if t.ndim == 1:
+        return _Table(flat.ctypes.data, flat.size, 1, 1, 0)
+    return _Table(flat.ctypes.data, flat.size, 2, t.shape[1], 1)
+
+
+def _run(oracle, case):
+    sd, io = case["state_dtype"], case["io_dtype"]
+    dtd = case.get("dt_dtype", io)
+    state = _arr(case["state"], _np_dtype(sd))
+    slots, H, P, N = state.shape
+    x = np.asarray(case["x"])
+    dense = x.ndim == 4
+    if dense:
+        Bt, T = x.shape[:2]
+        R = Bt * T
+    else:
+        R = x.shape[0]
+    xr = _arr(x.reshape(R, H, P), _np_dtype(io))
+    dt = np.asarray(case["dt"])
+    dt_per_head = dt.ndim == x.ndim - 1
+    dtr = _arr(dt.reshape((R, H) if dt_per_head else (R, H, P)), _np_dtype(dtd))
+    Bm = np.asarray(case["B"])
+    G = Bm.shape[-2]
+    Br = _arr(Bm.reshape(R, G, N), _np_dtype(io))
+    Cr = _arr(np.asarray(case["C"]).reshape(R, G, N), _np_dtype(io))
+    z = case.get("z")
+    zr = None if z is None else _arr(np.asarray(z).reshape(R, H, P), _np_dtype(io))
+    A = _arr(case["A"], np.float32)
+    D = case.get("D")
+    D = None if D is None else _arr(D, np.float32)
+    bias = case.get("dt_bias")
+    bias = None if bias is None else _arr(bias, np.float32)
+
+    cu = case.get("cu_seqlens")
+    acc = case.get("num_accepted_tokens")
+    keep = []
+    if cu is not None:
+        if dense:
+            raise OracleError("cu_seqlens goes with the packed [rows, heads, dim] form")
+        cu = np.ascontiguousarray(cu, dtype=np.int64)
+        layout, steps, nseq = CU, 0, cu.size - 1
+    elif dense:
+        layout, steps, nseq = DENSE, T, Bt
+    else:
+        layout, steps, nseq = ONE_TOKEN, 0, R
+    if acc is not None:
+        acc = np.ascontiguousarray(acc, dtype=np.int64)
+        if acc.size != nseq:
+            raise OracleError("num_accepted_tokens must have one entry per sequence")
+
+    pool_out = state.copy()
+    out = np.zeros((R, H, P), dtype=_np_dtype(io))
+    written = np.zeros(slots, dtype=np.uint8)
+    read_slot = np.zeros(max(nseq, 1), dtype=np.int64)
+    args = _Args()
+    args.pool_in, args.pool_out = _ptr(state), _ptr(pool_out)
+    args.state_dtype = DTYPES[sd]
+    args.slots, args.H, args.P, args.N, args.G = slots, H, P, N, G
+    args.R, args.io_dtype = R, DTYPES[io]
+    args.x, args.dt = _ptr(xr), _ptr(dtr)
+    args.dt_dtype, args.dt_per_head = DTYPES[dtd], int(dt_per_head)
+    args.A, args.B, args.C = _ptr(A), _ptr(Br), _ptr(Cr)
+    args.D, args.z, args.dt_bias = _ptr(D), _ptr(zr), _ptr(bias)
+    args.dt_softplus = int(bool(case.get("dt_softplus", False)))
+    args.layout, args.steps, args.nseq = layout, steps, nseq
+    args.cu, args.acc = _ptr(cu), _ptr(acc)
+    args.rtab = _table(case.get("state_batch_indices"), keep)
+    args.wtab = _table(case.get("dst_state_batch_indices"), keep)
+    args.pad = int(case.get("pad_slot_id", -1))
+    args.disable = int(bool(case.get("disable_state_update", False)))
+    args.out, args.written, args.read_slot = _ptr(out), _ptr(written), _ptr(read_slot)
+    err = ctypes.create_string_buffer(256)
+    rc = oracle.lib.oracle_ssu(ctypes.byref(args), err, 256)
+    if rc:
+        raise OracleError(err.value.decode())
+    y = out.reshape(x.shape) if dense else out
+    return {"y": y, "state": pool_out, "written": written.astype(bool),
+            "read_slot": read_slot[:nseq]}

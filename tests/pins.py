@@ -1,0 +1,531 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics
+fix, none of which retypes the oracle's own loop.
+
+Each pin takes an oracle instance (oracle.ssu_oracle.Oracle) and raises
+AssertionError (or the oracle's own error) when the oracle is wrong, so the
+same pins run against the real oracle and against copies of it with a planted
+mistake (tests/test_oracle_mutants.py).
+
+Sources:
+  MATE  = MATE docs, "Mamba / SSU" (table "SSU at a glance", the minimal, MTP
+          and flat-table examples, the API reference)
+  RSSM  = ReplaySSM article (lpnh.cn): section "三个瓶颈其实来自同一个动作"
+          (the Mamba-2 step and readout) and section "核心做法" (the unrolled
+          window S_h = g_h S_ckpt + sum_j g_{j+1:h} v_j k_j^T, and output-only
+          decode from a zero state, o = (v k^T) q = v (k^T q))
+"""
+import math
+
+import numpy as np
+import torch
+
+import workloads as W
+from oracle import brute64
+
+U32 = 2.0 ** -24  # unit roundoff of fp32
+
+
+def f64(a, dtype):
+    return brute64.to_f64(a, dtype)
+
+
+def ulp16(v, dtype):
+    """Spacing of the 16-bit format at |v| (bounded below by its subnormal step)."""
+    mant = 10 if dtype == "f16" else 7
+    e = np.floor(np.log2(np.maximum(np.abs(v), 1e-30)))
+    return np.maximum(2.0 ** (e - mant), 2.0 ** -24 if dtype == "f16" else 2.0 ** -133)
+
+
+def processed_dt(case):
+    """dt' = softplus(dt + dt_bias) in float64, broadcast to [R, H, P]."""
+    x = np.asarray(case["x"])
+    R = x.shape[0] * (x.shape[1] if x.ndim == 4 else 1)
+    H, P = x.shape[-2], x.shape[-1]
+    dt = f64(case["dt"], case.get("dt_dtype", case["io_dtype"]))
+    dt = dt.reshape(R, H, 1) if dt.size == R * H else dt.reshape(R, H, P)
+    dt = np.broadcast_to(dt, (R, H, P)).copy()
+    if case.get("dt_bias") is not None:
+        dt = dt + np.asarray(case["dt_bias"], np.float64)[None, :, None]
+    if case.get("dt_softplus"):
+        dt = np.where(dt > 20, dt, np.log1p(np.exp(np.minimum(dt, 20))))
+    return dt
+
+
+def small(kind, **kw):
+    return W.BUILDERS[kind](**kw)
+
+
+# ---------------------------------------------------------------- formats
+
+def pin_f16_decode_exhaustive(orc):
+    """Every binary16 bit pattern widens to NumPy's float16 -> float32 value."""
+    bits = np.arange(65536, dtype=np.uint16)
+    ref = bits.view(np.float16).astype(np.float32)
+    got = np.array([orc.f16_to_f32(b) for b in bits], dtype=np.float32)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def _f32_samples(n=60000, seed=0):
+    rng = np.random.default_rng(seed)
+    u = rng.integers(0, 2 ** 32, n, dtype=np.uint64).astype(np.uint32)
+    special = np.array([0.0, -0.0, 1.0, -1.0, 65504.0, 65519.99, 65520.0, 65536.0, 2.0 ** -24,
+                        2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -14, 2.0 ** -15 * 1.5, 1 + 2.0 ** -11,
+                        1 + 3 * 2.0 ** -11, 1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 3.0e38, np.inf,
+                        -np.inf, 1e-40], dtype=np.float32)
+    # values near binary16 / bfloat16 rounding boundaries
+    near = rng.standard_normal(20000).astype(np.float32) * np.float32(100)
+    near16 = near.astype(np.float16).astype(np.float32)
+    tie = (near16.view(np.uint32) + np.uint32(1 << 12)).view(np.float32)
+    return np.concatenate([u.view(np.float32), special, near, tie])
+
+
+def pin_f16_encode(orc):
+    """float32 -> binary16 rounds to nearest even, as NumPy's cast does."""
+    v = _f32_samples()
+    with np.errstate(over="ignore", invalid="ignore"):
+        ref = v.astype(np.float16).view(np.uint16)
+    got = np.array([orc.f32_to_f16(x) for x in v], dtype=np.uint16)
+    nan = np.isnan(v)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.all((got[nan] & 0x7C00) == 0x7C00) and np.all(got[nan] & 0x3FF)
+
+
+def pin_bf16_roundtrip(orc):
+    """float32 -> bfloat16 rounds to nearest even, as PyTorch's cast does;
+    bfloat16 -> float32 is the top half of the binary32 pattern."""
+    v = _f32_samples(seed=1)
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([orc.f32_to_bf16(x) for x in v], dtype=np.uint16)
+    nan = np.isnan(v)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.all((got[nan] & 0x7F80) == 0x7F80) and np.all(got[nan] & 0x7F)
+    bits = np.arange(0, 65536, 7, dtype=np.uint16)
+    back = np.array([orc.bf16_to_f32(b) for b in bits], dtype=np.float32)
+    ref_back = (bits.astype(np.uint32) << 16).view(np.float32)
+    ok = ~np.isnan(ref_back)
+    assert np.array_equal(back[ok].view(np.uint32), ref_back[ok].view(np.uint32))
+
+
+def pin_softplus(orc):
+    """softplus(0) = ln 2; softplus(v) = log(1 + e^v) to fp32 accuracy; and
+    above 20 the value itself (the difference is below half an ulp)."""
+    assert abs(orc.softplus(0.0) - math.log(2.0)) <= math.log(2.0) * U32 * 2
+    for v in np.linspace(-30, 30, 241):
+        v = float(np.float32(v))
+        ref = float(np.logaddexp(0.0, v))
+        assert abs(orc.softplus(v) - ref) <= 4 * U32 * max(ref, 1e-30), v
+    assert orc.softplus(25.5) == 25.5
+
+
+# ---------------------------------------------------------------- recurrence
+
+def pin_dt_zero_keeps_state(orc):
+    """dt = 0 without bias or softplus: the decay is exp(0) = 1 and the rank-1
+    term vanishes, so every stored tile equals the tile read, bit for bit."""
+    for sd in ("f32", "f16", "bf16"):
+        c = small("decode", batch=5, heads=4, dim=12, dstate=16, groups=2, slots=12,
+                  state_dtype=sd, io="bf16")
+        c["dt"] = np.zeros_like(c["dt"])
+        c["dt_bias"], c["dt_softplus"] = None, False
+        o = orc.run(c)
+        assert np.array_equal(o["state"], c["state"]), sd
+        assert o["written"].sum() == 5
+
+
+def pin_b_zero_pure_decay(orc):
+    """B = 0: each element becomes S * exp(dt * A[h]) (RSSM's step with a zero
+    rank-1 term); checked in float64 against the fp32 error bound."""
+    c = small("decode", batch=6, heads=4, dim=8, dstate=16, groups=2, slots=12, state_dtype="f32",
+              io="f32")
+    c["B"] = np.zeros_like(c["B"])
+    c["dt_bias"], c["dt_softplus"] = None, False
+    c["dt"] = np.abs(c["dt"]).astype(np.float32) * np.float32(0.5)
+    o = orc.run(c)
+    A = np.asarray(c["A"], np.float64)
+    rt = np.asarray(c["state_batch_indices"])
+    for b in range(6):
+        S0 = c["state"][rt[b]].astype(np.float64)
+        dt = np.asarray(c["dt"][b], np.float64)
+        arg = dt * A[:, None]
+        ref = S0 * np.exp(arg)[:, :, None]
+        bound = np.abs(ref) * (np.abs(arg)[:, :, None] * U32 + 3 * U32) * 1.5 + 1e-38
+        assert np.all(np.abs(o["state"][rt[b]] - ref) <= bound)
+
+
+def _zero_state_expected(case, rows):
+    """RSSM output-only decode from a zero state: S = dt' x B^T, so
+    y[d] = dt'[d] x[d] (B . C) + D x[d], times silu(z[d])."""
+    io = case["io_dtype"]
+    dtp = processed_dt(case)
+    X = f64(case["x"], io)
+    H = X.shape[1]
+    Bm, Cm = f64(case["B"], io), f64(case["C"], io)
+    G = Bm.shape[1]
+    out, scale = [], []
+    for r in rows:
+        bc = np.array([Bm[r, h // (H // G)] @ Cm[r, h // (H // G)] for h in range(H)])
+        babs = np.array([np.abs(Bm[r, h // (H // G)]) @ np.abs(Cm[r, h // (H // G)])
+                         for h in range(H)])
+        y = dtp[r] * X[r] * bc[:, None]
+        s = np.abs(dtp[r] * X[r]) * babs[:, None]
+        if case.get("D") is not None:
+            y = y + np.asarray(case["D"], np.float64)[:, None] * X[r]
+            s = s + np.abs(np.asarray(case["D"], np.float64)[:, None] * X[r])
+        if case.get("z") is not None:
+            Z = f64(case["z"], io)[r]
+            g = Z / (1 + np.exp(-Z))
+            y, s = y * g, s * np.abs(g)
+        out.append(y)
+        scale.append(s)
+    return np.array(out), np.array(scale)
+
+
+def pin_zero_state_closed_form(orc):
+    """Rows whose read slot is the pad id start from a zero state (MATE slot
+    semantics); their y must equal RSSM's output-only closed form."""
+    for io in ("f32", "bf16"):
+        c = small("decode_pad", batch=20, heads=4, dim=8, dstate=32, groups=2, slots=40,
+                  state_dtype="f32", io=io, pad_frac=0.25, pad_slot_id=0)
+        o = orc.run(c)
+        rows = c["pad_rows"]
+        ref, scale = _zero_state_expected(c, rows)
+        got = f64(o["y"], io)[rows]
+        tol = 40 * U32 * scale + 1e-30
+        if io != "f32":
+            tol = tol + ulp16(ref, io)
+        assert np.all(np.abs(got - ref) <= tol), io
+
+
+def pin_c_zero_and_z_zero(orc):
+    """C = 0 leaves y = D x silu(z); z = 0 makes y exactly 0 (silu(0) = 0)."""
+    c = small("decode", batch=4, heads=4, dim=8, dstate=16, groups=2, slots=8, state_dtype="f32",
+              io="f32")
+    c["C"] = np.zeros_like(c["C"])
+    o = orc.run(c)
+    X, Z = c["x"].astype(np.float64), c["z"].astype(np.float64)
+    ref = np.asarray(c["D"], np.float64)[None, :, None] * X * (Z / (1 + np.exp(-Z)))
+    assert np.all(np.abs(o["y"] - ref) <= 6 * U32 * np.abs(ref) + 1e-38)
+    c2 = small("decode", batch=4, heads=4, dim=8, dstate=16, groups=2, slots=8, state_dtype="f32",
+               io="f32")
+    c2["z"] = np.zeros_like(c2["z"])
+    assert np.all(orc.run(c2)["y"] == 0.0)
+
+
+def _chained(orc, case):
+    """The same sequences as T one-token calls: call t takes row bos+t of every
+    sequence with more than t tokens; call 0 reads the read slot, call t > 0
+    reads the slot call t-1 wrote; each call writes the token's destination."""
+    cu = np.asarray(case["cu_seqlens"], np.int64)
+    lens = np.diff(cu)
+    acc = case.get("num_accepted_tokens")
+    rt = np.asarray(case["state_batch_indices"])
+    wt = case.get("dst_state_batch_indices")
+    wt = rt if wt is None else np.asarray(wt)
+    two_d = rt.ndim == 2
+
+    def entry(tab, b, t):
+        return int(tab[b, t]) if two_d else int(tab[cu[b] + t])
+
+    pool = case["state"].copy()
+    y = np.zeros_like(case["x"])
+    for t in range(int(lens.max())):
+        seqs = [b for b in range(len(lens)) if lens[b] > t]
+        rows = np.array([cu[b] + t for b in seqs])
+        start = [0 if acc is None else max(int(acc[b]) - 1, 0) for b in seqs]
+        rd = np.array([entry(rt, b, s) if t == 0 else entry(wt, b, t - 1)
+                       for b, s in zip(seqs, start)], np.int64)
+        wr = np.array([entry(wt, b, t) for b in seqs], np.int64)
+        one = dict(case, state=pool, x=case["x"][rows], dt=case["dt"][rows], B=case["B"][rows],
+                   C=case["C"][rows], z=None if case.get("z") is None else case["z"][rows],
+                   state_batch_indices=rd, dst_state_batch_indices=wr, cu_seqlens=None,
+                   num_accepted_tokens=None)
+        o = orc.run(one)
+        pool = o["state"]
+        y[rows] = o["y"]
+    return y, pool
+
+
+def pin_mtp_equals_chained_calls(orc):
+    """A T-token MTP call equals T chained one-token calls, bit for bit, in
+    every state dtype (the carried state is the stored value)."""
+    for sd in ("f32", "f16", "bf16"):
+        c = small("mtp", nseq=5, steps=4, heads=4, dim=8, dstate=16, groups=2, state_dtype=sd,
+                  pad_slot_id=-1)
+        o = orc.run(c)
+        y, pool = _chained(orc, c)
+        assert np.array_equal(o["y"], y), sd
+        assert np.array_equal(o["state"], pool), sd
+    c = small("varlen", nseq=9, max_len=4, heads=4, dim=8, dstate=16, state_dtype="bf16", dst=False)
+    o = orc.run(c)
+    y, pool = _chained(orc, c)
+    assert np.array_equal(o["y"], y) and np.array_equal(o["state"], pool)
+
+
+def pin_unrolled_window(orc):
+    """RSSM's unrolled window: after T steps from S_0,
+    S_T = (prod_i a_i) S_0 + sum_j (prod_{i>j} a_i) dt_j x_j B_j^T, in float64."""
+    c = small("mtp", nseq=3, steps=6, heads=2, dim=8, dstate=16, groups=1, state_dtype="f32",
+              io="f32", pad_slot_id=-1)
+    c["num_accepted_tokens"] = np.ones(3, np.int32)
+    o = orc.run(c)
+    dtp = processed_dt(c)
+    A = np.asarray(c["A"], np.float64)
+    X, Bm = c["x"].astype(np.float64), c["B"].astype(np.float64)
+    rt, wt = c["state_batch_indices"], c["dst_state_batch_indices"]
+    for b in range(3):
+        for h in range(2):
+            S0 = c["state"][rt[b, 0], h].astype(np.float64)
+            rows = range(b * 6, b * 6 + 6)
+            alpha = [np.exp(dtp[r, h] * A[h]) for r in rows]
+            ST = np.prod(alpha, axis=0)[:, None] * S0
+            mag = np.abs(ST).copy()
+            for j, r in enumerate(rows):
+                tail = np.prod(alpha[j + 1:], axis=0) if j < 5 else np.ones(8)
+                term = (tail * dtp[r, h] * X[r, h])[:, None] * Bm[r, 0][None, :]
+                ST += term
+                mag += np.abs(term)
+            got = o["state"][wt[b, 5], h]
+            assert np.all(np.abs(got - ST) <= 6 * 8 * U32 * (mag + np.abs(S0)) + 1e-30)
+
+
+# ---------------------------------------------------------------- slots
+
+def pin_pad_slot_untouched(orc):
+    """pad_slot_id = 0 with slot 0 holding data: slot 0 stays byte-identical,
+    every other untouched slot too (MATE: pad is never written)."""
+    for sd in ("f32", "bf16"):
+        c = small("decode_pad", batch=24, heads=2, dim=8, dstate=16, groups=1, slots=48,
+                  state_dtype=sd, pad_frac=0.2, pad_slot_id=0)
+        assert np.any(c["state"][0] != 0)
+        o = orc.run(c)
+        assert not o["written"][0]
+        assert np.array_equal(o["state"][~o["written"]], c["state"][~o["written"]])
+        live = np.asarray(c["state_batch_indices"])
+        live = live[live != 0]
+        assert set(np.flatnonzero(o["written"])) == set(live.tolist())
+
+
+def pin_disable_keeps_pool(orc):
+    """disable_state_update leaves the whole pool byte-identical; y is the
+    same as with the update enabled."""
+    c = small("varlen", nseq=10, max_len=5, heads=2, dim=8, dstate=16)
+    o1 = orc.run(c)
+    o2 = orc.run(dict(c, disable_state_update=True))
+    assert np.array_equal(o2["state"], c["state"]) and not o2["written"].any()
+    assert np.array_equal(o1["y"], o2["y"])
+
+
+def pin_flat_equals_2d(orc):
+    """A 2-D [sequences, steps] table and the flat [rows] table name the same
+    entries for one sequence (MATE flat-table example) and, 1-D tables being
+    row-indexed, for uniform lengths."""
+    c = small("mtp", nseq=1, steps=7, heads=2, dim=8, dstate=16, groups=1, pad_slot_id=0)
+    c["num_accepted_tokens"] = np.array([1], np.int32)
+    o2 = orc.run(c)
+    flat = dict(c, state_batch_indices=c["state_batch_indices"].ravel(),
+                dst_state_batch_indices=c["dst_state_batch_indices"].ravel())
+    o1 = orc.run(flat)
+    assert np.array_equal(o1["y"], o2["y"]) and np.array_equal(o1["state"], o2["state"])
+    c = small("mtp", nseq=4, steps=3, heads=2, dim=8, dstate=16, groups=1, pad_slot_id=-1)
+    o2 = orc.run(c)
+    o1 = orc.run(dict(c, state_batch_indices=c["state_batch_indices"].ravel(),
+                      dst_state_batch_indices=c["dst_state_batch_indices"].ravel()))
+    assert np.array_equal(o1["y"], o2["y"]) and np.array_equal(o1["state"], o2["state"])
+    assert np.array_equal(o1["written"], o2["written"])
+
+
+def pin_strided_literal(orc):
+    """A [rows, 1] view with strides (1, 1) addresses entry b + t (MATE slot
+    semantics, "addressed by strides"); with one sequence that is row t."""
+    c = small("mtp", nseq=1, steps=5, heads=2, dim=8, dstate=16, groups=1, pad_slot_id=-1)
+    c["num_accepted_tokens"] = np.array([3], np.int32)
+    o2 = orc.run(c)
+    view = dict(c, state_batch_indices=W.Strided(c["state_batch_indices"].ravel(), (5, 1), (1, 1)),
+                dst_state_batch_indices=W.Strided(c["dst_state_batch_indices"].ravel(), (5, 1),
+                                                  (1, 1)))
+    o1 = orc.run(view)
+    assert np.array_equal(o1["y"], o2["y"]) and np.array_equal(o1["state"], o2["state"])
+    assert o1["read_slot"][0] == c["state_batch_indices"][0, 2]
+
+
+def pin_default_destination(orc):
+    """No destination table: each token publishes to its own entry of the read
+    table (MATE: the default the Triton kernel applies)."""
+    c = small("varlen", nseq=8, max_len=4, heads=2, dim=8, dstate=16, dst=False)
+    o1 = orc.run(c)
+    o2 = orc.run(dict(c, dst_state_batch_indices=c["state_batch_indices"].copy()))
+    assert np.array_equal(o1["y"], o2["y"]) and np.array_equal(o1["state"], o2["state"])
+    rows = int(np.asarray(c["cu_seqlens"])[-1])
+    assert set(np.flatnonzero(o1["written"])) == set(c["state_batch_indices"][:rows].tolist())
+
+
+def pin_empty_sequences(orc):
+    """Empty sequences are skipped: with a 2-D table their row of entries is
+    neither read nor written."""
+    c = small("mtp", nseq=4, steps=3, heads=2, dim=8, dstate=16, groups=1, pad_slot_id=-1)
+    # sequence 1 becomes empty: its rows are dropped from the packed inputs
+    keep = np.r_[0:3, 6:12]
+    c2 = dict(c, x=c["x"][keep], dt=c["dt"][keep], B=c["B"][keep], C=c["C"][keep],
+              z=c["z"][keep], cu_seqlens=np.array([0, 3, 3, 6, 9], np.int32))
+    o = orc.run(c2)
+    assert o["read_slot"][1] == np.iinfo(np.int64).min
+    for slot in list(c["state_batch_indices"][1]) + list(c["dst_state_batch_indices"][1]):
+        assert not o["written"][slot]
+    assert np.array_equal(o["state"][~o["written"]], c["state"][~o["written"]])
+
+
+def pin_accepted_floor(orc):
+    """num_accepted_tokens seeds the read at count - 1, floored at 0: 0 and 1
+    read the same entry; k reads entry k - 1."""
+    c = small("mtp", nseq=3, steps=4, heads=2, dim=8, dstate=16, groups=1, pad_slot_id=-1)
+    a0 = orc.run(dict(c, num_accepted_tokens=np.array([0, 0, 0], np.int32)))
+    a1 = orc.run(dict(c, num_accepted_tokens=np.array([1, 1, 1], np.int32)))
+    assert np.array_equal(a0["y"], a1["y"]) and np.array_equal(a0["state"], a1["state"])
+    a3 = orc.run(dict(c, num_accepted_tokens=np.array([3, 4, 2], np.int32)))
+    rt = c["state_batch_indices"]
+    assert list(a3["read_slot"]) == [rt[0, 2], rt[1, 3], rt[2, 1]]
+
+
+def pin_pad_destination_mid_sequence(orc):
+    """A pad destination skips that store only; later tokens continue from the
+    carried state, so y is unchanged and the pad slot keeps its bytes."""
+    c = small("mtp", nseq=2, steps=4, heads=2, dim=8, dstate=16, groups=1, pad_slot_id=-1)
+    w = c["dst_state_batch_indices"].copy()
+    # slot 0 is sequence 0's first read-table entry, which accepted count 2
+    # leaves unread
+    w[0, 1] = 0
+    c2 = dict(c, dst_state_batch_indices=w, pad_slot_id=0,
+              num_accepted_tokens=np.array([2, 2], np.int32))
+    ref = orc.run(dict(c, num_accepted_tokens=np.array([2, 2], np.int32)))
+    o = orc.run(c2)
+    assert np.array_equal(o["y"], ref["y"])
+    assert not o["written"][0] and np.array_equal(o["state"][0], c["state"][0])
+
+
+def pin_dt_per_head_broadcast(orc):
+    """dt with one value per head equals the same values repeated over dim."""
+    c = small("varlen", nseq=6, max_len=3, heads=4, dim=8, dstate=16)
+    o1 = orc.run(c)
+    P = c["x"].shape[-1]
+    o2 = orc.run(dict(c, dt=np.repeat(c["dt"][:, :, None], P, axis=2)))
+    assert np.array_equal(o1["y"], o2["y"]) and np.array_equal(o1["state"], o2["state"])
+
+
+def pin_groups(orc):
+    """groups = 1 equals B, C replicated to groups = heads; and with two groups
+    heads 0..H/2-1 use group 0 (a zero B, C there means pure decay)."""
+    c = small("decode", batch=3, heads=4, dim=8, dstate=16, groups=1, slots=6)
+    o1 = orc.run(c)
+    o2 = orc.run(dict(c, B=np.repeat(c["B"], 4, axis=1), C=np.repeat(c["C"], 4, axis=1)))
+    assert np.array_equal(o1["y"], o2["y"]) and np.array_equal(o1["state"], o2["state"])
+    c = small("decode", batch=3, heads=4, dim=8, dstate=16, groups=2, slots=6, state_dtype="f32",
+              io="f32")
+    c["B"][:, 0] = 0
+    c["C"][:, 0] = 0
+    o = orc.run(c)
+    X, Z = c["x"].astype(np.float64), c["z"].astype(np.float64)
+    ydz = np.asarray(c["D"], np.float64)[None, :, None] * X * (Z / (1 + np.exp(-Z)))
+    assert np.allclose(o["y"][:, :2], ydz[:, :2], rtol=1e-6, atol=0)
+    assert not np.allclose(o["y"][:, 2:], ydz[:, 2:], rtol=1e-3, atol=0)
+
+
+def pin_brute_force(orc, combos=48, seed=7):
+    """Whole oracle against the independent float64 brute force on tiny shapes
+    over the option space (layouts, tables, dtypes, bias/softplus, D, z, pad,
+    disable, accepted counts)."""
+    rng = np.random.default_rng(seed)
+    for k in range(combos):
+        kind = ["decode", "decode_pad", "mtp", "varlen"][k % 4]
+        sd = ["f32", "f16", "bf16"][rng.integers(3)]
+        io = ["bf16", "f16", "f32"][rng.integers(3)]
+        s = int(rng.integers(1 << 30))
+        if kind == "decode":
+            c = W.decode(seed=s, batch=3, heads=4, dim=4, dstate=8, groups=2, slots=8,
+                         state_dtype=sd, io=io)
+        elif kind == "decode_pad":
+            c = W.decode_pad(seed=s, batch=5, heads=2, dim=4, dstate=8, groups=1, slots=9,
+                             state_dtype=sd, io=io, pad_frac=0.4,
+                             pad_slot_id=int(rng.choice([0, -1])))
+        elif kind == "mtp":
+            c = W.mtp(seed=s, nseq=2, steps=3, heads=2, dim=4, dstate=8, groups=2, state_dtype=sd,
+                      io=io, pad_slot_id=int(rng.choice([0, -1])))
+        else:
+            c = W.varlen(seed=s, nseq=4, max_len=3, heads=2, dim=4, dstate=8, state_dtype=sd,
+                         io=io, dst=bool(rng.integers(2)), disable=bool(rng.integers(2)))
+        if rng.integers(2):
+            # without softplus dt must stay a non-negative step: U[0, 0.1) as
+            # in the MATE minimal example
+            c["dt_bias"], c["dt_softplus"] = None, False
+            dtd = c.get("dt_dtype", io)
+            c["dt"] = W.to_storage(rng.random(np.shape(c["dt"]), dtype=np.float32) * 0.1, dtd)
+        if rng.integers(3) == 0:
+            c["D"] = None
+        if rng.integers(3) == 0:
+            c["z"] = None
+        o = orc.run(c)
+        b = brute64.run(c)
+        assert np.array_equal(o["written"], b["written"]), k
+        S_o, S_b = f64(o["state"], sd), f64(b["state"], sd)
+        if sd == "f32":
+            tol = 64 * U32 * (np.abs(S_b) + 1)
+        else:
+            tol = 2 * ulp16(S_b, sd) + 64 * U32 * (np.abs(S_b) + 1)
+        assert np.all(np.abs(S_o - S_b) <= tol), (k, kind, sd)
+        y_o = f64(o["y"], io)
+        tol = 64 * U32 * (np.abs(b["y64"]) + 8) * 8
+        if io != "f32":
+            tol = tol + 2 * ulp16(b["y64"], io)
+        assert np.all(np.abs(y_o - b["y64"]) <= tol), (k, kind, io)
+
+
+# ---------------------------------------------------------------- golden
+
+GOLDEN = __import__("os").path.join(__import__("os").path.dirname(__file__), "golden",
+                                    "mate_examples.json")
+
+
+def golden_case(spec, seed=11):
+    """A call shaped like one of the MATE page's examples, with random layer
+    data (x, B, C bf16 N(0,1), dt fp32 U[0, 0.1), A = -U[0, 1))."""
+    import json
+    shape = json.load(open(GOLDEN))["shape"]
+    H, P, N, G = shape["heads"], shape["dim"], shape["dstate"], shape["groups"]
+    rng = np.random.default_rng(seed)
+    R = spec["x_rows"]
+    c = {"state_dtype": "f16", "io_dtype": "bf16", "dt_dtype": "f32"}
+    c["state"] = W.to_storage(rng.standard_normal((spec["slots"], H, P, N), dtype=np.float32), "f16")
+    c["x"] = W.to_storage(rng.standard_normal((R, H, P), dtype=np.float32), "bf16")
+    c["dt"] = rng.random((R, H, P), dtype=np.float32) * np.float32(0.1)
+    c["A"] = (-rng.random(H, dtype=np.float32)).astype(np.float32)
+    c["B"] = W.to_storage(rng.standard_normal((R, G, N), dtype=np.float32), "bf16")
+    c["C"] = W.to_storage(rng.standard_normal((R, G, N), dtype=np.float32), "bf16")
+    c.update(D=None, z=None, dt_bias=None, dt_softplus=False, disable_state_update=False,
+             pad_slot_id=spec["pad_slot_id"])
+    for k in ("state_batch_indices", "dst_state_batch_indices", "cu_seqlens",
+              "num_accepted_tokens"):
+        c[k] = None if spec[k] is None else np.array(spec[k], dtype=np.int32)
+    return c
+
+
+def pin_golden_mate_examples(orc):
+    """The MATE page's three examples: read and written slots as the page's
+    slot rules fix them (tests/golden/mate_examples.json)."""
+    import json
+    for spec in json.load(open(GOLDEN))["cases"]:
+        c = golden_case(spec)
+        o = orc.run(c)
+        assert list(o["read_slot"]) == spec["expected_read_slots"], spec["name"]
+        assert sorted(np.flatnonzero(o["written"]).tolist()) == spec["expected_written_slots"], \
+            spec["name"]
+        untouched = ~o["written"]
+        assert np.array_equal(o["state"][untouched], c["state"][untouched]), spec["name"]
+
+
+ALL = [pin_golden_mate_examples, pin_f16_decode_exhaustive, pin_f16_encode, pin_bf16_roundtrip, pin_softplus,
+       pin_dt_zero_keeps_state, pin_b_zero_pure_decay, pin_zero_state_closed_form,
+       pin_c_zero_and_z_zero, pin_mtp_equals_chained_calls, pin_unrolled_window,
+       pin_pad_slot_untouched, pin_disable_keeps_pool, pin_flat_equals_2d, pin_strided_literal,
+       pin_default_destination, pin_empty_sequences, pin_accepted_floor,
+       pin_pad_destination_mid_sequence, pin_dt_per_head_broadcast, pin_groups, pin_brute_force]

@@ -1,0 +1,76 @@
+"""Plants plausible mistakes in copies of the oracle's C source, on the CPU,
+and checks that the pins (tests/pins.py) catch every one of them."""
+import os
+
+import pytest
+
+import pins
+from oracle import build as obuild
+from oracle import ssu_oracle
+
+# (name, text in oracle/ssu_oracle.c, replacement)
+MUTANTS = [
+    ("drop_dt_bias", "v = v + a->dt_bias[h]; /* R3 */", "v = v;"),
+    ("softplus_is_exp", "v = oracle_softplus(v);", "v = expf(v);"),
+    ("softplus_threshold", "if (v > 20.0f)", "if (v > 0.0f)"),
+    ("decay_sign", "expf(v * a->A[h])", "expf(-v * a->A[h])"),
+    ("decay_without_dt", "expf(v * a->A[h])", "expf(a->A[h])"),
+    ("rank1_without_dt", "const float dtx = v * xv;", "const float dtx = xv;"),
+    ("decay_after_add", "Sd[n] = Sd[n] * decay + dtx * bn;", "Sd[n] = (Sd[n] + dtx * bn) * decay;"),
+    ("readout_uses_B", "const float cn = load_as_f32(a->C,", "const float cn = load_as_f32(a->B,"),
+    ("drop_D", "y = y + a->D[h] * xv;", "y = y;"),
+    ("gate_without_silu", "y = y * silu(load_as_f32(a->z, a->io_dtype, xi));",
+     "y = y * load_as_f32(a->z, a->io_dtype, xi);"),
+    ("gate_before_D",
+     "if (a->D)\n                        y = y + a->D[h] * xv;\n"
+     "                    if (a->z)\n"
+     "                        y = y * silu(load_as_f32(a->z, a->io_dtype, xi)); /* R6 */",
+     "if (a->z)\n                        y = y * silu(load_as_f32(a->z, a->io_dtype, xi));\n"
+     "                    if (a->D)\n                        y = y + a->D[h] * xv;"),
+    ("group_modulo", "const int64_t g = h / heads_per_group;", "const int64_t g = h % G;"),
+    ("dt_per_head_index", "load_as_f32(a->dt, a->dt_dtype, r * H + h)",
+     "load_as_f32(a->dt, a->dt_dtype, r * H)"),
+    ("no_accepted_floor", "if (pos0 < 0)\n            pos0 = 0;", ""),
+    ("accepted_not_minus_one", "pos0 = a->acc[b] - 1;", "pos0 = a->acc[b];"),
+    ("pad_written", "if (wslot == a->pad)\n                    continue; /* R10 */", ""),
+    ("pad_read_as_data", "S[e] = rslot == a->pad", "S[e] = rslot == -12345"),
+    ("disable_ignored",
+     "if (a->disable)\n                    continue;\n                int64_t wslot;",
+     "int64_t wslot;"),
+    ("carry_not_rounded", "S[e] = through_dtype(a->state_dtype, S[e]);", "S[e] = S[e];"),
+    ("default_dst_is_seq",
+     "a->wtab.data ? &a->wtab : (a->rtab.data ? &a->rtab : NULL)", "a->wtab.data ? &a->wtab : NULL"),
+    ("flat_write_b_plus_t", "int64_t i = tb->ndim == 1 ? bos + t :", "int64_t i = tb->ndim == 1 ? b + t :"),
+    ("flat_read_b_plus_pos",
+     "int64_t i = a->rtab.ndim == 1 ? bos + pos0 :", "int64_t i = a->rtab.ndim == 1 ? b + pos0 :"),
+    ("no_table_reads_zero", "if (!a->rtab.data) {\n        *slot = b;",
+     "if (!a->rtab.data) {\n        *slot = 0;"),
+    ("f16_truncates", "if (rem > 0x1000u || (rem == 0x1000u && (q & 1u)))\n        q++;", ""),
+    ("f16_ties_away", "(rem == 0x1000u && (q & 1u))", "(rem == 0x1000u)"),
+    ("f16_subnormal_decode", "(127 - 15 + 1 - k)", "(127 - 15 - k)"),
+    ("bf16_truncates", "round_shift(u, 16)", "(u >> 16)"),
+    ("bf16_decode_shift", "(uint32_t)b << 16", "(uint32_t)b << 15"),
+]
+
+
+def test_mutant_list_is_distinct():
+    assert len({m[0] for m in MUTANTS}) == len(MUTANTS)
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, old, new):
+    src = open(obuild.SRC).read()
+    assert src.count(old) == 1, "mutation site for %s not found exactly once" % name
+    path = tmp_path / ("oracle_%s.c" % name)
+    path.write_text(src.replace(old, new))
+    lib = obuild.build(str(path), str(tmp_path / ("liboracle_%s.so" % name)), extra=["-w"])
+    orc = ssu_oracle.Oracle(lib)
+    caught = None
+    for pin in pins.ALL:
+        try:
+            pin(orc)
+        except Exception as e:  # a failed assertion or an oracle refusal
+            caught = (pin.__name__, type(e).__name__)
+            break
+    assert caught is not None, "no pin catches mutant %s" % name
+    os.remove(lib)

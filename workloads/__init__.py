@@ -1,0 +1,239 @@
+"""Seeded synthetic inputs for the selective state update.
+
+Data only: this module draws random inputs and slot tables and holds none of
+the method's arithmetic. Both the CPU oracle and the GPU path take their inputs
+from here, as NumPy arrays in the format documented in oracle/ssu_oracle.py
+(16-bit floats are carried as uint16 bit patterns; PyTorch's CPU casts round
+float32 to them, nearest-even).
+
+The shapes follow the pages' workloads:
+  one_token_tiny  the MATE page's minimal example (batch 2, heads 8, dim 8,
+                  dstate 128, groups 2, 8 slots, fp16 state of zeros)
+  decode          one-token decode of a Mamba-2 layer (heads 128, dim 64,
+                  dstate 128, groups 8): a 4 MiB fp32 state per sequence, the
+                  size the ReplaySSM article quotes, at batch 256
+  decode_pad      the same layer with bf16 state at batch 1024, 5% pad rows,
+                  output into a caller-provided buffer
+  mtp             MTP packed decode, 64 sequences x 7 steps, 2-D read table and
+                  write table = read + rows, num_accepted_tokens ~ U{1..7}
+  varlen          512 sequences of lengths U{0..8}, flat tables, heads 64,
+                  groups 1, fp16 state, per-head dt, z gate and D
+Every builder takes keyword overrides so tests can shrink a workload.
+"""
+import numpy as np
+import torch
+
+__all__ = ["to_storage", "one_token_tiny", "decode", "decode_pad", "mtp", "varlen",
+           "Strided", "BUILDERS"]
+
+_CHUNK = 1 << 24
+
+
+class Strided:
+    """A strided view of a 1-D integer table: entry (i, j) is
+    base[i * strides[0] + j * strides[1]]."""
+
+    def __init__(self, base, shape, strides):
+        self.base = np.asarray(base)
+        self.shape = tuple(shape)
+        self.strides = tuple(strides)
+
+
+def to_storage(a, dtype):
+    """float32 array -> storage of `dtype` ('f32' | 'f16' | 'bf16')."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if dtype == "f32":
+        return a
+    tdt = torch.float16 if dtype == "f16" else torch.bfloat16
+    out = np.empty(a.shape, dtype=np.uint16)
+    fa, fo = a.reshape(-1), out.reshape(-1)
+    for i in range(0, fa.size, _CHUNK):
+        t = torch.from_numpy(fa[i:i + _CHUNK]).to(tdt)
+        fo[i:i + _CHUNK] = t.view(torch.int16).numpy().view(np.uint16)
+    return out
+
+
+def _normal(rng, shape, dtype):
+    """N(0,1) drawn in float32 chunks, stored in `dtype`."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float32 if dtype == "f32" else np.uint16)
+    for i in range(0, n, _CHUNK):
+        m = min(_CHUNK, n - i)
+        out[i:i + m] = to_storage(rng.standard_normal(m, dtype=np.float32), dtype)
+    return out.reshape(shape)
+
+
+def _pattern(shape, dtype):
+    """Deterministic filler for slots no row reads: the values (k % 251) / 64
+    for the flat element index k, so a stray store cannot go unnoticed."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float32 if dtype == "f32" else np.uint16)
+    for i in range(0, n, _CHUNK):
+        m = min(_CHUNK, n - i)
+        vals = ((np.arange(i, i + m, dtype=np.int64) % 251).astype(np.float32) - 125.0) / 64.0
+        out[i:i + m] = to_storage(vals, dtype)
+    return out.reshape(shape)
+
+
+def _pool(rng, slots, H, P, N, dtype, live_slots=None):
+    """State pool: N(0,1) on `live_slots` (all slots if None), the filler
+    pattern elsewhere."""
+    if live_slots is None:
+        return _normal(rng, (slots, H, P, N), dtype)
+    pool = _pattern((slots, H, P, N), dtype)
+    live = np.unique(np.asarray(live_slots))
+    live = live[(live >= 0) & (live < slots)]
+    if live.size:
+        pool[live] = _normal(rng, (live.size, H, P, N), dtype)
+    return pool
+
+
+def _layer(rng, R, H, P, N, G, io="bf16", dt_dtype="bf16", dt_per_head=False, z=True, D=True,
+           softplus=True, dt_dist="normal"):
+    """Per-row inputs of one Mamba-2 layer: x, dt, B, C, z, and the per-head
+    A, D, dt_bias (fp32). dt_bias = log(expm1(u)) with u log-uniform on
+    [1e-3, 1e-1], so softplus(dt_bias) = u, p. dt itself ~ N(0,1), or U[0,0.1)
+    for dt_dist='small' (the MATE example)."""
+    c = {"io_dtype": io, "dt_dtype": dt_dtype}
+    c["x"] = _normal(rng, (R, H, P), io)
+    dshape = (R, H) if dt_per_head else (R, H, P)
+    if dt_dist == "small":
+        c["dt"] = to_storage(rng.random(dshape, dtype=np.float32) * np.float32(0.1), dt_dtype)
+    else:
+        c["dt"] = _normal(rng, dshape, dt_dtype)
+    c["A"] = (-np.exp(rng.uniform(0.0, 4.0, H))).astype(np.float32)
+    c["B"] = _normal(rng, (R, G, N), io)
+    c["C"] = _normal(rng, (R, G, N), io)
+    c["z"] = _normal(rng, (R, H, P), io) if z else None
+    c["D"] = rng.standard_normal(H).astype(np.float32) if D else None
+    if softplus:
+        u = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), H))
+        c["dt_bias"] = np.log(np.expm1(u)).astype(np.float32)
+    else:
+        c["dt_bias"] = None
+    c["dt_softplus"] = bool(softplus)
+    return c
+
+
+def one_token_tiny(seed=0, tables=False):
+    """The MATE page's minimal example: batch 2, heads 8, dim 8, dstate 128,
+    groups 2, 8 slots; fp16 state of zeros; x, B, C bf16 N(0,1); dt fp32
+    U[0, 0.1); A = -U[0, 1); no D, z or dt_bias. Without tables each sequence
+    uses slot b; with tables, state_batch_indices = dst = [0, 1]."""
+    rng = np.random.default_rng(seed)
+    batch, H, P, N, G, slots = 2, 8, 8, 128, 2, 8
+    c = {"state_dtype": "f16", "io_dtype": "bf16", "dt_dtype": "f32"}
+    c["state"] = np.zeros((slots, H, P, N), dtype=np.uint16)
+    c["x"] = _normal(rng, (batch, H, P), "bf16")
+    c["dt"] = rng.random((batch, H, P), dtype=np.float32) * np.float32(0.1)
+    c["A"] = (-rng.random(H, dtype=np.float32)).astype(np.float32)
+    c["B"] = _normal(rng, (batch, G, N), "bf16")
+    c["C"] = _normal(rng, (batch, G, N), "bf16")
+    c.update(D=None, z=None, dt_bias=None, dt_softplus=False, pad_slot_id=-1,
+             disable_state_update=False, cu_seqlens=None, num_accepted_tokens=None)
+    if tables:
+        idx = np.array([0, 1], dtype=np.int32)
+        c["state_batch_indices"] = idx
+        c["dst_state_batch_indices"] = idx.copy()
+    else:
+        c["state_batch_indices"] = c["dst_state_batch_indices"] = None
+    return c
+
+
+def decode(seed=1, batch=256, heads=128, dim=64, dstate=128, groups=8, slots=512,
+           state_dtype="f32", io="bf16", index_dtype=np.int32, fill_unread=True):
+    """One-token decode of a Mamba-2 layer. Read = write slots are the first
+    `batch` entries of a random permutation of the pool (distinct slots).
+    Slots no row reads hold the deterministic filler when fill_unread."""
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(slots)[:batch].astype(index_dtype)
+    c = {"state_dtype": state_dtype}
+    c["state"] = _pool(rng, slots, heads, dim, dstate, state_dtype,
+                       perm if fill_unread else None)
+    c.update(_layer(rng, batch, heads, dim, dstate, groups, io=io, dt_dtype=io))
+    c.update(state_batch_indices=perm, dst_state_batch_indices=perm.copy(), pad_slot_id=-1,
+             disable_state_update=False, cu_seqlens=None, num_accepted_tokens=None)
+    return c
+
+
+def decode_pad(seed=2, batch=1024, heads=128, dim=64, dstate=128, groups=8, slots=2048,
+               state_dtype="bf16", io="bf16", pad_frac=0.05, pad_slot_id=0,
+               index_dtype=np.int32):
+    """Decode with pad rows: round(pad_frac * batch) rows read and write
+    pad_slot_id; live rows use distinct slots other than the pad id. With
+    pad_slot_id = 0, slot 0 holds non-zero data that must stay as it is."""
+    rng = np.random.default_rng(seed)
+    npad = int(round(pad_frac * batch))
+    pad_rows = rng.choice(batch, size=npad, replace=False)
+    cand = np.arange(slots)
+    cand = cand[cand != pad_slot_id]
+    live = rng.permutation(cand)[:batch - npad]
+    idx = np.empty(batch, dtype=np.int64)
+    mask = np.zeros(batch, dtype=bool)
+    mask[pad_rows] = True
+    idx[mask] = pad_slot_id
+    idx[~mask] = live
+    idx = idx.astype(index_dtype)
+    c = {"state_dtype": state_dtype}
+    live_and_pad = np.concatenate([live, [pad_slot_id]]) if pad_slot_id >= 0 else live
+    c["state"] = _pool(rng, slots, heads, dim, dstate, state_dtype, live_and_pad)
+    c.update(_layer(rng, batch, heads, dim, dstate, groups, io=io, dt_dtype=io))
+    c.update(state_batch_indices=idx, dst_state_batch_indices=idx.copy(),
+             pad_slot_id=pad_slot_id, disable_state_update=False, cu_seqlens=None,
+             num_accepted_tokens=None, pad_rows=np.sort(pad_rows))
+    return c
+
+
+def mtp(seed=3, nseq=64, steps=7, heads=128, dim=64, dstate=128, groups=8,
+        state_dtype="f32", io="bf16", pad_slot_id=0, index_dtype=np.int32,
+        meta_dtype=np.int32):
+    """MTP packed decode, as in the MATE page's MTP example: rows = nseq *
+    steps; read table arange(rows).view(nseq, steps), write table = read +
+    rows; cu_seqlens = arange(0, rows + 1, steps); num_accepted_tokens drawn
+    from U{1..steps}. The pool has 2 * rows slots."""
+    rng = np.random.default_rng(seed)
+    rows = nseq * steps
+    slots = 2 * rows
+    read = np.arange(rows, dtype=index_dtype).reshape(nseq, steps)
+    write = (read + rows).astype(index_dtype)
+    acc = rng.integers(1, steps + 1, nseq).astype(meta_dtype)
+    c = {"state_dtype": state_dtype}
+    read_slots = read[np.arange(nseq), np.maximum(acc.astype(np.int64) - 1, 0)]
+    c["state"] = _pool(rng, slots, heads, dim, dstate, state_dtype, read_slots)
+    c.update(_layer(rng, rows, heads, dim, dstate, groups, io=io, dt_dtype=io))
+    c.update(state_batch_indices=read, dst_state_batch_indices=write, pad_slot_id=pad_slot_id,
+             disable_state_update=False,
+             cu_seqlens=np.arange(0, rows + 1, steps).astype(meta_dtype),
+             num_accepted_tokens=acc)
+    return c
+
+
+def varlen(seed=4, nseq=512, max_len=8, heads=64, dim=64, dstate=128, groups=1,
+           state_dtype="f16", io="bf16", dst=True, disable=False, index_dtype=np.int32,
+           meta_dtype=np.int32, lengths=None):
+    """Variable-length packed decode: lengths ~ U{0..max_len} (empty sequences
+    included), flat [rows] tables (row-indexed), per-head dt, z gate and D.
+    The read table takes R distinct slots of a 2R-slot pool, the write table
+    the other R. dst=False omits the write table (stores go to the read
+    table's entries); disable=True sets disable_state_update."""
+    rng = np.random.default_rng(seed)
+    if lengths is None:
+        lengths = rng.integers(0, max_len + 1, nseq)
+    lengths = np.asarray(lengths, dtype=np.int64)
+    rows = int(lengths.sum())
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(meta_dtype)
+    slots = max(2 * rows, 1)
+    perm = rng.permutation(slots).astype(index_dtype)
+    read, write = perm[:rows], perm[rows:2 * rows]
+    starts = cu[:-1].astype(np.int64)[lengths > 0]
+    c = {"state_dtype": state_dtype}
+    c["state"] = _pool(rng, slots, heads, dim, dstate, state_dtype, read[starts])
+    c.update(_layer(rng, rows, heads, dim, dstate, groups, io=io, dt_dtype=io, dt_per_head=True))
+    c.update(state_batch_indices=read, dst_state_batch_indices=write if dst else None,
+             pad_slot_id=-1, disable_state_update=bool(disable), cu_seqlens=cu,
+             num_accepted_tokens=None)
+    return c
+
+
+BUILDERS = {"one_token_tiny": one_token_tiny, "decode": decode, "decode_pad": decode_pad,
+            "mtp": mtp, "varlen": varlen}
