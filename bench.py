@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark of the selective state update on one MI355X.
+
+One step = one ssu_update call over the whole workload (the decode workload
+by default: batch 256, heads 128, dim 64, dstate 128, groups 8, fp32 state,
+bf16 inputs, a 512-slot pool, read = write slots). Inputs are seeded,
+synthetic and resident in HBM before timing starts. W untimed warmup steps,
+then K timed steps bracketed by device synchronisation; HIP events on the
+launch stream give the kernel's average duration.
+
+Prints ONE JSON line:
+  value      whole-job algorithmic GB/s (minimal bytes the method must move,
+             per step, times K, over the timed wall time)
+  roofline   the kernel against the 8 TB/s HBM peak; traffic = HBM bytes from
+             the committed rocprofv3 FETCH_SIZE / WRITE_SIZE counters (scaled
+             by a plain copy of known size) when they were taken on the
+             current kernel source, else null
+  cpu_baseline  the CPU oracle timed on this host on the same workload
+Options: --config {decode, decode_pad, mtp, varlen, varlen_disable, varlen_nodst},
+--no-cpu-baseline, --calib-copy (also runs a plain device copy of the state's
+size, the calibration kernel for the counters).
+"""
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SSU decode achieved HBM GB/s (% of peak) and token-head updates/s"
+HBM_PEAK_GBS = 8000.0
+COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "mamba_selective_state_amd", "csrc", f)
+                  for f in ("ssu_kernels.hip", "ssu_internal.h")]
+
+DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+def workload(name):
+    import workloads as W
+    if name == "decode":
+        return W.decode(), ("decode: batch 256, heads 128, dim 64, dstate 128, groups 8, "
+                            "fp32 state (4 MiB per sequence), bf16 x/B/C/z/dt, 512-slot pool, "
+                            "read = write slots")
+    if name == "decode_pad":
+        return W.decode_pad(), ("decode_pad: batch 1024, heads 128, dim 64, dstate 128, groups 8, "
+                                "bf16 state, 2048-slot pool, 51 pad rows (pad id 0), out given")
+    if name == "mtp":
+        return W.mtp(), ("mtp: 64 sequences x 7 tokens, heads 128, dim 64, dstate 128, groups 8, "
+                         "fp32 state, 2-D tables, write = read + 448, accepted ~ U{1..7}")
+    if name.startswith("varlen"):
+        dst = name != "varlen_nodst"
+        dis = name == "varlen_disable"
+        return W.varlen(dst=dst, disable=dis), (
+            "%s: 512 sequences, lengths U{0..8}, heads 64, dim 64, dstate 128, groups 1, "
+            "fp16 state, flat tables, per-head dt%s" % (
+                name, ", disable_state_update" if dis else (", no dst table" if not dst else "")))
+    raise SystemExit("unknown --config %s" % name)
+
+
+def spans(case):
+    x = np.asarray(case["x"])
+    cu = case.get("cu_seqlens")
+    if cu is not None:
+        cu = np.asarray(cu, np.int64)
+        return [(int(cu[i]), int(cu[i + 1] - cu[i])) for i in range(cu.size - 1)]
+    if x.ndim == 4:
+        return [(b * x.shape[1], x.shape[1]) for b in range(x.shape[0])]
+    return [(r, 1) for r in range(x.shape[0])]
+
+
+def _entry(tab, b, first, t):
+    tab = np.asarray(tab)
+    return int(tab[first + t]) if tab.ndim == 1 else int(tab[b, t])
+
+
+def algorithmic_bytes(case):
+    """Minimal bytes one call must move: each distinct state tile read once
+    (pad reads cost nothing), each tile stored once, every input row and
+    per-head vector read once, y written once, table and metadata entries
+    read once. Returns (bytes, token-head updates)."""
+    slots, H, P, N = np.shape(case["state"])
+    sb = DTYPE_BYTES[case["state_dtype"]]
+    io = DTYPE_BYTES[case["io_dtype"]]
+    dtb = DTYPE_BYTES[case.get("dt_dtype", case["io_dtype"])]
+    x = np.asarray(case["x"])
+    R = x.shape[0] * (x.shape[1] if x.ndim == 4 else 1)
+    G = np.shape(case["B"])[-2]
+    pad = int(case.get("pad_slot_id", -1))
+    acc = case.get("num_accepted_tokens")
+    rt, wt = case.get("state_batch_indices"), case.get("dst_state_batch_indices")
+    wt = wt if wt is not None else rt
+    tile = H * P * N * sb
+    reads, writes, nseq = 0, 0, 0
+    for b, (first, n) in enumerate(spans(case)):
+        nseq += 1
+        if n == 0:
+            continue
+        start = 0 if acc is None else max(int(acc[b]) - 1, 0)
+        if (b if rt is None else _entry(rt, b, first, start)) != pad:
+            reads += 1
+        if not case.get("disable_state_update", False):
+            for t in range(n):
+                if (b if wt is None else _entry(wt, b, first, t)) != pad:
+                    writes += 1
+    per_head = np.ndim(case["dt"]) == x.ndim - 1
+    row = H * P * io * 2 + (H * P * io if case.get("z") is not None else 0)  # x, out, z
+    row += (H if per_head else H * P) * dtb + 2 * G * N * io                  # dt, B, C
+    vec = 4 * H * (1 + (case.get("D") is not None) + (case.get("dt_bias") is not None))
+    idx = 0
+    for t in (case.get("state_batch_indices"), case.get("dst_state_batch_indices")):
+        if t is not None:
+            idx += np.asarray(t).itemsize * (nseq if t is rt else R)
+    for t in (case.get("cu_seqlens"), acc):
+        if t is not None:
+            idx += np.asarray(t).nbytes
+    total = (reads + writes) * tile + R * row + vec + idx
+    return int(total), int(R * H)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()
+
+
+def traffic_from_counters(config):
+    """HBM bytes per launch from the committed counter summary, or None when
+    it is missing, for another workload, or taken on another kernel source."""
+    if not os.path.exists(COUNTERS):
+        return None
+    c = json.load(open(COUNTERS))
+    entry = c.get("workloads", {}).get(config)
+    if not entry or c.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return entry.get("hbm_bytes_per_dispatch")
+
+
+def cpu_baseline(case, alg_bytes, updates, reps):
+    from oracle import ssu_oracle
+    ssu_oracle.default()
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        ssu_oracle.run(case)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    return {"value": round(alg_bytes / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "updates_per_s": round(updates / t, 1),
+            "sample": "the whole workload, one call per repetition, median of %d (%.2f s each); "
+                      "single-threaded plain-C fp32 oracle incl. its NumPy wrapper" % (reps, t)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="decode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=4)
+    ap.add_argument("--calib-copy", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the selective state update has no cross-GPU step "
+              "(sequences and heads shard with no exchange); run it with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mamba_selective_state_amd as ssu
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_harness import TORCH, device_case
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    dev = torch.device("cuda", 0)
+    case, desc = workload(args.config)
+    alg_bytes, updates = algorithmic_bytes(case)
+    print("[bench] %s: %.3f GB per step" % (args.config, alg_bytes / 1e9), file=sys.stderr,
+          flush=True)
+    d = device_case(case, dev)
+    out = torch.empty(np.shape(case["x"]), dtype=TORCH[case["io_dtype"]], device=dev)
+    args_c = ssu.make_args(d["state"], d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                           d["dt_bias"], case.get("dt_softplus", False),
+                           d["state_batch_indices"], case.get("pad_slot_id", -1), out,
+                           case.get("disable_state_update", False),
+                           d["dst_state_batch_indices"], d["cu_seqlens"],
+                           d["num_accepted_tokens"])
+    x = np.asarray(case["x"])
+    plan = ssu.prewarm_selective_state_update(
+        state_dtype=TORCH[case["state_dtype"]], io_dtype=TORCH[case["io_dtype"]],
+        batch=x.shape[0], heads=x.shape[-2], dim=x.shape[-1], dstate=np.shape(case["state"])[-1],
+        groups=np.shape(case["B"])[-2],
+        slot_dtype=torch.int64 if np.asarray(case["state_batch_indices"]).dtype == np.int64
+        else torch.int32,
+        packed=x.ndim == 4 or case.get("cu_seqlens") is not None
+        or case.get("num_accepted_tokens") is not None,
+        dt_dtype=TORCH[case.get("dt_dtype", case["io_dtype"])])
+    stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream
+
+    for _ in range(args.warmup):
+        ssu.ssu_update(args_c, handle)
+    torch.cuda.synchronize(dev)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        ssu.ssu_update(args_c, handle)
+    end.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    event_ms = start.elapsed_time(end) / args.steps
+    print("[bench] %d steps: %.1f us per launch (events), %.1f us per step (wall)"
+          % (args.steps, event_ms * 1e3, wall / args.steps * 1e6), file=sys.stderr, flush=True)
+
+    if args.calib_copy:
+        nbytes = int(np.prod(np.shape(case["state"]))) * DTYPE_BYTES[case["state_dtype"]] // 2
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        print("[bench] calibration copy: %d bytes read, %d written" % (nbytes, nbytes),
+              file=sys.stderr, flush=True)
+
+    achieved = alg_bytes / (event_ms * 1e-3) / 1e9
+    traffic = traffic_from_counters(args.config)
+    result = {
+        "metric": METRIC,
+        "value": round(alg_bytes * args.steps / wall / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": desc, "bytes_per_step": alg_bytes,
+                   "token_head_updates_per_step": updates, "kernel": plan["kernel"]},
+        "pct_of_hbm_peak": round(100.0 * achieved / HBM_PEAK_GBS, 2),
+        "token_head_updates_per_s": round(updates * args.steps / wall, 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel_us": round(event_ms * 1e3, 2)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(case, alg_bytes, updates, args.cpu_reps)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

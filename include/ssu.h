@@ -1,0 +1,176 @@
+/*
+ * ssu.h -- C ABI of libssu: the Mamba-2 selective state update (SSU) decode
+ * step on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (MATE docs, "Mamba / SSU": the API reference of
+ * selective_state_update and the table "SSU at a glance"; ReplaySSM article,
+ * section "三个瓶颈其实来自同一个动作" for the step itself): for every sequence
+ * b and head h, with g = h / (heads / groups),
+ *
+ *   S      = state[read_slot(b), h]            ([dim, dstate]; zeros for the pad id)
+ *   for each token t of the sequence (row r):
+ *     dt'  = dt[r, h, d] (+ dt_bias[h]), then softplus if dt_softplus
+ *     S[d][n] = S[d][n] * exp(dt'[d] * A[h]) + dt'[d] * x[r, h, d] * B[r, g, n]
+ *     y[r, h, d] = (sum_n S[d][n] * C[r, g, n] + D[h] * x[r, h, d]) * silu(z[r, h, d])
+ *     state[write_slot(b, t), h] = S            (unless pad or disable_state_update)
+ *
+ * The recurrence runs in fp32; the state is stored in the state dtype (and
+ * the state carried to the next token is that stored value); 16-bit values
+ * round to nearest even.
+ *
+ * Slots (MATE, "SSU at a glance", rows "Slot semantics" and "Variable-length
+ * and MTP decode"):
+ *   - sequences: x [batch, heads, dim] is one token per sequence; x
+ *     [rows, heads, dim] with cu_seqlens [nseq + 1] is packed (sequence b owns
+ *     rows cu[b] .. cu[b+1]-1, empty sequences are skipped); x
+ *     [batch, steps, heads, dim] is the dense form (steps tokens each);
+ *   - read position: num_accepted_tokens[b] - 1, floored at 0 (0 without it);
+ *   - a 1-D table is row-indexed: sequence b's position t is entry
+ *     first_row(b) + t; a 2-D table is addressed by its strides,
+ *     b * stride[0] + t * stride[1]; without a read table the slot is b;
+ *   - every token stores to its own destination entry, or to its own entry of
+ *     the read table when no destination table is given;
+ *   - pad_slot_id reads as a zero state and is never written;
+ *     disable_state_update leaves the pool unchanged.
+ *
+ * Memory: every pointer in ssu_tensor_t is DEVICE memory owned by the caller.
+ * The library allocates nothing per call and keeps no pointer after a call
+ * returns. ssu_update is asynchronous on the given stream (a hipStream_t,
+ * NULL for the null stream) and performs no host/device synchronisation and
+ * no device-to-host copy, so it may be captured into a HIP graph.
+ *
+ * Device-resident values (slot ids, cu_seqlens, num_accepted_tokens) are never
+ * read on the host. Slot ids outside [0, slots) other than the pad id,
+ * decreasing cu_seqlens, read positions outside the table, or a slot written
+ * by one sequence and read or written by another are caller contract
+ * violations with undefined results.
+ *
+ * Errors: every entry point returns an ssu_status_t; ssu_last_error() gives a
+ * message (thread-local) naming the violated rule or the missing capability.
+ */
+#ifndef SSU_H
+#define SSU_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSU_ABI_VERSION 1
+
+#ifndef SSU_API
+#define SSU_API __attribute__((visibility("default")))
+#endif
+
+typedef enum {
+    SSU_F32 = 0,
+    SSU_F16 = 1,
+    SSU_BF16 = 2,
+    SSU_I32 = 3,
+    SSU_I64 = 4
+} ssu_dtype_t;
+
+typedef enum {
+    SSU_OK = 0,
+    SSU_ERR_VALUE = 1,           /* wrong shape, dtype, stride, alignment, or missing tensor */
+    SSU_ERR_NOT_IMPLEMENTED = 2, /* an option or size the library does not support */
+    SSU_ERR_HIP = 3              /* the HIP runtime reported an error (launch, attributes) */
+} ssu_status_t;
+
+/* A strided view of caller-owned device memory. data == NULL means "absent"
+ * (None). size[] and stride[] hold ndim entries; strides are in elements. */
+typedef struct {
+    const void *data;
+    int32_t dtype; /* ssu_dtype_t */
+    int32_t ndim;
+    int64_t size[4];
+    int64_t stride[4];
+} ssu_tensor_t;
+
+/* Bits of ssu_args_t.unsupported: options of the MATE API that this library
+ * does not implement; a set bit makes ssu_update return
+ * SSU_ERR_NOT_IMPLEMENTED naming the option. */
+enum {
+    SSU_OPT_STATE_SCALE = 1u << 0,
+    SSU_OPT_INTERMEDIATE_STATES = 1u << 1, /* intermediate_states_buffer / indices / scales */
+    SSU_OPT_RAND_SEED = 1u << 2,           /* stochastic rounding (not implemented on the MATE page either) */
+    SSU_OPT_CACHE_STEPS = 1u << 3,         /* cache_steps != 0 */
+    SSU_OPT_ALGORITHM = 1u << 4,           /* algorithm != "auto" */
+    SSU_OPT_BACKEND = 1u << 5              /* backend != "auto" */
+};
+
+/* Arguments of one update (MATE selective_state_update, same names).
+ *   state   [slots, heads, dim, dstate], contiguous, f32 / f16 / bf16, updated in place;
+ *           base 16-byte aligned.
+ *   x       [batch, heads, dim] | [rows, heads, dim] (with cu_seqlens) |
+ *           [batch, steps, heads, dim]; f32 / f16 / bf16; last stride 1.
+ *   dt      same leading shape as x with last axis dim (any strides, stride 0
+ *           over dim for one value per head), or without the last axis (one
+ *           value per head); f32 or the x dtype.
+ *   A       [heads] f32 (or more axes with stride 0: broadcast over dim/dstate).
+ *   B, C    [rows, groups, dstate] (or [batch, steps, groups, dstate]), x dtype,
+ *           last stride 1; heads % groups == 0.
+ *   D, dt_bias  [heads] f32 or absent (broadcast axes with stride 0 allowed).
+ *   z       like x or absent.
+ *   state_batch_indices, dst_state_batch_indices
+ *           absent, [rows] / [batch] (1-D, row-indexed), or 2-D [nseq, steps];
+ *           i32 / i64.
+ *   cu_seqlens          [nseq + 1] i32 / i64, with x [rows, heads, dim].
+ *   num_accepted_tokens [nseq] i32 / i64.
+ *   out     required at this level; same shape as x, x dtype, last stride 1.
+ *           Every row of out is written. */
+typedef struct {
+    ssu_tensor_t state, x, dt, A, B, C, D, z, dt_bias;
+    ssu_tensor_t state_batch_indices, dst_state_batch_indices;
+    ssu_tensor_t cu_seqlens, num_accepted_tokens;
+    ssu_tensor_t out;
+    int32_t dt_softplus;
+    int32_t disable_state_update;
+    int64_t pad_slot_id; /* default -1 */
+    uint32_t unsupported; /* SSU_OPT_* bits */
+} ssu_args_t;
+
+/* Configuration to prepare ahead of graph capture (MATE
+ * prewarm_selective_state_update). dt_dim is 1 for one dt value per head,
+ * else dim. packed selects the multi-token kernel (cu_seqlens, dense
+ * [batch, steps, ...], or num_accepted_tokens); slot_dtype and meta_dtype are
+ * accepted for compatibility (both index widths run in the same kernels). */
+typedef struct {
+    int32_t state_dtype, io_dtype, dt_dtype, slot_dtype, meta_dtype; /* ssu_dtype_t */
+    int32_t heads, dim, dstate, groups, dt_dim, packed;
+    int64_t max_rows; /* informational; 0 if unknown */
+} ssu_plan_desc_t;
+
+/* What ssu_plan selected (for logging and tests). */
+typedef struct {
+    char kernel[64];       /* name of the selected kernel variant */
+    int32_t block_threads; /* threads per workgroup */
+    int32_t rows_per_block;/* dim rows one workgroup covers */
+    int32_t blocks_per_seq_head; /* workgroups per (sequence, head) */
+    int32_t vgprs, sgprs;  /* registers of the selected kernel (0 if unknown) */
+} ssu_plan_info_t;
+
+/* Validate a configuration, select its kernel and load it onto the current
+ * device, so a later ssu_update of that shape launches with no first-use
+ * cost. Idempotent and thread-safe; info may be NULL. Errors: SSU_ERR_VALUE,
+ * SSU_ERR_NOT_IMPLEMENTED, SSU_ERR_HIP. */
+SSU_API ssu_status_t ssu_plan(const ssu_plan_desc_t *desc, ssu_plan_info_t *info);
+
+/* Validate the arguments on the host and enqueue exactly one kernel on
+ * `stream` (none when there are no rows). Asynchronous; allocates nothing;
+ * never reads device memory on the host. Works without a prior ssu_plan. */
+SSU_API ssu_status_t ssu_update(const ssu_args_t *args, void *stream);
+
+/* Message of the last failing call on this thread ("" if none). The pointer
+ * stays valid until the next call on the same thread. */
+SSU_API const char *ssu_last_error(void);
+
+/* SSU_ABI_VERSION of the library. */
+SSU_API int ssu_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSU_H */

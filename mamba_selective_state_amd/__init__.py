@@ -1,0 +1,11 @@
+"""Mamba-2 selective state update (SSU) decode for AMD MI355X (gfx950).
+
+The update runs in hand-written HIP kernels behind a C ABI (include/ssu.h,
+libssu.so); this package is its Python binding.
+"""
+from .ssu import (LIBRARY_PATH, SsuArgs, SsuError, make_args, prewarm_selective_state_update,
+                  selective_state_update, ssu_abi_version, ssu_last_error, ssu_plan, ssu_update)
+
+__all__ = ["selective_state_update", "prewarm_selective_state_update", "ssu_update", "ssu_plan",
+           "ssu_last_error", "ssu_abi_version", "make_args", "SsuArgs", "SsuError",
+           "LIBRARY_PATH"]

@@ -1,0 +1,489 @@
+// Host entry points of libssu: argument validation, kernel selection and the
+// single launch of ssu_update; ssu_plan (the prewarm of the MATE API).
+//
+// Validation only looks at shapes, strides, dtypes and pointer alignment; it
+// never reads device memory, so ssu_update makes no host/device copy and no
+// synchronisation (MATE docs, "Mamba / SSU", section "Graph capture").
+// Anything outside the supported contract is an error naming the rule or the
+// capability (MATE, the paragraph after "dt_limit": NotImplementedError or
+// ValueError rather than silently narrowing semantics).
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/ssu.h"
+#include "ssu_internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+ssu_status_t fail(ssu_status_t st, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_error = buf;
+    return st;
+}
+
+bool is_float(int d) { return d == SSU_F32 || d == SSU_F16 || d == SSU_BF16; }
+bool is_index(int d) { return d == SSU_I32 || d == SSU_I64; }
+int64_t elem_bytes(int d) { return (d == SSU_F16 || d == SSU_BF16) ? 2 : (d == SSU_I64 ? 8 : 4); }
+bool present(const ssu_tensor_t &t) { return t.data != nullptr; }
+bool dstate_supported(int64_t n) { return n == 16 || n == 32 || n == 64 || n == 128 || n == 256; }
+bool aligned(const void *p, int64_t bytes) { return (reinterpret_cast<uintptr_t>(p) % bytes) == 0; }
+
+const char *dtype_str(int d) {
+    switch (d) {
+    case SSU_F32: return "f32";
+    case SSU_F16: return "f16";
+    case SSU_BF16: return "bf16";
+    case SSU_I32: return "i32";
+    case SSU_I64: return "i64";
+    }
+    return "unknown";
+}
+
+// The row structure every per-row tensor shares with x.
+struct Rows {
+    int32_t ndim;   // 3 (rows, ...) or 4 (batch, steps, ...)
+    int64_t lead0;  // rows, or batch
+    int64_t lead1;  // steps (4-D only)
+    int64_t rows;   // total rows
+};
+
+// Checks that `t` is [lead..., M, K] (K omitted when k < 0) matching the row
+// structure, with strides >= 0, and returns the row stride and the strides
+// of the M and K axes. A 4-D tensor must be addressable as rows: its batch
+// stride equals steps * its step stride (or one of the two axes has size 1).
+ssu_status_t row_tensor(const char *name, const ssu_tensor_t &t, const Rows &rw, int64_t m,
+                        int64_t k, int64_t *sr, int64_t *sm, int64_t *sk) {
+    const int lead = rw.ndim - 2;
+    const int want = lead + 1 + (k >= 0 ? 1 : 0);
+    if (t.ndim != want)
+        return fail(SSU_ERR_VALUE, "%s must have %d dimensions, got %d", name, want, t.ndim);
+    for (int i = 0; i < t.ndim; i++)
+        if (t.stride[i] < 0)
+            return fail(SSU_ERR_VALUE, "%s has a negative stride", name);
+    if (t.size[0] != rw.lead0 || (lead == 2 && t.size[1] != rw.lead1))
+        return fail(SSU_ERR_VALUE, "%s leading shape does not match x", name);
+    if (t.size[lead] != m)
+        return fail(SSU_ERR_VALUE, "%s axis %d is %lld, expected %lld", name, lead,
+                    (long long)t.size[lead], (long long)m);
+    if (k >= 0 && t.size[lead + 1] != k)
+        return fail(SSU_ERR_VALUE, "%s last axis is %lld, expected %lld", name,
+                    (long long)t.size[lead + 1], (long long)k);
+    if (lead == 1) {
+        *sr = t.stride[0];
+    } else if (rw.lead1 == 1) {
+        *sr = t.stride[0];
+    } else {
+        if (rw.lead0 > 1 && t.stride[0] != rw.lead1 * t.stride[1])
+            return fail(SSU_ERR_NOT_IMPLEMENTED,
+                        "%s: a [batch, steps, ...] tensor must have batch stride = steps * step "
+                        "stride",
+                        name);
+        *sr = t.stride[1];
+    }
+    *sm = t.stride[lead];
+    *sk = k >= 0 ? t.stride[lead + 1] : 0;
+    return SSU_OK;
+}
+
+// Per-head fp32 vector: [heads], or [heads, ...] with stride 0 on the other
+// axes (a broadcast view).
+ssu_status_t head_vector(const char *name, const ssu_tensor_t &t, int64_t H, bool required,
+                         const float **ptr, int64_t *stride) {
+    if (!present(t)) {
+        if (required)
+            return fail(SSU_ERR_VALUE, "%s is required", name);
+        *ptr = nullptr;
+        *stride = 0;
+        return SSU_OK;
+    }
+    if (t.dtype != SSU_F32)
+        return fail(SSU_ERR_VALUE, "%s must be f32 per head, got %s", name, dtype_str(t.dtype));
+    if (t.ndim < 1 || t.ndim > 4 || t.size[0] != H)
+        return fail(SSU_ERR_VALUE, "%s must be [heads] (heads = %lld)", name, (long long)H);
+    for (int i = 1; i < t.ndim; i++)
+        if (t.stride[i] != 0 && t.size[i] != 1)
+            return fail(SSU_ERR_VALUE, "%s must be per head: axes after the first need stride 0",
+                        name);
+    if (t.stride[0] < 0 || !aligned(t.data, 4))
+        return fail(SSU_ERR_VALUE, "%s: bad stride or alignment", name);
+    *ptr = static_cast<const float *>(t.data);
+    *stride = t.stride[0];
+    return SSU_OK;
+}
+
+ssu_status_t slot_table(const char *name, const ssu_tensor_t &t, const Rows &rw, int64_t nseq,
+                        int32_t layout, int64_t steps, const void **ptr, int64_t *s0, int64_t *s1,
+                        bool *two_d, bool *i64) {
+    *ptr = nullptr;
+    *s0 = *s1 = 0;
+    *two_d = *i64 = false;
+    if (!present(t))
+        return SSU_OK;
+    if (!is_index(t.dtype))
+        return fail(SSU_ERR_VALUE, "%s must be i32 or i64, got %s", name, dtype_str(t.dtype));
+    if (!aligned(t.data, elem_bytes(t.dtype)))
+        return fail(SSU_ERR_VALUE, "%s is not aligned to its element size", name);
+    if (t.ndim == 1) {
+        if (t.size[0] != rw.rows)
+            return fail(SSU_ERR_VALUE,
+                        "%s is 1-D (one entry per row) with %lld entries; the call has %lld rows",
+                        name, (long long)t.size[0], (long long)rw.rows);
+        if (t.stride[0] < 0)
+            return fail(SSU_ERR_VALUE, "%s has a negative stride", name);
+        *s0 = t.stride[0];
+    } else if (t.ndim == 2) {
+        if (t.size[0] < nseq)
+            return fail(SSU_ERR_VALUE, "%s is 2-D with %lld rows; the call has %lld sequences",
+                        name, (long long)t.size[0], (long long)nseq);
+        if (layout == ssu::kDense && t.size[1] < steps)
+            return fail(SSU_ERR_VALUE, "%s has %lld columns; the call has %lld steps", name,
+                        (long long)t.size[1], (long long)steps);
+        if (t.stride[0] < 0 || t.stride[1] < 0)
+            return fail(SSU_ERR_VALUE, "%s has a negative stride", name);
+        *s0 = t.stride[0];
+        *s1 = t.stride[1];
+        *two_d = true;
+    } else {
+        return fail(SSU_ERR_VALUE, "%s must be 1-D [rows] or 2-D [sequences, steps]", name);
+    }
+    *ptr = t.data;
+    *i64 = t.dtype == SSU_I64;
+    return SSU_OK;
+}
+
+ssu_status_t meta_vector(const char *name, const ssu_tensor_t &t, int64_t want, const void **ptr,
+                         int64_t *stride, bool *i64) {
+    *ptr = nullptr;
+    *stride = 0;
+    *i64 = false;
+    if (!present(t))
+        return SSU_OK;
+    if (!is_index(t.dtype))
+        return fail(SSU_ERR_VALUE, "%s must be i32 or i64, got %s", name, dtype_str(t.dtype));
+    if (t.ndim != 1 || (want >= 0 && t.size[0] != want))
+        return fail(SSU_ERR_VALUE, "%s must be 1-D with %lld entries", name, (long long)want);
+    if (t.stride[0] < 0 || !aligned(t.data, elem_bytes(t.dtype)))
+        return fail(SSU_ERR_VALUE, "%s: bad stride or alignment", name);
+    *ptr = t.data;
+    *stride = t.stride[0];
+    *i64 = t.dtype == SSU_I64;
+    return SSU_OK;
+}
+
+struct Geometry {
+    int32_t block, rows_per_block, dim_tiles;
+};
+
+Geometry geometry(int64_t P, int64_t N) {
+    const int passes = ssu::passes_for(static_cast<int>(N));
+    const int64_t rows_per_wave = ssu::kRowsPerPass * passes;
+    int64_t waves = (P + rows_per_wave - 1) / rows_per_wave;
+    if (waves > ssu::kMaxWaves)
+        waves = ssu::kMaxWaves;
+    if (waves < 1)
+        waves = 1;
+    Geometry g;
+    g.block = static_cast<int32_t>(waves * ssu::kWaveLanes);
+    g.rows_per_block = static_cast<int32_t>(waves * rows_per_wave);
+    g.dim_tiles = static_cast<int32_t>((P + g.rows_per_block - 1) / g.rows_per_block);
+    return g;
+}
+
+const char *unsupported_option(uint32_t bits) {
+    if (bits & SSU_OPT_STATE_SCALE) return "state_scale";
+    if (bits & SSU_OPT_INTERMEDIATE_STATES) return "intermediate_states_buffer / intermediate_state_indices / intermediate_state_scales";
+    if (bits & SSU_OPT_RAND_SEED) return "rand_seed (stochastic rounding)";
+    if (bits & SSU_OPT_CACHE_STEPS) return "cache_steps";
+    if (bits & SSU_OPT_ALGORITHM) return "algorithm other than 'auto'";
+    if (bits & SSU_OPT_BACKEND) return "backend other than 'auto'";
+    return nullptr;
+}
+
+// Vector width (elements) of the kernel's dstate accesses for a state dtype.
+int64_t access_vec(int state_dtype, int64_t N) {
+    const int64_t per16 = 16 / elem_bytes(state_dtype);
+    const int64_t e = N / ssu::kLanesPerRow;
+    return per16 < e ? per16 : e;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssu_abi_version(void) { return SSU_ABI_VERSION; }
+
+const char *ssu_last_error(void) { return g_error.c_str(); }
+
+ssu_status_t ssu_plan(const ssu_plan_desc_t *desc, ssu_plan_info_t *info) {
+    if (!desc)
+        return fail(SSU_ERR_VALUE, "ssu_plan: desc is NULL");
+    if (!is_float(desc->state_dtype))
+        return fail(SSU_ERR_VALUE, "state_dtype must be f32, f16 or bf16");
+    if (!is_float(desc->io_dtype))
+        return fail(SSU_ERR_VALUE, "io_dtype must be f32, f16 or bf16");
+    if (desc->dt_dtype != SSU_F32 && desc->dt_dtype != desc->io_dtype)
+        return fail(SSU_ERR_VALUE, "dt_dtype must be f32 or the io dtype");
+    if (!is_index(desc->slot_dtype) || !is_index(desc->meta_dtype))
+        return fail(SSU_ERR_VALUE, "slot_dtype and meta_dtype must be i32 or i64");
+    if (desc->heads <= 0 || desc->dim <= 0 || desc->groups <= 0)
+        return fail(SSU_ERR_VALUE, "heads, dim and groups must be positive");
+    if (desc->heads % desc->groups != 0)
+        return fail(SSU_ERR_VALUE, "heads (%d) must be divisible by groups (%d)", desc->heads,
+                    desc->groups);
+    if (!dstate_supported(desc->dstate))
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "dstate %d is not supported (16, 32, 64, 128, 256)",
+                    desc->dstate);
+    if (desc->dt_dim != 1 && desc->dt_dim != desc->dim)
+        return fail(SSU_ERR_VALUE, "dt_dim must be 1 or dim");
+    ssu::KernelRef k;
+    const bool multi = desc->packed != 0;
+    if (!ssu::find_kernel(desc->state_dtype, desc->io_dtype, desc->dstate, multi, &k))
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "no kernel for this dtype combination");
+    int vgprs = 0, sgprs = 0;
+    const int e = ssu::kernel_attributes(k, &vgprs, &sgprs);
+    if (e != 0)
+        return fail(SSU_ERR_HIP, "loading the kernel failed: %s", ssu::hip_error_string(e));
+    if (info) {
+        const Geometry g = geometry(desc->dim, desc->dstate);
+        memset(info, 0, sizeof *info);
+        ssu::kernel_name(desc->state_dtype, desc->io_dtype, desc->dstate, multi, info->kernel,
+                         sizeof info->kernel);
+        info->block_threads = g.block;
+        info->rows_per_block = g.rows_per_block;
+        info->blocks_per_seq_head = g.dim_tiles;
+        info->vgprs = vgprs;
+        info->sgprs = sgprs;
+    }
+    g_error.clear();
+    return SSU_OK;
+}
+
+ssu_status_t ssu_update(const ssu_args_t *a, void *stream) {
+    if (!a)
+        return fail(SSU_ERR_VALUE, "ssu_update: args is NULL");
+    if (const char *opt = unsupported_option(a->unsupported))
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "%s is not implemented", opt);
+
+    // state pool [slots, heads, dim, dstate], contiguous
+    const ssu_tensor_t &st = a->state;
+    if (!present(st))
+        return fail(SSU_ERR_VALUE, "state is required");
+    if (!is_float(st.dtype))
+        return fail(SSU_ERR_VALUE, "state must be f32, f16 or bf16, got %s", dtype_str(st.dtype));
+    if (st.ndim != 4)
+        return fail(SSU_ERR_VALUE, "state must be [slots, heads, dim, dstate]");
+    const int64_t slots = st.size[0], H = st.size[1], P = st.size[2], N = st.size[3];
+    if (slots <= 0 || H <= 0 || P <= 0 || N <= 0)
+        return fail(SSU_ERR_VALUE, "state has an empty axis");
+    if (st.stride[3] != 1 || st.stride[2] != N || st.stride[1] != P * N || st.stride[0] != H * P * N)
+        return fail(SSU_ERR_VALUE, "state must be contiguous");
+    if (!aligned(st.data, 16))
+        return fail(SSU_ERR_VALUE, "state must be 16-byte aligned");
+    if (!dstate_supported(N))
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "dstate %lld is not supported (16, 32, 64, 128, 256)",
+                    (long long)N);
+    if (H > INT32_MAX || P > INT32_MAX)
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "heads or dim too large");
+
+    // x and the row structure
+    const ssu_tensor_t &x = a->x;
+    if (!present(x))
+        return fail(SSU_ERR_VALUE, "x is required");
+    if (!is_float(x.dtype))
+        return fail(SSU_ERR_VALUE, "x must be f32, f16 or bf16, got %s", dtype_str(x.dtype));
+    const int io = x.dtype;
+    Rows rw;
+    rw.ndim = x.ndim;
+    if (x.ndim == 3) {
+        rw.lead0 = x.size[0];
+        rw.lead1 = 1;
+        rw.rows = x.size[0];
+    } else if (x.ndim == 4) {
+        rw.lead0 = x.size[0];
+        rw.lead1 = x.size[1];
+        rw.rows = x.size[0] * x.size[1];
+    } else {
+        return fail(SSU_ERR_VALUE,
+                    "x must be [batch, heads, dim], [rows, heads, dim] or [batch, steps, heads, dim]");
+    }
+    if (rw.lead0 < 0 || rw.lead1 < 0)
+        return fail(SSU_ERR_VALUE, "x has a negative size");
+    ssu::Params p;
+    memset(&p, 0, sizeof p);
+    int64_t sk = 0;
+    ssu_status_t s;
+    if ((s = row_tensor("x", x, rw, H, P, &p.x_sr, &p.x_sh, &sk)) != SSU_OK)
+        return s;
+    if (sk != 1)
+        return fail(SSU_ERR_VALUE, "x must have unit stride over dim");
+    if (!aligned(x.data, elem_bytes(io)))
+        return fail(SSU_ERR_VALUE, "x is not aligned to its element size");
+
+    // sequences
+    int64_t nseq = 0, steps = 0;
+    int32_t layout;
+    if (present(a->cu_seqlens)) {
+        if (x.ndim != 3)
+            return fail(SSU_ERR_VALUE, "cu_seqlens goes with the packed [rows, heads, dim] x");
+        if (a->cu_seqlens.ndim != 1 || a->cu_seqlens.size[0] < 1)
+            return fail(SSU_ERR_VALUE, "cu_seqlens must be 1-D [nseq + 1]");
+        nseq = a->cu_seqlens.size[0] - 1;
+        layout = ssu::kCuSeqlens;
+    } else if (x.ndim == 4) {
+        nseq = rw.lead0;
+        steps = rw.lead1;
+        layout = ssu::kDense;
+    } else {
+        nseq = rw.rows;
+        layout = ssu::kOneToken;
+    }
+    bool cu_i64 = false, acc_i64 = false;
+    if ((s = meta_vector("cu_seqlens", a->cu_seqlens, nseq + 1, &p.cu, &p.cu_s, &cu_i64)) != SSU_OK)
+        return s;
+    if ((s = meta_vector("num_accepted_tokens", a->num_accepted_tokens, nseq, &p.acc, &p.acc_s,
+                         &acc_i64)) != SSU_OK)
+        return s;
+    const bool multi = layout != ssu::kOneToken || p.acc != nullptr;
+
+    // dt: full [.., heads, dim] (any strides) or one value per head
+    const ssu_tensor_t &dt = a->dt;
+    if (!present(dt))
+        return fail(SSU_ERR_VALUE, "dt is required");
+    if (dt.dtype != SSU_F32 && dt.dtype != io)
+        return fail(SSU_ERR_VALUE, "dt must be f32 or the x dtype, got %s", dtype_str(dt.dtype));
+    if (!aligned(dt.data, elem_bytes(dt.dtype)))
+        return fail(SSU_ERR_VALUE, "dt is not aligned to its element size");
+    if (dt.ndim == x.ndim) {
+        if ((s = row_tensor("dt", dt, rw, H, P, &p.dt_sr, &p.dt_sh, &p.dt_sp)) != SSU_OK)
+            return s;
+    } else if (dt.ndim == x.ndim - 1) {
+        if ((s = row_tensor("dt", dt, rw, H, -1, &p.dt_sr, &p.dt_sh, &sk)) != SSU_OK)
+            return s;
+        p.dt_sp = 0;
+    } else {
+        return fail(SSU_ERR_VALUE, "dt must be shaped like x, or like x without its last axis");
+    }
+
+    // per-head vectors
+    if ((s = head_vector("A", a->A, H, true, &p.A, &p.A_sh)) != SSU_OK)
+        return s;
+    if ((s = head_vector("D", a->D, H, false, &p.D, &p.D_sh)) != SSU_OK)
+        return s;
+    if ((s = head_vector("dt_bias", a->dt_bias, H, false, &p.dt_bias, &p.bias_sh)) != SSU_OK)
+        return s;
+
+    // B and C: [.., groups, dstate] in the x dtype
+    if (!present(a->B) || !present(a->C))
+        return fail(SSU_ERR_VALUE, "B and C are required");
+    if (a->B.dtype != io || a->C.dtype != io)
+        return fail(SSU_ERR_VALUE, "B and C must have the x dtype");
+    const int64_t G = a->B.ndim >= 2 ? a->B.size[a->B.ndim - 2] : 0;
+    if (G <= 0 || H % G != 0)
+        return fail(SSU_ERR_VALUE, "heads (%lld) must be divisible by groups (%lld)", (long long)H,
+                    (long long)G);
+    if ((s = row_tensor("B", a->B, rw, G, N, &p.B_sr, &p.B_sg, &sk)) != SSU_OK)
+        return s;
+    if (sk != 1)
+        return fail(SSU_ERR_VALUE, "B must have unit stride over dstate");
+    if ((s = row_tensor("C", a->C, rw, G, N, &p.C_sr, &p.C_sg, &sk)) != SSU_OK)
+        return s;
+    if (sk != 1)
+        return fail(SSU_ERR_VALUE, "C must have unit stride over dstate");
+    {
+        const int64_t vec = access_vec(st.dtype, N);
+        const int64_t bytes = vec * elem_bytes(io);
+        if (!aligned(a->B.data, bytes) || !aligned(a->C.data, bytes) || p.B_sr % vec ||
+            p.B_sg % vec || p.C_sr % vec || p.C_sg % vec)
+            return fail(SSU_ERR_VALUE,
+                        "B and C rows must start on %lld-byte boundaries (base and strides)",
+                        (long long)bytes);
+    }
+
+    // z and out
+    if (present(a->z)) {
+        if (a->z.dtype != io)
+            return fail(SSU_ERR_VALUE, "z must have the x dtype");
+        if ((s = row_tensor("z", a->z, rw, H, P, &p.z_sr, &p.z_sh, &sk)) != SSU_OK)
+            return s;
+        if (sk != 1)
+            return fail(SSU_ERR_VALUE, "z must have unit stride over dim");
+        if (!aligned(a->z.data, elem_bytes(io)))
+            return fail(SSU_ERR_VALUE, "z is not aligned to its element size");
+        p.z = a->z.data;
+    }
+    if (!present(a->out))
+        return fail(SSU_ERR_VALUE, "out is required");
+    if (a->out.dtype != io)
+        return fail(SSU_ERR_VALUE, "out must have the x dtype");
+    if ((s = row_tensor("out", a->out, rw, H, P, &p.out_sr, &p.out_sh, &sk)) != SSU_OK)
+        return s;
+    if (sk != 1)
+        return fail(SSU_ERR_VALUE, "out must have unit stride over dim");
+    if (!aligned(a->out.data, elem_bytes(io)))
+        return fail(SSU_ERR_VALUE, "out is not aligned to its element size");
+
+    // slot tables
+    bool r2d, ri64, w2d, wi64;
+    if ((s = slot_table("state_batch_indices", a->state_batch_indices, rw, nseq, layout, steps,
+                        &p.rtab, &p.r_s0, &p.r_s1, &r2d, &ri64)) != SSU_OK)
+        return s;
+    if ((s = slot_table("dst_state_batch_indices", a->dst_state_batch_indices, rw, nseq, layout,
+                        steps, &p.wtab, &p.w_s0, &p.w_s1, &w2d, &wi64)) != SSU_OK)
+        return s;
+
+    if (nseq <= 0 || rw.rows <= 0)
+        return g_error.clear(), SSU_OK;  // nothing to do
+    if (nseq > INT32_MAX)
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "too many sequences");
+
+    ssu::KernelRef k;
+    if (!ssu::find_kernel(st.dtype, io, static_cast<int>(N), multi, &k))
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "no kernel for state %s / io %s / dstate %lld",
+                    dtype_str(st.dtype), dtype_str(io), (long long)N);
+    const Geometry geo = geometry(P, N);
+    const int64_t grid = nseq * H * geo.dim_tiles;
+    if (grid > INT32_MAX)
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "grid of %lld workgroups is too large",
+                    (long long)grid);
+
+    p.state = const_cast<void *>(st.data);
+    p.slot_stride = H * P * N;
+    p.x = x.data;
+    p.dt = dt.data;
+    p.B = a->B.data;
+    p.C = a->C.data;
+    p.out = const_cast<void *>(a->out.data);
+    p.pad = a->pad_slot_id;
+    p.nseq = static_cast<int32_t>(nseq);
+    p.H = static_cast<int32_t>(H);
+    p.P = static_cast<int32_t>(P);
+    p.heads_per_group = static_cast<int32_t>(H / G);
+    p.steps = static_cast<int32_t>(steps);
+    p.layout = layout;
+    p.dim_tiles = geo.dim_tiles;
+    p.rows_per_block = geo.rows_per_block;
+    p.flags = (dt.dtype == SSU_F32 ? ssu::kDtF32 : 0) | (a->dt_softplus ? ssu::kSoftplus : 0) |
+              (a->disable_state_update ? ssu::kDisable : 0) | (r2d ? ssu::kRead2D : 0) |
+              (ri64 ? ssu::kReadI64 : 0) | (w2d ? ssu::kWrite2D : 0) |
+              (wi64 ? ssu::kWriteI64 : 0) | (cu_i64 ? ssu::kCuI64 : 0) |
+              (acc_i64 ? ssu::kAccI64 : 0);
+
+    const int e = ssu::launch(k, p, static_cast<unsigned>(grid), static_cast<unsigned>(geo.block),
+                              stream);
+    if (e != 0)
+        return fail(SSU_ERR_HIP, "kernel launch failed: %s", ssu::hip_error_string(e));
+    g_error.clear();
+    return SSU_OK;
+}
+
+}  // extern "C"

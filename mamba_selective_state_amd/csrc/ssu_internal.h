@@ -1,0 +1,101 @@
+// Internal interface between the host entry points (ssu_api.cpp) and the
+// gfx950 kernels (ssu_kernels.hip) of libssu.
+#pragma once
+
+#include <stdint.h>
+
+namespace ssu {
+
+// How rows are grouped into sequences.
+enum Layout : int32_t {
+    kOneToken = 0,  // x [batch, heads, dim]: sequence b is row b
+    kDense = 1,     // x [batch, steps, heads, dim]: sequence b is rows b*steps ..
+    kCuSeqlens = 2  // x [rows, heads, dim] split by cu_seqlens
+};
+
+enum Flags : int32_t {
+    kDtF32 = 1 << 0,     // dt is f32 (else the x dtype)
+    kSoftplus = 1 << 1,  // dt' = softplus(dt + dt_bias)
+    kDisable = 1 << 2,   // disable_state_update
+    kRead2D = 1 << 3,    // read table is 2-D (else 1-D, row-indexed)
+    kReadI64 = 1 << 4,
+    kWrite2D = 1 << 5,
+    kWriteI64 = 1 << 6,
+    kCuI64 = 1 << 7,
+    kAccI64 = 1 << 8
+};
+
+// Geometry of one workgroup: 16 lanes share a dim row (one DPP row), so a
+// 64-lane wave covers 4 dim rows per pass; each lane keeps dstate/16 state
+// elements of each of its rows in registers.
+constexpr int kWaveLanes = 64;
+constexpr int kLanesPerRow = 16;
+constexpr int kRowsPerPass = kWaveLanes / kLanesPerRow;
+constexpr int kMaxWaves = 4;
+
+// Passes (dim rows per lane) for a given dstate: 4, or 2 at dstate 256 to
+// bound the registers a lane holds (passes * dstate / 16 fp32 values).
+constexpr int passes_for(int dstate) { return dstate >= 256 ? 2 : 4; }
+
+// Kernel arguments. Strides are in elements. The pool is contiguous
+// [slots, heads, dim, dstate]; every other row tensor is addressed as
+// row * sr + head (or group) * sh + d (last stride 1, except dt's sp).
+struct Params {
+    void *state;
+    int64_t slot_stride;  // heads * dim * dstate
+    const void *x;
+    int64_t x_sr, x_sh;
+    const void *dt;
+    int64_t dt_sr, dt_sh, dt_sp;
+    const float *A;
+    int64_t A_sh;
+    const void *B;
+    int64_t B_sr, B_sg;
+    const void *C;
+    int64_t C_sr, C_sg;
+    const float *D;  // may be null
+    int64_t D_sh;
+    const void *z;   // may be null
+    int64_t z_sr, z_sh;
+    const float *dt_bias;  // may be null
+    int64_t bias_sh;
+    void *out;
+    int64_t out_sr, out_sh;
+    const void *rtab;  // may be null
+    int64_t r_s0, r_s1;
+    const void *wtab;  // may be null (then rtab, then the sequence index)
+    int64_t w_s0, w_s1;
+    const void *cu;    // kCuSeqlens only
+    int64_t cu_s;
+    const void *acc;   // may be null
+    int64_t acc_s;
+    int64_t pad;
+    int32_t nseq, H, P, heads_per_group;
+    int32_t steps;          // kDense: tokens per sequence
+    int32_t layout;         // Layout
+    int32_t dim_tiles;      // workgroups per (sequence, head)
+    int32_t rows_per_block; // dim rows per workgroup
+    int32_t flags;          // Flags
+};
+
+// Selected kernel variant for (state dtype, io dtype, dstate, multi-token).
+struct KernelRef {
+    const void *fn;
+};
+
+// Returns false if no variant exists for the combination.
+bool find_kernel(int state_dtype, int io_dtype, int dstate, bool multi, KernelRef *out);
+
+// "ssu_onetoken_<state>_<io>_n<dstate>" or "ssu_packed_...".
+void kernel_name(int state_dtype, int io_dtype, int dstate, bool multi, char *buf, int len);
+
+const char *hip_error_string(int e);
+
+// Launches `k` with `p`; returns the hipError_t value as int.
+int launch(const KernelRef &k, const Params &p, unsigned grid, unsigned block, void *stream);
+
+// Loads the kernel's code object on the current device and reports its
+// registers; returns the hipError_t value as int.
+int kernel_attributes(const KernelRef &k, int *vgprs, int *sgprs);
+
+}  // namespace ssu

@@ -1,0 +1,220 @@
+"""Python binding of libssu (include/ssu.h): argument marshalling only.
+
+Every step of the update runs in the library's gfx950 kernels; PyTorch only
+provides device memory and the current stream. The library must be built
+(mamba_selective_state_amd/build.py); importing this module without it raises.
+
+Low level, same names as the C ABI:  ssu_update, ssu_plan, ssu_last_error,
+ssu_abi_version (ssu_update takes an SsuArgs built by make_args).
+High level, same argument order and defaults as MATE's mate.mamba API (MATE
+docs, "Mamba / SSU", API reference): selective_state_update and
+prewarm_selective_state_update.
+"""
+import ctypes
+import os
+
+import torch
+
+from . import build as _build
+
+F32, F16, BF16, I32, I64 = 0, 1, 2, 3, 4
+OK, ERR_VALUE, ERR_NOT_IMPLEMENTED, ERR_HIP = 0, 1, 2, 3
+OPT_STATE_SCALE, OPT_INTERMEDIATE_STATES, OPT_RAND_SEED = 1, 2, 4
+OPT_CACHE_STEPS, OPT_ALGORITHM, OPT_BACKEND = 8, 16, 32
+
+_TORCH_DTYPES = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16,
+                 torch.int32: I32, torch.int64: I64}
+
+
+class SsuTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("size", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4)]
+
+
+class SsuArgs(ctypes.Structure):
+    _fields_ = [(n, SsuTensor) for n in
+                ("state", "x", "dt", "A", "B", "C", "D", "z", "dt_bias",
+                 "state_batch_indices", "dst_state_batch_indices", "cu_seqlens",
+                 "num_accepted_tokens", "out")] + [
+        ("dt_softplus", ctypes.c_int32), ("disable_state_update", ctypes.c_int32),
+        ("pad_slot_id", ctypes.c_int64), ("unsupported", ctypes.c_uint32)]
+
+
+class SsuPlanDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("state_dtype", "io_dtype", "dt_dtype", "slot_dtype", "meta_dtype", "heads",
+                 "dim", "dstate", "groups", "dt_dim", "packed")] + [("max_rows", ctypes.c_int64)]
+
+
+class SsuPlanInfo(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_char * 64), ("block_threads", ctypes.c_int32),
+                ("rows_per_block", ctypes.c_int32), ("blocks_per_seq_head", ctypes.c_int32),
+                ("vgprs", ctypes.c_int32), ("sgprs", ctypes.c_int32)]
+
+
+EXPORTS = ("ssu_plan", "ssu_update", "ssu_last_error", "ssu_abi_version")
+
+
+def load_library(path=None):
+    """Load libssu.so; raises if it has not been built."""
+    path = path or _build.LIB
+    if not os.path.exists(path):
+        raise ImportError("libssu.so is not built (run mamba_selective_state_amd/build.py): %s"
+                          % path)
+    lib = ctypes.CDLL(path)
+    lib.ssu_plan.argtypes = [ctypes.POINTER(SsuPlanDesc), ctypes.POINTER(SsuPlanInfo)]
+    lib.ssu_plan.restype = ctypes.c_int
+    lib.ssu_update.argtypes = [ctypes.POINTER(SsuArgs), ctypes.c_void_p]
+    lib.ssu_update.restype = ctypes.c_int
+    lib.ssu_last_error.argtypes = []
+    lib.ssu_last_error.restype = ctypes.c_char_p
+    lib.ssu_abi_version.argtypes = []
+    lib.ssu_abi_version.restype = ctypes.c_int
+    return lib
+
+
+_lib = load_library()
+LIBRARY_PATH = _build.LIB
+
+
+class SsuError(RuntimeError):
+    pass
+
+
+def _raise(status, what):
+    msg = "%s: %s" % (what, ssu_last_error())
+    if status == ERR_VALUE:
+        raise ValueError(msg)
+    if status == ERR_NOT_IMPLEMENTED:
+        raise NotImplementedError(msg)
+    raise SsuError(msg)
+
+
+def ssu_abi_version():
+    return _lib.ssu_abi_version()
+
+
+def ssu_last_error():
+    return _lib.ssu_last_error().decode()
+
+
+def ssu_update(args, stream=None):
+    """Enqueue one update (include/ssu.h ssu_update) on `stream` (a HIP stream
+    handle as int, or None for torch's current stream)."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    st = _lib.ssu_update(ctypes.byref(args), ctypes.c_void_p(stream))
+    if st != OK:
+        _raise(st, "ssu_update")
+
+
+def ssu_plan(desc):
+    """Validate and load one configuration (include/ssu.h ssu_plan); returns
+    the selection as a dict."""
+    info = SsuPlanInfo()
+    st = _lib.ssu_plan(ctypes.byref(desc), ctypes.byref(info))
+    if st != OK:
+        _raise(st, "ssu_plan")
+    return {"kernel": info.kernel.decode(), "block_threads": info.block_threads,
+            "rows_per_block": info.rows_per_block,
+            "blocks_per_seq_head": info.blocks_per_seq_head, "vgprs": info.vgprs}
+
+
+def tensor_desc(t, device=None):
+    """SsuTensor describing a torch tensor (None -> absent)."""
+    d = SsuTensor()
+    if t is None:
+        return d
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor, got %r" % type(t))
+    if t.dtype not in _TORCH_DTYPES:
+        raise ValueError("unsupported dtype %s" % t.dtype)
+    if t.dim() > 4:
+        raise ValueError("tensors have at most 4 dimensions")
+    if not t.is_cuda or (device is not None and t.device != device):
+        raise ValueError("every tensor must live on the state's GPU (%s), got %s"
+                         % (device, t.device))
+    d.data = t.data_ptr() if t.numel() > 0 else (t.data_ptr() or 16)
+    d.dtype = _TORCH_DTYPES[t.dtype]
+    d.ndim = t.dim()
+    for i, (s, st) in enumerate(zip(t.shape, t.stride())):
+        d.size[i] = s
+        d.stride[i] = st
+    return d
+
+
+def make_args(state, x, dt, A, B, C, D=None, z=None, dt_bias=None, dt_softplus=False,
+              state_batch_indices=None, pad_slot_id=-1, out=None, disable_state_update=False,
+              dst_state_batch_indices=None, cu_seqlens=None, num_accepted_tokens=None,
+              unsupported=0):
+    """SsuArgs for ssu_update; `out` must be given."""
+    dev = state.device
+    a = SsuArgs()
+    for name, t in (("state", state), ("x", x), ("dt", dt), ("A", A), ("B", B), ("C", C),
+                    ("D", D), ("z", z), ("dt_bias", dt_bias),
+                    ("state_batch_indices", state_batch_indices),
+                    ("dst_state_batch_indices", dst_state_batch_indices),
+                    ("cu_seqlens", cu_seqlens), ("num_accepted_tokens", num_accepted_tokens),
+                    ("out", out)):
+        setattr(a, name, tensor_desc(t, dev))
+    a.dt_softplus = int(bool(dt_softplus))
+    a.disable_state_update = int(bool(disable_state_update))
+    a.pad_slot_id = int(pad_slot_id)
+    a.unsupported = int(unsupported)
+    return a
+
+
+def selective_state_update(state, x, dt, A, B, C, D, z=None, dt_bias=None, dt_softplus=False,
+                           state_batch_indices=None, pad_slot_id=-1, state_scale=None, out=None,
+                           disable_state_update=False, intermediate_states_buffer=None,
+                           intermediate_state_indices=None, intermediate_state_scales=None,
+                           rand_seed=None, philox_rounds=10, cache_steps=0, algorithm="auto",
+                           dst_state_batch_indices=None, cu_seqlens=None,
+                           num_accepted_tokens=None, backend="auto"):
+    """Apply one decode step of the selective state update and return y.
+
+    Same arguments, order and defaults as MATE's selective_state_update (MATE
+    docs, "Mamba / SSU", API reference); the call shape decides the kernel.
+    Options the library does not implement raise NotImplementedError.
+    """
+    unsupported = 0
+    if state_scale is not None:
+        unsupported |= OPT_STATE_SCALE
+    if (intermediate_states_buffer is not None or intermediate_state_indices is not None
+            or intermediate_state_scales is not None):
+        unsupported |= OPT_INTERMEDIATE_STATES
+    if rand_seed is not None:
+        unsupported |= OPT_RAND_SEED
+    if cache_steps:
+        unsupported |= OPT_CACHE_STEPS
+    if algorithm != "auto":
+        unsupported |= OPT_ALGORITHM
+    if backend != "auto":
+        unsupported |= OPT_BACKEND
+    if out is None and not unsupported:
+        out = torch.empty(x.shape, dtype=x.dtype, device=x.device)
+    args = make_args(state, x, dt, A, B, C, D, z, dt_bias, dt_softplus, state_batch_indices,
+                     pad_slot_id, out, disable_state_update, dst_state_batch_indices, cu_seqlens,
+                     num_accepted_tokens, unsupported)
+    ssu_update(args, torch.cuda.current_stream(state.device).cuda_stream)
+    return out
+
+
+def prewarm_selective_state_update(*, state_dtype, io_dtype, batch, heads, dim, dstate, groups,
+                                   slot_dtype, rows_per_cta=4, lanes_per_row=32, packed=False,
+                                   meta_dtype=torch.int32, dt_dim=None, dt_dtype=None):
+    """Validate and load the kernel one configuration uses, before any graph
+    capture (MATE prewarm_selective_state_update; rows_per_cta and
+    lanes_per_row are accepted and ignored: the gfx950 kernels fix their own
+    tiling). Returns the selection."""
+    desc = SsuPlanDesc()
+    desc.state_dtype = _TORCH_DTYPES[state_dtype]
+    desc.io_dtype = _TORCH_DTYPES[io_dtype]
+    desc.dt_dtype = _TORCH_DTYPES[dt_dtype] if dt_dtype is not None else desc.io_dtype
+    desc.slot_dtype = _TORCH_DTYPES[slot_dtype]
+    desc.meta_dtype = _TORCH_DTYPES[meta_dtype]
+    desc.heads, desc.dim, desc.dstate, desc.groups = heads, dim, dstate, groups
+    desc.dt_dim = dim if dt_dim is None else dt_dim
+    desc.packed = int(bool(packed))
+    desc.max_rows = batch
+    return ssu_plan(desc)

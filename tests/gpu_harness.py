@@ -1,0 +1,229 @@
+"""Runs a workload case (numpy, the format of oracle/ssu_oracle.py) through
+the GPU library and compares it with the oracle.
+
+Comparison (the snapshot method of the vLLM PR #50729 digest, section
+"测试配套": expected values come from the untouched input, never from a second
+implementation that could share a bug):
+  - every slot the oracle does not write is byte-identical to the input pool;
+  - written slots: fp32 state max abs error <= 1e-5; 16-bit state max abs
+    error <= 2e-2 * max|ref|;
+  - y: 16-bit max abs error <= 2e-2 * max|ref|; fp32 y <= 1e-5 * max(1, max|ref|)
+    (a dstate-long fp32 dot product in another summation order);
+  - every row of y is written (out starts as NaN).
+"""
+import sys
+
+import numpy as np
+import torch
+
+import workloads as W
+from oracle import brute64, ssu_oracle
+import mamba_selective_state_amd as ssu
+
+TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a, dtype, device):
+    a = np.ascontiguousarray(a)
+    if dtype == "f32":
+        return torch.from_numpy(a).to(device)
+    return torch.from_numpy(a.view(np.int16)).to(device).view(TORCH[dtype])
+
+
+def dev_index(t, device):
+    if t is None:
+        return None
+    if isinstance(t, W.Strided):
+        base = torch.from_numpy(np.ascontiguousarray(t.base)).to(device)
+        return torch.as_strided(base, t.shape, t.strides)
+    return torch.from_numpy(np.ascontiguousarray(t)).to(device)
+
+
+def host(t, dtype):
+    t = t.detach().cpu().contiguous()
+    if dtype == "f32":
+        return t.numpy()
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def device_case(case, device="cuda:0"):
+    sd, io = case["state_dtype"], case["io_dtype"]
+    dtd = case.get("dt_dtype", io)
+    d = {"state": dev(case["state"], sd, device), "x": dev(case["x"], io, device),
+         "dt": dev(case["dt"], dtd, device), "A": torch.from_numpy(case["A"]).to(device),
+         "B": dev(case["B"], io, device), "C": dev(case["C"], io, device)}
+    for k in ("D", "dt_bias"):
+        d[k] = None if case.get(k) is None else torch.from_numpy(case[k]).to(device)
+    d["z"] = None if case.get("z") is None else dev(case["z"], io, device)
+    for k in ("state_batch_indices", "dst_state_batch_indices", "cu_seqlens",
+              "num_accepted_tokens"):
+        d[k] = dev_index(case.get(k), device)
+    return d
+
+
+def run_gpu(case, device="cuda:0", d=None, out=True, sync=True):
+    """One call through the Python binding; returns (y, state) on the host
+    (or the device tensors when sync is False)."""
+    if d is None:
+        d = device_case(case, device)
+    o = None
+    if out:
+        o = torch.full(np.shape(case["x"]), float("nan"), dtype=TORCH[case["io_dtype"]],
+                       device=device)
+    y = ssu.selective_state_update(
+        d["state"], d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], z=d["z"],
+        dt_bias=d["dt_bias"], dt_softplus=case.get("dt_softplus", False),
+        state_batch_indices=d["state_batch_indices"], pad_slot_id=case.get("pad_slot_id", -1),
+        out=o, disable_state_update=case.get("disable_state_update", False),
+        dst_state_batch_indices=d["dst_state_batch_indices"], cu_seqlens=d["cu_seqlens"],
+        num_accepted_tokens=d["num_accepted_tokens"])
+    if out:
+        assert y is o
+    if not sync:
+        return y, d
+    torch.cuda.synchronize()
+    return host(y, case["io_dtype"]), host(d["state"], case["state_dtype"])
+
+
+def tol_state(sd, ref):
+    if sd == "f32":
+        return 1e-5
+    return 2e-2 * max(float(np.abs(ref).max()), 1e-30)
+
+
+def tol_y(io, ref):
+    m = float(np.abs(ref).max()) if ref.size else 0.0
+    if io == "f32":
+        return 1e-5 * max(1.0, m)
+    return 2e-2 * max(m, 1e-30)
+
+
+def compare(case, y, state, ref, name=""):
+    """Asserts the GPU result (y, state) matches the oracle's `ref`; returns
+    the largest errors."""
+    sd, io = case["state_dtype"], case["io_dtype"]
+    written = ref["written"]
+    assert np.array_equal(state[~written], case["state"][~written]), \
+        "%s: a slot the oracle leaves alone changed" % name
+    stats = {}
+    if written.any():
+        g = brute64.to_f64(state[written], sd)
+        r = brute64.to_f64(ref["state"][written], sd)
+        err = float(np.abs(g - r).max())
+        stats["state_err"], stats["state_tol"] = err, tol_state(sd, r)
+        assert err <= stats["state_tol"], "%s: state error %g > %g" % (name, err, stats["state_tol"])
+    if np.size(y):
+        gy = brute64.to_f64(y, io)
+        ry = brute64.to_f64(ref["y"], io)
+        assert not np.isnan(gy).any(), "%s: a row of y was not written" % name
+        err = float(np.abs(gy - ry).max())
+        stats["y_err"], stats["y_tol"] = err, tol_y(io, ry)
+        assert err <= stats["y_tol"], "%s: y error %g > %g" % (name, err, stats["y_tol"])
+    return stats
+
+
+def check(case, name, device="cuda:0"):
+    """Oracle first (it also refuses out-of-range or aliased slots, so no
+    such input reaches the GPU), then the GPU, then the comparison."""
+    ref = ssu_oracle.run(case)
+    say("[gpu] %s: launching" % name)
+    y, state = run_gpu(case, device)
+    stats = compare(case, y, state, ref, name)
+    say("[gpu] %s: ok %s" % (name, {k: "%.3g" % v for k, v in stats.items()}))
+    return stats
+
+
+# ---------------------------------------------------------------- sampling
+
+def seq_spans(case):
+    """[(first row, length)] per sequence."""
+    x = np.asarray(case["x"])
+    cu = case.get("cu_seqlens")
+    if cu is not None:
+        cu = np.asarray(cu, np.int64)
+        return [(int(cu[i]), int(cu[i + 1] - cu[i])) for i in range(cu.size - 1)]
+    if x.ndim == 4:
+        return [(b * x.shape[1], x.shape[1]) for b in range(x.shape[0])]
+    return [(r, 1) for r in range(x.shape[0])]
+
+
+def written_slots(case):
+    """The oracle's written-slot mask for a case, computed on a copy shrunk to
+    one head, one dim row and dstate 16 (slot rules do not depend on them)."""
+    x = np.asarray(case["x"])
+    slots = np.shape(case["state"])[0]
+    lead = x.shape[:-2]
+    per_head = np.ndim(case["dt"]) == x.ndim - 1
+    shadow = dict(case)
+    shadow.update(
+        state=np.zeros((slots, 1, 1, 16), np.float32), state_dtype="f32", io_dtype="f32",
+        dt_dtype="f32", x=np.zeros(lead + (1, 1), np.float32),
+        dt=np.zeros(lead + ((1,) if per_head else (1, 1)), np.float32),
+        A=np.zeros(1, np.float32), B=np.zeros(lead + (1, 16), np.float32),
+        C=np.zeros(lead + (1, 16), np.float32), z=None, D=None, dt_bias=None)
+    return ssu_oracle.run(shadow)["written"]
+
+
+def subcase(case, seqs):
+    """The case restricted to sequences `seqs`, with a compact pool. Returns
+    (sub, rows, slots): the original rows and slots of the sub-case's rows and
+    pool entries. The pad id becomes -1 in the sub-case."""
+    x = np.asarray(case["x"])
+    dense = x.ndim == 4
+    spans = seq_spans(case)
+    rows = np.concatenate([np.arange(spans[b][0], spans[b][0] + spans[b][1]) for b in seqs]
+                          ).astype(np.int64) if len(seqs) else np.zeros(0, np.int64)
+    lens = np.array([spans[b][1] for b in seqs], np.int64)
+    pad = int(case.get("pad_slot_id", -1))
+
+    def rowsel(a):
+        a = np.asarray(a)
+        if dense:
+            return a[np.asarray(seqs)]
+        return a[rows]
+
+    sub = dict(case)
+    for k in ("x", "dt", "B", "C", "z"):
+        if case.get(k) is not None:
+            sub[k] = rowsel(case[k])
+    if case.get("cu_seqlens") is not None:
+        sub["cu_seqlens"] = np.concatenate([[0], np.cumsum(lens)]).astype(
+            np.asarray(case["cu_seqlens"]).dtype)
+    if case.get("num_accepted_tokens") is not None:
+        sub["num_accepted_tokens"] = np.asarray(case["num_accepted_tokens"])[np.asarray(seqs)]
+    tabs = {}
+    for k in ("state_batch_indices", "dst_state_batch_indices"):
+        t = case.get(k)
+        if t is None:
+            tabs[k] = None
+            continue
+        t = np.asarray(t)
+        if t.ndim == 1:
+            tabs[k] = t[rows] if not dense else t.reshape(x.shape[0], -1)[seqs].ravel()
+        else:
+            tabs[k] = t[np.asarray(seqs)]
+    if tabs["state_batch_indices"] is None:
+        # without tables the slot is the sequence index: make it explicit
+        base = np.asarray(seqs, np.int64)
+        if dense or case.get("cu_seqlens") is not None:
+            tabs["state_batch_indices"] = np.repeat(base[:, None], int(max(lens.max(), 1)),
+                                                    axis=1) if len(seqs) else base[:, None]
+        else:
+            tabs["state_batch_indices"] = base
+    used = np.concatenate([np.asarray(v).ravel() for v in tabs.values() if v is not None])
+    used = np.unique(used[used != pad])
+    remap = {int(s): i for i, s in enumerate(used)}
+    for k, t in tabs.items():
+        if t is None:
+            sub[k] = None
+            continue
+        m = np.vectorize(lambda s: -1 if s == pad else remap[int(s)], otypes=[np.int64])(t)
+        sub[k] = m.astype(np.asarray(t).dtype if np.asarray(t).dtype != np.uint64 else np.int64)
+    sub["pad_slot_id"] = -1
+    sub["state"] = np.asarray(case["state"])[used]
+    return sub, rows, used

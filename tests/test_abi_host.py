@@ -1,0 +1,299 @@
+"""C-ABI host logic on the CPU: the library loads, exports what include/ssu.h
+declares, and rejects every malformed call before any device work. The
+pointers below are fake (never dereferenced: validation only looks at shapes,
+strides, dtypes and alignment), and no valid call is made without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mamba_selective_state_amd import ssu as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssu.h")
+FAKE = 0x7F0000000000  # 16-byte aligned, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"SSU_API\s+[\w\s\*]*?\b(ssu_\w+)\s*\(", text)))
+
+
+def test_exports_match_header():
+    names = declared_functions()
+    assert names == sorted(S.EXPORTS)
+    lib = ctypes.CDLL(S.LIBRARY_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version():
+    text = open(HEADER).read()
+    v = int(re.search(r"#define SSU_ABI_VERSION (\d+)", text).group(1))
+    assert S.ssu_abi_version() == v
+
+
+def test_struct_layout_matches_header(tmp_path):
+    """Field offsets and sizes of the ctypes mirrors equal what a C compiler
+    makes of include/ssu.h."""
+    structs = {"ssu_tensor_t": S.SsuTensor, "ssu_args_t": S.SsuArgs,
+               "ssu_plan_desc_t": S.SsuPlanDesc, "ssu_plan_info_t": S.SsuPlanInfo}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ssu.h"', "int main(void) {"]
+    for cname, cls in structs.items():
+        lines.append('printf("%s SIZEOF %%zu\\n", sizeof(%s));' % (cname, cname))
+        for f, _ in cls._fields_:
+            lines.append('printf("%s %s %%zu\\n", offsetof(%s, %s));' % (cname, f, cname, f))
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    import subprocess
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), "-o", str(exe), str(src)],
+                   check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    got = {}
+    for line in out:
+        if line:
+            k1, k2, v = line.split()
+            got[(k1, k2)] = int(v)
+    for cname, cls in structs.items():
+        assert got[(cname, "SIZEOF")] == ctypes.sizeof(cls), cname
+        for f, _ in cls._fields_:
+            assert got[(cname, f)] == getattr(cls, f).offset, (cname, f)
+
+
+def tdesc(shape, dtype, strides=None, ptr=FAKE):
+    t = S.SsuTensor()
+    t.data = ptr
+    t.dtype = dtype
+    t.ndim = len(shape)
+    if strides is None:
+        strides, acc = [], 1
+        for s in reversed(shape):
+            strides.insert(0, acc)
+            acc *= s
+    for i, (s, st) in enumerate(zip(shape, strides)):
+        t.size[i] = s
+        t.stride[i] = st
+    return t
+
+
+def base_args(rows=4, H=8, P=16, N=128, G=2, slots=8, sd=S.F32, io=S.BF16):
+    a = S.SsuArgs()
+    a.state = tdesc((slots, H, P, N), sd)
+    a.x = tdesc((rows, H, P), io)
+    a.dt = tdesc((rows, H, P), io)
+    a.A = tdesc((H,), S.F32)
+    a.B = tdesc((rows, G, N), io)
+    a.C = tdesc((rows, G, N), io)
+    a.out = tdesc((rows, H, P), io)
+    a.pad_slot_id = -1
+    return a
+
+
+def update(a):
+    st = S._lib.ssu_update(ctypes.byref(a), None)
+    return st, S.ssu_last_error()
+
+
+
+
+def expect(a, status, words):
+    st, msg = update(a)
+    assert st == status, (st, msg)
+    for w in words:
+        assert w in msg, (w, msg)
+
+
+def test_empty_batch_is_ok_without_launch():
+    a = base_args(rows=0)
+    assert update(a) == (S.OK, "")
+
+
+def test_no_sequences_is_ok_without_launch():
+    a = base_args(rows=0)
+    a.cu_seqlens = tdesc((1,), S.I32)
+    assert update(a)[0] == S.OK
+
+
+def test_null_args():
+    assert S._lib.ssu_update(None, None) == S.ERR_VALUE
+    assert "NULL" in S.ssu_last_error()
+
+
+@pytest.mark.parametrize("bit,word", [(S.OPT_STATE_SCALE, "state_scale"),
+                                      (S.OPT_INTERMEDIATE_STATES, "intermediate"),
+                                      (S.OPT_RAND_SEED, "rand_seed"),
+                                      (S.OPT_CACHE_STEPS, "cache_steps"),
+                                      (S.OPT_ALGORITHM, "algorithm"),
+                                      (S.OPT_BACKEND, "backend")])
+def test_unsupported_options(bit, word):
+    a = base_args(rows=0)
+    a.unsupported = bit
+    expect(a, S.ERR_NOT_IMPLEMENTED, [word])
+
+
+def test_state_errors():
+    a = base_args(rows=0)
+    a.state = S.SsuTensor()
+    expect(a, S.ERR_VALUE, ["state is required"])
+    a = base_args(rows=0)
+    a.state = tdesc((8, 8, 16, 128), S.I32)
+    expect(a, S.ERR_VALUE, ["state must be f32"])
+    a = base_args(rows=0)
+    a.state = tdesc((8, 8, 16, 128), S.F32, strides=(8 * 16 * 128, 16 * 128, 1, 16))
+    expect(a, S.ERR_VALUE, ["contiguous"])
+    a = base_args(rows=0)
+    a.state = tdesc((8, 8, 16, 128), S.F32, ptr=FAKE + 4)
+    expect(a, S.ERR_VALUE, ["16-byte"])
+    a = base_args(rows=0, N=96)
+    expect(a, S.ERR_NOT_IMPLEMENTED, ["dstate 96"])
+    a = base_args(rows=0)
+    a.state = tdesc((8, 8, 16), S.F32)
+    expect(a, S.ERR_VALUE, ["[slots, heads, dim, dstate]"])
+
+
+def test_x_errors():
+    a = base_args(rows=0)
+    a.x = tdesc((0, 8, 16, 1), S.BF16)
+    a.x.ndim = 5
+    expect(a, S.ERR_VALUE, ["x must be"])
+    a = base_args(rows=0)
+    a.x = tdesc((0, 128), S.BF16)
+    expect(a, S.ERR_VALUE, ["x must be"])
+    a = base_args(rows=0)
+    a.x = tdesc((0, 4, 16), S.BF16)
+    expect(a, S.ERR_VALUE, ["x axis 1"])
+    a = base_args(rows=0)
+    a.x = tdesc((0, 8, 16), S.BF16, strides=(256, 16, 2))
+    expect(a, S.ERR_VALUE, ["unit stride"])
+    a = base_args(rows=0)
+    a.x = tdesc((0, 8, 16), S.I64)
+    expect(a, S.ERR_VALUE, ["x must be f32"])
+
+
+def test_dense_form_must_collapse_to_rows():
+    a = base_args(rows=0)
+    a.x = tdesc((2, 3, 8, 16), S.BF16, strides=(1000, 128, 16, 1))
+    expect(a, S.ERR_NOT_IMPLEMENTED, ["batch stride"])
+
+
+def test_dt_errors():
+    a = base_args(rows=0)
+    a.dt = tdesc((0, 8, 16), S.F16)
+    expect(a, S.ERR_VALUE, ["dt must be f32 or the x dtype"])
+    a = base_args(rows=0)
+    a.dt = tdesc((0,), S.F32)
+    expect(a, S.ERR_VALUE, ["dt must be shaped like x"])
+    a = base_args(rows=0)
+    a.dt = S.SsuTensor()
+    expect(a, S.ERR_VALUE, ["dt is required"])
+
+
+def test_head_vector_errors():
+    a = base_args(rows=0)
+    a.A = tdesc((4,), S.F32)
+    expect(a, S.ERR_VALUE, ["A must be [heads]"])
+    a = base_args(rows=0)
+    a.A = tdesc((8,), S.BF16)
+    expect(a, S.ERR_VALUE, ["A must be f32"])
+    a = base_args(rows=0)
+    a.D = tdesc((8, 16), S.F32)
+    expect(a, S.ERR_VALUE, ["D must be per head"])
+    a = base_args(rows=0)
+    a.dt_bias = tdesc((7,), S.F32)
+    expect(a, S.ERR_VALUE, ["dt_bias must be [heads]"])
+    a = base_args(rows=0)
+    a.A = tdesc((8, 16, 128), S.F32, strides=(1, 0, 0))  # broadcast view is fine
+    assert update(a)[0] == S.OK
+
+
+def test_groups_errors():
+    a = base_args(rows=0, G=3)
+    expect(a, S.ERR_VALUE, ["divisible by groups"])
+    a = base_args(rows=0)
+    a.B = tdesc((0, 2, 128), S.F16)
+    expect(a, S.ERR_VALUE, ["x dtype"])
+    a = base_args(rows=0)
+    a.C = tdesc((0, 2, 64), S.BF16)
+    expect(a, S.ERR_VALUE, ["C last axis"])
+    a = base_args(rows=0)
+    a.B = tdesc((0, 2, 128), S.BF16, ptr=FAKE + 2)
+    expect(a, S.ERR_VALUE, ["byte boundaries"])
+    a = base_args(rows=0)
+    a.B = tdesc((0, 2, 128), S.BF16, strides=(258, 129, 1))
+    expect(a, S.ERR_VALUE, ["byte boundaries"])
+
+
+def test_out_and_z_errors():
+    a = base_args(rows=0)
+    a.out = S.SsuTensor()
+    expect(a, S.ERR_VALUE, ["out is required"])
+    a = base_args(rows=0)
+    a.out = tdesc((0, 8, 16), S.F32)
+    expect(a, S.ERR_VALUE, ["out must have the x dtype"])
+    a = base_args(rows=0)
+    a.z = tdesc((0, 8, 8), S.BF16)
+    expect(a, S.ERR_VALUE, ["z last axis"])
+
+
+def test_table_errors():
+    a = base_args(rows=0)
+    a.state_batch_indices = tdesc((3,), S.I32)
+    expect(a, S.ERR_VALUE, ["one entry per row"])
+    a = base_args(rows=0)
+    a.state_batch_indices = tdesc((0,), S.F32)
+    expect(a, S.ERR_VALUE, ["i32 or i64"])
+    a = base_args(rows=0)
+    a.dst_state_batch_indices = tdesc((0, 1, 1), S.I64)
+    expect(a, S.ERR_VALUE, ["1-D [rows] or 2-D"])
+    a = base_args(rows=0)
+    a.x = tdesc((2, 3, 8, 16), S.BF16)
+    a.dt = tdesc((2, 3, 8, 16), S.BF16)
+    a.B = tdesc((2, 3, 2, 128), S.BF16)
+    a.C = tdesc((2, 3, 2, 128), S.BF16)
+    a.out = tdesc((2, 3, 8, 16), S.BF16)
+    a.state_batch_indices = tdesc((2, 2), S.I32)
+    expect(a, S.ERR_VALUE, ["columns"])
+
+
+def test_meta_errors():
+    a = base_args(rows=0)
+    a.cu_seqlens = tdesc((2, 2), S.I32)
+    expect(a, S.ERR_VALUE, ["cu_seqlens must be 1-D"])
+    a = base_args(rows=0)
+    a.cu_seqlens = tdesc((3,), S.I32)
+    a.num_accepted_tokens = tdesc((3,), S.I32)
+    expect(a, S.ERR_VALUE, ["num_accepted_tokens"])
+    a = base_args(rows=0)
+    a.x = tdesc((1, 1, 8, 16), S.BF16)
+    a.cu_seqlens = tdesc((2,), S.I32)
+    expect(a, S.ERR_VALUE, ["cu_seqlens goes with"])
+
+
+def test_plan_validation():
+    def plan(**kw):
+        d = S.SsuPlanDesc()
+        base = dict(state_dtype=S.F32, io_dtype=S.BF16, dt_dtype=S.BF16, slot_dtype=S.I32,
+                    meta_dtype=S.I32, heads=8, dim=64, dstate=128, groups=2, dt_dim=64, packed=0)
+        base.update(kw)
+        for k, v in base.items():
+            setattr(d, k, v)
+        info = S.SsuPlanInfo()
+        return S._lib.ssu_plan(ctypes.byref(d), ctypes.byref(info)), S.ssu_last_error()
+
+    assert plan(groups=3)[0] == S.ERR_VALUE
+    assert plan(dstate=48)[0] == S.ERR_NOT_IMPLEMENTED
+    assert plan(dt_dtype=S.F16)[0] == S.ERR_VALUE
+    assert plan(dt_dim=7)[0] == S.ERR_VALUE
+    assert plan(slot_dtype=S.F32)[0] == S.ERR_VALUE
+    assert plan(state_dtype=S.I32)[0] == S.ERR_VALUE
+    assert S._lib.ssu_plan(None, None) == S.ERR_VALUE
+
+
+def test_python_wrapper_rejects_cpu_tensors():
+    import torch
+    t = torch.zeros(2, 2, 2, 16)
+    with pytest.raises(ValueError, match="GPU"):
+        S.tensor_desc(t, torch.device("cuda", 0))

@@ -1,0 +1,282 @@
+"""GPU path against the CPU oracle, element by element, through the C ABI
+(the Python binding only marshals arguments).
+
+Small cases (the oracle runs whole) span several workgroup tiles and ragged
+dim tails; the workloads' full sizes run in the benchmark's launch
+configuration and are checked on sampled sequences plus the whole pool's
+untouched slots."""
+import numpy as np
+import pytest
+import torch
+
+import gpu_harness as G
+import workloads as W
+from oracle import ssu_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    torch.cuda.init()
+
+
+# ---------------------------------------------------------------- small cases
+
+def test_one_token_tiny_chained():
+    """The MATE minimal example: a call without tables, then a call with
+    tables [0, 1], on the pool the first call left."""
+    c0 = W.one_token_tiny(tables=False)
+    c1 = W.one_token_tiny(tables=True)
+    ref0 = ssu_oracle.run(c0)
+    ref1 = ssu_oracle.run(dict(c1, state=ref0["state"]))
+    G.say("[gpu] one_token_tiny: launching two calls")
+    d = G.device_case(c0)
+    y0, _ = G.run_gpu(c0, d=d, sync=True)
+    d1 = dict(d)
+    d1["state_batch_indices"] = G.dev_index(c1["state_batch_indices"], "cuda:0")
+    d1["dst_state_batch_indices"] = G.dev_index(c1["dst_state_batch_indices"], "cuda:0")
+    y1, s1 = G.run_gpu(c1, d=d1)
+    G.compare(c0, y0, ref0["state"], ref0, "call 0 y")
+    G.compare(dict(c1, state=ref0["state"]), y1, s1, ref1, "call 1")
+
+
+DECODE = [
+    # (state, io, dstate, dim, index dtype, dt dtype)
+    ("f32", "bf16", 128, 64, np.int32, "io"),
+    ("f32", "bf16", 128, 40, np.int64, "io"),
+    ("f32", "f16", 128, 64, np.int32, "f32"),
+    ("f32", "f32", 128, 20, np.int32, "f32"),
+    ("bf16", "bf16", 128, 64, np.int32, "io"),
+    ("f16", "bf16", 128, 36, np.int64, "io"),
+    ("f32", "bf16", 16, 64, np.int32, "io"),
+    ("bf16", "bf16", 16, 24, np.int32, "io"),
+    ("f32", "bf16", 32, 64, np.int32, "io"),
+    ("f16", "f16", 32, 64, np.int32, "io"),
+    ("f32", "bf16", 64, 64, np.int32, "io"),
+    ("bf16", "f16", 64, 72, np.int32, "io"),
+    ("f32", "bf16", 256, 64, np.int32, "io"),
+    ("bf16", "bf16", 256, 40, np.int64, "f32"),
+]
+
+
+@pytest.mark.parametrize("sd,io,N,P,idx,dtd", DECODE,
+                         ids=["%s-%s-n%d-p%d-%s-dt%s" % (a, b, c, d, np.dtype(e).name, f)
+                              for a, b, c, d, e, f in DECODE])
+def test_decode(sd, io, N, P, idx, dtd):
+    c = W.decode(seed=100 + N + P, batch=24, heads=16, dim=P, dstate=N, groups=4, slots=48,
+                 state_dtype=sd, io=io, index_dtype=idx)
+    if dtd == "f32":
+        c["dt"] = W.to_storage(np.random.default_rng(5).standard_normal(c["x"].shape,
+                                                                         dtype=np.float32), "f32")
+        c["dt_dtype"] = "f32"
+    G.check(c, "decode %s %s n%d p%d" % (sd, io, N, P))
+
+
+@pytest.mark.parametrize("pad", [0, -1])
+@pytest.mark.parametrize("sd", ["bf16", "f32"])
+def test_decode_pad(sd, pad):
+    c = W.decode_pad(batch=40, heads=16, dim=64, dstate=128, groups=4, slots=96, state_dtype=sd,
+                     pad_frac=0.1, pad_slot_id=pad)
+    G.check(c, "decode_pad %s pad=%d" % (sd, pad))
+
+
+@pytest.mark.parametrize("pad", [0, -1])
+@pytest.mark.parametrize("sd", ["f32", "f16", "bf16"])
+def test_mtp(sd, pad):
+    c = W.mtp(nseq=6, steps=7, heads=16, dim=64, dstate=128, groups=4, state_dtype=sd,
+              pad_slot_id=pad, index_dtype=np.int64 if sd == "f16" else np.int32,
+              meta_dtype=np.int64 if sd == "bf16" else np.int32)
+    G.check(c, "mtp %s pad=%d" % (sd, pad))
+
+
+@pytest.mark.parametrize("mode", ["dst", "disable", "omitted"])
+def test_varlen(mode):
+    c = W.varlen(nseq=40, heads=8, dim=64, dstate=128, state_dtype="f16", dst=mode != "omitted",
+                 disable=mode == "disable")
+    assert (np.diff(c["cu_seqlens"]) == 0).any()
+    G.check(c, "varlen %s" % mode)
+
+
+def test_varlen_f32_ragged():
+    c = W.varlen(seed=9, nseq=30, heads=4, dim=28, dstate=64, groups=2, state_dtype="f32",
+                 io="f32")
+    G.check(c, "varlen f32 ragged")
+
+
+def test_dense_4d():
+    c = W.mtp(nseq=5, steps=3, heads=8, dim=64, dstate=128, groups=2, pad_slot_id=-1)
+    R = 15
+    for k in ("x", "dt", "B", "C", "z"):
+        c[k] = c[k].reshape((5, 3) + c[k].shape[1:])
+    c["cu_seqlens"] = None
+    assert c["x"].shape[0] * c["x"].shape[1] == R
+    G.check(c, "dense 4-D")
+    flat = dict(c, state_batch_indices=c["state_batch_indices"].ravel(),
+                dst_state_batch_indices=c["dst_state_batch_indices"].ravel())
+    G.check(flat, "dense 4-D, flat tables")
+
+
+def test_one_token_with_accepted():
+    """x [batch, heads, dim] with num_accepted_tokens and a 2-D read table:
+    the multi-token kernel with one token per sequence."""
+    c = W.mtp(nseq=12, steps=1, heads=8, dim=64, dstate=128, groups=2, pad_slot_id=-1)
+    rt = np.arange(12 * 3, dtype=np.int32).reshape(12, 3)
+    c["state"] = np.concatenate([c["state"], c["state"][:12 * 3 - 24]])  # 36 slots
+    c.update(state_batch_indices=rt, dst_state_batch_indices=None, cu_seqlens=None,
+             num_accepted_tokens=np.random.default_rng(3).integers(0, 4, 12).astype(np.int32))
+    G.check(c, "one token with accepted counts")
+
+
+def test_strided_literal_view():
+    """A [rows, 1] table view with strides (1, 1): sequence b, position t is
+    entry b + t (one sequence)."""
+    c = W.mtp(nseq=1, steps=6, heads=8, dim=64, dstate=128, groups=2, pad_slot_id=-1)
+    c["num_accepted_tokens"] = np.array([4], np.int32)
+    c["state_batch_indices"] = W.Strided(c["state_batch_indices"].ravel(), (6, 1), (1, 1))
+    c["dst_state_batch_indices"] = W.Strided(c["dst_state_batch_indices"].ravel(), (6, 1), (1, 1))
+    G.check(c, "strided literal view")
+
+
+def test_packed_without_tables():
+    """cu_seqlens without tables: sequence b reads and writes slot b."""
+    c = W.varlen(nseq=12, heads=8, dim=64, dstate=128, state_dtype="bf16")
+    c["state_batch_indices"] = c["dst_state_batch_indices"] = None
+    c["state"] = c["state"][:12]
+    G.check(c, "packed without tables")
+
+
+def test_per_head_dt_as_stride0_view():
+    c = W.varlen(nseq=10, heads=8, dim=64, dstate=128, state_dtype="f32")
+    ref = ssu_oracle.run(c)
+    d = G.device_case(c)
+    d["dt"] = d["dt"][:, :, None].expand(-1, -1, 64)  # stride 0 over dim
+    assert d["dt"].stride(2) == 0
+    G.say("[gpu] per-head dt stride-0 view: launching")
+    y, s = G.run_gpu(c, d=d)
+    G.compare(c, y, s, ref, "per-head dt view")
+
+
+def test_empty_inputs():
+    c = W.varlen(nseq=6, heads=4, dim=64, dstate=128, lengths=[0, 0, 0, 0, 0, 0])
+    assert c["x"].shape[0] == 0
+    G.say("[gpu] all-empty varlen: launching")
+    y, s = G.run_gpu(c)
+    assert y.shape[0] == 0 and np.array_equal(s, c["state"])
+    c = W.varlen(nseq=6, heads=4, dim=64, dstate=128, lengths=[0, 3, 0, 0, 1, 0])
+    G.check(c, "mostly empty varlen")
+    c = W.decode(batch=0, heads=4, dim=64, dstate=128, groups=2, slots=4)
+    y, s = G.run_gpu(c)
+    assert y.shape[0] == 0 and np.array_equal(s, c["state"])
+
+
+@pytest.mark.parametrize("kind", ["in_place_decode", "varlen_dst_omitted"])
+def test_alias_repeat10(kind):
+    """Read slot == write slot (in-place decode; a sequence writing the entry
+    it read): 10 repeats from the same snapshot give the oracle's result
+    every time (the repeat-10 snapshot method of the PR #50729 digest)."""
+    if kind == "in_place_decode":
+        c = W.decode(batch=64, heads=16, dim=64, dstate=128, groups=4, slots=96)
+    else:
+        c = W.varlen(nseq=48, heads=8, dim=64, dstate=128, dst=False)
+    ref = ssu_oracle.run(c)
+    d = G.device_case(c)
+    snap = d["state"].clone()
+    first = None
+    for i in range(10):
+        d["state"].copy_(snap)
+        y, s = G.run_gpu(c, d=d)
+        G.compare(c, y, s, ref, "%s repeat %d" % (kind, i))
+        if first is None:
+            first = (y.copy(), s.copy())
+        else:
+            assert np.array_equal(first[0], y) and np.array_equal(first[1], s)
+    G.say("[gpu] %s: 10 repeats identical" % kind)
+
+
+def test_prewarm_and_graph_replay():
+    """prewarm selects and loads the kernel; the update captured in a HIP
+    graph replays to the eager result (read and write slots differ, so each
+    replay computes the same thing)."""
+    info = G.ssu.prewarm_selective_state_update(
+        state_dtype=torch.float32, io_dtype=torch.bfloat16, batch=16, heads=8, dim=64,
+        dstate=128, groups=2, slot_dtype=torch.int32, packed=True)
+    assert info["kernel"] == "ssu_packed_f32_bf16_n128" and info["block_threads"] == 256
+    c = W.mtp(nseq=8, steps=4, heads=8, dim=64, dstate=128, groups=2, pad_slot_id=-1)
+    ref = ssu_oracle.run(c)
+    d = G.device_case(c)
+    snap = d["state"].clone()
+    out = torch.empty(c["x"].shape, dtype=torch.bfloat16, device="cuda:0")
+    stream = torch.cuda.Stream()
+    args = G.ssu.make_args(d["state"], d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"],
+                           d["z"], d["dt_bias"], True, d["state_batch_indices"], -1, out, False,
+                           d["dst_state_batch_indices"], d["cu_seqlens"],
+                           d["num_accepted_tokens"])
+    G.say("[gpu] graph capture: capturing")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        G.ssu.ssu_update(args, torch.cuda.current_stream().cuda_stream)
+    for i in range(3):
+        out.fill_(float("nan"))
+        d["state"].copy_(snap)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        G.compare(c, G.host(out, "bf16"), G.host(d["state"], "f32"), ref, "replay %d" % i)
+    G.say("[gpu] graph replay: ok")
+
+
+# ---------------------------------------------------------------- full sizes
+
+def _full(case, name, seqs):
+    """Full-size case in the benchmark's launch configuration: the whole pool's
+    untouched slots byte-identical, written slots changed, and sampled
+    sequences against the oracle."""
+    G.say("[gpu] %s: slot rules on the host" % name)
+    written = G.written_slots(case)
+    d = G.device_case(case)
+    snap = d["state"].clone()
+    G.say("[gpu] %s: launching" % name)
+    y, d = G.run_gpu(case, d=d, sync=False)
+    torch.cuda.synchronize()
+    idx_w = torch.from_numpy(np.flatnonzero(written)).to("cuda:0")
+    idx_u = torch.from_numpy(np.flatnonzero(~written)).to("cuda:0")
+    assert torch.equal(d["state"][idx_u], snap[idx_u]), "untouched slots changed"
+    if idx_w.numel():
+        flat_new = d["state"][idx_w].reshape(idx_w.numel(), -1)
+        flat_old = snap[idx_w].reshape(idx_w.numel(), -1)
+        assert bool((flat_new != flat_old).any(dim=1).all()), "a written slot did not change"
+    yh = G.host(y, case["io_dtype"])
+    assert not np.isnan(G.brute64.to_f64(yh, case["io_dtype"])).any()
+    sub, rows, slots = G.subcase(case, seqs)
+    ref = ssu_oracle.run(sub)
+    got_state = G.host(d["state"][torch.from_numpy(slots).to("cuda:0")], case["state_dtype"])
+    got_y = yh[rows] if np.ndim(case["x"]) == 3 else yh[np.asarray(seqs)]
+    stats = G.compare(sub, got_y, got_state, ref, name)
+    G.say("[gpu] %s: ok %s" % (name, {k: "%.3g" % v for k, v in stats.items()}))
+
+
+def test_full_decode():
+    c = W.decode()
+    _full(c, "decode batch 256 fp32 state", [0, 1, 77, 128, 200, 255])
+
+
+def test_full_decode_pad():
+    c = W.decode_pad()
+    pads = list(c["pad_rows"][:3])
+    _full(c, "decode_pad batch 1024 bf16 state", sorted(set(pads + [0, 511, 1023])))
+
+
+def test_full_mtp():
+    c = W.mtp()
+    _full(c, "mtp 64x7 fp32 state", [0, 1, 31, 63])
+
+
+@pytest.mark.parametrize("mode", ["dst", "disable", "omitted"])
+def test_full_varlen(mode):
+    c = W.varlen(dst=mode != "omitted", disable=mode == "disable")
+    lens = np.diff(c["cu_seqlens"])
+    seqs = sorted(set([int(np.argmax(lens)), int(np.argmin(lens)), 0, 255, 511]))
+    _full(c, "varlen 512 seqs fp16 state (%s)" % mode, seqs)

@@ -20,6 +20,9 @@ The shapes follow the pages' workloads:
                   groups 1, fp16 state, per-head dt, z gate and D
 Every builder takes keyword overrides so tests can shrink a workload.
 """
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -27,6 +30,7 @@ __all__ = ["to_storage", "one_token_tiny", "decode", "decode_pad", "mtp", "varle
            "Strided", "BUILDERS"]
 
 _CHUNK = 1 << 24
+_THREADS = min(16, os.cpu_count() or 1)
 
 
 class Strided:
@@ -54,25 +58,36 @@ def to_storage(a, dtype):
 
 
 def _normal(rng, shape, dtype):
-    """N(0,1) drawn in float32 chunks, stored in `dtype`."""
+    """N(0,1) stored in `dtype`. Chunk i is drawn from stream i spawned from
+    one seed taken off `rng`, so the values do not depend on how many threads
+    draw them."""
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.float32 if dtype == "f32" else np.uint16)
-    for i in range(0, n, _CHUNK):
+    starts = list(range(0, n, _CHUNK))
+    streams = np.random.SeedSequence(int(rng.integers(1 << 63))).spawn(len(starts))
+
+    def fill(k):
+        i = starts[k]
         m = min(_CHUNK, n - i)
-        out[i:i + m] = to_storage(rng.standard_normal(m, dtype=np.float32), dtype)
+        g = np.random.Generator(np.random.PCG64(streams[k]))
+        out[i:i + m] = to_storage(g.standard_normal(m, dtype=np.float32), dtype)
+
+    if len(starts) <= 1:
+        for k in range(len(starts)):
+            fill(k)
+    else:
+        with ThreadPoolExecutor(min(_THREADS, len(starts))) as ex:
+            list(ex.map(fill, range(len(starts))))
     return out.reshape(shape)
 
 
 def _pattern(shape, dtype):
-    """Deterministic filler for slots no row reads: the values (k % 251) / 64
-    for the flat element index k, so a stray store cannot go unnoticed."""
+    """Deterministic filler for slots no row reads: the values
+    ((k % 251) - 125) / 64 for the flat element index k, so a stray store
+    cannot go unnoticed. Built by tiling one period."""
     n = int(np.prod(shape))
-    out = np.empty(n, dtype=np.float32 if dtype == "f32" else np.uint16)
-    for i in range(0, n, _CHUNK):
-        m = min(_CHUNK, n - i)
-        vals = ((np.arange(i, i + m, dtype=np.int64) % 251).astype(np.float32) - 125.0) / 64.0
-        out[i:i + m] = to_storage(vals, dtype)
-    return out.reshape(shape)
+    period = to_storage((np.arange(251, dtype=np.float32) - 125.0) / 64.0, dtype)
+    return np.resize(period, n).reshape(shape)
 
 
 def _pool(rng, slots, H, P, N, dtype, live_slots=None):
