@@ -184,8 +184,9 @@ struct Geometry {
     int32_t block, rows_per_block, dim_tiles;
 };
 
-Geometry geometry(int64_t P, int64_t N) {
-    const int passes = ssu::passes_for(static_cast<int>(N));
+Geometry geometry(int64_t P, int64_t N, int state_dtype, bool multi) {
+    const int passes =
+        ssu::passes_for(static_cast<int>(N), static_cast<int>(elem_bytes(state_dtype)), multi);
     const int64_t rows_per_wave = ssu::kRowsPerPass * passes;
     int64_t waves = (P + rows_per_wave - 1) / rows_per_wave;
     if (waves > ssu::kMaxWaves)
@@ -254,7 +255,7 @@ ssu_status_t ssu_plan(const ssu_plan_desc_t *desc, ssu_plan_info_t *info) {
     if (e != 0)
         return fail(SSU_ERR_HIP, "loading the kernel failed: %s", ssu::hip_error_string(e));
     if (info) {
-        const Geometry g = geometry(desc->dim, desc->dstate);
+        const Geometry g = geometry(desc->dim, desc->dstate, desc->state_dtype, multi);
         memset(info, 0, sizeof *info);
         ssu::kernel_name(desc->state_dtype, desc->io_dtype, desc->dstate, multi, info->kernel,
                          sizeof info->kernel);
@@ -450,7 +451,7 @@ ssu_status_t ssu_update(const ssu_args_t *a, void *stream) {
     if (!ssu::find_kernel(st.dtype, io, static_cast<int>(N), multi, &k))
         return fail(SSU_ERR_NOT_IMPLEMENTED, "no kernel for state %s / io %s / dstate %lld",
                     dtype_str(st.dtype), dtype_str(io), (long long)N);
-    const Geometry geo = geometry(P, N);
+    const Geometry geo = geometry(P, N, st.dtype, multi);
     const int64_t grid = nseq * H * geo.dim_tiles;
     if (grid > INT32_MAX)
         return fail(SSU_ERR_NOT_IMPLEMENTED, "grid of %lld workgroups is too large",

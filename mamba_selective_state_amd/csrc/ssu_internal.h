@@ -31,11 +31,26 @@ enum Flags : int32_t {
 constexpr int kWaveLanes = 64;
 constexpr int kLanesPerRow = 16;
 constexpr int kRowsPerPass = kWaveLanes / kLanesPerRow;
-constexpr int kMaxWaves = 4;
+#ifndef SSU_MAX_WAVES
+#define SSU_MAX_WAVES 4
+#endif
+constexpr int kMaxWaves = SSU_MAX_WAVES;
 
-// Passes (dim rows per lane) for a given dstate: 4, or 2 at dstate 256 to
-// bound the registers a lane holds (passes * dstate / 16 fp32 values).
-constexpr int passes_for(int dstate) { return dstate >= 256 ? 2 : 4; }
+// Passes (dim rows per lane): enough rows that each lane keeps about
+// `lane_bytes` of state in flight (dstate/16 elements per row, in the state
+// dtype), between 1 and 8 rows. The multi-token kernel, which also holds the
+// next token's inputs, uses a smaller budget than the one-token kernel.
+#ifndef SSU_LANE_BYTES
+#define SSU_LANE_BYTES 128
+#endif
+#ifndef SSU_LANE_BYTES_MULTI
+#define SSU_LANE_BYTES_MULTI 64
+#endif
+constexpr int passes_for(int dstate, int state_bytes, bool multi) {
+    const int per_row = (dstate / kLanesPerRow) * state_bytes;
+    const int rows = (multi ? SSU_LANE_BYTES_MULTI : SSU_LANE_BYTES) / per_row;
+    return rows < 1 ? 1 : (rows > 8 ? 8 : rows);
+}
 
 // Kernel arguments. Strides are in elements. The pool is contiguous
 // [slots, heads, dim, dstate]; every other row tensor is addressed as

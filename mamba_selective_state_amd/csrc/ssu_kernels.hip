@@ -28,6 +28,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "../../include/ssu.h"
 #include "ssu_internal.h"
 
@@ -64,6 +66,39 @@ struct alignas(sizeof(T) * VEC) Pack {
     T v[VEC];
 };
 
+// Streaming accesses of the state pool. Each state byte is touched once per
+// call, so the pool's loads and stores carry the non-temporal hint and do not
+// displace the per-row inputs (B and C are shared by a group's heads) from
+// the caches.
+#ifndef SSU_NT_STATE
+#define SSU_NT_STATE 1
+#endif
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+template <int BYTES> struct RawOf;
+template <> struct RawOf<2> { using T = unsigned short; };
+template <> struct RawOf<4> { using T = unsigned int; };
+template <> struct RawOf<8> { using T = u32x2; };
+template <> struct RawOf<16> { using T = u32x4; };
+
+template <typename P>
+__device__ __forceinline__ P load_state(const P *src) {
+    using R = typename RawOf<sizeof(P)>::T;
+    R r = SSU_NT_STATE ? __builtin_nontemporal_load(reinterpret_cast<const R *>(src))
+                       : *reinterpret_cast<const R *>(src);
+    return __builtin_bit_cast(P, r);
+}
+
+template <typename P>
+__device__ __forceinline__ void store_state(P *dst, const P &v) {
+    using R = typename RawOf<sizeof(P)>::T;
+    const R r = __builtin_bit_cast(R, v);
+    if (SSU_NT_STATE)
+        __builtin_nontemporal_store(r, reinterpret_cast<R *>(dst));
+    else
+        *reinterpret_cast<R *>(dst) = r;
+}
+
 __device__ __forceinline__ int64_t load_index(const void *base, bool i64, int64_t i) {
     return i64 ? static_cast<const int64_t *>(base)[i]
                : static_cast<int64_t>(static_cast<const int32_t *>(base)[i]);
@@ -79,6 +114,14 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
+// Value of lane Q of the caller's DPP row (lanes 16k .. 16k+15), in every
+// lane of that row.
+template <int Q>
+__device__ __forceinline__ float row16_bcast(float v) {
+    static_assert(Q >= 0 && Q < 16, "lane within a row");
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + Q, 0xF, 0xF, false));  // row_newbcast
+}
+
 __device__ __forceinline__ float softplus(float v) { return v > 20.0f ? v : log1pf(expf(v)); }
 
 // Entry of a slot table naming sequence b's position t.
@@ -88,14 +131,35 @@ __device__ __forceinline__ int64_t table_slot(const void *tab, bool two_d, bool 
     return load_index(tab, i64, i);
 }
 
+// Inputs of one token for the lane: its dstate columns of B and C (raw, in
+// the x dtype) and x, dt and z of the dim row whose scalars the lane computes.
+template <typename IT, int NCH, int IVEC>
+struct TokenInputs {
+    Pack<IT, IVEC> b[NCH], c[NCH];
+    uint32_t x, dt, z;
+};
+
+// Unrolled loop over the passes with the pass index as a constant (DPP
+// controls must be immediates).
+template <int Q, int PASSES, typename F>
+__device__ __forceinline__ void for_passes(F &&f) {
+    if constexpr (Q < PASSES) {
+        f(std::integral_constant<int, Q>());
+        for_passes<Q + 1, PASSES>(f);
+    }
+}
+
 template <typename ST, typename IT, int N, bool MULTI>
 __global__ __launch_bounds__(kMaxWaves *kWaveLanes) void ssu_kernel(const Params p) {
     constexpr int E = N / kLanesPerRow;  // state elements per lane per row
     constexpr int VEC = (16 / (int)sizeof(ST)) < E ? (16 / (int)sizeof(ST)) : E;
     constexpr int NCH = E / VEC;         // accesses per lane per row
-    constexpr int PASSES = passes_for(N);
+    constexpr int PASSES = passes_for(N, sizeof(ST), MULTI);
     constexpr int IVEC = VEC;            // B / C are read with the same column split
     static_assert(E * kLanesPerRow == N && NCH * VEC == E, "dstate split");
+    static_assert(PASSES <= kLanesPerRow, "one scalar-owning lane per pass");
+    using SPack = Pack<ST, VEC>;
+    using Inputs = TokenInputs<IT, NCH, IVEC>;
 
     const int lane = threadIdx.x & (kWaveLanes - 1);
     const int wave = threadIdx.x / kWaveLanes;
@@ -110,7 +174,12 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes) void ssu_kernel(const Params
     const int h = static_cast<int>(sh % p.H);
     const int64_t b = sh / p.H;
     const int g = h / p.heads_per_group;
-    const int d0 = tile * p.rows_per_block + wave * (kRowsPerPass * PASSES) + rsub;
+    // Pass q covers dim rows dw + 4q + rsub. The per-row scalars of pass q
+    // (decay, dt' x, the gate and y) are computed once, by lane col == q of
+    // each row group: the lane's "own" row is dw + 4 col + rsub.
+    const int dw = tile * p.rows_per_block + wave * (kRowsPerPass * PASSES);
+    const int d_own = dw + col * kRowsPerPass + rsub;
+    const bool owner = col < PASSES && d_own < p.P;
 
     // the sequence's rows
     int64_t first_row = b, len = 1;
@@ -140,26 +209,24 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes) void ssu_kernel(const Params
     const int64_t tile_off = static_cast<int64_t>(h) * p.P * N;
     ST *const pool = static_cast<ST *>(p.state);
 
-    // load the state tile (zeros for the pad id)
-    float S[PASSES][E];
+    // The lane's part of the tile, kept in the state dtype: what is stored is
+    // also what the next token starts from. The pad id reads as zeros.
+    SPack S[PASSES][NCH];
     const bool read_pad = rslot == p.pad;
+    const ST *const rbase = pool + rslot * p.slot_stride + tile_off;
 #pragma unroll
     for (int q = 0; q < PASSES; q++) {
-        const int d = d0 + q * kRowsPerPass;
-        if (!read_pad && d < p.P) {
-            const ST *src = pool + rslot * p.slot_stride + tile_off + static_cast<int64_t>(d) * N;
+        const int d = dw + q * kRowsPerPass + rsub;
 #pragma unroll
-            for (int c = 0; c < NCH; c++) {
-                const Pack<ST, VEC> v =
-                    *reinterpret_cast<const Pack<ST, VEC> *>(src + c * kLanesPerRow * VEC + col * VEC);
+        for (int c = 0; c < NCH; c++) {
+            if (!read_pad && d < p.P) {
+                S[q][c] = load_state(reinterpret_cast<const SPack *>(
+                    rbase + static_cast<int64_t>(d) * N + c * kLanesPerRow * VEC + col * VEC));
+            } else {
 #pragma unroll
                 for (int k = 0; k < VEC; k++)
-                    S[q][c * VEC + k] = widen(v.v[k]);
+                    S[q][c].v[k] = narrow<ST>(0.0f);
             }
-        } else {
-#pragma unroll
-            for (int e = 0; e < E; e++)
-                S[q][e] = 0.0f;
         }
     }
 
@@ -171,102 +238,105 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes) void ssu_kernel(const Params
     const IT *const Bs = static_cast<const IT *>(p.B);
     const IT *const Cs = static_cast<const IT *>(p.C);
     IT *const ys = static_cast<IT *>(p.out);
+    const bool dt_f32 = flags & kDtF32;
     const void *const wtab = p.wtab ? p.wtab : p.rtab;
     const bool w2d = p.wtab ? (flags & kWrite2D) : (flags & kRead2D);
     const bool wi64 = p.wtab ? (flags & kWriteI64) : (flags & kReadI64);
     const int64_t ws0 = p.wtab ? p.w_s0 : p.r_s0;
     const int64_t ws1 = p.wtab ? p.w_s1 : p.r_s1;
 
+    // issue the loads of row r's inputs (no use before the next wait)
+    auto fetch = [&](int64_t r, Inputs &in) {
+        const IT *bsrc = Bs + r * p.B_sr + static_cast<int64_t>(g) * p.B_sg + col * IVEC;
+        const IT *csrc = Cs + r * p.C_sr + static_cast<int64_t>(g) * p.C_sg + col * IVEC;
+#pragma unroll
+        for (int c = 0; c < NCH; c++) {
+            in.b[c] = *reinterpret_cast<const Pack<IT, IVEC> *>(bsrc + c * kLanesPerRow * IVEC);
+            in.c[c] = *reinterpret_cast<const Pack<IT, IVEC> *>(csrc + c * kLanesPerRow * IVEC);
+        }
+        in.x = in.dt = in.z = 0u;
+        if (owner) {
+            in.x = load_bits(xs + r * p.x_sr + h * p.x_sh + d_own);
+            const int64_t di = r * p.dt_sr + h * p.dt_sh + static_cast<int64_t>(d_own) * p.dt_sp;
+            in.dt = dt_f32 ? load_bits(static_cast<const float *>(p.dt) + di)
+                           : load_bits(static_cast<const IT *>(p.dt) + di);
+            if (zs)
+                in.z = load_bits(zs + r * p.z_sr + h * p.z_sh + d_own);
+        }
+    };
+
+    Inputs cur;
+    fetch(first_row, cur);
     for (int64_t t = 0; t < len; t++) {
         const int64_t r = first_row + t;
+        // the next token's inputs are requested before this token's stores,
+        // so waiting for them later does not wait for the stores
+        Inputs nxt;
+        if (MULTI && t + 1 < len)
+            fetch(r + 1, nxt);
 
-        // this lane's dstate columns of B and C
         float Bv[E], Cv[E];
-        {
-            const IT *bsrc = Bs + r * p.B_sr + static_cast<int64_t>(g) * p.B_sg;
-            const IT *csrc = Cs + r * p.C_sr + static_cast<int64_t>(g) * p.C_sg;
 #pragma unroll
-            for (int c = 0; c < NCH; c++) {
-                const Pack<IT, IVEC> bv =
-                    *reinterpret_cast<const Pack<IT, IVEC> *>(bsrc + c * kLanesPerRow * IVEC + col * IVEC);
-                const Pack<IT, IVEC> cv =
-                    *reinterpret_cast<const Pack<IT, IVEC> *>(csrc + c * kLanesPerRow * IVEC + col * IVEC);
+        for (int c = 0; c < NCH; c++)
 #pragma unroll
-                for (int k = 0; k < IVEC; k++) {
-                    Bv[c * IVEC + k] = widen(bv.v[k]);
-                    Cv[c * IVEC + k] = widen(cv.v[k]);
-                }
+            for (int k = 0; k < IVEC; k++) {
+                Bv[c * IVEC + k] = widen(cur.b[c].v[k]);
+                Cv[c * IVEC + k] = widen(cur.c[c].v[k]);
             }
-        }
 
-        // this token's per-row inputs for all of the lane's rows, issued
-        // together before any of them is used
-        uint32_t xb[PASSES], dtb[PASSES], zb[PASSES];
-        const bool dt_f32 = flags & kDtF32;
-#pragma unroll
-        for (int q = 0; q < PASSES; q++) {
-            const int d = d0 + q * kRowsPerPass;
-            xb[q] = dtb[q] = zb[q] = 0u;
-            if (d < p.P) {
-                xb[q] = load_bits(xs + r * p.x_sr + h * p.x_sh + d);
-                const int64_t di = r * p.dt_sr + h * p.dt_sh + static_cast<int64_t>(d) * p.dt_sp;
-                dtb[q] = dt_f32 ? load_bits(static_cast<const float *>(p.dt) + di)
-                                : load_bits(static_cast<const IT *>(p.dt) + di);
-                if (zs)
-                    zb[q] = load_bits(zs + r * p.z_sr + h * p.z_sh + d);
-            }
-        }
-        float xv[PASSES], dtv[PASSES], zv[PASSES];
-#pragma unroll
-        for (int q = 0; q < PASSES; q++) {
-            xv[q] = from_bits<IT>(xb[q]);
-            dtv[q] = dt_f32 ? __uint_as_float(dtb[q]) : from_bits<IT>(dtb[q]);
-            zv[q] = from_bits<IT>(zb[q]);
-        }
+        // scalars of the lane's own row
+        const float xv = from_bits<IT>(cur.x);
+        float v = (dt_f32 ? __uint_as_float(cur.dt) : from_bits<IT>(cur.dt)) + bias_h;
+        if (flags & kSoftplus)
+            v = softplus(v);
+        const float decay = expf(v * a_h);
+        const float dtx = v * xv;
 
-#pragma unroll
-        for (int q = 0; q < PASSES; q++) {
-            const int d = d0 + q * kRowsPerPass;
-            float v = dtv[q] + bias_h;
-            if (flags & kSoftplus)
-                v = softplus(v);
-            const float decay = expf(v * a_h);
-            const float dtx = v * xv[q];
-            float acc = 0.0f;
-#pragma unroll
-            for (int e = 0; e < E; e++) {
-                S[q][e] = fmaf(S[q][e], decay, dtx * Bv[e]);
-                acc = fmaf(S[q][e], Cv[e], acc);
-            }
-            float y = row16_sum(acc) + d_h * xv[q];
-            if (zs)
-                y *= zv[q] / (1.0f + expf(-zv[q]));
-            if (d < p.P && col == 0)
-                ys[r * p.out_sr + h * p.out_sh + d] = narrow<IT>(y);
-        }
-
-        // store through the token's destination (its own entry of the
-        // destination table, else of the read table, else slot b)
+        // destination: the token's own entry of the destination table, else
+        // of the read table, else slot b
         const int64_t wslot =
             wtab ? table_slot(wtab, w2d, wi64, ws0, ws1, b, first_row, t) : b;
         const bool store = !(flags & kDisable) && wslot != p.pad;
-#pragma unroll
-        for (int q = 0; q < PASSES; q++) {
-            const int d = d0 + q * kRowsPerPass;
-            ST *dst = pool + wslot * p.slot_stride + tile_off + static_cast<int64_t>(d) * N;
+        ST *const wbase = pool + wslot * p.slot_stride + tile_off;
+
+        float ysum = 0.0f;
+        for_passes<0, PASSES>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            const int d = dw + q * kRowsPerPass + rsub;
+            const float dq = row16_bcast<q>(decay);
+            const float tq = row16_bcast<q>(dtx);
+            float acc = 0.0f;
 #pragma unroll
             for (int c = 0; c < NCH; c++) {
-                Pack<ST, VEC> v;
 #pragma unroll
                 for (int k = 0; k < VEC; k++) {
-                    v.v[k] = narrow<ST>(S[q][c * VEC + k]);
-                    if (MULTI)
-                        S[q][c * VEC + k] = widen(v.v[k]);  // carry the stored value
+                    const int e = c * VEC + k;
+                    const float s = fmaf(widen(S[q][c].v[k]), dq, tq * Bv[e]);
+                    acc = fmaf(s, Cv[e], acc);
+                    S[q][c].v[k] = narrow<ST>(s);  // the stored and carried value
                 }
-                if (store && d < p.P)
-                    *reinterpret_cast<Pack<ST, VEC> *>(dst + c * kLanesPerRow * VEC + col * VEC) = v;
             }
+            const float sum = row16_sum(acc);
+            ysum = col == q ? sum : ysum;
+            if (store && d < p.P) {
+                ST *dst = wbase + static_cast<int64_t>(d) * N + col * VEC;
+#pragma unroll
+                for (int c = 0; c < NCH; c++)
+                    store_state(reinterpret_cast<SPack *>(dst + c * kLanesPerRow * VEC), S[q][c]);
+            }
+        });
+
+        // y of the lane's own row
+        if (owner) {
+            float y = ysum + d_h * xv;
+            if (zs) {
+                const float zv = from_bits<IT>(cur.z);
+                y *= zv / (1.0f + expf(-zv));
+            }
+            ys[r * p.out_sr + h * p.out_sh + d_own] = narrow<IT>(y);
         }
+        if (MULTI)
+            cur = nxt;
     }
 }
 
