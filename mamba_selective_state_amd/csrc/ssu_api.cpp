@@ -180,6 +180,17 @@ ssu_status_t meta_vector(const char *name, const ssu_tensor_t &t, int64_t want, 
     return SSU_OK;
 }
 
+// Largest element offset a strided view reaches (0 when it is empty).
+int64_t max_offset(const ssu_tensor_t &t) {
+    int64_t m = 0;
+    for (int i = 0; i < t.ndim; i++) {
+        if (t.size[i] <= 0)
+            return 0;
+        m += (t.size[i] - 1) * t.stride[i];
+    }
+    return m;
+}
+
 struct Geometry {
     int32_t block, rows_per_block, dim_tiles;
 };
@@ -322,8 +333,12 @@ ssu_status_t ssu_update(const ssu_args_t *a, void *stream) {
     ssu::Params p;
     memset(&p, 0, sizeof p);
     int64_t sk = 0;
+    // element strides, narrowed to 32 bits once every span is known to fit
+    int64_t x_sr = 0, x_sh = 0, dt_sr = 0, dt_sh = 0, dt_sp = 0, A_sh = 0, D_sh = 0, bias_sh = 0;
+    int64_t B_sr = 0, B_sg = 0, C_sr = 0, C_sg = 0, z_sr = 0, z_sh = 0, out_sr = 0, out_sh = 0;
+    int64_t r_s0 = 0, r_s1 = 0, w_s0 = 0, w_s1 = 0, cu_s = 0, acc_s = 0;
     ssu_status_t s;
-    if ((s = row_tensor("x", x, rw, H, P, &p.x_sr, &p.x_sh, &sk)) != SSU_OK)
+    if ((s = row_tensor("x", x, rw, H, P, &x_sr, &x_sh, &sk)) != SSU_OK)
         return s;
     if (sk != 1)
         return fail(SSU_ERR_VALUE, "x must have unit stride over dim");
@@ -349,9 +364,9 @@ ssu_status_t ssu_update(const ssu_args_t *a, void *stream) {
         layout = ssu::kOneToken;
     }
     bool cu_i64 = false, acc_i64 = false;
-    if ((s = meta_vector("cu_seqlens", a->cu_seqlens, nseq + 1, &p.cu, &p.cu_s, &cu_i64)) != SSU_OK)
+    if ((s = meta_vector("cu_seqlens", a->cu_seqlens, nseq + 1, &p.cu, &cu_s, &cu_i64)) != SSU_OK)
         return s;
-    if ((s = meta_vector("num_accepted_tokens", a->num_accepted_tokens, nseq, &p.acc, &p.acc_s,
+    if ((s = meta_vector("num_accepted_tokens", a->num_accepted_tokens, nseq, &p.acc, &acc_s,
                          &acc_i64)) != SSU_OK)
         return s;
     const bool multi = layout != ssu::kOneToken || p.acc != nullptr;
@@ -365,22 +380,22 @@ ssu_status_t ssu_update(const ssu_args_t *a, void *stream) {
     if (!aligned(dt.data, elem_bytes(dt.dtype)))
         return fail(SSU_ERR_VALUE, "dt is not aligned to its element size");
     if (dt.ndim == x.ndim) {
-        if ((s = row_tensor("dt", dt, rw, H, P, &p.dt_sr, &p.dt_sh, &p.dt_sp)) != SSU_OK)
+        if ((s = row_tensor("dt", dt, rw, H, P, &dt_sr, &dt_sh, &dt_sp)) != SSU_OK)
             return s;
     } else if (dt.ndim == x.ndim - 1) {
-        if ((s = row_tensor("dt", dt, rw, H, -1, &p.dt_sr, &p.dt_sh, &sk)) != SSU_OK)
+        if ((s = row_tensor("dt", dt, rw, H, -1, &dt_sr, &dt_sh, &sk)) != SSU_OK)
             return s;
-        p.dt_sp = 0;
+        dt_sp = 0;
     } else {
         return fail(SSU_ERR_VALUE, "dt must be shaped like x, or like x without its last axis");
     }
 
     // per-head vectors
-    if ((s = head_vector("A", a->A, H, true, &p.A, &p.A_sh)) != SSU_OK)
+    if ((s = head_vector("A", a->A, H, true, &p.A, &A_sh)) != SSU_OK)
         return s;
-    if ((s = head_vector("D", a->D, H, false, &p.D, &p.D_sh)) != SSU_OK)
+    if ((s = head_vector("D", a->D, H, false, &p.D, &D_sh)) != SSU_OK)
         return s;
-    if ((s = head_vector("dt_bias", a->dt_bias, H, false, &p.dt_bias, &p.bias_sh)) != SSU_OK)
+    if ((s = head_vector("dt_bias", a->dt_bias, H, false, &p.dt_bias, &bias_sh)) != SSU_OK)
         return s;
 
     // B and C: [.., groups, dstate] in the x dtype
@@ -392,19 +407,19 @@ ssu_status_t ssu_update(const ssu_args_t *a, void *stream) {
     if (G <= 0 || H % G != 0)
         return fail(SSU_ERR_VALUE, "heads (%lld) must be divisible by groups (%lld)", (long long)H,
                     (long long)G);
-    if ((s = row_tensor("B", a->B, rw, G, N, &p.B_sr, &p.B_sg, &sk)) != SSU_OK)
+    if ((s = row_tensor("B", a->B, rw, G, N, &B_sr, &B_sg, &sk)) != SSU_OK)
         return s;
     if (sk != 1)
         return fail(SSU_ERR_VALUE, "B must have unit stride over dstate");
-    if ((s = row_tensor("C", a->C, rw, G, N, &p.C_sr, &p.C_sg, &sk)) != SSU_OK)
+    if ((s = row_tensor("C", a->C, rw, G, N, &C_sr, &C_sg, &sk)) != SSU_OK)
         return s;
     if (sk != 1)
         return fail(SSU_ERR_VALUE, "C must have unit stride over dstate");
     {
         const int64_t vec = access_vec(st.dtype, N);
         const int64_t bytes = vec * elem_bytes(io);
-        if (!aligned(a->B.data, bytes) || !aligned(a->C.data, bytes) || p.B_sr % vec ||
-            p.B_sg % vec || p.C_sr % vec || p.C_sg % vec)
+        if (!aligned(a->B.data, bytes) || !aligned(a->C.data, bytes) || B_sr % vec || B_sg % vec ||
+            C_sr % vec || C_sg % vec)
             return fail(SSU_ERR_VALUE,
                         "B and C rows must start on %lld-byte boundaries (base and strides)",
                         (long long)bytes);
@@ -414,7 +429,7 @@ ssu_status_t ssu_update(const ssu_args_t *a, void *stream) {
     if (present(a->z)) {
         if (a->z.dtype != io)
             return fail(SSU_ERR_VALUE, "z must have the x dtype");
-        if ((s = row_tensor("z", a->z, rw, H, P, &p.z_sr, &p.z_sh, &sk)) != SSU_OK)
+        if ((s = row_tensor("z", a->z, rw, H, P, &z_sr, &z_sh, &sk)) != SSU_OK)
             return s;
         if (sk != 1)
             return fail(SSU_ERR_VALUE, "z must have unit stride over dim");
@@ -426,7 +441,7 @@ ssu_status_t ssu_update(const ssu_args_t *a, void *stream) {
         return fail(SSU_ERR_VALUE, "out is required");
     if (a->out.dtype != io)
         return fail(SSU_ERR_VALUE, "out must have the x dtype");
-    if ((s = row_tensor("out", a->out, rw, H, P, &p.out_sr, &p.out_sh, &sk)) != SSU_OK)
+    if ((s = row_tensor("out", a->out, rw, H, P, &out_sr, &out_sh, &sk)) != SSU_OK)
         return s;
     if (sk != 1)
         return fail(SSU_ERR_VALUE, "out must have unit stride over dim");
@@ -436,14 +451,55 @@ ssu_status_t ssu_update(const ssu_args_t *a, void *stream) {
     // slot tables
     bool r2d, ri64, w2d, wi64;
     if ((s = slot_table("state_batch_indices", a->state_batch_indices, rw, nseq, layout, steps,
-                        &p.rtab, &p.r_s0, &p.r_s1, &r2d, &ri64)) != SSU_OK)
+                        &p.rtab, &r_s0, &r_s1, &r2d, &ri64)) != SSU_OK)
         return s;
     if ((s = slot_table("dst_state_batch_indices", a->dst_state_batch_indices, rw, nseq, layout,
-                        steps, &p.wtab, &p.w_s0, &p.w_s1, &w2d, &wi64)) != SSU_OK)
+                        steps, &p.wtab, &w_s0, &w_s1, &w2d, &wi64)) != SSU_OK)
         return s;
 
     if (nseq <= 0 || rw.rows <= 0)
         return g_error.clear(), SSU_OK;  // nothing to do
+
+    // every tensor but the pool is addressed with 32-bit element offsets
+    {
+        const ssu_tensor_t *spans[] = {&x, &dt, &a->A, &a->B, &a->C, &a->D, &a->z, &a->dt_bias,
+                                       &a->out, &a->cu_seqlens, &a->num_accepted_tokens};
+        const char *names[] = {"x", "dt", "A", "B", "C", "D", "z", "dt_bias", "out",
+                               "cu_seqlens", "num_accepted_tokens"};
+        for (int i = 0; i < 11; i++)
+            if (present(*spans[i]) && max_offset(*spans[i]) >= INT32_MAX)
+                return fail(SSU_ERR_NOT_IMPLEMENTED, "%s spans 2^31 elements or more", names[i]);
+        // a 2-D table may be addressed past its declared extent (a strided
+        // view): bound what the kernel can reach
+        const int64_t reach_r = (nseq + rw.rows) * (r_s0 > r_s1 ? r_s0 : r_s1);
+        const int64_t reach_w = (nseq + rw.rows) * (w_s0 > w_s1 ? w_s0 : w_s1);
+        if (reach_r >= INT32_MAX || reach_w >= INT32_MAX)
+            return fail(SSU_ERR_NOT_IMPLEMENTED, "slot tables span 2^31 entries or more");
+        if (rw.rows >= INT32_MAX || max_offset(x) >= INT32_MAX)
+            return fail(SSU_ERR_NOT_IMPLEMENTED, "too many rows");
+    }
+    p.x_sr = static_cast<int32_t>(x_sr);
+    p.x_sh = static_cast<int32_t>(x_sh);
+    p.dt_sr = static_cast<int32_t>(dt_sr);
+    p.dt_sh = static_cast<int32_t>(dt_sh);
+    p.dt_sp = static_cast<int32_t>(dt_sp);
+    p.A_sh = static_cast<int32_t>(A_sh);
+    p.D_sh = static_cast<int32_t>(D_sh);
+    p.bias_sh = static_cast<int32_t>(bias_sh);
+    p.B_sr = static_cast<int32_t>(B_sr);
+    p.B_sg = static_cast<int32_t>(B_sg);
+    p.C_sr = static_cast<int32_t>(C_sr);
+    p.C_sg = static_cast<int32_t>(C_sg);
+    p.z_sr = static_cast<int32_t>(z_sr);
+    p.z_sh = static_cast<int32_t>(z_sh);
+    p.out_sr = static_cast<int32_t>(out_sr);
+    p.out_sh = static_cast<int32_t>(out_sh);
+    p.r_s0 = static_cast<int32_t>(r_s0);
+    p.r_s1 = static_cast<int32_t>(r_s1);
+    p.w_s0 = static_cast<int32_t>(w_s0);
+    p.w_s1 = static_cast<int32_t>(w_s1);
+    p.cu_s = static_cast<int32_t>(cu_s);
+    p.acc_s = static_cast<int32_t>(acc_s);
     if (nseq > INT32_MAX)
         return fail(SSU_ERR_NOT_IMPLEMENTED, "too many sequences");
 

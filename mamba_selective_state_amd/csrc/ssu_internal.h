@@ -32,19 +32,27 @@ constexpr int kWaveLanes = 64;
 constexpr int kLanesPerRow = 16;
 constexpr int kRowsPerPass = kWaveLanes / kLanesPerRow;
 #ifndef SSU_MAX_WAVES
-#define SSU_MAX_WAVES 4
+#define SSU_MAX_WAVES 1
 #endif
 constexpr int kMaxWaves = SSU_MAX_WAVES;
+// Minimum resident waves per SIMD the register allocation must allow, for the
+// one-token and the multi-token kernel.
+#ifndef SSU_WAVES_PER_EU
+#define SSU_WAVES_PER_EU 1
+#endif
+#ifndef SSU_WAVES_PER_EU_MULTI
+#define SSU_WAVES_PER_EU_MULTI 4
+#endif
 
 // Passes (dim rows per lane): enough rows that each lane keeps about
 // `lane_bytes` of state in flight (dstate/16 elements per row, in the state
-// dtype), between 1 and 8 rows. The multi-token kernel, which also holds the
-// next token's inputs, uses a smaller budget than the one-token kernel.
+// dtype), between 1 and 8 rows (separate budgets for the one-token and the
+// multi-token kernel, which also holds the next token's inputs).
 #ifndef SSU_LANE_BYTES
 #define SSU_LANE_BYTES 128
 #endif
 #ifndef SSU_LANE_BYTES_MULTI
-#define SSU_LANE_BYTES_MULTI 64
+#define SSU_LANE_BYTES_MULTI 128
 #endif
 constexpr int passes_for(int dstate, int state_bytes, bool multi) {
     const int per_row = (dstate / kLanesPerRow) * state_bytes;
@@ -53,38 +61,35 @@ constexpr int passes_for(int dstate, int state_bytes, bool multi) {
 }
 
 // Kernel arguments. Strides are in elements. The pool is contiguous
-// [slots, heads, dim, dstate]; every other row tensor is addressed as
-// row * sr + head (or group) * sh + d (last stride 1, except dt's sp).
+// [slots, heads, dim, dstate] and addressed with 64-bit offsets; every other
+// tensor spans fewer than 2^31 elements (checked on the host) and is
+// addressed with 32-bit offsets: row * sr + head (or group) * sh + d (last
+// stride 1, except dt's sp).
 struct Params {
     void *state;
     int64_t slot_stride;  // heads * dim * dstate
-    const void *x;
-    int64_t x_sr, x_sh;
-    const void *dt;
-    int64_t dt_sr, dt_sh, dt_sp;
-    const float *A;
-    int64_t A_sh;
-    const void *B;
-    int64_t B_sr, B_sg;
-    const void *C;
-    int64_t C_sr, C_sg;
-    const float *D;  // may be null
-    int64_t D_sh;
-    const void *z;   // may be null
-    int64_t z_sr, z_sh;
-    const float *dt_bias;  // may be null
-    int64_t bias_sh;
-    void *out;
-    int64_t out_sr, out_sh;
-    const void *rtab;  // may be null
-    int64_t r_s0, r_s1;
-    const void *wtab;  // may be null (then rtab, then the sequence index)
-    int64_t w_s0, w_s1;
-    const void *cu;    // kCuSeqlens only
-    int64_t cu_s;
-    const void *acc;   // may be null
-    int64_t acc_s;
     int64_t pad;
+    const void *x;
+    const void *dt;
+    const float *A;
+    const void *B;
+    const void *C;
+    const float *D;        // may be null
+    const void *z;         // may be null
+    const float *dt_bias;  // may be null
+    void *out;
+    const void *rtab;      // may be null
+    const void *wtab;      // may be null (then rtab, then the sequence index)
+    const void *cu;        // kCuSeqlens only
+    const void *acc;       // may be null
+    int32_t x_sr, x_sh;
+    int32_t dt_sr, dt_sh, dt_sp;
+    int32_t A_sh, D_sh, bias_sh;
+    int32_t B_sr, B_sg, C_sr, C_sg;
+    int32_t z_sr, z_sh;
+    int32_t out_sr, out_sh;
+    int32_t r_s0, r_s1, w_s0, w_s1;
+    int32_t cu_s, acc_s;
     int32_t nseq, H, P, heads_per_group;
     int32_t steps;          // kDense: tokens per sequence
     int32_t layout;         // Layout

@@ -99,7 +99,7 @@ __device__ __forceinline__ void store_state(P *dst, const P &v) {
         *reinterpret_cast<R *>(dst) = r;
 }
 
-__device__ __forceinline__ int64_t load_index(const void *base, bool i64, int64_t i) {
+__device__ __forceinline__ int64_t load_index(const void *base, bool i64, int32_t i) {
     return i64 ? static_cast<const int64_t *>(base)[i]
                : static_cast<int64_t>(static_cast<const int32_t *>(base)[i]);
 }
@@ -122,21 +122,93 @@ __device__ __forceinline__ float row16_bcast(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + Q, 0xF, 0xF, false));  // row_newbcast
 }
 
-__device__ __forceinline__ float softplus(float v) { return v > 20.0f ? v : log1pf(expf(v)); }
+// Per-row scalars use the hardware base-2 exponential, logarithm and
+// reciprocal (a few ulps each). Their errors stay far inside the update's
+// error budget: a relative error e in dt' or in the decay moves
+// S * exp(dt' A) by at most |S| x exp(-x) e <= 0.37 |S| e (x = |dt' A|), and
+// the rank-1 term by e |dt' x B|. exp(0) is exactly 1, so dt = 0 keeps the
+// state bit for bit.
+__device__ __forceinline__ float exp_hw(float v) {
+    return __builtin_amdgcn_exp2f(v * 1.44269504088896341f);
+}
+
+// log(1 + e^v), e^v itself above v = 20 (the difference is below half an
+// ulp there). log1p(u) = log(w) * u / (w - 1) with w = 1 + u keeps the
+// relative accuracy for small u (w - 1 is exact).
+__device__ __forceinline__ float softplus(float v) {
+    const float u = exp_hw(v);
+    const float w = 1.0f + u;
+    const float l = __builtin_amdgcn_logf(w) * 0.693147180559945309f;
+    const float r = w == 1.0f ? u : l * (u * __builtin_amdgcn_rcpf(w - 1.0f));
+    return v > 20.0f ? v : r;
+}
+
+// z * sigmoid(z)
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + exp_hw(-z)); }
 
 // Entry of a slot table naming sequence b's position t.
-__device__ __forceinline__ int64_t table_slot(const void *tab, bool two_d, bool i64, int64_t s0,
-                                              int64_t s1, int64_t b, int64_t first_row, int64_t t) {
-    const int64_t i = two_d ? b * s0 + t * s1 : (first_row + t) * s0;
+__device__ __forceinline__ int64_t table_slot(const void *tab, bool two_d, bool i64, int32_t s0,
+                                              int32_t s1, int32_t b, int32_t first_row, int32_t t) {
+    const int32_t i = two_d ? b * s0 + t * s1 : (first_row + t) * s0;
     return load_index(tab, i64, i);
 }
 
 // Inputs of one token for the lane: its dstate columns of B and C (raw, in
 // the x dtype) and x, dt and z of the dim row whose scalars the lane computes.
+// Raw 32-bit words of one B or C access (IVEC elements of the x dtype), kept
+// unconverted until they are used.
+template <typename IT, int IVEC>
+struct RawWords {
+    static constexpr int kBytes = IVEC * (int)sizeof(IT);
+    static constexpr int kWords = kBytes < 4 ? 1 : kBytes / 4;
+    uint32_t w[kWords];
+};
+
+template <typename IT, int IVEC>
+__device__ __forceinline__ RawWords<IT, IVEC> load_words(const IT *src) {
+    RawWords<IT, IVEC> r;
+    constexpr int kBytes = RawWords<IT, IVEC>::kBytes;
+    if constexpr (kBytes <= 2) {
+        r.w[0] = *reinterpret_cast<const uint16_t *>(src);
+    } else if constexpr (kBytes <= 16) {
+        using R = typename RawOf<kBytes>::T;
+        const R v = *reinterpret_cast<const R *>(src);
+        r = __builtin_bit_cast(RawWords<IT, IVEC>, v);
+    } else {
+#pragma unroll
+        for (int i = 0; i < kBytes / 16; i++) {
+            const u32x4 v = reinterpret_cast<const u32x4 *>(src)[i];
+            r.w[4 * i] = v.x;
+            r.w[4 * i + 1] = v.y;
+            r.w[4 * i + 2] = v.z;
+            r.w[4 * i + 3] = v.w;
+        }
+    }
+    return r;
+}
+
+// element k of a RawWords block, widened to fp32
+template <typename IT, int IVEC>
+__device__ __forceinline__ float word_elem(const RawWords<IT, IVEC> &r, int k) {
+    if constexpr (sizeof(IT) == 4)
+        return __uint_as_float(r.w[k]);
+    else {
+        const uint32_t word = r.w[k / 2];
+        return from_bits<IT>((k & 1) ? (word >> 16) : (word & 0xFFFFu));
+    }
+}
+
+// Inputs of one token for the lane, as loaded (raw bits): its dstate columns
+// of B and C, and x, z, dt of the dim row whose scalars it computes (dt in
+// two 16-bit halves, the high one used for fp32 dt), and the destination
+// table entry (two words, the high one used for i64 tables).
 template <typename IT, int NCH, int IVEC>
 struct TokenInputs {
-    Pack<IT, IVEC> b[NCH], c[NCH];
-    uint32_t x, dt, z;
+    using Bits = std::conditional_t<sizeof(IT) == 2, uint16_t, uint32_t>;
+    RawWords<IT, IVEC> b[NCH], c[NCH];
+    Bits x, z;
+    uint16_t dt_lo, dt_hi;
+    uint32_t ws_lo, ws_hi;
 };
 
 // Unrolled loop over the passes with the pass index as a constant (DPP
@@ -150,7 +222,8 @@ __device__ __forceinline__ void for_passes(F &&f) {
 }
 
 template <typename ST, typename IT, int N, bool MULTI>
-__global__ __launch_bounds__(kMaxWaves *kWaveLanes) void ssu_kernel(const Params p) {
+__global__ __launch_bounds__(kMaxWaves *kWaveLanes,
+                             MULTI ? SSU_WAVES_PER_EU_MULTI : SSU_WAVES_PER_EU) void ssu_kernel(const Params p) {
     constexpr int E = N / kLanesPerRow;  // state elements per lane per row
     constexpr int VEC = (16 / (int)sizeof(ST)) < E ? (16 / (int)sizeof(ST)) : E;
     constexpr int NCH = E / VEC;         // accesses per lane per row
@@ -168,11 +241,11 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes) void ssu_kernel(const Params
     const int flags = p.flags;
 
     // workgroup -> (sequence, head, dim tile)
-    const int64_t wg = blockIdx.x;
-    const int tile = static_cast<int>(wg % p.dim_tiles);
-    const int64_t sh = wg / p.dim_tiles;
-    const int h = static_cast<int>(sh % p.H);
-    const int64_t b = sh / p.H;
+    const int32_t wg = blockIdx.x;
+    const int tile = wg % p.dim_tiles;
+    const int32_t sh = wg / p.dim_tiles;
+    const int h = sh % p.H;
+    const int32_t b = sh / p.H;
     const int g = h / p.heads_per_group;
     // Pass q covers dim rows dw + 4q + rsub. The per-row scalars of pass q
     // (decay, dt' x, the gate and y) are computed once, by lane col == q of
@@ -182,11 +255,11 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes) void ssu_kernel(const Params
     const bool owner = col < PASSES && d_own < p.P;
 
     // the sequence's rows
-    int64_t first_row = b, len = 1;
+    int32_t first_row = b, len = 1;
     if (MULTI) {
         if (p.layout == kCuSeqlens) {
-            first_row = load_index(p.cu, flags & kCuI64, b * p.cu_s);
-            len = load_index(p.cu, flags & kCuI64, (b + 1) * p.cu_s) - first_row;
+            first_row = static_cast<int32_t>(load_index(p.cu, flags & kCuI64, b * p.cu_s));
+            len = static_cast<int32_t>(load_index(p.cu, flags & kCuI64, (b + 1) * p.cu_s)) - first_row;
         } else if (p.layout == kDense) {
             first_row = b * p.steps;
             len = p.steps;
@@ -197,9 +270,9 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes) void ssu_kernel(const Params
 
     // read slot: entry num_accepted_tokens[b] - 1 (floored at 0) of the read
     // table, or the sequence index without a table
-    int64_t start = 0;
+    int32_t start = 0;
     if (MULTI && p.acc) {
-        start = load_index(p.acc, flags & kAccI64, b * p.acc_s) - 1;
+        start = static_cast<int32_t>(load_index(p.acc, flags & kAccI64, b * p.acc_s)) - 1;
         start = start < 0 ? 0 : start;
     }
     const int64_t rslot = p.rtab ? table_slot(p.rtab, flags & kRead2D, flags & kReadI64, p.r_s0,
@@ -242,60 +315,76 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes) void ssu_kernel(const Params
     const void *const wtab = p.wtab ? p.wtab : p.rtab;
     const bool w2d = p.wtab ? (flags & kWrite2D) : (flags & kRead2D);
     const bool wi64 = p.wtab ? (flags & kWriteI64) : (flags & kReadI64);
-    const int64_t ws0 = p.wtab ? p.w_s0 : p.r_s0;
-    const int64_t ws1 = p.wtab ? p.w_s1 : p.r_s1;
+    const int32_t ws0 = p.wtab ? p.w_s0 : p.r_s0;
+    const int32_t ws1 = p.wtab ? p.w_s1 : p.r_s1;
 
-    // issue the loads of row r's inputs (no use before the next wait)
-    auto fetch = [&](int64_t r, Inputs &in) {
-        const IT *bsrc = Bs + r * p.B_sr + static_cast<int64_t>(g) * p.B_sg + col * IVEC;
-        const IT *csrc = Cs + r * p.C_sr + static_cast<int64_t>(g) * p.C_sg + col * IVEC;
+    // Issue the loads of token t's inputs; nothing here waits. Every load is
+    // unconditional and in bounds (a lane that owns no row reads its row
+    // group's first row; absent z reads x; a 16-bit dt or an i32 table reads
+    // the same address twice), so no branch joins pending loads; the values
+    // are selected where they are used.
+    const int d_fetch = owner ? d_own : 0;
+    const IT *const zsrc = zs ? zs : xs;
+    const int32_t z_sr = zs ? p.z_sr : p.x_sr, z_sh = zs ? p.z_sh : p.x_sh;
+    const int dt_bytes = dt_f32 ? 4 : 2;
+    const unsigned char *const dts = static_cast<const unsigned char *>(p.dt);
+    const unsigned char *const wtb =
+        static_cast<const unsigned char *>(wtab ? wtab : static_cast<const void *>(p.A));
+    const int w_bytes = wi64 ? 8 : 4;
+    auto fetch = [&](int32_t t, Inputs &in) {
+        const int32_t r = first_row + t;
+        const IT *bsrc = Bs + (r * p.B_sr + g * p.B_sg + col * IVEC);
+        const IT *csrc = Cs + (r * p.C_sr + g * p.C_sg + col * IVEC);
 #pragma unroll
         for (int c = 0; c < NCH; c++) {
-            in.b[c] = *reinterpret_cast<const Pack<IT, IVEC> *>(bsrc + c * kLanesPerRow * IVEC);
-            in.c[c] = *reinterpret_cast<const Pack<IT, IVEC> *>(csrc + c * kLanesPerRow * IVEC);
+            in.b[c] = load_words<IT, IVEC>(bsrc + c * kLanesPerRow * IVEC);
+            in.c[c] = load_words<IT, IVEC>(csrc + c * kLanesPerRow * IVEC);
         }
-        in.x = in.dt = in.z = 0u;
-        if (owner) {
-            in.x = load_bits(xs + r * p.x_sr + h * p.x_sh + d_own);
-            const int64_t di = r * p.dt_sr + h * p.dt_sh + static_cast<int64_t>(d_own) * p.dt_sp;
-            in.dt = dt_f32 ? load_bits(static_cast<const float *>(p.dt) + di)
-                           : load_bits(static_cast<const IT *>(p.dt) + di);
-            if (zs)
-                in.z = load_bits(zs + r * p.z_sr + h * p.z_sh + d_own);
-        }
+        const IT *xp = xs + (r * p.x_sr + h * p.x_sh + d_fetch);
+        const IT *zp = zsrc + (r * z_sr + h * z_sh + d_fetch);
+        in.x = *reinterpret_cast<const typename Inputs::Bits *>(xp);
+        in.z = *reinterpret_cast<const typename Inputs::Bits *>(zp);
+        const unsigned char *dp =
+            dts + static_cast<int64_t>(r * p.dt_sr + h * p.dt_sh + d_fetch * p.dt_sp) * dt_bytes;
+        in.dt_lo = *reinterpret_cast<const uint16_t *>(dp);
+        in.dt_hi = *reinterpret_cast<const uint16_t *>(dp + (dt_f32 ? 2 : 0));
+        // destination entry (the sequence index when there is no table)
+        const int32_t wi = wtab ? (w2d ? b * ws0 + t * ws1 : (first_row + t) * ws0) : 0;
+        const unsigned char *wp = wtb + static_cast<int64_t>(wi) * w_bytes;
+        in.ws_lo = *reinterpret_cast<const uint32_t *>(wp);
+        in.ws_hi = *reinterpret_cast<const uint32_t *>(wp + (wi64 ? 4 : 0));
     };
 
-    Inputs cur;
-    fetch(first_row, cur);
-    for (int64_t t = 0; t < len; t++) {
-        const int64_t r = first_row + t;
-        // the next token's inputs are requested before this token's stores,
-        // so waiting for them later does not wait for the stores
-        Inputs nxt;
-        if (MULTI && t + 1 < len)
-            fetch(r + 1, nxt);
-
+    // one token: update the tile with the inputs in `in`, store it, write y
+    auto process = [&](int32_t t, const Inputs &in) {
+        const int32_t r = first_row + t;
         float Bv[E], Cv[E];
 #pragma unroll
         for (int c = 0; c < NCH; c++)
 #pragma unroll
             for (int k = 0; k < IVEC; k++) {
-                Bv[c * IVEC + k] = widen(cur.b[c].v[k]);
-                Cv[c * IVEC + k] = widen(cur.c[c].v[k]);
+                Bv[c * IVEC + k] = word_elem(in.b[c], k);
+                Cv[c * IVEC + k] = word_elem(in.c[c], k);
             }
 
         // scalars of the lane's own row
-        const float xv = from_bits<IT>(cur.x);
-        float v = (dt_f32 ? __uint_as_float(cur.dt) : from_bits<IT>(cur.dt)) + bias_h;
+        const float xv = from_bits<IT>(in.x);
+        const float zv = from_bits<IT>(in.z);
+        const float dtv = dt_f32 ? __uint_as_float(uint32_t(in.dt_lo) | (uint32_t(in.dt_hi) << 16))
+                                 : from_bits<IT>(in.dt_lo);
+        float v = dtv + bias_h;
         if (flags & kSoftplus)
             v = softplus(v);
-        const float decay = expf(v * a_h);
+        const float decay = exp_hw(v * a_h);
         const float dtx = v * xv;
 
         // destination: the token's own entry of the destination table, else
         // of the read table, else slot b
-        const int64_t wslot =
-            wtab ? table_slot(wtab, w2d, wi64, ws0, ws1, b, first_row, t) : b;
+        const uint32_t wlo = __builtin_amdgcn_readfirstlane(in.ws_lo);
+        const uint32_t whi = __builtin_amdgcn_readfirstlane(in.ws_hi);
+        const int64_t wslot = !wtab ? b
+                              : wi64 ? static_cast<int64_t>((uint64_t(whi) << 32) | wlo)
+                                     : static_cast<int64_t>(static_cast<int32_t>(wlo));
         const bool store = !(flags & kDisable) && wslot != p.pad;
         ST *const wbase = pool + wslot * p.slot_stride + tile_off;
 
@@ -329,14 +418,38 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes) void ssu_kernel(const Params
         // y of the lane's own row
         if (owner) {
             float y = ysum + d_h * xv;
-            if (zs) {
-                const float zv = from_bits<IT>(cur.z);
-                y *= zv / (1.0f + expf(-zv));
-            }
+            if (zs)
+                y *= silu(zv);
             ys[r * p.out_sr + h * p.out_sh + d_own] = narrow<IT>(y);
         }
-        if (MULTI)
-            cur = nxt;
+    };
+
+    // Tokens alternate between two input buffers: the next token's inputs are
+    // requested before the current token's stores, and no register copy joins
+    // the two, so waiting for one buffer never waits for the other or for the
+    // stores issued in between.
+    Inputs in0, in1;
+    fetch(0, in0);
+    if (!MULTI) {
+        process(0, in0);
+        return;
+    }
+    // The vector-memory counter is in order: the scheduling barriers keep a
+    // buffer's loads issued after everything the current token waits for.
+    // The prefetch is unconditional (past the last token it reloads the last
+    // token's inputs, which stay unused), so no branch joins pending loads.
+    const int32_t last = len - 1;
+    for (int32_t t = 0; t < len; t += 2) {
+        __builtin_amdgcn_sched_barrier(0);
+        fetch(t + 1 < len ? t + 1 : last, in1);
+        __builtin_amdgcn_sched_barrier(0);
+        process(t, in0);
+        if (t + 1 >= len)
+            break;
+        __builtin_amdgcn_sched_barrier(0);
+        fetch(t + 2 < len ? t + 2 : last, in0);
+        __builtin_amdgcn_sched_barrier(0);
+        process(t + 1, in1);
     }
 }
 
