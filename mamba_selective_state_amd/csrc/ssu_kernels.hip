@@ -146,6 +146,31 @@ __device__ __forceinline__ float softplus(float v) {
 // z * sigmoid(z)
 __device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + exp_hw(-z)); }
 
+// Workgroups are dispatched to the 8 XCDs round-robin (id % 8), each XCD with
+// its own L2. Consecutive logical work units (the dim tiles of one head, the
+// heads of one group) read the same lines of x, dt, z, B and C. With a
+// cluster size K > 0, each block of 8K consecutive ids gives XCD x the K
+// consecutive logical units K x .. K x + K - 1 of that block (the last,
+// partial block maps to itself), so such units share an L2 while the grid
+// still sweeps the pool in order.
+#ifndef SSU_XCD_CLUSTER
+#define SSU_XCD_CLUSTER 16
+#endif
+constexpr int kXcds = 8;
+__device__ __forceinline__ int32_t xcd_clustered_index(int32_t id, int32_t n) {
+    constexpr int32_t K = SSU_XCD_CLUSTER;
+    if constexpr (K == 0) {
+        return id;
+    } else {
+        constexpr int32_t block = kXcds * K;
+        const int32_t m = id / block;
+        if ((m + 1) * block > n)
+            return id;
+        const int32_t r = id % block;
+        return m * block + (r % kXcds) * K + r / kXcds;
+    }
+}
+
 // Entry of a slot table naming sequence b's position t.
 __device__ __forceinline__ int64_t table_slot(const void *tab, bool two_d, bool i64, int32_t s0,
                                               int32_t s1, int32_t b, int32_t first_row, int32_t t) {
@@ -241,7 +266,7 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
     const int flags = p.flags;
 
     // workgroup -> (sequence, head, dim tile)
-    const int32_t wg = blockIdx.x;
+    const int32_t wg = xcd_clustered_index(blockIdx.x, gridDim.x);
     const int tile = wg % p.dim_tiles;
     const int32_t sh = wg / p.dim_tiles;
     const int h = sh % p.H;
