@@ -297,3 +297,20 @@ def test_python_wrapper_rejects_cpu_tensors():
     t = torch.zeros(2, 2, 2, 16)
     with pytest.raises(ValueError, match="GPU"):
         S.tensor_desc(t, torch.device("cuda", 0))
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(ImportError, match="not built"):
+        S.load_library(str(tmp_path / "libssu.so"))
+
+
+def test_package_never_touches_the_oracle():
+    """The product path has no CPU fallback: no package source names the
+    oracle or the workload generators."""
+    pkg = os.path.join(ROOT, "mamba_selective_state_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text, f
+                assert "workloads" not in text, f
