@@ -67,11 +67,19 @@ struct alignas(sizeof(T) * VEC) Pack {
 };
 
 // Streaming accesses of the state pool. Each state byte is touched once per
-// call, so the pool's loads and stores carry the non-temporal hint and do not
-// displace the per-row inputs (B and C are shared by a group's heads) from
-// the caches.
-#ifndef SSU_NT_STATE
-#define SSU_NT_STATE 1
+// call, so the pool's loads carry the non-temporal hint and do not displace
+// the per-row inputs (B and C are shared by a group's heads) from the caches.
+// The store hint is chosen per kernel: measured on this part, non-temporal
+// stores win for in-place read-modify-write streams, and plain stores for
+// write-mostly streams.
+#ifndef SSU_NT_LOAD
+#define SSU_NT_LOAD 1
+#endif
+#ifndef SSU_NT_STORE
+#define SSU_NT_STORE 1
+#endif
+#ifndef SSU_NT_STORE_MULTI
+#define SSU_NT_STORE_MULTI 1
 #endif
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -84,16 +92,16 @@ template <> struct RawOf<16> { using T = u32x4; };
 template <typename P>
 __device__ __forceinline__ P load_state(const P *src) {
     using R = typename RawOf<sizeof(P)>::T;
-    R r = SSU_NT_STATE ? __builtin_nontemporal_load(reinterpret_cast<const R *>(src))
-                       : *reinterpret_cast<const R *>(src);
+    R r = SSU_NT_LOAD ? __builtin_nontemporal_load(reinterpret_cast<const R *>(src))
+                      : *reinterpret_cast<const R *>(src);
     return __builtin_bit_cast(P, r);
 }
 
-template <typename P>
+template <bool NT, typename P>
 __device__ __forceinline__ void store_state(P *dst, const P &v) {
     using R = typename RawOf<sizeof(P)>::T;
     const R r = __builtin_bit_cast(R, v);
-    if (SSU_NT_STATE)
+    if constexpr (NT)
         __builtin_nontemporal_store(r, reinterpret_cast<R *>(dst));
     else
         *reinterpret_cast<R *>(dst) = r;
@@ -436,7 +444,8 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
                 ST *dst = wbase + static_cast<int64_t>(d) * N + col * VEC;
 #pragma unroll
                 for (int c = 0; c < NCH; c++)
-                    store_state(reinterpret_cast<SPack *>(dst + c * kLanesPerRow * VEC), S[q][c]);
+                    store_state<MULTI ? SSU_NT_STORE_MULTI : SSU_NT_STORE>(
+                        reinterpret_cast<SPack *>(dst + c * kLanesPerRow * VEC), S[q][c]);
             }
         });
 
