@@ -131,3 +131,86 @@ def run(case):
                 written[dst] = True
     y = from_f64(Y, io).reshape(x.shape)
     return {"y": y, "y64": Y.reshape(x.shape), "state": new_pool, "written": written}
+
+
+def run_replay(case):
+    """ReplaySSM decode step in float64 (readings R16..R19 of the C oracle):
+    a flush (h + 1 == L) folds the buffered steps and the current one into the
+    checkpoint one plain update after the other; any other step computes y
+    from the checkpoint and the buffer with the unrolled window and appends
+    its inputs at entry h."""
+    sd, io = case["state_dtype"], case["io_dtype"]
+    dtd = case.get("dt_dtype", io)
+    pool = np.asarray(case["state"])
+    slots, H, P, N = pool.shape
+    L = int(case["L"])
+    X = to_f64(case["x"], io)
+    R = X.shape[0]
+    dt = np.asarray(case["dt"])
+    per_head = dt.ndim == 2
+    DT = to_f64(dt, dtd)
+    Bm, Cm = to_f64(case["B"], io), to_f64(case["C"], io)
+    G = Bm.shape[1]
+    Z = None if case.get("z") is None else to_f64(case["z"], io)
+    A = np.asarray(case["A"], np.float64)
+    Dv = None if case.get("D") is None else np.asarray(case["D"], np.float64)
+    bias = None if case.get("dt_bias") is None else np.asarray(case["dt_bias"], np.float64)
+    pad = int(case.get("pad_slot_id", -1))
+    disable = bool(case.get("disable_state_update", False))
+    tab = case.get("state_batch_indices")
+    bx, bdt, bB = (np.asarray(case["buf_x"]), np.asarray(case["buf_dt"]),
+                   np.asarray(case["buf_B"]))
+    out = {"state": pool.copy(), "buf_x": bx.copy(), "buf_dt": bdt.copy(), "buf_B": bB.copy(),
+           "written": np.zeros(slots, dtype=bool)}
+    Y = np.zeros((R, H, P))
+
+    def proc(v, h):
+        if bias is not None:
+            v = v + bias[h]
+        if case.get("dt_softplus", False):
+            v = np.where(v > 20.0, v, np.log1p(np.exp(np.minimum(v, 20.0))))
+        return v
+
+    for b in range(R):
+        s = b if tab is None else int(np.asarray(tab)[b])
+        hb = int(np.asarray(case["buf_len"])[b])
+        for h in range(H):
+            g = h // (H // G)
+            # the steps' inputs: buffered entries, then the current step
+            xs = [to_f64(bx[s, j, h], io) for j in range(hb)] + [X[b, h]]
+            if per_head:
+                dts = [np.full(P, to_f64(bdt[s, j, h], dtd)) for j in range(hb)] + \
+                      [np.full(P, DT[b, h])]
+            else:
+                dts = [to_f64(bdt[s, j, h], dtd) for j in range(hb)] + [DT[b, h]]
+            Bs = [to_f64(bB[s, j, g], io) for j in range(hb)] + [Bm[b, g]]
+            steps = [proc(d, h) for d in dts]
+            alphas = [np.exp(st * A[h]) for st in steps]
+            S = np.zeros((P, N)) if s == pad else to_f64(pool[s, h], sd)
+            if hb + 1 == L:
+                for j in range(hb + 1):
+                    S = S * alphas[j][:, None] + np.outer(steps[j] * xs[j], Bs[j])
+                    if j == hb:
+                        y = S @ Cm[b, g]
+                    S = to_f64(from_f64(S, sd), sd)
+                if s != pad and not disable:
+                    out["state"][s, h] = from_f64(S, sd)
+                    out["written"][s] = True
+            else:
+                gamma = np.prod(alphas, axis=0)
+                y = gamma * (S @ Cm[b, g])
+                for j in range(hb + 1):
+                    tail = np.prod(alphas[j + 1:], axis=0) if j < hb else np.ones(P)
+                    y = y + steps[j] * xs[j] * tail * (Bs[j] @ Cm[b, g])
+                if s != pad and not disable:
+                    out["buf_x"][s, hb, h] = np.asarray(case["x"])[b, h]
+                    out["buf_dt"][s, hb, h] = dt[b, h]
+                    out["buf_B"][s, hb, g] = np.asarray(case["B"])[b, g]
+            if Dv is not None:
+                y = y + Dv[h] * X[b, h]
+            if Z is not None:
+                y = y * (Z[b, h] / (1.0 + np.exp(-Z[b, h])))
+            Y[b, h] = y
+    out["y"] = from_f64(Y, io)
+    out["y64"] = Y
+    return out

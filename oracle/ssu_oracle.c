@@ -471,3 +471,206 @@ int oracle_ssu(const oracle_args *a, char *err, int errlen)
     free(S);
     return 0;
 }
+
+/* ---- ReplaySSM decode: checkpoint plus input buffer
+ *
+ * ReplaySSM article (lpnh.cn), section "核心做法" (core method) and its
+ * minimal pseudocode: the state is kept as a checkpoint plus a buffer of the
+ * last steps' inputs. A step appends its inputs (v, Δ, k) = (x, dt, B) to the
+ * buffer and computes its output from the checkpoint and the buffer without
+ * writing the state; once every L steps a flush folds the buffer into the
+ * checkpoint and writes it back. With L = 1 every step is a flush and the step
+ * is the plain update ("the kernel degenerates to the baseline").
+ *
+ * Readings (the pages leave them open):
+ *  R16 the buffer holds the raw step inputs (x, dt and B in their own
+ *      dtypes); the step that fills it (h + 1 == L, h = entries before the
+ *      step) is the flush: the buffered steps and the current one are applied
+ *      to the checkpoint one after the other exactly as the plain update
+ *      does (state rounded to the state dtype after each), y comes from the
+ *      folded state, and the checkpoint is stored;
+ *  R17 any other step writes its inputs to entry h of the slot's buffer and
+ *      computes, per dim row d, with a_i = exp(dt'_i A[h]) and j, i over the
+ *      buffered steps and the current one (index h):
+ *        y = (prod_i a_i) (S_ckpt . C) + sum_j dt'_j x_j (prod_{i>j} a_i) (B_j . C)
+ *            + D x, times silu(z)
+ *      (the unrolled window of the same section; output-only decode);
+ *  R18 h is the caller's per-sequence buffer pointer (the article moves a
+ *      buffer pointer on commit); the caller resets it after a flush;
+ *  R19 one token per sequence, the checkpoint slot is read and written in
+ *      place; the pad id reads a zero checkpoint and writes nothing;
+ *      disable_state_update writes neither checkpoint nor buffer.
+ */
+typedef struct {
+    oracle_args base; /* one token per sequence; rtab 1-D or NULL; no wtab */
+    int64_t L;
+    const void *bx_in;  /* [slots, L, H, P] io dtype */
+    void *bx_out;
+    const void *bdt_in; /* [slots, L, H, P] (or [slots, L, H] when dt is per head), dt dtype */
+    void *bdt_out;
+    const void *bB_in;  /* [slots, L, G, N] io dtype */
+    void *bB_out;
+    const int64_t *buf_len; /* [nseq] entries in each sequence's buffer */
+} oracle_replay_args;
+
+/* dt' of one buffered or current step, one dim row */
+static float processed_dt(const oracle_args *a, float raw, int64_t h)
+{
+    float v = raw;
+    if (a->dt_bias)
+        v = v + a->dt_bias[h];
+    if (a->dt_softplus)
+        v = oracle_softplus(v);
+    return v;
+}
+
+static void copy_elem(void *dst, const void *src, int32_t dtype, int64_t di, int64_t si)
+{
+    if (dtype == OR_F32)
+        ((float *)dst)[di] = ((const float *)src)[si];
+    else
+        ((uint16_t *)dst)[di] = ((const uint16_t *)src)[si];
+}
+
+int oracle_replay(const oracle_replay_args *ra, char *err, int errlen)
+{
+    const oracle_args *a = &ra->base;
+    const int64_t H = a->H, P = a->P, N = a->N, G = a->G, L = ra->L;
+    const int64_t per_group = H / G, tile = P * N;
+    if (a->layout != OR_ONE_TOKEN || a->wtab.data || a->acc || L < 1 || H % G) {
+        set_err(err, errlen, "replay takes one token per sequence, no destination table, L >= 1%lld%lld", 0, 0);
+        return 1;
+    }
+    if (a->rtab.data && a->rtab.ndim != 1) {
+        set_err(err, errlen, "replay takes a 1-D slot table%lld%lld", 0, 0);
+        return 1;
+    }
+    const int64_t nseq = a->R;
+    const int64_t dtw = a->dt_per_head ? 1 : P; /* dt values per (step, head) */
+    /* slots in range, at most one sequence per slot, 0 <= h < L */
+    for (int64_t b = 0; b < nseq; b++) {
+        const int64_t s = a->rtab.data ? a->rtab.data[b] : b;
+        const int64_t h = ra->buf_len[b];
+        if (h < 0 || h >= L) {
+            set_err(err, errlen, "buffer length %lld of sequence %lld outside [0, L)", (long long)h, (long long)b);
+            return 1;
+        }
+        if (s == a->pad)
+            continue;
+        if (s < 0 || s >= a->slots) {
+            set_err(err, errlen, "slot %lld of sequence %lld outside the pool", (long long)s, (long long)b);
+            return 1;
+        }
+        for (int64_t b2 = 0; b2 < b; b2++)
+            if ((a->rtab.data ? a->rtab.data[b2] : b2) == s) {
+                set_err(err, errlen, "slot %lld used by two sequences (second: %lld)", (long long)s, (long long)b);
+                return 1;
+            }
+    }
+    float *S = (float *)malloc((size_t)tile * sizeof(float));
+    float *alpha = (float *)malloc((size_t)L * sizeof(float));
+    float *dtp = (float *)malloc((size_t)L * sizeof(float));
+    float *xs = (float *)malloc((size_t)L * sizeof(float));
+    for (int64_t b = 0; b < nseq; b++) {
+        const int64_t s = a->rtab.data ? a->rtab.data[b] : b;
+        const int64_t h = ra->buf_len[b];
+        const int pad = s == a->pad;
+        if (a->read_slot)
+            a->read_slot[b] = s;
+        for (int64_t hd = 0; hd < H; hd++) {
+            const int64_t g = hd / per_group;
+            /* inputs of step j (j < h buffered, j == h current) */
+#define RX(j, d) ((j) < h ? load_as_f32(ra->bx_in, a->io_dtype, ((s * L + (j)) * H + hd) * P + (d)) \
+                          : load_as_f32(a->x, a->io_dtype, (b * H + hd) * P + (d)))
+#define RDT(j, d) ((j) < h ? load_as_f32(ra->bdt_in, a->dt_dtype, ((s * L + (j)) * H + hd) * dtw + (a->dt_per_head ? 0 : (d))) \
+                           : load_as_f32(a->dt, a->dt_dtype, (b * H + hd) * dtw + (a->dt_per_head ? 0 : (d))))
+#define RB(j, n) ((j) < h ? load_as_f32(ra->bB_in, a->io_dtype, ((s * L + (j)) * G + g) * N + (n)) \
+                          : load_as_f32(a->B, a->io_dtype, (b * G + g) * N + (n)))
+            for (int64_t e = 0; e < tile; e++)
+                S[e] = pad ? 0.0f : load_as_f32(a->pool_in, a->state_dtype, (s * H + hd) * tile + e);
+            if (h + 1 == L) {
+                /* flush: fold the buffered steps and the current one into the
+                 * checkpoint, one plain update after the other */
+                for (int64_t j = 0; j <= h; j++) {
+                    for (int64_t d = 0; d < P; d++) {
+                        const float v = processed_dt(a, RDT(j, d), hd);
+                        const float xv = RX(j, d);
+                        const float decay = expf(v * a->A[hd]);
+                        const float dtx = v * xv;
+                        float *Sd = S + d * N;
+                        for (int64_t n = 0; n < N; n++)
+                            Sd[n] = Sd[n] * decay + dtx * RB(j, n);
+                        if (j == h) {
+                            float y = 0.0f;
+                            for (int64_t n = 0; n < N; n++)
+                                y = y + Sd[n] * load_as_f32(a->C, a->io_dtype, (b * G + g) * N + n);
+                            if (a->D)
+                                y = y + a->D[hd] * xv;
+                            if (a->z)
+                                y = y * silu(load_as_f32(a->z, a->io_dtype, (b * H + hd) * P + d));
+                            store_from_f32(a->out, a->io_dtype, (b * H + hd) * P + d, y);
+                        }
+                    }
+                    for (int64_t e = 0; e < tile; e++)
+                        S[e] = through_dtype(a->state_dtype, S[e]);
+                }
+                if (!pad && !a->disable) {
+                    for (int64_t e = 0; e < tile; e++)
+                        store_from_f32(a->pool_out, a->state_dtype, (s * H + hd) * tile + e, S[e]);
+                    if (a->written)
+                        a->written[s] = 1;
+                }
+            } else {
+                /* output-only: y from the checkpoint and the buffer */
+                for (int64_t d = 0; d < P; d++) {
+                    for (int64_t j = 0; j <= h; j++) {
+                        dtp[j] = processed_dt(a, RDT(j, d), hd);
+                        alpha[j] = expf(dtp[j] * a->A[hd]);
+                        xs[j] = RX(j, d);
+                    }
+                    float u = 0.0f; /* S_ckpt . C */
+                    for (int64_t n = 0; n < N; n++)
+                        u = u + S[d * N + n] * load_as_f32(a->C, a->io_dtype, (b * G + g) * N + n);
+                    float gamma = 1.0f;
+                    for (int64_t j = 0; j <= h; j++)
+                        gamma = gamma * alpha[j];
+                    float y = gamma * u;
+                    for (int64_t j = 0; j <= h; j++) {
+                        float tail = 1.0f; /* prod_{i > j} a_i */
+                        for (int64_t i = j + 1; i <= h; i++)
+                            tail = tail * alpha[i];
+                        float w = 0.0f; /* B_j . C */
+                        for (int64_t n = 0; n < N; n++)
+                            w = w + RB(j, n) * load_as_f32(a->C, a->io_dtype, (b * G + g) * N + n);
+                        y = y + dtp[j] * xs[j] * tail * w;
+                    }
+                    if (a->D)
+                        y = y + a->D[hd] * xs[h];
+                    if (a->z)
+                        y = y * silu(load_as_f32(a->z, a->io_dtype, (b * H + hd) * P + d));
+                    store_from_f32(a->out, a->io_dtype, (b * H + hd) * P + d, y);
+                }
+                /* append the step's inputs at entry h */
+                if (!pad && !a->disable) {
+                    for (int64_t d = 0; d < P; d++)
+                        copy_elem(ra->bx_out, a->x, a->io_dtype, ((s * L + h) * H + hd) * P + d,
+                                  (b * H + hd) * P + d);
+                    for (int64_t d = 0; d < dtw; d++)
+                        copy_elem(ra->bdt_out, a->dt, a->dt_dtype, ((s * L + h) * H + hd) * dtw + d,
+                                  (b * H + hd) * dtw + d);
+                    for (int64_t n = 0; n < N; n++)
+                        copy_elem(ra->bB_out, a->B, a->io_dtype, ((s * L + h) * G + g) * N + n,
+                                  (b * G + g) * N + n);
+                }
+            }
+#undef RX
+#undef RDT
+#undef RB
+        }
+    }
+    free(S);
+    free(alpha);
+    free(dtp);
+    free(xs);
+    return 0;
+}

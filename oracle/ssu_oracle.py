@@ -226,3 +226,94 @@ def _run(oracle, case):
     y = out.reshape(x.shape) if dense else out
     return {"y": y, "state": pool_out, "written": written.astype(bool),
             "read_slot": read_slot[:nseq]}
+
+
+# ---------------------------------------------------------------- ReplaySSM
+
+class _ReplayArgs(ctypes.Structure):
+    _fields_ = [("base", _Args), ("L", ctypes.c_int64),
+                ("bx_in", ctypes.c_void_p), ("bx_out", ctypes.c_void_p),
+                ("bdt_in", ctypes.c_void_p), ("bdt_out", ctypes.c_void_p),
+                ("bB_in", ctypes.c_void_p), ("bB_out", ctypes.c_void_p),
+                ("buf_len", ctypes.c_void_p)]
+
+
+def run_replay(case, oracle=None):
+    """ReplaySSM decode step (oracle_replay in ssu_oracle.c). The case holds
+    the one-token update's inputs (state = checkpoint pool, a 1-D slot table
+    or none, no destination table) plus
+      L         buffer length
+      buf_x     [slots, L, H, P]        io dtype
+      buf_dt    [slots, L, H, P] or [slots, L, H]  dt dtype
+      buf_B     [slots, L, G, N]        io dtype
+      buf_len   [batch] integer: entries in each sequence's buffer (< L)
+    Returns dict(y, state, buf_x, buf_dt, buf_B, written)."""
+    orc = oracle or default()
+    lib = orc.lib
+    if not hasattr(lib, "_replay_ready"):
+        lib.oracle_replay.argtypes = [ctypes.POINTER(_ReplayArgs), ctypes.c_char_p, ctypes.c_int]
+        lib.oracle_replay.restype = ctypes.c_int
+        lib._replay_ready = True
+    sd, io = case["state_dtype"], case["io_dtype"]
+    dtd = case.get("dt_dtype", io)
+    state = _arr(case["state"], _np_dtype(sd))
+    slots, H, P, N = state.shape
+    x = _arr(case["x"], _np_dtype(io))
+    if x.ndim != 3 or case.get("cu_seqlens") is not None or \
+            case.get("num_accepted_tokens") is not None or \
+            case.get("dst_state_batch_indices") is not None:
+        raise OracleError("replay takes x [batch, heads, dim], one slot table and nothing else")
+    R = x.shape[0]
+    dt = np.asarray(case["dt"])
+    dt_per_head = dt.ndim == 2
+    dtr = _arr(dt, _np_dtype(dtd))
+    Bm = _arr(case["B"], _np_dtype(io))
+    G = Bm.shape[1]
+    Cm = _arr(case["C"], _np_dtype(io))
+    z = case.get("z")
+    z = None if z is None else _arr(z, _np_dtype(io))
+    A = _arr(case["A"], np.float32)
+    D = case.get("D")
+    D = None if D is None else _arr(D, np.float32)
+    bias = case.get("dt_bias")
+    bias = None if bias is None else _arr(bias, np.float32)
+    L = int(case["L"])
+    bx = _arr(case["buf_x"], _np_dtype(io))
+    bdt = _arr(case["buf_dt"], _np_dtype(dtd))
+    bB = _arr(case["buf_B"], _np_dtype(io))
+    if bx.shape != (slots, L, H, P) or bB.shape != (slots, L, G, N) or \
+            bdt.shape != ((slots, L, H) if dt_per_head else (slots, L, H, P)):
+        raise OracleError("buffer shapes do not match the pool and L")
+    blen = np.ascontiguousarray(case["buf_len"], dtype=np.int64)
+    keep = []
+    args = _ReplayArgs()
+    base = args.base
+    pool_out = state.copy()
+    out = np.zeros((R, H, P), dtype=_np_dtype(io))
+    written = np.zeros(slots, dtype=np.uint8)
+    bx_out, bdt_out, bB_out = bx.copy(), bdt.copy(), bB.copy()
+    base.pool_in, base.pool_out = _ptr(state), _ptr(pool_out)
+    base.state_dtype = DTYPES[sd]
+    base.slots, base.H, base.P, base.N, base.G = slots, H, P, N, G
+    base.R, base.io_dtype = R, DTYPES[io]
+    base.x, base.dt = _ptr(x), _ptr(dtr)
+    base.dt_dtype, base.dt_per_head = DTYPES[dtd], int(dt_per_head)
+    base.A, base.B, base.C = _ptr(A), _ptr(Bm), _ptr(Cm)
+    base.D, base.z, base.dt_bias = _ptr(D), _ptr(z), _ptr(bias)
+    base.dt_softplus = int(bool(case.get("dt_softplus", False)))
+    base.layout, base.steps, base.nseq = ONE_TOKEN, 0, R
+    base.rtab = _table(case.get("state_batch_indices"), keep)
+    base.wtab = _table(None, keep)
+    base.pad = int(case.get("pad_slot_id", -1))
+    base.disable = int(bool(case.get("disable_state_update", False)))
+    base.out, base.written = _ptr(out), _ptr(written)
+    args.L = L
+    args.bx_in, args.bx_out = _ptr(bx), _ptr(bx_out)
+    args.bdt_in, args.bdt_out = _ptr(bdt), _ptr(bdt_out)
+    args.bB_in, args.bB_out = _ptr(bB), _ptr(bB_out)
+    args.buf_len = _ptr(blen)
+    err = ctypes.create_string_buffer(256)
+    if lib.oracle_replay(ctypes.byref(args), err, 256):
+        raise OracleError(err.value.decode())
+    return {"y": out, "state": pool_out, "buf_x": bx_out, "buf_dt": bdt_out, "buf_B": bB_out,
+            "written": written.astype(bool)}

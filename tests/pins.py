@@ -523,9 +523,168 @@ def pin_golden_mate_examples(orc):
         assert np.array_equal(o["state"][untouched], c["state"][untouched]), spec["name"]
 
 
+# ---------------------------------------------------------------- ReplaySSM
+
+def _replay_case(L, buf_len, sd="f32", io="f32", **kw):
+    base = dict(batch=4, heads=4, dim=8, dstate=16, groups=2, slots=8)
+    base.update(kw)
+    return W.replay(L=L, buf_len=buf_len, state_dtype=sd, io=io, **base)
+
+
+def _as_ssu(case):
+    return {k: v for k, v in case.items() if k not in ("L", "buf_x", "buf_dt", "buf_B", "buf_len")}
+
+
+def pin_replay_L1_is_plain_update(orc):
+    """L = 1: every step is a flush with an empty buffer, so the step is the
+    plain update bit for bit (ReplaySSM article, "核心做法": the kernel
+    degenerates to the baseline) - y, checkpoint, and untouched buffers."""
+    from oracle import ssu_oracle
+    for sd in ("f32", "bf16"):
+        c = _replay_case(1, 0, sd=sd, io="bf16")
+        r = ssu_oracle.run_replay(c, orc)
+        p = orc.run(_as_ssu(c))
+        assert np.array_equal(r["y"], p["y"]) and np.array_equal(r["state"], p["state"]), sd
+        assert np.array_equal(r["buf_x"], c["buf_x"]) and np.array_equal(r["buf_B"], c["buf_B"])
+
+
+def _replay_window(orc, L, sd, io, steps_inputs, case0):
+    """Run a window of L replay steps from an empty buffer (the caller moves
+    the pointer 0, 1, .., L-1) and the same steps as chained plain updates."""
+    from oracle import ssu_oracle
+    c = dict(case0)
+    plain = _as_ssu(case0)
+    ys_r, ys_p = [], []
+    for t, inp in enumerate(steps_inputs):
+        c.update(inp)
+        c["buf_len"] = np.full(len(c["buf_len"]), t, np.int32)
+        r = ssu_oracle.run_replay(c, orc)
+        c.update(state=r["state"], buf_x=r["buf_x"], buf_dt=r["buf_dt"], buf_B=r["buf_B"])
+        ys_r.append(r["y"])
+        plain.update(inp)
+        p = orc.run(plain)
+        plain["state"] = p["state"]
+        ys_p.append(p["y"])
+    return c, plain, ys_r, ys_p
+
+
+def _fresh_inputs(case, seed, n):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        inp = {}
+        for k in ("x", "dt", "B", "C", "z"):
+            a = case[k]
+            dtype = case.get("dt_dtype", case["io_dtype"]) if k == "dt" else case["io_dtype"]
+            inp[k] = W.to_storage(rng.standard_normal(a.shape, dtype=np.float32), dtype)
+        out.append(inp)
+    return out
+
+
+def pin_replay_flush_is_chain(orc):
+    """A window of L steps: after the flush the checkpoint equals L chained
+    plain updates bit for bit (the fold replays the same steps); before it,
+    the checkpoint is untouched and each step's y (from checkpoint + buffer,
+    the unrolled window of "核心做法") equals the plain update's y to fp32
+    accuracy."""
+    for sd in ("f32", "f16"):
+        L = 5
+        c0 = _replay_case(L, 0, sd=sd, io="f32")
+        inputs = _fresh_inputs(c0, 3, L)
+        c, plain, ys_r, ys_p = _replay_window(orc, L, sd, "f32", inputs, c0)
+        live = np.asarray(c0["state_batch_indices"])
+        assert np.array_equal(c["state"][live], plain["state"][live]), sd
+        for t in range(L):
+            scale = np.abs(ys_p[t]).max() + 1.0
+            tol = 1e-5 if sd == "f32" else 2e-2
+            assert np.abs(ys_r[t].astype(np.float64) - ys_p[t]).max() <= tol * scale, (sd, t)
+
+
+def pin_replay_nonflush_writes_entry_only(orc):
+    """A step that does not fill the buffer leaves the checkpoint pool
+    byte-identical and writes exactly entry h of its slot's buffer with the
+    step's raw inputs."""
+    from oracle import ssu_oracle
+    c = _replay_case(6, [0, 2, 4, 1], sd="bf16", io="bf16")
+    r = ssu_oracle.run_replay(c, orc)
+    assert np.array_equal(r["state"], c["state"]) and not r["written"].any()
+    bx, bB, bdt = c["buf_x"].copy(), c["buf_B"].copy(), c["buf_dt"].copy()
+    for b, s in enumerate(c["state_batch_indices"]):
+        h = c["buf_len"][b]
+        bx[s, h] = c["x"][b]
+        bdt[s, h] = c["dt"][b]
+        bB[s, h] = c["B"][b]
+    assert np.array_equal(r["buf_x"], bx) and np.array_equal(r["buf_B"], bB)
+    assert np.array_equal(r["buf_dt"], bdt)
+
+
+def pin_replay_zero_checkpoint(orc):
+    """Pad slot (zero checkpoint) and an empty buffer: y is the output-only
+    closed form dt' x (B . C) + D x, gated, and nothing is written."""
+    from oracle import ssu_oracle
+    c = _replay_case(4, 0, sd="f32", io="f32")
+    c["state_batch_indices"] = np.array([0, -1, 2, -1], np.int32)
+    r = ssu_oracle.run_replay(c, orc)
+    ref, scale = _zero_state_expected(_as_ssu(c), [1, 3])
+    assert np.all(np.abs(r["y"][[1, 3]] - ref) <= 40 * U32 * scale + 1e-30)
+    for s in (1, 3, 4, 5, 6, 7):
+        assert np.array_equal(r["buf_x"][s], c["buf_x"][s])
+
+
+def pin_replay_disable(orc):
+    """disable_state_update writes neither the checkpoint nor the buffer; y
+    is unchanged."""
+    from oracle import ssu_oracle
+    c = _replay_case(3, [2, 1, 0, 2], sd="f32", io="bf16")
+    r1 = ssu_oracle.run_replay(c, orc)
+    r2 = ssu_oracle.run_replay(dict(c, disable_state_update=True), orc)
+    assert np.array_equal(r1["y"], r2["y"])
+    for k in ("state", "buf_x", "buf_dt", "buf_B"):
+        assert np.array_equal(r2[k], c[k if k != "state" else "state"]), k
+
+
+def pin_replay_brute_force(orc, combos=24, seed=11):
+    """The replay step against the independent float64 version on tiny
+    shapes over L, buffer pointers, dtypes and options."""
+    from oracle import ssu_oracle
+    rng = np.random.default_rng(seed)
+    for k in range(combos):
+        L = int(rng.choice([1, 2, 3, 5]))
+        sd = ["f32", "f16", "bf16"][rng.integers(3)]
+        io = ["f32", "bf16"][rng.integers(2)]
+        c = W.replay(seed=int(rng.integers(1 << 30)), batch=3, heads=2, dim=4, dstate=8, groups=1,
+                     slots=5, L=L, state_dtype=sd, io=io, dt_per_head=bool(rng.integers(2)),
+                     buf_len=rng.integers(0, L, 3))
+        if rng.integers(2):
+            c["dt_bias"], c["dt_softplus"] = None, False
+            dtd = c.get("dt_dtype", io)
+            c["dt"] = W.to_storage(rng.random(np.shape(c["dt"]), dtype=np.float32) * 0.1, dtd)
+            c["buf_dt"] = W.to_storage(rng.random(np.shape(c["buf_dt"]), dtype=np.float32) * 0.1,
+                                       dtd)
+        if rng.integers(3) == 0:
+            c["z"] = None
+        o = ssu_oracle.run_replay(c, orc)
+        b = brute64.run_replay(c)
+        for key in ("buf_x", "buf_dt", "buf_B"):
+            assert np.array_equal(o[key], b[key]), (k, key)
+        assert np.array_equal(o["written"], b["written"]), k
+        S_o, S_b = f64(o["state"], sd), f64(b["state"], sd)
+        tol = (64 * U32 * (np.abs(S_b) + 1)) if sd == "f32" else \
+            (2 * ulp16(S_b, sd) + 64 * U32 * (np.abs(S_b) + 1))
+        assert np.all(np.abs(S_o - S_b) <= tol), (k, sd, L)
+        y_o = f64(o["y"], io)
+        tol = 64 * U32 * (np.abs(b["y64"]) + 8) * 8 * L
+        if io != "f32":
+            tol = tol + 2 * ulp16(b["y64"], io)
+        assert np.all(np.abs(y_o - b["y64"]) <= tol), (k, io, L)
+
+
 ALL = [pin_golden_mate_examples, pin_f16_decode_exhaustive, pin_f16_encode, pin_bf16_roundtrip, pin_softplus,
        pin_dt_zero_keeps_state, pin_b_zero_pure_decay, pin_zero_state_closed_form,
        pin_c_zero_and_z_zero, pin_mtp_equals_chained_calls, pin_unrolled_window,
        pin_pad_slot_untouched, pin_disable_keeps_pool, pin_flat_equals_2d, pin_strided_literal,
        pin_default_destination, pin_empty_sequences, pin_accepted_floor,
-       pin_pad_destination_mid_sequence, pin_dt_per_head_broadcast, pin_groups, pin_brute_force]
+       pin_pad_destination_mid_sequence, pin_dt_per_head_broadcast, pin_groups, pin_brute_force,
+       pin_replay_L1_is_plain_update, pin_replay_flush_is_chain,
+       pin_replay_nonflush_writes_entry_only, pin_replay_zero_checkpoint, pin_replay_disable,
+       pin_replay_brute_force]

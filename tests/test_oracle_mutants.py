@@ -11,11 +11,13 @@ from oracle import ssu_oracle
 # (name, text in oracle/ssu_oracle.c, replacement)
 MUTANTS = [
     ("drop_dt_bias", "v = v + a->dt_bias[h]; /* R3 */", "v = v;"),
-    ("softplus_is_exp", "v = oracle_softplus(v);", "v = expf(v);"),
+    ("softplus_is_exp", "if (a->dt_softplus)\n                        v = oracle_softplus(v);",
+     "if (a->dt_softplus)\n                        v = expf(v);"),
     ("softplus_threshold", "if (v > 20.0f)", "if (v > 0.0f)"),
     ("decay_sign", "expf(v * a->A[h])", "expf(-v * a->A[h])"),
     ("decay_without_dt", "expf(v * a->A[h])", "expf(a->A[h])"),
-    ("rank1_without_dt", "const float dtx = v * xv;", "const float dtx = xv;"),
+    ("rank1_without_dt", "const float dtx = v * xv;\n                    float *Sd = S + d * N;\n                    for (int64_t n = 0; n < N; n++) {",
+     "const float dtx = xv;\n                    float *Sd = S + d * N;\n                    for (int64_t n = 0; n < N; n++) {"),
     ("decay_after_add", "Sd[n] = Sd[n] * decay + dtx * bn;", "Sd[n] = (Sd[n] + dtx * bn) * decay;"),
     ("readout_uses_B", "const float cn = load_as_f32(a->C,", "const float cn = load_as_f32(a->B,"),
     ("drop_D", "y = y + a->D[h] * xv;", "y = y;"),
@@ -37,7 +39,22 @@ MUTANTS = [
     ("disable_ignored",
      "if (a->disable)\n                    continue;\n                int64_t wslot;",
      "int64_t wslot;"),
-    ("carry_not_rounded", "S[e] = through_dtype(a->state_dtype, S[e]);", "S[e] = S[e];"),
+    ("carry_not_rounded", "/* R5: carry what the state dtype holds */\n                for (int64_t e = 0; e < tile; e++)\n                    S[e] = through_dtype(a->state_dtype, S[e]);",
+     "/* R5: carry what the state dtype holds */"),
+    # ReplaySSM decode
+    ("replay_never_flushes", "if (h + 1 == L) {", "if (h == L) {"),
+    ("replay_flush_not_rounded",
+     "for (int64_t e = 0; e < tile; e++)\n                        S[e] = through_dtype(a->state_dtype, S[e]);\n                }",
+     "}"),
+    ("replay_gamma_without_current",
+     "for (int64_t j = 0; j <= h; j++)\n                        gamma = gamma * alpha[j];",
+     "for (int64_t j = 0; j < h; j++)\n                        gamma = gamma * alpha[j];"),
+    ("replay_tail_includes_own_decay", "for (int64_t i = j + 1; i <= h; i++)", "for (int64_t i = j; i <= h; i++)"),
+    ("replay_weight_without_dt", "y = y + dtp[j] * xs[j] * tail * w;", "y = y + xs[j] * tail * w;"),
+    ("replay_readout_uses_B", "u = u + S[d * N + n] * load_as_f32(a->C,", "u = u + S[d * N + n] * load_as_f32(a->B,"),
+    ("replay_append_skipped_x",
+     "copy_elem(ra->bx_out, a->x, a->io_dtype, ((s * L + h) * H + hd) * P + d,",
+     "copy_elem(ra->bx_out, a->x, a->io_dtype, ((s * L + h) * H + hd) * P + 0,"),
     ("default_dst_is_seq",
      "a->wtab.data ? &a->wtab : (a->rtab.data ? &a->rtab : NULL)", "a->wtab.data ? &a->wtab : NULL"),
     ("flat_write_b_plus_t", "int64_t i = tb->ndim == 1 ? bos + t :", "int64_t i = tb->ndim == 1 ? b + t :"),

@@ -252,3 +252,33 @@ def varlen(seed=4, nseq=512, max_len=8, heads=64, dim=64, dstate=128, groups=1,
 
 BUILDERS = {"one_token_tiny": one_token_tiny, "decode": decode, "decode_pad": decode_pad,
             "mtp": mtp, "varlen": varlen}
+
+
+def replay(seed=5, batch=256, heads=128, dim=64, dstate=128, groups=8, slots=512, L=16,
+           state_dtype="f32", io="bf16", buf_len=None, dt_per_head=False, index_dtype=np.int32,
+           fill_unread=True):
+    """A ReplaySSM decode step on the decode workload's layer: a checkpoint
+    pool, one slot per sequence (the first `batch` of a permutation), and per
+    slot an input buffer of L entries (x, dt, B as earlier steps would have
+    appended them, drawn like the current step's inputs). buf_len (entries
+    already buffered per sequence) defaults to U{0..L-1}."""
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(slots)[:batch].astype(index_dtype)
+    c = {"state_dtype": state_dtype}
+    c["state"] = _pool(rng, slots, heads, dim, dstate, state_dtype,
+                       perm if fill_unread else None)
+    c.update(_layer(rng, batch, heads, dim, dstate, groups, io=io, dt_dtype=io,
+                    dt_per_head=dt_per_head))
+    c.update(state_batch_indices=perm, dst_state_batch_indices=None, pad_slot_id=-1,
+             disable_state_update=False, cu_seqlens=None, num_accepted_tokens=None)
+    c["L"] = int(L)
+    c["buf_x"] = _normal(rng, (slots, L, heads, dim), io)
+    c["buf_dt"] = _normal(rng, (slots, L, heads) if dt_per_head else (slots, L, heads, dim), io)
+    c["buf_B"] = _normal(rng, (slots, L, groups, dstate), io)
+    if buf_len is None:
+        buf_len = rng.integers(0, L, batch)
+    c["buf_len"] = np.broadcast_to(np.asarray(buf_len, dtype=np.int32), (batch,)).copy()
+    return c
+
+
+BUILDERS["replay"] = replay
