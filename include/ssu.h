@@ -162,6 +162,42 @@ SSU_API ssu_status_t ssu_plan(const ssu_plan_desc_t *desc, ssu_plan_info_t *info
  * never reads device memory on the host. Works without a prior ssu_plan. */
 SSU_API ssu_status_t ssu_update(const ssu_args_t *args, void *stream);
 
+/* ReplaySSM decode (ReplaySSM article, lpnh.cn, section "核心做法" and its
+ * minimal pseudocode): the state of a slot is its checkpoint (the pool entry)
+ * plus a buffer of up to L past steps' inputs. For each sequence b with slot
+ * s and h = buf_len[b] entries already buffered (0 <= h < L):
+ *   - if h + 1 == L (the step fills the buffer: a flush), the buffered steps
+ *     and the current one are applied to the checkpoint one after the other
+ *     exactly as ssu_update applies a token (state rounded to the state dtype
+ *     after each), y is computed from the result, and the checkpoint is
+ *     stored; the buffer is not touched (the caller resets h to 0);
+ *   - otherwise (output only) the checkpoint is read but not written; with
+ *     a_i = exp(dt'_i A[h]) over the buffered steps i < h and the current
+ *     step i = h, for every dim row d:
+ *       y = (prod_i a_i) (S_ckpt . C) + sum_j dt'_j x_j (prod_{i>j} a_i) (B_j . C)
+ *           + D x, times silu(z)
+ *     and the current step's raw x, dt and B are written to buffer entry h
+ *     (the caller then advances h by one).
+ * With L = 1 every step is a flush and equals ssu_update bit for bit.
+ * base: as for ssu_update with x [batch, heads, dim] (one token per
+ * sequence), state_batch_indices 1-D or absent (slot b), and no
+ * dst_state_batch_indices, cu_seqlens or num_accepted_tokens; the pad id
+ * reads a zero checkpoint and writes nothing; disable_state_update writes
+ * neither checkpoint nor buffer.
+ *   buf_x   [slots, L, heads, dim], x dtype, contiguous
+ *   buf_dt  [slots, L, heads, dim], or [slots, L, heads] when dt is one value
+ *           per head, dt dtype, contiguous
+ *   buf_B   [slots, L, groups, dstate], x dtype, contiguous
+ *   buf_len [batch] i32 / i64 (device): entries buffered per sequence
+ * All DEVICE memory owned by the caller; buffers are updated in place. Same
+ * error, stream and allocation conventions as ssu_update. */
+typedef struct {
+    ssu_args_t base;
+    ssu_tensor_t buf_x, buf_dt, buf_B, buf_len;
+} ssu_replay_args_t;
+
+SSU_API ssu_status_t ssu_replay_update(const ssu_replay_args_t *args, void *stream);
+
 /* Message of the last failing call on this thread ("" if none). The pointer
  * stays valid until the next call on the same thread. */
 SSU_API const char *ssu_last_error(void);

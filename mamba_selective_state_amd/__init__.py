@@ -3,9 +3,12 @@
 The update runs in hand-written HIP kernels behind a C ABI (include/ssu.h,
 libssu.so); this package is its Python binding.
 """
-from .ssu import (LIBRARY_PATH, SsuArgs, SsuError, make_args, prewarm_selective_state_update,
-                  selective_state_update, ssu_abi_version, ssu_last_error, ssu_plan, ssu_update)
+from .ssu import (LIBRARY_PATH, SsuArgs, SsuError, SsuReplayArgs, make_args, make_replay_args,
+                  prewarm_selective_state_update, replay_selective_state_update,
+                  selective_state_update, ssu_abi_version, ssu_last_error, ssu_plan,
+                  ssu_replay_update, ssu_update)
 
-__all__ = ["selective_state_update", "prewarm_selective_state_update", "ssu_update", "ssu_plan",
-           "ssu_last_error", "ssu_abi_version", "make_args", "SsuArgs", "SsuError",
-           "LIBRARY_PATH"]
+__all__ = ["selective_state_update", "prewarm_selective_state_update",
+           "replay_selective_state_update", "ssu_update", "ssu_replay_update", "ssu_plan",
+           "ssu_last_error", "ssu_abi_version", "make_args", "make_replay_args", "SsuArgs",
+           "SsuReplayArgs", "SsuError", "LIBRARY_PATH"]

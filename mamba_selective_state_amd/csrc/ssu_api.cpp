@@ -228,61 +228,25 @@ int64_t access_vec(int state_dtype, int64_t N) {
     return per16 < e ? per16 : e;
 }
 
-}  // namespace
+// Everything ssu_update and ssu_replay_update check and derive from the
+// common arguments, without touching the device.
+struct Prepared {
+    ssu::Params p;
+    bool empty;        // no rows or no sequences: nothing to launch
+    bool multi;        // the multi-token kernel is needed
+    int state_dtype, io, dt_dtype;
+    int64_t slots, H, P, N, G, nseq;
+    int32_t layout;
+    bool rtab_2d;
+    int64_t dt_sp;     // dt's stride over dim (0: one value per head)
+    Geometry geo;
+    int64_t grid;
+};
 
-extern "C" {
-
-int ssu_abi_version(void) { return SSU_ABI_VERSION; }
-
-const char *ssu_last_error(void) { return g_error.c_str(); }
-
-ssu_status_t ssu_plan(const ssu_plan_desc_t *desc, ssu_plan_info_t *info) {
-    if (!desc)
-        return fail(SSU_ERR_VALUE, "ssu_plan: desc is NULL");
-    if (!is_float(desc->state_dtype))
-        return fail(SSU_ERR_VALUE, "state_dtype must be f32, f16 or bf16");
-    if (!is_float(desc->io_dtype))
-        return fail(SSU_ERR_VALUE, "io_dtype must be f32, f16 or bf16");
-    if (desc->dt_dtype != SSU_F32 && desc->dt_dtype != desc->io_dtype)
-        return fail(SSU_ERR_VALUE, "dt_dtype must be f32 or the io dtype");
-    if (!is_index(desc->slot_dtype) || !is_index(desc->meta_dtype))
-        return fail(SSU_ERR_VALUE, "slot_dtype and meta_dtype must be i32 or i64");
-    if (desc->heads <= 0 || desc->dim <= 0 || desc->groups <= 0)
-        return fail(SSU_ERR_VALUE, "heads, dim and groups must be positive");
-    if (desc->heads % desc->groups != 0)
-        return fail(SSU_ERR_VALUE, "heads (%d) must be divisible by groups (%d)", desc->heads,
-                    desc->groups);
-    if (!dstate_supported(desc->dstate))
-        return fail(SSU_ERR_NOT_IMPLEMENTED, "dstate %d is not supported (16, 32, 64, 128, 256)",
-                    desc->dstate);
-    if (desc->dt_dim != 1 && desc->dt_dim != desc->dim)
-        return fail(SSU_ERR_VALUE, "dt_dim must be 1 or dim");
-    ssu::KernelRef k;
-    const bool multi = desc->packed != 0;
-    if (!ssu::find_kernel(desc->state_dtype, desc->io_dtype, desc->dstate, multi, &k))
-        return fail(SSU_ERR_NOT_IMPLEMENTED, "no kernel for this dtype combination");
-    int vgprs = 0, sgprs = 0;
-    const int e = ssu::kernel_attributes(k, &vgprs, &sgprs);
-    if (e != 0)
-        return fail(SSU_ERR_HIP, "loading the kernel failed: %s", ssu::hip_error_string(e));
-    if (info) {
-        const Geometry g = geometry(desc->dim, desc->dstate, desc->state_dtype, multi);
-        memset(info, 0, sizeof *info);
-        ssu::kernel_name(desc->state_dtype, desc->io_dtype, desc->dstate, multi, info->kernel,
-                         sizeof info->kernel);
-        info->block_threads = g.block;
-        info->rows_per_block = g.rows_per_block;
-        info->blocks_per_seq_head = g.dim_tiles;
-        info->vgprs = vgprs;
-        info->sgprs = sgprs;
-    }
-    g_error.clear();
-    return SSU_OK;
-}
-
-ssu_status_t ssu_update(const ssu_args_t *a, void *stream) {
+ssu_status_t prepare(const ssu_args_t *a, Prepared *out) {
+    out->empty = false;
     if (!a)
-        return fail(SSU_ERR_VALUE, "ssu_update: args is NULL");
+        return fail(SSU_ERR_VALUE, "args is NULL");
     if (const char *opt = unsupported_option(a->unsupported))
         return fail(SSU_ERR_NOT_IMPLEMENTED, "%s is not implemented", opt);
 
@@ -457,8 +421,23 @@ ssu_status_t ssu_update(const ssu_args_t *a, void *stream) {
                         steps, &p.wtab, &w_s0, &w_s1, &w2d, &wi64)) != SSU_OK)
         return s;
 
-    if (nseq <= 0 || rw.rows <= 0)
-        return g_error.clear(), SSU_OK;  // nothing to do
+    out->state_dtype = st.dtype;
+    out->io = io;
+    out->dt_dtype = dt.dtype;
+    out->slots = slots;
+    out->H = H;
+    out->P = P;
+    out->N = N;
+    out->G = G;
+    out->nseq = nseq;
+    out->layout = layout;
+    out->multi = multi;
+    out->rtab_2d = r2d;
+    out->dt_sp = dt_sp;
+    if (nseq <= 0 || rw.rows <= 0) {
+        out->empty = true;  // nothing to do
+        return SSU_OK;
+    }
 
     // every tensor but the pool is addressed with 32-bit element offsets
     {
@@ -503,10 +482,6 @@ ssu_status_t ssu_update(const ssu_args_t *a, void *stream) {
     if (nseq > INT32_MAX)
         return fail(SSU_ERR_NOT_IMPLEMENTED, "too many sequences");
 
-    ssu::KernelRef k;
-    if (!ssu::find_kernel(st.dtype, io, static_cast<int>(N), multi, &k))
-        return fail(SSU_ERR_NOT_IMPLEMENTED, "no kernel for state %s / io %s / dstate %lld",
-                    dtype_str(st.dtype), dtype_str(io), (long long)N);
     const Geometry geo = geometry(P, N, st.dtype, multi);
     const int64_t grid = nseq * H * geo.dim_tiles;
     if (grid > INT32_MAX)
@@ -535,8 +510,172 @@ ssu_status_t ssu_update(const ssu_args_t *a, void *stream) {
               (wi64 ? ssu::kWriteI64 : 0) | (cu_i64 ? ssu::kCuI64 : 0) |
               (acc_i64 ? ssu::kAccI64 : 0);
 
-    const int e = ssu::launch(k, p, static_cast<unsigned>(grid), static_cast<unsigned>(geo.block),
-                              stream);
+    out->p = p;
+    out->geo = geo;
+    out->grid = grid;
+    return SSU_OK;
+}
+
+
+}  // namespace
+
+extern "C" {
+
+int ssu_abi_version(void) { return SSU_ABI_VERSION; }
+
+const char *ssu_last_error(void) { return g_error.c_str(); }
+
+ssu_status_t ssu_plan(const ssu_plan_desc_t *desc, ssu_plan_info_t *info) {
+    if (!desc)
+        return fail(SSU_ERR_VALUE, "ssu_plan: desc is NULL");
+    if (!is_float(desc->state_dtype))
+        return fail(SSU_ERR_VALUE, "state_dtype must be f32, f16 or bf16");
+    if (!is_float(desc->io_dtype))
+        return fail(SSU_ERR_VALUE, "io_dtype must be f32, f16 or bf16");
+    if (desc->dt_dtype != SSU_F32 && desc->dt_dtype != desc->io_dtype)
+        return fail(SSU_ERR_VALUE, "dt_dtype must be f32 or the io dtype");
+    if (!is_index(desc->slot_dtype) || !is_index(desc->meta_dtype))
+        return fail(SSU_ERR_VALUE, "slot_dtype and meta_dtype must be i32 or i64");
+    if (desc->heads <= 0 || desc->dim <= 0 || desc->groups <= 0)
+        return fail(SSU_ERR_VALUE, "heads, dim and groups must be positive");
+    if (desc->heads % desc->groups != 0)
+        return fail(SSU_ERR_VALUE, "heads (%d) must be divisible by groups (%d)", desc->heads,
+                    desc->groups);
+    if (!dstate_supported(desc->dstate))
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "dstate %d is not supported (16, 32, 64, 128, 256)",
+                    desc->dstate);
+    if (desc->dt_dim != 1 && desc->dt_dim != desc->dim)
+        return fail(SSU_ERR_VALUE, "dt_dim must be 1 or dim");
+    ssu::KernelRef k;
+    const bool multi = desc->packed != 0;
+    if (!ssu::find_kernel(desc->state_dtype, desc->io_dtype, desc->dstate, multi, &k))
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "no kernel for this dtype combination");
+    int vgprs = 0, sgprs = 0;
+    const int e = ssu::kernel_attributes(k, &vgprs, &sgprs);
+    if (e != 0)
+        return fail(SSU_ERR_HIP, "loading the kernel failed: %s", ssu::hip_error_string(e));
+    if (info) {
+        const Geometry g = geometry(desc->dim, desc->dstate, desc->state_dtype, multi);
+        memset(info, 0, sizeof *info);
+        ssu::kernel_name(desc->state_dtype, desc->io_dtype, desc->dstate, multi, info->kernel,
+                         sizeof info->kernel);
+        info->block_threads = g.block;
+        info->rows_per_block = g.rows_per_block;
+        info->blocks_per_seq_head = g.dim_tiles;
+        info->vgprs = vgprs;
+        info->sgprs = sgprs;
+    }
+    g_error.clear();
+    return SSU_OK;
+}
+
+ssu_status_t ssu_update(const ssu_args_t *a, void *stream) {
+    Prepared pr;
+    ssu_status_t s = prepare(a, &pr);
+    if (s != SSU_OK)
+        return s;
+    if (pr.empty)
+        return g_error.clear(), SSU_OK;
+    ssu::KernelRef k;
+    if (!ssu::find_kernel(pr.state_dtype, pr.io, static_cast<int>(pr.N), pr.multi, &k))
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "no kernel for state %s / io %s / dstate %lld",
+                    dtype_str(pr.state_dtype), dtype_str(pr.io), (long long)pr.N);
+    const int e = ssu::launch(k, pr.p, static_cast<unsigned>(pr.grid),
+                              static_cast<unsigned>(pr.geo.block), stream);
+    if (e != 0)
+        return fail(SSU_ERR_HIP, "kernel launch failed: %s", ssu::hip_error_string(e));
+    g_error.clear();
+    return SSU_OK;
+}
+
+ssu_status_t ssu_replay_update(const ssu_replay_args_t *ra, void *stream) {
+    if (!ra)
+        return fail(SSU_ERR_VALUE, "ssu_replay_update: args is NULL");
+    const ssu_args_t *a = &ra->base;
+    if (a && (present(a->dst_state_batch_indices) || present(a->cu_seqlens) ||
+              present(a->num_accepted_tokens)))
+        return fail(SSU_ERR_NOT_IMPLEMENTED,
+                    "replay decode takes one token per sequence and one slot table "
+                    "(no dst_state_batch_indices, cu_seqlens or num_accepted_tokens)");
+    if (a && a->x.ndim != 3)
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "replay decode takes x [batch, heads, dim]");
+    Prepared pr;
+    ssu_status_t s = prepare(a, &pr);
+    if (s != SSU_OK)
+        return s;
+    if (pr.rtab_2d)
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "replay decode takes a 1-D slot table");
+
+    // buffers: contiguous, shaped after the pool
+    const ssu_tensor_t &bx = ra->buf_x, &bdt = ra->buf_dt, &bB = ra->buf_B;
+    if (!present(bx) || !present(bdt) || !present(bB))
+        return fail(SSU_ERR_VALUE, "buf_x, buf_dt and buf_B are required");
+    if (bx.ndim != 4 || bx.size[0] != pr.slots || bx.size[1] < 1 || bx.size[2] != pr.H ||
+        bx.size[3] != pr.P)
+        return fail(SSU_ERR_VALUE, "buf_x must be [slots, L, heads, dim]");
+    const int64_t L = bx.size[1];
+    if (bx.dtype != pr.io || bB.dtype != pr.io)
+        return fail(SSU_ERR_VALUE, "buf_x and buf_B must have the x dtype");
+    if (bB.ndim != 4 || bB.size[0] != pr.slots || bB.size[1] != L || bB.size[2] != pr.G ||
+        bB.size[3] != pr.N)
+        return fail(SSU_ERR_VALUE, "buf_B must be [slots, L, groups, dstate]");
+    if (bdt.dtype != pr.dt_dtype)
+        return fail(SSU_ERR_VALUE, "buf_dt must have the dt dtype");
+    const bool dt_per_head = bdt.ndim == 3;
+    if (dt_per_head ? (bdt.size[0] != pr.slots || bdt.size[1] != L || bdt.size[2] != pr.H)
+                    : (bdt.ndim != 4 || bdt.size[0] != pr.slots || bdt.size[1] != L ||
+                       bdt.size[2] != pr.H || bdt.size[3] != pr.P))
+        return fail(SSU_ERR_VALUE, "buf_dt must be [slots, L, heads, dim] or [slots, L, heads]");
+    if (dt_per_head && pr.dt_sp != 0)
+        return fail(SSU_ERR_VALUE, "a per-head buf_dt needs dt with one value per head");
+    const ssu_tensor_t *bufs[] = {&bx, &bdt, &bB};
+    for (const ssu_tensor_t *t : bufs) {
+        int64_t want = 1;
+        for (int i = t->ndim - 1; i >= 0; i--) {
+            if (t->stride[i] != want && t->size[i] != 1)
+                return fail(SSU_ERR_VALUE, "replay buffers must be contiguous");
+            want *= t->size[i];
+        }
+    }
+    if (!aligned(bx.data, elem_bytes(pr.io)) || !aligned(bdt.data, elem_bytes(pr.dt_dtype)) ||
+        !aligned(bB.data, 16))
+        return fail(SSU_ERR_VALUE, "replay buffers are misaligned (buf_B needs 16 bytes)");
+    ssu::ReplayParams rp;
+    memset(&rp, 0, sizeof rp);
+    int64_t len_s = 0;
+    bool len_i64 = false;
+    if (!present(ra->buf_len))
+        return fail(SSU_ERR_VALUE, "buf_len is required");
+    if ((s = meta_vector("buf_len", ra->buf_len, pr.nseq, &rp.buf_len, &len_s, &len_i64)) !=
+        SSU_OK)
+        return s;
+    if (pr.empty)
+        return g_error.clear(), SSU_OK;
+    if (L > INT32_MAX || pr.nseq * len_s >= INT32_MAX)
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "buffer length or buf_len too large");
+    rp.buf_x = const_cast<void *>(bx.data);
+    rp.buf_dt = const_cast<void *>(bdt.data);
+    rp.buf_B = const_cast<void *>(bB.data);
+    rp.L = static_cast<int32_t>(L);
+    rp.len_s = static_cast<int32_t>(len_s);
+    rp.len_i64 = len_i64;
+    rp.dt_per_head = dt_per_head;
+    rp.G = static_cast<int32_t>(pr.G);
+
+    ssu::KernelRef k;
+    if (!ssu::find_replay_kernel(pr.state_dtype, pr.io, static_cast<int>(pr.N), &k))
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "no replay kernel for state %s / io %s / dstate %lld",
+                    dtype_str(pr.state_dtype), dtype_str(pr.io), (long long)pr.N);
+    // the replay kernel uses the one-token geometry
+    const Geometry geo = geometry(pr.P, pr.N, pr.state_dtype, false);
+    ssu::Params p = pr.p;
+    p.dim_tiles = geo.dim_tiles;
+    p.rows_per_block = geo.rows_per_block;
+    const int64_t grid = pr.nseq * pr.H * geo.dim_tiles;
+    if (grid > INT32_MAX)
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "grid too large");
+    const int e = ssu::launch_replay(k, p, rp, static_cast<unsigned>(grid),
+                                     static_cast<unsigned>(geo.block), stream);
     if (e != 0)
         return fail(SSU_ERR_HIP, "kernel launch failed: %s", ssu::hip_error_string(e));
     g_error.clear();

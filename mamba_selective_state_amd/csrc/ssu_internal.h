@@ -98,6 +98,20 @@ struct Params {
     int32_t flags;          // Flags
 };
 
+// ReplaySSM decode: the per-slot input buffers (contiguous) and the caller's
+// per-sequence buffer pointers.
+struct ReplayParams {
+    void *buf_x;        // [slots, L, H, P]
+    void *buf_dt;       // [slots, L, H, P] or [slots, L, H]
+    void *buf_B;        // [slots, L, G, N]
+    const void *buf_len;
+    int32_t L;
+    int32_t len_s;      // element stride of buf_len
+    int32_t len_i64;    // buf_len is i64
+    int32_t dt_per_head;  // buf_dt is [slots, L, H]
+    int32_t G;
+};
+
 // Selected kernel variant for (state dtype, io dtype, dstate, multi-token).
 struct KernelRef {
     const void *fn;
@@ -113,6 +127,11 @@ const char *hip_error_string(int e);
 
 // Launches `k` with `p`; returns the hipError_t value as int.
 int launch(const KernelRef &k, const Params &p, unsigned grid, unsigned block, void *stream);
+
+// The ReplaySSM decode kernel for (state dtype, io dtype, dstate).
+bool find_replay_kernel(int state_dtype, int io_dtype, int dstate, KernelRef *out);
+int launch_replay(const KernelRef &k, const Params &p, const ReplayParams &rp, unsigned grid,
+                  unsigned block, void *stream);
 
 // Loads the kernel's code object on the current device and reports its
 // registers; returns the hipError_t value as int.

@@ -487,6 +487,274 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
     }
 }
 
+// ReplaySSM decode (ReplaySSM article, section "核心做法"): one workgroup per
+// (sequence, head, dim tile), the same lane layout as ssu_kernel. A step with
+// h buffered entries either fills the buffer (h + 1 == L: replay the buffered
+// steps and the current one through the update, exactly as ssu_kernel applies
+// a token, then y and the checkpoint store) or is output-only: the
+// checkpoint tile is streamed once for u = S_ckpt . C, and each row's window
+// term is accumulated over the steps j = 0..h as
+//   R <- R a_j + dt'_j x_j (B_j . C),   G <- G a_j,
+// so y = G u + R + D x, gated; the step's raw inputs go to buffer entry h.
+template <typename ST, typename IT, int N>
+__global__ __launch_bounds__(kMaxWaves *kWaveLanes, SSU_WAVES_PER_EU_MULTI) void ssu_replay_kernel(
+    const Params p, const ReplayParams rp) {
+    constexpr int E = N / kLanesPerRow;
+    constexpr int VEC = (16 / (int)sizeof(ST)) < E ? (16 / (int)sizeof(ST)) : E;
+    constexpr int NCH = E / VEC;
+    constexpr int PASSES = passes_for(N, sizeof(ST), false);
+    constexpr int IVEC = VEC;
+    static_assert(PASSES <= kLanesPerRow, "one scalar-owning lane per pass");
+    using SPack = Pack<ST, VEC>;
+
+    const int lane = threadIdx.x & (kWaveLanes - 1);
+    const int wave = threadIdx.x / kWaveLanes;
+    const int col = lane & (kLanesPerRow - 1);
+    const int rsub = lane / kLanesPerRow;
+    const int flags = p.flags;
+
+    const int32_t wg = xcd_clustered_index(blockIdx.x, gridDim.x);
+    const int tile = wg % p.dim_tiles;
+    const int32_t sh = wg / p.dim_tiles;
+    const int h = sh % p.H;
+    const int32_t b = sh / p.H;
+    const int g = h / p.heads_per_group;
+    const int dw = tile * p.rows_per_block + wave * (kRowsPerPass * PASSES);
+    const int d_own = dw + col * kRowsPerPass + rsub;
+    const bool owner = col < PASSES && d_own < p.P;
+    const int d_fetch = owner ? d_own : 0;
+
+    const int64_t s = p.rtab ? load_index(p.rtab, flags & kReadI64, b * p.r_s0) : b;
+    const bool pad = s == p.pad;  // no checkpoint and no buffer: h is taken as 0
+    const int32_t hb =
+        pad ? 0 : static_cast<int32_t>(load_index(rp.buf_len, rp.len_i64, b * rp.len_s));
+    const bool flush = hb + 1 == rp.L;
+    const bool write = !pad && !(flags & kDisable);
+    const bool dt_f32 = flags & kDtF32;
+
+    const int64_t tile_off = static_cast<int64_t>(h) * p.P * N;
+    ST *const pool = static_cast<ST *>(p.state);
+    ST *const sbase = pool + (pad ? 0 : s) * p.slot_stride + tile_off;
+
+    // the checkpoint tile (zeros for the pad id)
+    SPack S[PASSES][NCH];
+#pragma unroll
+    for (int q = 0; q < PASSES; q++) {
+        const int d = dw + q * kRowsPerPass + rsub;
+#pragma unroll
+        for (int c = 0; c < NCH; c++) {
+            if (!pad && d < p.P) {
+                S[q][c] = load_state(reinterpret_cast<const SPack *>(
+                    sbase + static_cast<int64_t>(d) * N + c * kLanesPerRow * VEC + col * VEC));
+            } else {
+#pragma unroll
+                for (int k = 0; k < VEC; k++)
+                    S[q][c].v[k] = narrow<ST>(0.0f);
+            }
+        }
+    }
+
+    const float a_h = p.A[h * p.A_sh];
+    const float d_h = p.D ? p.D[h * p.D_sh] : 0.0f;
+    const float bias_h = p.dt_bias ? p.dt_bias[h * p.bias_sh] : 0.0f;
+    const IT *const xs = static_cast<const IT *>(p.x);
+    const IT *const zs = static_cast<const IT *>(p.z);
+    IT *const ys = static_cast<IT *>(p.out);
+    const IT *const Bcur = static_cast<const IT *>(p.B) + (b * p.B_sr + g * p.B_sg + col * IVEC);
+    const IT *const Ccur = static_cast<const IT *>(p.C) + (b * p.C_sr + g * p.C_sg + col * IVEC);
+    const int P = p.P, H = p.H;
+    const int64_t sl = (pad ? 0 : s) * rp.L;  // first buffer entry of the slot
+    IT *const bxs = static_cast<IT *>(rp.buf_x);
+    IT *const bBs = static_cast<IT *>(rp.buf_B);
+    unsigned char *const bdts = static_cast<unsigned char *>(rp.buf_dt);
+    const int dt_bytes = dt_f32 ? 4 : 2;
+
+    float Cv[E];
+#pragma unroll
+    for (int c = 0; c < NCH; c++) {
+        const RawWords<IT, IVEC> w = load_words<IT, IVEC>(Ccur + c * kLanesPerRow * IVEC);
+#pragma unroll
+        for (int k = 0; k < IVEC; k++)
+            Cv[c * IVEC + k] = word_elem(w, k);
+    }
+
+    // step j's B columns, x and raw dt of the lane's own row
+    auto step_B = [&](int32_t j, float *Bv) {
+        const IT *src = j < hb ? bBs + ((sl + j) * rp.G + g) * N + col * IVEC : Bcur;
+#pragma unroll
+        for (int c = 0; c < NCH; c++) {
+            const RawWords<IT, IVEC> w = load_words<IT, IVEC>(src + c * kLanesPerRow * IVEC);
+#pragma unroll
+            for (int k = 0; k < IVEC; k++)
+                Bv[c * IVEC + k] = word_elem(w, k);
+        }
+    };
+    auto step_x = [&](int32_t j) -> float {
+        const IT *src = j < hb ? bxs + ((sl + j) * H + h) * P + d_fetch
+                               : xs + (b * p.x_sr + h * p.x_sh + d_fetch);
+        return widen(*src);
+    };
+    auto step_dt = [&](int32_t j) -> float {
+        const unsigned char *src;
+        if (j < hb)
+            src = bdts + (rp.dt_per_head ? (sl + j) * H + h : ((sl + j) * H + h) * P + d_fetch) *
+                             dt_bytes;
+        else
+            src = static_cast<const unsigned char *>(p.dt) +
+                  static_cast<int64_t>(b * p.dt_sr + h * p.dt_sh + d_fetch * p.dt_sp) * dt_bytes;
+        float v = (dt_f32 ? *reinterpret_cast<const float *>(src)
+                          : widen(*reinterpret_cast<const IT *>(src))) + bias_h;
+        if (flags & kSoftplus)
+            v = softplus(v);
+        return v;
+    };
+
+    float ysum = 0.0f, xcur = 0.0f;
+    if (flush) {
+        // replay the buffered steps and the current one through the update
+        for (int32_t j = 0; j <= hb; j++) {
+            float Bv[E];
+            step_B(j, Bv);
+            const float xv = step_x(j);
+            const float v = step_dt(j);
+            const float decay = exp_hw(v * a_h);
+            const float dtx = v * xv;
+            const bool last = j == hb;
+            xcur = xv;
+            for_passes<0, PASSES>([&](auto qc) {
+                constexpr int q = decltype(qc)::value;
+                const float dq = row16_bcast<q>(decay);
+                const float tq = row16_bcast<q>(dtx);
+                float acc = 0.0f;
+#pragma unroll
+                for (int c = 0; c < NCH; c++) {
+#pragma unroll
+                    for (int k = 0; k < VEC; k++) {
+                        const int e = c * VEC + k;
+                        const float sv = fmaf(widen(S[q][c].v[k]), dq, tq * Bv[e]);
+                        acc = fmaf(sv, Cv[e], acc);
+                        S[q][c].v[k] = narrow<ST>(sv);
+                    }
+                }
+                if (last) {
+                    const float sum = row16_sum(acc);
+                    ysum = col == q ? sum : ysum;
+                }
+            });
+        }
+        if (write) {
+#pragma unroll
+            for (int q = 0; q < PASSES; q++) {
+                const int d = dw + q * kRowsPerPass + rsub;
+                if (d < P) {
+                    ST *dst = sbase + static_cast<int64_t>(d) * N + col * VEC;
+#pragma unroll
+                    for (int c = 0; c < NCH; c++)
+                        store_state<SSU_NT_STORE>(
+                            reinterpret_cast<SPack *>(dst + c * kLanesPerRow * VEC), S[q][c]);
+                }
+            }
+        }
+    } else {
+        // u = S_ckpt . C of the lane's own row
+        float u = 0.0f;
+        for_passes<0, PASSES>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;
+            float acc = 0.0f;
+#pragma unroll
+            for (int c = 0; c < NCH; c++)
+#pragma unroll
+                for (int k = 0; k < VEC; k++)
+                    acc = fmaf(widen(S[q][c].v[k]), Cv[c * VEC + k], acc);
+            const float sum = row16_sum(acc);
+            u = col == q ? sum : u;
+        });
+        // the window over the buffered steps and the current one
+        float G = 1.0f, R = 0.0f;
+        for (int32_t j = 0; j <= hb; j++) {
+            float Bv[E];
+            step_B(j, Bv);
+            const float xv = step_x(j);
+            const float v = step_dt(j);
+            float part = 0.0f;
+#pragma unroll
+            for (int e = 0; e < E; e++)
+                part = fmaf(Bv[e], Cv[e], part);
+            const float w = row16_sum(part);  // B_j . C
+            const float alpha = exp_hw(v * a_h);
+            R = fmaf(R, alpha, v * xv * w);
+            G = G * alpha;
+            xcur = xv;
+        }
+        ysum = G * u + R;
+        // append the step's raw inputs at entry hb
+        if (write) {
+            if (owner) {
+                bxs[((sl + hb) * H + h) * P + d_own] = xs[b * p.x_sr + h * p.x_sh + d_own];
+                if (!rp.dt_per_head) {
+                    const int64_t di = b * p.dt_sr + h * p.dt_sh + d_own * p.dt_sp;
+                    unsigned char *dst = bdts + (((sl + hb) * H + h) * P + d_own) * dt_bytes;
+                    if (dt_f32)
+                        *reinterpret_cast<float *>(dst) = static_cast<const float *>(p.dt)[di];
+                    else
+                        *reinterpret_cast<IT *>(dst) = static_cast<const IT *>(p.dt)[di];
+                }
+            }
+            if (rp.dt_per_head && tile == 0 && threadIdx.x == 0) {
+                const int64_t di = b * p.dt_sr + h * p.dt_sh;
+                unsigned char *dst = bdts + ((sl + hb) * H + h) * dt_bytes;
+                if (dt_f32)
+                    *reinterpret_cast<float *>(dst) = static_cast<const float *>(p.dt)[di];
+                else
+                    *reinterpret_cast<IT *>(dst) = static_cast<const IT *>(p.dt)[di];
+            }
+            if (h % p.heads_per_group == 0 && tile == 0 && wave == 0 && rsub == 0) {
+                IT *dst = bBs + ((sl + hb) * rp.G + g) * N + col * IVEC;
+#pragma unroll
+                for (int c = 0; c < NCH; c++)
+#pragma unroll
+                    for (int k = 0; k < IVEC; k++)
+                        dst[c * kLanesPerRow * IVEC + k] = Bcur[c * kLanesPerRow * IVEC + k];
+            }
+        }
+    }
+
+    // y of the lane's own row
+    if (owner) {
+        float y = ysum + d_h * xcur;
+        if (zs)
+            y *= silu(widen(zs[b * p.z_sr + h * p.z_sh + d_own]));
+        ys[b * p.out_sr + h * p.out_sh + d_own] = narrow<IT>(y);
+    }
+}
+
+template <typename ST, typename IT>
+bool pick_replay_n(int n, KernelRef *k) {
+    switch (n) {
+#define SSU_CASE(NN)                                                                     \
+    case NN:                                                                             \
+        k->fn = reinterpret_cast<const void *>(&ssu_replay_kernel<ST, IT, NN>);         \
+        return true;
+        SSU_CASE(16)
+        SSU_CASE(32)
+        SSU_CASE(64)
+        SSU_CASE(128)
+        SSU_CASE(256)
+#undef SSU_CASE
+    }
+    return false;
+}
+
+template <typename ST>
+bool pick_replay_io(int io, int n, KernelRef *k) {
+    switch (io) {
+    case SSU_F32: return pick_replay_n<ST, float>(n, k);
+    case SSU_F16: return pick_replay_n<ST, _Float16>(n, k);
+    case SSU_BF16: return pick_replay_n<ST, __bf16>(n, k);
+    }
+    return false;
+}
+
 template <typename ST, typename IT, bool M>
 bool pick_n(int n, KernelRef *k) {
     switch (n) {
@@ -540,6 +808,24 @@ void kernel_name(int state_dtype, int io_dtype, int dstate, bool multi, char *bu
 }
 
 const char *hip_error_string(int e) { return hipGetErrorString(static_cast<hipError_t>(e)); }
+
+bool find_replay_kernel(int state_dtype, int io_dtype, int dstate, KernelRef *out) {
+    switch (state_dtype) {
+    case SSU_F32: return pick_replay_io<float>(io_dtype, dstate, out);
+    case SSU_F16: return pick_replay_io<_Float16>(io_dtype, dstate, out);
+    case SSU_BF16: return pick_replay_io<__bf16>(io_dtype, dstate, out);
+    }
+    return false;
+}
+
+int launch_replay(const KernelRef &k, const Params &p, const ReplayParams &rp, unsigned grid,
+                  unsigned block, void *stream) {
+    Params pc = p;
+    ReplayParams rc = rp;
+    void *args[] = {&pc, &rc};
+    return static_cast<int>(hipLaunchKernel(k.fn, dim3(grid), dim3(block), args, 0,
+                                            static_cast<hipStream_t>(stream)));
+}
 
 int launch(const KernelRef &k, const Params &p, unsigned grid, unsigned block, void *stream) {
     Params copy = p;

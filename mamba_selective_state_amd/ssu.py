@@ -40,6 +40,11 @@ class SsuArgs(ctypes.Structure):
         ("pad_slot_id", ctypes.c_int64), ("unsupported", ctypes.c_uint32)]
 
 
+class SsuReplayArgs(ctypes.Structure):
+    _fields_ = [("base", SsuArgs), ("buf_x", SsuTensor), ("buf_dt", SsuTensor),
+                ("buf_B", SsuTensor), ("buf_len", SsuTensor)]
+
+
 class SsuPlanDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("state_dtype", "io_dtype", "dt_dtype", "slot_dtype", "meta_dtype", "heads",
@@ -52,7 +57,7 @@ class SsuPlanInfo(ctypes.Structure):
                 ("vgprs", ctypes.c_int32), ("sgprs", ctypes.c_int32)]
 
 
-EXPORTS = ("ssu_plan", "ssu_update", "ssu_last_error", "ssu_abi_version")
+EXPORTS = ("ssu_plan", "ssu_update", "ssu_replay_update", "ssu_last_error", "ssu_abi_version")
 
 
 def load_library(path=None):
@@ -66,6 +71,8 @@ def load_library(path=None):
     lib.ssu_plan.restype = ctypes.c_int
     lib.ssu_update.argtypes = [ctypes.POINTER(SsuArgs), ctypes.c_void_p]
     lib.ssu_update.restype = ctypes.c_int
+    lib.ssu_replay_update.argtypes = [ctypes.POINTER(SsuReplayArgs), ctypes.c_void_p]
+    lib.ssu_replay_update.restype = ctypes.c_int
     lib.ssu_last_error.argtypes = []
     lib.ssu_last_error.restype = ctypes.c_char_p
     lib.ssu_abi_version.argtypes = []
@@ -106,6 +113,15 @@ def ssu_update(args, stream=None):
     st = _lib.ssu_update(ctypes.byref(args), ctypes.c_void_p(stream))
     if st != OK:
         _raise(st, "ssu_update")
+
+
+def ssu_replay_update(args, stream=None):
+    """Enqueue one ReplaySSM decode step (include/ssu.h ssu_replay_update)."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    st = _lib.ssu_replay_update(ctypes.byref(args), ctypes.c_void_p(stream))
+    if st != OK:
+        _raise(st, "ssu_replay_update")
 
 
 def ssu_plan(desc):
@@ -218,3 +234,36 @@ def prewarm_selective_state_update(*, state_dtype, io_dtype, batch, heads, dim, 
     desc.packed = int(bool(packed))
     desc.max_rows = batch
     return ssu_plan(desc)
+
+
+def make_replay_args(state, x, dt, A, B, C, D, buf_x, buf_dt, buf_B, buf_len, z=None,
+                     dt_bias=None, dt_softplus=False, state_batch_indices=None, pad_slot_id=-1,
+                     out=None, disable_state_update=False):
+    """SsuReplayArgs for ssu_replay_update; `out` must be given."""
+    r = SsuReplayArgs()
+    r.base = make_args(state, x, dt, A, B, C, D, z, dt_bias, dt_softplus, state_batch_indices,
+                       pad_slot_id, out, disable_state_update)
+    dev = state.device
+    r.buf_x = tensor_desc(buf_x, dev)
+    r.buf_dt = tensor_desc(buf_dt, dev)
+    r.buf_B = tensor_desc(buf_B, dev)
+    r.buf_len = tensor_desc(buf_len, dev)
+    return r
+
+
+def replay_selective_state_update(state, x, dt, A, B, C, D, buf_x, buf_dt, buf_B, buf_len, z=None,
+                                  dt_bias=None, dt_softplus=False, state_batch_indices=None,
+                                  pad_slot_id=-1, out=None, disable_state_update=False):
+    """One ReplaySSM decode step (ReplaySSM article, section "核心做法"): the
+    state is the checkpoint in `state` plus per-slot input buffers; buf_len[b]
+    is the number of steps sequence b has buffered (< L = buf_x.shape[1]).
+    A step that fills the buffer folds it into the checkpoint; any other step
+    computes y from checkpoint and buffer and appends its inputs. The caller
+    advances buf_len (to 0 after a fold). Returns y."""
+    if out is None:
+        out = torch.empty(x.shape, dtype=x.dtype, device=x.device)
+    args = make_replay_args(state, x, dt, A, B, C, D, buf_x, buf_dt, buf_B, buf_len, z, dt_bias,
+                            dt_softplus, state_batch_indices, pad_slot_id, out,
+                            disable_state_update)
+    ssu_replay_update(args, torch.cuda.current_stream(state.device).cuda_stream)
+    return out

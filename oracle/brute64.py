@@ -173,7 +173,7 @@ def run_replay(case):
 
     for b in range(R):
         s = b if tab is None else int(np.asarray(tab)[b])
-        hb = int(np.asarray(case["buf_len"])[b])
+        hb = 0 if s == pad else int(np.asarray(case["buf_len"])[b])  # the pad id has no buffer
         for h in range(H):
             g = h // (H // G)
             # the steps' inputs: buffered entries, then the current step

@@ -498,8 +498,9 @@ int oracle_ssu(const oracle_args *a, char *err, int errlen)
  *  R18 h is the caller's per-sequence buffer pointer (the article moves a
  *      buffer pointer on commit); the caller resets it after a flush;
  *  R19 one token per sequence, the checkpoint slot is read and written in
- *      place; the pad id reads a zero checkpoint and writes nothing;
- *      disable_state_update writes neither checkpoint nor buffer.
+ *      place; the pad id reads a zero checkpoint, has no buffer (its pointer
+ *      is taken as 0) and writes nothing; disable_state_update writes neither
+ *      checkpoint nor buffer.
  */
 typedef struct {
     oracle_args base; /* one token per sequence; rtab 1-D or NULL; no wtab */
@@ -551,7 +552,7 @@ int oracle_replay(const oracle_replay_args *ra, char *err, int errlen)
     for (int64_t b = 0; b < nseq; b++) {
         const int64_t s = a->rtab.data ? a->rtab.data[b] : b;
         const int64_t h = ra->buf_len[b];
-        if (h < 0 || h >= L) {
+        if (s != a->pad && (h < 0 || h >= L)) {
             set_err(err, errlen, "buffer length %lld of sequence %lld outside [0, L)", (long long)h, (long long)b);
             return 1;
         }
@@ -573,8 +574,8 @@ int oracle_replay(const oracle_replay_args *ra, char *err, int errlen)
     float *xs = (float *)malloc((size_t)L * sizeof(float));
     for (int64_t b = 0; b < nseq; b++) {
         const int64_t s = a->rtab.data ? a->rtab.data[b] : b;
-        const int64_t h = ra->buf_len[b];
         const int pad = s == a->pad;
+        const int64_t h = pad ? 0 : ra->buf_len[b]; /* R19 */
         if (a->read_slot)
             a->read_slot[b] = s;
         for (int64_t hd = 0; hd < H; hd++) {

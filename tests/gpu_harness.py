@@ -227,3 +227,76 @@ def subcase(case, seqs):
     sub["pad_slot_id"] = -1
     sub["state"] = np.asarray(case["state"])[used]
     return sub, rows, used
+
+
+# ---------------------------------------------------------------- ReplaySSM
+
+def device_replay(case, device="cuda:0"):
+    d = device_case(case, device)
+    io, dtd = case["io_dtype"], case.get("dt_dtype", case["io_dtype"])
+    d["buf_x"] = dev(case["buf_x"], io, device)
+    d["buf_dt"] = dev(case["buf_dt"], dtd, device)
+    d["buf_B"] = dev(case["buf_B"], io, device)
+    d["buf_len"] = torch.from_numpy(np.ascontiguousarray(case["buf_len"])).to(device)
+    return d
+
+
+def run_gpu_replay(case, d=None, device="cuda:0"):
+    """One ReplaySSM step through the binding; returns host copies of y, the
+    checkpoint pool and the three buffers."""
+    if d is None:
+        d = device_replay(case, device)
+    o = torch.full(np.shape(case["x"]), float("nan"), dtype=TORCH[case["io_dtype"]],
+                   device=device)
+    y = ssu.replay_selective_state_update(
+        d["state"], d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["buf_x"], d["buf_dt"],
+        d["buf_B"], d["buf_len"], z=d["z"], dt_bias=d["dt_bias"],
+        dt_softplus=case.get("dt_softplus", False), state_batch_indices=d["state_batch_indices"],
+        pad_slot_id=case.get("pad_slot_id", -1), out=o,
+        disable_state_update=case.get("disable_state_update", False))
+    assert y is o
+    torch.cuda.synchronize()
+    io, dtd = case["io_dtype"], case.get("dt_dtype", case["io_dtype"])
+    return {"y": host(y, io), "state": host(d["state"], case["state_dtype"]),
+            "buf_x": host(d["buf_x"], io), "buf_dt": host(d["buf_dt"], dtd),
+            "buf_B": host(d["buf_B"], io)}
+
+
+def compare_replay(case, got, ref, name=""):
+    """The checkpoint pool as compare() checks a pool; the buffers bit for
+    bit (they hold raw copies of inputs)."""
+    stats = compare(case, got["y"], got["state"], ref, name)
+    for k in ("buf_x", "buf_dt", "buf_B"):
+        assert np.array_equal(got[k], ref[k]), "%s: %s differs from the oracle" % (name, k)
+    return stats
+
+
+def check_replay(case, name, device="cuda:0"):
+    ref = ssu_oracle.run_replay(case)
+    say("[gpu] %s: launching" % name)
+    got = run_gpu_replay(case, device=device)
+    stats = compare_replay(case, got, ref, name)
+    say("[gpu] %s: ok %s" % (name, {k: "%.3g" % v for k, v in stats.items()}))
+    return stats
+
+
+def replay_subcase(case, seqs):
+    """The replay case restricted to sequences `seqs` with a compact pool and
+    buffers; returns (sub, slots) with the original slots of the pool
+    entries (pad rows keep the pad id, -1 in the sub-case)."""
+    seqs = np.asarray(seqs)
+    pad = int(case.get("pad_slot_id", -1))
+    tab = np.asarray(case["state_batch_indices"])[seqs]
+    used = np.unique(tab[tab != pad])
+    remap = {int(s): i for i, s in enumerate(used)}
+    sub = dict(case)
+    for k in ("x", "dt", "B", "C", "z"):
+        if case.get(k) is not None:
+            sub[k] = np.asarray(case[k])[seqs]
+    sub["state_batch_indices"] = np.array([-1 if s == pad else remap[int(s)] for s in tab],
+                                          np.int64)
+    sub["pad_slot_id"] = -1
+    sub["buf_len"] = np.asarray(case["buf_len"])[seqs]
+    for k in ("state", "buf_x", "buf_dt", "buf_B"):
+        sub[k] = np.asarray(case[k])[used]
+    return sub, used

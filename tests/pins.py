@@ -622,8 +622,8 @@ def pin_replay_zero_checkpoint(orc):
     """Pad slot (zero checkpoint) and an empty buffer: y is the output-only
     closed form dt' x (B . C) + D x, gated, and nothing is written."""
     from oracle import ssu_oracle
-    c = _replay_case(4, 0, sd="f32", io="f32")
-    c["state_batch_indices"] = np.array([0, -1, 2, -1], np.int32)
+    c = _replay_case(4, [0, 3, 0, 2], sd="f32", io="f32")
+    c["state_batch_indices"] = np.array([0, -1, 2, -1], np.int32)  # pad rows' pointers ignored
     r = ssu_oracle.run_replay(c, orc)
     ref, scale = _zero_state_expected(_as_ssu(c), [1, 3])
     assert np.all(np.abs(r["y"][[1, 3]] - ref) <= 40 * U32 * scale + 1e-30)

@@ -38,7 +38,8 @@ def test_struct_layout_matches_header(tmp_path):
     """Field offsets and sizes of the ctypes mirrors equal what a C compiler
     makes of include/ssu.h."""
     structs = {"ssu_tensor_t": S.SsuTensor, "ssu_args_t": S.SsuArgs,
-               "ssu_plan_desc_t": S.SsuPlanDesc, "ssu_plan_info_t": S.SsuPlanInfo}
+               "ssu_plan_desc_t": S.SsuPlanDesc, "ssu_plan_info_t": S.SsuPlanInfo,
+               "ssu_replay_args_t": S.SsuReplayArgs}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ssu.h"', "int main(void) {"]
     for cname, cls in structs.items():
         lines.append('printf("%s SIZEOF %%zu\\n", sizeof(%s));' % (cname, cname))
@@ -314,3 +315,62 @@ def test_package_never_touches_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text, f
                 assert "workloads" not in text, f
+
+
+# ---------------------------------------------------------------- replay
+
+
+def replay_args(rows=0, L=4, H=8, P=16, N=128, G=2, slots=8, dt_full=True):
+    r = S.SsuReplayArgs()
+    r.base = base_args(rows=rows, H=H, P=P, N=N, G=G, slots=slots)
+    r.buf_x = tdesc((slots, L, H, P), S.BF16)
+    r.buf_dt = tdesc((slots, L, H, P) if dt_full else (slots, L, H), S.BF16)
+    r.buf_B = tdesc((slots, L, G, N), S.BF16)
+    r.buf_len = tdesc((rows,), S.I32)
+    return r
+
+
+def replay(r):
+    st = S._lib.ssu_replay_update(ctypes.byref(r), None)
+    return st, S.ssu_last_error()
+
+
+def test_replay_empty_is_ok_without_launch():
+    assert replay(replay_args())[0] == S.OK
+
+
+def test_replay_errors():
+    assert S._lib.ssu_replay_update(None, None) == S.ERR_VALUE
+    r = replay_args()
+    r.base.dst_state_batch_indices = tdesc((0,), S.I32)
+    assert replay(r)[0] == S.ERR_NOT_IMPLEMENTED
+    r = replay_args()
+    r.base.cu_seqlens = tdesc((1,), S.I32)
+    assert replay(r)[0] == S.ERR_NOT_IMPLEMENTED
+    r = replay_args()
+    r.buf_x = tdesc((8, 4, 8, 8), S.BF16)
+    st, msg = replay(r)
+    assert st == S.ERR_VALUE and "buf_x" in msg
+    r = replay_args()
+    r.buf_B = tdesc((8, 3, 2, 128), S.BF16)
+    st, msg = replay(r)
+    assert st == S.ERR_VALUE and "buf_B" in msg
+    r = replay_args()
+    r.buf_dt = tdesc((8, 4, 8, 16), S.F32)
+    st, msg = replay(r)
+    assert st == S.ERR_VALUE and "dt dtype" in msg
+    r = replay_args(dt_full=False)  # per-head buffer but dt [rows, heads, dim]
+    st, msg = replay(r)
+    assert st == S.ERR_VALUE and "per-head" in msg
+    r = replay_args()
+    r.buf_x = tdesc((8, 4, 8, 16), S.BF16, strides=(4 * 8 * 16, 8 * 16, 1, 8))
+    st, msg = replay(r)
+    assert st == S.ERR_VALUE and "contiguous" in msg
+    r = replay_args()
+    r.buf_len = S.SsuTensor()
+    st, msg = replay(r)
+    assert st == S.ERR_VALUE and "buf_len" in msg
+    r = replay_args()
+    r.buf_len = tdesc((3,), S.I32)
+    st, msg = replay(r)
+    assert st == S.ERR_VALUE and "buf_len" in msg
