@@ -16,7 +16,7 @@ Prints ONE JSON line:
              by a plain copy of known size) when they were taken on the
              current kernel source, else null
   cpu_baseline  the CPU oracle timed on this host on the same workload
-Options: --config {decode, decode_pad, mtp, varlen, varlen_disable, varlen_nodst},
+Options: --config {decode, decode_pad, mtp, varlen, varlen_disable, varlen_nodst, replay},
 --no-cpu-baseline, --calib-copy (also runs a plain device copy of the state's
 size, the calibration kernel for the counters).
 """
@@ -54,6 +54,11 @@ def workload(name):
     if name == "mtp":
         return W.mtp(), ("mtp: 64 sequences x 7 tokens, heads 128, dim 64, dstate 128, groups 8, "
                          "fp32 state, 2-D tables, write = read + 448, accepted ~ U{1..7}")
+    if name == "replay":
+        return W.replay(), ("replay: ReplaySSM decode step on the decode workload's layer (batch "
+                            "256, heads 128, dim 64, dstate 128, groups 8, fp32 checkpoint), "
+                            "buffer length L = 16, bf16 x/dt/B buffers, per-sequence buffer "
+                            "pointers ~ U{0..15} (about 1/16 of the sequences fold each step)")
     if name.startswith("varlen"):
         dst = name != "varlen_nodst"
         dis = name == "varlen_disable"
@@ -124,6 +129,40 @@ def algorithmic_bytes(case):
     return int(total), int(R * H)
 
 
+def replay_algorithmic_bytes(case):
+    """Minimal bytes of one ReplaySSM step: each live sequence reads its
+    checkpoint tile and its h buffered entries; a folding sequence (h + 1 ==
+    L) writes its checkpoint, any other writes one buffer entry; plus the
+    current step's inputs and y, and per-head vectors and tables, as for the
+    plain update. Returns (bytes, token-head updates)."""
+    slots, H, P, N = np.shape(case["state"])
+    sb = DTYPE_BYTES[case["state_dtype"]]
+    io = DTYPE_BYTES[case["io_dtype"]]
+    dtb = DTYPE_BYTES[case.get("dt_dtype", case["io_dtype"])]
+    G = np.shape(case["B"])[-2]
+    L = int(case["L"])
+    per_head = np.ndim(case["buf_dt"]) == 3
+    entry = H * P * io + (H if per_head else H * P) * dtb + G * N * io
+    tile = H * P * N * sb
+    pad = int(case.get("pad_slot_id", -1))
+    tab = case.get("state_batch_indices")
+    total = 0
+    R = np.shape(case["x"])[0]
+    for b in range(R):
+        s = b if tab is None else int(np.asarray(tab)[b])
+        if s == pad:
+            continue
+        h = int(case["buf_len"][b])
+        total += tile + h * entry
+        if not case.get("disable_state_update", False):
+            total += tile if h + 1 == L else entry
+    row = H * P * io * 2 + (H * P * io if case.get("z") is not None else 0)
+    row += (H if np.ndim(case["dt"]) == 2 else H * P) * dtb + 2 * G * N * io
+    vec = 4 * H * (1 + (case.get("D") is not None) + (case.get("dt_bias") is not None))
+    idx = (np.asarray(tab).itemsize * R if tab is not None else 0) + np.asarray(case["buf_len"]).nbytes
+    return int(total + R * row + vec + idx), int(R * H)
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
@@ -146,10 +185,11 @@ def traffic_from_counters(config):
 def cpu_baseline(case, alg_bytes, updates, reps):
     from oracle import ssu_oracle
     ssu_oracle.default()
+    run = ssu_oracle.run_replay if "buf_len" in case else ssu_oracle.run
     times = []
     for _ in range(reps):
         t0 = time.perf_counter()
-        ssu_oracle.run(case)
+        run(case)
         times.append(time.perf_counter() - t0)
     t = statistics.median(times)
     return {"value": round(alg_bytes / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
@@ -177,25 +217,35 @@ def main():
     import torch
     import mamba_selective_state_amd as ssu
     sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from gpu_harness import TORCH, device_case
+    from gpu_harness import TORCH, device_case, device_replay
 
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     dev = torch.device("cuda", 0)
     case, desc = workload(args.config)
-    alg_bytes, updates = algorithmic_bytes(case)
+    is_replay = args.config == "replay"
+    alg_bytes, updates = (replay_algorithmic_bytes if is_replay else algorithmic_bytes)(case)
     print("[bench] %s: %.3f GB per step" % (args.config, alg_bytes / 1e9), file=sys.stderr,
           flush=True)
-    d = device_case(case, dev)
+    d = device_replay(case, dev) if is_replay else device_case(case, dev)
     out = torch.empty(np.shape(case["x"]), dtype=TORCH[case["io_dtype"]], device=dev)
-    args_c = ssu.make_args(d["state"], d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"],
-                           d["dt_bias"], case.get("dt_softplus", False),
-                           d["state_batch_indices"], case.get("pad_slot_id", -1), out,
-                           case.get("disable_state_update", False),
-                           d["dst_state_batch_indices"], d["cu_seqlens"],
-                           d["num_accepted_tokens"])
+    if is_replay:
+        args_c = ssu.make_replay_args(d["state"], d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"],
+                                      d["buf_x"], d["buf_dt"], d["buf_B"], d["buf_len"], d["z"],
+                                      d["dt_bias"], case.get("dt_softplus", False),
+                                      d["state_batch_indices"], case.get("pad_slot_id", -1), out,
+                                      case.get("disable_state_update", False))
+        launch = ssu.ssu_replay_update
+    else:
+        args_c = ssu.make_args(d["state"], d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"],
+                               d["z"], d["dt_bias"], case.get("dt_softplus", False),
+                               d["state_batch_indices"], case.get("pad_slot_id", -1), out,
+                               case.get("disable_state_update", False),
+                               d["dst_state_batch_indices"], d["cu_seqlens"],
+                               d["num_accepted_tokens"])
+        launch = ssu.ssu_update
     x = np.asarray(case["x"])
-    plan = ssu.prewarm_selective_state_update(
+    plan = {"kernel": "ssu_replay_kernel"} if is_replay else ssu.prewarm_selective_state_update(
         state_dtype=TORCH[case["state_dtype"]], io_dtype=TORCH[case["io_dtype"]],
         batch=x.shape[0], heads=x.shape[-2], dim=x.shape[-1], dstate=np.shape(case["state"])[-1],
         groups=np.shape(case["B"])[-2],
@@ -208,13 +258,13 @@ def main():
     handle = stream.cuda_stream
 
     for _ in range(args.warmup):
-        ssu.ssu_update(args_c, handle)
+        launch(args_c, handle)
     torch.cuda.synchronize(dev)
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record(stream)
     for _ in range(args.steps):
-        ssu.ssu_update(args_c, handle)
+        launch(args_c, handle)
     end.record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0

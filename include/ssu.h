@@ -188,7 +188,10 @@ SSU_API ssu_status_t ssu_update(const ssu_args_t *args, void *stream);
  *   buf_dt  [slots, L, heads, dim], or [slots, L, heads] when dt is one value
  *           per head, dt dtype, contiguous
  *   buf_B   [slots, L, groups, dstate], x dtype, contiguous
- *   buf_len [batch] i32 / i64 (device): entries buffered per sequence
+ *   buf_len [batch] i32 / i64 (device): entries buffered per sequence; a
+ *           value outside [0, L) for a slot other than the pad id makes
+ *           that sequence's y NaN and writes nothing for it (the kernel
+ *           checks it; nothing outside the buffers is read)
  * All DEVICE memory owned by the caller; buffers are updated in place. Same
  * error, stream and allocation conventions as ssu_update. */
 typedef struct {

@@ -195,9 +195,9 @@ struct Geometry {
     int32_t block, rows_per_block, dim_tiles;
 };
 
-Geometry geometry(int64_t P, int64_t N, int state_dtype, bool multi) {
+Geometry geometry(int64_t P, int64_t N, int state_dtype, int kind) {
     const int passes =
-        ssu::passes_for(static_cast<int>(N), static_cast<int>(elem_bytes(state_dtype)), multi);
+        ssu::passes_for(static_cast<int>(N), static_cast<int>(elem_bytes(state_dtype)), kind);
     const int64_t rows_per_wave = ssu::kRowsPerPass * passes;
     int64_t waves = (P + rows_per_wave - 1) / rows_per_wave;
     if (waves > ssu::kMaxWaves)
@@ -482,7 +482,7 @@ ssu_status_t prepare(const ssu_args_t *a, Prepared *out) {
     if (nseq > INT32_MAX)
         return fail(SSU_ERR_NOT_IMPLEMENTED, "too many sequences");
 
-    const Geometry geo = geometry(P, N, st.dtype, multi);
+    const Geometry geo = geometry(P, N, st.dtype, multi ? ssu::kTileMulti : ssu::kTileOneToken);
     const int64_t grid = nseq * H * geo.dim_tiles;
     if (grid > INT32_MAX)
         return fail(SSU_ERR_NOT_IMPLEMENTED, "grid of %lld workgroups is too large",
@@ -555,7 +555,8 @@ ssu_status_t ssu_plan(const ssu_plan_desc_t *desc, ssu_plan_info_t *info) {
     if (e != 0)
         return fail(SSU_ERR_HIP, "loading the kernel failed: %s", ssu::hip_error_string(e));
     if (info) {
-        const Geometry g = geometry(desc->dim, desc->dstate, desc->state_dtype, multi);
+        const Geometry g = geometry(desc->dim, desc->dstate, desc->state_dtype,
+                                    multi ? ssu::kTileMulti : ssu::kTileOneToken);
         memset(info, 0, sizeof *info);
         ssu::kernel_name(desc->state_dtype, desc->io_dtype, desc->dstate, multi, info->kernel,
                          sizeof info->kernel);
@@ -651,8 +652,10 @@ ssu_status_t ssu_replay_update(const ssu_replay_args_t *ra, void *stream) {
         return s;
     if (pr.empty)
         return g_error.clear(), SSU_OK;
-    if (L > INT32_MAX || pr.nseq * len_s >= INT32_MAX)
-        return fail(SSU_ERR_NOT_IMPLEMENTED, "buffer length or buf_len too large");
+    // the kernel addresses one slot's buffer entries with 32-bit offsets
+    if (L * pr.H * pr.P >= INT32_MAX || L * pr.G * pr.N >= INT32_MAX ||
+        pr.nseq * len_s >= INT32_MAX)
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "buffer per slot or buf_len too large");
     rp.buf_x = const_cast<void *>(bx.data);
     rp.buf_dt = const_cast<void *>(bdt.data);
     rp.buf_B = const_cast<void *>(bB.data);
@@ -666,8 +669,7 @@ ssu_status_t ssu_replay_update(const ssu_replay_args_t *ra, void *stream) {
     if (!ssu::find_replay_kernel(pr.state_dtype, pr.io, static_cast<int>(pr.N), &k))
         return fail(SSU_ERR_NOT_IMPLEMENTED, "no replay kernel for state %s / io %s / dstate %lld",
                     dtype_str(pr.state_dtype), dtype_str(pr.io), (long long)pr.N);
-    // the replay kernel uses the one-token geometry
-    const Geometry geo = geometry(pr.P, pr.N, pr.state_dtype, false);
+    const Geometry geo = geometry(pr.P, pr.N, pr.state_dtype, ssu::kTileReplay);
     ssu::Params p = pr.p;
     p.dim_tiles = geo.dim_tiles;
     p.rows_per_block = geo.rows_per_block;

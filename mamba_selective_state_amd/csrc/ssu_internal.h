@@ -40,6 +40,22 @@ constexpr int kMaxWaves = SSU_MAX_WAVES;
 #ifndef SSU_WAVES_PER_EU
 #define SSU_WAVES_PER_EU 1
 #endif
+// The replay kernel: fp32 state with dstate <= 128 fits 4 waves per SIMD
+// without spills; the other tiles need more registers for the fold path.
+// Its output-only path requests the inputs of the first SSU_REPLAY_PREFETCH
+// steps of every run before the checkpoint tile.
+#ifndef SSU_WAVES_PER_EU_REPLAY
+#define SSU_WAVES_PER_EU_REPLAY 4
+#endif
+#ifndef SSU_WAVES_PER_EU_REPLAY_WIDE
+#define SSU_WAVES_PER_EU_REPLAY_WIDE 3
+#endif
+#ifndef SSU_REPLAY_PREFETCH
+#define SSU_REPLAY_PREFETCH 4
+#endif
+constexpr int replay_waves_per_eu(int state_bytes, int dstate) {
+    return state_bytes == 4 && dstate <= 128 ? SSU_WAVES_PER_EU_REPLAY : SSU_WAVES_PER_EU_REPLAY_WIDE;
+}
 #ifndef SSU_WAVES_PER_EU_MULTI
 #define SSU_WAVES_PER_EU_MULTI 4
 #endif
@@ -54,9 +70,16 @@ constexpr int kMaxWaves = SSU_MAX_WAVES;
 #ifndef SSU_LANE_BYTES_MULTI
 #define SSU_LANE_BYTES_MULTI 128
 #endif
-constexpr int passes_for(int dstate, int state_bytes, bool multi) {
+#ifndef SSU_LANE_BYTES_REPLAY
+#define SSU_LANE_BYTES_REPLAY 128
+#endif
+enum TileKind { kTileOneToken = 0, kTileMulti = 1, kTileReplay = 2 };
+constexpr int passes_for(int dstate, int state_bytes, int kind) {
     const int per_row = (dstate / kLanesPerRow) * state_bytes;
-    const int rows = (multi ? SSU_LANE_BYTES_MULTI : SSU_LANE_BYTES) / per_row;
+    const int budget = kind == kTileMulti    ? SSU_LANE_BYTES_MULTI
+                       : kind == kTileReplay ? SSU_LANE_BYTES_REPLAY
+                                             : SSU_LANE_BYTES;
+    const int rows = budget / per_row;
     return rows < 1 ? 1 : (rows > 8 ? 8 : rows);
 }
 

@@ -220,6 +220,22 @@ __device__ __forceinline__ RawWords<IT, IVEC> load_words(const IT *src) {
     return r;
 }
 
+// Stores a RawWords block as loaded (exactly IVEC elements).
+template <typename IT, int IVEC>
+__device__ __forceinline__ void store_words(IT *dst, const RawWords<IT, IVEC> &r) {
+    constexpr int kBytes = RawWords<IT, IVEC>::kBytes;
+    if constexpr (kBytes <= 2) {
+        *reinterpret_cast<uint16_t *>(dst) = static_cast<uint16_t>(r.w[0]);
+    } else if constexpr (kBytes <= 16) {
+        using R = typename RawOf<kBytes>::T;
+        *reinterpret_cast<R *>(dst) = __builtin_bit_cast(R, r);
+    } else {
+#pragma unroll
+        for (int i = 0; i < kBytes / 16; i++)
+            reinterpret_cast<u32x4 *>(dst)[i] = u32x4{r.w[4 * i], r.w[4 * i + 1], r.w[4 * i + 2], r.w[4 * i + 3]};
+    }
+}
+
 // element k of a RawWords block, widened to fp32
 template <typename IT, int IVEC>
 __device__ __forceinline__ float word_elem(const RawWords<IT, IVEC> &r, int k) {
@@ -260,7 +276,7 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
     constexpr int E = N / kLanesPerRow;  // state elements per lane per row
     constexpr int VEC = (16 / (int)sizeof(ST)) < E ? (16 / (int)sizeof(ST)) : E;
     constexpr int NCH = E / VEC;         // accesses per lane per row
-    constexpr int PASSES = passes_for(N, sizeof(ST), MULTI);
+    constexpr int PASSES = passes_for(N, sizeof(ST), MULTI ? kTileMulti : kTileOneToken);
     constexpr int IVEC = VEC;            // B / C are read with the same column split
     static_assert(E * kLanesPerRow == N && NCH * VEC == E, "dstate split");
     static_assert(PASSES <= kLanesPerRow, "one scalar-owning lane per pass");
@@ -488,24 +504,34 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
 }
 
 // ReplaySSM decode (ReplaySSM article, section "核心做法"): one workgroup per
-// (sequence, head, dim tile), the same lane layout as ssu_kernel. A step with
-// h buffered entries either fills the buffer (h + 1 == L: replay the buffered
-// steps and the current one through the update, exactly as ssu_kernel applies
-// a token, then y and the checkpoint store) or is output-only: the
-// checkpoint tile is streamed once for u = S_ckpt . C, and each row's window
-// term is accumulated over the steps j = 0..h as
+// (sequence, head, dim tile), the checkpoint tile in ssu_kernel's lane
+// layout. A step with h buffered entries either fills the buffer (h + 1 == L:
+// replay the buffered steps and the current one through the update, exactly
+// as ssu_kernel applies a token, then y and the checkpoint store) or is
+// output-only: the checkpoint tile is streamed once for u = S_ckpt . C and
+// each dim row's window term over the steps j = 0..h,
 //   R <- R a_j + dt'_j x_j (B_j . C),   G <- G a_j,
-// so y = G u + R + D x, gated; the step's raw inputs go to buffer entry h.
+// gives y = G u + R + D x, gated; the step's raw inputs go to buffer entry h.
+// The output-only window is split into NSEG contiguous runs of steps: lane
+// col of a DPP row takes dim row col % PASSES and run col / PASSES, and the
+// runs' (R, G) pairs are then joined in step order ((R0, G0) followed by
+// (R1, G1) is (R0 G1 + R1, G0 G1)). Each B_j . C is formed once per DPP row
+// and handed to the lanes whose step it is. An entry count outside [0, L)
+// (not for the pad id) makes the sequence's y NaN and writes nothing.
 template <typename ST, typename IT, int N>
-__global__ __launch_bounds__(kMaxWaves *kWaveLanes, SSU_WAVES_PER_EU_MULTI) void ssu_replay_kernel(
+__global__ __launch_bounds__(kMaxWaves *kWaveLanes, replay_waves_per_eu(sizeof(ST), N)) void ssu_replay_kernel(
     const Params p, const ReplayParams rp) {
     constexpr int E = N / kLanesPerRow;
     constexpr int VEC = (16 / (int)sizeof(ST)) < E ? (16 / (int)sizeof(ST)) : E;
     constexpr int NCH = E / VEC;
-    constexpr int PASSES = passes_for(N, sizeof(ST), false);
+    constexpr int PASSES = passes_for(N, sizeof(ST), kTileReplay);
     constexpr int IVEC = VEC;
-    static_assert(PASSES <= kLanesPerRow, "one scalar-owning lane per pass");
+    // window runs per dim row, and B . C rounds (one per DPP row) per window step
+    constexpr int NSEG = kLanesPerRow / PASSES;
+    constexpr int NDOT = NSEG < kRowsPerPass ? 1 : NSEG / kRowsPerPass;
+    static_assert(PASSES <= kLanesPerRow && kLanesPerRow % PASSES == 0, "runs tile the row");
     using SPack = Pack<ST, VEC>;
+    using Bits = typename TokenInputs<IT, NCH, IVEC>::Bits;
 
     const int lane = threadIdx.x & (kWaveLanes - 1);
     const int wave = threadIdx.x / kWaveLanes;
@@ -526,101 +552,138 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes, SSU_WAVES_PER_EU_MULTI) void
 
     const int64_t s = p.rtab ? load_index(p.rtab, flags & kReadI64, b * p.r_s0) : b;
     const bool pad = s == p.pad;  // no checkpoint and no buffer: h is taken as 0
-    const int32_t hb =
-        pad ? 0 : static_cast<int32_t>(load_index(rp.buf_len, rp.len_i64, b * rp.len_s));
-    const bool flush = hb + 1 == rp.L;
-    const bool write = !pad && !(flags & kDisable);
+    const int64_t h_in = pad ? 0 : load_index(rp.buf_len, rp.len_i64, b * rp.len_s);
+    const bool bad = h_in < 0 || h_in >= rp.L;
+    const int32_t hb = bad ? 0 : static_cast<int32_t>(h_in);
+    const bool flush = !bad && hb + 1 == rp.L;
+    const bool write = !pad && !bad && !(flags & kDisable);
     const bool dt_f32 = flags & kDtF32;
+    const int dt_bytes = dt_f32 ? 4 : 2;
 
-    const int64_t tile_off = static_cast<int64_t>(h) * p.P * N;
-    ST *const pool = static_cast<ST *>(p.state);
-    ST *const sbase = pool + (pad ? 0 : s) * p.slot_stride + tile_off;
-
-    // the checkpoint tile (zeros for the pad id)
-    SPack S[PASSES][NCH];
-#pragma unroll
-    for (int q = 0; q < PASSES; q++) {
-        const int d = dw + q * kRowsPerPass + rsub;
-#pragma unroll
-        for (int c = 0; c < NCH; c++) {
-            if (!pad && d < p.P) {
-                S[q][c] = load_state(reinterpret_cast<const SPack *>(
-                    sbase + static_cast<int64_t>(d) * N + c * kLanesPerRow * VEC + col * VEC));
-            } else {
-#pragma unroll
-                for (int k = 0; k < VEC; k++)
-                    S[q][c].v[k] = narrow<ST>(0.0f);
-            }
-        }
-    }
+    const int P = p.P, H = p.H;
+    const int64_t tile_off = static_cast<int64_t>(h) * P * N;
+    ST *const sbase = static_cast<ST *>(p.state) + (pad ? 0 : s) * p.slot_stride + tile_off;
+    const int64_t sl = (pad ? 0 : s) * rp.L;  // first buffer entry of the slot
+    const IT *const xs = static_cast<const IT *>(p.x);
+    const IT *const zs = static_cast<const IT *>(p.z);
+    IT *const ys = static_cast<IT *>(p.out);
+    const unsigned char *const dts = static_cast<const unsigned char *>(p.dt);
+    const IT *const Bcur = static_cast<const IT *>(p.B) + (b * p.B_sr + g * p.B_sg + col * IVEC);
+    const IT *const Ccur = static_cast<const IT *>(p.C) + (b * p.C_sr + g * p.C_sg + col * IVEC);
+    IT *const bxs = static_cast<IT *>(rp.buf_x);
+    IT *const bBs = static_cast<IT *>(rp.buf_B);
+    unsigned char *const bdts = static_cast<unsigned char *>(rp.buf_dt);
 
     const float a_h = p.A[h * p.A_sh];
     const float d_h = p.D ? p.D[h * p.D_sh] : 0.0f;
     const float bias_h = p.dt_bias ? p.dt_bias[h * p.bias_sh] : 0.0f;
-    const IT *const xs = static_cast<const IT *>(p.x);
-    const IT *const zs = static_cast<const IT *>(p.z);
-    IT *const ys = static_cast<IT *>(p.out);
-    const IT *const Bcur = static_cast<const IT *>(p.B) + (b * p.B_sr + g * p.B_sg + col * IVEC);
-    const IT *const Ccur = static_cast<const IT *>(p.C) + (b * p.C_sr + g * p.C_sg + col * IVEC);
-    const int P = p.P, H = p.H;
-    const int64_t sl = (pad ? 0 : s) * rp.L;  // first buffer entry of the slot
-    IT *const bxs = static_cast<IT *>(rp.buf_x);
-    IT *const bBs = static_cast<IT *>(rp.buf_B);
-    unsigned char *const bdts = static_cast<unsigned char *>(rp.buf_dt);
-    const int dt_bytes = dt_f32 ? 4 : 2;
 
-    float Cv[E];
-#pragma unroll
-    for (int c = 0; c < NCH; c++) {
-        const RawWords<IT, IVEC> w = load_words<IT, IVEC>(Ccur + c * kLanesPerRow * IVEC);
-#pragma unroll
-        for (int k = 0; k < IVEC; k++)
-            Cv[c * IVEC + k] = word_elem(w, k);
-    }
-
-    // step j's B columns, x and raw dt of the lane's own row
-    auto step_B = [&](int32_t j, float *Bv) {
-        const IT *src = j < hb ? bBs + ((sl + j) * rp.G + g) * N + col * IVEC : Bcur;
-#pragma unroll
-        for (int c = 0; c < NCH; c++) {
-            const RawWords<IT, IVEC> w = load_words<IT, IVEC>(src + c * kLanesPerRow * IVEC);
-#pragma unroll
-            for (int k = 0; k < IVEC; k++)
-                Bv[c * IVEC + k] = word_elem(w, k);
-        }
+    // Inputs of step j (j < hb: buffer entry j; j == hb: the current step)
+    // for dim row d, which must be in range: a uniform base (the slot's
+    // entry 0 at this head or group, or the current row) plus a 32-bit lane
+    // offset (one slot's buffer spans fewer than 2^31 elements).
+    const IT *const bx0 = bxs + (sl * H + h) * P;
+    const unsigned char *const bdt0 = bdts + (rp.dt_per_head ? sl * H + h : (sl * H + h) * P) * dt_bytes;
+    const IT *const bB0 = bBs + (sl * rp.G + g) * N + col * IVEC;
+    const IT *const xcur0 = xs + (b * p.x_sr + h * p.x_sh);
+    const unsigned char *const dtcur0 = dts + static_cast<int64_t>(b * p.dt_sr + h * p.dt_sh) * dt_bytes;
+    const uint32_t HP = static_cast<uint32_t>(H * P), GN = static_cast<uint32_t>(rp.G * N);
+    auto x_at = [&](int32_t j, int d) -> const Bits * {
+        const IT *q = j < hb ? bx0 + (static_cast<uint32_t>(j) * HP + d) : xcur0 + static_cast<uint32_t>(d);
+        return reinterpret_cast<const Bits *>(q);
     };
-    auto step_x = [&](int32_t j) -> float {
-        const IT *src = j < hb ? bxs + ((sl + j) * H + h) * P + d_fetch
-                               : xs + (b * p.x_sr + h * p.x_sh + d_fetch);
-        return widen(*src);
+    auto dt_at = [&](int32_t j, int d) -> const unsigned char * {
+        return j < hb ? bdt0 + (static_cast<uint32_t>(j) * (rp.dt_per_head ? H : HP) +
+                                (rp.dt_per_head ? 0u : static_cast<uint32_t>(d))) * dt_bytes
+                      : dtcur0 + static_cast<uint32_t>(d * p.dt_sp * dt_bytes);
     };
-    auto step_dt = [&](int32_t j) -> float {
-        const unsigned char *src;
-        if (j < hb)
-            src = bdts + (rp.dt_per_head ? (sl + j) * H + h : ((sl + j) * H + h) * P + d_fetch) *
-                             dt_bytes;
-        else
-            src = static_cast<const unsigned char *>(p.dt) +
-                  static_cast<int64_t>(b * p.dt_sr + h * p.dt_sh + d_fetch * p.dt_sp) * dt_bytes;
-        float v = (dt_f32 ? *reinterpret_cast<const float *>(src)
-                          : widen(*reinterpret_cast<const IT *>(src))) + bias_h;
+    auto B_at = [&](int32_t j) -> const IT * {
+        return j < hb ? bB0 + static_cast<uint32_t>(j) * GN : Bcur;
+    };
+    auto step_dt = [&](uint16_t lo, uint16_t hi) {
+        float v = (dt_f32 ? __uint_as_float(uint32_t(lo) | (uint32_t(hi) << 16)) : from_bits<IT>(lo)) + bias_h;
         if (flags & kSoftplus)
             v = softplus(v);
         return v;
     };
 
-    float ysum = 0.0f, xcur = 0.0f;
+    // the lane's columns of C, the owner row's x and z (z read from x when
+    // there is no gate, to keep the load unconditional), the checkpoint tile
+    RawWords<IT, IVEC> cw[NCH];
+    Bits x_bits, z_bits;
+    uint16_t dto_lo, dto_hi;  // the owner row's dt, for the append
+    SPack S[PASSES][NCH];
+    auto load_current = [&]() {
+#pragma unroll
+        for (int c = 0; c < NCH; c++)
+            cw[c] = load_words<IT, IVEC>(Ccur + c * kLanesPerRow * IVEC);
+        const int64_t xo = b * p.x_sr + h * p.x_sh + d_fetch;
+        x_bits = *reinterpret_cast<const Bits *>(xs + xo);
+        z_bits = *reinterpret_cast<const Bits *>(zs ? zs + (b * p.z_sr + h * p.z_sh + d_fetch) : xs + xo);
+    };
+    // (rows past the dim read the last row; their results are never stored)
+    auto load_checkpoint = [&]() {
+        if (pad) {  // uniform
+#pragma unroll
+            for (int q = 0; q < PASSES; q++)
+#pragma unroll
+                for (int c = 0; c < NCH; c++)
+#pragma unroll
+                    for (int k = 0; k < VEC; k++)
+                        S[q][c].v[k] = narrow<ST>(0.0f);
+            return;
+        }
+#pragma unroll
+        for (int q = 0; q < PASSES; q++) {
+            const int d0 = dw + q * kRowsPerPass + rsub;
+            const uint32_t d = d0 < P ? d0 : P - 1;
+#pragma unroll
+            for (int c = 0; c < NCH; c++)
+                S[q][c] = load_state(reinterpret_cast<const SPack *>(
+                    sbase + (d * N + static_cast<uint32_t>(c * kLanesPerRow * VEC + col * VEC))));
+        }
+    };
+    float Cv[E];
+    auto decode_C = [&]() {
+#pragma unroll
+        for (int c = 0; c < NCH; c++)
+#pragma unroll
+            for (int k = 0; k < IVEC; k++)
+                Cv[c * IVEC + k] = word_elem(cw[c], k);
+    };
+
+    float ysum = 0.0f;
     if (flush) {
-        // replay the buffered steps and the current one through the update
-        for (int32_t j = 0; j <= hb; j++) {
-            float Bv[E];
-            step_B(j, Bv);
-            const float xv = step_x(j);
-            const float v = step_dt(j);
+        // Replay the buffered steps and the current one through the update,
+        // one step ahead in loads (two buffers, scheduling barriers: the
+        // vector-memory counter is in order; the prefetch past the last step
+        // reloads the last step, so no branch joins pending loads).
+        struct StepIn {
+            RawWords<IT, IVEC> b[NCH];
+            Bits x;
+            uint16_t dt_lo, dt_hi;
+        };
+        auto fetch_step = [&](int32_t j, StepIn &in) {
+            const IT *bsrc = B_at(j);
+#pragma unroll
+            for (int c = 0; c < NCH; c++)
+                in.b[c] = load_words<IT, IVEC>(bsrc + c * kLanesPerRow * IVEC);
+            in.x = *x_at(j, d_fetch);
+            const unsigned char *dp = dt_at(j, d_fetch);
+            in.dt_lo = *reinterpret_cast<const uint16_t *>(dp);
+            in.dt_hi = *reinterpret_cast<const uint16_t *>(dp + (dt_f32 ? 2 : 0));
+        };
+        auto run = [&](int32_t j, const StepIn &in) {
+            const float v = step_dt(in.dt_lo, in.dt_hi);
             const float decay = exp_hw(v * a_h);
-            const float dtx = v * xv;
+            const float dtx = v * from_bits<IT>(in.x);
             const bool last = j == hb;
-            xcur = xv;
+            float Bv[E];
+#pragma unroll
+            for (int c = 0; c < NCH; c++)
+#pragma unroll
+                for (int k = 0; k < IVEC; k++)
+                    Bv[c * IVEC + k] = word_elem(in.b[c], k);
             for_passes<0, PASSES>([&](auto qc) {
                 constexpr int q = decltype(qc)::value;
                 const float dq = row16_bcast<q>(decay);
@@ -641,6 +704,23 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes, SSU_WAVES_PER_EU_MULTI) void
                     ysum = col == q ? sum : ysum;
                 }
             });
+        };
+        StepIn in0, in1;
+        fetch_step(0, in0);
+        load_current();
+        load_checkpoint();
+        decode_C();
+        for (int32_t j = 0; j <= hb; j += 2) {
+            __builtin_amdgcn_sched_barrier(0);
+            fetch_step(j + 1 <= hb ? j + 1 : hb, in1);
+            __builtin_amdgcn_sched_barrier(0);
+            run(j, in0);
+            if (j + 1 > hb)
+                break;
+            __builtin_amdgcn_sched_barrier(0);
+            fetch_step(j + 2 <= hb ? j + 2 : hb, in0);
+            __builtin_amdgcn_sched_barrier(0);
+            run(j + 1, in1);
         }
         if (write) {
 #pragma unroll
@@ -656,7 +736,110 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes, SSU_WAVES_PER_EU_MULTI) void
             }
         }
     } else {
-        // u = S_ckpt . C of the lane's own row
+        // the lane's window row and run; run k holds steps k*SL .. k*SL+SL-1
+        const int kseg = col / PASSES;
+        const int d_win = dw + (col % PASSES) * kRowsPerPass + rsub;
+        const int d_wf = d_win < P ? d_win : 0;
+        const int32_t SL = (hb + NSEG) / NSEG;  // ceil((hb + 1) / NSEG)
+        struct WinIn {
+            RawWords<IT, IVEC> b[NDOT][NCH];  // B rows this DPP row dots with C
+            Bits x;
+            uint16_t dt_lo, dt_hi;
+        };
+        // loads for the t-th step of every run (steps past hb reload step hb)
+        auto fetch_win = [&](int32_t t, WinIn &in) {
+#pragma unroll
+            for (int rr = 0; rr < NDOT; rr++) {
+                const int kd = NSEG < kRowsPerPass ? rsub % NSEG : rr * kRowsPerPass + rsub;
+                const int32_t jd = kd * SL + t;
+                const IT *src = B_at(jd < hb ? jd : hb);
+#pragma unroll
+                for (int c = 0; c < NCH; c++)
+                    in.b[rr][c] = load_words<IT, IVEC>(src + c * kLanesPerRow * IVEC);
+            }
+            const int32_t j = kseg * SL + t;
+            const int32_t jc = j < hb ? j : hb;
+            in.x = *x_at(jc, d_wf);
+            const unsigned char *dp = dt_at(jc, d_wf);
+            in.dt_lo = *reinterpret_cast<const uint16_t *>(dp);
+            in.dt_hi = *reinterpret_cast<const uint16_t *>(dp + (dt_f32 ? 2 : 0));
+        };
+        float R = 0.0f, G = 1.0f;
+        auto run_win = [&](int32_t t, const WinIn &in) {
+            // B_jd . C for this DPP row's steps, then the lane's own one:
+            // run k's value sits in DPP row k % 4 of round k / 4
+            float w = 0.0f;
+#pragma unroll
+            for (int rr = 0; rr < NDOT; rr++) {
+                float part = 0.0f;
+#pragma unroll
+                for (int c = 0; c < NCH; c++)
+#pragma unroll
+                    for (int k = 0; k < IVEC; k++)
+                        part = fmaf(word_elem(in.b[rr][c], k), Cv[c * IVEC + k], part);
+                const float dot = row16_sum(part);
+                const int src = ((kseg % kRowsPerPass) * kLanesPerRow + col) * 4;
+                const float got = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(dot)));
+                w = kseg / kRowsPerPass == rr ? got : w;
+            }
+            const int32_t j = kseg * SL + t;
+            const bool valid = j <= hb;
+            const float v = step_dt(in.dt_lo, in.dt_hi);
+            const float alpha = valid ? exp_hw(v * a_h) : 1.0f;
+            const float term = valid ? v * from_bits<IT>(in.x) * w : 0.0f;
+            R = fmaf(R, alpha, term);
+            G = G * alpha;
+        };
+        // the first T0 steps of every run are requested before the tile
+        // (as many as about 32 registers hold)
+        constexpr int kWinWords = NDOT * NCH * RawWords<IT, IVEC>::kWords + 2;
+        constexpr int T0 = SSU_REPLAY_PREFETCH < 32 / kWinWords ? SSU_REPLAY_PREFETCH
+                           : (32 / kWinWords < 1 ? 1 : 32 / kWinWords);
+        WinIn wb[T0];
+        fetch_win(0, wb[0]);
+#pragma unroll
+        for (int i = 1; i < T0; i++)
+            if (i < SL)  // uniform
+                fetch_win(i, wb[i]);
+        load_current();
+        const unsigned char *dpo = dt_at(hb, d_fetch);
+        dto_lo = *reinterpret_cast<const uint16_t *>(dpo);
+        dto_hi = *reinterpret_cast<const uint16_t *>(dpo + (dt_f32 ? 2 : 0));
+        load_checkpoint();
+        decode_C();
+#pragma unroll
+        for (int i = 0; i < T0; i++)
+            if (i < SL)
+                run_win(i, wb[i]);
+        // longer runs: one step ahead in loads, as in the fold
+        WinIn w0, w1;
+        if (SL > T0) {
+            fetch_win(T0, w0);
+            for (int32_t t = T0; t < SL; t += 2) {
+                __builtin_amdgcn_sched_barrier(0);
+                fetch_win(t + 1 < SL ? t + 1 : SL - 1, w1);
+                __builtin_amdgcn_sched_barrier(0);
+                run_win(t, w0);
+                if (t + 1 >= SL)
+                    break;
+                __builtin_amdgcn_sched_barrier(0);
+                fetch_win(t + 2 < SL ? t + 2 : SL - 1, w0);
+                __builtin_amdgcn_sched_barrier(0);
+                run_win(t + 1, w1);
+            }
+        }
+        // join the runs in step order: the run PASSES lanes up follows
+        for_passes<0, 4>([&](auto lc) {
+            constexpr int span = PASSES << decltype(lc)::value;
+            if constexpr (span < kLanesPerRow) {
+                constexpr int ctrl = 0x120 + (kLanesPerRow - span);  // row_ror: lane i reads lane i + span
+                const float Rn = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(R), ctrl, 0xF, 0xF, false));
+                const float Gn = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(G), ctrl, 0xF, 0xF, false));
+                R = fmaf(R, Gn, Rn);
+                G = G * Gn;
+            }
+        });
+        // u = S_ckpt . C of the lane's own row (run 0 lanes are the owners)
         float u = 0.0f;
         for_passes<0, PASSES>([&](auto qc) {
             constexpr int q = decltype(qc)::value;
@@ -669,62 +852,40 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes, SSU_WAVES_PER_EU_MULTI) void
             const float sum = row16_sum(acc);
             u = col == q ? sum : u;
         });
-        // the window over the buffered steps and the current one
-        float G = 1.0f, R = 0.0f;
-        for (int32_t j = 0; j <= hb; j++) {
-            float Bv[E];
-            step_B(j, Bv);
-            const float xv = step_x(j);
-            const float v = step_dt(j);
-            float part = 0.0f;
-#pragma unroll
-            for (int e = 0; e < E; e++)
-                part = fmaf(Bv[e], Cv[e], part);
-            const float w = row16_sum(part);  // B_j . C
-            const float alpha = exp_hw(v * a_h);
-            R = fmaf(R, alpha, v * xv * w);
-            G = G * alpha;
-            xcur = xv;
-        }
-        ysum = G * u + R;
+        ysum = fmaf(G, u, R);
         // append the step's raw inputs at entry hb
         if (write) {
-            if (owner) {
-                bxs[((sl + hb) * H + h) * P + d_own] = xs[b * p.x_sr + h * p.x_sh + d_own];
-                if (!rp.dt_per_head) {
-                    const int64_t di = b * p.dt_sr + h * p.dt_sh + d_own * p.dt_sp;
-                    unsigned char *dst = bdts + (((sl + hb) * H + h) * P + d_own) * dt_bytes;
-                    if (dt_f32)
-                        *reinterpret_cast<float *>(dst) = static_cast<const float *>(p.dt)[di];
-                    else
-                        *reinterpret_cast<IT *>(dst) = static_cast<const IT *>(p.dt)[di];
-                }
-            }
-            if (rp.dt_per_head && tile == 0 && threadIdx.x == 0) {
-                const int64_t di = b * p.dt_sr + h * p.dt_sh;
-                unsigned char *dst = bdts + ((sl + hb) * H + h) * dt_bytes;
+            const int64_t e = sl + hb;
+            auto put_dt = [&](unsigned char *dst) {
                 if (dt_f32)
-                    *reinterpret_cast<float *>(dst) = static_cast<const float *>(p.dt)[di];
+                    *reinterpret_cast<uint32_t *>(dst) = uint32_t(dto_lo) | (uint32_t(dto_hi) << 16);
                 else
-                    *reinterpret_cast<IT *>(dst) = static_cast<const IT *>(p.dt)[di];
+                    *reinterpret_cast<uint16_t *>(dst) = dto_lo;
+            };
+            if (owner) {
+                *reinterpret_cast<Bits *>(bxs + (e * H + h) * P + d_own) = x_bits;
+                if (!rp.dt_per_head)
+                    put_dt(bdts + ((e * H + h) * P + d_own) * dt_bytes);
             }
+            if (rp.dt_per_head && tile == 0 && threadIdx.x == 0)
+                put_dt(bdts + (e * H + h) * dt_bytes);  // lane 0 owns a row; dt is the head's
             if (h % p.heads_per_group == 0 && tile == 0 && wave == 0 && rsub == 0) {
-                IT *dst = bBs + ((sl + hb) * rp.G + g) * N + col * IVEC;
+                IT *dst = bBs + (e * rp.G + g) * N + col * IVEC;
 #pragma unroll
-                for (int c = 0; c < NCH; c++)
-#pragma unroll
-                    for (int k = 0; k < IVEC; k++)
-                        dst[c * kLanesPerRow * IVEC + k] = Bcur[c * kLanesPerRow * IVEC + k];
+                for (int c = 0; c < NCH; c++) {
+                    store_words<IT, IVEC>(dst + c * kLanesPerRow * IVEC,
+                                          load_words<IT, IVEC>(Bcur + c * kLanesPerRow * IVEC));
+                }
             }
         }
     }
 
     // y of the lane's own row
     if (owner) {
-        float y = ysum + d_h * xcur;
+        float y = ysum + d_h * from_bits<IT>(x_bits);
         if (zs)
-            y *= silu(widen(zs[b * p.z_sr + h * p.z_sh + d_own]));
-        ys[b * p.out_sr + h * p.out_sh + d_own] = narrow<IT>(y);
+            y *= silu(from_bits<IT>(z_bits));
+        ys[b * p.out_sr + h * p.out_sh + d_own] = narrow<IT>(bad ? __builtin_nanf("") : y);
     }
 }
 

@@ -28,6 +28,11 @@ CASES = [
     ("f16", "f16", 3, True, 64, 64),
     ("f32", "f32", 5, False, 32, 28),
     ("f32", "bf16", 2, False, 256, 64),
+    # long windows for each split of a dim row's window into runs of steps
+    # (8 runs: fp32 state, dstate 256; 4: fp32, dstate 128; 2: 16-bit state)
+    ("f32", "bf16", 16, False, 256, 64),
+    ("bf16", "bf16", 16, True, 128, 64),
+    ("f32", "f16", 33, False, 64, 64),
 ]
 
 
@@ -37,7 +42,8 @@ CASES = [
 def test_replay_small(sd, io, L, per_head, N, P):
     c = W.replay(seed=20 + L + N, batch=24, heads=8, dim=P, dstate=N, groups=2, slots=40, L=L,
                  state_dtype=sd, io=io, dt_per_head=per_head)
-    # make sure both kinds of step occur
+    # make sure both kinds of step occur, and every window length up to L
+    c["buf_len"][:] = np.arange(24) % L
     c["buf_len"][:3] = [0, L - 1, L // 2]
     G.check_replay(c, "replay %s %s L=%d" % (sd, io, L))
 
@@ -126,3 +132,25 @@ def test_replay_full_workload():
         sub_got[k] = got[k][used]
     stats = G.compare_replay(sub, sub_got, ref, "replay full")
     G.say("[gpu] replay full: ok %s" % {k: "%.3g" % v for k, v in stats.items()})
+
+
+def test_replay_out_of_range_counts():
+    """buf_len outside [0, L) for a live slot: that sequence's y is NaN and
+    nothing of it is written; the other sequences are unaffected."""
+    L = 8
+    c = W.replay(seed=11, batch=12, heads=8, dim=64, dstate=128, groups=2, slots=20, L=L)
+    bad = [2, 7, 9]
+    c["buf_len"][bad] = [L, -1, L + 5]
+    G.say("[gpu] replay out-of-range counts: launching")
+    got = G.run_gpu_replay(c)
+    assert np.isnan(G.brute64.to_f64(got["y"][bad], c["io_dtype"])).all()
+    tab = np.asarray(c["state_batch_indices"])
+    for k in ("state", "buf_x", "buf_dt", "buf_B"):
+        assert np.array_equal(got[k][tab[bad]], np.asarray(c[k])[tab[bad]]), k
+    good = [b for b in range(12) if b not in bad]
+    sub, used = G.replay_subcase(c, good)
+    ref = ssu_oracle.run_replay(sub)
+    sub_got = {"y": got["y"][good], "state": got["state"][used]}
+    for k in ("buf_x", "buf_dt", "buf_B"):
+        sub_got[k] = got[k][used]
+    G.compare_replay(sub, sub_got, ref, "replay, valid rows")
