@@ -214,3 +214,91 @@ def run_replay(case):
     out["y"] = from_f64(Y, io)
     out["y64"] = Y
     return out
+
+
+def run_replay_spec(case):
+    """ReplaySSM speculative step in float64 (readings R21..R23 of the C
+    oracle): T drafts per sequence; when h + 2T > L the h committed entries
+    are first applied to the checkpoint (stored), and the window restarts
+    empty; draft t is read out over the window's committed entries and drafts
+    0..t; the drafts are appended after the window's committed entries."""
+    sd, io = case["state_dtype"], case["io_dtype"]
+    dtd = case.get("dt_dtype", io)
+    pool = np.asarray(case["state"])
+    slots, H, P, N = pool.shape
+    L = int(case["L"])
+    x = np.asarray(case["x"])
+    Bt, T = x.shape[:2]
+    X = to_f64(x, io)
+    dt = np.asarray(case["dt"])
+    per_head = dt.ndim == 3
+    DT = to_f64(dt, dtd)
+    Bm, Cm = to_f64(case["B"], io), to_f64(case["C"], io)
+    G = Bm.shape[2]
+    Z = None if case.get("z") is None else to_f64(case["z"], io)
+    A = np.asarray(case["A"], np.float64)
+    Dv = None if case.get("D") is None else np.asarray(case["D"], np.float64)
+    bias = None if case.get("dt_bias") is None else np.asarray(case["dt_bias"], np.float64)
+    pad = int(case.get("pad_slot_id", -1))
+    disable = bool(case.get("disable_state_update", False))
+    tab = case.get("state_batch_indices")
+    bx, bdt, bB = (np.asarray(case["buf_x"]), np.asarray(case["buf_dt"]),
+                   np.asarray(case["buf_B"]))
+    out = {"state": pool.copy(), "buf_x": bx.copy(), "buf_dt": bdt.copy(), "buf_B": bB.copy(),
+           "written": np.zeros(slots, dtype=bool)}
+    Y = np.zeros((Bt, T, H, P))
+
+    def proc(v, h):
+        if bias is not None:
+            v = v + bias[h]
+        if case.get("dt_softplus", False):
+            v = np.where(v > 20.0, v, np.log1p(np.exp(np.minimum(v, 20.0))))
+        return v
+
+    for b in range(Bt):
+        s = b if tab is None else int(np.asarray(tab)[b])
+        hc = 0 if s == pad else int(np.asarray(case["buf_len"])[b])
+        fold = hc + 2 * T > L
+        w = 0 if fold else hc
+        for h in range(H):
+            g = h // (H // G)
+
+            def entry(j):  # (dt' over dim, x, B) of buffer entry j
+                d = np.full(P, to_f64(bdt[s, j, h], dtd)) if per_head else to_f64(bdt[s, j, h], dtd)
+                return proc(d, h), to_f64(bx[s, j, h], io), to_f64(bB[s, j, g], io)
+
+            def draft(t):
+                d = np.full(P, DT[b, t, h]) if per_head else DT[b, t, h]
+                return proc(d, h), X[b, t, h], Bm[b, t, g]
+
+            S = np.zeros((P, N)) if s == pad else to_f64(pool[s, h], sd)
+            if fold:
+                for j in range(hc):
+                    st, xv, Bv = entry(j)
+                    S = S * np.exp(st * A[h])[:, None] + np.outer(st * xv, Bv)
+                    S = to_f64(from_f64(S, sd), sd)
+                if s != pad and not disable:
+                    out["state"][s, h] = from_f64(S, sd)
+                    out["written"][s] = True
+            steps = [entry(j) for j in range(w)] + [draft(t) for t in range(T)]
+            for t in range(T):
+                C = Cm[b, t, g]
+                window = steps[:w + t + 1]
+                alphas = [np.exp(st * A[h]) for st, _, _ in window]
+                y = np.prod(alphas, axis=0) * (S @ C)
+                for j, (st, xv, Bv) in enumerate(window):
+                    tail = np.prod(alphas[j + 1:], axis=0) if j + 1 < len(window) else np.ones(P)
+                    y = y + st * xv * tail * (Bv @ C)
+                if Dv is not None:
+                    y = y + Dv[h] * X[b, t, h]
+                if Z is not None:
+                    y = y * (Z[b, t, h] / (1.0 + np.exp(-Z[b, t, h])))
+                Y[b, t, h] = y
+            if s != pad and not disable:
+                for t in range(T):
+                    out["buf_x"][s, w + t, h] = x[b, t, h]
+                    out["buf_dt"][s, w + t, h] = dt[b, t, h]
+                    out["buf_B"][s, w + t, g] = np.asarray(case["B"])[b, t, g]
+    out["y"] = from_f64(Y, io)
+    out["y64"] = Y
+    return out

@@ -675,3 +675,174 @@ int oracle_replay(const oracle_replay_args *ra, char *err, int errlen)
     free(xs);
     return 0;
 }
+
+/* ---- ReplaySSM speculative step: T draft tokens per sequence
+ *
+ * ReplaySSM article (lpnh.cn), section "投机解码回滚变成挪指针" (speculative
+ * decoding: rollback becomes moving a pointer). The inputs of all T draft
+ * tokens are appended to the same buffer and the caller commits the accepted
+ * prefix by advancing the buffer pointer; every draft query is evaluated
+ * against the same checkpoint and buffer window, the drafts differing only by
+ * the causal mask; the fold is triggered one window early, at h + 2T > L
+ * instead of the natural h + T > L, so that a step always has T free entries.
+ *
+ * Readings (the page gives the rule, not the layout of a folding step):
+ *  R21 x, dt, z are [batch, T, H, P] (dt [batch, T, H] per head), B and C
+ *      [batch, T, G, N]; h = buf_len[b] committed entries, 0 <= h <= L,
+ *      1 <= T <= L. If h + 2T > L the step folds first: the h committed
+ *      entries are applied to the checkpoint one plain update after the other
+ *      (rounded to the state dtype after each) and the checkpoint is stored;
+ *      the window then starts empty (w = 0). Otherwise w = h and the
+ *      checkpoint is only read;
+ *  R22 draft t's output, with the steps k of the window being the w committed
+ *      entries followed by drafts 0..t, a_k = exp(dt'_k A[h]) and S the
+ *      checkpoint (folded or not):
+ *        y_t = (prod_k a_k) (S . C_t) + sum_j dt'_j x_j (prod_{k>j} a_k) (B_j . C_t)
+ *              + D x_t, times silu(z_t)
+ *      (the unrolled window of "核心做法" with the causal mask);
+ *  R23 the drafts' raw inputs are written to entries w .. w+T-1; the caller
+ *      then sets the pointer to w + the accepted count. The pad id reads a
+ *      zero checkpoint, has no buffer (h taken as 0) and writes nothing;
+ *      disable_state_update writes neither checkpoint nor buffer.
+ */
+int oracle_replay_spec(const oracle_replay_args *ra, char *err, int errlen)
+{
+    const oracle_args *a = &ra->base;
+    const int64_t H = a->H, P = a->P, N = a->N, G = a->G, L = ra->L, T = a->steps;
+    const int64_t per_group = H / G, tile = P * N;
+    if (a->layout != OR_DENSE || T < 1 || T > L || a->R % T || a->wtab.data || a->acc || H % G) {
+        set_err(err, errlen, "speculative replay takes [batch, T, ...] inputs with 1 <= T <= L%lld%lld", 0, 0);
+        return 1;
+    }
+    if (a->rtab.data && a->rtab.ndim != 1) {
+        set_err(err, errlen, "replay takes a 1-D slot table%lld%lld", 0, 0);
+        return 1;
+    }
+    const int64_t nseq = a->R / T;
+    const int64_t dtw = a->dt_per_head ? 1 : P;
+    for (int64_t b = 0; b < nseq; b++) {
+        const int64_t s = a->rtab.data ? a->rtab.data[b] : b;
+        const int64_t h = ra->buf_len[b];
+        if (s == a->pad)
+            continue;
+        if (h < 0 || h > L) {
+            set_err(err, errlen, "buffer length %lld of sequence %lld outside [0, L]", (long long)h, (long long)b);
+            return 1;
+        }
+        if (s < 0 || s >= a->slots) {
+            set_err(err, errlen, "slot %lld of sequence %lld outside the pool", (long long)s, (long long)b);
+            return 1;
+        }
+        for (int64_t b2 = 0; b2 < b; b2++)
+            if ((a->rtab.data ? a->rtab.data[b2] : b2) == s) {
+                set_err(err, errlen, "slot %lld used by two sequences (second: %lld)", (long long)s, (long long)b);
+                return 1;
+            }
+    }
+    float *S = (float *)malloc((size_t)tile * sizeof(float));
+    float *alpha = (float *)malloc((size_t)(L + T) * sizeof(float));
+    float *dtp = (float *)malloc((size_t)(L + T) * sizeof(float));
+    float *xs = (float *)malloc((size_t)(L + T) * sizeof(float));
+    for (int64_t b = 0; b < nseq; b++) {
+        const int64_t s = a->rtab.data ? a->rtab.data[b] : b;
+        const int pad = s == a->pad;
+        const int64_t h = pad ? 0 : ra->buf_len[b]; /* R23 */
+        const int fold = h + 2 * T > L;               /* R21: one window early */
+        const int64_t w = fold ? 0 : h;
+        if (a->read_slot)
+            a->read_slot[b] = s;
+        for (int64_t hd = 0; hd < H; hd++) {
+            const int64_t g = hd / per_group;
+            /* buffer entry j of this slot */
+#define BX(j, d) load_as_f32(ra->bx_in, a->io_dtype, ((s * L + (j)) * H + hd) * P + (d))
+#define BDT(j, d) load_as_f32(ra->bdt_in, a->dt_dtype, ((s * L + (j)) * H + hd) * dtw + (a->dt_per_head ? 0 : (d)))
+#define BB(j, n) load_as_f32(ra->bB_in, a->io_dtype, ((s * L + (j)) * G + g) * N + (n))
+            /* draft t of this sequence: packed row b*T + t */
+#define DX(t, d) load_as_f32(a->x, a->io_dtype, ((b * T + (t)) * H + hd) * P + (d))
+#define DDT(t, d) load_as_f32(a->dt, a->dt_dtype, ((b * T + (t)) * H + hd) * dtw + (a->dt_per_head ? 0 : (d)))
+#define DB(t, n) load_as_f32(a->B, a->io_dtype, ((b * T + (t)) * G + g) * N + (n))
+#define DC(t, n) load_as_f32(a->C, a->io_dtype, ((b * T + (t)) * G + g) * N + (n))
+            for (int64_t e = 0; e < tile; e++)
+                S[e] = pad ? 0.0f : load_as_f32(a->pool_in, a->state_dtype, (s * H + hd) * tile + e);
+            if (fold) {
+                /* apply the committed entries to the checkpoint */
+                for (int64_t j = 0; j < h; j++) {
+                    for (int64_t d = 0; d < P; d++) {
+                        const float v = processed_dt(a, BDT(j, d), hd);
+                        const float decay = expf(v * a->A[hd]);
+                        const float dtx = v * BX(j, d);
+                        for (int64_t n = 0; n < N; n++)
+                            S[d * N + n] = S[d * N + n] * decay + dtx * BB(j, n);
+                    }
+                    for (int64_t e = 0; e < tile; e++) /* R21: rounded after each */
+                        S[e] = through_dtype(a->state_dtype, S[e]);
+                }
+                if (!pad && !a->disable) {
+                    for (int64_t e = 0; e < tile; e++)
+                        store_from_f32(a->pool_out, a->state_dtype, (s * H + hd) * tile + e, S[e]);
+                    if (a->written)
+                        a->written[s] = 1;
+                }
+            }
+            for (int64_t d = 0; d < P; d++) {
+                /* the window: w committed entries, then the T drafts */
+                for (int64_t k = 0; k < w + T; k++) {
+                    const float raw = k < w ? BDT(k, d) : DDT(k - w, d);
+                    dtp[k] = processed_dt(a, raw, hd);
+                    alpha[k] = expf(dtp[k] * a->A[hd]);
+                    xs[k] = k < w ? BX(k, d) : DX(k - w, d);
+                }
+                for (int64_t t = 0; t < T; t++) {
+                    const int64_t last = w + t; /* draft t's place in the window */
+                    float u = 0.0f;             /* S . C_t */
+                    for (int64_t n = 0; n < N; n++)
+                        u = u + S[d * N + n] * DC(t, n);
+                    float gamma = 1.0f;
+                    for (int64_t k = 0; k <= last; k++)
+                        gamma = gamma * alpha[k];
+                    float y = gamma * u;
+                    for (int64_t j = 0; j <= last; j++) {
+                        float tail = 1.0f; /* prod_{j < k <= last} a_k */
+                        for (int64_t k = j + 1; k <= last; k++)
+                            tail = tail * alpha[k];
+                        float wj = 0.0f; /* B_j . C_t */
+                        for (int64_t n = 0; n < N; n++)
+                            wj = wj + (j < w ? BB(j, n) : DB(j - w, n)) * DC(t, n);
+                        y = y + dtp[j] * xs[j] * tail * wj;
+                    }
+                    if (a->D)
+                        y = y + a->D[hd] * xs[last];
+                    if (a->z)
+                        y = y * silu(load_as_f32(a->z, a->io_dtype, ((b * T + t) * H + hd) * P + d));
+                    store_from_f32(a->out, a->io_dtype, ((b * T + t) * H + hd) * P + d, y);
+                }
+            }
+            /* append the drafts at entries w .. w+T-1 */
+            if (!pad && !a->disable) {
+                for (int64_t t = 0; t < T; t++) {
+                    for (int64_t d = 0; d < P; d++)
+                        copy_elem(ra->bx_out, a->x, a->io_dtype, ((s * L + w + t) * H + hd) * P + d,
+                                  ((b * T + t) * H + hd) * P + d);
+                    for (int64_t d = 0; d < dtw; d++)
+                        copy_elem(ra->bdt_out, a->dt, a->dt_dtype, ((s * L + w + t) * H + hd) * dtw + d,
+                                  ((b * T + t) * H + hd) * dtw + d);
+                    for (int64_t n = 0; n < N; n++)
+                        copy_elem(ra->bB_out, a->B, a->io_dtype, ((s * L + w + t) * G + g) * N + n,
+                                  ((b * T + t) * G + g) * N + n);
+                }
+            }
+#undef BX
+#undef BDT
+#undef BB
+#undef DX
+#undef DDT
+#undef DB
+#undef DC
+        }
+    }
+    free(S);
+    free(alpha);
+    free(dtp);
+    free(xs);
+    return 0;
+}

@@ -248,30 +248,47 @@ def run_replay(case, oracle=None):
       buf_B     [slots, L, G, N]        io dtype
       buf_len   [batch] integer: entries in each sequence's buffer (< L)
     Returns dict(y, state, buf_x, buf_dt, buf_B, written)."""
+    return _run_replay(case, oracle, spec=False)
+
+
+def run_replay_spec(case, oracle=None):
+    """ReplaySSM speculative step (oracle_replay_spec): as run_replay with
+    x, dt, z [batch, T, H, P] (dt [batch, T, H] per head) and B, C
+    [batch, T, G, N] holding T draft tokens per sequence; buf_len in [0, L].
+    y has x's shape."""
+    return _run_replay(case, oracle, spec=True)
+
+
+def _run_replay(case, oracle, spec):
     orc = oracle or default()
     lib = orc.lib
     if not hasattr(lib, "_replay_ready"):
-        lib.oracle_replay.argtypes = [ctypes.POINTER(_ReplayArgs), ctypes.c_char_p, ctypes.c_int]
-        lib.oracle_replay.restype = ctypes.c_int
+        for f in (lib.oracle_replay, lib.oracle_replay_spec):
+            f.argtypes = [ctypes.POINTER(_ReplayArgs), ctypes.c_char_p, ctypes.c_int]
+            f.restype = ctypes.c_int
         lib._replay_ready = True
     sd, io = case["state_dtype"], case["io_dtype"]
     dtd = case.get("dt_dtype", io)
     state = _arr(case["state"], _np_dtype(sd))
     slots, H, P, N = state.shape
-    x = _arr(case["x"], _np_dtype(io))
-    if x.ndim != 3 or case.get("cu_seqlens") is not None or \
+    x = np.asarray(case["x"])
+    if x.ndim != (4 if spec else 3) or case.get("cu_seqlens") is not None or \
             case.get("num_accepted_tokens") is not None or \
             case.get("dst_state_batch_indices") is not None:
-        raise OracleError("replay takes x [batch, heads, dim], one slot table and nothing else")
-    R = x.shape[0]
+        raise OracleError("replay takes x [batch, %sheads, dim], one slot table and nothing else"
+                          % ("T, " if spec else ""))
+    T = x.shape[1] if spec else 1
+    R = x.shape[0] * T
+    xr = _arr(x.reshape(R, H, P), _np_dtype(io))
     dt = np.asarray(case["dt"])
-    dt_per_head = dt.ndim == 2
-    dtr = _arr(dt, _np_dtype(dtd))
-    Bm = _arr(case["B"], _np_dtype(io))
-    G = Bm.shape[1]
-    Cm = _arr(case["C"], _np_dtype(io))
+    dt_per_head = dt.ndim == x.ndim - 1
+    dtr = _arr(dt.reshape((R, H) if dt_per_head else (R, H, P)), _np_dtype(dtd))
+    Bm = np.asarray(case["B"])
+    G = Bm.shape[-2]
+    Br = _arr(Bm.reshape(R, G, N), _np_dtype(io))
+    Cr = _arr(np.asarray(case["C"]).reshape(R, G, N), _np_dtype(io))
     z = case.get("z")
-    z = None if z is None else _arr(z, _np_dtype(io))
+    zr = None if z is None else _arr(np.asarray(z).reshape(R, H, P), _np_dtype(io))
     A = _arr(case["A"], np.float32)
     D = case.get("D")
     D = None if D is None else _arr(D, np.float32)
@@ -296,12 +313,15 @@ def run_replay(case, oracle=None):
     base.state_dtype = DTYPES[sd]
     base.slots, base.H, base.P, base.N, base.G = slots, H, P, N, G
     base.R, base.io_dtype = R, DTYPES[io]
-    base.x, base.dt = _ptr(x), _ptr(dtr)
+    base.x, base.dt = _ptr(xr), _ptr(dtr)
     base.dt_dtype, base.dt_per_head = DTYPES[dtd], int(dt_per_head)
-    base.A, base.B, base.C = _ptr(A), _ptr(Bm), _ptr(Cm)
-    base.D, base.z, base.dt_bias = _ptr(D), _ptr(z), _ptr(bias)
+    base.A, base.B, base.C = _ptr(A), _ptr(Br), _ptr(Cr)
+    base.D, base.z, base.dt_bias = _ptr(D), _ptr(zr), _ptr(bias)
     base.dt_softplus = int(bool(case.get("dt_softplus", False)))
-    base.layout, base.steps, base.nseq = ONE_TOKEN, 0, R
+    if spec:
+        base.layout, base.steps, base.nseq = DENSE, T, x.shape[0]
+    else:
+        base.layout, base.steps, base.nseq = ONE_TOKEN, 0, R
     base.rtab = _table(case.get("state_batch_indices"), keep)
     base.wtab = _table(None, keep)
     base.pad = int(case.get("pad_slot_id", -1))
@@ -313,7 +333,8 @@ def run_replay(case, oracle=None):
     args.bB_in, args.bB_out = _ptr(bB), _ptr(bB_out)
     args.buf_len = _ptr(blen)
     err = ctypes.create_string_buffer(256)
-    if lib.oracle_replay(ctypes.byref(args), err, 256):
+    fn = lib.oracle_replay_spec if spec else lib.oracle_replay
+    if fn(ctypes.byref(args), err, 256):
         raise OracleError(err.value.decode())
-    return {"y": out, "state": pool_out, "buf_x": bx_out, "buf_dt": bdt_out, "buf_B": bB_out,
-            "written": written.astype(bool)}
+    return {"y": out.reshape(x.shape), "state": pool_out, "buf_x": bx_out, "buf_dt": bdt_out,
+            "buf_B": bB_out, "written": written.astype(bool)}

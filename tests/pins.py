@@ -679,6 +679,191 @@ def pin_replay_brute_force(orc, combos=24, seed=11):
         assert np.all(np.abs(y_o - b["y64"]) <= tol), (k, io, L)
 
 
+# ------------------------------------------------ ReplaySSM, speculative step
+
+def _spec_case(L, T, buf_len, sd="f32", io="f32", **kw):
+    base = dict(batch=4, heads=4, dim=8, dstate=16, groups=2, slots=8)
+    base.update(kw)
+    return W.replay_spec(L=L, T=T, buf_len=buf_len, state_dtype=sd, io=io, **base)
+
+
+def _spec_chain(orc, c, b, entries):
+    """Plain update over one sequence: from slot s's checkpoint, the buffer
+    entries `entries` of the slot and then the T drafts of sequence b, one
+    token after the other (dense [1, steps] form). Returns (y [steps, H, P],
+    pool after the first len(entries) steps, pool after all)."""
+    s = int(np.asarray(c["state_batch_indices"])[b])
+    T = np.shape(c["x"])[1]
+    per_head = np.ndim(c["dt"]) == 3
+    rows = {}
+    for k, buf in (("x", "buf_x"), ("dt", "buf_dt"), ("B", "buf_B")):
+        rows[k] = np.concatenate([np.asarray(c[buf])[s, list(entries)],
+                                  np.asarray(c[k])[b]], axis=0)[None]
+    rows["C"] = np.concatenate([np.asarray(c["C"])[b][:1].repeat(len(entries), 0),
+                                np.asarray(c["C"])[b]], axis=0)[None]
+    if c.get("z") is not None:
+        rows["z"] = np.concatenate([np.asarray(c["z"])[b][:1].repeat(len(entries), 0),
+                                    np.asarray(c["z"])[b]], axis=0)[None]
+    plain = {k: v for k, v in c.items()
+             if k not in ("L", "buf_x", "buf_dt", "buf_B", "buf_len")}
+    plain.update(rows)
+    plain["state_batch_indices"] = np.array([[s] * (len(entries) + T)], np.int64)
+    plain["dst_state_batch_indices"] = np.array([list(range(len(entries) + T))], np.int64) + \
+        np.shape(c["state"])[0]
+    pool = np.asarray(c["state"])
+    plain["state"] = np.concatenate([pool, np.zeros((len(entries) + T,) + pool.shape[1:],
+                                                    pool.dtype)], axis=0)
+    o = orc.run(plain)
+    nslots = pool.shape[0]
+    after_entries = o["state"][nslots + len(entries) - 1] if entries else pool[s]
+    return o["y"][0], after_entries, per_head
+
+
+def pin_replay_spec_is_chain(orc):
+    """Speculative step (ReplaySSM article, "投机解码回滚变成挪指针"): draft t's
+    y equals the plain update's y after the committed entries and drafts
+    0..t (the causal mask), to fp32 accuracy; a folding step (h + 2T > L)
+    stores the checkpoint the plain update reaches after the committed entries
+    bit for bit, and the drafts go to entries w..w+T-1 (w = 0 after a fold)."""
+    from oracle import ssu_oracle
+    for sd, io in (("f32", "f32"), ("bf16", "f32")):
+        L, T = 8, 3
+        c = _spec_case(L, T, [0, 2, 3, 5], sd=sd, io=io)  # folds: h > L - 2T = 2
+        r = ssu_oracle.run_replay_spec(c, orc)
+        for b, h in enumerate(c["buf_len"]):
+            s = int(c["state_batch_indices"][b])
+            fold = h + 2 * T > L
+            w = 0 if fold else h
+            y, after, _ = _spec_chain(orc, c, b, range(h))
+            scale = np.abs(y).max() + 1.0
+            tol = 1e-5 if sd == "f32" else 2e-2
+            got = r["y"][b].astype(np.float64)
+            assert np.abs(got - y[h:]).max() <= tol * scale, (sd, b)
+            if fold:
+                assert r["written"][s] and np.array_equal(r["state"][s], after), (sd, b)
+            else:
+                assert not r["written"][s] and np.array_equal(r["state"][s], c["state"][s])
+            for k, buf in (("x", "buf_x"), ("dt", "buf_dt"), ("B", "buf_B")):
+                want = np.asarray(c[buf])[s].copy()
+                want[w:w + T] = np.asarray(c[k])[b]
+                assert np.array_equal(r[buf][s], want), (sd, b, buf)
+
+
+def pin_replay_spec_rollback(orc):
+    """Rejected drafts cost nothing: after a step whose drafts were appended
+    at h.., the caller accepts a prefix (pointer h + a); the next step's
+    drafts overwrite the rejected entries and read out exactly as the plain
+    update over the committed entries, the accepted drafts and the new ones."""
+    from oracle import ssu_oracle
+    L, T = 12, 3
+    c = _spec_case(L, T, [1, 0, 2, 4])
+    r = ssu_oracle.run_replay_spec(c, orc)
+    acc = [2, 3, 1, 2]
+    c2 = dict(c, buf_x=r["buf_x"], buf_dt=r["buf_dt"], buf_B=r["buf_B"], state=r["state"])
+    c2.update(_fresh_inputs_spec(c, 5))
+    c2["buf_len"] = np.asarray(c["buf_len"]) + np.asarray(acc, np.int32)
+    r2 = ssu_oracle.run_replay_spec(c2, orc)
+    for b in range(4):
+        h2 = int(c2["buf_len"][b])
+        y, _, _ = _spec_chain(orc, c2, b, range(h2))
+        scale = np.abs(y).max() + 1.0
+        assert np.abs(r2["y"][b].astype(np.float64) - y[h2:]).max() <= 1e-5 * scale, b
+
+
+def _fresh_inputs_spec(case, seed):
+    rng = np.random.default_rng(seed)
+    inp = {}
+    for k in ("x", "dt", "B", "C", "z"):
+        a = case[k]
+        dtype = case.get("dt_dtype", case["io_dtype"]) if k == "dt" else case["io_dtype"]
+        inp[k] = W.to_storage(rng.standard_normal(a.shape, dtype=np.float32), dtype)
+    return inp
+
+
+def pin_replay_spec_fold_boundary(orc):
+    """The fold comes one window early: at h + 2T > L, not at h + T > L
+    (L = 8, T = 2: h = 4 keeps the window, h = 5 folds although its drafts
+    would still fit)."""
+    from oracle import ssu_oracle
+    c = _spec_case(8, 2, [4, 5, 0, 6], sd="f32", io="bf16")
+    r = ssu_oracle.run_replay_spec(c, orc)
+    tab = c["state_batch_indices"]
+    assert [bool(r["written"][s]) for s in tab] == [False, True, False, True]
+    for b, w in enumerate([4, 0, 0, 0]):
+        s = tab[b]
+        assert np.array_equal(r["buf_x"][s, w:w + 2], c["x"][b]), b
+
+
+def pin_replay_spec_pad_and_disable(orc):
+    """The pad id reads a zero checkpoint with no buffer (its pointer is
+    ignored) and writes nothing: its drafts read out as the plain update's
+    chain from a zero state; disable_state_update writes nothing and leaves
+    y unchanged."""
+    from oracle import ssu_oracle
+    c = _spec_case(6, 2, [1, 3, 4, 0], sd="f32", io="f32")
+    tab = c["state_batch_indices"].copy()
+    tab[2] = -1
+    c["state_batch_indices"] = tab
+    r = ssu_oracle.run_replay_spec(c, orc)
+    live = set(int(v) for v in tab[[0, 1, 3]])
+    others = [s for s in range(8) if s not in live]
+    for k in ("state", "buf_x", "buf_dt", "buf_B"):
+        assert np.array_equal(r[k][others], c[k][others]), k
+    zero = dict(c)
+    zero["state"] = np.zeros_like(c["state"])
+    zero["state_batch_indices"] = np.where(tab < 0, 7, tab)  # an all-zero slot instead of the pad
+    y, _, _ = _spec_chain(orc, zero, 2, [])
+    scale = np.abs(y).max() + 1.0
+    assert np.abs(r["y"][2].astype(np.float64) - y).max() <= 1e-5 * scale
+    d = ssu_oracle.run_replay_spec(dict(c, disable_state_update=True), orc)
+    assert np.array_equal(d["y"], r["y"])
+    for k in ("state", "buf_x", "buf_dt", "buf_B"):
+        assert np.array_equal(d[k], c[k]), k
+
+
+def pin_replay_spec_brute_force(orc, combos=20, seed=12):
+    """The speculative step against the independent float64 version on tiny
+    shapes over L, T, pointers (folding or not), dtypes and options."""
+    from oracle import ssu_oracle
+    rng = np.random.default_rng(seed)
+    for k in range(combos):
+        L = int(rng.choice([1, 2, 4, 7]))
+        T = int(rng.integers(1, L + 1))
+        sd = ["f32", "f16", "bf16"][rng.integers(3)]
+        io = ["f32", "bf16"][rng.integers(2)]
+        c = W.replay_spec(seed=int(rng.integers(1 << 30)), batch=3, T=T, heads=2, dim=4, dstate=8,
+                          groups=1, slots=5, L=L, state_dtype=sd, io=io,
+                          dt_per_head=bool(rng.integers(2)), buf_len=rng.integers(0, L + 1, 3))
+        if rng.integers(2):
+            c["dt_bias"], c["dt_softplus"] = None, False
+            dtd = c.get("dt_dtype", io)
+            c["dt"] = W.to_storage(rng.random(np.shape(c["dt"]), dtype=np.float32) * 0.1, dtd)
+            c["buf_dt"] = W.to_storage(rng.random(np.shape(c["buf_dt"]), dtype=np.float32) * 0.1,
+                                       dtd)
+        if rng.integers(3) == 0:
+            c["z"] = None
+        if rng.integers(4) == 0:
+            tab = c["state_batch_indices"].copy()
+            tab[1] = -1
+            c["state_batch_indices"] = tab
+        if rng.integers(5) == 0:
+            c["disable_state_update"] = True
+        o = ssu_oracle.run_replay_spec(c, orc)
+        b = brute64.run_replay_spec(c)
+        for key in ("buf_x", "buf_dt", "buf_B"):
+            assert np.array_equal(o[key], b[key]), (k, key)
+        assert np.array_equal(o["written"], b["written"]), k
+        S_o, S_b = f64(o["state"], sd), f64(b["state"], sd)
+        tol = (64 * U32 * (np.abs(S_b) + 1)) if sd == "f32" else \
+            (2 * ulp16(S_b, sd) + 64 * U32 * (np.abs(S_b) + 1))
+        assert np.all(np.abs(S_o - S_b) <= tol), (k, sd, L)
+        y_o = f64(o["y"], io)
+        tol = 64 * U32 * (np.abs(b["y64"]) + 8) * 8 * (L + T)
+        if io != "f32":
+            tol = tol + 2 * ulp16(b["y64"], io)
+        assert np.all(np.abs(y_o - b["y64"]) <= tol), (k, io, L, T)
+
+
 ALL = [pin_golden_mate_examples, pin_f16_decode_exhaustive, pin_f16_encode, pin_bf16_roundtrip, pin_softplus,
        pin_dt_zero_keeps_state, pin_b_zero_pure_decay, pin_zero_state_closed_form,
        pin_c_zero_and_z_zero, pin_mtp_equals_chained_calls, pin_unrolled_window,
@@ -687,4 +872,5 @@ ALL = [pin_golden_mate_examples, pin_f16_decode_exhaustive, pin_f16_encode, pin_
        pin_pad_destination_mid_sequence, pin_dt_per_head_broadcast, pin_groups, pin_brute_force,
        pin_replay_L1_is_plain_update, pin_replay_flush_is_chain,
        pin_replay_nonflush_writes_entry_only, pin_replay_zero_checkpoint, pin_replay_disable,
-       pin_replay_brute_force]
+       pin_replay_brute_force, pin_replay_spec_is_chain, pin_replay_spec_rollback,
+       pin_replay_spec_fold_boundary, pin_replay_spec_pad_and_disable, pin_replay_spec_brute_force]

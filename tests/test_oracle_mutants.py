@@ -55,6 +55,21 @@ MUTANTS = [
     ("replay_append_skipped_x",
      "copy_elem(ra->bx_out, a->x, a->io_dtype, ((s * L + h) * H + hd) * P + d,",
      "copy_elem(ra->bx_out, a->x, a->io_dtype, ((s * L + h) * H + hd) * P + 0,"),
+    # ReplaySSM speculative step
+    ("spec_natural_fold", "const int fold = h + 2 * T > L;", "const int fold = h + T > L;"),
+    ("spec_no_causal_mask", "const int64_t last = w + t; /* draft t's place in the window */",
+     "const int64_t last = w + T - 1;"),
+    ("spec_append_reversed", "copy_elem(ra->bx_out, a->x, a->io_dtype, ((s * L + w + t) * H + hd) * P + d,",
+     "copy_elem(ra->bx_out, a->x, a->io_dtype, ((s * L + w + (T - 1 - t)) * H + hd) * P + d,"),
+    ("spec_fold_not_rounded",
+     "for (int64_t e = 0; e < tile; e++) /* R21: rounded after each */\n"
+     "                        S[e] = through_dtype(a->state_dtype, S[e]);", ""),
+    ("spec_readout_first_draft", "u = u + S[d * N + n] * DC(t, n);", "u = u + S[d * N + n] * DC(0, n);"),
+    ("spec_D_of_window_start", "y = y + a->D[hd] * xs[last];", "y = y + a->D[hd] * xs[w];"),
+    ("spec_draft_B_row", "wj = wj + (j < w ? BB(j, n) : DB(j - w, n)) * DC(t, n);",
+     "wj = wj + (j < w ? BB(j, n) : DB(0, n)) * DC(t, n);"),
+    ("spec_draft_dt_row", "const float raw = k < w ? BDT(k, d) : DDT(k - w, d);",
+     "const float raw = k < w ? BDT(k, d) : DDT(0, d);"),
     ("default_dst_is_seq",
      "a->wtab.data ? &a->wtab : (a->rtab.data ? &a->rtab : NULL)", "a->wtab.data ? &a->wtab : NULL"),
     ("flat_write_b_plus_t", "int64_t i = tb->ndim == 1 ? bos + t :", "int64_t i = tb->ndim == 1 ? b + t :"),

@@ -282,3 +282,36 @@ def replay(seed=5, batch=256, heads=128, dim=64, dstate=128, groups=8, slots=512
 
 
 BUILDERS["replay"] = replay
+
+
+def replay_spec(seed=6, batch=512, T=4, heads=128, dim=64, dstate=128, groups=8, slots=1024,
+                L=16, state_dtype="f32", io="bf16", buf_len=None, dt_per_head=False,
+                index_dtype=np.int32, fill_unread=True):
+    """A ReplaySSM speculative step (T draft tokens per sequence) on the decode
+    workload's layer: the replay() pool and buffers, with x, dt, z [batch, T,
+    heads, dim] and B, C [batch, T, groups, dstate]. buf_len defaults to
+    U{0..L-T} (the pointers a caller that folds at h + 2T > L can hold)."""
+    rng = np.random.default_rng(seed)
+    perm = rng.permutation(slots)[:batch].astype(index_dtype)
+    c = {"state_dtype": state_dtype}
+    c["state"] = _pool(rng, slots, heads, dim, dstate, state_dtype,
+                       perm if fill_unread else None)
+    lay = _layer(rng, batch * T, heads, dim, dstate, groups, io=io, dt_dtype=io,
+                 dt_per_head=dt_per_head)
+    for k in ("x", "dt", "B", "C", "z"):
+        if lay[k] is not None:
+            lay[k] = lay[k].reshape((batch, T) + lay[k].shape[1:])
+    c.update(lay)
+    c.update(state_batch_indices=perm, dst_state_batch_indices=None, pad_slot_id=-1,
+             disable_state_update=False, cu_seqlens=None, num_accepted_tokens=None)
+    c["L"] = int(L)
+    c["buf_x"] = _normal(rng, (slots, L, heads, dim), io)
+    c["buf_dt"] = _normal(rng, (slots, L, heads) if dt_per_head else (slots, L, heads, dim), io)
+    c["buf_B"] = _normal(rng, (slots, L, groups, dstate), io)
+    if buf_len is None:
+        buf_len = rng.integers(0, L - T + 1, batch)
+    c["buf_len"] = np.broadcast_to(np.asarray(buf_len, dtype=np.int32), (batch,)).copy()
+    return c
+
+
+BUILDERS["replay_spec"] = replay_spec
