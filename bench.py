@@ -16,7 +16,8 @@ Prints ONE JSON line:
              by a plain copy of known size) when they were taken on the
              current kernel source, else null
   cpu_baseline  the CPU oracle timed on this host on the same workload
-Options: --config {decode, decode_pad, mtp, varlen, varlen_disable, varlen_nodst, replay},
+Options: --config {decode, decode_pad, mtp, varlen, varlen_disable, varlen_nodst, replay,
+replay_spec, spec_snapshots},
 --no-cpu-baseline, --calib-copy (also runs a plain device copy of the state's
 size, the calibration kernel for the counters).
 """
@@ -59,6 +60,16 @@ def workload(name):
                             "256, heads 128, dim 64, dstate 128, groups 8, fp32 checkpoint), "
                             "buffer length L = 16, bf16 x/dt/B buffers, per-sequence buffer "
                             "pointers ~ U{0..15} (about 1/16 of the sequences fold each step)")
+    if name == "replay_spec":
+        return W.replay_spec(), ("replay_spec: ReplaySSM speculative step, batch 512 x T = 4 draft "
+                                 "tokens, heads 128, dim 64, dstate 128, groups 8, fp32 "
+                                 "checkpoint, L = 16, bf16 buffers, committed pointers ~ U{0..12} "
+                                 "(a sequence folds at h + 2T > L)")
+    if name == "spec_snapshots":
+        return W.spec_snapshots(), ("spec_snapshots: the same drafts through the plain update "
+                                    "with one fp32 state snapshot per draft (batch 512 x T = 4, "
+                                    "heads 128, dim 64, dstate 128, groups 8), the design "
+                                    "ReplaySSM replaces")
     if name.startswith("varlen"):
         dst = name != "varlen_nodst"
         dis = name == "varlen_disable"
@@ -131,35 +142,45 @@ def algorithmic_bytes(case):
 
 def replay_algorithmic_bytes(case):
     """Minimal bytes of one ReplaySSM step: each live sequence reads its
-    checkpoint tile and its h buffered entries; a folding sequence (h + 1 ==
-    L) writes its checkpoint, any other writes one buffer entry; plus the
-    current step's inputs and y, and per-head vectors and tables, as for the
-    plain update. Returns (bytes, token-head updates)."""
+    checkpoint tile and its h committed entries; a folding sequence writes its
+    checkpoint; the step's tokens are appended (one entry per token, or none
+    for a one-token fold); plus the step's inputs and y, and per-head vectors
+    and tables, as for the plain update. One-token steps fold at h + 1 = L,
+    speculative steps (x [batch, T, ...]) at h + 2T > L. Returns (bytes,
+    token-head updates)."""
     slots, H, P, N = np.shape(case["state"])
     sb = DTYPE_BYTES[case["state_dtype"]]
     io = DTYPE_BYTES[case["io_dtype"]]
     dtb = DTYPE_BYTES[case.get("dt_dtype", case["io_dtype"])]
     G = np.shape(case["B"])[-2]
     L = int(case["L"])
+    x = np.asarray(case["x"])
+    spec = x.ndim == 4
+    T = x.shape[1] if spec else 1
     per_head = np.ndim(case["buf_dt"]) == 3
     entry = H * P * io + (H if per_head else H * P) * dtb + G * N * io
     tile = H * P * N * sb
     pad = int(case.get("pad_slot_id", -1))
     tab = case.get("state_batch_indices")
     total = 0
-    R = np.shape(case["x"])[0]
-    for b in range(R):
+    batch = x.shape[0]
+    for b in range(batch):
         s = b if tab is None else int(np.asarray(tab)[b])
         if s == pad:
             continue
         h = int(case["buf_len"][b])
         total += tile + h * entry
         if not case.get("disable_state_update", False):
-            total += tile if h + 1 == L else entry
+            if spec:
+                total += (tile if h + 2 * T > L else 0) + T * entry
+            else:
+                total += tile if h + 1 == L else entry
+    R = batch * T
     row = H * P * io * 2 + (H * P * io if case.get("z") is not None else 0)
-    row += (H if np.ndim(case["dt"]) == 2 else H * P) * dtb + 2 * G * N * io
+    row += (H if np.ndim(case["dt"]) == x.ndim - 1 else H * P) * dtb + 2 * G * N * io
     vec = 4 * H * (1 + (case.get("D") is not None) + (case.get("dt_bias") is not None))
-    idx = (np.asarray(tab).itemsize * R if tab is not None else 0) + np.asarray(case["buf_len"]).nbytes
+    idx = (np.asarray(tab).itemsize * batch if tab is not None else 0) + \
+        np.asarray(case["buf_len"]).nbytes
     return int(total + R * row + vec + idx), int(R * H)
 
 
@@ -185,7 +206,10 @@ def traffic_from_counters(config):
 def cpu_baseline(case, alg_bytes, updates, reps):
     from oracle import ssu_oracle
     ssu_oracle.default()
-    run = ssu_oracle.run_replay if "buf_len" in case else ssu_oracle.run
+    if "buf_len" in case:
+        run = ssu_oracle.run_replay_spec if np.ndim(case["x"]) == 4 else ssu_oracle.run_replay
+    else:
+        run = ssu_oracle.run
     times = []
     for _ in range(reps):
         t0 = time.perf_counter()
@@ -216,14 +240,13 @@ def main():
 
     import torch
     import mamba_selective_state_amd as ssu
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from gpu_harness import TORCH, device_case, device_replay
+    from workloads.device import TORCH, device_case, device_replay
 
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     dev = torch.device("cuda", 0)
     case, desc = workload(args.config)
-    is_replay = args.config == "replay"
+    is_replay = args.config in ("replay", "replay_spec")
     alg_bytes, updates = (replay_algorithmic_bytes if is_replay else algorithmic_bytes)(case)
     print("[bench] %s: %.3f GB per step" % (args.config, alg_bytes / 1e9), file=sys.stderr,
           flush=True)
@@ -235,7 +258,8 @@ def main():
                                       d["dt_bias"], case.get("dt_softplus", False),
                                       d["state_batch_indices"], case.get("pad_slot_id", -1), out,
                                       case.get("disable_state_update", False))
-        launch = ssu.ssu_replay_update
+        launch = ssu.ssu_replay_spec_update if args.config == "replay_spec" else \
+            ssu.ssu_replay_update
     else:
         args_c = ssu.make_args(d["state"], d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"],
                                d["z"], d["dt_bias"], case.get("dt_softplus", False),
@@ -245,7 +269,8 @@ def main():
                                d["num_accepted_tokens"])
         launch = ssu.ssu_update
     x = np.asarray(case["x"])
-    plan = {"kernel": "ssu_replay_kernel"} if is_replay else ssu.prewarm_selective_state_update(
+    plan = {"kernel": "ssu_replay_spec_kernel" if args.config == "replay_spec"
+            else "ssu_replay_kernel"} if is_replay else ssu.prewarm_selective_state_update(
         state_dtype=TORCH[case["state_dtype"]], io_dtype=TORCH[case["io_dtype"]],
         batch=x.shape[0], heads=x.shape[-2], dim=x.shape[-1], dstate=np.shape(case["state"])[-1],
         groups=np.shape(case["B"])[-2],

@@ -201,6 +201,33 @@ typedef struct {
 
 SSU_API ssu_status_t ssu_replay_update(const ssu_replay_args_t *args, void *stream);
 
+/* ReplaySSM speculative step (ReplaySSM article, lpnh.cn, section
+ * "投机解码回滚变成挪指针"): T draft tokens per sequence are read out against
+ * the same checkpoint and buffer window under a causal mask and appended to
+ * the buffer; the caller commits the accepted prefix by moving the pointer.
+ * For each sequence b with slot s and h = buf_len[b] committed entries:
+ *   - if h + 2T > L (the fold, one window early), the h committed entries
+ *     are applied to the checkpoint one after the other exactly as
+ *     ssu_update applies tokens (state rounded to the state dtype after each)
+ *     and the checkpoint is stored; the window then starts empty (w = 0);
+ *     otherwise w = h and the checkpoint is only read;
+ *   - draft t (t = 0..T-1) reads out, with the steps i, j of the window being
+ *     the w committed entries followed by drafts 0..t and a_i = exp(dt'_i A):
+ *       y_t = (prod_i a_i) (S . C_t) + sum_j dt'_j x_j (prod_{i>j} a_i) (B_j . C_t)
+ *             + D x_t, times silu(z_t)       (S: the checkpoint, folded or not)
+ *   - the drafts' raw x, dt and B are written to entries w .. w+T-1; the
+ *     caller then sets the pointer to w + the number of accepted drafts.
+ * base: as for ssu_update with x [batch, T, heads, dim] (dt [batch, T,
+ * heads, dim] or [batch, T, heads], B and C [batch, T, groups, dstate], z
+ * and out like x), state_batch_indices 1-D [batch] or absent (slot b), and no
+ * dst_state_batch_indices, cu_seqlens or num_accepted_tokens; 1 <= T <= L.
+ * Buffers as for ssu_replay_update; buf_len values lie in [0, L] (a value
+ * outside for a slot other than the pad id makes that sequence's y NaN and
+ * writes nothing). The pad id reads a zero checkpoint, has no buffer and
+ * writes nothing; disable_state_update writes neither checkpoint nor buffer.
+ * Same error, stream and allocation conventions as ssu_update. */
+SSU_API ssu_status_t ssu_replay_spec_update(const ssu_replay_args_t *args, void *stream);
+
 /* Message of the last failing call on this thread ("" if none). The pointer
  * stays valid until the next call on the same thread. */
 SSU_API const char *ssu_last_error(void);

@@ -589,22 +589,37 @@ ssu_status_t ssu_update(const ssu_args_t *a, void *stream) {
     return SSU_OK;
 }
 
-ssu_status_t ssu_replay_update(const ssu_replay_args_t *ra, void *stream) {
+// Both ReplaySSM entry points: validate, then launch the one-token or the
+// speculative kernel.
+static ssu_status_t replay_common(const ssu_replay_args_t *ra, bool spec, void *stream) {
+    const char *fn = spec ? "ssu_replay_spec_update" : "ssu_replay_update";
     if (!ra)
-        return fail(SSU_ERR_VALUE, "ssu_replay_update: args is NULL");
+        return fail(SSU_ERR_VALUE, "%s: args is NULL", fn);
     const ssu_args_t *a = &ra->base;
-    if (a && (present(a->dst_state_batch_indices) || present(a->cu_seqlens) ||
-              present(a->num_accepted_tokens)))
+    if (present(a->dst_state_batch_indices) || present(a->cu_seqlens) ||
+        present(a->num_accepted_tokens))
         return fail(SSU_ERR_NOT_IMPLEMENTED,
-                    "replay decode takes one token per sequence and one slot table "
-                    "(no dst_state_batch_indices, cu_seqlens or num_accepted_tokens)");
-    if (a && a->x.ndim != 3)
-        return fail(SSU_ERR_NOT_IMPLEMENTED, "replay decode takes x [batch, heads, dim]");
+                    "replay decode takes one slot table and no dst_state_batch_indices, "
+                    "cu_seqlens or num_accepted_tokens");
+    if (a->x.ndim != (spec ? 4 : 3))
+        return fail(SSU_ERR_NOT_IMPLEMENTED, spec ? "speculative replay takes x [batch, T, heads, dim]"
+                                                  : "replay decode takes x [batch, heads, dim]");
+    // The speculative step names one slot per sequence: its 1-D table is
+    // viewed as [batch, T] with a zero step stride for the shared checks.
+    ssu_args_t view = *a;
+    const ssu_tensor_t &tab = a->state_batch_indices;
+    if (spec && present(tab)) {
+        if (tab.ndim != 1 || tab.size[0] != a->x.size[0])
+            return fail(SSU_ERR_VALUE, "state_batch_indices must be 1-D [batch]");
+        view.state_batch_indices.ndim = 2;
+        view.state_batch_indices.size[1] = a->x.size[1];
+        view.state_batch_indices.stride[1] = 0;
+    }
     Prepared pr;
-    ssu_status_t s = prepare(a, &pr);
+    ssu_status_t s = prepare(&view, &pr);
     if (s != SSU_OK)
         return s;
-    if (pr.rtab_2d)
+    if (!spec && pr.rtab_2d)
         return fail(SSU_ERR_NOT_IMPLEMENTED, "replay decode takes a 1-D slot table");
 
     // buffers: contiguous, shaped after the pool
@@ -641,6 +656,10 @@ ssu_status_t ssu_replay_update(const ssu_replay_args_t *ra, void *stream) {
     if (!aligned(bx.data, elem_bytes(pr.io)) || !aligned(bdt.data, elem_bytes(pr.dt_dtype)) ||
         !aligned(bB.data, 16))
         return fail(SSU_ERR_VALUE, "replay buffers are misaligned (buf_B needs 16 bytes)");
+    const int64_t T = spec ? a->x.size[1] : 1;
+    if (spec && T > L)
+        return fail(SSU_ERR_VALUE, "T = %lld drafts do not fit a buffer of L = %lld entries",
+                    (long long)T, (long long)L);
     ssu::ReplayParams rp;
     memset(&rp, 0, sizeof rp);
     int64_t len_s = 0;
@@ -666,7 +685,7 @@ ssu_status_t ssu_replay_update(const ssu_replay_args_t *ra, void *stream) {
     rp.G = static_cast<int32_t>(pr.G);
 
     ssu::KernelRef k;
-    if (!ssu::find_replay_kernel(pr.state_dtype, pr.io, static_cast<int>(pr.N), &k))
+    if (!ssu::find_replay_kernel(pr.state_dtype, pr.io, static_cast<int>(pr.N), spec, &k))
         return fail(SSU_ERR_NOT_IMPLEMENTED, "no replay kernel for state %s / io %s / dstate %lld",
                     dtype_str(pr.state_dtype), dtype_str(pr.io), (long long)pr.N);
     const Geometry geo = geometry(pr.P, pr.N, pr.state_dtype, ssu::kTileReplay);
@@ -682,6 +701,14 @@ ssu_status_t ssu_replay_update(const ssu_replay_args_t *ra, void *stream) {
         return fail(SSU_ERR_HIP, "kernel launch failed: %s", ssu::hip_error_string(e));
     g_error.clear();
     return SSU_OK;
+}
+
+ssu_status_t ssu_replay_update(const ssu_replay_args_t *ra, void *stream) {
+    return replay_common(ra, false, stream);
+}
+
+ssu_status_t ssu_replay_spec_update(const ssu_replay_args_t *ra, void *stream) {
+    return replay_common(ra, true, stream);
 }
 
 }  // extern "C"

@@ -56,6 +56,11 @@ constexpr int kMaxWaves = SSU_MAX_WAVES;
 constexpr int replay_waves_per_eu(int state_bytes, int dstate) {
     return state_bytes == 4 && dstate <= 128 ? SSU_WAVES_PER_EU_REPLAY : SSU_WAVES_PER_EU_REPLAY_WIDE;
 }
+// The speculative replay kernel also holds a group of drafts' C and their
+// per-draft accumulators.
+constexpr int replay_spec_waves_per_eu(int state_bytes, int dstate) {
+    return state_bytes == 4 && dstate <= 128 ? 3 : 2;
+}
 #ifndef SSU_WAVES_PER_EU_MULTI
 #define SSU_WAVES_PER_EU_MULTI 4
 #endif
@@ -152,7 +157,7 @@ const char *hip_error_string(int e);
 int launch(const KernelRef &k, const Params &p, unsigned grid, unsigned block, void *stream);
 
 // The ReplaySSM decode kernel for (state dtype, io dtype, dstate).
-bool find_replay_kernel(int state_dtype, int io_dtype, int dstate, KernelRef *out);
+bool find_replay_kernel(int state_dtype, int io_dtype, int dstate, bool spec, KernelRef *out);
 int launch_replay(const KernelRef &k, const Params &p, const ReplayParams &rp, unsigned grid,
                   unsigned block, void *stream);
 

@@ -889,12 +889,401 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes, replay_waves_per_eu(sizeof(S
     }
 }
 
-template <typename ST, typename IT>
+// ReplaySSM speculative step (ReplaySSM article, section "投机解码回滚变成挪指针"):
+// T draft tokens per sequence, packed as rows b*T + t. One workgroup per
+// (sequence, head, dim tile), the checkpoint tile in ssu_kernel's layout. If
+// h + 2T > L (the fold one window early), the h committed entries are first
+// applied to the tile with the plain update's arithmetic (no readout) and the
+// tile is stored; the window then starts empty (w = 0), else w = h. Drafts
+// are read out kSpecGroup at a time: the window (w committed entries, then
+// the drafts up to the group's last) is split into runs as in
+// ssu_replay_kernel, every run keeps one (R, G) pair per draft of the group,
+// updated only at steps that draft can see (the causal mask), and each
+// B_j . C_t is formed once per DPP row and draft. The drafts' raw inputs go
+// to entries w .. w+T-1. An entry count outside [0, L] (not for the pad id)
+// makes the sequence's y NaN and writes nothing.
+constexpr int kSpecGroup = 4;
+
+template <typename ST, typename IT, int N>
+__global__ __launch_bounds__(kMaxWaves *kWaveLanes, replay_spec_waves_per_eu(sizeof(ST), N)) void ssu_replay_spec_kernel(
+    const Params p, const ReplayParams rp) {
+    constexpr int E = N / kLanesPerRow;
+    constexpr int VEC = (16 / (int)sizeof(ST)) < E ? (16 / (int)sizeof(ST)) : E;
+    constexpr int NCH = E / VEC;
+    constexpr int PASSES = passes_for(N, sizeof(ST), kTileReplay);
+    constexpr int IVEC = VEC;
+    constexpr int NSEG = kLanesPerRow / PASSES;
+    constexpr int NDOT = NSEG < kRowsPerPass ? 1 : NSEG / kRowsPerPass;
+    constexpr int TG = kSpecGroup;
+    static_assert(PASSES <= kLanesPerRow && kLanesPerRow % PASSES == 0, "runs tile the row");
+    using SPack = Pack<ST, VEC>;
+    using Bits = typename TokenInputs<IT, NCH, IVEC>::Bits;
+
+    const int lane = threadIdx.x & (kWaveLanes - 1);
+    const int wave = threadIdx.x / kWaveLanes;
+    const int col = lane & (kLanesPerRow - 1);
+    const int rsub = lane / kLanesPerRow;
+    const int flags = p.flags;
+
+    const int32_t wg = xcd_clustered_index(blockIdx.x, gridDim.x);
+    const int tile = wg % p.dim_tiles;
+    const int32_t sh = wg / p.dim_tiles;
+    const int h = sh % p.H;
+    const int32_t b = sh / p.H;
+    const int g = h / p.heads_per_group;
+    const int dw = tile * p.rows_per_block + wave * (kRowsPerPass * PASSES);
+    const int d_own = dw + col * kRowsPerPass + rsub;
+    const bool owner = col < PASSES && d_own < p.P;
+    const int d_fetch = owner ? d_own : 0;
+    const int32_t T = p.steps;
+
+    const int64_t s = p.rtab ? load_index(p.rtab, flags & kReadI64, b * p.r_s0) : b;
+    const bool pad = s == p.pad;  // no checkpoint and no buffer: h is taken as 0
+    const int64_t h_in = pad ? 0 : load_index(rp.buf_len, rp.len_i64, b * rp.len_s);
+    const bool bad = h_in < 0 || h_in > rp.L;
+    const int32_t hc = bad ? 0 : static_cast<int32_t>(h_in);
+    const bool fold = !bad && hc + 2 * T > rp.L;
+    const int32_t w = fold ? 0 : hc;
+    const bool write = !pad && !bad && !(flags & kDisable);
+    const bool dt_f32 = flags & kDtF32;
+    const int dt_bytes = dt_f32 ? 4 : 2;
+
+    const int P = p.P, H = p.H;
+    const int64_t tile_off = static_cast<int64_t>(h) * P * N;
+    ST *const sbase = static_cast<ST *>(p.state) + (pad ? 0 : s) * p.slot_stride + tile_off;
+    const int64_t sl = (pad ? 0 : s) * rp.L;
+    const IT *const xs = static_cast<const IT *>(p.x);
+    const IT *const zs = static_cast<const IT *>(p.z);
+    const IT *const Bs = static_cast<const IT *>(p.B);
+    const IT *const Cs = static_cast<const IT *>(p.C);
+    IT *const ys = static_cast<IT *>(p.out);
+    const unsigned char *const dts = static_cast<const unsigned char *>(p.dt);
+    IT *const bxs = static_cast<IT *>(rp.buf_x);
+    IT *const bBs = static_cast<IT *>(rp.buf_B);
+    unsigned char *const bdts = static_cast<unsigned char *>(rp.buf_dt);
+
+    const float a_h = p.A[h * p.A_sh];
+    const float d_h = p.D ? p.D[h * p.D_sh] : 0.0f;
+    const float bias_h = p.dt_bias ? p.dt_bias[h * p.bias_sh] : 0.0f;
+
+    // buffer entry k of the slot (32-bit lane offsets from per-slot bases),
+    // draft t (row b*T + t), and step k of the window (k < w: entry k, else
+    // draft k - w), each for a dim row d in range
+    const IT *const bx0 = bxs + (sl * H + h) * P;
+    const unsigned char *const bdt0 = bdts + (rp.dt_per_head ? sl * H + h : (sl * H + h) * P) * dt_bytes;
+    const IT *const bB0 = bBs + (sl * rp.G + g) * N + col * IVEC;
+    const uint32_t HP = static_cast<uint32_t>(H * P), GN = static_cast<uint32_t>(rp.G * N);
+    const uint32_t entry_dt = rp.dt_per_head ? static_cast<uint32_t>(H) : HP;
+    auto row = [&](int32_t t) { return b * T + t; };
+    auto entry_x = [&](int32_t k, int d) { return bx0 + (static_cast<uint32_t>(k) * HP + d); };
+    auto entry_dt_p = [&](int32_t k, int d) {
+        return bdt0 + (static_cast<uint32_t>(k) * entry_dt + (rp.dt_per_head ? 0u : static_cast<uint32_t>(d))) * dt_bytes;
+    };
+    auto entry_B = [&](int32_t k) { return bB0 + static_cast<uint32_t>(k) * GN; };
+    auto draft_x = [&](int32_t t, int d) { return xs + (row(t) * p.x_sr + h * p.x_sh + d); };
+    auto draft_dt_p = [&](int32_t t, int d) {
+        return dts + static_cast<int64_t>(row(t) * p.dt_sr + h * p.dt_sh + d * p.dt_sp) * dt_bytes;
+    };
+    auto draft_B = [&](int32_t t) { return Bs + (row(t) * p.B_sr + g * p.B_sg + col * IVEC); };
+    auto x_at = [&](int32_t k, int d) -> const Bits * {
+        return reinterpret_cast<const Bits *>(k < w ? entry_x(k, d) : draft_x(k - w, d));
+    };
+    auto dt_at = [&](int32_t k, int d) { return k < w ? entry_dt_p(k, d) : draft_dt_p(k - w, d); };
+    auto B_at = [&](int32_t k) { return k < w ? entry_B(k) : draft_B(k - w); };
+    auto step_dt = [&](uint16_t lo, uint16_t hi) {
+        float v = (dt_f32 ? __uint_as_float(uint32_t(lo) | (uint32_t(hi) << 16)) : from_bits<IT>(lo)) + bias_h;
+        if (flags & kSoftplus)
+            v = softplus(v);
+        return v;
+    };
+
+    // the checkpoint tile (zeros for the pad id; rows past the dim read the
+    // last row, their results are never stored)
+    SPack S[PASSES][NCH];
+    if (pad) {  // uniform
+#pragma unroll
+        for (int q = 0; q < PASSES; q++)
+#pragma unroll
+            for (int c = 0; c < NCH; c++)
+#pragma unroll
+                for (int k = 0; k < VEC; k++)
+                    S[q][c].v[k] = narrow<ST>(0.0f);
+    } else {
+#pragma unroll
+        for (int q = 0; q < PASSES; q++) {
+            const int d0 = dw + q * kRowsPerPass + rsub;
+            const uint32_t d = d0 < P ? d0 : P - 1;
+#pragma unroll
+            for (int c = 0; c < NCH; c++)
+                S[q][c] = load_state(reinterpret_cast<const SPack *>(
+                    sbase + (d * N + static_cast<uint32_t>(c * kLanesPerRow * VEC + col * VEC))));
+        }
+    }
+
+    if (fold) {
+        // the committed entries, one plain update after the other, one entry
+        // ahead in loads
+        struct StepIn {
+            RawWords<IT, IVEC> b[NCH];
+            Bits x;
+            uint16_t dt_lo, dt_hi;
+        };
+        auto fetch_entry = [&](int32_t j, StepIn &in) {
+#pragma unroll
+            for (int c = 0; c < NCH; c++)
+                in.b[c] = load_words<IT, IVEC>(entry_B(j) + c * kLanesPerRow * IVEC);
+            in.x = *reinterpret_cast<const Bits *>(entry_x(j, d_fetch));
+            const unsigned char *dp = entry_dt_p(j, d_fetch);
+            in.dt_lo = *reinterpret_cast<const uint16_t *>(dp);
+            in.dt_hi = *reinterpret_cast<const uint16_t *>(dp + (dt_f32 ? 2 : 0));
+        };
+        auto apply = [&](const StepIn &in) {
+            const float v = step_dt(in.dt_lo, in.dt_hi);
+            const float decay = exp_hw(v * a_h);
+            const float dtx = v * from_bits<IT>(in.x);
+            float Bv[E];
+#pragma unroll
+            for (int c = 0; c < NCH; c++)
+#pragma unroll
+                for (int k = 0; k < IVEC; k++)
+                    Bv[c * IVEC + k] = word_elem(in.b[c], k);
+            for_passes<0, PASSES>([&](auto qc) {
+                constexpr int q = decltype(qc)::value;
+                const float dq = row16_bcast<q>(decay);
+                const float tq = row16_bcast<q>(dtx);
+#pragma unroll
+                for (int c = 0; c < NCH; c++)
+#pragma unroll
+                    for (int k = 0; k < VEC; k++)
+                        S[q][c].v[k] = narrow<ST>(fmaf(widen(S[q][c].v[k]), dq, tq * Bv[c * VEC + k]));
+            });
+        };
+        if (hc > 0) {
+            StepIn in0, in1;
+            fetch_entry(0, in0);
+            for (int32_t j = 0; j < hc; j += 2) {
+                __builtin_amdgcn_sched_barrier(0);
+                fetch_entry(j + 1 < hc ? j + 1 : hc - 1, in1);
+                __builtin_amdgcn_sched_barrier(0);
+                apply(in0);
+                if (j + 1 >= hc)
+                    break;
+                __builtin_amdgcn_sched_barrier(0);
+                fetch_entry(j + 2 < hc ? j + 2 : hc - 1, in0);
+                __builtin_amdgcn_sched_barrier(0);
+                apply(in1);
+            }
+        }
+        if (write) {
+#pragma unroll
+            for (int q = 0; q < PASSES; q++) {
+                const int d = dw + q * kRowsPerPass + rsub;
+                if (d < P) {
+                    ST *dst = sbase + static_cast<int64_t>(d) * N + col * VEC;
+#pragma unroll
+                    for (int c = 0; c < NCH; c++)
+                        store_state<SSU_NT_STORE>(
+                            reinterpret_cast<SPack *>(dst + c * kLanesPerRow * VEC), S[q][c]);
+                }
+            }
+        }
+    }
+
+    // the drafts, kSpecGroup at a time
+    const int kseg = col / PASSES;
+    const int d_win = dw + (col % PASSES) * kRowsPerPass + rsub;
+    const int d_wf = d_win < P ? d_win : 0;
+    for (int32_t t0 = 0; t0 < T; t0 += TG) {
+        const int32_t W = w + (T < t0 + TG ? T : t0 + TG);  // window steps this group sees
+        const int32_t SL = (W + NSEG - 1) / NSEG;
+        // the group's C (the lane's columns, raw) and the owner row's x, z, dt
+        RawWords<IT, IVEC> cw[TG][NCH];
+        Bits xo[TG], zo[TG];
+        uint16_t dlo[TG], dhi[TG];
+#pragma unroll
+        for (int i = 0; i < TG; i++) {
+            const int32_t t = t0 + i < T ? t0 + i : T - 1;
+            const IT *cp = Cs + (row(t) * p.C_sr + g * p.C_sg + col * IVEC);
+#pragma unroll
+            for (int c = 0; c < NCH; c++)
+                cw[i][c] = load_words<IT, IVEC>(cp + c * kLanesPerRow * IVEC);
+            xo[i] = *reinterpret_cast<const Bits *>(draft_x(t, d_fetch));
+            zo[i] = *reinterpret_cast<const Bits *>(
+                zs ? zs + (row(t) * p.z_sr + h * p.z_sh + d_fetch) : draft_x(t, d_fetch));
+            const unsigned char *dp = draft_dt_p(t, d_fetch);
+            dlo[i] = *reinterpret_cast<const uint16_t *>(dp);
+            dhi[i] = *reinterpret_cast<const uint16_t *>(dp + (dt_f32 ? 2 : 0));
+        }
+
+        struct WinIn {
+            RawWords<IT, IVEC> b[NDOT][NCH];
+            Bits x;
+            uint16_t dt_lo, dt_hi;
+        };
+        auto fetch_win = [&](int32_t st, WinIn &in) {
+#pragma unroll
+            for (int rr = 0; rr < NDOT; rr++) {
+                const int kd = NSEG < kRowsPerPass ? rsub % NSEG : rr * kRowsPerPass + rsub;
+                const int32_t jd = kd * SL + st;
+                const IT *src = B_at(jd < W ? jd : W - 1);
+#pragma unroll
+                for (int c = 0; c < NCH; c++)
+                    in.b[rr][c] = load_words<IT, IVEC>(src + c * kLanesPerRow * IVEC);
+            }
+            const int32_t j = kseg * SL + st;
+            const int32_t jc = j < W ? j : W - 1;
+            in.x = *x_at(jc, d_wf);
+            const unsigned char *dp = dt_at(jc, d_wf);
+            in.dt_lo = *reinterpret_cast<const uint16_t *>(dp);
+            in.dt_hi = *reinterpret_cast<const uint16_t *>(dp + (dt_f32 ? 2 : 0));
+        };
+        float R[TG], Gp[TG];
+#pragma unroll
+        for (int i = 0; i < TG; i++) {
+            R[i] = 0.0f;
+            Gp[i] = 1.0f;
+        }
+        auto run_win = [&](int32_t st, const WinIn &in) {
+            float wv[TG];
+#pragma unroll
+            for (int i = 0; i < TG; i++)
+                wv[i] = 0.0f;
+#pragma unroll
+            for (int rr = 0; rr < NDOT; rr++) {
+                float Bd[E];
+#pragma unroll
+                for (int c = 0; c < NCH; c++)
+#pragma unroll
+                    for (int k = 0; k < IVEC; k++)
+                        Bd[c * IVEC + k] = word_elem(in.b[rr][c], k);
+                const int src = ((kseg % kRowsPerPass) * kLanesPerRow + col) * 4;
+#pragma unroll
+                for (int i = 0; i < TG; i++) {
+                    float part = 0.0f;
+#pragma unroll
+                    for (int c = 0; c < NCH; c++)
+#pragma unroll
+                        for (int k = 0; k < IVEC; k++)
+                            part = fmaf(Bd[c * IVEC + k], word_elem(cw[i][c], k), part);
+                    const float dot = row16_sum(part);
+                    const float got = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(dot)));
+                    wv[i] = kseg / kRowsPerPass == rr ? got : wv[i];
+                }
+            }
+            const int32_t j = kseg * SL + st;
+            const float v = step_dt(in.dt_lo, in.dt_hi);
+            const float alpha = exp_hw(v * a_h);
+            const float cx = v * from_bits<IT>(in.x);
+#pragma unroll
+            for (int i = 0; i < TG; i++) {
+                const bool vis = j < W && j <= w + t0 + i;  // causal mask
+                R[i] = vis ? fmaf(R[i], alpha, cx * wv[i]) : R[i];
+                Gp[i] = vis ? Gp[i] * alpha : Gp[i];
+            }
+        };
+        constexpr int kWinWords = NDOT * NCH * RawWords<IT, IVEC>::kWords + 2;
+        constexpr int T0 = 2 < 32 / kWinWords ? 2 : (32 / kWinWords < 1 ? 1 : 32 / kWinWords);
+        WinIn wb[T0];
+        fetch_win(0, wb[0]);
+#pragma unroll
+        for (int i = 1; i < T0; i++)
+            if (i < SL)  // uniform
+                fetch_win(i, wb[i]);
+#pragma unroll
+        for (int i = 0; i < T0; i++)
+            if (i < SL)
+                run_win(i, wb[i]);
+        WinIn w0, w1;
+        if (SL > T0) {
+            fetch_win(T0, w0);
+            for (int32_t st = T0; st < SL; st += 2) {
+                __builtin_amdgcn_sched_barrier(0);
+                fetch_win(st + 1 < SL ? st + 1 : SL - 1, w1);
+                __builtin_amdgcn_sched_barrier(0);
+                run_win(st, w0);
+                if (st + 1 >= SL)
+                    break;
+                __builtin_amdgcn_sched_barrier(0);
+                fetch_win(st + 2 < SL ? st + 2 : SL - 1, w0);
+                __builtin_amdgcn_sched_barrier(0);
+                run_win(st + 1, w1);
+            }
+        }
+        // join the runs in step order, per draft
+        for_passes<0, 4>([&](auto lc) {
+            constexpr int span = PASSES << decltype(lc)::value;
+            if constexpr (span < kLanesPerRow) {
+                constexpr int ctrl = 0x120 + (kLanesPerRow - span);  // row_ror: lane i reads lane i + span
+#pragma unroll
+                for (int i = 0; i < TG; i++) {
+                    const float Rn = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(R[i]), ctrl, 0xF, 0xF, false));
+                    const float Gn = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(Gp[i]), ctrl, 0xF, 0xF, false));
+                    R[i] = fmaf(R[i], Gn, Rn);
+                    Gp[i] = Gp[i] * Gn;
+                }
+            }
+        });
+        // y of each draft: G (S . C_t) + R + D x, gated
+#pragma unroll
+        for (int i = 0; i < TG; i++) {
+            float u = 0.0f;
+            for_passes<0, PASSES>([&](auto qc) {
+                constexpr int q = decltype(qc)::value;
+                float acc = 0.0f;
+#pragma unroll
+                for (int c = 0; c < NCH; c++)
+#pragma unroll
+                    for (int k = 0; k < VEC; k++)
+                        acc = fmaf(widen(S[q][c].v[k]), word_elem(cw[i][c], k), acc);
+                const float sum = row16_sum(acc);
+                u = col == q ? sum : u;
+            });
+            if (owner && t0 + i < T) {
+                float y = fmaf(Gp[i], u, R[i]) + d_h * from_bits<IT>(xo[i]);
+                if (zs)
+                    y *= silu(from_bits<IT>(zo[i]));
+                ys[row(t0 + i) * p.out_sr + h * p.out_sh + d_own] = narrow<IT>(bad ? __builtin_nanf("") : y);
+            }
+        }
+        // append the group's drafts at entries w + t
+        if (write) {
+#pragma unroll
+            for (int i = 0; i < TG; i++) {
+                if (t0 + i >= T)
+                    break;
+                const int64_t e = sl + w + t0 + i;
+                auto put_dt = [&](unsigned char *dst) {
+                    if (dt_f32)
+                        *reinterpret_cast<uint32_t *>(dst) = uint32_t(dlo[i]) | (uint32_t(dhi[i]) << 16);
+                    else
+                        *reinterpret_cast<uint16_t *>(dst) = dlo[i];
+                };
+                if (owner) {
+                    *reinterpret_cast<Bits *>(bxs + (e * H + h) * P + d_own) = xo[i];
+                    if (!rp.dt_per_head)
+                        put_dt(bdts + ((e * H + h) * P + d_own) * dt_bytes);
+                }
+                if (rp.dt_per_head && tile == 0 && threadIdx.x == 0)
+                    put_dt(bdts + (e * H + h) * dt_bytes);  // lane 0 owns a row; dt is the head's
+                if (h % p.heads_per_group == 0 && tile == 0 && wave == 0 && rsub == 0) {
+                    IT *dst = bBs + (e * rp.G + g) * N + col * IVEC;
+#pragma unroll
+                    for (int c = 0; c < NCH; c++)
+                        store_words<IT, IVEC>(dst + c * kLanesPerRow * IVEC,
+                                              load_words<IT, IVEC>(draft_B(t0 + i) + c * kLanesPerRow * IVEC));
+                }
+            }
+        }
+    }
+}
+
+template <typename ST, typename IT, bool SPEC>
 bool pick_replay_n(int n, KernelRef *k) {
     switch (n) {
 #define SSU_CASE(NN)                                                                     \
     case NN:                                                                             \
-        k->fn = reinterpret_cast<const void *>(&ssu_replay_kernel<ST, IT, NN>);         \
+        k->fn = SPEC ? reinterpret_cast<const void *>(&ssu_replay_spec_kernel<ST, IT, NN>) \
+                     : reinterpret_cast<const void *>(&ssu_replay_kernel<ST, IT, NN>);   \
         return true;
         SSU_CASE(16)
         SSU_CASE(32)
@@ -906,12 +1295,12 @@ bool pick_replay_n(int n, KernelRef *k) {
     return false;
 }
 
-template <typename ST>
+template <typename ST, bool SPEC>
 bool pick_replay_io(int io, int n, KernelRef *k) {
     switch (io) {
-    case SSU_F32: return pick_replay_n<ST, float>(n, k);
-    case SSU_F16: return pick_replay_n<ST, _Float16>(n, k);
-    case SSU_BF16: return pick_replay_n<ST, __bf16>(n, k);
+    case SSU_F32: return pick_replay_n<ST, float, SPEC>(n, k);
+    case SSU_F16: return pick_replay_n<ST, _Float16, SPEC>(n, k);
+    case SSU_BF16: return pick_replay_n<ST, __bf16, SPEC>(n, k);
     }
     return false;
 }
@@ -970,11 +1359,17 @@ void kernel_name(int state_dtype, int io_dtype, int dstate, bool multi, char *bu
 
 const char *hip_error_string(int e) { return hipGetErrorString(static_cast<hipError_t>(e)); }
 
-bool find_replay_kernel(int state_dtype, int io_dtype, int dstate, KernelRef *out) {
+bool find_replay_kernel(int state_dtype, int io_dtype, int dstate, bool spec, KernelRef *out) {
     switch (state_dtype) {
-    case SSU_F32: return pick_replay_io<float>(io_dtype, dstate, out);
-    case SSU_F16: return pick_replay_io<_Float16>(io_dtype, dstate, out);
-    case SSU_BF16: return pick_replay_io<__bf16>(io_dtype, dstate, out);
+    case SSU_F32:
+        return spec ? pick_replay_io<float, true>(io_dtype, dstate, out)
+                    : pick_replay_io<float, false>(io_dtype, dstate, out);
+    case SSU_F16:
+        return spec ? pick_replay_io<_Float16, true>(io_dtype, dstate, out)
+                    : pick_replay_io<_Float16, false>(io_dtype, dstate, out);
+    case SSU_BF16:
+        return spec ? pick_replay_io<__bf16, true>(io_dtype, dstate, out)
+                    : pick_replay_io<__bf16, false>(io_dtype, dstate, out);
     }
     return false;
 }

@@ -57,7 +57,8 @@ class SsuPlanInfo(ctypes.Structure):
                 ("vgprs", ctypes.c_int32), ("sgprs", ctypes.c_int32)]
 
 
-EXPORTS = ("ssu_plan", "ssu_update", "ssu_replay_update", "ssu_last_error", "ssu_abi_version")
+EXPORTS = ("ssu_plan", "ssu_update", "ssu_replay_update", "ssu_replay_spec_update",
+           "ssu_last_error", "ssu_abi_version")
 
 
 def load_library(path=None):
@@ -73,6 +74,8 @@ def load_library(path=None):
     lib.ssu_update.restype = ctypes.c_int
     lib.ssu_replay_update.argtypes = [ctypes.POINTER(SsuReplayArgs), ctypes.c_void_p]
     lib.ssu_replay_update.restype = ctypes.c_int
+    lib.ssu_replay_spec_update.argtypes = [ctypes.POINTER(SsuReplayArgs), ctypes.c_void_p]
+    lib.ssu_replay_spec_update.restype = ctypes.c_int
     lib.ssu_last_error.argtypes = []
     lib.ssu_last_error.restype = ctypes.c_char_p
     lib.ssu_abi_version.argtypes = []
@@ -122,6 +125,15 @@ def ssu_replay_update(args, stream=None):
     st = _lib.ssu_replay_update(ctypes.byref(args), ctypes.c_void_p(stream))
     if st != OK:
         _raise(st, "ssu_replay_update")
+
+
+def ssu_replay_spec_update(args, stream=None):
+    """Enqueue one ReplaySSM speculative step (include/ssu.h ssu_replay_spec_update)."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    st = _lib.ssu_replay_spec_update(ctypes.byref(args), ctypes.c_void_p(stream))
+    if st != OK:
+        _raise(st, "ssu_replay_spec_update")
 
 
 def ssu_plan(desc):
@@ -266,4 +278,24 @@ def replay_selective_state_update(state, x, dt, A, B, C, D, buf_x, buf_dt, buf_B
                             dt_softplus, state_batch_indices, pad_slot_id, out,
                             disable_state_update)
     ssu_replay_update(args, torch.cuda.current_stream(state.device).cuda_stream)
+    return out
+
+
+def replay_spec_selective_state_update(state, x, dt, A, B, C, D, buf_x, buf_dt, buf_B, buf_len,
+                                       z=None, dt_bias=None, dt_softplus=False,
+                                       state_batch_indices=None, pad_slot_id=-1, out=None,
+                                       disable_state_update=False):
+    """One ReplaySSM speculative step (ReplaySSM article, section
+    "投机解码回滚变成挪指针"): x [batch, T, heads, dim] holds T draft tokens per
+    sequence, buf_len[b] the committed entries of sequence b (0..L). When
+    buf_len + 2T > L the committed entries are first folded into the
+    checkpoint and the drafts go to entries 0..T-1, else to buf_len..; the
+    caller then advances the pointer by the accepted count (from 0 after a
+    fold). Returns y [batch, T, heads, dim]."""
+    if out is None:
+        out = torch.empty(x.shape, dtype=x.dtype, device=x.device)
+    args = make_replay_args(state, x, dt, A, B, C, D, buf_x, buf_dt, buf_B, buf_len, z, dt_bias,
+                            dt_softplus, state_batch_indices, pad_slot_id, out,
+                            disable_state_update)
+    ssu_replay_spec_update(args, torch.cuda.current_stream(state.device).cuda_stream)
     return out

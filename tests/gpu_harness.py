@@ -18,52 +18,12 @@ import torch
 
 import workloads as W
 from oracle import brute64, ssu_oracle
+from workloads.device import TORCH, dev, dev_index, device_case, device_replay, host  # noqa: F401
 import mamba_selective_state_amd as ssu
-
-TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
-
 
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
-
-
-def dev(a, dtype, device):
-    a = np.ascontiguousarray(a)
-    if dtype == "f32":
-        return torch.from_numpy(a).to(device)
-    return torch.from_numpy(a.view(np.int16)).to(device).view(TORCH[dtype])
-
-
-def dev_index(t, device):
-    if t is None:
-        return None
-    if isinstance(t, W.Strided):
-        base = torch.from_numpy(np.ascontiguousarray(t.base)).to(device)
-        return torch.as_strided(base, t.shape, t.strides)
-    return torch.from_numpy(np.ascontiguousarray(t)).to(device)
-
-
-def host(t, dtype):
-    t = t.detach().cpu().contiguous()
-    if dtype == "f32":
-        return t.numpy()
-    return t.view(torch.int16).numpy().view(np.uint16)
-
-
-def device_case(case, device="cuda:0"):
-    sd, io = case["state_dtype"], case["io_dtype"]
-    dtd = case.get("dt_dtype", io)
-    d = {"state": dev(case["state"], sd, device), "x": dev(case["x"], io, device),
-         "dt": dev(case["dt"], dtd, device), "A": torch.from_numpy(case["A"]).to(device),
-         "B": dev(case["B"], io, device), "C": dev(case["C"], io, device)}
-    for k in ("D", "dt_bias"):
-        d[k] = None if case.get(k) is None else torch.from_numpy(case[k]).to(device)
-    d["z"] = None if case.get("z") is None else dev(case["z"], io, device)
-    for k in ("state_batch_indices", "dst_state_batch_indices", "cu_seqlens",
-              "num_accepted_tokens"):
-        d[k] = dev_index(case.get(k), device)
-    return d
 
 
 def run_gpu(case, device="cuda:0", d=None, out=True, sync=True):
@@ -231,24 +191,17 @@ def subcase(case, seqs):
 
 # ---------------------------------------------------------------- ReplaySSM
 
-def device_replay(case, device="cuda:0"):
-    d = device_case(case, device)
-    io, dtd = case["io_dtype"], case.get("dt_dtype", case["io_dtype"])
-    d["buf_x"] = dev(case["buf_x"], io, device)
-    d["buf_dt"] = dev(case["buf_dt"], dtd, device)
-    d["buf_B"] = dev(case["buf_B"], io, device)
-    d["buf_len"] = torch.from_numpy(np.ascontiguousarray(case["buf_len"])).to(device)
-    return d
-
-
 def run_gpu_replay(case, d=None, device="cuda:0"):
-    """One ReplaySSM step through the binding; returns host copies of y, the
-    checkpoint pool and the three buffers."""
+    """One ReplaySSM step (the speculative one for a 4-D x) through the
+    binding; returns host copies of y, the checkpoint pool and the three
+    buffers."""
     if d is None:
         d = device_replay(case, device)
     o = torch.full(np.shape(case["x"]), float("nan"), dtype=TORCH[case["io_dtype"]],
                    device=device)
-    y = ssu.replay_selective_state_update(
+    fn = ssu.replay_spec_selective_state_update if np.ndim(case["x"]) == 4 else \
+        ssu.replay_selective_state_update
+    y = fn(
         d["state"], d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["buf_x"], d["buf_dt"],
         d["buf_B"], d["buf_len"], z=d["z"], dt_bias=d["dt_bias"],
         dt_softplus=case.get("dt_softplus", False), state_batch_indices=d["state_batch_indices"],
@@ -271,8 +224,15 @@ def compare_replay(case, got, ref, name=""):
     return stats
 
 
+def oracle_replay(case):
+    """The oracle's one-token or speculative replay step, by x's rank."""
+    if np.ndim(case["x"]) == 4:
+        return ssu_oracle.run_replay_spec(case)
+    return ssu_oracle.run_replay(case)
+
+
 def check_replay(case, name, device="cuda:0"):
-    ref = ssu_oracle.run_replay(case)
+    ref = oracle_replay(case)
     say("[gpu] %s: launching" % name)
     got = run_gpu_replay(case, device=device)
     stats = compare_replay(case, got, ref, name)

@@ -374,3 +374,44 @@ def test_replay_errors():
     r.buf_len = tdesc((3,), S.I32)
     st, msg = replay(r)
     assert st == S.ERR_VALUE and "buf_len" in msg
+
+
+# ------------------------------------------------------ replay, speculative
+
+
+def spec_args(batch=0, T=2, L=4, H=8, P=16, N=128, G=2, slots=8):
+    r = replay_args(rows=batch, L=L, H=H, P=P, N=N, G=G, slots=slots)
+    for k, tail in (("x", (H, P)), ("dt", (H, P)), ("B", (G, N)), ("C", (G, N)), ("out", (H, P))):
+        setattr(r.base, k, tdesc((batch, T) + tail, S.BF16))
+    return r
+
+
+def spec(r):
+    st = S._lib.ssu_replay_spec_update(ctypes.byref(r), None)
+    return st, S.ssu_last_error()
+
+
+def test_replay_spec_empty_is_ok_without_launch():
+    assert spec(spec_args())[0] == S.OK
+
+
+def test_replay_spec_errors():
+    assert S._lib.ssu_replay_spec_update(None, None) == S.ERR_VALUE
+    st, msg = spec(replay_args())  # a 3-D x
+    assert st == S.ERR_NOT_IMPLEMENTED and "[batch, T, heads, dim]" in msg
+    st, msg = replay(spec_args())  # the one-token entry point with a 4-D x
+    assert st == S.ERR_NOT_IMPLEMENTED and "[batch, heads, dim]" in msg
+    r = spec_args(batch=3)
+    r.base.state_batch_indices = tdesc((6,), S.I32)  # one entry per row, not per sequence
+    st, msg = spec(r)
+    assert st == S.ERR_VALUE and "1-D [batch]" in msg
+    r = spec_args(batch=3)
+    r.base.state_batch_indices = tdesc((3, 2), S.I32)
+    st, msg = spec(r)
+    assert st == S.ERR_VALUE and "1-D [batch]" in msg
+    r = spec_args(T=5, L=4)
+    st, msg = spec(r)
+    assert st == S.ERR_VALUE and "do not fit" in msg
+    r = spec_args()
+    r.base.num_accepted_tokens = tdesc((0,), S.I32)
+    assert spec(r)[0] == S.ERR_NOT_IMPLEMENTED

@@ -315,3 +315,33 @@ def replay_spec(seed=6, batch=512, T=4, heads=128, dim=64, dstate=128, groups=8,
 
 
 BUILDERS["replay_spec"] = replay_spec
+
+
+def spec_snapshots(seed=7, batch=512, T=4, heads=128, dim=64, dstate=128, groups=8,
+                   state_dtype="f32", io="bf16", index_dtype=np.int32):
+    """The speculative step done the way ReplaySSM replaces (its article,
+    section "三个瓶颈其实来自同一个动作": one full state snapshot per draft
+    token): T draft tokens per sequence through the plain multi-token update
+    ([batch, T, ...] dense form), read table [batch, T] naming the sequence's
+    committed slot (read at position 0), write table [batch, T] naming T
+    snapshot slots per sequence. Pool: batch committed slots (N(0,1)) plus
+    batch*T snapshot slots (zeros)."""
+    rng = np.random.default_rng(seed)
+    slots = batch * (1 + T)
+    c = {"state_dtype": state_dtype}
+    pool = np.zeros((slots, heads, dim, dstate),
+                    dtype=np.float32 if state_dtype == "f32" else np.uint16)
+    pool[:batch] = _normal(rng, (batch, heads, dim, dstate), state_dtype)
+    c["state"] = pool
+    lay = _layer(rng, batch * T, heads, dim, dstate, groups, io=io, dt_dtype=io)
+    for k in ("x", "dt", "B", "C", "z"):
+        lay[k] = lay[k].reshape((batch, T) + lay[k].shape[1:])
+    c.update(lay)
+    read = np.repeat(np.arange(batch, dtype=index_dtype)[:, None], T, axis=1)
+    write = (batch + np.arange(batch * T, dtype=index_dtype)).reshape(batch, T)
+    c.update(state_batch_indices=read, dst_state_batch_indices=write, pad_slot_id=-1,
+             disable_state_update=False, cu_seqlens=None, num_accepted_tokens=None)
+    return c
+
+
+BUILDERS["spec_snapshots"] = spec_snapshots
