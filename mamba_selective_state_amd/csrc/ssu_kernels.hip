@@ -1223,23 +1223,70 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes, replay_spec_waves_per_eu(siz
                 }
             }
         });
-        // y of each draft: G (S . C_t) + R + D x, gated
+        // u_t = S . C_t of the owner rows: all drafts of the group in one
+        // sweep over the tile when their decoded C fits in about 32
+        // registers, else one draft at a time
+        float u[TG];
+        auto sweep = [&](auto ni_c, int i0) {
+            constexpr int NI = decltype(ni_c)::value;
+            float Cd[NI][E];
 #pragma unroll
-        for (int i = 0; i < TG; i++) {
-            float u = 0.0f;
-            for_passes<0, PASSES>([&](auto qc) {
-                constexpr int q = decltype(qc)::value;
-                float acc = 0.0f;
+            for (int i = 0; i < NI; i++)
 #pragma unroll
                 for (int c = 0; c < NCH; c++)
 #pragma unroll
-                    for (int k = 0; k < VEC; k++)
-                        acc = fmaf(widen(S[q][c].v[k]), word_elem(cw[i][c], k), acc);
-                const float sum = row16_sum(acc);
-                u = col == q ? sum : u;
+                    for (int k = 0; k < IVEC; k++)
+                        Cd[i][c * IVEC + k] = word_elem(cw[i0 + i][c], k);
+            float uu[NI];
+#pragma unroll
+            for (int i = 0; i < NI; i++)
+                uu[i] = 0.0f;
+            for_passes<0, PASSES>([&](auto qc) {
+                constexpr int q = decltype(qc)::value;
+                float acc[NI];
+#pragma unroll
+                for (int i = 0; i < NI; i++)
+                    acc[i] = 0.0f;
+#pragma unroll
+                for (int c = 0; c < NCH; c++)
+#pragma unroll
+                    for (int k = 0; k < VEC; k++) {
+                        const float sv = widen(S[q][c].v[k]);
+#pragma unroll
+                        for (int i = 0; i < NI; i++)
+                            acc[i] = fmaf(sv, Cd[i][c * VEC + k], acc[i]);
+                    }
+#pragma unroll
+                for (int i = 0; i < NI; i++) {
+                    const float sum = row16_sum(acc[i]);
+                    uu[i] = col == q ? sum : uu[i];
+                }
             });
+#pragma unroll
+            for (int i = 0; i < NI; i++)
+                u[i0 + i] = uu[i];
+        };
+        if constexpr (TG * E <= 32)
+            sweep(std::integral_constant<int, TG>(), 0);
+        // y of each draft: G u + R + D x, gated
+#pragma unroll
+        for (int i = 0; i < TG; i++) {
+            if constexpr (TG * E > 32) {
+                u[i] = 0.0f;
+                for_passes<0, PASSES>([&](auto qc) {
+                    constexpr int q = decltype(qc)::value;
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int c = 0; c < NCH; c++)
+#pragma unroll
+                        for (int k = 0; k < VEC; k++)
+                            acc = fmaf(widen(S[q][c].v[k]), word_elem(cw[i][c], k), acc);
+                    const float sum = row16_sum(acc);
+                    u[i] = col == q ? sum : u[i];
+                });
+            }
             if (owner && t0 + i < T) {
-                float y = fmaf(Gp[i], u, R[i]) + d_h * from_bits<IT>(xo[i]);
+                float y = fmaf(Gp[i], u[i], R[i]) + d_h * from_bits<IT>(xo[i]);
                 if (zs)
                     y *= silu(from_bits<IT>(zo[i]));
                 ys[row(t0 + i) * p.out_sr + h * p.out_sh + d_own] = narrow<IT>(bad ? __builtin_nanf("") : y);
