@@ -846,3 +846,97 @@ int oracle_replay_spec(const oracle_replay_args *ra, char *err, int errlen)
     free(xs);
     return 0;
 }
+
+/* ---- memmove-safe Mamba state copies
+ *
+ * vLLM PR #50729 digest (prhub), sections "实现拆解" (implementation) and
+ * "关键源码片段" (key source excerpts): speculative decoding shifts a sequence's
+ * convolution state left inside one physical block, so a parallel copy whose
+ * source and destination ranges overlap must still behave like memmove; the
+ * generic batched copy needs the same guarantee whenever a destination starts
+ * below its source inside the copied range.
+ *
+ * Readings:
+ *  R24 batched copy: copy i moves sizes[i] bytes from src_off[i] to
+ *      dst_off[i] (byte offsets into one buffer here; device addresses on the
+ *      GPU) with memmove semantics in both directions (the page's fix covers a
+ *      destination below its source; a destination above it is the mirror
+ *      case). Two different copies may not touch the same bytes (that would
+ *      make the result depend on their order): this oracle refuses it.
+ *  R25 convolution-state shift: a pool of blocks, each conv_width tokens of
+ *      `inner` elements of elem_size bytes, token-major ([blocks, W, inner],
+ *      "SD") or dim-major ([blocks, inner, W], "DS"). Request r writes
+ *      state[dst][:W - bias] = state[src][bias:] (the page's
+ *      state[bt[src_col], token_bias:] -> state[bt[dst_col], :conv_width -
+ *      token_bias]) and leaves the rest of the destination block alone; bias
+ *      in [0, W]. Two requests may not write the same block or write a block
+ *      another reads (refused here). A request whose block ids or bias are out
+ *      of range writes nothing (the GPU library checks them on the device).
+ */
+int oracle_batch_memmove(uint8_t *buf, int64_t buf_len, const int64_t *src_off,
+                         const int64_t *dst_off, const int64_t *sizes, int64_t n,
+                         char *err, int errlen)
+{
+    for (int64_t i = 0; i < n; i++) {
+        if (sizes[i] < 0 || src_off[i] < 0 || dst_off[i] < 0 || src_off[i] + sizes[i] > buf_len ||
+            dst_off[i] + sizes[i] > buf_len) {
+            set_err(err, errlen, "copy %lld outside the buffer (size %lld)", (long long)i, (long long)sizes[i]);
+            return 1;
+        }
+        for (int64_t j = 0; j < i; j++) {
+            /* copy i's bytes (source or destination) against copy j's */
+            const int64_t ai[2] = {src_off[i], dst_off[i]}, aj[2] = {src_off[j], dst_off[j]};
+            for (int u = 0; u < 2; u++)
+                for (int v = 0; v < 2; v++) {
+                    if (u == 0 && v == 0)
+                        continue; /* two reads of the same bytes are fine */
+                    if (ai[u] < aj[v] + sizes[j] && aj[v] < ai[u] + sizes[i] && sizes[i] && sizes[j]) {
+                        set_err(err, errlen, "copies %lld and %lld touch the same bytes", (long long)j, (long long)i);
+                        return 1;
+                    }
+                }
+        }
+    }
+    for (int64_t i = 0; i < n; i++)
+        memmove(buf + dst_off[i], buf + src_off[i], (size_t)sizes[i]); /* R24 */
+    return 0;
+}
+
+enum { OR_CONV_SD = 0, OR_CONV_DS = 1 };
+
+int oracle_conv_shift(uint8_t *pool, int64_t blocks, int32_t layout, int64_t W, int64_t inner,
+                      int64_t elem_size, const int64_t *src_blk, const int64_t *dst_blk,
+                      const int64_t *bias, int64_t n, char *err, int errlen)
+{
+    const int64_t block_bytes = W * inner * elem_size;
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t q = 0; q < r; q++) {
+            const int ok_r = src_blk[r] >= 0 && src_blk[r] < blocks && dst_blk[r] >= 0 &&
+                             dst_blk[r] < blocks && bias[r] >= 0 && bias[r] <= W;
+            const int ok_q = src_blk[q] >= 0 && src_blk[q] < blocks && dst_blk[q] >= 0 &&
+                             dst_blk[q] < blocks && bias[q] >= 0 && bias[q] <= W;
+            if (ok_r && ok_q && (dst_blk[r] == dst_blk[q] || dst_blk[r] == src_blk[q] ||
+                                 src_blk[r] == dst_blk[q])) {
+                set_err(err, errlen, "requests %lld and %lld share a written block", (long long)q, (long long)r);
+                return 1;
+            }
+        }
+    for (int64_t r = 0; r < n; r++) {
+        if (src_blk[r] < 0 || src_blk[r] >= blocks || dst_blk[r] < 0 || dst_blk[r] >= blocks ||
+            bias[r] < 0 || bias[r] > W)
+            continue; /* R25: out of range, nothing written */
+        uint8_t *src = pool + src_blk[r] * block_bytes;
+        uint8_t *dst = pool + dst_blk[r] * block_bytes;
+        const int64_t keep = W - bias[r]; /* tokens moved */
+        if (layout == OR_CONV_SD) {
+            /* tokens bias..W-1 of the source become tokens 0..W-bias-1 */
+            memmove(dst, src + bias[r] * inner * elem_size, (size_t)(keep * inner * elem_size));
+        } else {
+            /* each of the inner rows shifts left by bias tokens */
+            for (int64_t d = 0; d < inner; d++)
+                memmove(dst + d * W * elem_size, src + (d * W + bias[r]) * elem_size,
+                        (size_t)(keep * elem_size));
+        }
+    }
+    return 0;
+}

@@ -338,3 +338,62 @@ def _run_replay(case, oracle, spec):
         raise OracleError(err.value.decode())
     return {"y": out.reshape(x.shape), "state": pool_out, "buf_x": bx_out, "buf_dt": bdt_out,
             "buf_B": bB_out, "written": written.astype(bool)}
+
+
+# ---------------------------------------------------------------- state copies
+
+CONV_LAYOUTS = {"SD": 0, "DS": 1}
+
+
+def _copy_fns(lib):
+    if not hasattr(lib, "_copy_ready"):
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        lib.oracle_batch_memmove.argtypes = [ctypes.c_void_p, ctypes.c_int64, i64p, i64p, i64p,
+                                             ctypes.c_int64, ctypes.c_char_p, ctypes.c_int]
+        lib.oracle_batch_memmove.restype = ctypes.c_int
+        lib.oracle_conv_shift.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                          ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, i64p,
+                                          i64p, i64p, ctypes.c_int64, ctypes.c_char_p,
+                                          ctypes.c_int]
+        lib.oracle_conv_shift.restype = ctypes.c_int
+        lib._copy_ready = True
+
+
+def _i64(a):
+    return np.ascontiguousarray(a, dtype=np.int64)
+
+
+def run_batch_memmove(buf, src_off, dst_off, sizes, oracle=None):
+    """Batched copy with memmove semantics (oracle_batch_memmove): copy i
+    moves sizes[i] bytes from byte offset src_off[i] to dst_off[i] of `buf`
+    (a uint8 array). Returns the new buffer."""
+    lib = (oracle or default()).lib
+    _copy_fns(lib)
+    out = np.array(buf, dtype=np.uint8, copy=True).ravel()
+    s, d, z = _i64(src_off), _i64(dst_off), _i64(sizes)
+    err = ctypes.create_string_buffer(256)
+    p = ctypes.POINTER(ctypes.c_int64)
+    if lib.oracle_batch_memmove(out.ctypes.data, out.size, s.ctypes.data_as(p),
+                                d.ctypes.data_as(p), z.ctypes.data_as(p), len(z), err, 256):
+        raise OracleError(err.value.decode())
+    return out.reshape(np.shape(buf))
+
+
+def run_conv_shift(pool, layout, src_blk, dst_blk, bias, oracle=None):
+    """Convolution-state shift (oracle_conv_shift): pool [blocks, W, inner]
+    ("SD") or [blocks, inner, W] ("DS") of any element type; request r writes
+    state[dst][:W - bias] = state[src][bias:]. Returns the new pool."""
+    lib = (oracle or default()).lib
+    _copy_fns(lib)
+    pool = np.ascontiguousarray(pool)
+    out = pool.copy()
+    blocks = pool.shape[0]
+    W, inner = (pool.shape[1], pool.shape[2]) if layout == "SD" else (pool.shape[2], pool.shape[1])
+    s, d, b = _i64(src_blk), _i64(dst_blk), _i64(bias)
+    err = ctypes.create_string_buffer(256)
+    p = ctypes.POINTER(ctypes.c_int64)
+    if lib.oracle_conv_shift(out.ctypes.data, blocks, CONV_LAYOUTS[layout], W, inner,
+                             pool.itemsize, s.ctypes.data_as(p), d.ctypes.data_as(p),
+                             b.ctypes.data_as(p), len(s), err, 256):
+        raise OracleError(err.value.decode())
+    return out

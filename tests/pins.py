@@ -864,6 +864,58 @@ def pin_replay_spec_brute_force(orc, combos=20, seed=12):
         assert np.all(np.abs(y_o - b["y64"]) <= tol), (k, io, L, T)
 
 
+# ------------------------------------------------------------ state copies
+
+def pin_memmove_matches_snapshot(orc):
+    """Batched copies with memmove semantics (vLLM PR #50729 digest, "测试配套":
+    expected values come from slicing the untouched snapshot): rows copied
+    onto themselves shifted left (the PR's regression case, scaled down) and
+    right, copies to other rows, and empty copies."""
+    from oracle import ssu_oracle
+    for direction in ("left", "right", "apart"):
+        for shift in (1, 16, 2000):
+            c = W.memmove_rows(rows=6, row_bytes=4096, shift=shift, direction=direction)
+            snap = c["buf"].copy()
+            got = ssu_oracle.run_batch_memmove(c["buf"], c["src_off"], c["dst_off"], c["sizes"], orc)
+            want = snap.copy()
+            for s, d, n in zip(c["src_off"], c["dst_off"], c["sizes"]):
+                want[d:d + n] = snap[s:s + n]
+            assert np.array_equal(got, want), (direction, shift)
+    buf = np.arange(64, dtype=np.uint8)
+    got = ssu_oracle.run_batch_memmove(buf, [3], [9], [0], orc)
+    assert np.array_equal(got, buf)
+
+
+def pin_conv_shift_matches_snapshot(orc):
+    """Convolution-state shift (vLLM PR #50729 digest, "实现拆解": state[dst][:W -
+    bias] = state[src][bias:]), both layouts, the same or another block, every
+    bias 0..W, element sizes 2/4/8 (the PR's fp16/fp32/fp64 cases), against
+    slices of the untouched snapshot; the two layouts agree after a
+    transpose; out-of-range requests write nothing."""
+    from oracle import ssu_oracle
+    for dt in (np.float16, np.float32, np.float64):
+        for width in (4, 3):
+            for bias in range(width + 1):
+                sd = W.conv_shift(seed=bias, requests=4, width=width, inner=6, dtype=dt,
+                                  layout="SD", same_frac=0.5)
+                sd["bias"][:] = bias
+                got = ssu_oracle.run_conv_shift(sd["pool"], "SD", sd["src_blk"], sd["dst_blk"],
+                                                sd["bias"], orc)
+                want = sd["pool"].copy()
+                for s, d in zip(sd["src_blk"], sd["dst_blk"]):
+                    want[d, :width - bias] = sd["pool"][s, bias:].copy()
+                assert np.array_equal(got, want), (dt, width, bias)
+                ds_pool = np.ascontiguousarray(sd["pool"].transpose(0, 2, 1))
+                got_ds = ssu_oracle.run_conv_shift(ds_pool, "DS", sd["src_blk"], sd["dst_blk"],
+                                                   sd["bias"], orc)
+                assert np.array_equal(got_ds, np.ascontiguousarray(want.transpose(0, 2, 1)))
+    c = W.conv_shift(seed=1, requests=3, width=4, inner=5, dtype=np.float32, layout="DS")
+    c["bias"][:] = [5, -1, 1]
+    c["src_blk"][2] = 99
+    got = ssu_oracle.run_conv_shift(c["pool"], "DS", c["src_blk"], c["dst_blk"], c["bias"], orc)
+    assert np.array_equal(got, c["pool"])
+
+
 ALL = [pin_golden_mate_examples, pin_f16_decode_exhaustive, pin_f16_encode, pin_bf16_roundtrip, pin_softplus,
        pin_dt_zero_keeps_state, pin_b_zero_pure_decay, pin_zero_state_closed_form,
        pin_c_zero_and_z_zero, pin_mtp_equals_chained_calls, pin_unrolled_window,
@@ -873,4 +925,5 @@ ALL = [pin_golden_mate_examples, pin_f16_decode_exhaustive, pin_f16_encode, pin_
        pin_replay_L1_is_plain_update, pin_replay_flush_is_chain,
        pin_replay_nonflush_writes_entry_only, pin_replay_zero_checkpoint, pin_replay_disable,
        pin_replay_brute_force, pin_replay_spec_is_chain, pin_replay_spec_rollback,
-       pin_replay_spec_fold_boundary, pin_replay_spec_pad_and_disable, pin_replay_spec_brute_force]
+       pin_replay_spec_fold_boundary, pin_replay_spec_pad_and_disable, pin_replay_spec_brute_force,
+       pin_memmove_matches_snapshot, pin_conv_shift_matches_snapshot]

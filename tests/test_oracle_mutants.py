@@ -70,6 +70,15 @@ MUTANTS = [
      "wj = wj + (j < w ? BB(j, n) : DB(0, n)) * DC(t, n);"),
     ("spec_draft_dt_row", "const float raw = k < w ? BDT(k, d) : DDT(k - w, d);",
      "const float raw = k < w ? BDT(k, d) : DDT(0, d);"),
+    # memmove-safe state copies
+    ("copy_forward_bytes", "memmove(buf + dst_off[i], buf + src_off[i], (size_t)sizes[i]); /* R24 */",
+     "for (int64_t k = 0; k < sizes[i]; k++) buf[dst_off[i] + k] = buf[src_off[i] + k];"),
+    ("copy_backward_bytes", "memmove(buf + dst_off[i], buf + src_off[i], (size_t)sizes[i]); /* R24 */",
+     "for (int64_t k = sizes[i] - 1; k >= 0; k--) buf[dst_off[i] + k] = buf[src_off[i] + k];"),
+    ("conv_sd_without_bias", "memmove(dst, src + bias[r] * inner * elem_size,", "memmove(dst, src,"),
+    ("conv_ds_without_bias", "memmove(dst + d * W * elem_size, src + (d * W + bias[r]) * elem_size,",
+     "memmove(dst + d * W * elem_size, src + (d * W) * elem_size,"),
+    ("conv_ds_as_sd", "if (layout == OR_CONV_SD) {", "if (layout != 7) {"),
     ("default_dst_is_seq",
      "a->wtab.data ? &a->wtab : (a->rtab.data ? &a->rtab : NULL)", "a->wtab.data ? &a->wtab : NULL"),
     ("flat_write_b_plus_t", "int64_t i = tb->ndim == 1 ? bos + t :", "int64_t i = tb->ndim == 1 ? b + t :"),

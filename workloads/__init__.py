@@ -345,3 +345,52 @@ def spec_snapshots(seed=7, batch=512, T=4, heads=128, dim=64, dstate=128, groups
 
 
 BUILDERS["spec_snapshots"] = spec_snapshots
+
+
+# ------------------------------------------------------------ state copies
+
+def memmove_rows(rows=128, row_bytes=32 * 1024, shift=16, direction="left", seed=8):
+    """Rows of a byte buffer, each copied onto itself shifted by `shift`
+    bytes: 'left' moves row[shift:] to row[:-shift] (the vLLM PR #50729
+    regression test: 128 rows x 32 KiB, shift 16, a mod-251 pattern), 'right'
+    the mirror case, 'apart' copies row i to row rows + i. Returns dict(buf
+    uint8, src_off, dst_off, sizes)."""
+    n_rows = rows * (2 if direction == "apart" else 1)
+    buf = ((np.arange(n_rows * row_bytes, dtype=np.int64) + seed) % 251).astype(np.uint8)
+    base = np.arange(rows, dtype=np.int64) * row_bytes
+    size = row_bytes - shift
+    if direction == "left":
+        src, dst = base + shift, base
+    elif direction == "right":
+        src, dst = base, base + shift
+    else:
+        src, dst = base, base + rows * row_bytes
+        size = row_bytes
+    return {"buf": buf, "src_off": src, "dst_off": dst, "sizes": np.full(rows, size, np.int64)}
+
+
+def conv_shift(seed=9, requests=6144, width=4, inner=8192, dtype=np.float16, layout="SD",
+               same_frac=0.5, max_bias=3):
+    """Convolution-state shifts on a pool of 2 * requests blocks ([blocks, W,
+    inner] for 'SD', [blocks, inner, W] for 'DS'), N(0,1) values stored in
+    `dtype` (for floats) or random bits. Request r reads block 2r and writes
+    block 2r (a shift inside one block) for a `same_frac` share of the
+    requests, else block 2r + 1; bias ~ U{1..max_bias} (accepted-token biases
+    1..3 in the vLLM tests)."""
+    rng = np.random.default_rng(seed)
+    blocks = 2 * requests
+    shape = (blocks, width, inner) if layout == "SD" else (blocks, inner, width)
+    dt = np.dtype(dtype)
+    if dt.kind == "f":
+        pool = rng.standard_normal(shape, dtype=np.float32).astype(dt)
+    else:
+        pool = rng.integers(0, 256, size=shape + (dt.itemsize,), dtype=np.uint8).view(dt)[..., 0]
+    src = 2 * np.arange(requests, dtype=np.int64)
+    same = rng.random(requests) < same_frac
+    dst = np.where(same, src, src + 1)
+    bias = rng.integers(1, max_bias + 1, requests).astype(np.int64)
+    return {"pool": pool, "layout": layout, "src_blk": src, "dst_blk": dst, "bias": bias}
+
+
+BUILDERS["memmove_rows"] = memmove_rows
+BUILDERS["conv_shift"] = conv_shift
