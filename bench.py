@@ -17,7 +17,7 @@ Prints ONE JSON line:
              current kernel source, else null
   cpu_baseline  the CPU oracle timed on this host on the same workload
 Options: --config {decode, decode_pad, mtp, varlen, varlen_disable, varlen_nodst, replay,
-replay_spec, spec_snapshots},
+replay_spec, spec_snapshots, conv_shift_sd, conv_shift_ds, memcpy_left},
 --no-cpu-baseline, --calib-copy (also runs a plain device copy of the state's
 size, the calibration kernel for the counters).
 """
@@ -38,7 +38,7 @@ METRIC = "SSU decode achieved HBM GB/s (% of peak) and token-head updates/s"
 HBM_PEAK_GBS = 8000.0
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "mamba_selective_state_amd", "csrc", f)
-                  for f in ("ssu_kernels.hip", "ssu_internal.h")]
+                  for f in ("ssu_kernels.hip", "ssu_copy.hip", "ssu_internal.h")]
 
 DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 
@@ -70,6 +70,16 @@ def workload(name):
                                     "with one fp32 state snapshot per draft (batch 512 x T = 4, "
                                     "heads 128, dim 64, dstate 128, groups 8), the design "
                                     "ReplaySSM replaces")
+    if name in ("conv_shift_sd", "conv_shift_ds"):
+        layout = "SD" if name.endswith("sd") else "DS"
+        return W.conv_shift(layout=layout), (
+            "%s: 6144 convolution-state shifts (256 sequences x 24 layers), width 4, inner 8192, "
+            "fp16 (64 KiB blocks), %s layout, half of them inside one block, bias ~ U{1..3}"
+            % (name, "token-major" if layout == "SD" else "dim-major"))
+    if name == "memcpy_left":
+        return W.memmove_rows(rows=4096, row_bytes=32 * 1024, shift=16, direction="left"), (
+            "memcpy_left: 4096 rows of 32 KiB each copied onto itself shifted left by 16 bytes "
+            "(the vLLM PR #50729 regression case, 32x the rows)")
     if name.startswith("varlen"):
         dst = name != "varlen_nodst"
         dis = name == "varlen_disable"
@@ -184,6 +194,93 @@ def replay_algorithmic_bytes(case):
     return int(total + R * row + vec + idx), int(R * H)
 
 
+COPY_CONFIGS = ("conv_shift_sd", "conv_shift_ds", "memcpy_left")
+
+
+def copy_algorithmic_bytes(case):
+    """Bytes a copy must read and write: every moved byte once each way, plus
+    the request vectors. Returns (bytes, requests)."""
+    if "pool" in case:
+        pool = case["pool"]
+        Wd = pool.shape[1] if case["layout"] == "SD" else pool.shape[2]
+        inner = pool.shape[2] if case["layout"] == "SD" else pool.shape[1]
+        moved = int(np.sum(Wd - np.asarray(case["bias"]))) * inner * pool.itemsize
+        return 2 * moved + 3 * 8 * len(case["bias"]), len(case["bias"])
+    sizes = np.asarray(case["sizes"])
+    return int(2 * np.sum(np.maximum(sizes, 0)) + 3 * 8 * len(sizes)), len(sizes)
+
+
+def copy_bench(args, name, case, desc):
+    """bench.py for the state copies: one step is one call over the workload."""
+    import torch
+    import mamba_selective_state_amd as ssu
+    dev = torch.device("cuda", 0)
+    alg_bytes, requests = copy_algorithmic_bytes(case)
+    if "pool" in case:
+        pool = case["pool"]
+        t = torch.from_numpy(pool.view(np.uint8)).to(dev).view(torch.float16).reshape(pool.shape)
+        idx = [torch.from_numpy(np.asarray(case[k])).to(dev) for k in ("src_blk", "dst_blk", "bias")]
+        cargs = ssu.make_conv_shift_args(t, *idx, layout=case["layout"])
+        launch = lambda h: ssu.ssu_conv_state_shift(cargs, h)  # noqa: E731
+        kernel = "conv_shift_%s_kernel" % ("token_major" if case["layout"] == "SD" else "dim_major")
+    else:
+        buf = torch.from_numpy(case["buf"]).to(dev)
+        base = buf.data_ptr()
+        src = (torch.from_numpy(np.asarray(case["src_off"])) + base).to(dev)
+        dst = (torch.from_numpy(np.asarray(case["dst_off"])) + base).to(dev)
+        sizes = torch.from_numpy(np.asarray(case["sizes"])).to(dev)
+        from mamba_selective_state_amd import ssu as binding
+        descs = [binding.tensor_desc(v, dev) for v in (src, dst, sizes)]
+        max_size = int(np.max(case["sizes"]))
+        launch = lambda h: ssu.ssu_batch_memcpy(*descs, max_size, h)  # noqa: E731
+        kernel = "batch_memcpy_kernel"
+    stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream
+    for _ in range(args.warmup):
+        launch(handle)
+    torch.cuda.synchronize(dev)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        launch(handle)
+    end.record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    event_ms = start.elapsed_time(end) / args.steps
+    achieved = alg_bytes / (event_ms * 1e-3) / 1e9
+    result = {
+        "metric": "state copy achieved HBM GB/s (% of peak)", "value": round(alg_bytes * args.steps / wall / 1e9, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+        "config": {"workload": desc, "bytes_per_step": alg_bytes, "requests_per_step": requests,
+                   "kernel": kernel},
+        "pct_of_hbm_peak": round(100.0 * achieved / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_counters(name),
+                     "kernel_us": round(event_ms * 1e3, 2)},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import ssu_oracle
+        times = []
+        for _ in range(args.cpu_reps):
+            t1 = time.perf_counter()
+            if "pool" in case:
+                ssu_oracle.run_conv_shift(case["pool"], case["layout"], case["src_blk"], case["dst_blk"],
+                                          case["bias"])
+            else:
+                ssu_oracle.run_batch_memmove(case["buf"], case["src_off"], case["dst_off"], case["sizes"])
+            times.append(time.perf_counter() - t1)
+        tm = statistics.median(times)
+        result["cpu_baseline"] = {"value": round(alg_bytes / tm / 1e9, 4), "unit": "GB/s", "cores": 1,
+                                  "kind": "oracle",
+                                  "sample": "the whole workload, median of %d calls (%.3f s each), "
+                                            "plain-C memmove oracle incl. its NumPy wrapper"
+                                            % (args.cpu_reps, tm)}
+    print(json.dumps(result), flush=True)
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
@@ -237,6 +334,14 @@ def main():
               "(sequences and heads shard with no exchange); run it with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.config in COPY_CONFIGS:
+        import torch
+        if not torch.cuda.is_available():
+            raise SystemExit("bench.py needs a GPU")
+        case, desc = workload(args.config)
+        copy_bench(args, args.config, case, desc)
+        return
 
     import torch
     import mamba_selective_state_amd as ssu

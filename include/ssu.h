@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SSU_ABI_VERSION 1
+#define SSU_ABI_VERSION 2
 
 #ifndef SSU_API
 #define SSU_API __attribute__((visibility("default")))
@@ -68,7 +68,9 @@ typedef enum {
     SSU_F16 = 1,
     SSU_BF16 = 2,
     SSU_I32 = 3,
-    SSU_I64 = 4
+    SSU_I64 = 4,
+    SSU_F64 = 5, /* state copies only */
+    SSU_U8 = 6   /* state copies only */
 } ssu_dtype_t;
 
 typedef enum {
@@ -227,6 +229,52 @@ SSU_API ssu_status_t ssu_replay_update(const ssu_replay_args_t *args, void *stre
  * writes nothing; disable_state_update writes neither checkpoint nor buffer.
  * Same error, stream and allocation conventions as ssu_update. */
 SSU_API ssu_status_t ssu_replay_spec_update(const ssu_replay_args_t *args, void *stream);
+
+/* ---- memmove-safe Mamba state copies (vLLM PR #50729 digest, prhub:
+ * sections "实现拆解" and "关键源码片段"). Speculative decoding shifts a
+ * convolution state left inside one physical block; a parallel copy whose
+ * destination overlaps its own source must still end as if the whole source
+ * had been read first (memmove). */
+
+/* Batched byte copy with memmove semantics: copy i moves sizes[i] bytes from
+ * address src_ptrs[i] to dst_ptrs[i]. A copy whose destination overlaps its
+ * own source (on either side) is done by one workgroup in source order away
+ * from the overlap, each chunk read completely before any of it is written;
+ * other copies are split over several workgroups.
+ *   src_ptrs, dst_ptrs  [n] i64 (device): device byte addresses
+ *   sizes               [n] i32 / i64 (device): byte counts (<= 0: nothing)
+ *   max_size            the caller's bound on the sizes; it only sets how many
+ *                       workgroups share one copy (larger sizes are still
+ *                       copied in full)
+ * Two different copies must not touch the same bytes (the result would
+ * depend on their order). DEVICE memory owned by the caller; one kernel on
+ * `stream`, asynchronous, allocates nothing; n = 0 launches nothing. */
+SSU_API ssu_status_t ssu_batch_memcpy(const ssu_tensor_t *src_ptrs, const ssu_tensor_t *dst_ptrs,
+                                      const ssu_tensor_t *sizes, int64_t max_size, void *stream);
+
+/* Convolution-state layouts: token-major [blocks, W, inner] ("SD") and
+ * dim-major [blocks, inner, W] ("DS"). */
+typedef enum { SSU_CONV_TOKEN_MAJOR = 0, SSU_CONV_DIM_MAJOR = 1 } ssu_conv_layout_t;
+
+typedef struct {
+    ssu_tensor_t state;      /* [blocks, W, inner] or [blocks, inner, W], contiguous,
+                                16-byte aligned, any dtype (only its element size
+                                matters) */
+    int32_t layout;          /* ssu_conv_layout_t */
+    ssu_tensor_t src_block;  /* [n] i32 / i64 (device) */
+    ssu_tensor_t dst_block;  /* [n] i32 / i64 (device) */
+    ssu_tensor_t bias;       /* [n] i32 / i64 (device): tokens dropped, 0..W */
+} ssu_conv_shift_args_t;
+
+/* Convolution-state shift: request r writes
+ *   state[dst_block[r]][:W - bias[r]] = state[src_block[r]][bias[r]:]
+ * (token rows for the token-major layout, each of the inner rows for the
+ * dim-major one) and leaves the rest of the destination block as it was; a
+ * request with src == dst shifts a block inside itself. A request whose block
+ * ids or bias are out of range writes nothing (checked on the device). Two
+ * requests must not write the same block or one that another reads. One
+ * kernel on `stream`, asynchronous, allocates nothing. */
+SSU_API ssu_status_t ssu_conv_state_shift(const ssu_conv_shift_args_t *args, void *stream);
 
 /* Message of the last failing call on this thread ("" if none). The pointer
  * stays valid until the next call on the same thread. */

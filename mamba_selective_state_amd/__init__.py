@@ -3,13 +3,16 @@
 The update runs in hand-written HIP kernels behind a C ABI (include/ssu.h,
 libssu.so); this package is its Python binding.
 """
-from .ssu import (LIBRARY_PATH, SsuArgs, SsuError, SsuReplayArgs, make_args, make_replay_args,
+from .ssu import (LIBRARY_PATH, SsuArgs, SsuConvShiftArgs, SsuError, SsuReplayArgs, batch_memcpy,
+                  conv_state_shift, make_args, make_conv_shift_args, make_replay_args,
                   prewarm_selective_state_update, replay_selective_state_update,
                   replay_spec_selective_state_update, selective_state_update, ssu_abi_version,
-                  ssu_last_error, ssu_plan, ssu_replay_spec_update, ssu_replay_update, ssu_update)
+                  ssu_batch_memcpy, ssu_conv_state_shift, ssu_last_error, ssu_plan,
+                  ssu_replay_spec_update, ssu_replay_update, ssu_update)
 
 __all__ = ["selective_state_update", "prewarm_selective_state_update",
            "replay_selective_state_update", "replay_spec_selective_state_update", "ssu_update",
            "ssu_replay_update", "ssu_replay_spec_update", "ssu_plan", "ssu_last_error",
            "ssu_abi_version", "make_args", "make_replay_args", "SsuArgs", "SsuReplayArgs",
-           "SsuError", "LIBRARY_PATH"]
+           "SsuError", "LIBRARY_PATH", "batch_memcpy", "conv_state_shift", "ssu_batch_memcpy",
+           "ssu_conv_state_shift", "make_conv_shift_args", "SsuConvShiftArgs"]

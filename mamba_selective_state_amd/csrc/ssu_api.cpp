@@ -12,6 +12,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 
 #include "../../include/ssu.h"
@@ -33,7 +34,10 @@ ssu_status_t fail(ssu_status_t st, const char *fmt, ...) {
 
 bool is_float(int d) { return d == SSU_F32 || d == SSU_F16 || d == SSU_BF16; }
 bool is_index(int d) { return d == SSU_I32 || d == SSU_I64; }
-int64_t elem_bytes(int d) { return (d == SSU_F16 || d == SSU_BF16) ? 2 : (d == SSU_I64 ? 8 : 4); }
+int64_t elem_bytes(int d) {
+    return (d == SSU_F16 || d == SSU_BF16) ? 2 : (d == SSU_I64 || d == SSU_F64) ? 8 : d == SSU_U8 ? 1 : 4;
+}
+bool known_dtype(int d) { return d >= SSU_F32 && d <= SSU_U8; }
 bool present(const ssu_tensor_t &t) { return t.data != nullptr; }
 bool dstate_supported(int64_t n) { return n == 16 || n == 32 || n == 64 || n == 128 || n == 256; }
 bool aligned(const void *p, int64_t bytes) { return (reinterpret_cast<uintptr_t>(p) % bytes) == 0; }
@@ -45,6 +49,8 @@ const char *dtype_str(int d) {
     case SSU_BF16: return "bf16";
     case SSU_I32: return "i32";
     case SSU_I64: return "i64";
+    case SSU_F64: return "f64";
+    case SSU_U8: return "u8";
     }
     return "unknown";
 }
@@ -522,6 +528,111 @@ ssu_status_t prepare(const ssu_args_t *a, Prepared *out) {
 extern "C" {
 
 int ssu_abi_version(void) { return SSU_ABI_VERSION; }
+
+// ---- memmove-safe state copies
+
+// Workgroups that share one non-overlapping copy of up to `bytes` bytes:
+// one per 16 KiB (256 lanes x 4 words of 16 bytes), between 1 and 64.
+static int32_t copy_tiles_for(int64_t bytes) {
+    const int64_t tile = static_cast<int64_t>(ssu::kCopyThreads) * 4 * 16;
+    int64_t t = (bytes + tile - 1) / tile;
+    return static_cast<int32_t>(t < 1 ? 1 : (t > 64 ? 64 : t));
+}
+
+ssu_status_t ssu_batch_memcpy(const ssu_tensor_t *src_ptrs, const ssu_tensor_t *dst_ptrs,
+                              const ssu_tensor_t *sizes, int64_t max_size, void *stream) {
+    if (!src_ptrs || !dst_ptrs || !sizes)
+        return fail(SSU_ERR_VALUE, "ssu_batch_memcpy: NULL argument");
+    const ssu_tensor_t *ptrs[] = {src_ptrs, dst_ptrs};
+    const char *names[] = {"src_ptrs", "dst_ptrs"};
+    for (int k = 0; k < 2; k++) {
+        const ssu_tensor_t &t = *ptrs[k];
+        if (!present(t) || t.dtype != SSU_I64 || t.ndim != 1)
+            return fail(SSU_ERR_VALUE, "%s must be a 1-D i64 array of device addresses", names[k]);
+        if (t.stride[0] < 0 || !aligned(t.data, 8))
+            return fail(SSU_ERR_VALUE, "%s: bad stride or alignment", names[k]);
+    }
+    const int64_t n = src_ptrs->size[0];
+    if (dst_ptrs->size[0] != n)
+        return fail(SSU_ERR_VALUE, "src_ptrs and dst_ptrs differ in length");
+    ssu::CopyParams cp;
+    memset(&cp, 0, sizeof cp);
+    int64_t sizes_s = 0;
+    bool sizes_i64 = false;
+    if (!present(*sizes))
+        return fail(SSU_ERR_VALUE, "sizes is required");
+    ssu_status_t s = meta_vector("sizes", *sizes, n, &cp.sizes, &sizes_s, &sizes_i64);
+    if (s != SSU_OK)
+        return s;
+    if (n == 0)
+        return g_error.clear(), SSU_OK;
+    cp.src_ptrs = src_ptrs->data;
+    cp.dst_ptrs = dst_ptrs->data;
+    cp.src_s = src_ptrs->stride[0];
+    cp.dst_s = dst_ptrs->stride[0];
+    cp.sizes_s = sizes_s;
+    cp.sizes_i64 = sizes_i64;
+    cp.tiles = copy_tiles_for(max_size);
+    const int64_t grid = n * cp.tiles;
+    if (grid > INT32_MAX)
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "too many copies");
+    const int e = ssu::launch_batch_memcpy(cp, static_cast<unsigned>(grid), stream);
+    if (e != 0)
+        return fail(SSU_ERR_HIP, "kernel launch failed: %s", ssu::hip_error_string(e));
+    g_error.clear();
+    return SSU_OK;
+}
+
+ssu_status_t ssu_conv_state_shift(const ssu_conv_shift_args_t *a, void *stream) {
+    if (!a)
+        return fail(SSU_ERR_VALUE, "ssu_conv_state_shift: args is NULL");
+    const ssu_tensor_t &st = a->state;
+    if (!present(st) || st.ndim != 3 || !known_dtype(st.dtype))
+        return fail(SSU_ERR_VALUE, "state must be a 3-D conv-state pool");
+    if (a->layout != SSU_CONV_TOKEN_MAJOR && a->layout != SSU_CONV_DIM_MAJOR)
+        return fail(SSU_ERR_VALUE, "layout must be SSU_CONV_TOKEN_MAJOR or SSU_CONV_DIM_MAJOR");
+    const int64_t es = elem_bytes(st.dtype);
+    if (st.stride[2] != 1 || st.stride[1] != st.size[2] || st.stride[0] != st.size[1] * st.size[2] ||
+        !aligned(st.data, 16))
+        return fail(SSU_ERR_VALUE, "state must be contiguous and 16-byte aligned");
+    ssu::ConvParams cv;
+    memset(&cv, 0, sizeof cv);
+    const bool dim_major = a->layout == SSU_CONV_DIM_MAJOR;
+    cv.state = const_cast<void *>(st.data);
+    cv.blocks = st.size[0];
+    cv.W = dim_major ? st.size[2] : st.size[1];
+    cv.inner = dim_major ? st.size[1] : st.size[2];
+    cv.elem = es;
+    const int64_t n = present(a->src_block) ? a->src_block.size[0] : -1;
+    if (!present(a->src_block) || !present(a->dst_block) || !present(a->bias))
+        return fail(SSU_ERR_VALUE, "src_block, dst_block and bias are required");
+    bool i64 = false;
+    ssu_status_t s;
+    if ((s = meta_vector("src_block", a->src_block, n, &cv.src, &cv.src_s, &i64)) != SSU_OK)
+        return s;
+    cv.src_i64 = i64;
+    if ((s = meta_vector("dst_block", a->dst_block, n, &cv.dst, &cv.dst_s, &i64)) != SSU_OK)
+        return s;
+    cv.dst_i64 = i64;
+    if ((s = meta_vector("bias", a->bias, n, &cv.bias, &cv.bias_s, &i64)) != SSU_OK)
+        return s;
+    cv.bias_i64 = i64;
+    if (n == 0 || cv.blocks == 0 || cv.W == 0 || cv.inner == 0)
+        return g_error.clear(), SSU_OK;
+    // dim-major: a workgroup per 8 rows a lane; token-major: one workgroup a
+    // request (it loops over the block's 16 KiB tiles)
+    cv.tiles = dim_major ? static_cast<int32_t>(std::min<int64_t>(
+                               64, (cv.inner + 8 * ssu::kCopyThreads - 1) / (8 * ssu::kCopyThreads)))
+                         : 1;
+    const int64_t grid = n * cv.tiles;
+    if (grid > INT32_MAX)
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "too many requests");
+    const int e = ssu::launch_conv_shift(cv, dim_major, static_cast<unsigned>(grid), stream);
+    if (e != 0)
+        return fail(SSU_ERR_HIP, "kernel launch failed: %s", ssu::hip_error_string(e));
+    g_error.clear();
+    return SSU_OK;
+}
 
 const char *ssu_last_error(void) { return g_error.c_str(); }
 

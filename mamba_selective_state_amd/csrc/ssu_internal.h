@@ -157,6 +157,26 @@ const char *hip_error_string(int e);
 int launch(const KernelRef &k, const Params &p, unsigned grid, unsigned block, void *stream);
 
 // The ReplaySSM decode kernel for (state dtype, io dtype, dstate).
+// memmove-safe state copies (ssu_copy.hip): workgroup size, the batched
+// copy's and the convolution shift's arguments (strides in elements).
+constexpr int kCopyThreads = 256;
+struct CopyParams {
+    const void *src_ptrs, *dst_ptrs, *sizes;
+    int64_t src_s, dst_s, sizes_s;
+    int32_t sizes_i64;
+    int32_t tiles;  // workgroups per copy
+};
+struct ConvParams {
+    void *state;
+    int64_t blocks, W, inner, elem;
+    const void *src, *dst, *bias;
+    int64_t src_s, dst_s, bias_s;
+    int32_t src_i64, dst_i64, bias_i64;
+    int32_t tiles;  // workgroups per request
+};
+int launch_batch_memcpy(const CopyParams &cp, unsigned grid, void *stream);
+int launch_conv_shift(const ConvParams &cv, bool dim_major, unsigned grid, void *stream);
+
 bool find_replay_kernel(int state_dtype, int io_dtype, int dstate, bool spec, KernelRef *out);
 int launch_replay(const KernelRef &k, const Params &p, const ReplayParams &rp, unsigned grid,
                   unsigned block, void *stream);

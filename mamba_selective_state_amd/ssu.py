@@ -17,13 +17,14 @@ import torch
 
 from . import build as _build
 
-F32, F16, BF16, I32, I64 = 0, 1, 2, 3, 4
+F32, F16, BF16, I32, I64, F64, U8 = 0, 1, 2, 3, 4, 5, 6
 OK, ERR_VALUE, ERR_NOT_IMPLEMENTED, ERR_HIP = 0, 1, 2, 3
 OPT_STATE_SCALE, OPT_INTERMEDIATE_STATES, OPT_RAND_SEED = 1, 2, 4
 OPT_CACHE_STEPS, OPT_ALGORITHM, OPT_BACKEND = 8, 16, 32
 
 _TORCH_DTYPES = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16,
-                 torch.int32: I32, torch.int64: I64}
+                 torch.int32: I32, torch.int64: I64, torch.float64: F64, torch.uint8: U8}
+CONV_TOKEN_MAJOR, CONV_DIM_MAJOR = 0, 1
 
 
 class SsuTensor(ctypes.Structure):
@@ -45,6 +46,11 @@ class SsuReplayArgs(ctypes.Structure):
                 ("buf_B", SsuTensor), ("buf_len", SsuTensor)]
 
 
+class SsuConvShiftArgs(ctypes.Structure):
+    _fields_ = [("state", SsuTensor), ("layout", ctypes.c_int32), ("src_block", SsuTensor),
+                ("dst_block", SsuTensor), ("bias", SsuTensor)]
+
+
 class SsuPlanDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("state_dtype", "io_dtype", "dt_dtype", "slot_dtype", "meta_dtype", "heads",
@@ -58,6 +64,7 @@ class SsuPlanInfo(ctypes.Structure):
 
 
 EXPORTS = ("ssu_plan", "ssu_update", "ssu_replay_update", "ssu_replay_spec_update",
+           "ssu_batch_memcpy", "ssu_conv_state_shift",
            "ssu_last_error", "ssu_abi_version")
 
 
@@ -76,6 +83,11 @@ def load_library(path=None):
     lib.ssu_replay_update.restype = ctypes.c_int
     lib.ssu_replay_spec_update.argtypes = [ctypes.POINTER(SsuReplayArgs), ctypes.c_void_p]
     lib.ssu_replay_spec_update.restype = ctypes.c_int
+    lib.ssu_batch_memcpy.argtypes = [ctypes.POINTER(SsuTensor)] * 3 + [ctypes.c_int64,
+                                                                       ctypes.c_void_p]
+    lib.ssu_batch_memcpy.restype = ctypes.c_int
+    lib.ssu_conv_state_shift.argtypes = [ctypes.POINTER(SsuConvShiftArgs), ctypes.c_void_p]
+    lib.ssu_conv_state_shift.restype = ctypes.c_int
     lib.ssu_last_error.argtypes = []
     lib.ssu_last_error.restype = ctypes.c_char_p
     lib.ssu_abi_version.argtypes = []
@@ -299,3 +311,57 @@ def replay_spec_selective_state_update(state, x, dt, A, B, C, D, buf_x, buf_dt, 
                             disable_state_update)
     ssu_replay_spec_update(args, torch.cuda.current_stream(state.device).cuda_stream)
     return out
+
+
+# ---------------------------------------------------------------- state copies
+
+def ssu_batch_memcpy(src_ptrs, dst_ptrs, sizes, max_size, stream=None):
+    """Enqueue a batched memmove-safe copy (include/ssu.h ssu_batch_memcpy);
+    the first three arguments are SsuTensor descriptors."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    st = _lib.ssu_batch_memcpy(ctypes.byref(src_ptrs), ctypes.byref(dst_ptrs), ctypes.byref(sizes),
+                               int(max_size), ctypes.c_void_p(stream))
+    if st != OK:
+        _raise(st, "ssu_batch_memcpy")
+
+
+def batch_memcpy(src_ptrs, dst_ptrs, sizes, max_size=None):
+    """Copy sizes[i] bytes from device address src_ptrs[i] to dst_ptrs[i] for
+    every i, with memmove semantics where a copy overlaps its own source (vLLM
+    PR #50729 digest, "实现拆解"). src_ptrs, dst_ptrs: int64 CUDA tensors of
+    addresses; sizes: int32/int64 CUDA tensor; max_size: a bound on the sizes
+    (it only sets the parallelism; default 64 KiB)."""
+    dev = src_ptrs.device
+    ssu_batch_memcpy(tensor_desc(src_ptrs, dev), tensor_desc(dst_ptrs, dev),
+                     tensor_desc(sizes, dev), 65536 if max_size is None else max_size,
+                     torch.cuda.current_stream(dev).cuda_stream)
+
+
+def ssu_conv_state_shift(args, stream=None):
+    """Enqueue a convolution-state shift (include/ssu.h ssu_conv_state_shift)."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    st = _lib.ssu_conv_state_shift(ctypes.byref(args), ctypes.c_void_p(stream))
+    if st != OK:
+        _raise(st, "ssu_conv_state_shift")
+
+
+def make_conv_shift_args(state, src_block, dst_block, bias, layout="SD"):
+    a = SsuConvShiftArgs()
+    dev = state.device
+    a.state = tensor_desc(state, dev)
+    a.layout = CONV_TOKEN_MAJOR if layout == "SD" else CONV_DIM_MAJOR
+    a.src_block = tensor_desc(src_block, dev)
+    a.dst_block = tensor_desc(dst_block, dev)
+    a.bias = tensor_desc(bias, dev)
+    return a
+
+
+def conv_state_shift(state, src_block, dst_block, bias, layout="SD"):
+    """state[dst_block[r]][:W - bias[r]] = state[src_block[r]][bias[r]:] for
+    every request r (vLLM PR #50729 digest, "实现拆解"), in place and safe
+    when a request shifts a block inside itself. state: [blocks, W, inner]
+    for layout "SD" (token-major) or [blocks, inner, W] for "DS"."""
+    ssu_conv_state_shift(make_conv_shift_args(state, src_block, dst_block, bias, layout),
+                         torch.cuda.current_stream(state.device).cuda_stream)

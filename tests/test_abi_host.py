@@ -39,7 +39,8 @@ def test_struct_layout_matches_header(tmp_path):
     makes of include/ssu.h."""
     structs = {"ssu_tensor_t": S.SsuTensor, "ssu_args_t": S.SsuArgs,
                "ssu_plan_desc_t": S.SsuPlanDesc, "ssu_plan_info_t": S.SsuPlanInfo,
-               "ssu_replay_args_t": S.SsuReplayArgs}
+               "ssu_replay_args_t": S.SsuReplayArgs,
+               "ssu_conv_shift_args_t": S.SsuConvShiftArgs}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ssu.h"', "int main(void) {"]
     for cname, cls in structs.items():
         lines.append('printf("%s SIZEOF %%zu\\n", sizeof(%s));' % (cname, cname))
@@ -415,3 +416,55 @@ def test_replay_spec_errors():
     r = spec_args()
     r.base.num_accepted_tokens = tdesc((0,), S.I32)
     assert spec(r)[0] == S.ERR_NOT_IMPLEMENTED
+
+
+# ---------------------------------------------------------------- state copies
+
+
+def memcpy(src, dst, sizes, max_size=0):
+    st = S._lib.ssu_batch_memcpy(ctypes.byref(src), ctypes.byref(dst), ctypes.byref(sizes),
+                                 max_size, None)
+    return st, S.ssu_last_error()
+
+
+def test_batch_memcpy_empty_and_errors():
+    assert memcpy(tdesc((0,), S.I64), tdesc((0,), S.I64), tdesc((0,), S.I64))[0] == S.OK
+    assert S._lib.ssu_batch_memcpy(None, None, None, 0, None) == S.ERR_VALUE
+    st, msg = memcpy(tdesc((3,), S.I32), tdesc((3,), S.I64), tdesc((3,), S.I64))
+    assert st == S.ERR_VALUE and "src_ptrs" in msg
+    st, msg = memcpy(tdesc((3,), S.I64), tdesc((2,), S.I64), tdesc((3,), S.I64))
+    assert st == S.ERR_VALUE and "length" in msg
+    st, msg = memcpy(tdesc((3,), S.I64), tdesc((3,), S.I64), tdesc((2,), S.I64))
+    assert st == S.ERR_VALUE and "sizes" in msg
+    st, msg = memcpy(tdesc((3,), S.I64), tdesc((3,), S.I64), tdesc((3,), S.F32))
+    assert st == S.ERR_VALUE and "sizes" in msg
+    st, msg = memcpy(tdesc((3,), S.I64), tdesc((3,), S.I64), S.SsuTensor())
+    assert st == S.ERR_VALUE and "sizes" in msg
+
+
+def shift(state, src, dst, bias, layout=S.CONV_TOKEN_MAJOR):
+    a = S.SsuConvShiftArgs()
+    a.state, a.layout, a.src_block, a.dst_block, a.bias = state, layout, src, dst, bias
+    st = S._lib.ssu_conv_state_shift(ctypes.byref(a), None)
+    return st, S.ssu_last_error()
+
+
+def test_conv_state_shift_empty_and_errors():
+    pool = tdesc((6, 4, 32), S.F16)
+    v0 = tdesc((0,), S.I32)
+    assert shift(pool, v0, v0, v0)[0] == S.OK
+    assert shift(tdesc((6, 32, 4), S.F64), v0, v0, v0, S.CONV_DIM_MAJOR)[0] == S.OK
+    assert S._lib.ssu_conv_state_shift(None, None) == S.ERR_VALUE
+    v3 = tdesc((3,), S.I64)
+    st, msg = shift(tdesc((6, 128), S.F16), v3, v3, v3)
+    assert st == S.ERR_VALUE and "3-D" in msg
+    st, msg = shift(pool, v3, v3, v3, layout=7)
+    assert st == S.ERR_VALUE and "layout" in msg
+    st, msg = shift(tdesc((6, 4, 32), S.F16, strides=(256, 64, 2)), v3, v3, v3)
+    assert st == S.ERR_VALUE and "contiguous" in msg
+    st, msg = shift(pool, v3, tdesc((2,), S.I64), v3)
+    assert st == S.ERR_VALUE and "dst_block" in msg
+    st, msg = shift(pool, v3, v3, S.SsuTensor())
+    assert st == S.ERR_VALUE and "required" in msg
+    st, msg = shift(pool, v3, v3, tdesc((3,), S.F32))
+    assert st == S.ERR_VALUE and "bias" in msg

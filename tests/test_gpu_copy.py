@@ -1,0 +1,121 @@
+"""memmove-safe Mamba state copies on the GPU (ssu_batch_memcpy,
+ssu_conv_state_shift) against the CPU oracle and against slices of the
+untouched snapshot, each case repeated 10 times (vLLM PR #50729 digest,
+"测试配套": the race is intermittent, so a single pass proves little)."""
+import numpy as np
+import pytest
+import torch
+
+import gpu_harness as G
+import workloads as W
+from oracle import ssu_oracle
+
+pytestmark = pytest.mark.gpu
+REPEAT = 10
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    torch.cuda.init()
+
+
+def run_memcpy(c, repeat=REPEAT, max_size=None):
+    """Device copies of c["buf"] per c's offsets; checks every repetition
+    against the snapshot's slices and the oracle."""
+    buf = torch.from_numpy(c["buf"]).to("cuda:0")
+    snap = buf.clone()
+    base = buf.data_ptr()
+    src = (torch.from_numpy(np.asarray(c["src_off"], np.int64)) + base).to("cuda:0")
+    dst = (torch.from_numpy(np.asarray(c["dst_off"], np.int64)) + base).to("cuda:0")
+    sizes = torch.from_numpy(np.asarray(c["sizes"])).to("cuda:0")
+    want = c["buf"].copy()
+    for s, d, n in zip(c["src_off"], c["dst_off"], c["sizes"]):
+        if n > 0:
+            want[d:d + n] = c["buf"][s:s + n]
+    ref = ssu_oracle.run_batch_memmove(c["buf"], c["src_off"], c["dst_off"], np.maximum(c["sizes"], 0))
+    assert np.array_equal(ref, want)
+    for r in range(repeat):
+        buf.copy_(snap)
+        G.ssu.batch_memcpy(src, dst, sizes, max_size)
+        torch.cuda.synchronize()
+        got = buf.cpu().numpy()
+        assert np.array_equal(got, want), "repetition %d" % r
+
+
+@pytest.mark.parametrize("direction", ["left", "right", "apart"])
+@pytest.mark.parametrize("shift", [16, 1, 6, 4096])
+def test_batch_memcpy_rows(direction, shift):
+    """The PR's regression case (128 rows x 32 KiB shifted left by 16 bytes,
+    a mod-251 pattern) and its mirror and misaligned variants."""
+    G.say("[gpu] batch memcpy %s shift %d" % (direction, shift))
+    run_memcpy(W.memmove_rows(rows=128, row_bytes=32 * 1024, shift=shift, direction=direction))
+
+
+def test_batch_memcpy_large_and_empty():
+    """One 8 MiB copy shifted onto itself (many ordered chunks), large disjoint
+    copies beyond the max_size hint (tiles loop), and zero / negative sizes."""
+    G.say("[gpu] batch memcpy large")
+    c = W.memmove_rows(rows=1, row_bytes=8 << 20, shift=4096 + 8, direction="left")
+    run_memcpy(c, repeat=3)
+    c = W.memmove_rows(rows=1, row_bytes=8 << 20, shift=12, direction="right")
+    run_memcpy(c, repeat=3)
+    c = W.memmove_rows(rows=4, row_bytes=1 << 20, direction="apart")
+    run_memcpy(c, repeat=2, max_size=4096)
+    c = W.memmove_rows(rows=6, row_bytes=4096, shift=16, direction="left")
+    c["sizes"][[1, 4]] = [0, -5]
+    run_memcpy(c, repeat=2)
+
+
+def run_shift(c, repeat=REPEAT):
+    pool = c["pool"]
+    dev = torch.from_numpy(pool.view(np.uint8)).to("cuda:0").view(
+        {1: torch.uint8, 2: torch.float16, 4: torch.float32, 8: torch.float64}[pool.itemsize])
+    dev = dev.reshape(pool.shape)
+    snap = dev.clone()
+    idx = {k: torch.from_numpy(np.asarray(c[k])).to("cuda:0") for k in ("src_blk", "dst_blk", "bias")}
+    ref = ssu_oracle.run_conv_shift(pool, c["layout"], c["src_blk"], c["dst_blk"], c["bias"])
+    want = pool.copy()
+    Wd = pool.shape[1] if c["layout"] == "SD" else pool.shape[2]
+    for s, d, b in zip(c["src_blk"], c["dst_blk"], c["bias"]):
+        if 0 <= b <= Wd and 0 <= s < pool.shape[0] and 0 <= d < pool.shape[0]:
+            if c["layout"] == "SD":
+                want[d, :Wd - b] = pool[s, b:].copy()
+            else:
+                want[d, :, :Wd - b] = pool[s, :, b:].copy()
+    assert np.array_equal(ref.view(np.uint8), want.view(np.uint8))
+    for r in range(repeat):
+        dev.copy_(snap)
+        G.ssu.conv_state_shift(dev, idx["src_blk"], idx["dst_blk"], idx["bias"], c["layout"])
+        torch.cuda.synchronize()
+        got = dev.cpu().numpy().view(np.uint8).reshape(want.view(np.uint8).shape)
+        assert np.array_equal(got, want.view(np.uint8)), "repetition %d" % r
+
+
+@pytest.mark.parametrize("layout", ["SD", "DS"])
+@pytest.mark.parametrize("dtype", [np.float16, np.float32, np.float64])
+def test_conv_shift(layout, dtype):
+    """Same and distinct blocks, biases 1..3 (the PR's accept-token biases),
+    fp16 / fp32 / fp64 conv states, both layouts."""
+    G.say("[gpu] conv shift %s %s" % (layout, np.dtype(dtype).name))
+    c = W.conv_shift(seed=3, requests=48, width=4, inner=1000, dtype=dtype, layout=layout)
+    run_shift(c)
+
+
+def test_conv_shift_edges():
+    """Bias 0 and W, width 3 and 7, inner sizes not a multiple of a chunk,
+    byte elements, and out-of-range requests (written nowhere)."""
+    G.say("[gpu] conv shift edges")
+    for layout in ("SD", "DS"):
+        for width, inner in ((3, 37), (7, 300), (4, 8192)):
+            c = W.conv_shift(seed=width, requests=12, width=width, inner=inner, dtype=np.uint8,
+                             layout=layout)
+            c["bias"][:4] = [0, width, 1, width - 1]
+            run_shift(c, repeat=3)
+        c = W.conv_shift(seed=5, requests=6, width=4, inner=64, dtype=np.float32, layout=layout)
+        c["bias"][0] = 5
+        c["bias"][1] = -1
+        c["src_blk"][2] = 999
+        c["dst_blk"][3] = -2
+        run_shift(c, repeat=2)
