@@ -248,6 +248,15 @@ def copy_bench(args, name, case, desc):
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
     event_ms = start.elapsed_time(end) / args.steps
+    if args.calib_copy:
+        nbytes = 1 << 30
+        src_c = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst_c = torch.empty_like(src_c)
+        for _ in range(3):
+            dst_c.copy_(src_c)
+        torch.cuda.synchronize(dev)
+        print("[bench] calibration copy: %d bytes read, %d written" % (nbytes, nbytes),
+              file=sys.stderr, flush=True)
     achieved = alg_bytes / (event_ms * 1e-3) / 1e9
     result = {
         "metric": "state copy achieved HBM GB/s (% of peak)", "value": round(alg_bytes * args.steps / wall / 1e9, 2),
