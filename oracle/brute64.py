@@ -302,3 +302,66 @@ def run_replay_spec(case):
     out["y"] = from_f64(Y, io)
     out["y64"] = Y
     return out
+
+
+def run_ssd_chunked(case):
+    """SSD prefill in float64 by the chunked algorithm (not the token loop of
+    the C oracle): per chunk, the decay cumsum, the chunk's own state from a
+    zero start, the state passed in from the previous chunk (or the initial
+    state where seq_idx opens a sequence), and each token's output as the
+    intra-chunk causal sum plus the decayed entering state read out by C."""
+    io, sd = case["io_dtype"], case["state_dtype"]
+    dtd = case.get("dt_dtype", io)
+    X = to_f64(case["x"], io)
+    T, H, P = X.shape
+    DT = to_f64(case["dt"], dtd)
+    Bm, Cm = to_f64(case["B"], io), to_f64(case["C"], io)
+    G, N = Bm.shape[1:]
+    Z = None if case.get("z") is None else to_f64(case["z"], io)
+    A = np.asarray(case["A"], np.float64)
+    Dv = None if case.get("D") is None else np.asarray(case["D"], np.float64)
+    bias = None if case.get("dt_bias") is None else np.asarray(case["dt_bias"], np.float64)
+    lo, hi = case.get("dt_limit", (0.0, float("inf")))
+    init = None if case.get("initial_states") is None else to_f64(case["initial_states"], sd)
+    cu = np.asarray(case["cu_chunk_seqlens"])
+    seq = np.asarray(case["seq_idx"])
+    nch = len(seq)
+    Y = np.zeros((T, H, P))
+    states = np.zeros((nch, H, P, N))
+    for h in range(H):
+        g = h // (H // G)
+        S_prev = None
+        for c in range(nch):
+            t0, t1 = int(cu[c]), int(cu[c + 1])
+            v = DT[t0:t1, h].copy()
+            if bias is not None:
+                v = v + bias[h]
+            if case.get("dt_softplus", False):
+                v = np.where(v > 20.0, v, np.log1p(np.exp(np.minimum(v, 20.0))))
+            v = np.clip(v, lo, hi)
+            acum = np.cumsum(v * A[h])                      # decay cumsum in the chunk
+            x, Bc, Cc = X[t0:t1, h], Bm[t0:t1, g], Cm[t0:t1, g]
+            if c == 0 or seq[c] != seq[c - 1]:
+                S_in = init[seq[c], h] if init is not None else np.zeros((P, N))
+            else:
+                S_in = S_prev
+            # the chunk's own state from zero: sum_t exp(acum[-1] - acum[t]) dt'_t x_t B_t^T
+            w = np.exp(acum[-1] - acum) * v if len(v) else v
+            S_own = (x * w[:, None]).T @ Bc
+            S_out = np.exp(acum[-1] if len(v) else 0.0) * S_in + S_own
+            # outputs: causal intra-chunk sum plus the entering state
+            L = t1 - t0
+            CB = Cc @ Bc.T
+            decay = np.exp(acum[:, None] - acum[None, :]) * np.tril(np.ones((L, L)))
+            y = (CB * decay * v[None, :]) @ x + np.exp(acum)[:, None] * (Cc @ S_in.T)
+            if Dv is not None:
+                y = y + Dv[h] * x
+            if Z is not None:
+                zz = Z[t0:t1, h]
+                y = y * (zz / (1.0 + np.exp(-zz)))
+            Y[t0:t1, h] = y
+            states[c, h] = S_out
+            S_prev = S_out
+    last = np.asarray(case["last_chunk_indices"])
+    return {"y64": Y, "chunk_states64": states, "states64": states[last],
+            "y": from_f64(Y, io), "chunk_states": from_f64(states, sd)}

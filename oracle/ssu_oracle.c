@@ -940,3 +940,115 @@ int oracle_conv_shift(uint8_t *pool, int64_t blocks, int32_t layout, int64_t W, 
     }
     return 0;
 }
+
+/* ---- SSD packed variable-length prefill
+ *
+ * MATE docs, "Mamba / SSU", section "SSD packed prefill" and the API entry of
+ * ssd_combined_fwd_varlen: one packed call over a variable-length batch runs
+ * the same recurrence as the decode step over every token of every sequence
+ * (the five SSD stages are a chunked way to compute it), with x [tokens,
+ * heads, dim], one dt per (token, head), dt' = softplus(dt + dt_bias) (or
+ * dt + dt_bias) clamped to dt_limit = (lo, hi) (default (0, inf): floored at
+ * zero), optional initial states, D and z; it returns the state after each
+ * sequence's last chunk, or after every chunk.
+ *
+ * Readings:
+ *  R26 the oracle is the recurrence itself, token by token in chunk order:
+ *      S = S * exp(dt' A[h]) + (dt' x) B^T, y = S . C + D x, times silu(z);
+ *      the state is carried in fp32 and rounded to the state dtype only where
+ *      it is returned;
+ *  R27 chunk c covers tokens cu_chunk_seqlens[c] .. cu_chunk_seqlens[c+1]-1
+ *      (the only authority for that mapping); chunk c opens a sequence when
+ *      c = 0 or seq_idx[c] != seq_idx[c-1], and then starts from
+ *      initial_states[seq_idx[c]] (or zeros); any other chunk continues from
+ *      the previous chunk's state;
+ *  R28 the state recorded for chunk c is the state after its last token; the
+ *      returned states are those of chunks last_chunk_indices[b] (or all
+ *      chunks when intermediate states are asked for);
+ *  R29 D is one value per head; z gates after D, as in the decode step.
+ */
+typedef struct {
+    int64_t T, H, P, N, G, nchunks, batch, chunk_size;
+    int32_t io_dtype, dt_dtype, state_dtype;
+    const void *x;            /* [T, H, P] io dtype */
+    const void *dt;           /* [T, H] dt dtype */
+    const float *A;           /* [H] */
+    const void *B, *C;        /* [T, G, N] io dtype */
+    const float *D;           /* [H] or NULL */
+    const void *z;            /* [T, H, P] or NULL */
+    const float *dt_bias;     /* [H] or NULL */
+    int32_t dt_softplus;
+    float dt_lo, dt_hi;
+    const int64_t *cu_chunk;  /* [nchunks + 1] */
+    const int64_t *seq_idx;   /* [nchunks] */
+    const void *init;         /* [batch, H, P, N] state dtype, or NULL */
+    void *out;                /* [T, H, P] io dtype */
+    void *chunk_states;       /* [nchunks, H, P, N] state dtype */
+} oracle_ssd_args;
+
+int oracle_ssd(const oracle_ssd_args *a, char *err, int errlen)
+{
+    const int64_t H = a->H, P = a->P, N = a->N, G = a->G, tile = P * N;
+    if (G <= 0 || H % G || a->nchunks < 0 || a->chunk_size < 1) {
+        set_err(err, errlen, "bad shape%lld%lld", 0, 0);
+        return 1;
+    }
+    if (a->nchunks > 0 && (a->cu_chunk[0] != 0 || a->cu_chunk[a->nchunks] != a->T)) {
+        set_err(err, errlen, "cu_chunk_seqlens must run from 0 to the token count (%lld)%lld", (long long)a->T, 0);
+        return 1;
+    }
+    for (int64_t c = 0; c < a->nchunks; c++) {
+        const int64_t len = a->cu_chunk[c + 1] - a->cu_chunk[c];
+        if (len < 0 || len > a->chunk_size) {
+            set_err(err, errlen, "chunk %lld has %lld tokens", (long long)c, (long long)len);
+            return 1;
+        }
+        if (a->seq_idx[c] < 0 || a->seq_idx[c] >= a->batch) {
+            set_err(err, errlen, "seq_idx[%lld] = %lld outside the batch", (long long)c, (long long)a->seq_idx[c]);
+            return 1;
+        }
+    }
+    const int64_t per_group = H / G;
+    float *S = (float *)malloc((size_t)(H * tile) * sizeof(float));
+    for (int64_t c = 0; c < a->nchunks; c++) {
+        const int opens = c == 0 || a->seq_idx[c] != a->seq_idx[c - 1]; /* R27 */
+        for (int64_t h = 0; h < H; h++) {
+            float *Sh = S + h * tile;
+            const int64_t g = h / per_group;
+            if (opens)
+                for (int64_t e = 0; e < tile; e++)
+                    Sh[e] = a->init ? load_as_f32(a->init, a->state_dtype, (a->seq_idx[c] * H + h) * tile + e) : 0.0f;
+            for (int64_t t = a->cu_chunk[c]; t < a->cu_chunk[c + 1]; t++) {
+                float v = load_as_f32(a->dt, a->dt_dtype, t * H + h);
+                if (a->dt_bias)
+                    v = v + a->dt_bias[h];
+                if (a->dt_softplus)
+                    v = oracle_softplus(v);
+                if (v < a->dt_lo) /* dt_limit, after softplus */
+                    v = a->dt_lo;
+                if (v > a->dt_hi)
+                    v = a->dt_hi;
+                const float decay = expf(a->A[h] * v); /* R26 */
+                for (int64_t d = 0; d < P; d++) {
+                    const float xv = load_as_f32(a->x, a->io_dtype, (t * H + h) * P + d);
+                    const float dtx = v * xv;
+                    float y = 0.0f;
+                    for (int64_t n = 0; n < N; n++) {
+                        float *s = Sh + d * N + n;
+                        *s = *s * decay + dtx * load_as_f32(a->B, a->io_dtype, (t * G + g) * N + n);
+                        y = y + *s * load_as_f32(a->C, a->io_dtype, (t * G + g) * N + n);
+                    }
+                    if (a->D) /* R29 */
+                        y = y + xv * a->D[h];
+                    if (a->z)
+                        y = y * silu(load_as_f32(a->z, a->io_dtype, (t * H + h) * P + d));
+                    store_from_f32(a->out, a->io_dtype, (t * H + h) * P + d, y);
+                }
+            }
+            for (int64_t e = 0; e < tile; e++) /* R28 */
+                store_from_f32(a->chunk_states, a->state_dtype, (c * H + h) * tile + e, Sh[e]);
+        }
+    }
+    free(S);
+    return 0;
+}

@@ -397,3 +397,72 @@ def run_conv_shift(pool, layout, src_blk, dst_blk, bias, oracle=None):
                              b.ctypes.data_as(p), len(s), err, 256):
         raise OracleError(err.value.decode())
     return out
+
+
+# ---------------------------------------------------------------- SSD prefill
+
+class _SsdArgs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("T", "H", "P", "N", "G", "nchunks", "batch",
+                                              "chunk_size")] + [
+        ("io_dtype", ctypes.c_int32), ("dt_dtype", ctypes.c_int32), ("state_dtype", ctypes.c_int32),
+        ("x", ctypes.c_void_p), ("dt", ctypes.c_void_p), ("A", ctypes.c_void_p),
+        ("B", ctypes.c_void_p), ("C", ctypes.c_void_p), ("D", ctypes.c_void_p),
+        ("z", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p), ("dt_softplus", ctypes.c_int32),
+        ("dt_lo", ctypes.c_float), ("dt_hi", ctypes.c_float),
+        ("cu_chunk", ctypes.c_void_p), ("seq_idx", ctypes.c_void_p), ("init", ctypes.c_void_p),
+        ("out", ctypes.c_void_p), ("chunk_states", ctypes.c_void_p)]
+
+
+def run_ssd(case, oracle=None):
+    """SSD packed prefill (oracle_ssd): the case holds x [T, H, P], dt [T, H],
+    A, B / C [T, G, N], D, z, dt_bias (as for the decode step), dt_softplus,
+    dt_limit (lo, hi), chunk_size, cu_chunk_seqlens, seq_idx,
+    last_chunk_indices, initial_states ([batch, H, P, N] or None),
+    state_dtype, io_dtype, dt_dtype. Returns dict(y, chunk_states [nchunks,
+    H, P, N], states = chunk_states[last_chunk_indices])."""
+    lib = (oracle or default()).lib
+    if not hasattr(lib, "_ssd_ready"):
+        lib.oracle_ssd.argtypes = [ctypes.POINTER(_SsdArgs), ctypes.c_char_p, ctypes.c_int]
+        lib.oracle_ssd.restype = ctypes.c_int
+        lib._ssd_ready = True
+    io, sd = case["io_dtype"], case["state_dtype"]
+    dtd = case.get("dt_dtype", io)
+    x = _arr(case["x"], _np_dtype(io))
+    T, H, P = x.shape
+    dt = _arr(case["dt"], _np_dtype(dtd))
+    Bm, Cm = _arr(case["B"], _np_dtype(io)), _arr(case["C"], _np_dtype(io))
+    G, N = Bm.shape[1:]
+    z = case.get("z")
+    z = None if z is None else _arr(z, _np_dtype(io))
+    A = _arr(case["A"], np.float32)
+    D = case.get("D")
+    D = None if D is None else _arr(D, np.float32)
+    bias = case.get("dt_bias")
+    bias = None if bias is None else _arr(bias, np.float32)
+    cu = _i64(case["cu_chunk_seqlens"])
+    seq = _i64(case["seq_idx"])
+    last = _i64(case["last_chunk_indices"])
+    nchunks = len(seq)
+    batch = len(last)
+    init = case.get("initial_states")
+    init = None if init is None else _arr(init, _np_dtype(sd))
+    out = np.zeros((T, H, P), dtype=_np_dtype(io))
+    states = np.zeros((nchunks, H, P, N), dtype=_np_dtype(sd))
+    a = _SsdArgs()
+    a.T, a.H, a.P, a.N, a.G, a.nchunks, a.batch = T, H, P, N, G, nchunks, batch
+    a.chunk_size = int(case["chunk_size"])
+    a.io_dtype, a.dt_dtype, a.state_dtype = DTYPES[io], DTYPES[dtd], DTYPES[sd]
+    a.x, a.dt, a.A, a.B, a.C = _ptr(x), _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm)
+    a.D, a.z, a.dt_bias = _ptr(D), _ptr(z), _ptr(bias)
+    a.dt_softplus = int(bool(case.get("dt_softplus", False)))
+    lo, hi = case.get("dt_limit", (0.0, float("inf")))
+    a.dt_lo, a.dt_hi = lo, hi
+    a.cu_chunk, a.seq_idx, a.init = _ptr(cu), _ptr(seq), _ptr(init)
+    a.out, a.chunk_states = _ptr(out), _ptr(states)
+    err = ctypes.create_string_buffer(256)
+    if lib.oracle_ssd(ctypes.byref(a), err, 256):
+        raise OracleError(err.value.decode())
+    if np.any((last < 0) | (last >= max(nchunks, 1))):
+        raise OracleError("last_chunk_indices outside the chunks")
+    return {"y": out, "chunk_states": states,
+            "states": states[last] if nchunks else np.zeros((batch, H, P, N), states.dtype)}

@@ -916,6 +916,123 @@ def pin_conv_shift_matches_snapshot(orc):
     assert np.array_equal(got, c["pool"])
 
 
+# ------------------------------------------------------------ SSD prefill
+
+def _ssd_case(**kw):
+    base = dict(seed=1, lengths=(70, 16, 1, 33), heads=4, dim=8, dstate=16, groups=2,
+                chunk_size=16)
+    base.update(kw)
+    return W.ssd(**base)
+
+
+def pin_ssd_matches_chunked_float64(orc):
+    """SSD prefill (MATE "SSD packed prefill"): the token-by-token oracle
+    against an independent float64 implementation of the chunked algorithm
+    (decay cumsum, chunk states, state passing, intra-chunk causal sum plus
+    the decayed entering state), over chunk sizes, dtypes, initial states,
+    dt_limit and softplus on and off."""
+    from oracle import ssu_oracle
+    combos = [dict(io="f32", state_dtype="f32"), dict(io="bf16", state_dtype="f32", chunk_size=8),
+              dict(io="bf16", state_dtype="bf16", initial_states=False),
+              dict(io="f32", state_dtype="f32", softplus=False),            # negative dt' floored at 0
+              dict(io="f32", state_dtype="f16", dt_limit=(0.01, 0.05)),
+              dict(io="f32", state_dtype="f32", z=False, D=False, lengths=(5, 40, 17))]
+    for kw in combos:
+        c = _ssd_case(**kw)
+        r = ssu_oracle.run_ssd(c, orc)
+        q = brute64.run_ssd_chunked(c)
+        io, sd = c["io_dtype"], c["state_dtype"]
+        scale_y = np.abs(q["y64"]).max() + 1.0
+        tol_y = (1e-5 if io == "f32" else 8e-3) * scale_y
+        assert np.abs(f64(r["y"], io) - q["y64"]).max() <= tol_y, kw
+        scale_s = np.abs(q["chunk_states64"]).max() + 1.0
+        tol_s = (1e-5 if sd == "f32" else 8e-3) * scale_s
+        assert np.abs(f64(r["chunk_states"], sd) - q["chunk_states64"]).max() <= tol_s, kw
+        assert np.array_equal(r["states"], r["chunk_states"][c["last_chunk_indices"]])
+
+
+def _ssd_as_decode(c, b):
+    """Sequence b of an SSD case as a dense [1, len] plain-update case from
+    its initial state (slot 0 of a one-slot pool)."""
+    cu = np.asarray(c["cu_seqlens"])
+    t0, t1 = int(cu[b]), int(cu[b + 1])
+    H, P = np.shape(c["x"])[1:]
+    N = np.shape(c["B"])[2]
+    pool = (np.asarray(c["initial_states"])[b:b + 1] if c.get("initial_states") is not None
+            else np.zeros((1, H, P, N), np.float32 if c["state_dtype"] == "f32" else np.uint16))
+    d = {"state": pool.copy(), "state_dtype": c["state_dtype"], "io_dtype": c["io_dtype"],
+         "dt_dtype": c["dt_dtype"], "A": c["A"], "D": c["D"], "dt_bias": c["dt_bias"],
+         "dt_softplus": c["dt_softplus"], "pad_slot_id": -1, "disable_state_update": False,
+         "cu_seqlens": None, "num_accepted_tokens": None,
+         "state_batch_indices": np.zeros((1, t1 - t0), np.int64),
+         "dst_state_batch_indices": np.zeros((1, t1 - t0), np.int64)}
+    for k in ("x", "dt", "B", "C", "z"):
+        d[k] = None if c.get(k) is None else np.asarray(c[k])[t0:t1][None]
+    return d, t0, t1
+
+
+def pin_ssd_equals_decode_chain(orc):
+    """Each sequence of a prefill equals the plain update applied to its
+    tokens one after the other from its initial state (dt' stays positive, so
+    the default dt_limit is inactive), y and final state bit for bit."""
+    from oracle import ssu_oracle
+    c = _ssd_case(io="bf16", state_dtype="f32")
+    r = ssu_oracle.run_ssd(c, orc)
+    for b in (0, 1, 3):
+        d, t0, t1 = _ssd_as_decode(c, b)
+        p = orc.run(d)
+        assert np.array_equal(r["y"][t0:t1], p["y"][0]), b
+        assert np.array_equal(r["states"][b], p["state"][0]), b
+
+
+def pin_ssd_chunking_invariance(orc):
+    """Chunk boundaries change nothing: the same sequences split into chunks
+    of 5, 16 or 64 tokens give the same outputs and final states bit for bit."""
+    from oracle import ssu_oracle
+    outs = [ssu_oracle.run_ssd(_ssd_case(chunk_size=k), orc) for k in (5, 16, 64)]
+    for o in outs[1:]:
+        assert np.array_equal(o["y"], outs[0]["y"]) and np.array_equal(o["states"], outs[0]["states"])
+
+
+def pin_ssd_seq_idx_authority(orc):
+    """seq_idx decides where a sequence opens: relabelling the second
+    sequence's chunks as the first's makes them continue its state (the same
+    as one sequence of both token ranges), whatever last_chunk_indices says."""
+    from oracle import ssu_oracle
+    c = _ssd_case(lengths=(40, 30), initial_states=False)
+    merged = dict(c, seq_idx=np.zeros_like(c["seq_idx"]), last_chunk_indices=c["last_chunk_indices"])
+    one = dict(_ssd_case(lengths=(70,), initial_states=False), x=c["x"], dt=c["dt"], B=c["B"],
+               C=c["C"], z=c["z"], A=c["A"], D=c["D"], dt_bias=c["dt_bias"])
+    r = ssu_oracle.run_ssd(merged, orc)
+    o = ssu_oracle.run_ssd(one, orc)
+    assert np.array_equal(r["y"], o["y"])
+    assert np.array_equal(r["chunk_states"][-1], o["chunk_states"][-1])
+    s = ssu_oracle.run_ssd(c, orc)  # the proper labels reset at the second sequence
+    assert not np.array_equal(s["y"][40:], r["y"][40:])
+
+
+def pin_ssd_dt_limit_zero(orc):
+    """dt_limit = (0, 0) clamps every dt' to 0: the state never moves from its
+    initial value and y = S_init . C + D x, gated (closed form)."""
+    from oracle import ssu_oracle
+    c = _ssd_case(io="f32", state_dtype="f32", dt_limit=(0.0, 0.0))
+    r = ssu_oracle.run_ssd(c, orc)
+    init = np.asarray(c["initial_states"], np.float64)
+    for b in range(len(c["last_chunk_indices"])):
+        assert np.array_equal(r["states"][b], c["initial_states"][b]), b
+    cu = c["cu_seqlens"]
+    G = c["B"].shape[1]
+    H = c["x"].shape[1]
+    for b in range(len(cu) - 1):
+        for t in range(cu[b], cu[b + 1]):
+            for h in range(H):
+                g = h // (H // G)
+                y = init[b, h] @ c["C"][t, g].astype(np.float64) + c["D"][h] * c["x"][t, h]
+                zz = c["z"][t, h].astype(np.float64)
+                y = y * zz / (1 + np.exp(-zz))
+                assert np.allclose(r["y"][t, h], y, rtol=1e-5, atol=1e-5), (b, t, h)
+
+
 ALL = [pin_golden_mate_examples, pin_f16_decode_exhaustive, pin_f16_encode, pin_bf16_roundtrip, pin_softplus,
        pin_dt_zero_keeps_state, pin_b_zero_pure_decay, pin_zero_state_closed_form,
        pin_c_zero_and_z_zero, pin_mtp_equals_chained_calls, pin_unrolled_window,
@@ -926,4 +1043,6 @@ ALL = [pin_golden_mate_examples, pin_f16_decode_exhaustive, pin_f16_encode, pin_
        pin_replay_nonflush_writes_entry_only, pin_replay_zero_checkpoint, pin_replay_disable,
        pin_replay_brute_force, pin_replay_spec_is_chain, pin_replay_spec_rollback,
        pin_replay_spec_fold_boundary, pin_replay_spec_pad_and_disable, pin_replay_spec_brute_force,
-       pin_memmove_matches_snapshot, pin_conv_shift_matches_snapshot]
+       pin_memmove_matches_snapshot, pin_conv_shift_matches_snapshot,
+       pin_ssd_matches_chunked_float64, pin_ssd_equals_decode_chain, pin_ssd_chunking_invariance,
+       pin_ssd_seq_idx_authority, pin_ssd_dt_limit_zero]

@@ -79,6 +79,16 @@ MUTANTS = [
     ("conv_ds_without_bias", "memmove(dst + d * W * elem_size, src + (d * W + bias[r]) * elem_size,",
      "memmove(dst + d * W * elem_size, src + (d * W) * elem_size,"),
     ("conv_ds_as_sd", "if (layout == OR_CONV_SD) {", "if (layout != 7) {"),
+    # SSD prefill
+    ("ssd_never_reset", "const int opens = c == 0 || a->seq_idx[c] != a->seq_idx[c - 1]; /* R27 */",
+     "const int opens = c == 0;"),
+    ("ssd_reset_every_chunk", "const int opens = c == 0 || a->seq_idx[c] != a->seq_idx[c - 1]; /* R27 */",
+     "const int opens = 1;"),
+    ("ssd_no_floor", "if (v < a->dt_lo) /* dt_limit, after softplus */\n                    v = a->dt_lo;", ""),
+    ("ssd_no_ceiling", "if (v > a->dt_hi)\n                    v = a->dt_hi;", ""),
+    ("ssd_decay_without_dt", "const float decay = expf(a->A[h] * v); /* R26 */", "const float decay = expf(a->A[h]);"),
+    ("ssd_init_of_chunk", "load_as_f32(a->init, a->state_dtype, (a->seq_idx[c] * H + h) * tile + e)",
+     "load_as_f32(a->init, a->state_dtype, (0 * H + h) * tile + e)"),
     ("default_dst_is_seq",
      "a->wtab.data ? &a->wtab : (a->rtab.data ? &a->rtab : NULL)", "a->wtab.data ? &a->wtab : NULL"),
     ("flat_write_b_plus_t", "int64_t i = tb->ndim == 1 ? bos + t :", "int64_t i = tb->ndim == 1 ? b + t :"),

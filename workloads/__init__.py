@@ -394,3 +394,50 @@ def conv_shift(seed=9, requests=6144, width=4, inner=8192, dtype=np.float16, lay
 
 BUILDERS["memmove_rows"] = memmove_rows
 BUILDERS["conv_shift"] = conv_shift
+
+
+# ------------------------------------------------------------ SSD prefill
+
+def ssd(seed=10, lengths=(700, 256, 1, 513, 1200), heads=8, dim=64, dstate=128, groups=2,
+        chunk_size=256, io="bf16", state_dtype="f32", dt_dtype="f32", initial_states=True,
+        dt_limit=(0.0, float("inf")), z=True, D=True, softplus=True):
+    """A packed variable-length prefill: sequences of the given lengths,
+    each split from its start into chunks of chunk_size tokens (the last one
+    partial), x / z [T, H, P] and B / C [T, G, N] ~ N(0,1) in the io dtype,
+    dt [T, H] ~ N(0,1) in dt_dtype with the decode layer's dt_bias (softplus
+    on) and A, optional initial states ~ N(0,1) in the state dtype. cu_seqlens,
+    cu_chunk_seqlens, seq_idx and last_chunk_indices follow from the lengths."""
+    rng = np.random.default_rng(seed)
+    lengths = [int(n) for n in lengths]
+    T = sum(lengths)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    chunks, seq, last = [0], [], []
+    for b, n in enumerate(lengths):
+        start = int(cu[b])
+        for off in range(0, max(n, 1), chunk_size):
+            if n == 0:
+                break
+            chunks.append(start + min(off + chunk_size, n))
+            seq.append(b)
+        last.append(len(seq) - 1)
+    c = {"io_dtype": io, "dt_dtype": dt_dtype, "state_dtype": state_dtype,
+         "chunk_size": int(chunk_size), "dt_softplus": bool(softplus), "dt_limit": tuple(dt_limit)}
+    c["x"] = _normal(rng, (T, heads, dim), io)
+    c["dt"] = _normal(rng, (T, heads), dt_dtype)
+    c["A"] = (-np.exp(rng.uniform(0.0, 4.0, heads))).astype(np.float32)
+    c["B"] = _normal(rng, (T, groups, dstate), io)
+    c["C"] = _normal(rng, (T, groups, dstate), io)
+    c["z"] = _normal(rng, (T, heads, dim), io) if z else None
+    c["D"] = rng.standard_normal(heads).astype(np.float32) if D else None
+    u = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), heads))
+    c["dt_bias"] = np.log(np.expm1(u)).astype(np.float32) if softplus else None
+    c["initial_states"] = _normal(rng, (len(lengths), heads, dim, dstate), state_dtype) \
+        if initial_states else None
+    c["cu_seqlens"] = cu
+    c["cu_chunk_seqlens"] = np.asarray(chunks, np.int64)
+    c["seq_idx"] = np.asarray(seq, np.int64)
+    c["last_chunk_indices"] = np.asarray(last, np.int64)
+    return c
+
+
+BUILDERS["ssd"] = ssd
