@@ -17,7 +17,7 @@ Prints ONE JSON line:
              current kernel source, else null
   cpu_baseline  the CPU oracle timed on this host on the same workload
 Options: --config {decode, decode_pad, mtp, varlen, varlen_disable, varlen_nodst, replay,
-replay_spec, spec_snapshots, conv_shift_sd, conv_shift_ds, memcpy_left},
+replay_spec, spec_snapshots, conv_shift_sd, conv_shift_ds, memcpy_left, ssd},
 --no-cpu-baseline, --calib-copy (also runs a plain device copy of the state's
 size, the calibration kernel for the counters).
 """
@@ -38,7 +38,7 @@ METRIC = "SSU decode achieved HBM GB/s (% of peak) and token-head updates/s"
 HBM_PEAK_GBS = 8000.0
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "mamba_selective_state_amd", "csrc", f)
-                  for f in ("ssu_kernels.hip", "ssu_copy.hip", "ssu_internal.h")]
+                  for f in ("ssu_kernels.hip", "ssu_copy.hip", "ssu_ssd.hip", "ssu_internal.h")]
 
 DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 
@@ -76,6 +76,12 @@ def workload(name):
             "%s: 6144 convolution-state shifts (256 sequences x 24 layers), width 4, inner 8192, "
             "fp16 (64 KiB blocks), %s layout, half of them inside one block, bias ~ U{1..3}"
             % (name, "token-major" if layout == "SD" else "dim-major"))
+    if name == "ssd":
+        c = W.ssd_bench()
+        return c, ("ssd: packed variable-length SSD prefill, 8 sequences of U{512..4096} tokens "
+                   "(%d tokens, %d chunks of up to 256), heads 128, dim 64, dstate 128, groups 8, "
+                   "bf16 x/B/C/z, f32 dt and states, initial states"
+                   % (np.shape(c["x"])[0], len(c["seq_idx"])))
     if name == "memcpy_left":
         return W.memmove_rows(rows=4096, row_bytes=32 * 1024, shift=16, direction="left"), (
             "memcpy_left: 4096 rows of 32 KiB each copied onto itself shifted left by 16 bytes "
@@ -195,6 +201,98 @@ def replay_algorithmic_bytes(case):
 
 
 COPY_CONFIGS = ("conv_shift_sd", "conv_shift_ds", "memcpy_left")
+
+
+def ssd_algorithmic(case):
+    """Bytes the prefill must move (inputs read once, y and the returned
+    states written once) and the chunked algorithm's matrix flops: per chunk
+    of L tokens and head, the chunk state 2 L P N, C.B^T over the causal half
+    L (L + 1) N, its product with x L (L + 1) P, and the entering state read
+    out 2 L N P. Returns (bytes, flops)."""
+    T, H, P = np.shape(case["x"])
+    G, N = np.shape(case["B"])[1:]
+    io = DTYPE_BYTES[case["io_dtype"]]
+    sb = DTYPE_BYTES[case["state_dtype"]]
+    batch = len(case["last_chunk_indices"])
+    nbytes = T * H * P * io * (2 + (case.get("z") is not None))          # x, out, z
+    nbytes += T * H * DTYPE_BYTES[case["dt_dtype"]] + 2 * T * G * N * io  # dt, B, C
+    nbytes += batch * H * P * N * sb * (1 + (case.get("initial_states") is not None))
+    cu = np.asarray(case["cu_chunk_seqlens"])
+    flops = 0
+    for L in np.diff(cu):
+        L = int(L)
+        flops += H * (2 * L * P * N + L * (L + 1) * N + L * (L + 1) * P + 2 * L * N * P)
+    return int(nbytes), int(flops)
+
+
+def ssd_bench_run(args, case, desc):
+    import torch
+    import mamba_selective_state_amd as ssu
+    from workloads.device import TORCH, dev as to_dev
+    d = torch.device("cuda", 0)
+    io, sd = case["io_dtype"], case["state_dtype"]
+    x, B, C, z = (to_dev(case[k], io, d) for k in ("x", "B", "C", "z"))
+    dt = to_dev(case["dt"], case["dt_dtype"], d)
+    A, D, bias = (torch.from_numpy(case[k]).to(d) for k in ("A", "D", "dt_bias"))
+    idx = {k: torch.from_numpy(np.asarray(case[k])).to(d)
+           for k in ("cu_seqlens", "cu_chunk_seqlens", "last_chunk_indices", "seq_idx")}
+    init = to_dev(case["initial_states"], sd, d)
+    out = torch.empty_like(x)
+    def step():
+        return ssu.ssd_combined_fwd_varlen(
+            x, dt, A, B, C, case["chunk_size"], idx["cu_seqlens"], idx["cu_chunk_seqlens"],
+            idx["last_chunk_indices"], idx["seq_idx"], out=out, D=D, z=z, dt_bias=bias,
+            dt_softplus=case["dt_softplus"], dt_limit=case["dt_limit"], initial_states=init,
+            state_dtype=TORCH[sd])
+    stream = torch.cuda.current_stream(d)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(d)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize(d)
+    wall = time.perf_counter() - t0
+    event_ms = start.elapsed_time(end) / args.steps
+    if args.calib_copy:
+        src_c = torch.empty((1 << 30) // 4, dtype=torch.float32, device=d).fill_(1.0)
+        dst_c = torch.empty_like(src_c)
+        for _ in range(3):
+            dst_c.copy_(src_c)
+        torch.cuda.synchronize(d)
+    nbytes, flops = ssd_algorithmic(case)
+    tflops = flops / (event_ms * 1e-3) / 1e12
+    result = {
+        "metric": "SSD prefill matrix TFLOP/s (bf16 MFMA) and tokens/s", "value": round(flops * args.steps / wall / 1e12, 3),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": desc, "flops_per_step": flops, "bytes_per_step": nbytes,
+                   "kernels": "ssd_chunk_state_kernel, ssd_state_pass_kernel, ssd_chunk_scan_kernel"},
+        "tokens_per_s": round(np.shape(case["x"])[0] * args.steps / wall, 1),
+        "hbm_gbs_algorithmic": round(nbytes / (event_ms * 1e-3) / 1e9, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": 2500.0, "unit": "TFLOP/s",
+                     "frac": round(tflops / 2500.0, 5), "traffic": traffic_from_counters("ssd"),
+                     "kernel_us": round(event_ms * 1e3, 2),
+                     "note": "the three launches of one call timed together"},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import ssu_oracle
+        import workloads as W
+        heads = [0, 64]
+        sub = W.ssd_heads(case, heads)
+        t1 = time.perf_counter()
+        ssu_oracle.run_ssd(sub)
+        tm = (time.perf_counter() - t1) * np.shape(case["x"])[1] / len(heads)
+        result["cpu_baseline"] = {"value": round(flops / tm / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+                                  "kind": "oracle",
+                                  "sample": "2 of the 128 heads (heads are independent), scaled to all "
+                                            "heads: %.1f s per call; single-threaded token-by-token C oracle"
+                                            % tm}
+    print(json.dumps(result), flush=True)
 
 
 def copy_algorithmic_bytes(case):
@@ -344,6 +442,13 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.config == "ssd":
+        import torch
+        if not torch.cuda.is_available():
+            raise SystemExit("bench.py needs a GPU")
+        case, desc = workload(args.config)
+        ssd_bench_run(args, case, desc)
+        return
     if args.config in COPY_CONFIGS:
         import torch
         if not torch.cuda.is_available():

@@ -99,7 +99,8 @@ enum {
     SSU_OPT_RAND_SEED = 1u << 2,           /* stochastic rounding (not implemented on the MATE page either) */
     SSU_OPT_CACHE_STEPS = 1u << 3,         /* cache_steps != 0 */
     SSU_OPT_ALGORITHM = 1u << 4,           /* algorithm != "auto" */
-    SSU_OPT_BACKEND = 1u << 5              /* backend != "auto" */
+    SSU_OPT_BACKEND = 1u << 5,             /* backend != "auto" */
+    SSU_OPT_SSD_CHECKPOINT = 1u << 6       /* ssu_ssd_prefill: checkpoint_* arguments */
 };
 
 /* Arguments of one update (MATE selective_state_update, same names).
@@ -275,6 +276,55 @@ typedef struct {
  * requests must not write the same block or one that another reads. One
  * kernel on `stream`, asynchronous, allocates nothing. */
 SSU_API ssu_status_t ssu_conv_state_shift(const ssu_conv_shift_args_t *args, void *stream);
+
+/* ---- SSD packed variable-length prefill (MATE docs, "Mamba / SSU",
+ * section "SSD packed prefill" and the API entry of ssd_combined_fwd_varlen):
+ * the decode step's recurrence run over every token of a packed batch,
+ * chunk by chunk, from each sequence's initial state (or zeros):
+ *   dt' = clamp(softplus(dt + dt_bias) or dt + dt_bias, dt_limit)
+ *   S   = S exp(dt' A[h]) + dt' x B^T,   y = (S . C + D x) silu(z)
+ * Chunk c covers tokens cu_chunk_seqlens[c] .. cu_chunk_seqlens[c+1]-1 (the
+ * only authority for that mapping; at most chunk_size tokens); it opens a
+ * sequence when c = 0 or seq_idx[c] != seq_idx[c-1], and then starts from
+ * initial_states[seq_idx[c]]. The state is carried in fp32; `states`
+ * receives, in its dtype, the state after chunk last_chunk_indices[b] for
+ * every sequence b, or the state after every chunk when
+ * return_intermediate_states is set. The products run on bf16 / f16 matrix
+ * cores (the x dtype) with fp32 accumulation.
+ * Supported: head dim 64, dstate 64 or 128, chunk_size <= 256, x bf16 or f16,
+ * states f32 / f16 / bf16. A chunk whose cu_chunk_seqlens entries are out of
+ * range or longer than chunk_size is taken as empty (checked on the device). */
+typedef struct {
+    ssu_tensor_t x;                  /* [tokens, heads, dim], dim contiguous, rows 16-byte aligned */
+    ssu_tensor_t dt;                 /* [tokens, heads], f32 or the x dtype */
+    ssu_tensor_t A;                  /* [heads] f32 */
+    ssu_tensor_t B, C;               /* [tokens, groups, dstate], x dtype, rows 16-byte aligned */
+    ssu_tensor_t D;                  /* [heads] f32, or absent */
+    ssu_tensor_t z;                  /* like x (dim contiguous), or absent */
+    ssu_tensor_t dt_bias;            /* [heads] f32, or absent */
+    ssu_tensor_t cu_seqlens;         /* [batch + 1] i32 / i64, or absent (not read) */
+    ssu_tensor_t cu_chunk_seqlens;   /* [nchunks + 1] i32 / i64 (device) */
+    ssu_tensor_t last_chunk_indices; /* [batch] i32 / i64 (device) */
+    ssu_tensor_t seq_idx;            /* [nchunks] i32 / i64 (device) */
+    ssu_tensor_t initial_states;     /* [batch, heads, dim, dstate] contiguous, the state dtype, or absent */
+    ssu_tensor_t out;                /* like x (dim contiguous): y, written */
+    ssu_tensor_t states;             /* [batch or nchunks, heads, dim, dstate] contiguous: written */
+    int64_t chunk_size;
+    int32_t dt_softplus;
+    int32_t return_intermediate_states;
+    float dt_limit_lo, dt_limit_hi;  /* (0, +inf) by default */
+    uint32_t unsupported;            /* SSU_OPT_SSD_CHECKPOINT: the checkpoint_* arguments */
+} ssu_ssd_args_t;
+
+/* Bytes of device workspace ssu_ssd_prefill needs for `nchunks` chunks. */
+SSU_API int64_t ssu_ssd_workspace_bytes(int64_t heads, int64_t dim, int64_t dstate, int64_t nchunks);
+
+/* Three kernels on `stream` (none when there are no chunks); asynchronous;
+ * allocates nothing: the caller passes `workspace` (DEVICE memory, 256-byte
+ * aligned, at least ssu_ssd_workspace_bytes) and keeps it for the call's
+ * duration. Errors as for ssu_update. */
+SSU_API ssu_status_t ssu_ssd_prefill(const ssu_ssd_args_t *args, void *workspace, int64_t workspace_bytes,
+                                     void *stream);
 
 /* Message of the last failing call on this thread ("" if none). The pointer
  * stays valid until the next call on the same thread. */

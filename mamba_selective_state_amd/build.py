@@ -7,6 +7,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssu.so")
 SOURCES = [os.path.join(CSRC, "ssu_kernels.hip"), os.path.join(CSRC, "ssu_copy.hip"),
+           os.path.join(CSRC, "ssu_ssd.hip"),
            os.path.join(CSRC, "ssu_api.cpp")]
 HEADERS = [os.path.join(CSRC, "ssu_internal.h"),
            os.path.join(os.path.dirname(HERE), "include", "ssu.h")]

@@ -583,6 +583,178 @@ ssu_status_t ssu_batch_memcpy(const ssu_tensor_t *src_ptrs, const ssu_tensor_t *
     return SSU_OK;
 }
 
+// ---- SSD packed prefill
+
+static int64_t ssd_ws_parts(int64_t H, int64_t P, int64_t N, int64_t nchunks, int64_t *rows_bytes) {
+    auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
+    *rows_bytes = up(nchunks * H * ssu::kSsdMaxChunk * 4);
+    return 2 * *rows_bytes + up(nchunks * H * P * N * 4);
+}
+
+int64_t ssu_ssd_workspace_bytes(int64_t heads, int64_t dim, int64_t dstate, int64_t nchunks) {
+    if (heads < 0 || dim < 0 || dstate < 0 || nchunks < 0)
+        return -1;
+    int64_t rows;
+    return ssd_ws_parts(heads, dim, dstate, nchunks, &rows);
+}
+
+// A [rows, a, b] tensor with unit stride on the last axis; returns its row
+// and second-axis strides.
+static ssu_status_t ssd_rows(const char *name, const ssu_tensor_t &t, int64_t rows, int64_t a, int64_t b,
+                             int dtype, bool vec16, int64_t *st, int64_t *s1) {
+    if (t.ndim != 3 || t.size[0] != rows || t.size[1] != a || t.size[2] != b)
+        return fail(SSU_ERR_VALUE, "%s must be [%lld, %lld, %lld]", name, (long long)rows, (long long)a,
+                    (long long)b);
+    if (t.dtype != dtype)
+        return fail(SSU_ERR_VALUE, "%s must have the x dtype", name);
+    if (t.stride[2] != 1 || t.stride[0] < 0 || t.stride[1] < 0)
+        return fail(SSU_ERR_VALUE, "%s must have unit stride on its last axis", name);
+    if (vec16 && (!aligned(t.data, 16) || t.stride[0] % 8 || t.stride[1] % 8))
+        return fail(SSU_ERR_VALUE, "%s rows must start on 16-byte boundaries", name);
+    if (!aligned(t.data, 2))
+        return fail(SSU_ERR_VALUE, "%s is misaligned", name);
+    *st = t.stride[0];
+    *s1 = t.stride[1];
+    return SSU_OK;
+}
+
+static bool contiguous4(const ssu_tensor_t &t) {
+    return t.ndim == 4 && t.stride[3] == 1 && t.stride[2] == t.size[3] &&
+           t.stride[1] == t.size[2] * t.size[3] && t.stride[0] == t.size[1] * t.size[2] * t.size[3];
+}
+
+ssu_status_t ssu_ssd_prefill(const ssu_ssd_args_t *a, void *workspace, int64_t workspace_bytes, void *stream) {
+    if (!a)
+        return fail(SSU_ERR_VALUE, "ssu_ssd_prefill: args is NULL");
+    if (a->unsupported & SSU_OPT_SSD_CHECKPOINT)
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "checkpoint_token_indices / checkpoint_state_slots / "
+                                             "checkpoint_states are not implemented");
+    if (a->unsupported & ~static_cast<uint32_t>(SSU_OPT_SSD_CHECKPOINT))
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "unknown option bits");
+    const ssu_tensor_t &x = a->x;
+    if (!present(x) || x.ndim != 3)
+        return fail(SSU_ERR_VALUE, "x must be [tokens, heads, dim]");
+    if (x.dtype != SSU_BF16 && x.dtype != SSU_F16)
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "SSD prefill takes bf16 or f16 x, got %s", dtype_str(x.dtype));
+    const int64_t T = x.size[0], H = x.size[1], P = x.size[2];
+    if (P != ssu::kSsdDim)
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "SSD prefill supports head dim %d, got %lld", ssu::kSsdDim,
+                    (long long)P);
+    ssu::SsdParams sp;
+    memset(&sp, 0, sizeof sp);
+    ssu_status_t s;
+    if ((s = ssd_rows("x", x, T, H, P, x.dtype, true, &sp.x_st, &sp.x_sh)) != SSU_OK)
+        return s;
+    if (!present(a->B) || !present(a->C) || a->B.ndim != 3)
+        return fail(SSU_ERR_VALUE, "B and C [tokens, groups, dstate] are required");
+    const int64_t G = a->B.size[1], N = a->B.size[2];
+    if (G <= 0 || H % G)
+        return fail(SSU_ERR_VALUE, "heads (%lld) must be divisible by groups (%lld)", (long long)H, (long long)G);
+    if (N != 64 && N != 128)
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "SSD prefill supports dstate 64 or 128, got %lld", (long long)N);
+    if ((s = ssd_rows("B", a->B, T, G, N, x.dtype, true, &sp.B_st, &sp.B_sg)) != SSU_OK)
+        return s;
+    if ((s = ssd_rows("C", a->C, T, G, N, x.dtype, true, &sp.C_st, &sp.C_sg)) != SSU_OK)
+        return s;
+    if (present(a->z) && (s = ssd_rows("z", a->z, T, H, P, x.dtype, false, &sp.z_st, &sp.z_sh)) != SSU_OK)
+        return s;
+    if (!present(a->out))
+        return fail(SSU_ERR_VALUE, "out is required");
+    if ((s = ssd_rows("out", a->out, T, H, P, x.dtype, false, &sp.out_st, &sp.out_sh)) != SSU_OK)
+        return s;
+    const ssu_tensor_t &dt = a->dt;
+    if (!present(dt) || dt.ndim != 2 || dt.size[0] != T || dt.size[1] != H || (dt.dtype != SSU_F32 && dt.dtype != x.dtype))
+        return fail(SSU_ERR_VALUE, "dt must be [tokens, heads], f32 or the x dtype");
+    if (dt.stride[0] < 0 || dt.stride[1] < 0 || !aligned(dt.data, elem_bytes(dt.dtype)))
+        return fail(SSU_ERR_VALUE, "dt: bad stride or alignment");
+    sp.dt_st = dt.stride[0];
+    sp.dt_sh = dt.stride[1];
+    if ((s = head_vector("A", a->A, H, true, &sp.A, &sp.A_sh)) != SSU_OK)
+        return s;
+    if ((s = head_vector("D", a->D, H, false, &sp.D, &sp.D_sh)) != SSU_OK)
+        return s;
+    if ((s = head_vector("dt_bias", a->dt_bias, H, false, &sp.dt_bias, &sp.bias_sh)) != SSU_OK)
+        return s;
+    if (a->chunk_size < 1 || a->chunk_size > ssu::kSsdMaxChunk)
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "chunk_size must be 1..%d, got %lld", ssu::kSsdMaxChunk,
+                    (long long)a->chunk_size);
+    if (!(a->dt_limit_lo <= a->dt_limit_hi))
+        return fail(SSU_ERR_VALUE, "dt_limit must be (lo, hi) with lo <= hi");
+    // chunk metadata
+    if (!present(a->cu_chunk_seqlens) || a->cu_chunk_seqlens.ndim != 1 || a->cu_chunk_seqlens.size[0] < 1)
+        return fail(SSU_ERR_VALUE, "cu_chunk_seqlens must be 1-D [nchunks + 1]");
+    const int64_t nchunks = a->cu_chunk_seqlens.size[0] - 1;
+    bool i64 = false;
+    if ((s = meta_vector("cu_chunk_seqlens", a->cu_chunk_seqlens, nchunks + 1, &sp.cu_chunk, &sp.cu_chunk_s, &i64)) != SSU_OK)
+        return s;
+    sp.cu_chunk_i64 = i64;
+    if (!present(a->seq_idx))
+        return fail(SSU_ERR_VALUE, "seq_idx is required");
+    if ((s = meta_vector("seq_idx", a->seq_idx, nchunks, &sp.seq_idx, &sp.seq_idx_s, &i64)) != SSU_OK)
+        return s;
+    sp.seq_idx_i64 = i64;
+    if (!present(a->last_chunk_indices) || a->last_chunk_indices.ndim != 1)
+        return fail(SSU_ERR_VALUE, "last_chunk_indices must be 1-D [batch]");
+    const int64_t batch = a->last_chunk_indices.size[0];
+    if ((s = meta_vector("last_chunk_indices", a->last_chunk_indices, batch, &sp.last_chunk, &sp.last_chunk_s, &i64)) != SSU_OK)
+        return s;
+    sp.last_chunk_i64 = i64;
+    if (present(a->cu_seqlens) && (a->cu_seqlens.ndim != 1 || a->cu_seqlens.size[0] != batch + 1))
+        return fail(SSU_ERR_VALUE, "cu_seqlens must be 1-D [batch + 1]");
+    // states
+    const ssu_tensor_t &st = a->states;
+    const int64_t srows = a->return_intermediate_states ? nchunks : batch;
+    if (!present(st) || !contiguous4(st) || st.size[0] != srows || st.size[1] != H || st.size[2] != P ||
+        st.size[3] != N || !is_float(st.dtype) || !aligned(st.data, 16))
+        return fail(SSU_ERR_VALUE, "states must be contiguous [%s, heads, dim, dstate] (f32/f16/bf16)",
+                    a->return_intermediate_states ? "nchunks" : "batch");
+    if (present(a->initial_states)) {
+        const ssu_tensor_t &in = a->initial_states;
+        if (!contiguous4(in) || in.size[0] != batch || in.size[1] != H || in.size[2] != P || in.size[3] != N ||
+            in.dtype != st.dtype)
+            return fail(SSU_ERR_VALUE, "initial_states must be contiguous [batch, heads, dim, dstate] in the states dtype");
+        sp.init = in.data;
+    }
+    if (nchunks == 0 || T == 0 || H == 0)
+        return g_error.clear(), SSU_OK;
+    if (!a->return_intermediate_states && nchunks > 16384)
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "more than 16384 chunks");
+    if (nchunks * H > INT32_MAX)
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "grid too large");
+    int64_t rows_bytes;
+    const int64_t need = ssd_ws_parts(H, P, N, nchunks, &rows_bytes);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return fail(SSU_ERR_VALUE, "workspace must be 256-byte aligned with at least %lld bytes", (long long)need);
+    char *ws = static_cast<char *>(workspace);
+    sp.ws_dtp = reinterpret_cast<float *>(ws);
+    sp.ws_acum = reinterpret_cast<float *>(ws + rows_bytes);
+    sp.ws_state = reinterpret_cast<float *>(ws + 2 * rows_bytes);
+    sp.x = x.data;
+    sp.dt = dt.data;
+    sp.B = a->B.data;
+    sp.C = a->C.data;
+    sp.z = a->z.data;
+    sp.out = const_cast<void *>(a->out.data);
+    sp.states = const_cast<void *>(st.data);
+    sp.T = T;
+    sp.H = H;
+    sp.N = N;
+    sp.nchunks = nchunks;
+    sp.batch = batch;
+    sp.chunk_size = a->chunk_size;
+    sp.hpg = static_cast<int32_t>(H / G);
+    sp.dt_f32 = dt.dtype == SSU_F32;
+    sp.softplus = a->dt_softplus != 0;
+    sp.intermediate = a->return_intermediate_states != 0;
+    sp.dt_lo = a->dt_limit_lo;
+    sp.dt_hi = a->dt_limit_hi;
+    const int e = ssu::launch_ssd(sp, x.dtype, st.dtype, stream);
+    if (e != 0)
+        return fail(SSU_ERR_HIP, "kernel launch failed: %s", ssu::hip_error_string(e));
+    g_error.clear();
+    return SSU_OK;
+}
+
 ssu_status_t ssu_conv_state_shift(const ssu_conv_shift_args_t *a, void *stream) {
     if (!a)
         return fail(SSU_ERR_VALUE, "ssu_conv_state_shift: args is NULL");

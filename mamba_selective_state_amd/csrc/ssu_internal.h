@@ -175,6 +175,28 @@ struct ConvParams {
     int32_t tiles;  // workgroups per request
 };
 int launch_batch_memcpy(const CopyParams &cp, unsigned grid, void *stream);
+
+// SSD packed prefill (ssu_ssd.hip): head dim, largest chunk, arguments
+// (strides in elements; the workspace holds dt' and the decay cumsum per
+// [chunk, head, token] and one fp32 state per [chunk, head]).
+constexpr int kSsdDim = 64;
+constexpr int kSsdMaxChunk = 256;
+struct SsdParams {
+    const void *x, *dt, *B, *C, *z;
+    void *out, *states;
+    const void *init;
+    const float *A, *D, *dt_bias;
+    const void *cu_chunk, *seq_idx, *last_chunk;
+    float *ws_dtp, *ws_acum, *ws_state;
+    int64_t T, H, N, nchunks, batch, chunk_size;
+    int64_t x_st, x_sh, dt_st, dt_sh, B_st, B_sg, C_st, C_sg, z_st, z_sh, out_st, out_sh;
+    int64_t A_sh, D_sh, bias_sh;
+    int64_t cu_chunk_s, seq_idx_s, last_chunk_s;
+    int32_t cu_chunk_i64, seq_idx_i64, last_chunk_i64;
+    int32_t hpg, dt_f32, softplus, intermediate;
+    float dt_lo, dt_hi;
+};
+int launch_ssd(const SsdParams &sp, int io_dtype, int state_dtype, void *stream);
 int launch_conv_shift(const ConvParams &cv, bool dim_major, unsigned grid, void *stream);
 
 bool find_replay_kernel(int state_dtype, int io_dtype, int dstate, bool spec, KernelRef *out);

@@ -51,6 +51,18 @@ class SsuConvShiftArgs(ctypes.Structure):
                 ("dst_block", SsuTensor), ("bias", SsuTensor)]
 
 
+class SsuSsdArgs(ctypes.Structure):
+    _fields_ = [(n, SsuTensor) for n in
+                ("x", "dt", "A", "B", "C", "D", "z", "dt_bias", "cu_seqlens", "cu_chunk_seqlens",
+                 "last_chunk_indices", "seq_idx", "initial_states", "out", "states")] + [
+        ("chunk_size", ctypes.c_int64), ("dt_softplus", ctypes.c_int32),
+        ("return_intermediate_states", ctypes.c_int32), ("dt_limit_lo", ctypes.c_float),
+        ("dt_limit_hi", ctypes.c_float), ("unsupported", ctypes.c_uint32)]
+
+
+OPT_SSD_CHECKPOINT = 64
+
+
 class SsuPlanDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("state_dtype", "io_dtype", "dt_dtype", "slot_dtype", "meta_dtype", "heads",
@@ -64,7 +76,7 @@ class SsuPlanInfo(ctypes.Structure):
 
 
 EXPORTS = ("ssu_plan", "ssu_update", "ssu_replay_update", "ssu_replay_spec_update",
-           "ssu_batch_memcpy", "ssu_conv_state_shift",
+           "ssu_batch_memcpy", "ssu_conv_state_shift", "ssu_ssd_workspace_bytes", "ssu_ssd_prefill",
            "ssu_last_error", "ssu_abi_version")
 
 
@@ -88,6 +100,11 @@ def load_library(path=None):
     lib.ssu_batch_memcpy.restype = ctypes.c_int
     lib.ssu_conv_state_shift.argtypes = [ctypes.POINTER(SsuConvShiftArgs), ctypes.c_void_p]
     lib.ssu_conv_state_shift.restype = ctypes.c_int
+    lib.ssu_ssd_workspace_bytes.argtypes = [ctypes.c_int64] * 4
+    lib.ssu_ssd_workspace_bytes.restype = ctypes.c_int64
+    lib.ssu_ssd_prefill.argtypes = [ctypes.POINTER(SsuSsdArgs), ctypes.c_void_p, ctypes.c_int64,
+                                    ctypes.c_void_p]
+    lib.ssu_ssd_prefill.restype = ctypes.c_int
     lib.ssu_last_error.argtypes = []
     lib.ssu_last_error.restype = ctypes.c_char_p
     lib.ssu_abi_version.argtypes = []
@@ -365,3 +382,71 @@ def conv_state_shift(state, src_block, dst_block, bias, layout="SD"):
     for layout "SD" (token-major) or [blocks, inner, W] for "DS"."""
     ssu_conv_state_shift(make_conv_shift_args(state, src_block, dst_block, bias, layout),
                          torch.cuda.current_stream(state.device).cuda_stream)
+
+
+# ---------------------------------------------------------------- SSD prefill
+
+_ssd_workspaces = {}
+
+
+def ssu_ssd_workspace_bytes(heads, dim, dstate, nchunks):
+    return _lib.ssu_ssd_workspace_bytes(heads, dim, dstate, nchunks)
+
+
+def ssu_ssd_prefill(args, workspace, workspace_bytes, stream=None):
+    """Enqueue an SSD prefill (include/ssu.h ssu_ssd_prefill)."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    st = _lib.ssu_ssd_prefill(ctypes.byref(args), ctypes.c_void_p(workspace), int(workspace_bytes),
+                              ctypes.c_void_p(stream))
+    if st != OK:
+        _raise(st, "ssu_ssd_prefill")
+
+
+def ssd_workspace(device, nbytes):
+    """The cached workspace of `device`, grown to at least `nbytes` (a call
+    of an already seen size allocates nothing)."""
+    ws = _ssd_workspaces.get(device)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _ssd_workspaces[device] = ws
+    return ws
+
+
+def ssd_combined_fwd_varlen(x, dt, A, B, C, chunk_size, cu_seqlens, cu_chunk_seqlens,
+                            last_chunk_indices, seq_idx, out=None, D=None, z=None, dt_bias=None,
+                            dt_softplus=False, dt_limit=(0.0, float("inf")), initial_states=None,
+                            return_intermediate_states=False, state_dtype=None,
+                            checkpoint_token_indices=None, checkpoint_state_slots=None,
+                            checkpoint_states=None):
+    """Packed variable-length SSD prefill (MATE docs, "SSD packed prefill"):
+    x [tokens, heads, dim], dt [tokens, heads]; writes y into `out` (allocated
+    when None) and returns the states after each sequence's last chunk
+    [batch, heads, dim, dstate] (or after every chunk with
+    return_intermediate_states), in state_dtype (default: initial_states'
+    dtype, else C's)."""
+    dev = x.device
+    if state_dtype is None:
+        state_dtype = initial_states.dtype if initial_states is not None else C.dtype
+    nchunks = int(cu_chunk_seqlens.shape[0]) - 1
+    rows = nchunks if return_intermediate_states else int(last_chunk_indices.shape[0])
+    states = torch.empty((rows, x.shape[1], x.shape[2], B.shape[2]), dtype=state_dtype, device=dev)
+    if out is None:
+        out = torch.empty_like(x)
+    a = SsuSsdArgs()
+    for k, v in (("x", x), ("dt", dt), ("A", A), ("B", B), ("C", C), ("D", D), ("z", z),
+                 ("dt_bias", dt_bias), ("cu_seqlens", cu_seqlens),
+                 ("cu_chunk_seqlens", cu_chunk_seqlens), ("last_chunk_indices", last_chunk_indices),
+                 ("seq_idx", seq_idx), ("initial_states", initial_states), ("out", out),
+                 ("states", states)):
+        setattr(a, k, tensor_desc(v, dev))
+    a.chunk_size = int(chunk_size)
+    a.dt_softplus = int(bool(dt_softplus))
+    a.return_intermediate_states = int(bool(return_intermediate_states))
+    a.dt_limit_lo, a.dt_limit_hi = float(dt_limit[0]), float(dt_limit[1])
+    if any(v is not None for v in (checkpoint_token_indices, checkpoint_state_slots, checkpoint_states)):
+        a.unsupported |= OPT_SSD_CHECKPOINT
+    nbytes = ssu_ssd_workspace_bytes(x.shape[1], x.shape[2], B.shape[2], max(nchunks, 0))
+    ws = ssd_workspace(dev, nbytes)
+    ssu_ssd_prefill(a, ws.data_ptr(), ws.numel(), torch.cuda.current_stream(dev).cuda_stream)
+    return states

@@ -40,7 +40,8 @@ def test_struct_layout_matches_header(tmp_path):
     structs = {"ssu_tensor_t": S.SsuTensor, "ssu_args_t": S.SsuArgs,
                "ssu_plan_desc_t": S.SsuPlanDesc, "ssu_plan_info_t": S.SsuPlanInfo,
                "ssu_replay_args_t": S.SsuReplayArgs,
-               "ssu_conv_shift_args_t": S.SsuConvShiftArgs}
+               "ssu_conv_shift_args_t": S.SsuConvShiftArgs,
+               "ssu_ssd_args_t": S.SsuSsdArgs}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ssu.h"', "int main(void) {"]
     for cname, cls in structs.items():
         lines.append('printf("%s SIZEOF %%zu\\n", sizeof(%s));' % (cname, cname))

@@ -1,0 +1,112 @@
+"""SSD packed variable-length prefill on the GPU (ssu_ssd_prefill) against the
+CPU oracle (MATE docs, "Mamba / SSU", section "SSD packed prefill").
+
+Tolerance: the products run on bf16 / f16 matrix cores, so every operand
+that is scaled before a product (w_t B_t in the chunk states, the masked
+C.B^T in the scan, the entering state read out by C) is rounded to the x
+dtype: 2^-9 relative per operand, summed over at most chunk_size + dstate
+terms of random sign. y and the returned states are compared at
+3e-2 x max|ref| (the 16-bit tolerance of the decode path with headroom for
+the extra operand rounding), on every element.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gpu_harness as G
+import workloads as W
+from oracle import ssu_oracle
+
+pytestmark = pytest.mark.gpu
+TOL = 3e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    torch.cuda.init()
+
+
+def run_gpu_ssd(c, intermediate=False):
+    dev = "cuda:0"
+    io, sd = c["io_dtype"], c["state_dtype"]
+    d = {k: G.dev(c[k], io, dev) for k in ("x", "B", "C")}
+    d["z"] = None if c.get("z") is None else G.dev(c["z"], io, dev)
+    d["dt"] = G.dev(c["dt"], c["dt_dtype"], dev)
+    idx = {k: torch.from_numpy(np.asarray(c[k])).to(dev)
+           for k in ("cu_seqlens", "cu_chunk_seqlens", "last_chunk_indices", "seq_idx")}
+    init = None if c.get("initial_states") is None else G.dev(c["initial_states"], sd, dev)
+    out = torch.full(np.shape(c["x"]), float("nan"), dtype=G.TORCH[io], device=dev)
+    states = G.ssu.ssd_combined_fwd_varlen(
+        d["x"], d["dt"], torch.from_numpy(c["A"]).to(dev), d["B"], d["C"], c["chunk_size"],
+        idx["cu_seqlens"], idx["cu_chunk_seqlens"], idx["last_chunk_indices"], idx["seq_idx"],
+        out=out, D=None if c.get("D") is None else torch.from_numpy(c["D"]).to(dev), z=d["z"],
+        dt_bias=None if c.get("dt_bias") is None else torch.from_numpy(c["dt_bias"]).to(dev),
+        dt_softplus=c["dt_softplus"], dt_limit=c["dt_limit"], initial_states=init,
+        return_intermediate_states=intermediate, state_dtype=G.TORCH[sd])
+    torch.cuda.synchronize()
+    return G.host(out, io), G.host(states, sd)
+
+
+def check_ssd(c, name, intermediate=False, heads=None):
+    """GPU against the oracle; with `heads`, the oracle runs on those heads
+    only (they are independent) and the GPU's full result is sliced."""
+    ref = ssu_oracle.run_ssd(c if heads is None else W.ssd_heads(c, heads))
+    G.say("[gpu] %s: launching" % name)
+    y, st = run_gpu_ssd(c, intermediate)
+    if heads is not None:
+        y, st = y[:, heads], st[:, heads]
+    io, sd = c["io_dtype"], c["state_dtype"]
+    gy, ry = G.brute64.to_f64(y, io), G.brute64.to_f64(ref["y"], io)
+    assert not np.isnan(gy).any(), "%s: a row of y was not written" % name
+    ey = float(np.abs(gy - ry).max())
+    assert ey <= TOL * np.abs(ry).max(), "%s: y error %g (max |ref| %g)" % (name, ey, np.abs(ry).max())
+    want = ref["chunk_states"] if intermediate else ref["states"]
+    gs, rs = G.brute64.to_f64(st, sd), G.brute64.to_f64(want, sd)
+    es = float(np.abs(gs - rs).max())
+    assert es <= TOL * np.abs(rs).max(), "%s: state error %g (max |ref| %g)" % (name, es, np.abs(rs).max())
+    G.say("[gpu] %s: ok y %.3g state %.3g" % (name, ey / np.abs(ry).max(), es / np.abs(rs).max()))
+
+
+CASES = [
+    # (io, state, dstate, chunk_size, lengths, initial states)
+    ("bf16", "f32", 128, 256, (700, 256, 1, 513, 1200), True),
+    ("bf16", "bf16", 128, 64, (70, 16, 1, 33, 300), True),
+    ("f16", "f32", 64, 128, (129, 128, 127, 5), False),
+    ("bf16", "f16", 64, 256, (1000,), True),
+    ("f16", "f16", 128, 32, (31, 64, 1, 2), True),
+]
+
+
+@pytest.mark.parametrize("io,sd,N,L,lengths,init", CASES,
+                         ids=["%s-%s-n%d-L%d-%dseq" % (a, b, c, d, len(e)) for a, b, c, d, e, f in CASES])
+def test_ssd_prefill(io, sd, N, L, lengths, init):
+    c = W.ssd(seed=N + L, lengths=lengths, heads=8, dim=64, dstate=N, groups=2, chunk_size=L, io=io,
+              state_dtype=sd, initial_states=init)
+    check_ssd(c, "ssd %s %s n%d L%d" % (io, sd, N, L))
+
+
+def test_ssd_intermediate_states_and_options():
+    c = W.ssd(seed=3, lengths=(300, 40, 260), heads=8, dim=64, dstate=128, groups=1, chunk_size=128,
+              io="bf16", state_dtype="f32", z=False, D=False, dt_dtype="bf16")
+    check_ssd(c, "ssd intermediate states", intermediate=True)
+    c = W.ssd(seed=4, lengths=(90, 200), heads=4, dim=64, dstate=64, groups=4, chunk_size=64,
+              io="bf16", state_dtype="f32", softplus=False, dt_limit=(0.0, 0.05))
+    check_ssd(c, "ssd no softplus, dt_limit (0, 0.05)")
+
+
+def test_ssd_seq_idx_authority():
+    """seq_idx decides openings: relabelling the second sequence's chunks
+    as the first's continues its state on the GPU exactly as in the oracle."""
+    c = W.ssd(seed=5, lengths=(100, 80), heads=8, dim=64, dstate=128, groups=2, chunk_size=64,
+              io="bf16", state_dtype="f32", initial_states=False)
+    c["seq_idx"] = np.zeros_like(c["seq_idx"])
+    check_ssd(c, "ssd seq_idx relabelled")
+
+
+def test_ssd_full_workload():
+    """The benchmark's prefill workload at full size, every token and
+    sequence, sampled over heads (the oracle runs on 3 of the 128)."""
+    c = W.ssd_bench()
+    check_ssd(c, "ssd bench workload", heads=[0, 77, 127])

@@ -441,3 +441,40 @@ def ssd(seed=10, lengths=(700, 256, 1, 513, 1200), heads=8, dim=64, dstate=128, 
 
 
 BUILDERS["ssd"] = ssd
+
+
+def ssd_bench(seed=11, nseq=8, heads=128, dim=64, dstate=128, groups=8, chunk_size=256,
+              io="bf16", state_dtype="f32"):
+    """The prefill benchmark: nseq sequences of lengths ~ U{512..4096} (a
+    variable-length prefill batch of the decode workload's layer), chunk
+    size 256, initial states (prefix-cached continuations)."""
+    rng = np.random.default_rng(seed)
+    lengths = tuple(int(v) for v in rng.integers(512, 4097, nseq))
+    return ssd(seed=seed + 1, lengths=lengths, heads=heads, dim=dim, dstate=dstate, groups=groups,
+               chunk_size=chunk_size, io=io, state_dtype=state_dtype, initial_states=True)
+
+
+def ssd_heads(case, heads):
+    """The prefill case restricted to the given heads (heads are independent
+    in the recurrence): each kept head gets its own group, the one it reads
+    in the full case."""
+    heads = np.asarray(heads)
+    H = np.shape(case["x"])[1]
+    G = np.shape(case["B"])[1]
+    groups = heads // (H // G)
+    sub = dict(case)
+    sub["x"] = np.ascontiguousarray(np.asarray(case["x"])[:, heads])
+    sub["dt"] = np.ascontiguousarray(np.asarray(case["dt"])[:, heads])
+    if case.get("z") is not None:
+        sub["z"] = np.ascontiguousarray(np.asarray(case["z"])[:, heads])
+    for k in ("A", "D", "dt_bias"):
+        if case.get(k) is not None:
+            sub[k] = np.ascontiguousarray(np.asarray(case[k])[heads])
+    for k in ("B", "C"):
+        sub[k] = np.ascontiguousarray(np.asarray(case[k])[:, groups])
+    if case.get("initial_states") is not None:
+        sub["initial_states"] = np.ascontiguousarray(np.asarray(case["initial_states"])[:, heads])
+    return sub
+
+
+BUILDERS["ssd_bench"] = ssd_bench
