@@ -472,6 +472,89 @@ int oracle_ssu(const oracle_args *a, char *err, int errlen)
     return 0;
 }
 
+/* ---- MXFP8 (E4M3) block format: the low-precision read copy
+ *
+ * ReplaySSM article, section "数据与边界" (and the low-precision paragraph
+ * after it): output-only steps can read a low-precision copy of the
+ * checkpoint while the recurrence stays high precision; only the fold reads
+ * and writes the high-precision state, and rewrites the copy. The pages use
+ * NVFP4 on NVIDIA parts; on this hardware the copy is the OCP Microscaling
+ * (MX) v1.0 format MXFP8: blocks of 32 consecutive dstate elements sharing
+ * a power-of-two scale (E8M0) with elements in FP8 E4M3 (1 sign, 4 exponent
+ * bits with bias 7, 3 mantissa bits; no infinities; 0x7F / 0xFF are NaN;
+ * largest magnitude 448; subnormals m x 2^-9).
+ *
+ * Readings:
+ *  R30 block scale exponent = floor(log2(max |x|)) - 8 (8 = the exponent of
+ *      E4M3's largest power of two, so the largest element lands in
+ *      [256, 512)), clamped to [-126, 127]; a block of zeros gets -126; the
+ *      scale byte is exponent + 127;
+ *  R31 elements: x / 2^exponent (exact) rounded to nearest, ties to even, in
+ *      E4M3; magnitudes above 448 saturate to 448 (the MX rule for FP8
+ *      element types); decoding multiplies the E4M3 value by 2^exponent.
+ */
+float oracle_e4m3_decode(uint8_t b)
+{
+    const int s = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    if (e == 15 && m == 7)
+        return NAN;
+    const float mag = e == 0 ? ldexpf((float)m, -9) : ldexpf(1.0f + (float)m / 8.0f, e - 7);
+    return s ? -mag : mag;
+}
+
+uint8_t oracle_e4m3_encode(float v)
+{
+    if (isnan(v))
+        return 0x7F;
+    const uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    const float a = fabsf(v);
+    if (a >= 448.0f)
+        return sign | 0x7E; /* R31: saturate */
+    if (a < ldexpf(1.0f, -6)) {
+        /* subnormal range: multiples of 2^-9 (q = 8 is the smallest normal) */
+        const float q = nearbyintf(ldexpf(a, 9));
+        return sign | (uint8_t)q;
+    }
+    int ex;
+    frexpf(a, &ex); /* a = f 2^ex, f in [0.5, 1) */
+    int e = ex - 1; /* floor(log2 a), -6 .. 8 */
+    float q = nearbyintf((ldexpf(a, -e) - 1.0f) * 8.0f); /* 0 .. 8 */
+    if (q == 8.0f) {
+        q = 0.0f;
+        e = e + 1;
+    }
+    if (e > 8 || (e == 8 && q == 7.0f))
+        return sign | 0x7E; /* rounded past 448 */
+    return sign | (uint8_t)(((e + 7) << 3) | (int)q);
+}
+
+/* one block of 32 values -> 32 codes and the scale byte */
+void oracle_mx8_block(const float *x, uint8_t *codes, uint8_t *scale)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < 32; i++)
+        if (fabsf(x[i]) > amax)
+            amax = fabsf(x[i]);
+    int k = -126;
+    if (amax > 0.0f) {
+        int ex;
+        frexpf(amax, &ex);
+        k = (ex - 1) - 8; /* R30 */
+        if (k < -126)
+            k = -126;
+        if (k > 127)
+            k = 127;
+    }
+    *scale = (uint8_t)(k + 127);
+    for (int i = 0; i < 32; i++)
+        codes[i] = oracle_e4m3_encode(ldexpf(x[i], -k));
+}
+
+float oracle_mx8_value(uint8_t code, uint8_t scale)
+{
+    return ldexpf(oracle_e4m3_decode(code), (int)scale - 127);
+}
+
 /* ---- ReplaySSM decode: checkpoint plus input buffer
  *
  * ReplaySSM article (lpnh.cn), section "核心做法" (core method) and its
@@ -497,6 +580,10 @@ int oracle_ssu(const oracle_args *a, char *err, int errlen)
  *      (the unrolled window of the same section; output-only decode);
  *  R18 h is the caller's per-sequence buffer pointer (the article moves a
  *      buffer pointer on commit); the caller resets it after a flush;
+ *  R32 with an MXFP8 read copy (R30, R31), an output-only step takes the
+ *      checkpoint from the copy (the high-precision pool is not read); a fold
+ *      reads and writes the high-precision checkpoint as before and then
+ *      rewrites the copy of that slot from the folded state;
  *  R19 one token per sequence, the checkpoint slot is read and written in
  *      place; the pad id reads a zero checkpoint, has no buffer (its pointer
  *      is taken as 0) and writes nothing; disable_state_update writes neither
@@ -512,6 +599,10 @@ typedef struct {
     const void *bB_in;  /* [slots, L, G, N] io dtype */
     void *bB_out;
     const int64_t *buf_len; /* [nseq] entries in each sequence's buffer */
+    /* optional MXFP8 read copy of the checkpoint pool (one-token step only):
+     * codes [slots, H, P, N], scales [slots, H, P, N / 32] */
+    const uint8_t *lp_in, *lps_in;
+    uint8_t *lp_out, *lps_out;
 } oracle_replay_args;
 
 /* dt' of one buffered or current step, one dim row */
@@ -544,6 +635,10 @@ int oracle_replay(const oracle_replay_args *ra, char *err, int errlen)
     }
     if (a->rtab.data && a->rtab.ndim != 1) {
         set_err(err, errlen, "replay takes a 1-D slot table%lld%lld", 0, 0);
+        return 1;
+    }
+    if ((ra->lp_in || ra->lp_out) && N % 32) {
+        set_err(err, errlen, "a read copy needs dstate divisible by 32%lld%lld", 0, 0);
         return 1;
     }
     const int64_t nseq = a->R;
@@ -587,8 +682,13 @@ int oracle_replay(const oracle_replay_args *ra, char *err, int errlen)
                            : load_as_f32(a->dt, a->dt_dtype, (b * H + hd) * dtw + (a->dt_per_head ? 0 : (d))))
 #define RB(j, n) ((j) < h ? load_as_f32(ra->bB_in, a->io_dtype, ((s * L + (j)) * G + g) * N + (n)) \
                           : load_as_f32(a->B, a->io_dtype, (b * G + g) * N + (n)))
+            /* R32: an output-only step reads the read copy when there is one */
+            const int from_copy = ra->lp_in && h + 1 != L && !pad;
             for (int64_t e = 0; e < tile; e++)
-                S[e] = pad ? 0.0f : load_as_f32(a->pool_in, a->state_dtype, (s * H + hd) * tile + e);
+                S[e] = pad ? 0.0f
+                           : from_copy ? oracle_mx8_value(ra->lp_in[(s * H + hd) * tile + e],
+                                                          ra->lps_in[((s * H + hd) * tile + e) / 32])
+                                       : load_as_f32(a->pool_in, a->state_dtype, (s * H + hd) * tile + e);
             if (h + 1 == L) {
                 /* flush: fold the buffered steps and the current one into the
                  * checkpoint, one plain update after the other */
@@ -620,6 +720,10 @@ int oracle_replay(const oracle_replay_args *ra, char *err, int errlen)
                         store_from_f32(a->pool_out, a->state_dtype, (s * H + hd) * tile + e, S[e]);
                     if (a->written)
                         a->written[s] = 1;
+                    if (ra->lp_out) /* R32: the fold rewrites the read copy */
+                        for (int64_t e = 0; e < tile; e += 32)
+                            oracle_mx8_block(S + e, ra->lp_out + (s * H + hd) * tile + e,
+                                             ra->lps_out + ((s * H + hd) * tile + e) / 32);
                 }
             } else {
                 /* output-only: y from the checkpoint and the buffer */
@@ -716,6 +820,10 @@ int oracle_replay_spec(const oracle_replay_args *ra, char *err, int errlen)
     }
     if (a->rtab.data && a->rtab.ndim != 1) {
         set_err(err, errlen, "replay takes a 1-D slot table%lld%lld", 0, 0);
+        return 1;
+    }
+    if (ra->lp_in || ra->lp_out) {
+        set_err(err, errlen, "the speculative step takes no read copy%lld%lld", 0, 0);
         return 1;
     }
     const int64_t nseq = a->R / T;
@@ -1051,4 +1159,17 @@ int oracle_ssd(const oracle_ssd_args *a, char *err, int errlen)
     }
     free(S);
     return 0;
+}
+
+/* bulk MXFP8: nblocks consecutive blocks of 32 values */
+void oracle_mx8_quantize(const float *x, int64_t nblocks, uint8_t *codes, uint8_t *scales)
+{
+    for (int64_t b = 0; b < nblocks; b++)
+        oracle_mx8_block(x + 32 * b, codes + 32 * b, scales + b);
+}
+
+void oracle_mx8_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t nblocks, float *x)
+{
+    for (int64_t i = 0; i < 32 * nblocks; i++)
+        x[i] = oracle_mx8_value(codes[i], scales[i / 32]);
 }

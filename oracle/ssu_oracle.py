@@ -235,7 +235,9 @@ class _ReplayArgs(ctypes.Structure):
                 ("bx_in", ctypes.c_void_p), ("bx_out", ctypes.c_void_p),
                 ("bdt_in", ctypes.c_void_p), ("bdt_out", ctypes.c_void_p),
                 ("bB_in", ctypes.c_void_p), ("bB_out", ctypes.c_void_p),
-                ("buf_len", ctypes.c_void_p)]
+                ("buf_len", ctypes.c_void_p),
+                ("lp_in", ctypes.c_void_p), ("lps_in", ctypes.c_void_p),
+                ("lp_out", ctypes.c_void_p), ("lps_out", ctypes.c_void_p)]
 
 
 def run_replay(case, oracle=None):
@@ -332,12 +334,22 @@ def _run_replay(case, oracle, spec):
     args.bdt_in, args.bdt_out = _ptr(bdt), _ptr(bdt_out)
     args.bB_in, args.bB_out = _ptr(bB), _ptr(bB_out)
     args.buf_len = _ptr(blen)
+    lp = case.get("lp")
+    out_lp = {}
+    if lp is not None:
+        lp = np.ascontiguousarray(lp, dtype=np.uint8)
+        lps = np.ascontiguousarray(case["lp_scale"], dtype=np.uint8)
+        if lp.shape != state.shape or lps.shape != state.shape[:3] + (N // 32,):
+            raise OracleError("read copy shapes do not match the pool")
+        out_lp = {"lp": lp.copy(), "lp_scale": lps.copy()}
+        args.lp_in, args.lps_in = _ptr(lp), _ptr(lps)
+        args.lp_out, args.lps_out = _ptr(out_lp["lp"]), _ptr(out_lp["lp_scale"])
     err = ctypes.create_string_buffer(256)
     fn = lib.oracle_replay_spec if spec else lib.oracle_replay
     if fn(ctypes.byref(args), err, 256):
         raise OracleError(err.value.decode())
-    return {"y": out.reshape(x.shape), "state": pool_out, "buf_x": bx_out, "buf_dt": bdt_out,
-            "buf_B": bB_out, "written": written.astype(bool)}
+    return dict({"y": out.reshape(x.shape), "state": pool_out, "buf_x": bx_out, "buf_dt": bdt_out,
+                 "buf_B": bB_out, "written": written.astype(bool)}, **out_lp)
 
 
 # ---------------------------------------------------------------- state copies
@@ -466,3 +478,56 @@ def run_ssd(case, oracle=None):
         raise OracleError("last_chunk_indices outside the chunks")
     return {"y": out, "chunk_states": states,
             "states": states[last] if nchunks else np.zeros((batch, H, P, N), states.dtype)}
+
+
+# ---------------------------------------------------------------- MXFP8 copies
+
+def _mx8_fns(lib):
+    if not hasattr(lib, "_mx8_ready"):
+        lib.oracle_mx8_quantize.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                            ctypes.c_void_p]
+        lib.oracle_mx8_quantize.restype = None
+        lib.oracle_mx8_dequantize.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                              ctypes.c_void_p]
+        lib.oracle_mx8_dequantize.restype = None
+        lib.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+        lib.oracle_e4m3_encode.restype = ctypes.c_uint8
+        lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_decode.restype = ctypes.c_float
+        lib._mx8_ready = True
+
+
+def mx8_quantize(x, oracle=None):
+    """MXFP8 (E4M3, blocks of 32 along the last axis) of a float32 array:
+    returns (codes uint8 like x, scales uint8 [..., last / 32])."""
+    lib = (oracle or default()).lib
+    _mx8_fns(lib)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.shape[-1] % 32:
+        raise OracleError("the last axis must be a multiple of 32")
+    codes = np.zeros(x.shape, np.uint8)
+    scales = np.zeros(x.shape[:-1] + (x.shape[-1] // 32,), np.uint8)
+    lib.oracle_mx8_quantize(x.ctypes.data, x.size // 32, codes.ctypes.data, scales.ctypes.data)
+    return codes, scales
+
+
+def mx8_dequantize(codes, scales, oracle=None):
+    lib = (oracle or default()).lib
+    _mx8_fns(lib)
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    x = np.zeros(codes.shape, np.float32)
+    lib.oracle_mx8_dequantize(codes.ctypes.data, scales.ctypes.data, codes.size // 32, x.ctypes.data)
+    return x
+
+
+def e4m3_encode(v, oracle=None):
+    lib = (oracle or default()).lib
+    _mx8_fns(lib)
+    return int(lib.oracle_e4m3_encode(float(v)))
+
+
+def e4m3_decode(b, oracle=None):
+    lib = (oracle or default()).lib
+    _mx8_fns(lib)
+    return float(lib.oracle_e4m3_decode(int(b)))

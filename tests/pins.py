@@ -1033,6 +1033,105 @@ def pin_ssd_dt_limit_zero(orc):
                 assert np.allclose(r["y"][t, h], y, rtol=1e-5, atol=1e-5), (b, t, h)
 
 
+# ---------------------------------------------------- MXFP8 read copy (R30-R32)
+
+def pin_e4m3_codec(orc):
+    """FP8 E4M3 (OCP): decoding every one of the 256 codes and encoding
+    in-range values (ties to even included) agree with PyTorch's float8_e4m3fn
+    (a library implementation); every finite code round-trips; magnitudes
+    above 448 saturate (R31)."""
+    import torch
+    from oracle import ssu_oracle
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    lib_vals = codes.view(torch.float8_e4m3fn).float().numpy()
+    for c in range(256):
+        v = ssu_oracle.e4m3_decode(c, orc)
+        assert (np.isnan(v) and np.isnan(lib_vals[c])) or v == lib_vals[c], c
+        if not np.isnan(v):
+            assert ssu_oracle.e4m3_encode(v, orc) == c or (v == 0.0 and c in (0, 0x80)), c
+    finite = np.sort(lib_vals[np.isfinite(lib_vals) & (lib_vals >= 0)])
+    finite = np.unique(finite)
+    mids = (finite[:-1] + finite[1:]) / 2            # ties
+    rng = np.random.default_rng(3)
+    probes = np.concatenate([mids, np.nextafter(mids, 0), np.nextafter(mids, 1000),
+                             rng.uniform(0, 463.9, 4000), rng.uniform(0, 2 ** -5, 2000)]).astype(np.float32)
+    probes = np.concatenate([probes, -probes])
+    want = torch.from_numpy(probes).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([ssu_oracle.e4m3_encode(v, orc) for v in probes], np.uint8)
+    assert np.array_equal(got, want)
+    for v in (464.0, 500.0, 1e30, -480.0):
+        assert ssu_oracle.e4m3_encode(v, orc) == (0x7E if v > 0 else 0xFE), v
+
+
+def pin_mx8_blocks(orc):
+    """MXFP8 blocks (R30): the scale exponent is floor(log2 max|x|) - 8, a
+    block of zeros gets byte 1 and zero codes, the decoded block errs by at
+    most half an E4M3 step (1/16 relative, 2^-10 of the scale in the
+    subnormal range) except clipped maxima, which decode to +-448 x scale,
+    and an already decoded block is a fixed point."""
+    from oracle import ssu_oracle
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((64, 32)) * np.exp(rng.uniform(-12, 12, (64, 1)))).astype(np.float32)
+    x[3] = 0.0
+    codes, scales = ssu_oracle.mx8_quantize(x, orc)
+    amax = np.abs(x).max(axis=1)
+    k = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1))) - 8, -126)
+    assert np.array_equal(scales[:, 0].astype(int) - 127, k.astype(int))
+    assert scales[3, 0] == 1 and not codes[3].any()
+    deq = ssu_oracle.mx8_dequantize(codes, scales, orc)
+    sc = np.exp2(k)[:, None]
+    clipped = np.abs(x) / sc >= 464
+    assert np.all(np.abs(deq[clipped]) == (448 * np.broadcast_to(sc, x.shape))[clipped])
+    err = np.abs(deq - x)
+    bound = np.maximum(np.abs(x) / 16, np.broadcast_to(sc, x.shape) * 2.0 ** -10)
+    assert np.all(err[~clipped] <= bound[~clipped])
+    c2, s2 = ssu_oracle.mx8_quantize(deq, orc)
+    assert np.array_equal(ssu_oracle.mx8_dequantize(c2, s2, orc), deq)
+
+
+def _lp_case(L, buf_len, **kw):
+    from oracle import ssu_oracle
+    c = _replay_case(L, buf_len, sd="f32", io="bf16", dstate=64, **kw)
+    c["lp"], c["lp_scale"] = ssu_oracle.mx8_quantize(
+        np.asarray(c["state"], np.float32) * np.float32(1.7), orc_default())
+    return c
+
+
+def orc_default():
+    from oracle import ssu_oracle
+    return ssu_oracle.default()
+
+
+def pin_replay_read_copy(orc):
+    """ReplaySSM with an MXFP8 read copy (R32): an output-only step equals the
+    plain replay step run on the copy's decoded values (the high-precision
+    pool is not read); a fold ignores the copy, matches the plain replay step
+    bit for bit, and rewrites exactly the folded slot's copy with the
+    quantized new checkpoint."""
+    from oracle import ssu_oracle
+    c = _lp_case(6, [0, 5, 3, 5])                  # sequences 1 and 3 fold
+    r = ssu_oracle.run_replay(c, orc)
+    deq = ssu_oracle.mx8_dequantize(c["lp"], c["lp_scale"], orc)
+    plain_deq = ssu_oracle.run_replay(dict({k: v for k, v in c.items() if not k.startswith("lp")},
+                                           state=deq), orc)
+    plain = ssu_oracle.run_replay({k: v for k, v in c.items() if not k.startswith("lp")}, orc)
+    tab = c["state_batch_indices"]
+    for b in (0, 2):
+        assert np.array_equal(r["y"][b], plain_deq["y"][b]), b
+    for b in (1, 3):
+        assert np.array_equal(r["y"][b], plain["y"][b]), b
+    assert np.array_equal(r["state"], plain["state"])
+    for b in range(4):
+        s = tab[b]
+        if b in (1, 3):
+            qc, qs = ssu_oracle.mx8_quantize(plain["state"][s], orc)
+            assert np.array_equal(r["lp"][s], qc) and np.array_equal(r["lp_scale"][s], qs), b
+        else:
+            assert np.array_equal(r["lp"][s], c["lp"][s]), b
+    d = ssu_oracle.run_replay(dict(c, disable_state_update=True), orc)
+    assert np.array_equal(d["lp"], c["lp"]) and np.array_equal(d["lp_scale"], c["lp_scale"])
+
+
 ALL = [pin_golden_mate_examples, pin_f16_decode_exhaustive, pin_f16_encode, pin_bf16_roundtrip, pin_softplus,
        pin_dt_zero_keeps_state, pin_b_zero_pure_decay, pin_zero_state_closed_form,
        pin_c_zero_and_z_zero, pin_mtp_equals_chained_calls, pin_unrolled_window,
@@ -1045,4 +1144,5 @@ ALL = [pin_golden_mate_examples, pin_f16_decode_exhaustive, pin_f16_encode, pin_
        pin_replay_spec_fold_boundary, pin_replay_spec_pad_and_disable, pin_replay_spec_brute_force,
        pin_memmove_matches_snapshot, pin_conv_shift_matches_snapshot,
        pin_ssd_matches_chunked_float64, pin_ssd_equals_decode_chain, pin_ssd_chunking_invariance,
-       pin_ssd_seq_idx_authority, pin_ssd_dt_limit_zero]
+       pin_ssd_seq_idx_authority, pin_ssd_dt_limit_zero, pin_e4m3_codec, pin_mx8_blocks,
+       pin_replay_read_copy]

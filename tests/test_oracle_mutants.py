@@ -89,6 +89,16 @@ MUTANTS = [
     ("ssd_decay_without_dt", "const float decay = expf(a->A[h] * v); /* R26 */", "const float decay = expf(a->A[h]);"),
     ("ssd_init_of_chunk", "load_as_f32(a->init, a->state_dtype, (a->seq_idx[c] * H + h) * tile + e)",
      "load_as_f32(a->init, a->state_dtype, (0 * H + h) * tile + e)"),
+    # MXFP8 read copy
+    ("e4m3_truncates", "float q = nearbyintf((ldexpf(a, -e) - 1.0f) * 8.0f);",
+     "float q = floorf((ldexpf(a, -e) - 1.0f) * 8.0f);"),
+    ("e4m3_subnormal_truncates", "const float q = nearbyintf(ldexpf(a, 9));",
+     "const float q = floorf(ldexpf(a, 9));"),
+    ("e4m3_decode_bias", "ldexpf(1.0f + (float)m / 8.0f, e - 7)", "ldexpf(1.0f + (float)m / 8.0f, e - 8)"),
+    ("mx8_scale_off_by_one", "k = (ex - 1) - 8; /* R30 */", "k = (ex - 1) - 7;"),
+    ("lp_read_at_fold", "const int from_copy = ra->lp_in && h + 1 != L && !pad;",
+     "const int from_copy = ra->lp_in && !pad;"),
+    ("lp_not_rewritten", "if (ra->lp_out) /* R32: the fold rewrites the read copy */", "if (0)"),
     ("default_dst_is_seq",
      "a->wtab.data ? &a->wtab : (a->rtab.data ? &a->rtab : NULL)", "a->wtab.data ? &a->wtab : NULL"),
     ("flat_write_b_plus_t", "int64_t i = tb->ndim == 1 ? bos + t :", "int64_t i = tb->ndim == 1 ? b + t :"),
