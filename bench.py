@@ -17,7 +17,7 @@ Prints ONE JSON line:
              current kernel source, else null
   cpu_baseline  the CPU oracle timed on this host on the same workload
 Options: --config {decode, decode_pad, mtp, varlen, varlen_disable, varlen_nodst, replay,
-replay_spec, spec_snapshots, conv_shift_sd, conv_shift_ds, memcpy_left, ssd},
+replay_spec, replay_lp, spec_snapshots, conv_shift_sd, conv_shift_ds, memcpy_left, ssd},
 --no-cpu-baseline, --calib-copy (also runs a plain device copy of the state's
 size, the calibration kernel for the counters).
 """
@@ -60,6 +60,10 @@ def workload(name):
                             "256, heads 128, dim 64, dstate 128, groups 8, fp32 checkpoint), "
                             "buffer length L = 16, bf16 x/dt/B buffers, per-sequence buffer "
                             "pointers ~ U{0..15} (about 1/16 of the sequences fold each step)")
+    if name == "replay_lp":
+        return W.replay(), ("replay_lp: the replay workload with an MXFP8 read copy of the fp32 "
+                            "checkpoint (E4M3 codes, one E8M0 scale per 32 values): output-only "
+                            "steps read the copy, folds store the checkpoint and rewrite the copy")
     if name == "replay_spec":
         return W.replay_spec(), ("replay_spec: ReplaySSM speculative step, batch 512 x T = 4 draft "
                                  "tokens, heads 128, dim 64, dstate 128, groups 8, fp32 "
@@ -156,13 +160,15 @@ def algorithmic_bytes(case):
     return int(total), int(R * H)
 
 
-def replay_algorithmic_bytes(case):
+def replay_algorithmic_bytes(case, lp=False):
     """Minimal bytes of one ReplaySSM step: each live sequence reads its
     checkpoint tile and its h committed entries; a folding sequence writes its
     checkpoint; the step's tokens are appended (one entry per token, or none
     for a one-token fold); plus the step's inputs and y, and per-head vectors
     and tables, as for the plain update. One-token steps fold at h + 1 = L,
-    speculative steps (x [batch, T, ...]) at h + 2T > L. Returns (bytes,
+    speculative steps (x [batch, T, ...]) at h + 2T > L. With the MXFP8 read
+    copy (lp) an output-only step reads the copy (1 + 1/32 bytes a value) in
+    place of the tile, and a fold also writes the copy. Returns (bytes,
     token-head updates)."""
     slots, H, P, N = np.shape(case["state"])
     sb = DTYPE_BYTES[case["state_dtype"]]
@@ -176,6 +182,7 @@ def replay_algorithmic_bytes(case):
     per_head = np.ndim(case["buf_dt"]) == 3
     entry = H * P * io + (H if per_head else H * P) * dtb + G * N * io
     tile = H * P * N * sb
+    copy = H * P * N + H * P * N // 32
     pad = int(case.get("pad_slot_id", -1))
     tab = case.get("state_batch_indices")
     total = 0
@@ -185,12 +192,13 @@ def replay_algorithmic_bytes(case):
         if s == pad:
             continue
         h = int(case["buf_len"][b])
-        total += tile + h * entry
+        fold = h + 2 * T > L if spec else h + 1 == L
+        total += (copy if lp and not fold else tile) + h * entry
         if not case.get("disable_state_update", False):
             if spec:
-                total += (tile if h + 2 * T > L else 0) + T * entry
+                total += (tile if fold else 0) + T * entry
             else:
-                total += tile if h + 1 == L else entry
+                total += tile + (copy if lp else 0) if fold else entry
     R = batch * T
     row = H * P * io * 2 + (H * P * io if case.get("z") is not None else 0)
     row += (H if np.ndim(case["dt"]) == x.ndim - 1 else H * P) * dtb + 2 * G * N * io
@@ -407,11 +415,15 @@ def traffic_from_counters(config):
     return entry.get("hbm_bytes_per_dispatch")
 
 
-def cpu_baseline(case, alg_bytes, updates, reps):
+def cpu_baseline(case, alg_bytes, updates, reps, lp=False):
     from oracle import ssu_oracle
     ssu_oracle.default()
     if "buf_len" in case:
         run = ssu_oracle.run_replay_spec if np.ndim(case["x"]) == 4 else ssu_oracle.run_replay
+        if lp:
+            case = dict(case)
+            case["lp"], case["lp_scale"] = ssu_oracle.mx8_quantize(
+                np.asarray(case["state"], np.float32))
     else:
         run = ssu_oracle.run
     times = []
@@ -465,8 +477,10 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     dev = torch.device("cuda", 0)
     case, desc = workload(args.config)
-    is_replay = args.config in ("replay", "replay_spec")
-    alg_bytes, updates = (replay_algorithmic_bytes if is_replay else algorithmic_bytes)(case)
+    is_replay = args.config in ("replay", "replay_spec", "replay_lp")
+    lp = args.config == "replay_lp"
+    alg_bytes, updates = replay_algorithmic_bytes(case, lp) if is_replay else \
+        algorithmic_bytes(case)
     print("[bench] %s: %.3f GB per step" % (args.config, alg_bytes / 1e9), file=sys.stderr,
           flush=True)
     d = device_replay(case, dev) if is_replay else device_case(case, dev)
@@ -479,6 +493,16 @@ def main():
                                       case.get("disable_state_update", False))
         launch = ssu.ssu_replay_spec_update if args.config == "replay_spec" else \
             ssu.ssu_replay_update
+        if lp:
+            # the read copy is resident state like the checkpoint: made once,
+            # on the GPU, before the timed steps
+            d["lp"], d["lp_scale"] = ssu.mx8_quantize(d["state"])
+            args_c = ssu.make_replay_lp_args(
+                d["state"], d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["buf_x"],
+                d["buf_dt"], d["buf_B"], d["buf_len"], d["lp"], d["lp_scale"], d["z"],
+                d["dt_bias"], case.get("dt_softplus", False), d["state_batch_indices"],
+                case.get("pad_slot_id", -1), out, case.get("disable_state_update", False))
+            launch = ssu.ssu_replay_lp_update
     else:
         args_c = ssu.make_args(d["state"], d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"],
                                d["z"], d["dt_bias"], case.get("dt_softplus", False),
@@ -551,7 +575,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(case, alg_bytes, updates, args.cpu_reps)
+        result["cpu_baseline"] = cpu_baseline(case, alg_bytes, updates, args.cpu_reps, lp)
     print(json.dumps(result), flush=True)
 
 

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SSU_ABI_VERSION 2
+#define SSU_ABI_VERSION 3
 
 #ifndef SSU_API
 #define SSU_API __attribute__((visibility("default")))
@@ -230,6 +230,50 @@ SSU_API ssu_status_t ssu_replay_update(const ssu_replay_args_t *args, void *stre
  * writes nothing; disable_state_update writes neither checkpoint nor buffer.
  * Same error, stream and allocation conventions as ssu_update. */
 SSU_API ssu_status_t ssu_replay_spec_update(const ssu_replay_args_t *args, void *stream);
+
+/* ---- ReplaySSM with a low-precision read copy (ReplaySSM article, lpnh.cn,
+ * section "效果与代价": the checkpoint is a read-mostly value that a
+ * low-precision copy can stand in for on the steps that only read it).
+ * Format: OCP Microscaling (MX) v1.0, MXFP8 with E4M3 elements: every 32
+ * consecutive dstate values of a checkpoint row form a block with one E8M0
+ * scale byte X = 2^(e - 127), where e - 127 = floor(log2 max|v|) - 8 clamped
+ * to [-126, 127] (-126 for an all-zero block); each element is v / X rounded
+ * to nearest even in E4M3 (bias 7, subnormals, largest finite 448, codes
+ * 0x7F / 0xFF are NaN), saturating to +-448. A value decodes as code * X. */
+
+/* Quantize fp32 values to MXFP8:
+ *   src     [n] f32 (device), n a multiple of 32; blocks are consecutive
+ *           runs of 32 values
+ *   codes   [n] u8 (device): E4M3 codes
+ *   scales  [n / 32] u8 (device): E8M0 scale bytes
+ * A NaN element becomes code 0x7F and does not count toward the block's
+ * largest magnitude; a block holding an infinity has no defined scale and
+ * its bytes are unspecified (a checkpoint is finite). One kernel on
+ * `stream`, asynchronous, allocates nothing; n = 0 launches nothing. All
+ * three must be contiguous 1-D tensors (any shape whose element count is n
+ * is read as flat). */
+SSU_API ssu_status_t ssu_mx8_quantize(const ssu_tensor_t *src, const ssu_tensor_t *codes,
+                                      const ssu_tensor_t *scales, void *stream);
+
+/* ssu_replay_update with the checkpoint's MXFP8 copy: output-only steps read
+ * the copy (codes * scale, decoded to fp32) in place of the fp32 checkpoint;
+ * a flush reads the fp32 checkpoint, folds and stores it as ssu_replay_update
+ * does, and then writes the copy of the stored state (the format above) into
+ * lp and lp_scale. The pad id reads zeros and writes nothing;
+ * disable_state_update writes neither checkpoint, copy nor buffer.
+ * base: as for ssu_replay_update, with an f32 state pool whose [heads, dim,
+ * dstate] part is contiguous, and dstate a multiple of 32.
+ *   lp        [slots, heads, dim, dstate] u8, contiguous, 4-byte aligned (device)
+ *   lp_scale  [slots, heads, dim, dstate / 32] u8, contiguous, 8-byte aligned (device)
+ * The caller keeps the copy in step with the checkpoint (ssu_mx8_quantize
+ * of the pool makes a first copy). Same error, stream and allocation
+ * conventions as ssu_update. */
+typedef struct {
+    ssu_replay_args_t base;
+    ssu_tensor_t lp, lp_scale;
+} ssu_replay_lp_args_t;
+
+SSU_API ssu_status_t ssu_replay_lp_update(const ssu_replay_lp_args_t *args, void *stream);
 
 /* ---- memmove-safe Mamba state copies (vLLM PR #50729 digest, prhub:
  * sections "实现拆解" and "关键源码片段"). Speculative decoding shifts a

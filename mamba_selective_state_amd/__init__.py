@@ -3,7 +3,9 @@
 The update runs in hand-written HIP kernels behind a C ABI (include/ssu.h,
 libssu.so); this package is its Python binding.
 """
-from .ssu import (LIBRARY_PATH, SsuArgs, SsuConvShiftArgs, SsuError, SsuReplayArgs, SsuSsdArgs,
+from .ssu import (LIBRARY_PATH, SsuArgs, SsuConvShiftArgs, SsuError, SsuReplayArgs, SsuReplayLpArgs,
+                  SsuSsdArgs, mx8_quantize, replay_lp_selective_state_update,
+                  ssu_mx8_quantize, ssu_replay_lp_update, make_replay_lp_args,
                   batch_memcpy, ssd_combined_fwd_varlen, ssu_ssd_prefill, ssu_ssd_workspace_bytes,
                   conv_state_shift, make_args, make_conv_shift_args, make_replay_args,
                   prewarm_selective_state_update, replay_selective_state_update,
@@ -17,4 +19,6 @@ __all__ = ["selective_state_update", "prewarm_selective_state_update",
            "ssu_abi_version", "make_args", "make_replay_args", "SsuArgs", "SsuReplayArgs",
            "SsuError", "LIBRARY_PATH", "batch_memcpy", "conv_state_shift", "ssu_batch_memcpy",
            "ssu_conv_state_shift", "make_conv_shift_args", "SsuConvShiftArgs",
-           "ssd_combined_fwd_varlen", "ssu_ssd_prefill", "ssu_ssd_workspace_bytes", "SsuSsdArgs"]
+           "ssd_combined_fwd_varlen", "ssu_ssd_prefill", "ssu_ssd_workspace_bytes", "SsuSsdArgs",
+           "replay_lp_selective_state_update", "ssu_replay_lp_update", "make_replay_lp_args",
+           "SsuReplayLpArgs", "mx8_quantize", "ssu_mx8_quantize"]

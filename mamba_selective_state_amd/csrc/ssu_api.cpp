@@ -874,8 +874,9 @@ ssu_status_t ssu_update(const ssu_args_t *a, void *stream) {
 
 // Both ReplaySSM entry points: validate, then launch the one-token or the
 // speculative kernel.
-static ssu_status_t replay_common(const ssu_replay_args_t *ra, bool spec, void *stream) {
-    const char *fn = spec ? "ssu_replay_spec_update" : "ssu_replay_update";
+static ssu_status_t replay_common(const ssu_replay_args_t *ra, bool spec, void *stream,
+                                  const ssu_replay_lp_args_t *lpa = nullptr) {
+    const char *fn = lpa ? "ssu_replay_lp_update" : spec ? "ssu_replay_spec_update" : "ssu_replay_update";
     if (!ra)
         return fail(SSU_ERR_VALUE, "%s: args is NULL", fn);
     const ssu_args_t *a = &ra->base;
@@ -952,6 +953,40 @@ static ssu_status_t replay_common(const ssu_replay_args_t *ra, bool spec, void *
     if ((s = meta_vector("buf_len", ra->buf_len, pr.nseq, &rp.buf_len, &len_s, &len_i64)) !=
         SSU_OK)
         return s;
+    if (lpa) {
+        // the copy mirrors the pool's [slots, heads, dim, dstate], one byte a value
+        if (pr.state_dtype != SSU_F32)
+            return fail(SSU_ERR_NOT_IMPLEMENTED, "the MXFP8 read copy needs an f32 checkpoint");
+        if (pr.N % 32 != 0)
+            return fail(SSU_ERR_VALUE, "the MXFP8 read copy needs dstate a multiple of 32");
+        const ssu_tensor_t &lp = lpa->lp, &lps = lpa->lp_scale;
+        if (!present(lp) || !present(lps))
+            return fail(SSU_ERR_VALUE, "lp and lp_scale are required");
+        if (lp.dtype != SSU_U8 || lps.dtype != SSU_U8)
+            return fail(SSU_ERR_VALUE, "lp and lp_scale must be u8");
+        const int64_t want_lp[4] = {pr.slots, pr.H, pr.P, pr.N};
+        const int64_t want_sc[4] = {pr.slots, pr.H, pr.P, pr.N / 32};
+        const ssu_tensor_t *ts[2] = {&lp, &lps};
+        const int64_t *wants[2] = {want_lp, want_sc};
+        for (int i = 0; i < 2; i++) {
+            const ssu_tensor_t *t = ts[i];
+            if (t->ndim != 4)
+                return fail(SSU_ERR_VALUE, "lp and lp_scale must be 4-D");
+            int64_t want = 1;
+            for (int j = 3; j >= 0; j--) {
+                if (t->size[j] != wants[i][j])
+                    return fail(SSU_ERR_VALUE, i ? "lp_scale must be [slots, heads, dim, dstate / 32]"
+                                                 : "lp must be [slots, heads, dim, dstate]");
+                if (t->stride[j] != want && t->size[j] != 1)
+                    return fail(SSU_ERR_VALUE, "lp and lp_scale must be contiguous");
+                want *= t->size[j];
+            }
+        }
+        if (!aligned(lp.data, 4) || !aligned(lps.data, 8))
+            return fail(SSU_ERR_VALUE, "lp must be 4-byte and lp_scale 8-byte aligned");
+        rp.lp = static_cast<uint8_t *>(const_cast<void *>(lp.data));
+        rp.lp_scale = static_cast<uint8_t *>(const_cast<void *>(lps.data));
+    }
     if (pr.empty)
         return g_error.clear(), SSU_OK;
     // the kernel addresses one slot's buffer entries with 32-bit offsets
@@ -968,7 +1003,8 @@ static ssu_status_t replay_common(const ssu_replay_args_t *ra, bool spec, void *
     rp.G = static_cast<int32_t>(pr.G);
 
     ssu::KernelRef k;
-    if (!ssu::find_replay_kernel(pr.state_dtype, pr.io, static_cast<int>(pr.N), spec, &k))
+    if (lpa ? !ssu::find_replay_lp_kernel(pr.io, static_cast<int>(pr.N), &k)
+            : !ssu::find_replay_kernel(pr.state_dtype, pr.io, static_cast<int>(pr.N), spec, &k))
         return fail(SSU_ERR_NOT_IMPLEMENTED, "no replay kernel for state %s / io %s / dstate %lld",
                     dtype_str(pr.state_dtype), dtype_str(pr.io), (long long)pr.N);
     const Geometry geo = geometry(pr.P, pr.N, pr.state_dtype, ssu::kTileReplay);
@@ -992,6 +1028,53 @@ ssu_status_t ssu_replay_update(const ssu_replay_args_t *ra, void *stream) {
 
 ssu_status_t ssu_replay_spec_update(const ssu_replay_args_t *ra, void *stream) {
     return replay_common(ra, true, stream);
+}
+
+ssu_status_t ssu_replay_lp_update(const ssu_replay_lp_args_t *la, void *stream) {
+    if (!la)
+        return fail(SSU_ERR_VALUE, "ssu_replay_lp_update: args is NULL");
+    return replay_common(&la->base, false, stream, la);
+}
+
+// a contiguous tensor of `dtype` read as flat; returns its element count or -1
+static int64_t flat_count(const ssu_tensor_t &t, int dtype) {
+    if (!present(t) || t.dtype != dtype || t.ndim < 1 || t.ndim > 4)
+        return -1;
+    int64_t want = 1;
+    for (int j = t.ndim - 1; j >= 0; j--) {
+        if (t.size[j] < 0 || (t.stride[j] != want && t.size[j] != 1))
+            return -1;
+        want *= t.size[j];
+    }
+    return want;
+}
+
+ssu_status_t ssu_mx8_quantize(const ssu_tensor_t *src, const ssu_tensor_t *codes,
+                              const ssu_tensor_t *scales, void *stream) {
+    if (!src || !codes || !scales)
+        return fail(SSU_ERR_VALUE, "ssu_mx8_quantize: a tensor is NULL");
+    const int64_t n = flat_count(*src, SSU_F32);
+    if (n < 0)
+        return fail(SSU_ERR_VALUE, "src must be a contiguous f32 tensor");
+    if (n % 32 != 0)
+        return fail(SSU_ERR_VALUE, "src holds %lld values, not a multiple of 32", (long long)n);
+    if (flat_count(*codes, SSU_U8) != n)
+        return fail(SSU_ERR_VALUE, "codes must be a contiguous u8 tensor of %lld values", (long long)n);
+    if (flat_count(*scales, SSU_U8) != n / 32)
+        return fail(SSU_ERR_VALUE, "scales must be a contiguous u8 tensor of %lld values",
+                    (long long)(n / 32));
+    if (n == 0)
+        return g_error.clear(), SSU_OK;
+    if (!aligned(src->data, 16) || !aligned(codes->data, 8))
+        return fail(SSU_ERR_VALUE, "src must be 16-byte and codes 8-byte aligned");
+    const int e = ssu::launch_mx8_quantize(static_cast<const float *>(src->data),
+                                           static_cast<uint8_t *>(const_cast<void *>(codes->data)),
+                                           static_cast<uint8_t *>(const_cast<void *>(scales->data)),
+                                           n / 32, stream);
+    if (e != 0)
+        return fail(SSU_ERR_HIP, "kernel launch failed: %s", ssu::hip_error_string(e));
+    g_error.clear();
+    return SSU_OK;
 }
 
 }  // extern "C"

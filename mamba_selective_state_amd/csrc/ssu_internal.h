@@ -138,6 +138,10 @@ struct ReplayParams {
     int32_t len_i64;    // buf_len is i64
     int32_t dt_per_head;  // buf_dt is [slots, L, H]
     int32_t G;
+    // MXFP8 read copy of the checkpoint pool (LP kernels): E4M3 codes
+    // [slots, H, P, N] and E8M0 scales [slots, H, P, N / 32]
+    uint8_t *lp;
+    uint8_t *lp_scale;
 };
 
 // Selected kernel variant for (state dtype, io dtype, dstate, multi-token).
@@ -200,6 +204,10 @@ int launch_ssd(const SsdParams &sp, int io_dtype, int state_dtype, void *stream)
 int launch_conv_shift(const ConvParams &cv, bool dim_major, unsigned grid, void *stream);
 
 bool find_replay_kernel(int state_dtype, int io_dtype, int dstate, bool spec, KernelRef *out);
+// The one-token replay kernel with an MXFP8 read copy (fp32 checkpoints).
+bool find_replay_lp_kernel(int io_dtype, int dstate, KernelRef *out);
+// MXFP8 quantization of `nblocks` blocks of 32 fp32 values.
+int launch_mx8_quantize(const float *src, uint8_t *codes, uint8_t *scales, int64_t nblocks, void *stream);
 int launch_replay(const KernelRef &k, const Params &p, const ReplayParams &rp, unsigned grid,
                   unsigned block, void *stream);
 

@@ -122,6 +122,21 @@ __device__ __forceinline__ float row16_sum(float v) {
     return v;
 }
 
+// Largest value over each aligned group of LANES lanes (2, 4, 8 or 16) of a
+// DPP row, in every lane of the group (same steps as row16_sum).
+template <int LANES>
+__device__ __forceinline__ float group_max(float v) {
+    static_assert(LANES == 2 || LANES == 4 || LANES == 8 || LANES == 16, "a DPP row splits in powers of two");
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+    if constexpr (LANES >= 4)
+        v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+    if constexpr (LANES >= 8)
+        v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+    if constexpr (LANES >= 16)
+        v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+    return v;
+}
+
 // Value of lane Q of the caller's DPP row (lanes 16k .. 16k+15), in every
 // lane of that row.
 template <int Q>
@@ -503,6 +518,55 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
     }
 }
 
+// MXFP8 (OCP Microscaling, E4M3 elements, E8M0 scale per 32 values) for the
+// checkpoint's read copy. A block's scale is 2^k with k = floor(log2 max|x|)
+// - 8 clamped to [-126, 127] (-126 for a block of zeros); elements x 2^-k
+// round to nearest even in E4M3 and saturate at 448.
+__device__ __forceinline__ float mx8_scale(uint32_t byte) {
+    return byte ? __uint_as_float(byte << 23) : 0x1p-127f;
+}
+
+// Two E4M3 codes (bytes 2*HI and 2*HI + 1 of `codes`) times the scale: the
+// conversion unit decodes the OCP format (NaN codes to NaN) and applies the
+// power-of-two scale exactly, fp32 subnormal results included.
+template <bool HI>
+__device__ __forceinline__ float2 e4m3_pair(uint32_t codes, float scale) {
+    const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(codes, scale, HI);
+    return float2{v[0], v[1]};
+}
+
+// E4M3 codes of v[0..3] / 2^k, packed byte i = value i. The conversion unit
+// divides by the power-of-two scale and rounds to nearest even; it turns a
+// quotient beyond the largest finite value into NaN, so the inputs are first
+// clamped to +-448 * 2^k (saturation), and a NaN input is given code 0x7F.
+__device__ __forceinline__ uint32_t e4m3_codes4(const float v[4], int k) {
+    const float X = __uint_as_float(static_cast<uint32_t>(k + 127) << 23);
+    const float lim = 448.0f * X;  // infinite for k = 127: no value reaches it
+    float c[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        c[i] = v[i] != v[i] ? 0.0f : fminf(fmaxf(v[i], -lim), lim);
+    typedef short short2_t __attribute__((ext_vector_type(2)));
+    short2_t r = {0, 0};
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, c[0], c[1], X, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, c[2], c[3], X, true);
+    uint32_t codes = static_cast<uint32_t>(static_cast<uint16_t>(r[0])) |
+                     (static_cast<uint32_t>(static_cast<uint16_t>(r[1])) << 16);
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        codes = v[i] != v[i] ? (codes & ~(0xFFu << (8 * i))) | (0x7Fu << (8 * i)) : codes;
+    return codes;
+}
+
+// scale exponent of a block from its largest magnitude
+__device__ __forceinline__ int mx8_exponent(float amax) {
+    const int ex = static_cast<int>((__float_as_uint(amax) >> 23) & 0xFFu);
+    if (ex == 0)
+        return -126;  // zero or subnormal
+    const int k = ex - 127 - 8;
+    return k < -126 ? -126 : (k > 127 ? 127 : k);
+}
+
 // ReplaySSM decode (ReplaySSM article, section "核心做法"): one workgroup per
 // (sequence, head, dim tile), the checkpoint tile in ssu_kernel's lane
 // layout. A step with h buffered entries either fills the buffer (h + 1 == L:
@@ -518,7 +582,7 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
 // (R1, G1) is (R0 G1 + R1, G0 G1)). Each B_j . C is formed once per DPP row
 // and handed to the lanes whose step it is. An entry count outside [0, L)
 // (not for the pad id) makes the sequence's y NaN and writes nothing.
-template <typename ST, typename IT, int N>
+template <typename ST, typename IT, int N, bool LP>
 __global__ __launch_bounds__(kMaxWaves *kWaveLanes, replay_waves_per_eu(sizeof(ST), N)) void ssu_replay_kernel(
     const Params p, const ReplayParams rp) {
     constexpr int E = N / kLanesPerRow;
@@ -530,6 +594,7 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes, replay_waves_per_eu(sizeof(S
     constexpr int NSEG = kLanesPerRow / PASSES;
     constexpr int NDOT = NSEG < kRowsPerPass ? 1 : NSEG / kRowsPerPass;
     static_assert(PASSES <= kLanesPerRow && kLanesPerRow % PASSES == 0, "runs tile the row");
+    static_assert(!LP || (sizeof(ST) == 4 && VEC >= 2 && N % 32 == 0), "MX blocks span whole lanes of a row");
     using SPack = Pack<ST, VEC>;
     using Bits = typename TokenInputs<IT, NCH, IVEC>::Bits;
 
@@ -620,6 +685,79 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes, replay_waves_per_eu(sizeof(S
         const int64_t xo = b * p.x_sr + h * p.x_sh + d_fetch;
         x_bits = *reinterpret_cast<const Bits *>(xs + xo);
         z_bits = *reinterpret_cast<const Bits *>(zs ? zs + (b * p.z_sr + h * p.z_sh + d_fetch) : xs + xo);
+    };
+    // The read copy: lanes of one 32-value block (32 / VEC lanes of a row)
+    // read VEC codes each and the block's scale byte.
+    const int64_t lp_tile = (pad ? 0 : s) * (static_cast<int64_t>(p.H) * P * N) + tile_off;  // byte offset of the tile
+    // A row's N / 32 scale bytes (at most 8) come in one load per pass.
+    auto load_copy = [&]() {
+#pragma unroll
+        for (int q = 0; q < PASSES; q++) {
+            const int d0 = dw + q * kRowsPerPass + rsub;
+            const int64_t d = d0 < P ? d0 : P - 1;
+            const int64_t row = lp_tile + d * N;
+            uint64_t sw;
+            if constexpr (N / 32 > 4) {
+                const uint2 w = *reinterpret_cast<const uint2 *>(rp.lp_scale + row / 32);
+                sw = w.x | (static_cast<uint64_t>(w.y) << 32);
+            } else if constexpr (N / 32 == 4) {
+                sw = *reinterpret_cast<const uint32_t *>(rp.lp_scale + row / 32);
+            } else if constexpr (N / 32 == 2) {
+                sw = *reinterpret_cast<const uint16_t *>(rp.lp_scale + row / 32);
+            } else {
+                sw = rp.lp_scale[row / 32];
+            }
+#pragma unroll
+            for (int c = 0; c < NCH; c++) {
+                const int n0 = c * kLanesPerRow * VEC + col * VEC;
+                uint32_t codes;
+                if constexpr (VEC == 4)
+                    codes = *reinterpret_cast<const uint32_t *>(rp.lp + row + n0);
+                else
+                    codes = *reinterpret_cast<const uint16_t *>(rp.lp + row + n0);
+                const float sc = mx8_scale(static_cast<uint32_t>(sw >> (8 * (n0 / 32))) & 0xFFu);
+                const float2 lo = e4m3_pair<false>(codes, sc);
+                S[q][c].v[0] = narrow<ST>(lo.x);
+                S[q][c].v[1] = narrow<ST>(lo.y);
+                if constexpr (VEC == 4) {
+                    const float2 hi = e4m3_pair<true>(codes, sc);
+                    S[q][c].v[2] = narrow<ST>(hi.x);
+                    S[q][c].v[3] = narrow<ST>(hi.y);
+                }
+            }
+        }
+    };
+    // the folded tile into the read copy (after its fp32 store)
+    auto store_copy = [&]() {
+        constexpr int kBlockLanes = LP ? 32 / VEC : 2;  // lanes sharing a block
+#pragma unroll
+        for (int q = 0; q < PASSES; q++) {
+            const int d = dw + q * kRowsPerPass + rsub;
+#pragma unroll
+            for (int c = 0; c < NCH; c++) {
+                float amax = 0.0f;
+#pragma unroll
+                for (int k = 0; k < VEC; k++)
+                    amax = fmaxf(amax, fabsf(widen(S[q][c].v[k])));
+                amax = group_max<kBlockLanes>(amax);
+                const int kexp = mx8_exponent(amax);
+                float v4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int k = 0; k < VEC; k++)
+                    v4[k] = widen(S[q][c].v[k]);
+                const uint32_t codes = e4m3_codes4(v4, kexp);
+                if (d < P) {
+                    const int64_t n0 = c * kLanesPerRow * VEC + col * VEC;
+                    const int64_t at = lp_tile + static_cast<int64_t>(d) * N + n0;
+                    if constexpr (VEC == 4)
+                        *reinterpret_cast<uint32_t *>(rp.lp + at) = codes;
+                    else
+                        *reinterpret_cast<uint16_t *>(rp.lp + at) = static_cast<uint16_t>(codes);
+                    if (col % kBlockLanes == 0)
+                        rp.lp_scale[at / 32] = static_cast<uint8_t>(kexp + 127);
+                }
+            }
+        }
     };
     // (rows past the dim read the last row; their results are never stored)
     auto load_checkpoint = [&]() {
@@ -734,6 +872,8 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes, replay_waves_per_eu(sizeof(S
                             reinterpret_cast<SPack *>(dst + c * kLanesPerRow * VEC), S[q][c]);
                 }
             }
+            if constexpr (LP)
+                store_copy();
         }
     } else {
         // the lane's window row and run; run k holds steps k*SL .. k*SL+SL-1
@@ -805,7 +945,14 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes, replay_waves_per_eu(sizeof(S
         const unsigned char *dpo = dt_at(hb, d_fetch);
         dto_lo = *reinterpret_cast<const uint16_t *>(dpo);
         dto_hi = *reinterpret_cast<const uint16_t *>(dpo + (dt_f32 ? 2 : 0));
-        load_checkpoint();
+        if constexpr (LP) {
+            if (pad)
+                load_checkpoint();  // zeros
+            else
+                load_copy();
+        } else {
+            load_checkpoint();
+        }
         decode_C();
 #pragma unroll
         for (int i = 0; i < T0; i++)
@@ -1330,7 +1477,7 @@ bool pick_replay_n(int n, KernelRef *k) {
 #define SSU_CASE(NN)                                                                     \
     case NN:                                                                             \
         k->fn = SPEC ? reinterpret_cast<const void *>(&ssu_replay_spec_kernel<ST, IT, NN>) \
-                     : reinterpret_cast<const void *>(&ssu_replay_kernel<ST, IT, NN>);   \
+                     : reinterpret_cast<const void *>(&ssu_replay_kernel<ST, IT, NN, false>);  \
         return true;
         SSU_CASE(16)
         SSU_CASE(32)
@@ -1419,6 +1566,65 @@ bool find_replay_kernel(int state_dtype, int io_dtype, int dstate, bool spec, Ke
                     : pick_replay_io<__bf16, false>(io_dtype, dstate, out);
     }
     return false;
+}
+
+template <typename IT>
+bool pick_replay_lp_n(int n, KernelRef *k) {
+    switch (n) {
+    case 32: k->fn = reinterpret_cast<const void *>(&ssu_replay_kernel<float, IT, 32, true>); return true;
+    case 64: k->fn = reinterpret_cast<const void *>(&ssu_replay_kernel<float, IT, 64, true>); return true;
+    case 128: k->fn = reinterpret_cast<const void *>(&ssu_replay_kernel<float, IT, 128, true>); return true;
+    case 256: k->fn = reinterpret_cast<const void *>(&ssu_replay_kernel<float, IT, 256, true>); return true;
+    }
+    return false;
+}
+
+bool find_replay_lp_kernel(int io_dtype, int dstate, KernelRef *out) {
+    switch (io_dtype) {
+    case SSU_F32: return pick_replay_lp_n<float>(dstate, out);
+    case SSU_F16: return pick_replay_lp_n<_Float16>(dstate, out);
+    case SSU_BF16: return pick_replay_lp_n<__bf16>(dstate, out);
+    }
+    return false;
+}
+
+// MXFP8 quantization: 4 lanes per block of 32 values (8 each), grid-stride
+__global__ __launch_bounds__(256) void mx8_quantize_kernel(const float *src, uint8_t *codes, uint8_t *scales,
+                                                           int64_t nblocks) {
+    const int64_t lanes = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    // every lane of a wave runs the same number of iterations (the shuffles need all lanes)
+    const int64_t total = (nblocks * 4 + 63) / 64 * 64;
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < (total + lanes - 1) / lanes * lanes;
+         i += lanes) {
+        const bool live = i < nblocks * 4;
+        const int64_t at = (live ? i : 0) * 8;
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(src + at);
+        const u32x4 b = *reinterpret_cast<const u32x4 *>(src + at + 4);
+        float v[8] = {__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z), __uint_as_float(a.w),
+                      __uint_as_float(b.x), __uint_as_float(b.y), __uint_as_float(b.z), __uint_as_float(b.w)};
+        float amax = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; k++)
+            amax = fmaxf(amax, fabsf(v[k]));
+        amax = group_max<4>(amax);
+        const int kexp = mx8_exponent(amax);
+        const uint32_t lo = e4m3_codes4(v, kexp);
+        const uint32_t hi = e4m3_codes4(v + 4, kexp);
+        if (live) {
+            *reinterpret_cast<u32x2 *>(codes + at) = u32x2{lo, hi};
+            if ((i & 3) == 0)
+                scales[i / 4] = static_cast<uint8_t>(kexp + 127);
+        }
+    }
+}
+
+int launch_mx8_quantize(const float *src, uint8_t *codes, uint8_t *scales, int64_t nblocks, void *stream) {
+    int64_t blocks = (nblocks * 4 + 255) / 256;
+    blocks = blocks < 1 ? 1 : (blocks > 65536 ? 65536 : blocks);
+    void *args[] = {const_cast<float **>(&src), &codes, &scales, &nblocks};
+    return static_cast<int>(hipLaunchKernel(reinterpret_cast<const void *>(&mx8_quantize_kernel),
+                                            dim3(static_cast<unsigned>(blocks)), dim3(256), args, 0,
+                                            static_cast<hipStream_t>(stream)));
 }
 
 int launch_replay(const KernelRef &k, const Params &p, const ReplayParams &rp, unsigned grid,

@@ -46,6 +46,10 @@ class SsuReplayArgs(ctypes.Structure):
                 ("buf_B", SsuTensor), ("buf_len", SsuTensor)]
 
 
+class SsuReplayLpArgs(ctypes.Structure):
+    _fields_ = [("base", SsuReplayArgs), ("lp", SsuTensor), ("lp_scale", SsuTensor)]
+
+
 class SsuConvShiftArgs(ctypes.Structure):
     _fields_ = [("state", SsuTensor), ("layout", ctypes.c_int32), ("src_block", SsuTensor),
                 ("dst_block", SsuTensor), ("bias", SsuTensor)]
@@ -76,7 +80,7 @@ class SsuPlanInfo(ctypes.Structure):
 
 
 EXPORTS = ("ssu_plan", "ssu_update", "ssu_replay_update", "ssu_replay_spec_update",
-           "ssu_batch_memcpy", "ssu_conv_state_shift", "ssu_ssd_workspace_bytes", "ssu_ssd_prefill",
+           "ssu_replay_lp_update", "ssu_mx8_quantize", "ssu_batch_memcpy", "ssu_conv_state_shift", "ssu_ssd_workspace_bytes", "ssu_ssd_prefill",
            "ssu_last_error", "ssu_abi_version")
 
 
@@ -95,6 +99,10 @@ def load_library(path=None):
     lib.ssu_replay_update.restype = ctypes.c_int
     lib.ssu_replay_spec_update.argtypes = [ctypes.POINTER(SsuReplayArgs), ctypes.c_void_p]
     lib.ssu_replay_spec_update.restype = ctypes.c_int
+    lib.ssu_replay_lp_update.argtypes = [ctypes.POINTER(SsuReplayLpArgs), ctypes.c_void_p]
+    lib.ssu_replay_lp_update.restype = ctypes.c_int
+    lib.ssu_mx8_quantize.argtypes = [ctypes.POINTER(SsuTensor)] * 3 + [ctypes.c_void_p]
+    lib.ssu_mx8_quantize.restype = ctypes.c_int
     lib.ssu_batch_memcpy.argtypes = [ctypes.POINTER(SsuTensor)] * 3 + [ctypes.c_int64,
                                                                        ctypes.c_void_p]
     lib.ssu_batch_memcpy.restype = ctypes.c_int
@@ -163,6 +171,27 @@ def ssu_replay_spec_update(args, stream=None):
     st = _lib.ssu_replay_spec_update(ctypes.byref(args), ctypes.c_void_p(stream))
     if st != OK:
         _raise(st, "ssu_replay_spec_update")
+
+
+def ssu_replay_lp_update(args, stream=None):
+    """Enqueue one ReplaySSM decode step with the MXFP8 read copy (include/ssu.h
+    ssu_replay_lp_update)."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    st = _lib.ssu_replay_lp_update(ctypes.byref(args), ctypes.c_void_p(stream))
+    if st != OK:
+        _raise(st, "ssu_replay_lp_update")
+
+
+def ssu_mx8_quantize(src, codes, scales, stream=None):
+    """Enqueue an MXFP8 quantization (include/ssu.h ssu_mx8_quantize); the
+    arguments are SsuTensor descriptors."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    st = _lib.ssu_mx8_quantize(ctypes.byref(src), ctypes.byref(codes), ctypes.byref(scales),
+                               ctypes.c_void_p(stream))
+    if st != OK:
+        _raise(st, "ssu_mx8_quantize")
 
 
 def ssu_plan(desc):
@@ -328,6 +357,53 @@ def replay_spec_selective_state_update(state, x, dt, A, B, C, D, buf_x, buf_dt, 
                             disable_state_update)
     ssu_replay_spec_update(args, torch.cuda.current_stream(state.device).cuda_stream)
     return out
+
+
+def make_replay_lp_args(state, x, dt, A, B, C, D, buf_x, buf_dt, buf_B, buf_len, lp, lp_scale,
+                        z=None, dt_bias=None, dt_softplus=False, state_batch_indices=None,
+                        pad_slot_id=-1, out=None, disable_state_update=False):
+    """SsuReplayLpArgs for ssu_replay_lp_update; `out` must be given."""
+    r = SsuReplayLpArgs()
+    r.base = make_replay_args(state, x, dt, A, B, C, D, buf_x, buf_dt, buf_B, buf_len, z, dt_bias,
+                              dt_softplus, state_batch_indices, pad_slot_id, out,
+                              disable_state_update)
+    r.lp = tensor_desc(lp, state.device)
+    r.lp_scale = tensor_desc(lp_scale, state.device)
+    return r
+
+
+def replay_lp_selective_state_update(state, x, dt, A, B, C, D, buf_x, buf_dt, buf_B, buf_len, lp,
+                                     lp_scale, z=None, dt_bias=None, dt_softplus=False,
+                                     state_batch_indices=None, pad_slot_id=-1, out=None,
+                                     disable_state_update=False):
+    """replay_selective_state_update with an MXFP8 copy of the f32 checkpoint
+    (ReplaySSM article, section "效果与代价"; OCP MX v1.0 MXFP8 E4M3):
+    output-only steps read lp (uint8 E4M3 codes, [slots, heads, dim, dstate])
+    times lp_scale (uint8 E8M0, [slots, heads, dim, dstate / 32]) instead of
+    the checkpoint; a fold stores the checkpoint and rewrites both. Returns y."""
+    if out is None:
+        out = torch.empty(x.shape, dtype=x.dtype, device=x.device)
+    args = make_replay_lp_args(state, x, dt, A, B, C, D, buf_x, buf_dt, buf_B, buf_len, lp,
+                               lp_scale, z, dt_bias, dt_softplus, state_batch_indices,
+                               pad_slot_id, out, disable_state_update)
+    ssu_replay_lp_update(args, torch.cuda.current_stream(state.device).cuda_stream)
+    return out
+
+
+def mx8_quantize(src, codes=None, scales=None):
+    """MXFP8 (E4M3 elements, an E8M0 scale per 32 consecutive values) of a
+    contiguous float32 CUDA tensor whose size is a multiple of 32; the codes
+    take src's shape, the scales its shape with the last dimension / 32.
+    Returns (codes, scales)."""
+    if codes is None:
+        codes = torch.empty(src.shape, dtype=torch.uint8, device=src.device)
+    if scales is None:
+        shape = tuple(src.shape[:-1]) + (src.shape[-1] // 32,) if src.dim() else (0,)
+        scales = torch.empty(shape, dtype=torch.uint8, device=src.device)
+    dev = src.device
+    ssu_mx8_quantize(tensor_desc(src, dev), tensor_desc(codes, dev), tensor_desc(scales, dev),
+                     torch.cuda.current_stream(dev).cuda_stream)
+    return codes, scales
 
 
 # ---------------------------------------------------------------- state copies

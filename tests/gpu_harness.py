@@ -260,3 +260,76 @@ def replay_subcase(case, seqs):
     for k in ("state", "buf_x", "buf_dt", "buf_B"):
         sub[k] = np.asarray(case[k])[used]
     return sub, used
+
+
+# ---------------------------------------------------------------- MXFP8 read copy
+
+def with_copy(case, source=None):
+    """The case with an MXFP8 read copy of `source` (default: its own pool),
+    made by the oracle's quantizer."""
+    c = dict(case)
+    c["lp"], c["lp_scale"] = ssu_oracle.mx8_quantize(
+        np.asarray(case["state"] if source is None else source, np.float32))
+    return c
+
+
+def device_replay_lp(case, device="cuda:0"):
+    d = device_replay(case, device)
+    d["lp"] = torch.from_numpy(np.ascontiguousarray(case["lp"])).to(device)
+    d["lp_scale"] = torch.from_numpy(np.ascontiguousarray(case["lp_scale"])).to(device)
+    return d
+
+
+def run_gpu_replay_lp(case, d=None, device="cuda:0"):
+    """One ReplaySSM step with the read copy through the binding; returns host
+    copies of y, the pool, the buffers and the copy."""
+    if d is None:
+        d = device_replay_lp(case, device)
+    o = torch.full(np.shape(case["x"]), float("nan"), dtype=TORCH[case["io_dtype"]],
+                   device=device)
+    y = ssu.replay_lp_selective_state_update(
+        d["state"], d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["buf_x"], d["buf_dt"],
+        d["buf_B"], d["buf_len"], d["lp"], d["lp_scale"], z=d["z"], dt_bias=d["dt_bias"],
+        dt_softplus=case.get("dt_softplus", False), state_batch_indices=d["state_batch_indices"],
+        pad_slot_id=case.get("pad_slot_id", -1), out=o,
+        disable_state_update=case.get("disable_state_update", False))
+    assert y is o
+    torch.cuda.synchronize()
+    io, dtd = case["io_dtype"], case.get("dt_dtype", case["io_dtype"])
+    return {"y": host(y, io), "state": host(d["state"], "f32"), "buf_x": host(d["buf_x"], io),
+            "buf_dt": host(d["buf_dt"], dtd), "buf_B": host(d["buf_B"], io),
+            "lp": d["lp"].cpu().numpy(), "lp_scale": d["lp_scale"].cpu().numpy()}
+
+
+def compare_copy(case, got, ref, name=""):
+    """The read copy: slots the oracle does not write keep their bytes; a
+    written slot's copy is, byte for byte, the quantization of the state the
+    GPU stored (the codes are decided on the same fp32 values), and within one
+    E4M3 step of the oracle's copy (its state differs by rounding order)."""
+    written = ref["written"]
+    for k in ("lp", "lp_scale"):
+        assert np.array_equal(got[k][~written], np.asarray(case[k])[~written]), \
+            "%s: %s of a slot the oracle leaves alone changed" % (name, k)
+    if not written.any():
+        return 0
+    codes, scales = ssu_oracle.mx8_quantize(got["state"][written])
+    assert np.array_equal(got["lp_scale"][written], scales), "%s: scale bytes" % name
+    assert np.array_equal(got["lp"][written], codes), "%s: code bytes" % name
+    g = ssu_oracle.mx8_dequantize(got["lp"][written], got["lp_scale"][written]).astype(np.float64)
+    r = ssu_oracle.mx8_dequantize(ref["lp"][written], ref["lp_scale"][written]).astype(np.float64)
+    # the block scale X = 2^(byte - 127) of every element
+    sc = np.repeat(np.ldexp(1.0, ref["lp_scale"][written].astype(np.int64) - 127), 32, axis=-1)
+    # one E4M3 step: |v| / 8 for a normal value, 2^-9 X for a subnormal
+    assert (np.abs(g - r) <= np.abs(r) / 8 + sc * 2.0 ** -9 * 1.0001).all(), \
+        "%s: copy more than one E4M3 step from the oracle's" % name
+    return int((got["lp"][written] != ref["lp"][written]).sum())
+
+
+def check_replay_lp(case, name, device="cuda:0"):
+    ref = ssu_oracle.run_replay(case)
+    say("[gpu] %s: launching" % name)
+    got = run_gpu_replay_lp(case, device=device)
+    stats = compare_replay(case, got, ref, name)
+    stats["copy_mismatch"] = compare_copy(case, got, ref, name)
+    say("[gpu] %s: ok %s" % (name, {k: "%.3g" % v for k, v in stats.items()}))
+    return stats

@@ -39,7 +39,7 @@ def test_struct_layout_matches_header(tmp_path):
     makes of include/ssu.h."""
     structs = {"ssu_tensor_t": S.SsuTensor, "ssu_args_t": S.SsuArgs,
                "ssu_plan_desc_t": S.SsuPlanDesc, "ssu_plan_info_t": S.SsuPlanInfo,
-               "ssu_replay_args_t": S.SsuReplayArgs,
+               "ssu_replay_args_t": S.SsuReplayArgs, "ssu_replay_lp_args_t": S.SsuReplayLpArgs,
                "ssu_conv_shift_args_t": S.SsuConvShiftArgs,
                "ssu_ssd_args_t": S.SsuSsdArgs}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ssu.h"', "int main(void) {"]
@@ -448,6 +448,86 @@ def shift(state, src, dst, bias, layout=S.CONV_TOKEN_MAJOR):
     a.state, a.layout, a.src_block, a.dst_block, a.bias = state, layout, src, dst, bias
     st = S._lib.ssu_conv_state_shift(ctypes.byref(a), None)
     return st, S.ssu_last_error()
+
+
+# ---------------------------------------------------------------- MXFP8 read copy
+
+
+def replay_lp_args(rows=0, N=128, sd=S.F32, slots=8, H=8, P=16):
+    r = S.SsuReplayLpArgs()
+    r.base = replay_args(rows=rows, N=N, slots=slots, H=H, P=P)
+    r.base.base.state = tdesc((slots, H, P, N), sd)
+    r.lp = tdesc((slots, H, P, N), S.U8)
+    r.lp_scale = tdesc((slots, H, P, N // 32), S.U8)
+    return r
+
+
+def replay_lp(r):
+    st = S._lib.ssu_replay_lp_update(ctypes.byref(r), None)
+    return st, S.ssu_last_error()
+
+
+def test_replay_lp_empty_is_ok_without_launch():
+    assert replay_lp(replay_lp_args()) == (S.OK, "")
+
+
+def test_replay_lp_errors():
+    assert S._lib.ssu_replay_lp_update(None, None) == S.ERR_VALUE
+    st, msg = replay_lp(replay_lp_args(sd=S.BF16))
+    assert st == S.ERR_NOT_IMPLEMENTED and "f32" in msg
+    r = replay_lp_args()
+    r.lp = S.SsuTensor()
+    st, msg = replay_lp(r)
+    assert st == S.ERR_VALUE and "required" in msg
+    r = replay_lp_args()
+    r.lp = tdesc((8, 8, 16, 128), S.I32)
+    st, msg = replay_lp(r)
+    assert st == S.ERR_VALUE and "u8" in msg
+    r = replay_lp_args()
+    r.lp = tdesc((8, 8, 16, 64), S.U8)
+    st, msg = replay_lp(r)
+    assert st == S.ERR_VALUE and "lp must be" in msg
+    r = replay_lp_args()
+    r.lp_scale = tdesc((8, 8, 16, 8), S.U8)
+    st, msg = replay_lp(r)
+    assert st == S.ERR_VALUE and "lp_scale must be" in msg
+    r = replay_lp_args()
+    r.lp = tdesc((8, 8, 16, 128), S.U8, strides=(8 * 16 * 128, 16 * 128, 1, 16))
+    st, msg = replay_lp(r)
+    assert st == S.ERR_VALUE and "contiguous" in msg
+    r = replay_lp_args()
+    r.lp = tdesc((8, 8, 16, 128), S.U8, ptr=FAKE + 2)
+    st, msg = replay_lp(r)
+    assert st == S.ERR_VALUE and "aligned" in msg
+    # the replay checks still apply
+    r = replay_lp_args()
+    r.base.buf_len = S.SsuTensor()
+    st, msg = replay_lp(r)
+    assert st == S.ERR_VALUE and "buf_len" in msg
+
+
+def quantize(src, codes, scales):
+    st = S._lib.ssu_mx8_quantize(ctypes.byref(src), ctypes.byref(codes), ctypes.byref(scales), None)
+    return st, S.ssu_last_error()
+
+
+def test_mx8_quantize_empty_and_errors():
+    assert quantize(tdesc((0,), S.F32), tdesc((0,), S.U8), tdesc((0,), S.U8)) == (S.OK, "")
+    assert quantize(tdesc((4, 0, 32), S.F32), tdesc((0,), S.U8), tdesc((0,), S.U8))[0] == S.OK
+    assert S._lib.ssu_mx8_quantize(None, None, None, None) == S.ERR_VALUE
+    st, msg = quantize(tdesc((48,), S.F32), tdesc((48,), S.U8), tdesc((1,), S.U8))
+    assert st == S.ERR_VALUE and "multiple of 32" in msg
+    st, msg = quantize(tdesc((64,), S.BF16), tdesc((64,), S.U8), tdesc((2,), S.U8))
+    assert st == S.ERR_VALUE and "f32" in msg
+    st, msg = quantize(tdesc((64,), S.F32), tdesc((32,), S.U8), tdesc((2,), S.U8))
+    assert st == S.ERR_VALUE and "codes" in msg
+    st, msg = quantize(tdesc((64,), S.F32), tdesc((64,), S.U8), tdesc((3,), S.U8))
+    assert st == S.ERR_VALUE and "scales" in msg
+    st, msg = quantize(tdesc((2, 64), S.F32, strides=(128, 1)), tdesc((128,), S.U8),
+                       tdesc((4,), S.U8))
+    assert st == S.ERR_VALUE and "contiguous" in msg
+    st, msg = quantize(tdesc((64,), S.F32, ptr=FAKE + 4), tdesc((64,), S.U8), tdesc((2,), S.U8))
+    assert st == S.ERR_VALUE and "aligned" in msg
 
 
 def test_conv_state_shift_empty_and_errors():

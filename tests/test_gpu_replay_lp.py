@@ -1,0 +1,234 @@
+"""ReplaySSM decode with an MXFP8 read copy of the checkpoint
+(ssu_replay_lp_update, ssu_mx8_quantize) against the CPU oracle (ReplaySSM
+article, section "效果与代价"; OCP Microscaling v1.0, MXFP8 E4M3).
+
+Output-only steps read the copy, so y is compared with the oracle run on the
+same copy bytes; a flush stores the fp32 checkpoint and rewrites the copy,
+whose bytes are the quantization of the stored state, exactly."""
+import numpy as np
+import pytest
+import torch
+
+import gpu_harness as G
+import workloads as W
+from oracle import ssu_oracle
+import mamba_selective_state_amd as ssu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    torch.cuda.init()
+
+
+# ---------------------------------------------------------------- quantizer
+
+def gpu_quantize(x):
+    t = torch.from_numpy(np.ascontiguousarray(x, np.float32)).to("cuda:0")
+    codes, scales = ssu.mx8_quantize(t)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), scales.cpu().numpy()
+
+
+def special_blocks():
+    """Blocks that exercise every branch of the conversion: ties between
+    neighbouring E4M3 values (normal and subnormal, at several scales),
+    saturation, zeros, NaN, fp32 subnormals (the clamped scale exponent) and
+    the largest fp32 magnitudes."""
+    rows = []
+    for k in (-20, -7, 0, 5, 100):
+        # amax 2^(8 + k) gives the scale 2^k exactly
+        X = 2.0 ** k
+        ties = [X * 256.0]
+        for m in range(8):                       # normal ties in [1, 2) * 2^e
+            for e in (-6, 0, 3, 7):
+                ties.append(X * 2.0 ** e * (1 + (m + 0.5) / 8))
+        for m in range(8):                       # subnormal ties (m + 0.5) 2^-9
+            ties.append(X * (m + 0.5) * 2.0 ** -9)
+        ties = np.array(ties, np.float64)
+        sgn = np.where(np.arange(ties.size) % 3 == 0, -1.0, 1.0)
+        v = (ties * sgn).astype(np.float32)
+        v = np.concatenate([v, np.zeros((-v.size) % 32, np.float32)])
+        v[1 + 32 * np.arange(v.size // 32)] = X * 256.0  # each block keeps amax 2^(8+k)
+        rows.append(v.reshape(-1, 32))
+    sat = np.full(32, 1.0, np.float32)
+    sat[0] = 1.99  # scaled values above 448 saturate
+    sat[1] = -1.9
+    rows.append(sat[None])
+    rows.append(np.zeros((1, 32), np.float32))
+    nan = np.linspace(-1, 1, 32).astype(np.float32)
+    nan[4] = np.nan
+    rows.append(nan[None])
+    tiny = (np.arange(32) * 1e-41).astype(np.float32)  # fp32 subnormals: scale 2^-126
+    rows.append(tiny[None])
+    huge = np.full(32, 3.0e38, np.float32)             # the largest scale an fp32 block reaches
+    rows.append(huge[None])
+    return np.concatenate(rows).ravel()
+
+
+def test_mx8_quantize_special_values():
+    x = special_blocks()
+    G.say("[gpu] mx8 quantize, %d special values: launching" % x.size)
+    codes, scales = gpu_quantize(x)
+    rc, rs = ssu_oracle.mx8_quantize(x)
+    assert np.array_equal(scales, rs)
+    assert np.array_equal(codes, rc)
+    G.say("[gpu] mx8 quantize special: ok")
+
+
+@pytest.mark.parametrize("nblocks", [1, 3, 64, 4095, 20001])
+def test_mx8_quantize_random(nblocks):
+    rng = np.random.default_rng(nblocks)
+    x = (rng.standard_normal(nblocks * 32) *
+         np.repeat(np.exp2(rng.integers(-30, 30, nblocks)), 32)).astype(np.float32)
+    G.say("[gpu] mx8 quantize %d blocks: launching" % nblocks)
+    codes, scales = gpu_quantize(x)
+    rc, rs = ssu_oracle.mx8_quantize(x)
+    assert np.array_equal(scales, rs) and np.array_equal(codes, rc)
+
+
+def test_mx8_quantize_pool_size():
+    """More blocks than the grid has lanes for (the grid-stride loop runs more
+    than once) with a ragged tail; the replay benchmark's pool is this
+    large."""
+    nblocks = 65536 * 64 + 17
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal(nblocks * 32, dtype=np.float32)
+    G.say("[gpu] mx8 quantize %d blocks: launching" % nblocks)
+    codes, scales = gpu_quantize(x)
+    rc, rs = ssu_oracle.mx8_quantize(x)
+    assert np.array_equal(scales, rs)
+    assert np.array_equal(codes, rc)
+    G.say("[gpu] mx8 quantize pool size: ok")
+
+
+# ---------------------------------------------------------------- replay
+
+CASES = [
+    # (io, L, dt per head, dstate, dim)
+    ("bf16", 16, False, 128, 64),
+    ("bf16", 4, True, 128, 40),
+    ("f16", 8, False, 64, 64),
+    ("f32", 5, False, 32, 28),
+    ("bf16", 16, False, 256, 64),
+    ("f16", 33, True, 64, 64),
+]
+
+
+@pytest.mark.parametrize("io,L,per_head,N,P", CASES,
+                         ids=["%s-L%d-%s-n%d-p%d" % (a, b, "ph" if c else "full", d, e)
+                              for a, b, c, d, e in CASES])
+def test_replay_lp_small(io, L, per_head, N, P):
+    c = W.replay(seed=40 + L + N, batch=24, heads=8, dim=P, dstate=N, groups=2, slots=40, L=L,
+                 io=io, dt_per_head=per_head)
+    c["buf_len"][:] = np.arange(24) % L
+    c["buf_len"][:3] = [0, L - 1, L // 2]
+    G.check_replay_lp(G.with_copy(c), "replay lp %s L=%d n=%d" % (io, L, N))
+
+
+def test_replay_lp_reads_the_copy():
+    """A copy that differs from the checkpoint (here: of half the pool): the
+    output-only steps follow the copy, the flushes the checkpoint."""
+    c = W.replay(seed=51, batch=32, heads=8, dim=64, dstate=128, groups=2, slots=48, L=8)
+    c["buf_len"][:] = np.arange(32) % 8
+    half = np.asarray(c["state"], np.float32) * 0.5
+    st = G.check_replay_lp(G.with_copy(c, half), "replay lp, stale copy")
+    # and the result differs from the one read from the checkpoint
+    plain = ssu_oracle.run_replay(c)
+    lp = ssu_oracle.run_replay(G.with_copy(c, half))
+    assert not np.array_equal(plain["y"], lp["y"])
+    assert st["y_err"] <= st["y_tol"]
+
+
+def test_replay_lp_pad_and_disable():
+    c = W.replay(seed=52, batch=12, heads=8, dim=64, dstate=128, groups=2, slots=20, L=4)
+    tab = c["state_batch_indices"].copy()
+    tab[[1, 5]] = -1
+    c["state_batch_indices"] = tab
+    c["buf_len"][:] = [3, 3, 1, 3, 0, 2, 3, 1, 2, 3, 0, 3]
+    c = G.with_copy(c)
+    G.check_replay_lp(c, "replay lp with pad rows")
+    G.check_replay_lp(dict(c, disable_state_update=True), "replay lp disabled")
+
+
+def test_replay_lp_out_of_range_counts():
+    L = 8
+    c = G.with_copy(W.replay(seed=53, batch=12, heads=8, dim=64, dstate=128, groups=2, slots=20,
+                             L=L))
+    bad = [2, 7, 9]
+    c["buf_len"][bad] = [L, -1, L + 5]
+    G.say("[gpu] replay lp out-of-range counts: launching")
+    got = G.run_gpu_replay_lp(c)
+    assert np.isnan(G.brute64.to_f64(got["y"][bad], c["io_dtype"])).all()
+    tab = np.asarray(c["state_batch_indices"])
+    for k in ("state", "buf_x", "buf_dt", "buf_B", "lp", "lp_scale"):
+        assert np.array_equal(got[k][tab[bad]], np.asarray(c[k])[tab[bad]]), k
+
+
+def test_replay_lp_sequence_of_steps():
+    """Twenty steps of a caller's loop (buf_len advanced, reset after a fold),
+    the copy carried on the GPU: every step's y and the final pool, buffers
+    and copy equal the oracle's chain."""
+    L = 4
+    c = G.with_copy(W.replay(seed=54, batch=16, heads=8, dim=64, dstate=64, groups=2, slots=24,
+                             L=L))
+    d = G.device_replay_lp(c)
+    rng = np.random.default_rng(55)
+    cur = dict(c)
+    for step in range(20):
+        if step:
+            fresh = W.replay(seed=100 + step, batch=16, heads=8, dim=64, dstate=64, groups=2,
+                             slots=24, L=L)
+            for k in ("x", "dt", "B", "C", "z"):
+                cur[k] = fresh[k]
+                dtype = c.get("dt_dtype", c["io_dtype"]) if k == "dt" else c["io_dtype"]
+                d[k] = G.dev(fresh[k], dtype, "cuda:0")
+        ref = ssu_oracle.run_replay(cur)
+        got = G.run_gpu_replay_lp(cur, d=d)
+        G.compare_replay(cur, got, ref, "lp step %d" % step)
+        G.compare_copy(cur, got, ref, "lp step %d" % step)
+        # the next step starts from what the GPU holds (the oracle's state
+        # differs by rounding order; the copy is the GPU's, exact)
+        for k in ("state", "buf_x", "buf_dt", "buf_B", "lp", "lp_scale"):
+            cur[k] = got[k]
+        blen = np.asarray(cur["buf_len"]) + 1
+        blen[blen == L] = 0
+        skip = rng.random(16) < 0.2  # some sequences idle a step (their count stays)
+        blen[skip] = np.asarray(cur["buf_len"])[skip]
+        cur["buf_len"] = blen.astype(np.int32)
+        d["buf_len"] = torch.from_numpy(cur["buf_len"]).to("cuda:0")
+    G.say("[gpu] replay lp 20 steps: ok")
+
+
+def test_replay_lp_full_workload():
+    """The replay benchmark's workload with its copy made on the GPU: the copy
+    equals the oracle's quantization of the pool; untouched slots keep pool
+    and copy; sampled sequences against the oracle."""
+    c = W.replay()
+    G.say("[gpu] replay lp full: launching")
+    d = G.device_replay(c)
+    d["lp"], d["lp_scale"] = ssu.mx8_quantize(d["state"])
+    torch.cuda.synchronize()
+    lp0, lps0 = d["lp"].cpu().numpy(), d["lp_scale"].cpu().numpy()
+    rc, rs = ssu_oracle.mx8_quantize(np.asarray(c["state"], np.float32))
+    assert np.array_equal(lps0, rs) and np.array_equal(lp0, rc)
+    c = dict(c, lp=lp0, lp_scale=lps0)
+    got = G.run_gpu_replay_lp(c, d=d)
+    tab = np.asarray(c["state_batch_indices"])
+    flush = np.asarray(c["buf_len"]) + 1 == c["L"]
+    written = np.zeros(c["state"].shape[0], bool)
+    written[tab[flush]] = True
+    for k in ("state", "lp", "lp_scale"):
+        assert np.array_equal(got[k][~written], np.asarray(c[k])[~written]), k
+    seqs = sorted(set([0, 255] + list(np.flatnonzero(flush)[:2]) + list(np.flatnonzero(~flush)[:3])))
+    sub, used = G.replay_subcase(c, seqs)
+    sub["lp"], sub["lp_scale"] = lp0[used], lps0[used]
+    ref = ssu_oracle.run_replay(sub)
+    sub_got = {k: got[k][used] for k in ("state", "buf_x", "buf_dt", "buf_B", "lp", "lp_scale")}
+    sub_got["y"] = got["y"][seqs]
+    stats = G.compare_replay(sub, sub_got, ref, "replay lp full")
+    G.compare_copy(sub, sub_got, ref, "replay lp full")
+    G.say("[gpu] replay lp full: ok %s" % {k: "%.3g" % v for k, v in stats.items()})
