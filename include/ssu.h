@@ -232,7 +232,7 @@ SSU_API ssu_status_t ssu_replay_update(const ssu_replay_args_t *args, void *stre
 SSU_API ssu_status_t ssu_replay_spec_update(const ssu_replay_args_t *args, void *stream);
 
 /* ---- ReplaySSM with a low-precision read copy (ReplaySSM article, lpnh.cn,
- * section "效果与代价": the checkpoint is a read-mostly value that a
+ * section "数据与边界": the checkpoint is a read-mostly value that a
  * low-precision copy can stand in for on the steps that only read it).
  * Format: OCP Microscaling (MX) v1.0, MXFP8 with E4M3 elements: every 32
  * consecutive dstate values of a checkpoint row form a block with one E8M0

@@ -377,7 +377,7 @@ def replay_lp_selective_state_update(state, x, dt, A, B, C, D, buf_x, buf_dt, bu
                                      state_batch_indices=None, pad_slot_id=-1, out=None,
                                      disable_state_update=False):
     """replay_selective_state_update with an MXFP8 copy of the f32 checkpoint
-    (ReplaySSM article, section "效果与代价"; OCP MX v1.0 MXFP8 E4M3):
+    (ReplaySSM article, section "数据与边界"; OCP MX v1.0 MXFP8 E4M3):
     output-only steps read lp (uint8 E4M3 codes, [slots, heads, dim, dstate])
     times lp_scale (uint8 E8M0, [slots, heads, dim, dstate / 32]) instead of
     the checkpoint; a fold stores the checkpoint and rewrites both. Returns y."""

@@ -1,6 +1,6 @@
 """ReplaySSM decode with an MXFP8 read copy of the checkpoint
 (ssu_replay_lp_update, ssu_mx8_quantize) against the CPU oracle (ReplaySSM
-article, section "效果与代价"; OCP Microscaling v1.0, MXFP8 E4M3).
+article, section "数据与边界"; OCP Microscaling v1.0, MXFP8 E4M3).
 
 Output-only steps read the copy, so y is compared with the oracle run on the
 same copy bytes; a flush stores the fp32 checkpoint and rewrites the copy,
