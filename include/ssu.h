@@ -344,14 +344,14 @@ typedef struct {
     ssu_tensor_t A;                  /* [heads] f32 */
     ssu_tensor_t B, C;               /* [tokens, groups, dstate], x dtype, rows 16-byte aligned */
     ssu_tensor_t D;                  /* [heads] f32, or absent */
-    ssu_tensor_t z;                  /* like x (dim contiguous), or absent */
+    ssu_tensor_t z;                  /* like x (dim contiguous, rows 16-byte aligned), or absent */
     ssu_tensor_t dt_bias;            /* [heads] f32, or absent */
     ssu_tensor_t cu_seqlens;         /* [batch + 1] i32 / i64, or absent (not read) */
     ssu_tensor_t cu_chunk_seqlens;   /* [nchunks + 1] i32 / i64 (device) */
     ssu_tensor_t last_chunk_indices; /* [batch] i32 / i64 (device) */
     ssu_tensor_t seq_idx;            /* [nchunks] i32 / i64 (device) */
     ssu_tensor_t initial_states;     /* [batch, heads, dim, dstate] contiguous, the state dtype, or absent */
-    ssu_tensor_t out;                /* like x (dim contiguous): y, written */
+    ssu_tensor_t out;                /* like x (dim contiguous, rows 16-byte aligned): y, written */
     ssu_tensor_t states;             /* [batch or nchunks, heads, dim, dstate] contiguous: written */
     int64_t chunk_size;
     int32_t dt_softplus;

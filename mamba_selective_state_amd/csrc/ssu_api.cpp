@@ -656,11 +656,11 @@ ssu_status_t ssu_ssd_prefill(const ssu_ssd_args_t *a, void *workspace, int64_t w
         return s;
     if ((s = ssd_rows("C", a->C, T, G, N, x.dtype, true, &sp.C_st, &sp.C_sg)) != SSU_OK)
         return s;
-    if (present(a->z) && (s = ssd_rows("z", a->z, T, H, P, x.dtype, false, &sp.z_st, &sp.z_sh)) != SSU_OK)
+    if (present(a->z) && (s = ssd_rows("z", a->z, T, H, P, x.dtype, true, &sp.z_st, &sp.z_sh)) != SSU_OK)
         return s;
     if (!present(a->out))
         return fail(SSU_ERR_VALUE, "out is required");
-    if ((s = ssd_rows("out", a->out, T, H, P, x.dtype, false, &sp.out_st, &sp.out_sh)) != SSU_OK)
+    if ((s = ssd_rows("out", a->out, T, H, P, x.dtype, true, &sp.out_st, &sp.out_sh)) != SSU_OK)
         return s;
     const ssu_tensor_t &dt = a->dt;
     if (!present(dt) || dt.ndim != 2 || dt.size[0] != T || dt.size[1] != H || (dt.dtype != SSU_F32 && dt.dtype != x.dtype))
