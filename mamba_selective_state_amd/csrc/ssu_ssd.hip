@@ -234,12 +234,12 @@ __device__ __forceinline__ int32_t xcd_grouped(int32_t id, int32_t n) {
 
 // y_t = exp(A_t) C_t . S_in + sum_{s<=t} (C_t . B_s) exp(A_t - A_s) dt'_s x_s
 //       + D x_t, gated by silu(z_t);   A = the decay cumsum of the chunk.
-// Per (chunk, head) 8 waves; rows t in 16-row tiles (wave w takes tiles w and
+// One workgroup of 8 waves per (chunk, group, block of kScanHeads heads of
+// the group). The chunk's B rows are staged in LDS once and each wave's C
+// operands stay in registers for all its heads; per head, x^T, the entering
+// state and the cumsums are staged in LDS, the next head's requested while
+// the current one computes. Rows t in 16-row tiles (wave w takes tiles w and
 // 15-w: equal work under the causal mask), columns s in 32-column blocks J.
-// The chunk's B rows, x^T, the entering state and the cumsums are staged in
-// LDS once (whole-word stores), so after one barrier the waves run with no
-// further barriers; each wave's C rows, x rows and gate are requested with
-// the staging.
 // Both products are formed transposed, so that a lane owns one token t:
 //   (B_J C^T)[s][t]: the lane holds t and the 8 columns s = 32J + 4g + i,
 //   32J + 16 + 4g + i (g = lane / 16, i < 4), which after scaling is the
@@ -255,108 +255,81 @@ __device__ __forceinline__ int32_t xcd_grouped(int32_t id, int32_t n) {
 // under the causal mask.
 constexpr int kScanThreads = 512;
 constexpr int kScanTiles = 2;  // 16-token tiles per wave
+constexpr int kScanHeads = 4;  // heads per workgroup
 
 template <typename IT, int N>
 __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(const SsdParams sp) {
     using M = Mfma<IT>;
     using V = typename M::V;
-    constexpr int KN = N / 32;                  // k steps over dstate
+    constexpr int KN = N / 32;                      // k steps over dstate
     constexpr int kSinSeg = kP * N / kScanThreads;  // entering-state elements a lane stages
+    constexpr int kRowPieces = N / 8;               // 16-byte pieces of a B row
+    constexpr int kBPass = kL * kRowPieces / kScanThreads;
     static_assert(kSinSeg == 8 || kSinSeg == 16, "whole 16-byte LDS stores");
     static_assert(kP == 64, "a lane's 16 consecutive p per g");
     __shared__ float acum_s[kL], dtp_s[kL];
     __shared__ __attribute__((aligned(16))) float q_s[kL];          // column factors
-    __shared__ __attribute__((aligned(16))) IT Xs[kP][kL + kPad];   // x^T: [p][s]
+    // x^T: [p][s]; rows of kL + 4 elements (read 8 bytes at a time) spread the
+    // transposed 4-byte stores of one wave over the banks
+    __shared__ __attribute__((aligned(16))) IT Xs[kP][kL + 4];
     __shared__ __attribute__((aligned(16))) IT Bs[kL][N + kPad];    // B rows [s][n]
     __shared__ __attribute__((aligned(16))) IT Sin[kP][N + kPad];   // entering state [p][n]
 
+    const int ngroups = static_cast<int>(sp.H / sp.hpg);
+    const int nhb = (sp.hpg + kScanHeads - 1) / kScanHeads;
     const int32_t wg = xcd_grouped(blockIdx.x, gridDim.x);
-    const int64_t c = wg / sp.H;
-    const int h = static_cast<int>(wg % sp.H);
-    const int g = h / sp.hpg;
+    const int64_t c = wg / (ngroups * nhb);
+    const int g = (wg / nhb) % ngroups;
+    const int hb = wg % nhb;
+    const int h0 = g * sp.hpg + hb * kScanHeads;
+    const int nh = sp.hpg - hb * kScanHeads < kScanHeads ? sp.hpg - hb * kScanHeads : kScanHeads;
     const int t = threadIdx.x;
     int64_t t0;
     int len;
     chunk_range(sp, c, &t0, &len);
     if (len == 0)
         return;  // uniform
-    const int64_t wrow = (c * sp.H + h) * kL;
     const int lane = t & 63, wv = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform per wave
     const int r = lane & 15, gq = lane >> 4, g4 = 4 * gq, k8 = 8 * gq;
     const int ntiles = (len + 15) / 16;
     const int rts[kScanTiles] = {wv, 15 - wv};
-    const IT *zs = static_cast<const IT *>(sp.z);
-    // the wave's own global inputs, requested with the staging: for each tile,
-    // the C row of the lane's token (B operands of B_J C^T, of S_in C^T) and
-    // its 16 x and z values p = 16 gq ..
-    V ac[kScanTiles][KN], xo[kScanTiles][2], zo[kScanTiles][2];
-#pragma unroll
-    for (int i = 0; i < kScanTiles; i++) {
-        const int tr = 16 * rts[i] + r;
-        const int64_t tok = t0 + (tr < len ? tr : len - 1);
-        const IT *crow = static_cast<const IT *>(sp.C) + g * sp.C_sg + tok * sp.C_st;
-#pragma unroll
-        for (int k = 0; k < KN; k++)
-            ac[i][k] = *reinterpret_cast<const V *>(crow + 32 * k + k8);
-        const IT *xrow = static_cast<const IT *>(sp.x) + tok * sp.x_st + h * sp.x_sh + 16 * gq;
-        const IT *zrow = zs + tok * sp.z_st + h * sp.z_sh + 16 * gq;
-#pragma unroll
-        for (int k = 0; k < 2; k++) {
-            xo[i][k] = *reinterpret_cast<const V *>(xrow + 8 * k);
-            zo[i][k] = zs ? *reinterpret_cast<const V *>(zrow + 8 * k) : V{};
-        }
-    }
-    if (t < kL) {
-        // and the column factor of token t: exp(A_J - A_t) dt'_t, J = t / 32
-        const float at = sp.ws_acum[wrow + t], dt = sp.ws_dtp[wrow + t];
-        acum_s[t] = at;
-        dtp_s[t] = dt;
-        q_s[t] = exp_f(sp.ws_acum[wrow + (t | 31)] - at) * dt;
-    }
-    {
-        // B: 16-byte pieces, consecutive lanes along a row (rows past the
-        // chunk repeat its last row): kL * N / 8 pieces, kBPass per lane
-        constexpr int kRowPieces = N / 8;
-        constexpr int kBPass = kL * kRowPieces / kScanThreads;
-        const IT *Bg = static_cast<const IT *>(sp.B) + g * sp.B_sg;
-        V bv[kBPass];
-#pragma unroll
-        for (int k = 0; k < kBPass; k++) {
-            const int piece = k * kScanThreads + t, srow = piece / kRowPieces;
-            bv[k] = *reinterpret_cast<const V *>(Bg + (t0 + (srow < len ? srow : len - 1)) * sp.B_st +
-                                                 (piece % kRowPieces) * 8);
-        }
-        // x^T: lane t takes the 16-byte dim piece t % 8 of tokens 2j, 2j + 1,
-        // j = t / 8 and j + 64 (eight lanes cover a token pair's rows)
-        const int pc = 8 * (t & 7);
-        const IT *xs = static_cast<const IT *>(sp.x) + h * sp.x_sh + pc;
+
+    // per head: x^T pieces (lane t: the 16-byte dim piece t % 8 of tokens 2j,
+    // 2j + 1, j = t / 8 and j + 64), the entering state (kSinSeg consecutive
+    // elements) and, for t < 256, token t's cumsum, dt' and block-end cumsum
+    struct HeadIn {
         V xv[2][2];
+        f32x4 sv[kSinSeg / 4];
+        float at, dt, aj;
+    };
+    const int pc = 8 * (t & 7);
+    auto load_head = [&](int h, HeadIn &in) {
+        const IT *xs = static_cast<const IT *>(sp.x) + h * sp.x_sh + pc;
 #pragma unroll
         for (int u = 0; u < 2; u++)
 #pragma unroll
             for (int v = 0; v < 2; v++) {
                 const int tok = 2 * ((t >> 3) + 64 * u) + v;
-                xv[u][v] = *reinterpret_cast<const V *>(xs + (t0 + (tok < len ? tok : 0)) * sp.x_st);
+                in.xv[u][v] = *reinterpret_cast<const V *>(xs + (t0 + (tok < len ? tok : 0)) * sp.x_st);
             }
-        // entering state: lane t takes kSinSeg consecutive elements
         const float *sin = sp.ws_state + (c * sp.H + h) * static_cast<int64_t>(kP * N) + t * kSinSeg;
-        f32x4 sv[kSinSeg / 4];
 #pragma unroll
         for (int k = 0; k < kSinSeg / 4; k++)
-            sv[k] = *reinterpret_cast<const f32x4 *>(sin + 4 * k);
-
-#pragma unroll
-        for (int k = 0; k < kBPass; k++) {
-            const int piece = k * kScanThreads + t;
-            *reinterpret_cast<V *>(&Bs[piece / kRowPieces][(piece % kRowPieces) * 8]) = bv[k];
-        }
+            in.sv[k] = *reinterpret_cast<const f32x4 *>(sin + 4 * k);
+        const int64_t wrow = (c * sp.H + h) * kL;
+        const int tc = t & (kL - 1);
+        in.at = sp.ws_acum[wrow + tc];
+        in.dt = sp.ws_dtp[wrow + tc];
+        in.aj = sp.ws_acum[wrow + (tc | 31)];
+    };
+    auto store_head = [&](const HeadIn &in) {
 #pragma unroll
         for (int u = 0; u < 2; u++) {
             const int j2 = 2 * ((t >> 3) + 64 * u);
 #pragma unroll
             for (int e = 0; e < 8; e++) {
-                const IT lo = j2 < len ? xv[u][0][e] : static_cast<IT>(0.0f);
-                const IT hi = j2 + 1 < len ? xv[u][1][e] : static_cast<IT>(0.0f);
+                const IT lo = j2 < len ? in.xv[u][0][e] : static_cast<IT>(0.0f);
+                const IT hi = j2 + 1 < len ? in.xv[u][1][e] : static_cast<IT>(0.0f);
                 *reinterpret_cast<uint32_t *>(&Xs[pc + e][j2]) =
                     static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
                     (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
@@ -368,113 +341,176 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(const SsdP
             V w;
 #pragma unroll
             for (int e = 0; e < 8; e++)
-                w[e] = static_cast<IT>(sv[2 * k + e / 4][e % 4]);
+                w[e] = static_cast<IT>(in.sv[2 * k + e / 4][e % 4]);
             *reinterpret_cast<V *>(&Sin[sp0][sn0 + 8 * k]) = w;
         }
+        if (t < kL) {
+            acum_s[t] = in.at;
+            dtp_s[t] = in.dt;
+            q_s[t] = exp_f(in.aj - in.at) * in.dt;  // exp(A_J - A_t) dt'_t, J = t / 32
+        }
+    };
+
+    // shared by the heads: B rows (16-byte pieces, consecutive lanes along a
+    // row; rows past the chunk repeat its last row) and the C operands
+    {
+        const IT *Bg = static_cast<const IT *>(sp.B) + g * sp.B_sg;
+        V bv[kBPass];
+#pragma unroll
+        for (int k = 0; k < kBPass; k++) {
+            const int piece = k * kScanThreads + t, srow = piece / kRowPieces;
+            bv[k] = *reinterpret_cast<const V *>(Bg + (t0 + (srow < len ? srow : len - 1)) * sp.B_st +
+                                                 (piece % kRowPieces) * 8);
+        }
+        HeadIn first;
+        load_head(h0, first);
+#pragma unroll
+        for (int k = 0; k < kBPass; k++) {
+            const int piece = k * kScanThreads + t;
+            *reinterpret_cast<V *>(&Bs[piece / kRowPieces][(piece % kRowPieces) * 8]) = bv[k];
+        }
+        store_head(first);
+    }
+    V ac[kScanTiles][KN];  // the C row of the lane's token in each tile
+#pragma unroll
+    for (int i = 0; i < kScanTiles; i++) {
+        const int tr = 16 * rts[i] + r;
+        const int64_t tok = t0 + (tr < len ? tr : len - 1);
+        const IT *crow = static_cast<const IT *>(sp.C) + g * sp.C_sg + tok * sp.C_st;
+#pragma unroll
+        for (int k = 0; k < KN; k++)
+            ac[i][k] = *reinterpret_cast<const V *>(crow + 32 * k + k8);
     }
     __syncthreads();
 
     IT *outp = static_cast<IT *>(sp.out);
-    const float dh = sp.D ? sp.D[h * sp.D_sh] : 0.0f;
+    const IT *zs = static_cast<const IT *>(sp.z);
     const int pr = 16 * (r >> 2) + (r & 3);  // p of MFMA row r in p tile 0 (+ 4 pt)
 
+    for (int hk = 0; hk < nh; hk++) {
+        const int h = h0 + hk;
+        HeadIn next;
+        if (hk + 1 < nh)
+            load_head(h + 1, next);  // in flight during this head
+        // this head's x and z of the lane's tokens (16 consecutive p), for the output
+        V xo[kScanTiles][2], zo[kScanTiles][2];
 #pragma unroll
-    for (int i = 0; i < kScanTiles; i++) {
-        const int rt = rts[i];
-        if (rt >= ntiles)
-            continue;  // uniform per wave
-        const int tt = 16 * rt + r;  // this lane's token in the chunk
-        const float at = acum_s[tt];
-        // the entering state's contribution, y^T = S_in C^T, scaled by exp(A_t)
-        f32x4 y[kP / 16];
+        for (int i = 0; i < kScanTiles; i++) {
+            const int tr = 16 * rts[i] + r;
+            const int64_t tok = t0 + (tr < len ? tr : len - 1);
+            const IT *xrow = static_cast<const IT *>(sp.x) + tok * sp.x_st + h * sp.x_sh + 16 * gq;
+            const IT *zrow = zs + tok * sp.z_st + h * sp.z_sh + 16 * gq;
 #pragma unroll
-        for (int pt = 0; pt < kP / 16; pt++) {
-            f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int k = 0; k < KN; k++)
-                a = M::run(*reinterpret_cast<const V *>(&Sin[pr + 4 * pt][32 * k + k8]), ac[i][k], a);
-            y[pt] = a;
-        }
-        {
-            const float rs = exp_f(at);
-#pragma unroll
-            for (int pt = 0; pt < kP / 16; pt++)
-#pragma unroll
-                for (int ii = 0; ii < 4; ii++)
-                    y[pt][ii] *= rs;
-        }
-        // (B_J C^T) for the lane's token and columns; block J + 1's product is
-        // formed while block J's is scaled and applied (MFMA and VALU overlap)
-        auto bc = [&](int J, f32x4 &dl, f32x4 &dh) {
-            dl = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            dh = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int k = 0; k < KN; k++) {
-                dl = M::run(*reinterpret_cast<const V *>(&Bs[32 * J + r][32 * k + k8]), ac[i][k], dl);
-                dh = M::run(*reinterpret_cast<const V *>(&Bs[32 * J + 16 + r][32 * k + k8]), ac[i][k], dh);
+            for (int k = 0; k < 2; k++) {
+                xo[i][k] = *reinterpret_cast<const V *>(xrow + 8 * k);
+                zo[i][k] = zs ? *reinterpret_cast<const V *>(zrow + 8 * k) : V{};
             }
-        };
-        auto apply = [&](int J, const V &a) {
-            const int s_lo = 32 * J + g4;
+        }
+        const float dh = sp.D ? sp.D[h * sp.D_sh] : 0.0f;
+
+#pragma unroll
+        for (int i = 0; i < kScanTiles; i++) {
+            const int rt = rts[i];
+            if (rt >= ntiles)
+                continue;  // uniform per wave
+            const int tt = 16 * rt + r;  // this lane's token in the chunk
+            const float at = acum_s[tt];
+            // the entering state's contribution, y^T = S_in C^T, scaled by exp(A_t)
+            f32x4 y[kP / 16];
 #pragma unroll
             for (int pt = 0; pt < kP / 16; pt++) {
-                const uint2 lo = *reinterpret_cast<const uint2 *>(&Xs[pr + 4 * pt][s_lo]);
-                const uint2 hi = *reinterpret_cast<const uint2 *>(&Xs[pr + 4 * pt][s_lo + 16]);
-                const V xa = __builtin_bit_cast(V, (uint4{lo.x, lo.y, hi.x, hi.y}));
-                y[pt] = M::run(xa, a, y[pt]);
-            }
-        };
-        const int nj = rt >> 1;  // blocks J < nj lie below the diagonal, J = nj on it
-        f32x4 d_lo, d_hi;
-        bc(0, d_lo, d_hi);
-        for (int J = 0; J < nj; J++) {
-            f32x4 n_lo, n_hi;
-            bc(J + 1, n_lo, n_hi);
-            const int s_lo = 32 * J + g4;  // this lane's columns: s_lo + i, s_lo + 16 + i
-            const float rf = exp_f(at - acum_s[32 * J + 31]);
-            const f32x4 q_lo = *reinterpret_cast<const f32x4 *>(&q_s[s_lo]);
-            const f32x4 q_hi = *reinterpret_cast<const f32x4 *>(&q_s[s_lo + 16]);
-            V a;
+                f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int ii = 0; ii < 4; ii++) {
-                a[ii] = static_cast<IT>(d_lo[ii] * (rf * q_lo[ii]));
-                a[4 + ii] = static_cast<IT>(d_hi[ii] * (rf * q_hi[ii]));
+                for (int k = 0; k < KN; k++)
+                    a = M::run(*reinterpret_cast<const V *>(&Sin[pr + 4 * pt][32 * k + k8]), ac[i][k], a);
+                y[pt] = a;
             }
-            apply(J, a);
-            d_lo = n_lo;
-            d_hi = n_hi;
-        }
-        {
-            // the diagonal block: exact factor, causal mask
-            const int s_lo = 32 * nj + g4;
-            V a;
+            {
+                const float rs = exp_f(at);
 #pragma unroll
-            for (int ii = 0; ii < 4; ii++) {
-                const int s0 = s_lo + ii, s1 = s_lo + 16 + ii;
-                const float m0 = s0 <= tt ? d_lo[ii] * (exp_f(at - acum_s[s0]) * dtp_s[s0]) : 0.0f;
-                const float m1 = s1 <= tt ? d_hi[ii] * (exp_f(at - acum_s[s1]) * dtp_s[s1]) : 0.0f;
-                a[ii] = static_cast<IT>(m0);
-                a[4 + ii] = static_cast<IT>(m1);
+                for (int pt = 0; pt < kP / 16; pt++)
+#pragma unroll
+                    for (int ii = 0; ii < 4; ii++)
+                        y[pt][ii] *= rs;
             }
-            apply(nj, a);
-        }
-        // D x, the gate, the store: y[pt][ii] is p = 16 gq + 4 pt + ii of token tt
-        if (tt < len) {
-            const int64_t tok = t0 + tt;
-            V o[2];
+            // (B_J C^T) for the lane's token and columns; block J + 1's product is
+            // formed while block J's is scaled and applied (MFMA and VALU overlap)
+            auto bc = [&](int J, f32x4 &dl, f32x4 &dh) {
+                dl = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                dh = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int pt = 0; pt < kP / 16; pt++)
+                for (int k = 0; k < KN; k++) {
+                    dl = M::run(*reinterpret_cast<const V *>(&Bs[32 * J + r][32 * k + k8]), ac[i][k], dl);
+                    dh = M::run(*reinterpret_cast<const V *>(&Bs[32 * J + 16 + r][32 * k + k8]), ac[i][k], dh);
+                }
+            };
+            auto apply = [&](int J, const V &a) {
+                const int s_lo = 32 * J + g4;
+#pragma unroll
+                for (int pt = 0; pt < kP / 16; pt++) {
+                    const uint2 lo = *reinterpret_cast<const uint2 *>(&Xs[pr + 4 * pt][s_lo]);
+                    const uint2 hi = *reinterpret_cast<const uint2 *>(&Xs[pr + 4 * pt][s_lo + 16]);
+                    const V xa = __builtin_bit_cast(V, (uint4{lo.x, lo.y, hi.x, hi.y}));
+                    y[pt] = M::run(xa, a, y[pt]);
+                }
+            };
+            const int nj = rt >> 1;  // blocks J < nj lie below the diagonal, J = nj on it
+            f32x4 d_lo, d_hi;
+            bc(0, d_lo, d_hi);
+            for (int J = 0; J < nj; J++) {
+                f32x4 n_lo, n_hi;
+                bc(J + 1, n_lo, n_hi);
+                const int s_lo = 32 * J + g4;  // this lane's columns: s_lo + i, s_lo + 16 + i
+                const float rf = exp_f(at - acum_s[32 * J + 31]);
+                const f32x4 q_lo = *reinterpret_cast<const f32x4 *>(&q_s[s_lo]);
+                const f32x4 q_hi = *reinterpret_cast<const f32x4 *>(&q_s[s_lo + 16]);
+                V a;
 #pragma unroll
                 for (int ii = 0; ii < 4; ii++) {
-                    const int e = 4 * pt + ii;  // 0..15
-                    float v = y[pt][ii] + dh * to_f(xo[i][e / 8][e % 8]);
-                    if (zs)
-                        v *= silu_f(to_f(zo[i][e / 8][e % 8]));
-                    o[e / 8][e % 8] = static_cast<IT>(v);
+                    a[ii] = static_cast<IT>(d_lo[ii] * (rf * q_lo[ii]));
+                    a[4 + ii] = static_cast<IT>(d_hi[ii] * (rf * q_hi[ii]));
                 }
-            IT *orow = outp + tok * sp.out_st + h * sp.out_sh + 16 * gq;
-            *reinterpret_cast<V *>(orow) = o[0];
-            *reinterpret_cast<V *>(orow + 8) = o[1];
+                apply(J, a);
+                d_lo = n_lo;
+                d_hi = n_hi;
+            }
+            {
+                // the diagonal block: exact factor, causal mask
+                const int s_lo = 32 * nj + g4;
+                V a;
+#pragma unroll
+                for (int ii = 0; ii < 4; ii++) {
+                    const int s0 = s_lo + ii, s1 = s_lo + 16 + ii;
+                    const float m0 = s0 <= tt ? d_lo[ii] * (exp_f(at - acum_s[s0]) * dtp_s[s0]) : 0.0f;
+                    const float m1 = s1 <= tt ? d_hi[ii] * (exp_f(at - acum_s[s1]) * dtp_s[s1]) : 0.0f;
+                    a[ii] = static_cast<IT>(m0);
+                    a[4 + ii] = static_cast<IT>(m1);
+                }
+                apply(nj, a);
+            }
+            // D x, the gate, the store: y[pt][ii] is p = 16 gq + 4 pt + ii of token tt
+            if (tt < len) {
+                const int64_t tok = t0 + tt;
+                V o[2];
+#pragma unroll
+                for (int pt = 0; pt < kP / 16; pt++)
+#pragma unroll
+                    for (int ii = 0; ii < 4; ii++) {
+                        const int e = 4 * pt + ii;  // 0..15
+                        float v = y[pt][ii] + dh * to_f(xo[i][e / 8][e % 8]);
+                        if (zs)
+                            v *= silu_f(to_f(zo[i][e / 8][e % 8]));
+                        o[e / 8][e % 8] = static_cast<IT>(v);
+                    }
+                IT *orow = outp + tok * sp.out_st + h * sp.out_sh + 16 * gq;
+                *reinterpret_cast<V *>(orow) = o[0];
+                *reinterpret_cast<V *>(orow + 8) = o[1];
+            }
+        }
+        if (hk + 1 < nh) {  // uniform: the next head's inputs replace this one's
+            __syncthreads();
+            store_head(next);
+            __syncthreads();
         }
     }
 }
@@ -497,7 +533,9 @@ int launch_ssd_typed(const SsdParams &sp, int state_dtype, void *stream) {
     e = hipLaunchKernel(pass, dim3(pass_grid), dim3(256), args, owner_bytes, s);
     if (e != hipSuccess)
         return static_cast<int>(e);
-    e = hipLaunchKernel(reinterpret_cast<const void *>(&ssd_chunk_scan_kernel<IT, N>), dim3(chunk_grid),
+    const unsigned scan_grid = static_cast<unsigned>(sp.nchunks * (sp.H / sp.hpg) *
+                                                     ((sp.hpg + kScanHeads - 1) / kScanHeads));
+    e = hipLaunchKernel(reinterpret_cast<const void *>(&ssd_chunk_scan_kernel<IT, N>), dim3(scan_grid),
                         dim3(kScanThreads), args, 0, s);
     return static_cast<int>(e);
 }
