@@ -91,82 +91,109 @@ __device__ __forceinline__ float processed_dt(const SsdParams &sp, int64_t t, in
 }
 
 // ---- stage 1: dt', the decay cumsum, and the chunk's own state
+//
+// One workgroup (256 lanes, lane = token of the chunk) per (chunk, group,
+// block of kStateHeads heads of the group): B^T is staged in LDS once for
+// the heads; per head, dt' and the cumsum (an LDS scan), then
+// (w x)^T with w_t = exp(A_end - A_t) dt'_t and the chunk's own state
+// [64 x N] = sum_t (w_t x_t) B_t^T as MFMA tiles (wave w: rows 16w ..). The
+// next head's x row and dt are requested during the current head's products.
+
+constexpr int kStateHeads = 4;
 
 template <typename IT, int N>
 __global__ __launch_bounds__(256) void ssd_chunk_state_kernel(const SsdParams sp) {
     using M = Mfma<IT>;
     using V = typename M::V;
     __shared__ float scan[kL];
-    __shared__ __attribute__((aligned(16))) IT Xs[kP][kL + kPad];  // x^T:  [p][t]
-    __shared__ __attribute__((aligned(16))) IT Bs[N][kL + kPad];   // (w B)^T: [n][t]
+    __shared__ __attribute__((aligned(16))) IT Xs[kP][kL + kPad];  // (w x)^T: [p][t]
+    __shared__ __attribute__((aligned(16))) IT Bs[N][kL + kPad];   // B^T: [n][t]
 
-    const int64_t c = blockIdx.x / sp.H;
-    const int h = blockIdx.x % sp.H;
-    const int g = h / sp.hpg;
+    const int ngroups = static_cast<int>(sp.H / sp.hpg);
+    const int nhb = (sp.hpg + kStateHeads - 1) / kStateHeads;
+    const int64_t c = blockIdx.x / (ngroups * nhb);
+    const int g = (blockIdx.x / nhb) % ngroups;
+    const int hb = blockIdx.x % nhb;
+    const int h0 = g * sp.hpg + hb * kStateHeads;
+    const int nh = sp.hpg - hb * kStateHeads < kStateHeads ? sp.hpg - hb * kStateHeads : kStateHeads;
     const int t = threadIdx.x;  // token in the chunk (kL threads)
     int64_t t0;
     int len;
     chunk_range(sp, c, &t0, &len);
-
-    const float dtp = t < len ? processed_dt<IT>(sp, t0 + t, h) : 0.0f;
-    scan[t] = dtp * sp.A[h * sp.A_sh];
-    __syncthreads();
-    for (int off = 1; off < kL; off <<= 1) {  // inclusive prefix sum
-        const float add = t >= off ? scan[t - off] : 0.0f;
-        __syncthreads();
-        scan[t] += add;
-        __syncthreads();
-    }
-    const float acum = scan[t];
-    const float total = scan[kL - 1];  // padding adds nothing
-    const int64_t wrow = (c * sp.H + h) * kL;
-    sp.ws_dtp[wrow + t] = dtp;
-    sp.ws_acum[wrow + t] = acum;
-    const float w = t < len ? exp_f(total - acum) * dtp : 0.0f;
-
-    // token t's x row and scaled B row, transposed into LDS (lanes past the
-    // chunk read token 0, always present, and store zeros)
+    // lanes past the chunk read token 0 (always present) and contribute zeros
     const int64_t tok = t < len ? t0 + t : 0;
-    const IT *xrow = static_cast<const IT *>(sp.x) + (tok * sp.x_st + h * sp.x_sh);
-    const IT *brow = static_cast<const IT *>(sp.B) + (tok * sp.B_st + g * sp.B_sg);
-#pragma unroll
-    for (int p0 = 0; p0 < kP; p0 += 8) {
-        const V v = *reinterpret_cast<const V *>(xrow + p0);
-#pragma unroll
-        for (int k = 0; k < 8; k++)
-            Xs[p0 + k][t] = t < len ? v[k] : static_cast<IT>(0.0f);
-    }
-#pragma unroll
-    for (int n0 = 0; n0 < N; n0 += 8) {
-        const V v = *reinterpret_cast<const V *>(brow + n0);
-#pragma unroll
-        for (int k = 0; k < 8; k++)
-            Bs[n0 + k][t] = static_cast<IT>(to_f(v[k]) * w);
-    }
-    __syncthreads();
 
-    // state[p][n] = sum_t Xs[p][t] Bs[n][t]; wave wv takes rows p = 16 wv ..
-    const int lane = t & 63, wv = t >> 6;
-    f32x4 acc[N / 16];
+    auto load_x = [&](int h, V (&xv)[kP / 8]) {
+        const IT *xrow = static_cast<const IT *>(sp.x) + (tok * sp.x_st + h * sp.x_sh);
 #pragma unroll
-    for (int nt = 0; nt < N / 16; nt++)
-        acc[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    const int ksteps = (len + 31) / 32;
-    const int r = lane & 15, k8 = 8 * (lane >> 4);
-    for (int k = 0; k < ksteps; k++) {
-        const V a = *reinterpret_cast<const V *>(&Xs[16 * wv + r][32 * k + k8]);
+        for (int p0 = 0; p0 < kP / 8; p0++)
+            xv[p0] = *reinterpret_cast<const V *>(xrow + 8 * p0);
+    };
+    V xv[kP / 8];
+    load_x(h0, xv);
+    float dtp = t < len ? processed_dt<IT>(sp, t0 + t, h0) : 0.0f;
+    {
+        const IT *brow = static_cast<const IT *>(sp.B) + (tok * sp.B_st + g * sp.B_sg);
 #pragma unroll
-        for (int nt = 0; nt < N / 16; nt++) {
-            const V b = *reinterpret_cast<const V *>(&Bs[16 * nt + r][32 * k + k8]);
-            acc[nt] = M::run(a, b, acc[nt]);
+        for (int n0 = 0; n0 < N; n0 += 8) {
+            const V v = *reinterpret_cast<const V *>(brow + n0);
+#pragma unroll
+            for (int k = 0; k < 8; k++)
+                Bs[n0 + k][t] = t < len ? v[k] : static_cast<IT>(0.0f);
         }
     }
-    float *dst = sp.ws_state + (c * sp.H + h) * static_cast<int64_t>(kP * N);
+
+    const int lane = t & 63, wv = t >> 6;
+    const int r = lane & 15, k8 = 8 * (lane >> 4);
+    const int ksteps = (len + 31) / 32;
+    for (int hk = 0; hk < nh; hk++) {
+        const int h = h0 + hk;
+        scan[t] = dtp * sp.A[h * sp.A_sh];
+        __syncthreads();
+        for (int off = 1; off < kL; off <<= 1) {  // inclusive prefix sum
+            const float add = t >= off ? scan[t - off] : 0.0f;
+            __syncthreads();
+            scan[t] += add;
+            __syncthreads();
+        }
+        const float acum = scan[t];
+        const float total = scan[kL - 1];  // padding adds nothing
+        const int64_t wrow = (c * sp.H + h) * kL;
+        sp.ws_dtp[wrow + t] = dtp;
+        sp.ws_acum[wrow + t] = acum;
+        const float w = t < len ? exp_f(total - acum) * dtp : 0.0f;
 #pragma unroll
-    for (int nt = 0; nt < N / 16; nt++)
+        for (int p0 = 0; p0 < kP / 8; p0++)
 #pragma unroll
-        for (int i = 0; i < 4; i++)
-            dst[(16 * wv + 4 * (lane >> 4) + i) * N + 16 * nt + r] = acc[nt][i];
+            for (int k = 0; k < 8; k++)
+                Xs[8 * p0 + k][t] = static_cast<IT>(to_f(xv[p0][k]) * w);
+        __syncthreads();
+        if (hk + 1 < nh) {  // the next head's inputs, in flight during the products
+            load_x(h + 1, xv);
+            dtp = t < len ? processed_dt<IT>(sp, t0 + t, h + 1) : 0.0f;
+        }
+
+        // state[p][n] = sum_t Xs[p][t] Bs[n][t]; wave wv takes rows p = 16 wv ..
+        f32x4 acc[N / 16];
+#pragma unroll
+        for (int nt = 0; nt < N / 16; nt++)
+            acc[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int k = 0; k < ksteps; k++) {
+            const V a = *reinterpret_cast<const V *>(&Xs[16 * wv + r][32 * k + k8]);
+#pragma unroll
+            for (int nt = 0; nt < N / 16; nt++) {
+                const V b = *reinterpret_cast<const V *>(&Bs[16 * nt + r][32 * k + k8]);
+                acc[nt] = M::run(a, b, acc[nt]);
+            }
+        }
+        float *dst = sp.ws_state + (c * sp.H + h) * static_cast<int64_t>(kP * N);
+#pragma unroll
+        for (int nt = 0; nt < N / 16; nt++)
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                dst[(16 * wv + 4 * (lane >> 4) + i) * N + 16 * nt + r] = acc[nt][i];
+        __syncthreads();  // Xs and scan are rewritten for the next head
+    }
 }
 
 // ---- stage 2: state passing
@@ -520,8 +547,9 @@ int launch_ssd_typed(const SsdParams &sp, int state_dtype, void *stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     SsdParams p = sp;
     void *args[] = {&p};
-    const unsigned chunk_grid = static_cast<unsigned>(sp.nchunks * sp.H);
-    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&ssd_chunk_state_kernel<IT, N>), dim3(chunk_grid),
+    const unsigned state_grid = static_cast<unsigned>(sp.nchunks * (sp.H / sp.hpg) *
+                                                      ((sp.hpg + kStateHeads - 1) / kStateHeads));
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&ssd_chunk_state_kernel<IT, N>), dim3(state_grid),
                                    dim3(256), args, 0, s);
     if (e != hipSuccess)
         return static_cast<int>(e);
