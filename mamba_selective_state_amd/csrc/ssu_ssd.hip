@@ -90,6 +90,16 @@ __device__ __forceinline__ float processed_dt(const SsdParams &sp, int64_t t, in
     return v > sp.dt_hi ? sp.dt_hi : v;
 }
 
+// Inclusive prefix sum over a wave's 64 lanes (log-step shuffles)
+__device__ __forceinline__ float wave_inclusive_sum(float v, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const float u = __shfl_up(v, off, 64);
+        v += lane >= off ? u : 0.0f;
+    }
+    return v;
+}
+
 // ---- stage 1: dt', the decay cumsum, and the chunk's own state
 //
 // One workgroup (256 lanes, lane = token of the chunk) per (chunk, group,
@@ -105,7 +115,7 @@ template <typename IT, int N>
 __global__ __launch_bounds__(256) void ssd_chunk_state_kernel(const SsdParams sp) {
     using M = Mfma<IT>;
     using V = typename M::V;
-    __shared__ float scan[kL];
+    __shared__ float wave_tot[kL / 64];
     __shared__ __attribute__((aligned(16))) IT Xs[kP][kL + kPad];  // (w x)^T: [p][t]
     __shared__ __attribute__((aligned(16))) IT Bs[N][kL + kPad];   // B^T: [n][t]
 
@@ -117,6 +127,7 @@ __global__ __launch_bounds__(256) void ssd_chunk_state_kernel(const SsdParams sp
     const int h0 = g * sp.hpg + hb * kStateHeads;
     const int nh = sp.hpg - hb * kStateHeads < kStateHeads ? sp.hpg - hb * kStateHeads : kStateHeads;
     const int t = threadIdx.x;  // token in the chunk (kL threads)
+    const int lane = t & 63, wv = t >> 6;
     int64_t t0;
     int len;
     chunk_range(sp, c, &t0, &len);
@@ -143,21 +154,25 @@ __global__ __launch_bounds__(256) void ssd_chunk_state_kernel(const SsdParams sp
         }
     }
 
-    const int lane = t & 63, wv = t >> 6;
     const int r = lane & 15, k8 = 8 * (lane >> 4);
     const int ksteps = (len + 31) / 32;
     for (int hk = 0; hk < nh; hk++) {
         const int h = h0 + hk;
-        scan[t] = dtp * sp.A[h * sp.A_sh];
+        // inclusive prefix sum of dt' A over the chunk: within each wave, then
+        // the wave totals through LDS
+        float acum = wave_inclusive_sum(dtp * sp.A[h * sp.A_sh], lane);
+        if (lane == 63)
+            wave_tot[wv] = acum;
         __syncthreads();
-        for (int off = 1; off < kL; off <<= 1) {  // inclusive prefix sum
-            const float add = t >= off ? scan[t - off] : 0.0f;
-            __syncthreads();
-            scan[t] += add;
-            __syncthreads();
+        // the chunk's total, summed in the order of the last lane's cumsum
+        // (padding adds nothing)
+        float total = wave_tot[kL / 64 - 1];
+#pragma unroll
+        for (int k = 0; k < kL / 64; k++) {
+            const float wt = wave_tot[k];
+            acum += k < wv ? wt : 0.0f;
+            total += k < kL / 64 - 1 ? wt : 0.0f;
         }
-        const float acum = scan[t];
-        const float total = scan[kL - 1];  // padding adds nothing
         const int64_t wrow = (c * sp.H + h) * kL;
         sp.ws_dtp[wrow + t] = dtp;
         sp.ws_acum[wrow + t] = acum;
@@ -192,7 +207,7 @@ __global__ __launch_bounds__(256) void ssd_chunk_state_kernel(const SsdParams sp
 #pragma unroll
             for (int i = 0; i < 4; i++)
                 dst[(16 * wv + 4 * (lane >> 4) + i) * N + 16 * nt + r] = acc[nt][i];
-        __syncthreads();  // Xs and scan are rewritten for the next head
+        __syncthreads();  // Xs and the wave totals are rewritten for the next head
     }
 }
 
