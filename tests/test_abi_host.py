@@ -549,3 +549,84 @@ def test_conv_state_shift_empty_and_errors():
     assert st == S.ERR_VALUE and "required" in msg
     st, msg = shift(pool, v3, v3, tdesc((3,), S.F32))
     assert st == S.ERR_VALUE and "bias" in msg
+
+
+# ---------------------------------------------------------------- SSD prefill
+
+
+def ssd_args(T=0, H=8, P=64, N=128, G=2, nchunks=0, batch=0, chunk=256, io=S.BF16, sd=S.F32):
+    a = S.SsuSsdArgs()
+    a.x = tdesc((T, H, P), io)
+    a.dt = tdesc((T, H), S.F32)
+    a.A = tdesc((H,), S.F32)
+    a.B = tdesc((T, G, N), io)
+    a.C = tdesc((T, G, N), io)
+    a.z = tdesc((T, H, P), io)
+    a.out = tdesc((T, H, P), io)
+    a.cu_chunk_seqlens = tdesc((nchunks + 1,), S.I32)
+    a.seq_idx = tdesc((nchunks,), S.I32)
+    a.last_chunk_indices = tdesc((batch,), S.I32)
+    a.states = tdesc((batch, H, P, N), sd)
+    a.chunk_size = chunk
+    a.dt_limit_lo, a.dt_limit_hi = 0.0, float("inf")
+    return a
+
+
+def ssd(a, ws=0, ws_bytes=0):
+    st = S._lib.ssu_ssd_prefill(ctypes.byref(a), ctypes.c_void_p(ws), ws_bytes, None)
+    return st, S.ssu_last_error()
+
+
+def test_ssd_empty_is_ok_without_workspace():
+    assert ssd(ssd_args()) == (S.OK, "")
+    assert ssd(ssd_args(batch=3)) == (S.OK, "")
+
+
+def test_ssd_workspace_bytes():
+    assert S.ssu_ssd_workspace_bytes(8, 64, 128, 0) >= 0
+    assert S.ssu_ssd_workspace_bytes(8, 64, 128, 10) > S.ssu_ssd_workspace_bytes(8, 64, 128, 1)
+    assert S.ssu_ssd_workspace_bytes(-1, 64, 128, 1) == -1
+
+
+def test_ssd_errors():
+    assert S._lib.ssu_ssd_prefill(None, None, 0, None) == S.ERR_VALUE
+    a = ssd_args()
+    a.unsupported = S.OPT_SSD_CHECKPOINT
+    st, msg = ssd(a)
+    assert st == S.ERR_NOT_IMPLEMENTED and "checkpoint" in msg
+    st, msg = ssd(ssd_args(io=S.F32))
+    assert st == S.ERR_NOT_IMPLEMENTED and "bf16 or f16" in msg
+    st, msg = ssd(ssd_args(P=32))
+    assert st == S.ERR_NOT_IMPLEMENTED and "head dim" in msg
+    st, msg = ssd(ssd_args(N=96))
+    assert st == S.ERR_NOT_IMPLEMENTED and "dstate" in msg
+    st, msg = ssd(ssd_args(H=6, G=4))
+    assert st == S.ERR_VALUE and "divisible" in msg
+    for chunk in (0, 257):
+        st, msg = ssd(ssd_args(chunk=chunk))
+        assert st == S.ERR_NOT_IMPLEMENTED and "chunk_size" in msg
+    a = ssd_args()
+    a.dt_limit_lo, a.dt_limit_hi = 1.0, 0.5
+    st, msg = ssd(a)
+    assert st == S.ERR_VALUE and "dt_limit" in msg
+    # rows of x, B, C, z and out start on 16-byte boundaries
+    for name in ("x", "z", "out"):
+        a = ssd_args(T=4)
+        setattr(a, name, tdesc((4, 8, 64), S.BF16, strides=(8 * 68, 68, 1)))
+        st, msg = ssd(a)
+        assert st == S.ERR_VALUE and "16-byte" in msg, (name, msg)
+    a = ssd_args(T=4)
+    a.B = tdesc((4, 2, 128), S.BF16, strides=(2 * 132, 132, 1))
+    st, msg = ssd(a)
+    assert st == S.ERR_VALUE and "16-byte" in msg
+    a = ssd_args(T=4, nchunks=1, batch=1)
+    a.states = tdesc((2, 8, 64, 128), S.F32)
+    st, msg = ssd(a)
+    assert st == S.ERR_VALUE and "states" in msg
+    a = ssd_args(T=4, nchunks=1, batch=1)
+    st, msg = ssd(a, ws=FAKE, ws_bytes=16)
+    assert st == S.ERR_VALUE and "workspace" in msg
+    a = ssd_args(T=4, nchunks=1, batch=1)
+    a.cu_chunk_seqlens = S.SsuTensor()
+    st, msg = ssd(a)
+    assert st == S.ERR_VALUE and "cu_chunk_seqlens" in msg

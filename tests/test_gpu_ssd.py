@@ -110,3 +110,23 @@ def test_ssd_full_workload():
     sequence, sampled over heads (the oracle runs on 3 of the 128)."""
     c = W.ssd_bench()
     check_ssd(c, "ssd bench workload", heads=[0, 77, 127])
+
+
+@pytest.mark.parametrize("heads,groups", [(6, 1), (12, 4)], ids=["6-per-group", "3-per-group"])
+def test_ssd_head_blocks(heads, groups):
+    """Heads per group that the kernels' 4-head blocks do not divide (6:
+    a block of 4 and one of 2; 3: one partial block), with intermediate
+    states so every chunk's state is checked."""
+    c = W.ssd(seed=7 + heads, lengths=(300, 17, 129), heads=heads, dim=64, dstate=128, groups=groups,
+              chunk_size=128, io="bf16", state_dtype="f32")
+    check_ssd(c, "ssd %d heads / %d groups" % (heads, groups))
+    check_ssd(c, "ssd %d heads / %d groups, intermediate" % (heads, groups), intermediate=True)
+
+
+def test_ssd_tiny_chunks():
+    """Seventeen sequences of 1..17 tokens at chunk size 16: every chunk is
+    shorter than a 32-token block and most are ragged 16-row tiles."""
+    c = W.ssd(seed=9, lengths=tuple(range(1, 18)), heads=8, dim=64, dstate=64, groups=2, chunk_size=16,
+              io="f16", state_dtype="f32")
+    check_ssd(c, "ssd tiny chunks")
+    check_ssd(c, "ssd tiny chunks, intermediate", intermediate=True)
