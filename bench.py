@@ -17,7 +17,7 @@ Prints ONE JSON line:
              current kernel source, else null
   cpu_baseline  the CPU oracle timed on this host on the same workload
 Options: --config {decode, decode_pad, mtp, varlen, varlen_disable, varlen_nodst, replay,
-replay_spec, replay_lp, spec_snapshots, conv_shift_sd, conv_shift_ds, memcpy_left, ssd},
+replay_spec, replay_lp, spec_snapshots, tiny, conv_shift_sd, conv_shift_ds, memcpy_left, ssd},
 --no-cpu-baseline, --calib-copy (also runs a plain device copy of the state's
 size, the calibration kernel for the counters).
 """
@@ -396,6 +396,101 @@ def copy_bench(args, name, case, desc):
     print(json.dumps(result), flush=True)
 
 
+def tiny_bench(args):
+    """The MATE page's minimal example (batch 2, heads 8, dim 8, dstate 128,
+    fp16 state): one step is its two chained calls (no tables, then tables
+    [0, 1]). Launch-bound: reported as latency per step on the stream (HIP
+    events, eager launches), with the wall time and the replay of a HIP graph
+    holding both calls alongside."""
+    import torch
+    import mamba_selective_state_amd as ssu
+    from workloads import one_token_tiny
+    from workloads.device import TORCH, device_case
+    dev = torch.device("cuda", 0)
+    cases = [one_token_tiny(tables=False), one_token_tiny(tables=True)]
+    d0 = device_case(cases[0], dev)
+    calls = []
+    for c in cases:
+        d = device_case(c, dev)
+        d["state"] = d0["state"]  # the two calls share the pool, as on the page
+        out = torch.empty(np.shape(c["x"]), dtype=TORCH[c["io_dtype"]], device=dev)
+        calls.append(ssu.make_args(d["state"], d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["z"],
+                                   d["dt_bias"], False, d["state_batch_indices"], -1, out, False,
+                                   d["dst_state_batch_indices"], None, None))
+        calls[-1]._keep = (d, out)
+    nbytes = sum(algorithmic_bytes(c)[0] for c in cases)
+    updates = sum(algorithmic_bytes(c)[1] for c in cases)
+    stream = torch.cuda.Stream(dev)
+    with torch.cuda.stream(stream):
+        handle = stream.cuda_stream
+
+        def step():
+            for a in calls:
+                ssu.ssu_update(a, handle)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize(dev)
+        steps = max(args.steps, 1000)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize(dev)
+        eager = (time.perf_counter() - t0) / steps
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        for _ in range(steps):
+            step()
+        s1.record(stream)
+        torch.cuda.synchronize(dev)
+        eager_events = s0.elapsed_time(s1) / steps * 1e-3
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            step()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize(dev)
+        s0.record(stream)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        s1.record(stream)
+        torch.cuda.synchronize(dev)
+        graph_wall = (time.perf_counter() - t0) / steps
+        graph = s0.elapsed_time(s1) / steps * 1e-3
+    achieved = nbytes / eager_events / 1e9
+    result = {
+        "metric": "SSU decode latency, MATE minimal example (two chained calls)",
+        "value": round(eager_events * 1e6, 3), "unit": "us", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": round(eager_events * 1e3, 5), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "tiny: the MATE page's minimal example, batch 2, heads 8, dim 8, "
+                               "dstate 128, groups 2, fp16 state, two chained calls (no tables, then "
+                               "tables [0, 1])", "bytes_per_step": nbytes,
+                   "token_head_updates_per_step": updates},
+        "eager_us_per_step_wall": round(eager * 1e6, 3),
+        "eager_us_per_step_events": round(eager_events * 1e6, 3),
+        "graph_us_per_step_events": round(graph * 1e6, 3),
+        "graph_us_per_step_wall": round(graph_wall * 1e6, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 6), "traffic": None,
+                     "note": "launch-bound: the two launches move %d bytes" % nbytes},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import ssu_oracle
+        ssu_oracle.default()
+        reps = 200
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            for c in cases:
+                ssu_oracle.run(c)
+        t = (time.perf_counter() - t0) / reps
+        result["cpu_baseline"] = {"value": round(t * 1e6, 2), "unit": "us", "cores": 1, "kind": "oracle",
+                                  "sample": "the two calls, mean of %d repetitions; single-threaded "
+                                            "plain-C oracle incl. its NumPy wrapper" % reps}
+    print(json.dumps(result), flush=True)
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
@@ -467,6 +562,12 @@ def main():
             raise SystemExit("bench.py needs a GPU")
         case, desc = workload(args.config)
         copy_bench(args, args.config, case, desc)
+        return
+    if args.config == "tiny":
+        import torch
+        if not torch.cuda.is_available():
+            raise SystemExit("bench.py needs a GPU")
+        tiny_bench(args)
         return
 
     import torch
