@@ -119,3 +119,28 @@ def test_conv_shift_edges():
         c["src_blk"][2] = 999
         c["dst_blk"][3] = -2
         run_shift(c, repeat=2)
+
+
+# ---------------------------------------------------------------- full sizes
+
+def test_memcpy_left_full_workload():
+    """The benchmark's memcpy_left workload (4096 rows of 32 KiB, each moved
+    onto itself 16 bytes to the left) with its max_size, twice, every byte
+    against the snapshot and the oracle."""
+    import bench
+    c, _ = bench.workload("memcpy_left")
+    G.say("[gpu] memcpy_left full: launching")
+    run_memcpy(c, repeat=2, max_size=int(np.max(c["sizes"])))
+    G.say("[gpu] memcpy_left full: ok")
+
+
+@pytest.mark.parametrize("config", ["conv_shift_sd", "conv_shift_ds"])
+def test_conv_shift_full_workload(config):
+    """The benchmark's convolution-state shift workloads (6144 shifts of
+    64 KiB fp16 blocks, half inside one block), twice, every byte against
+    the snapshot and the oracle."""
+    import bench
+    c, _ = bench.workload(config)
+    G.say("[gpu] %s full: launching" % config)
+    run_shift(c, repeat=2)
+    G.say("[gpu] %s full: ok" % config)
