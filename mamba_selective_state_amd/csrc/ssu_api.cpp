@@ -585,10 +585,17 @@ ssu_status_t ssu_batch_memcpy(const ssu_tensor_t *src_ptrs, const ssu_tensor_t *
 
 // ---- SSD packed prefill
 
-static int64_t ssd_ws_parts(int64_t H, int64_t P, int64_t N, int64_t nchunks, int64_t *rows_bytes) {
+// Workspace: dt' and the cumsum [nchunks, H, 256] f32, each chunk's own
+// state [nchunks, H, P, N] f32, each chunk's entering state in the x dtype
+// (2 bytes), each part 256-byte aligned.
+static int64_t ssd_ws_parts(int64_t H, int64_t P, int64_t N, int64_t nchunks, int64_t *rows_bytes,
+                            int64_t *state_bytes = nullptr) {
     auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
     *rows_bytes = up(nchunks * H * ssu::kSsdMaxChunk * 4);
-    return 2 * *rows_bytes + up(nchunks * H * P * N * 4);
+    const int64_t sb = up(nchunks * H * P * N * 4);
+    if (state_bytes)
+        *state_bytes = sb;
+    return 2 * *rows_bytes + sb + up(nchunks * H * P * N * 2);
 }
 
 int64_t ssu_ssd_workspace_bytes(int64_t heads, int64_t dim, int64_t dstate, int64_t nchunks) {
@@ -721,14 +728,15 @@ ssu_status_t ssu_ssd_prefill(const ssu_ssd_args_t *a, void *workspace, int64_t w
         return fail(SSU_ERR_NOT_IMPLEMENTED, "more than 16384 chunks");
     if (nchunks * H > INT32_MAX)
         return fail(SSU_ERR_NOT_IMPLEMENTED, "grid too large");
-    int64_t rows_bytes;
-    const int64_t need = ssd_ws_parts(H, P, N, nchunks, &rows_bytes);
+    int64_t rows_bytes, state_bytes;
+    const int64_t need = ssd_ws_parts(H, P, N, nchunks, &rows_bytes, &state_bytes);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
         return fail(SSU_ERR_VALUE, "workspace must be 256-byte aligned with at least %lld bytes", (long long)need);
     char *ws = static_cast<char *>(workspace);
     sp.ws_dtp = reinterpret_cast<float *>(ws);
     sp.ws_acum = reinterpret_cast<float *>(ws + rows_bytes);
     sp.ws_state = reinterpret_cast<float *>(ws + 2 * rows_bytes);
+    sp.ws_sin = ws + 2 * rows_bytes + state_bytes;
     sp.x = x.data;
     sp.dt = dt.data;
     sp.B = a->B.data;

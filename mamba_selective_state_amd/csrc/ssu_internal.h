@@ -192,6 +192,7 @@ struct SsdParams {
     const float *A, *D, *dt_bias;
     const void *cu_chunk, *seq_idx, *last_chunk;
     float *ws_dtp, *ws_acum, *ws_state;
+    void *ws_sin;  // entering states [nchunks, H, P, N] in the x dtype
     int64_t T, H, N, nchunks, batch, chunk_size;
     int64_t x_st, x_sh, dt_st, dt_sh, B_st, B_sg, C_st, C_sg, z_st, z_sh, out_st, out_sh;
     int64_t A_sh, D_sh, bias_sh;

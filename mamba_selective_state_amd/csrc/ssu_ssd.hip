@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void ssd_chunk_state_kernel(const SsdParams sp
 
 // ---- stage 2: state passing
 
-template <typename ST>
+template <typename ST, typename IT>
 __global__ __launch_bounds__(256) void ssd_state_pass_kernel(const SsdParams sp) {
     extern __shared__ int owner[];  // owner[c]: the sequence whose state chunk c returns, or -1
     const int64_t tiles = (static_cast<int64_t>(kP) * sp.N + 255) / 256;
@@ -247,7 +247,7 @@ __global__ __launch_bounds__(256) void ssd_state_pass_kernel(const SsdParams sp)
         // next chunk's own state requested before this one is overwritten
         const float own_next = c + 1 < sp.nchunks ? sp.ws_state[at + sp.H * PN] : 0.0f;
         const float total = sp.ws_acum[(c * sp.H + h) * kL + kL - 1];
-        sp.ws_state[at] = S;  // the entering state, read by the scan
+        static_cast<IT *>(sp.ws_sin)[at] = static_cast<IT>(S);  // the entering state, as the scan reads it
         S = exp_f(total) * S + own;
         if (sp.intermediate) {
             outs[at] = static_cast<ST>(S);
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(const SsdP
     // elements) and, for t < 256, token t's cumsum, dt' and block-end cumsum
     struct HeadIn {
         V xv[2][2];
-        f32x4 sv[kSinSeg / 4];
+        V sv[kSinSeg / 8];
         float at, dt, aj;
     };
     const int pc = 8 * (t & 7);
@@ -354,10 +354,10 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(const SsdP
                 const int tok = 2 * ((t >> 3) + 64 * u) + v;
                 in.xv[u][v] = *reinterpret_cast<const V *>(xs + (t0 + (tok < len ? tok : 0)) * sp.x_st);
             }
-        const float *sin = sp.ws_state + (c * sp.H + h) * static_cast<int64_t>(kP * N) + t * kSinSeg;
+        const IT *sin = static_cast<const IT *>(sp.ws_sin) + (c * sp.H + h) * static_cast<int64_t>(kP * N) + t * kSinSeg;
 #pragma unroll
-        for (int k = 0; k < kSinSeg / 4; k++)
-            in.sv[k] = *reinterpret_cast<const f32x4 *>(sin + 4 * k);
+        for (int k = 0; k < kSinSeg / 8; k++)
+            in.sv[k] = *reinterpret_cast<const V *>(sin + 8 * k);
         const int64_t wrow = (c * sp.H + h) * kL;
         const int tc = t & (kL - 1);
         in.at = sp.ws_acum[wrow + tc];
@@ -379,13 +379,8 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(const SsdP
         }
         const int sp0 = (t * kSinSeg) / N, sn0 = (t * kSinSeg) % N;
 #pragma unroll
-        for (int k = 0; k < kSinSeg / 8; k++) {
-            V w;
-#pragma unroll
-            for (int e = 0; e < 8; e++)
-                w[e] = static_cast<IT>(in.sv[2 * k + e / 4][e % 4]);
-            *reinterpret_cast<V *>(&Sin[sp0][sn0 + 8 * k]) = w;
-        }
+        for (int k = 0; k < kSinSeg / 8; k++)
+            *reinterpret_cast<V *>(&Sin[sp0][sn0 + 8 * k]) = in.sv[k];
         if (t < kL) {
             acum_s[t] = in.at;
             dtp_s[t] = in.dt;
@@ -570,9 +565,9 @@ int launch_ssd_typed(const SsdParams &sp, int state_dtype, void *stream) {
         return static_cast<int>(e);
     const unsigned pass_grid = static_cast<unsigned>(sp.H * ((static_cast<int64_t>(kP) * N + 255) / 256));
     const size_t owner_bytes = sp.intermediate ? 0 : static_cast<size_t>(sp.nchunks) * sizeof(int);
-    const void *pass = state_dtype == SSU_F32    ? reinterpret_cast<const void *>(&ssd_state_pass_kernel<float>)
-                       : state_dtype == SSU_F16  ? reinterpret_cast<const void *>(&ssd_state_pass_kernel<_Float16>)
-                                                 : reinterpret_cast<const void *>(&ssd_state_pass_kernel<__bf16>);
+    const void *pass = state_dtype == SSU_F32    ? reinterpret_cast<const void *>(&ssd_state_pass_kernel<float, IT>)
+                       : state_dtype == SSU_F16  ? reinterpret_cast<const void *>(&ssd_state_pass_kernel<_Float16, IT>)
+                                                 : reinterpret_cast<const void *>(&ssd_state_pass_kernel<__bf16, IT>);
     e = hipLaunchKernel(pass, dim3(pass_grid), dim3(256), args, owner_bytes, s);
     if (e != hipSuccess)
         return static_cast<int>(e);
