@@ -445,88 +445,153 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(const SsdP
         }
         const float dh = sp.D ? sp.D[h * sp.D_sh] : 0.0f;
 
-#pragma unroll
-        for (int i = 0; i < kScanTiles; i++) {
-            const int rt = rts[i];
-            if (rt >= ntiles)
-                continue;  // uniform per wave
-            const int tt = 16 * rt + r;  // this lane's token in the chunk
-            const float at = acum_s[tt];
+        // The wave's tiles: rt0 = wv (blocks J <= rt0 / 2) and rt1 = 15 - wv
+        // (J <= rt1 / 2, more). For J <= rt0 / 2 both tiles read the same B_J
+        // and x operands: those blocks are done for both at once (two
+        // independent MFMA chains), the rest for tile 1 alone.
+        const int rt0 = rts[0], rt1 = rts[1];
+        const bool has1 = rt1 < ntiles;  // implies rt0 < ntiles
+        if (rt0 < ntiles) {  // uniform per wave
+            const int tt0 = 16 * rt0 + r, tt1 = 16 * rt1 + r;  // the lane's tokens
+            const float at0 = acum_s[tt0], at1 = acum_s[tt1];
             // the entering state's contribution, y^T = S_in C^T, scaled by exp(A_t)
-            f32x4 y[kP / 16];
-#pragma unroll
-            for (int pt = 0; pt < kP / 16; pt++) {
-                f32x4 a = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int k = 0; k < KN; k++)
-                    a = M::run(*reinterpret_cast<const V *>(&Sin[pr + 4 * pt][32 * k + k8]), ac[i][k], a);
-                y[pt] = a;
-            }
-            {
+            auto init = [&](const V (&acv)[KN], float at, f32x4 (&y)[kP / 16]) {
                 const float rs = exp_f(at);
 #pragma unroll
-                for (int pt = 0; pt < kP / 16; pt++)
+                for (int pt = 0; pt < kP / 16; pt++) {
+                    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int k = 0; k < KN; k++)
+                        acc = M::run(*reinterpret_cast<const V *>(&Sin[pr + 4 * pt][32 * k + k8]), acv[k], acc);
 #pragma unroll
                     for (int ii = 0; ii < 4; ii++)
-                        y[pt][ii] *= rs;
-            }
-            // (B_J C^T) for the lane's token and columns; block J + 1's product is
-            // formed while block J's is scaled and applied (MFMA and VALU overlap)
-            auto bc = [&](int J, f32x4 &dl, f32x4 &dh) {
+                        acc[ii] *= rs;
+                    y[pt] = acc;
+                }
+            };
+            f32x4 y0[kP / 16], y1[kP / 16];
+            init(ac[0], at0, y0);
+            if (has1)
+                init(ac[1], at1, y1);
+            // (B_J C^T) of one tile: the lane's token, columns s_lo + i, s_lo + 16 + i
+            auto bc1 = [&](int J, const V (&acv)[KN], f32x4 &dl, f32x4 &dh) {
                 dl = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
                 dh = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int k = 0; k < KN; k++) {
-                    dl = M::run(*reinterpret_cast<const V *>(&Bs[32 * J + r][32 * k + k8]), ac[i][k], dl);
-                    dh = M::run(*reinterpret_cast<const V *>(&Bs[32 * J + 16 + r][32 * k + k8]), ac[i][k], dh);
+                    dl = M::run(*reinterpret_cast<const V *>(&Bs[32 * J + r][32 * k + k8]), acv[k], dl);
+                    dh = M::run(*reinterpret_cast<const V *>(&Bs[32 * J + 16 + r][32 * k + k8]), acv[k], dh);
                 }
             };
-            auto apply = [&](int J, const V &a) {
-                const int s_lo = 32 * J + g4;
+            // ... of both tiles, the B_J operands read once
+            auto bc2 = [&](int J, f32x4 &l0, f32x4 &h0, f32x4 &l1, f32x4 &h1) {
+                l0 = h0 = l1 = h1 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int pt = 0; pt < kP / 16; pt++) {
-                    const uint2 lo = *reinterpret_cast<const uint2 *>(&Xs[pr + 4 * pt][s_lo]);
-                    const uint2 hi = *reinterpret_cast<const uint2 *>(&Xs[pr + 4 * pt][s_lo + 16]);
-                    const V xa = __builtin_bit_cast(V, (uint4{lo.x, lo.y, hi.x, hi.y}));
-                    y[pt] = M::run(xa, a, y[pt]);
+                for (int k = 0; k < KN; k++) {
+                    const V b_lo = *reinterpret_cast<const V *>(&Bs[32 * J + r][32 * k + k8]);
+                    const V b_hi = *reinterpret_cast<const V *>(&Bs[32 * J + 16 + r][32 * k + k8]);
+                    l0 = M::run(b_lo, ac[0][k], l0);
+                    h0 = M::run(b_hi, ac[0][k], h0);
+                    l1 = M::run(b_lo, ac[1][k], l1);
+                    h1 = M::run(b_hi, ac[1][k], h1);
                 }
             };
-            const int nj = rt >> 1;  // blocks J < nj lie below the diagonal, J = nj on it
-            f32x4 d_lo, d_hi;
-            bc(0, d_lo, d_hi);
-            for (int J = 0; J < nj; J++) {
-                f32x4 n_lo, n_hi;
-                bc(J + 1, n_lo, n_hi);
-                const int s_lo = 32 * J + g4;  // this lane's columns: s_lo + i, s_lo + 16 + i
+            // below the diagonal: the row factor exp(A_t - A_J) and the columns' factors
+            auto scale_off = [&](int J, float at, const f32x4 &dl, const f32x4 &dh) {
+                const int s_lo = 32 * J + g4;
                 const float rf = exp_f(at - acum_s[32 * J + 31]);
                 const f32x4 q_lo = *reinterpret_cast<const f32x4 *>(&q_s[s_lo]);
                 const f32x4 q_hi = *reinterpret_cast<const f32x4 *>(&q_s[s_lo + 16]);
                 V a;
 #pragma unroll
                 for (int ii = 0; ii < 4; ii++) {
-                    a[ii] = static_cast<IT>(d_lo[ii] * (rf * q_lo[ii]));
-                    a[4 + ii] = static_cast<IT>(d_hi[ii] * (rf * q_hi[ii]));
+                    a[ii] = static_cast<IT>(dl[ii] * (rf * q_lo[ii]));
+                    a[4 + ii] = static_cast<IT>(dh[ii] * (rf * q_hi[ii]));
                 }
-                apply(J, a);
-                d_lo = n_lo;
-                d_hi = n_hi;
-            }
-            {
-                // the diagonal block: exact factor, causal mask
-                const int s_lo = 32 * nj + g4;
+                return a;
+            };
+            // the diagonal block: exact factor, causal mask
+            auto scale_diag = [&](int J, int tt, float at, const f32x4 &dl, const f32x4 &dh) {
+                const int s_lo = 32 * J + g4;
                 V a;
 #pragma unroll
                 for (int ii = 0; ii < 4; ii++) {
                     const int s0 = s_lo + ii, s1 = s_lo + 16 + ii;
-                    const float m0 = s0 <= tt ? d_lo[ii] * (exp_f(at - acum_s[s0]) * dtp_s[s0]) : 0.0f;
-                    const float m1 = s1 <= tt ? d_hi[ii] * (exp_f(at - acum_s[s1]) * dtp_s[s1]) : 0.0f;
+                    const float m0 = s0 <= tt ? dl[ii] * (exp_f(at - acum_s[s0]) * dtp_s[s0]) : 0.0f;
+                    const float m1 = s1 <= tt ? dh[ii] * (exp_f(at - acum_s[s1]) * dtp_s[s1]) : 0.0f;
                     a[ii] = static_cast<IT>(m0);
                     a[4 + ii] = static_cast<IT>(m1);
                 }
-                apply(nj, a);
+                return a;
+            };
+            auto xop = [&](int J, int pt) {
+                const int s_lo = 32 * J + g4;
+                const uint2 lo = *reinterpret_cast<const uint2 *>(&Xs[pr + 4 * pt][s_lo]);
+                const uint2 hi = *reinterpret_cast<const uint2 *>(&Xs[pr + 4 * pt][s_lo + 16]);
+                return __builtin_bit_cast(V, (uint4{lo.x, lo.y, hi.x, hi.y}));
+            };
+            const int nj0 = rt0 >> 1, nj1 = rt1 >> 1;  // diagonal blocks (nj0 < nj1)
+            if (has1) {
+                f32x4 dl0, dh0, dl1, dh1;
+                bc2(0, dl0, dh0, dl1, dh1);
+                // blocks 0 .. nj0: both tiles; block J + 1's products are formed
+                // while block J's are scaled and applied
+                for (int J = 0; J <= nj0; J++) {
+                    f32x4 nl0, nh0, nl1, nh1;
+                    if (J < nj0)
+                        bc2(J + 1, nl0, nh0, nl1, nh1);
+                    else
+                        bc1(J + 1, ac[1], nl1, nh1);  // J + 1 <= nj1
+                    const V a0 = J < nj0 ? scale_off(J, at0, dl0, dh0) : scale_diag(J, tt0, at0, dl0, dh0);
+                    const V a1 = scale_off(J, at1, dl1, dh1);
+#pragma unroll
+                    for (int pt = 0; pt < kP / 16; pt++) {
+                        const V xa = xop(J, pt);
+                        y0[pt] = M::run(xa, a0, y0[pt]);
+                        y1[pt] = M::run(xa, a1, y1[pt]);
+                    }
+                    dl0 = nl0;
+                    dh0 = nh0;
+                    dl1 = nl1;
+                    dh1 = nh1;
+                }
+                // blocks nj0 + 1 .. nj1: tile 1
+                for (int J = nj0 + 1; J < nj1; J++) {
+                    f32x4 nl1, nh1;
+                    bc1(J + 1, ac[1], nl1, nh1);
+                    const V a1 = scale_off(J, at1, dl1, dh1);
+#pragma unroll
+                    for (int pt = 0; pt < kP / 16; pt++)
+                        y1[pt] = M::run(xop(J, pt), a1, y1[pt]);
+                    dl1 = nl1;
+                    dh1 = nh1;
+                }
+                const V a1 = scale_diag(nj1, tt1, at1, dl1, dh1);
+#pragma unroll
+                for (int pt = 0; pt < kP / 16; pt++)
+                    y1[pt] = M::run(xop(nj1, pt), a1, y1[pt]);
+            } else {
+                f32x4 dl0, dh0;
+                bc1(0, ac[0], dl0, dh0);
+                for (int J = 0; J < nj0; J++) {
+                    f32x4 nl0, nh0;
+                    bc1(J + 1, ac[0], nl0, nh0);
+                    const V a0 = scale_off(J, at0, dl0, dh0);
+#pragma unroll
+                    for (int pt = 0; pt < kP / 16; pt++)
+                        y0[pt] = M::run(xop(J, pt), a0, y0[pt]);
+                    dl0 = nl0;
+                    dh0 = nh0;
+                }
+                const V a0 = scale_diag(nj0, tt0, at0, dl0, dh0);
+#pragma unroll
+                for (int pt = 0; pt < kP / 16; pt++)
+                    y0[pt] = M::run(xop(nj0, pt), a0, y0[pt]);
             }
-            // D x, the gate, the store: y[pt][ii] is p = 16 gq + 4 pt + ii of token tt
-            if (tt < len) {
+            // D x, the gate, the store: y[pt][ii] is p = 16 gq + 4 pt + ii of the token
+            auto finish = [&](const f32x4 (&y)[kP / 16], const V (&xv2)[2], const V (&zv2)[2], int tt) {
+                if (tt >= len)
+                    return;
                 const int64_t tok = t0 + tt;
                 V o[2];
 #pragma unroll
@@ -534,15 +599,18 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(const SsdP
 #pragma unroll
                     for (int ii = 0; ii < 4; ii++) {
                         const int e = 4 * pt + ii;  // 0..15
-                        float v = y[pt][ii] + dh * to_f(xo[i][e / 8][e % 8]);
+                        float v = y[pt][ii] + dh * to_f(xv2[e / 8][e % 8]);
                         if (zs)
-                            v *= silu_f(to_f(zo[i][e / 8][e % 8]));
+                            v *= silu_f(to_f(zv2[e / 8][e % 8]));
                         o[e / 8][e % 8] = static_cast<IT>(v);
                     }
                 IT *orow = outp + tok * sp.out_st + h * sp.out_sh + 16 * gq;
                 *reinterpret_cast<V *>(orow) = o[0];
                 *reinterpret_cast<V *>(orow + 8) = o[1];
-            }
+            };
+            finish(y0, xo[0], zo[0], tt0);
+            if (has1)
+                finish(y1, xo[1], zo[1], tt1);
         }
         if (hk + 1 < nh) {  // uniform: the next head's inputs replace this one's
             __syncthreads();
