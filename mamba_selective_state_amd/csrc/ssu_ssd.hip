@@ -110,11 +110,13 @@ __device__ __forceinline__ float wave_inclusive_sum(float v, int lane) {
 // next head's x row and dt are requested during the current head's products.
 
 constexpr int kStateHeads = 4;
+constexpr int kStateThreads = 512;  // two halves of 256 lanes, lane t % 256 = token
 
 template <typename IT, int N>
-__global__ __launch_bounds__(256) void ssd_chunk_state_kernel(const SsdParams sp) {
+__global__ __launch_bounds__(kStateThreads) void ssd_chunk_state_kernel(const SsdParams sp) {
     using M = Mfma<IT>;
     using V = typename M::V;
+    constexpr int kHalfP = kP / 2, kHalfN = N / 2;  // each half stages half of a token's x and B rows
     __shared__ float wave_tot[kL / 64];
     __shared__ __attribute__((aligned(16))) IT Xs[kP][kL + kPad];  // (w x)^T: [p][t]
     __shared__ __attribute__((aligned(16))) IT Bs[N][kL + kPad];   // B^T: [n][t]
@@ -126,43 +128,48 @@ __global__ __launch_bounds__(256) void ssd_chunk_state_kernel(const SsdParams sp
     const int hb = blockIdx.x % nhb;
     const int h0 = g * sp.hpg + hb * kStateHeads;
     const int nh = sp.hpg - hb * kStateHeads < kStateHeads ? sp.hpg - hb * kStateHeads : kStateHeads;
-    const int t = threadIdx.x;  // token in the chunk (kL threads)
-    const int lane = t & 63, wv = t >> 6;
+    const int t = threadIdx.x;
+    const int tk = t & (kL - 1), half = t / kL;  // token in the chunk, half of the rows
+    const int lane = t & 63, wv = t >> 6, wq = wv & 3;  // wq: the wave within its half
     int64_t t0;
     int len;
     chunk_range(sp, c, &t0, &len);
     // lanes past the chunk read token 0 (always present) and contribute zeros
-    const int64_t tok = t < len ? t0 + t : 0;
+    const int64_t tok = tk < len ? t0 + tk : 0;
 
-    auto load_x = [&](int h, V (&xv)[kP / 8]) {
-        const IT *xrow = static_cast<const IT *>(sp.x) + (tok * sp.x_st + h * sp.x_sh);
+    auto load_x = [&](int h, V (&xv)[kHalfP / 8]) {
+        const IT *xrow = static_cast<const IT *>(sp.x) + (tok * sp.x_st + h * sp.x_sh) + half * kHalfP;
 #pragma unroll
-        for (int p0 = 0; p0 < kP / 8; p0++)
+        for (int p0 = 0; p0 < kHalfP / 8; p0++)
             xv[p0] = *reinterpret_cast<const V *>(xrow + 8 * p0);
     };
-    V xv[kP / 8];
+    V xv[kHalfP / 8];
     load_x(h0, xv);
-    float dtp = t < len ? processed_dt<IT>(sp, t0 + t, h0) : 0.0f;
+    float dtp = tk < len ? processed_dt<IT>(sp, t0 + tk, h0) : 0.0f;
     {
-        const IT *brow = static_cast<const IT *>(sp.B) + (tok * sp.B_st + g * sp.B_sg);
+        const IT *brow = static_cast<const IT *>(sp.B) + (tok * sp.B_st + g * sp.B_sg) + half * kHalfN;
 #pragma unroll
-        for (int n0 = 0; n0 < N; n0 += 8) {
+        for (int n0 = 0; n0 < kHalfN; n0 += 8) {
             const V v = *reinterpret_cast<const V *>(brow + n0);
 #pragma unroll
             for (int k = 0; k < 8; k++)
-                Bs[n0 + k][t] = t < len ? v[k] : static_cast<IT>(0.0f);
+                Bs[half * kHalfN + n0 + k][tk] = tk < len ? v[k] : static_cast<IT>(0.0f);
         }
     }
 
     const int r = lane & 15, k8 = 8 * (lane >> 4);
     const int ksteps = (len + 31) / 32;
+    // products: wave wv takes p tile wv / 2 and half of the n tiles
+    constexpr int kNT = N / 32;  // n tiles per wave
+    const int ptile = wv >> 1, nt0 = (wv & 1) * kNT;
     for (int hk = 0; hk < nh; hk++) {
         const int h = h0 + hk;
         // inclusive prefix sum of dt' A over the chunk: within each wave, then
-        // the wave totals through LDS
+        // the wave totals through LDS (both halves compute the same sums; the
+        // first half publishes them)
         float acum = wave_inclusive_sum(dtp * sp.A[h * sp.A_sh], lane);
-        if (lane == 63)
-            wave_tot[wv] = acum;
+        if (lane == 63 && half == 0)
+            wave_tot[wq] = acum;
         __syncthreads();
         // the chunk's total, summed in the order of the last lane's cumsum
         // (padding adds nothing)
@@ -170,43 +177,45 @@ __global__ __launch_bounds__(256) void ssd_chunk_state_kernel(const SsdParams sp
 #pragma unroll
         for (int k = 0; k < kL / 64; k++) {
             const float wt = wave_tot[k];
-            acum += k < wv ? wt : 0.0f;
+            acum += k < wq ? wt : 0.0f;
             total += k < kL / 64 - 1 ? wt : 0.0f;
         }
-        const int64_t wrow = (c * sp.H + h) * kL;
-        sp.ws_dtp[wrow + t] = dtp;
-        sp.ws_acum[wrow + t] = acum;
-        const float w = t < len ? exp_f(total - acum) * dtp : 0.0f;
+        if (half == 0) {
+            const int64_t wrow = (c * sp.H + h) * kL;
+            sp.ws_dtp[wrow + tk] = dtp;
+            sp.ws_acum[wrow + tk] = acum;
+        }
+        const float w = tk < len ? exp_f(total - acum) * dtp : 0.0f;
 #pragma unroll
-        for (int p0 = 0; p0 < kP / 8; p0++)
+        for (int p0 = 0; p0 < kHalfP / 8; p0++)
 #pragma unroll
             for (int k = 0; k < 8; k++)
-                Xs[8 * p0 + k][t] = static_cast<IT>(to_f(xv[p0][k]) * w);
+                Xs[half * kHalfP + 8 * p0 + k][tk] = static_cast<IT>(to_f(xv[p0][k]) * w);
         __syncthreads();
         if (hk + 1 < nh) {  // the next head's inputs, in flight during the products
             load_x(h + 1, xv);
-            dtp = t < len ? processed_dt<IT>(sp, t0 + t, h + 1) : 0.0f;
+            dtp = tk < len ? processed_dt<IT>(sp, t0 + tk, h + 1) : 0.0f;
         }
 
-        // state[p][n] = sum_t Xs[p][t] Bs[n][t]; wave wv takes rows p = 16 wv ..
-        f32x4 acc[N / 16];
+        // state[p][n] = sum_t Xs[p][t] Bs[n][t]
+        f32x4 acc[kNT];
 #pragma unroll
-        for (int nt = 0; nt < N / 16; nt++)
+        for (int nt = 0; nt < kNT; nt++)
             acc[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         for (int k = 0; k < ksteps; k++) {
-            const V a = *reinterpret_cast<const V *>(&Xs[16 * wv + r][32 * k + k8]);
+            const V a = *reinterpret_cast<const V *>(&Xs[16 * ptile + r][32 * k + k8]);
 #pragma unroll
-            for (int nt = 0; nt < N / 16; nt++) {
-                const V b = *reinterpret_cast<const V *>(&Bs[16 * nt + r][32 * k + k8]);
+            for (int nt = 0; nt < kNT; nt++) {
+                const V b = *reinterpret_cast<const V *>(&Bs[16 * (nt0 + nt) + r][32 * k + k8]);
                 acc[nt] = M::run(a, b, acc[nt]);
             }
         }
         float *dst = sp.ws_state + (c * sp.H + h) * static_cast<int64_t>(kP * N);
 #pragma unroll
-        for (int nt = 0; nt < N / 16; nt++)
+        for (int nt = 0; nt < kNT; nt++)
 #pragma unroll
             for (int i = 0; i < 4; i++)
-                dst[(16 * wv + 4 * (lane >> 4) + i) * N + 16 * nt + r] = acc[nt][i];
+                dst[(16 * ptile + 4 * (lane >> 4) + i) * N + 16 * (nt0 + nt) + r] = acc[nt][i];
         __syncthreads();  // Xs and the wave totals are rewritten for the next head
     }
 }
@@ -628,7 +637,7 @@ int launch_ssd_typed(const SsdParams &sp, int state_dtype, void *stream) {
     const unsigned state_grid = static_cast<unsigned>(sp.nchunks * (sp.H / sp.hpg) *
                                                       ((sp.hpg + kStateHeads - 1) / kStateHeads));
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&ssd_chunk_state_kernel<IT, N>), dim3(state_grid),
-                                   dim3(256), args, 0, s);
+                                   dim3(kStateThreads), args, 0, s);
     if (e != hipSuccess)
         return static_cast<int>(e);
     const unsigned pass_grid = static_cast<unsigned>(sp.H * ((static_cast<int64_t>(kP) * N + 255) / 256));
