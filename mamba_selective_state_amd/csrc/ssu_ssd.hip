@@ -1,18 +1,19 @@
 // SSD packed variable-length prefill for gfx950 (MATE docs, "Mamba / SSU",
 // section "SSD packed prefill"): the same recurrence as the decode step over
 // every token of a packed batch, computed chunk by chunk. Three launches:
-//   ssd_chunk_state_kernel   per (chunk, head): dt' (softplus, dt_limit),
-//                            the decay cumsum, and the chunk's own state
-//                            sum_t exp(A_end - A_t) dt'_t x_t B_t^T (MFMA);
+//   ssd_chunk_state_kernel   per (chunk, group, 4 heads): dt' (softplus,
+//                            dt_limit), the decay cumsum, and the chunk's own
+//                            state sum_t exp(A_end - A_t) dt'_t x_t B_t^T (MFMA);
 //   ssd_state_pass_kernel    per (head, state slice): walks the chunks in
 //                            order, resetting where seq_idx opens a sequence;
-//                            leaves each chunk's entering state in the
-//                            workspace and writes the returned states;
-//   ssd_chunk_scan_kernel    per (chunk, head): y_t = sum_{s<=t} (C_t . B_s)
-//                            exp(A_t - A_s) dt'_s x_s + exp(A_t) C_t . S_in
-//                            + D x_t, gated by silu(z_t) (MFMA).
+//                            writes each chunk's entering state (in the x
+//                            dtype) to the workspace and the returned states;
+//   ssd_chunk_scan_kernel    per (chunk, group, 4 heads): y_t = sum_{s<=t}
+//                            (C_t . B_s) exp(A_t - A_s) dt'_s x_s
+//                            + exp(A_t) C_t . S_in + D x_t, gated by
+//                            silu(z_t) (MFMA).
 // MFMA operands are bf16 / f16 (the x dtype): 16x16x32 tiles with fp32
-// accumulation; the scaled operands (w_t B_t, the masked C.B^T, the entering
+// accumulation; the scaled operands (w_t x_t, the scaled C.B^T, the entering
 // state) are rounded to the x dtype before they enter a product.
 
 #include <hip/hip_runtime.h>
@@ -102,12 +103,14 @@ __device__ __forceinline__ float wave_inclusive_sum(float v, int lane) {
 
 // ---- stage 1: dt', the decay cumsum, and the chunk's own state
 //
-// One workgroup (256 lanes, lane = token of the chunk) per (chunk, group,
-// block of kStateHeads heads of the group): B^T is staged in LDS once for
-// the heads; per head, dt' and the cumsum (an LDS scan), then
-// (w x)^T with w_t = exp(A_end - A_t) dt'_t and the chunk's own state
-// [64 x N] = sum_t (w_t x_t) B_t^T as MFMA tiles (wave w: rows 16w ..). The
-// next head's x row and dt are requested during the current head's products.
+// One workgroup per (chunk, group, block of kStateHeads heads of the group),
+// 512 lanes in two halves of 256 (lane t % 256 = token of the chunk; each
+// half stages half of the token's x and B rows): B^T is staged in LDS once
+// for the heads; per head, dt' and the cumsum (a wave scan plus the wave
+// totals through LDS), then (w x)^T with w_t = exp(A_end - A_t) dt'_t and
+// the chunk's own state [64 x N] = sum_t (w_t x_t) B_t^T as MFMA tiles (wave
+// w: p tile w / 2, half of the n tiles). The next head's x rows and dt are
+// requested during the current head's products.
 
 constexpr int kStateHeads = 4;
 constexpr int kStateThreads = 512;  // two halves of 256 lanes, lane t % 256 = token
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(kStateThreads) void ssd_chunk_state_kernel(const Ss
     const int h0 = g * sp.hpg + hb * kStateHeads;
     const int nh = sp.hpg - hb * kStateHeads < kStateHeads ? sp.hpg - hb * kStateHeads : kStateHeads;
     const int t = threadIdx.x;
-    const int tk = t & (kL - 1), half = t / kL;  // token in the chunk, half of the rows
+    const int tk = t & (kL - 1), half = t / kL;  // token in the chunk, which half of its rows
     const int lane = t & 63, wv = t >> 6, wq = wv & 3;  // wq: the wave within its half
     int64_t t0;
     int len;

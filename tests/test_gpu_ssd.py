@@ -2,8 +2,8 @@
 CPU oracle (MATE docs, "Mamba / SSU", section "SSD packed prefill").
 
 Tolerance: the products run on bf16 / f16 matrix cores, so every operand
-that is scaled before a product (w_t B_t in the chunk states, the masked
-C.B^T in the scan, the entering state read out by C) is rounded to the x
+that is scaled before a product (w_t x_t in the chunk states, the masked
+and scaled C.B^T in the scan, the entering state read out by C) is rounded to the x
 dtype: 2^-9 relative per operand, summed over at most chunk_size + dstate
 terms of random sign. y and the returned states are compared at
 3e-2 x max|ref| (the 16-bit tolerance of the decode path with headroom for
