@@ -242,16 +242,16 @@ SSU_API ssu_status_t ssu_replay_spec_update(const ssu_replay_args_t *args, void 
  * 0x7F / 0xFF are NaN), saturating to +-448. A value decodes as code * X. */
 
 /* Quantize fp32 values to MXFP8:
- *   src     [n] f32 (device), n a multiple of 32; blocks are consecutive
- *           runs of 32 values
- *   codes   [n] u8 (device): E4M3 codes
+ *   src     [n] f32 (device), n a multiple of 32, 16-byte aligned; blocks
+ *           are consecutive runs of 32 values
+ *   codes   [n] u8 (device), 8-byte aligned: E4M3 codes
  *   scales  [n / 32] u8 (device): E8M0 scale bytes
  * A NaN element becomes code 0x7F and does not count toward the block's
  * largest magnitude; a block holding an infinity has no defined scale and
  * its bytes are unspecified (a checkpoint is finite). One kernel on
  * `stream`, asynchronous, allocates nothing; n = 0 launches nothing. All
- * three must be contiguous 1-D tensors (any shape whose element count is n
- * is read as flat). */
+ * three must be contiguous (of any shape: they are read as flat); a rule
+ * broken returns SSU_ERR_VALUE naming it. */
 SSU_API ssu_status_t ssu_mx8_quantize(const ssu_tensor_t *src, const ssu_tensor_t *codes,
                                       const ssu_tensor_t *scales, void *stream);
 
