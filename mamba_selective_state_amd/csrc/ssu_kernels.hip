@@ -691,6 +691,7 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes, replay_waves_per_eu(sizeof(S
     const int64_t lp_tile = (pad ? 0 : s) * (static_cast<int64_t>(p.H) * P * N) + tile_off;  // byte offset of the tile
     // A row's N / 32 scale bytes (at most 8) come in one load per pass.
     auto load_copy = [&]() {
+        if constexpr (LP) {  // compiled for the copy kernels only (their rows hold >= 2 values per lane)
 #pragma unroll
         for (int q = 0; q < PASSES; q++) {
             const int d0 = dw + q * kRowsPerPass + rsub;
@@ -725,6 +726,7 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes, replay_waves_per_eu(sizeof(S
                     S[q][c].v[3] = narrow<ST>(hi.y);
                 }
             }
+        }
         }
     };
     // the folded tile into the read copy (after its fp32 store)
