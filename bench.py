@@ -41,6 +41,7 @@ KERNEL_SOURCES = [os.path.join(ROOT, "mamba_selective_state_amd", "csrc", f)
                   for f in ("ssu_kernels.hip", "ssu_copy.hip", "ssu_ssd.hip", "ssu_internal.h")]
 
 DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 / f16 matrix peak of MI355X
 
 
 def workload(name):
@@ -273,6 +274,10 @@ def ssd_bench_run(args, case, desc):
         torch.cuda.synchronize(d)
     nbytes, flops = ssd_algorithmic(case)
     tflops = flops / (event_ms * 1e-3) / 1e12
+    gbs = nbytes / (event_ms * 1e-3) / 1e9
+    # the binding roofline: the larger of the time the flops need at the bf16
+    # MFMA peak and the time the bytes need at the HBM peak
+    hbm_bound = nbytes / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
     result = {
         "metric": "SSD prefill matrix TFLOP/s (bf16 MFMA) and tokens/s", "value": round(flops * args.steps / wall / 1e12, 3),
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -282,9 +287,16 @@ def ssd_bench_run(args, case, desc):
                    "kernels": "ssd_chunk_state_kernel, ssd_state_pass_kernel, ssd_chunk_scan_kernel"},
         "tokens_per_s": round(np.shape(case["x"])[0] * args.steps / wall, 1),
         "hbm_gbs_algorithmic": round(nbytes / (event_ms * 1e-3) / 1e9, 2),
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": 2500.0, "unit": "TFLOP/s",
-                     "frac": round(tflops / 2500.0, 5), "traffic": traffic_from_counters("ssd"),
+        "roofline": {"bound": "hbm" if hbm_bound else "mfma",
+                     "achieved": round(gbs if hbm_bound else tflops, 3),
+                     "peak": HBM_PEAK_GBS if hbm_bound else MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "GB/s" if hbm_bound else "TFLOP/s",
+                     "frac": round(gbs / HBM_PEAK_GBS if hbm_bound else tflops / MFMA_BF16_PEAK_TFLOPS, 5),
+                     "traffic": traffic_from_counters("ssd"),
                      "kernel_us": round(event_ms * 1e3, 2),
+                     "intensity_flop_per_byte": round(flops / nbytes, 1),
+                     "ridge_flop_per_byte": round(MFMA_BF16_PEAK_TFLOPS * 1e3 / HBM_PEAK_GBS, 1),
+                     "mfma_tflops": round(tflops, 3), "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 5),
                      "note": "the three launches of one call timed together"},
     }
     if not args.no_cpu_baseline:
