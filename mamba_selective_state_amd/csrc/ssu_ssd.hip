@@ -224,51 +224,106 @@ __global__ __launch_bounds__(kStateThreads) void ssd_chunk_state_kernel(const Ss
 }
 
 // ---- stage 2: state passing
+//
+// One workgroup of 256 lanes per (head, slice of 1024 state elements), 4
+// consecutive elements per lane (16-byte loads). The walk over the chunks is
+// sequential; what each step needs besides the chunk's own state -- its decay
+// factor exp(total cumsum) and its sequence -- is staged in LDS for a segment
+// of kPassSeg chunks at a time, so that a step waits on nothing but the own
+// states, which are requested kPassAhead chunks ahead.
+
+constexpr int kPassThreads = 256;
+constexpr int kPassVec = 4;      // elements per lane
+constexpr int kPassAhead = 4;    // own states in flight per lane
+constexpr int kPassSeg = 1024;   // chunks whose decay and sequence are staged at a time
+
+template <typename T> struct alignas(4 * sizeof(T)) Vec4 { T v[4]; };  // one 8- or 16-byte access
 
 template <typename ST, typename IT>
-__global__ __launch_bounds__(256) void ssd_state_pass_kernel(const SsdParams sp) {
+__global__ __launch_bounds__(kPassThreads) void ssd_state_pass_kernel(const SsdParams sp) {
     extern __shared__ int owner[];  // owner[c]: the sequence whose state chunk c returns, or -1
-    const int64_t tiles = (static_cast<int64_t>(kP) * sp.N + 255) / 256;
-    const int h = static_cast<int>(blockIdx.x / tiles);
-    const int64_t e = (blockIdx.x % tiles) * 256 + threadIdx.x;  // element of the [P, N] tile
+    __shared__ float decay_s[kPassSeg];
+    __shared__ int64_t seq_s[kPassSeg];
+    constexpr int kSlice = kPassThreads * kPassVec;
     const int64_t PN = static_cast<int64_t>(kP) * sp.N;
+    const int64_t slices = (PN + kSlice - 1) / kSlice;
+    const int h = static_cast<int>(blockIdx.x / slices);
+    const int64_t e = (blockIdx.x % slices) * kSlice + threadIdx.x * kPassVec;  // first element of the lane
     if (!sp.intermediate) {
-        for (int64_t c = threadIdx.x; c < sp.nchunks; c += 256)
+        for (int64_t c = threadIdx.x; c < sp.nchunks; c += kPassThreads)
             owner[c] = -1;
         __syncthreads();
-        for (int64_t b = threadIdx.x; b < sp.batch; b += 256) {
+        for (int64_t b = threadIdx.x; b < sp.batch; b += kPassThreads) {
             const int64_t c = idx_at(sp.last_chunk, sp.last_chunk_i64, b * sp.last_chunk_s);
             if (c >= 0 && c < sp.nchunks)
                 owner[c] = static_cast<int>(b);
         }
-        __syncthreads();
     }
-    if (e >= PN)
-        return;
+    const bool live = e < PN;  // PN is a multiple of 4: a lane's 4 elements are all in or all out
     ST *outs = static_cast<ST *>(sp.states);
     const ST *init = static_cast<const ST *>(sp.init);
-    float S = 0.0f;
+    const int64_t step = sp.H * PN;  // between one chunk's states and the next's
+    const float *own_p = sp.ws_state + h * PN + (live ? e : 0);
+    auto load_own = [&](int64_t c) {
+        return c < sp.nchunks ? *reinterpret_cast<const f32x4 *>(own_p + c * step) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    };
+    f32x4 own[kPassAhead];
+#pragma unroll
+    for (int j = 0; j < kPassAhead; j++)
+        own[j] = load_own(j);
+    f32x4 S = {0.0f, 0.0f, 0.0f, 0.0f};
     int64_t prev = -1;
-    float own = sp.nchunks > 0 ? sp.ws_state[h * PN + e] : 0.0f;
-    for (int64_t c = 0; c < sp.nchunks; c++) {
-        const int64_t seq = idx_at(sp.seq_idx, sp.seq_idx_i64, c * sp.seq_idx_s);
-        if (c == 0 || seq != prev)  // a chunk opens a sequence: its entering state
-            S = (init && seq >= 0 && seq < sp.batch) ? static_cast<float>(init[(seq * sp.H + h) * PN + e]) : 0.0f;
-        prev = seq;
-        const int64_t at = (c * sp.H + h) * PN + e;
-        // next chunk's own state requested before this one is overwritten
-        const float own_next = c + 1 < sp.nchunks ? sp.ws_state[at + sp.H * PN] : 0.0f;
-        const float total = sp.ws_acum[(c * sp.H + h) * kL + kL - 1];
-        static_cast<IT *>(sp.ws_sin)[at] = static_cast<IT>(S);  // the entering state, as the scan reads it
-        S = exp_f(total) * S + own;
-        if (sp.intermediate) {
-            outs[at] = static_cast<ST>(S);
-        } else {
-            const int b = owner[c];
-            if (b >= 0)
-                outs[(static_cast<int64_t>(b) * sp.H + h) * PN + e] = static_cast<ST>(S);
+    for (int64_t c0 = 0; c0 < sp.nchunks; c0 += kPassSeg) {
+        const int64_t nseg = sp.nchunks - c0 < kPassSeg ? sp.nchunks - c0 : kPassSeg;
+        __syncthreads();  // the previous segment's entries are read; the owner map is written
+        for (int64_t k = threadIdx.x; k < nseg; k += kPassThreads) {
+            const int64_t c = c0 + k;
+            decay_s[k] = exp_f(sp.ws_acum[(c * sp.H + h) * kL + kL - 1]);
+            seq_s[k] = idx_at(sp.seq_idx, sp.seq_idx_i64, c * sp.seq_idx_s);
         }
-        own = own_next;
+        __syncthreads();
+        // kPassAhead chunks per trip (the register ring's index is a constant)
+        for (int64_t k0 = 0; k0 < nseg; k0 += kPassAhead) {
+#pragma unroll
+            for (int j = 0; j < kPassAhead; j++) {
+                const int64_t k = k0 + j;
+                if (k < nseg) {  // uniform
+                    const int64_t c = c0 + k;
+                    const int64_t seq = seq_s[k];
+                    if (c == 0 || seq != prev) {  // a chunk opens a sequence: its entering state
+                        const bool has = init && seq >= 0 && seq < sp.batch && live;
+                        const ST *ip = init + ((has ? seq : 0) * sp.H + h) * PN + (live ? e : 0);
+#pragma unroll
+                        for (int i = 0; i < kPassVec; i++)
+                            S[i] = has ? static_cast<float>(ip[i]) : 0.0f;
+                    }
+                    prev = seq;
+                    const f32x4 o = own[j];
+                    own[j] = load_own(c + kPassAhead);
+                    const int64_t at = (c * sp.H + h) * PN + e;
+                    const float d = decay_s[k];
+                    if (live) {
+                        Vec4<IT> sv;
+#pragma unroll
+                        for (int i = 0; i < kPassVec; i++)
+                            sv.v[i] = static_cast<IT>(S[i]);  // the entering state, as the scan reads it
+                        *reinterpret_cast<Vec4<IT> *>(static_cast<IT *>(sp.ws_sin) + at) = sv;
+                    }
+#pragma unroll
+                    for (int i = 0; i < kPassVec; i++)
+                        S[i] = d * S[i] + o[i];
+                    const int b = sp.intermediate ? 0 : owner[c];
+                    if (live && (sp.intermediate || b >= 0)) {
+                        Vec4<ST> ov;
+#pragma unroll
+                        for (int i = 0; i < kPassVec; i++)
+                            ov.v[i] = static_cast<ST>(S[i]);
+                        ST *dst = sp.intermediate ? outs + at : outs + (static_cast<int64_t>(b) * sp.H + h) * PN + e;
+                        *reinterpret_cast<Vec4<ST> *>(dst) = ov;
+                    }
+                }
+            }
+        }
     }
 }
 
@@ -289,12 +344,15 @@ __device__ __forceinline__ int32_t xcd_grouped(int32_t id, int32_t n) {
 // y_t = exp(A_t) C_t . S_in + sum_{s<=t} (C_t . B_s) exp(A_t - A_s) dt'_s x_s
 //       + D x_t, gated by silu(z_t);   A = the decay cumsum of the chunk.
 // One workgroup of 8 waves per (chunk, group, block of kScanHeads heads of
-// the group). The chunk's B rows are staged in LDS once and each wave's C
-// operands stay in registers for all its heads; per head, x^T, the entering
-// state and the cumsums are staged in LDS, the next head's requested while
-// the current one computes. Rows t in 16-row tiles (wave w takes tiles w and
-// 15-w: equal work under the causal mask), columns s in 32-column blocks J.
-// Both products are formed transposed, so that a lane owns one token t:
+// the group). Rows t in 16-row tiles (wave w takes tiles w and 15-w: equal
+// work under the causal mask), columns s in 32-column blocks J. C . B^T does
+// not depend on the head: each wave forms its part once, for its 9 (block,
+// tile) pairs, and keeps it in registers (fp32) for all heads of the
+// workgroup; per head only the decay scaling and the products with x and the
+// entering state remain. Per head, x^T, the entering state and the cumsums
+// are staged in LDS, the next head's requested while the current one
+// computes. Both products are formed transposed, so that a lane owns one
+// token t:
 //   (B_J C^T)[s][t]: the lane holds t and the 8 columns s = 32J + 4g + i,
 //   32J + 16 + 4g + i (g = lane / 16, i < 4), which after scaling is the
 //   B operand of y^T += x_J^T (...)^T with that k order (the x side reads
@@ -302,14 +360,20 @@ __device__ __forceinline__ int32_t xcd_grouped(int32_t id, int32_t n) {
 //   y^T[p][t]: MFMA row m of p tile pt is p = 16 (m / 4) + 4 pt + m % 4, so
 //   the lane ends with the 16 consecutive p = 16g .. 16g + 15 of its token
 //   (two 16-byte stores, loads of x and z alike).
+// Dim p is stored at LDS row 4 (p % 16) + p / 16 of x^T and of the entering
+// state, so the 16 rows an operand read touches start 4 banks apart.
 // Below the diagonal block the decay factors into a row and a column term,
 // exp(A_t - A_s) dt'_s = exp(A_t - A_J) * exp(A_J - A_s) dt'_s with A_J the
 // cumsum at the block's last token; both are at most 1 there (the cumsum
 // does not increase). The diagonal block takes the exact factor per element
 // under the causal mask.
 constexpr int kScanThreads = 512;
-constexpr int kScanTiles = 2;  // 16-token tiles per wave
-constexpr int kScanHeads = 4;  // heads per workgroup
+constexpr int kScanTiles = 2;   // 16-token tiles per wave
+constexpr int kScanHeads = 4;   // heads per workgroup
+constexpr int kScanSlots = 9;   // (block, tile) pairs of a wave: (w / 2 + 1) + ((15 - w) / 2 + 1)
+constexpr int kXsRow = kL + 24; // x^T row stride (elements): 140 words, 12 banks past a multiple of 64
+
+__device__ __forceinline__ int dim_row(int p) { return 4 * (p & 15) + (p >> 4); }
 
 template <typename IT, int N>
 __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(const SsdParams sp) {
@@ -320,14 +384,14 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(const SsdP
     constexpr int kRowPieces = N / 8;               // 16-byte pieces of a B row
     constexpr int kBPass = kL * kRowPieces / kScanThreads;
     static_assert(kSinSeg == 8 || kSinSeg == 16, "whole 16-byte LDS stores");
-    static_assert(kP == 64, "a lane's 16 consecutive p per g");
-    __shared__ float acum_s[kL], dtp_s[kL];
+    static_assert(kP == 64, "a lane's 16 consecutive p per g; the dim-row map");
+    static_assert(kL == 256 && kScanThreads == 512, "8 waves of two 16-token tiles");
+    __shared__ __attribute__((aligned(16))) float acum_s[kL];
+    __shared__ __attribute__((aligned(16))) float dtp_s[kL];
     __shared__ __attribute__((aligned(16))) float q_s[kL];          // column factors
-    // x^T: [p][s]; rows of kL + 4 elements (read 8 bytes at a time) spread the
-    // transposed 4-byte stores of one wave over the banks
-    __shared__ __attribute__((aligned(16))) IT Xs[kP][kL + 4];
+    __shared__ __attribute__((aligned(16))) IT Xs[kP][kXsRow];      // x^T: [dim row][s]
     __shared__ __attribute__((aligned(16))) IT Bs[kL][N + kPad];    // B rows [s][n]
-    __shared__ __attribute__((aligned(16))) IT Sin[kP][N + kPad];   // entering state [p][n]
+    __shared__ __attribute__((aligned(16))) IT Sin[kP][N + kPad];   // entering state [dim row][n]
 
     const int ngroups = static_cast<int>(sp.H / sp.hpg);
     const int nhb = (sp.hpg + kScanHeads - 1) / kScanHeads;
@@ -341,6 +405,10 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(const SsdP
     int64_t t0;
     int len;
     chunk_range(sp, c, &t0, &len);
+    // the same for every lane: keep them (and what depends on them) scalar
+    len = __builtin_amdgcn_readfirstlane(len);
+    t0 = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(static_cast<int32_t>(t0 >> 32))) << 32 |
+         static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int32_t>(t0)));
     if (len == 0)
         return;  // uniform
     const int lane = t & 63, wv = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform per wave
@@ -384,7 +452,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(const SsdP
             for (int e = 0; e < 8; e++) {
                 const IT lo = j2 < len ? in.xv[u][0][e] : static_cast<IT>(0.0f);
                 const IT hi = j2 + 1 < len ? in.xv[u][1][e] : static_cast<IT>(0.0f);
-                *reinterpret_cast<uint32_t *>(&Xs[pc + e][j2]) =
+                *reinterpret_cast<uint32_t *>(&Xs[dim_row(pc + e)][j2]) =
                     static_cast<uint32_t>(__builtin_bit_cast(uint16_t, lo)) |
                     (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, hi)) << 16);
             }
@@ -392,7 +460,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(const SsdP
         const int sp0 = (t * kSinSeg) / N, sn0 = (t * kSinSeg) % N;
 #pragma unroll
         for (int k = 0; k < kSinSeg / 8; k++)
-            *reinterpret_cast<V *>(&Sin[sp0][sn0 + 8 * k]) = in.sv[k];
+            *reinterpret_cast<V *>(&Sin[dim_row(sp0)][sn0 + 8 * k]) = in.sv[k];
         if (t < kL) {
             acum_s[t] = in.at;
             dtp_s[t] = in.dt;
@@ -432,197 +500,188 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(const SsdP
     }
     __syncthreads();
 
+    // The wave's (block, tile) slots: tile rt0 = wv keeps block J in slot J
+    // (J = 0 .. nj0, its diagonal block nj0 = rt0 / 2 <= 3), tile
+    // rt1 = 15 - wv block J in slot 8 - J (J = 0 .. nj1, nj1 = rt1 / 2 =
+    // 7 - nj0): slots nj0 + 1 .. 8, and every slot index a constant.
+    const int rt0 = rts[0], rt1 = rts[1];
+    const int nj0 = rt0 >> 1, nj1 = rt1 >> 1;
+    const bool act0 = rt0 < ntiles, act1 = rt1 < ntiles;  // uniform; act1 implies act0
+    const int tt0 = 16 * rt0 + r, tt1 = 16 * rt1 + r;     // the lane's tokens
+    // (B_J C^T) of one tile: the lane's token, columns s_lo + i, s_lo + 16 + i
+    auto bc = [&](int J, const V (&acv)[KN], f32x4 (&d)[2]) {
+        d[0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        d[1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int k = 0; k < KN; k++) {
+            d[0] = M::run(*reinterpret_cast<const V *>(&Bs[32 * J + r][32 * k + k8]), acv[k], d[0]);
+            d[1] = M::run(*reinterpret_cast<const V *>(&Bs[32 * J + 16 + r][32 * k + k8]), acv[k], d[1]);
+        }
+    };
+    f32x4 cb[kScanSlots][2];
+#pragma unroll
+    for (int q = 0; q < kScanSlots; q++)
+        cb[q][0] = cb[q][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if (act0) {
+#pragma unroll
+        for (int J = 0; J < 4; J++)
+            if (J <= nj0)
+                bc(J, ac[0], cb[J]);
+    }
+    if (act1) {
+#pragma unroll
+        for (int J = 0; J < 8; J++)
+            if (J <= nj1)
+                bc(J, ac[1], cb[8 - J]);
+    }
+    // B is no longer needed: its rows take the C rows (row = token), the B
+    // operands of the entering-state product, read back per head by the
+    // lanes that wrote them
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kScanTiles; i++)
+#pragma unroll
+        for (int k = 0; k < KN; k++)
+            *reinterpret_cast<V *>(&Bs[16 * rts[i] + r][32 * k + k8]) = ac[i][k];
+    IT(*const Cs)[N + kPad] = Bs;
+
     IT *outp = static_cast<IT *>(sp.out);
     const IT *zs = static_cast<const IT *>(sp.z);
     const int pr = 16 * (r >> 2) + (r & 3);  // p of MFMA row r in p tile 0 (+ 4 pt)
+    int xrow[kP / 16];                       // LDS row of p = pr + 4 pt
+#pragma unroll
+    for (int pt = 0; pt < kP / 16; pt++)
+        xrow[pt] = dim_row(pr + 4 * pt);
 
     for (int hk = 0; hk < nh; hk++) {
         const int h = h0 + hk;
         HeadIn next;
         if (hk + 1 < nh)
             load_head(h + 1, next);  // in flight during this head
-        // this head's x and z of the lane's tokens (16 consecutive p), for the output
-        V xo[kScanTiles][2], zo[kScanTiles][2];
-#pragma unroll
-        for (int i = 0; i < kScanTiles; i++) {
-            const int tr = 16 * rts[i] + r;
-            const int64_t tok = t0 + (tr < len ? tr : len - 1);
-            const IT *xrow = static_cast<const IT *>(sp.x) + tok * sp.x_st + h * sp.x_sh + 16 * gq;
-            const IT *zrow = zs + tok * sp.z_st + h * sp.z_sh + 16 * gq;
+        const float dh = sp.D ? sp.D[h * sp.D_sh] : 0.0f;
+        // x and z of the lane's token (16 consecutive p), for the output
+        auto load_xz = [&](int tt, V (&xv2)[2], V (&zv2)[2]) {
+            const int64_t tok = t0 + (tt < len ? tt : len - 1);
+            const IT *xg = static_cast<const IT *>(sp.x) + tok * sp.x_st + h * sp.x_sh + 16 * gq;
+            const IT *zg = zs + tok * sp.z_st + h * sp.z_sh + 16 * gq;
 #pragma unroll
             for (int k = 0; k < 2; k++) {
-                xo[i][k] = *reinterpret_cast<const V *>(xrow + 8 * k);
-                zo[i][k] = zs ? *reinterpret_cast<const V *>(zrow + 8 * k) : V{};
+                xv2[k] = *reinterpret_cast<const V *>(xg + 8 * k);
+                zv2[k] = zs ? *reinterpret_cast<const V *>(zg + 8 * k) : V{};
             }
-        }
-        const float dh = sp.D ? sp.D[h * sp.D_sh] : 0.0f;
+        };
+        // the entering state's contribution, y^T = S_in C^T, scaled by exp(A_t)
+        auto init = [&](int tt, float at, f32x4 (&y)[kP / 16]) {
+            const float rs = exp_f(at);
+#pragma unroll
+            for (int pt = 0; pt < kP / 16; pt++) {
+                f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int k = 0; k < KN; k++)
+                    acc = M::run(*reinterpret_cast<const V *>(&Sin[xrow[pt]][32 * k + k8]),
+                                 *reinterpret_cast<const V *>(&Cs[tt][32 * k + k8]), acc);
+#pragma unroll
+                for (int ii = 0; ii < 4; ii++)
+                    acc[ii] *= rs;
+                y[pt] = acc;
+            }
+        };
+        // below the diagonal: the row factor exp(A_t - A_J) and the columns' factors
+        auto scale_off = [&](int J, float at, const f32x4 (&d)[2]) {
+            const int s_lo = 32 * J + g4;
+            const float rf = exp_f(at - acum_s[32 * J + 31]);
+            const f32x4 q_lo = *reinterpret_cast<const f32x4 *>(&q_s[s_lo]);
+            const f32x4 q_hi = *reinterpret_cast<const f32x4 *>(&q_s[s_lo + 16]);
+            V a;
+#pragma unroll
+            for (int ii = 0; ii < 4; ii++) {
+                a[ii] = static_cast<IT>(d[0][ii] * (rf * q_lo[ii]));
+                a[4 + ii] = static_cast<IT>(d[1][ii] * (rf * q_hi[ii]));
+            }
+            return a;
+        };
+        // the diagonal block: exact factor, causal mask (a select, no branch;
+        // A_t - A_s <= 0 for s <= t, the clamp only keeps the masked-out
+        // factors finite)
+        auto scale_diag = [&](int J, int tt, float at, const f32x4 (&d)[2]) {
+            const int s_lo = 32 * J + g4;
+            const f32x4 a_lo = *reinterpret_cast<const f32x4 *>(&acum_s[s_lo]);
+            const f32x4 a_hi = *reinterpret_cast<const f32x4 *>(&acum_s[s_lo + 16]);
+            const f32x4 w_lo = *reinterpret_cast<const f32x4 *>(&dtp_s[s_lo]);
+            const f32x4 w_hi = *reinterpret_cast<const f32x4 *>(&dtp_s[s_lo + 16]);
+            // the compares are made here, per head: hoisted out of the head
+            // loop their masks would hold 2 SGPRs each for the whole loop
+            int lim = tt - s_lo;
+            asm volatile("" : "+v"(lim));
+            V a;
+#pragma unroll
+            for (int ii = 0; ii < 4; ii++) {
+                const float m0 = d[0][ii] * (exp_f(fminf(at - a_lo[ii], 0.0f)) * w_lo[ii]);
+                const float m1 = d[1][ii] * (exp_f(fminf(at - a_hi[ii], 0.0f)) * w_hi[ii]);
+                a[ii] = static_cast<IT>(ii <= lim ? m0 : 0.0f);
+                a[4 + ii] = static_cast<IT>(16 + ii <= lim ? m1 : 0.0f);
+            }
+            return a;
+        };
+        auto xop = [&](int J, int pt) {
+            const int s_lo = 32 * J + g4;
+            const uint2 lo = *reinterpret_cast<const uint2 *>(&Xs[xrow[pt]][s_lo]);
+            const uint2 hi = *reinterpret_cast<const uint2 *>(&Xs[xrow[pt]][s_lo + 16]);
+            return __builtin_bit_cast(V, (uint4{lo.x, lo.y, hi.x, hi.y}));
+        };
+        // block J of a tile: scaled, then y^T += x_J^T (...)^T
+        auto block = [&](int J, bool diag, int tt, float at, const f32x4 (&d)[2], f32x4 (&y)[kP / 16]) {
+            const V a = diag ? scale_diag(J, tt, at, d) : scale_off(J, at, d);
+#pragma unroll
+            for (int pt = 0; pt < kP / 16; pt++)
+                y[pt] = M::run(xop(J, pt), a, y[pt]);
+        };
+        // D x, the gate, the store: y[pt][ii] is p = 16 gq + 4 pt + ii of the token
+        auto finish = [&](const f32x4 (&y)[kP / 16], const V (&xv2)[2], const V (&zv2)[2], int tt) {
+            if (tt >= len)
+                return;
+            const int64_t tok = t0 + tt;
+            V o[2];
+#pragma unroll
+            for (int pt = 0; pt < kP / 16; pt++)
+#pragma unroll
+                for (int ii = 0; ii < 4; ii++) {
+                    const int e = 4 * pt + ii;  // 0..15
+                    float v = y[pt][ii] + dh * to_f(xv2[e / 8][e % 8]);
+                    if (zs)
+                        v *= silu_f(to_f(zv2[e / 8][e % 8]));
+                    o[e / 8][e % 8] = static_cast<IT>(v);
+                }
+            IT *orow = outp + tok * sp.out_st + h * sp.out_sh + 16 * gq;
+            *reinterpret_cast<V *>(orow) = o[0];
+            *reinterpret_cast<V *>(orow + 8) = o[1];
+        };
 
-        // The wave's tiles: rt0 = wv (blocks J <= rt0 / 2) and rt1 = 15 - wv
-        // (J <= rt1 / 2, more). For J <= rt0 / 2 both tiles read the same B_J
-        // and x operands: those blocks are done for both at once (two
-        // independent MFMA chains), the rest for tile 1 alone.
-        const int rt0 = rts[0], rt1 = rts[1];
-        const bool has1 = rt1 < ntiles;  // implies rt0 < ntiles
-        if (rt0 < ntiles) {  // uniform per wave
-            const int tt0 = 16 * rt0 + r, tt1 = 16 * rt1 + r;  // the lane's tokens
-            const float at0 = acum_s[tt0], at1 = acum_s[tt1];
-            // the entering state's contribution, y^T = S_in C^T, scaled by exp(A_t)
-            auto init = [&](const V (&acv)[KN], float at, f32x4 (&y)[kP / 16]) {
-                const float rs = exp_f(at);
+        // the two tiles one after the other: one tile's accumulators and
+        // x, z rows are live at a time
+        if (act0) {  // uniform per wave
+            V xv2[2], zv2[2];
+            load_xz(tt0, xv2, zv2);
+            const float at0 = acum_s[tt0];
+            f32x4 y[kP / 16];
+            init(tt0, at0, y);
 #pragma unroll
-                for (int pt = 0; pt < kP / 16; pt++) {
-                    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+            for (int J = 0; J < 4; J++)
+                if (J <= nj0)  // uniform
+                    block(J, J == nj0, tt0, at0, cb[J], y);
+            finish(y, xv2, zv2, tt0);
+        }
+        if (act1) {
+            V xv2[2], zv2[2];
+            load_xz(tt1, xv2, zv2);
+            const float at1 = acum_s[tt1];
+            f32x4 y[kP / 16];
+            init(tt1, at1, y);
 #pragma unroll
-                    for (int k = 0; k < KN; k++)
-                        acc = M::run(*reinterpret_cast<const V *>(&Sin[pr + 4 * pt][32 * k + k8]), acv[k], acc);
-#pragma unroll
-                    for (int ii = 0; ii < 4; ii++)
-                        acc[ii] *= rs;
-                    y[pt] = acc;
-                }
-            };
-            f32x4 y0[kP / 16], y1[kP / 16];
-            init(ac[0], at0, y0);
-            if (has1)
-                init(ac[1], at1, y1);
-            // (B_J C^T) of one tile: the lane's token, columns s_lo + i, s_lo + 16 + i
-            auto bc1 = [&](int J, const V (&acv)[KN], f32x4 &dl, f32x4 &dh) {
-                dl = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-                dh = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int k = 0; k < KN; k++) {
-                    dl = M::run(*reinterpret_cast<const V *>(&Bs[32 * J + r][32 * k + k8]), acv[k], dl);
-                    dh = M::run(*reinterpret_cast<const V *>(&Bs[32 * J + 16 + r][32 * k + k8]), acv[k], dh);
-                }
-            };
-            // ... of both tiles, the B_J operands read once
-            auto bc2 = [&](int J, f32x4 &l0, f32x4 &h0, f32x4 &l1, f32x4 &h1) {
-                l0 = h0 = l1 = h1 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int k = 0; k < KN; k++) {
-                    const V b_lo = *reinterpret_cast<const V *>(&Bs[32 * J + r][32 * k + k8]);
-                    const V b_hi = *reinterpret_cast<const V *>(&Bs[32 * J + 16 + r][32 * k + k8]);
-                    l0 = M::run(b_lo, ac[0][k], l0);
-                    h0 = M::run(b_hi, ac[0][k], h0);
-                    l1 = M::run(b_lo, ac[1][k], l1);
-                    h1 = M::run(b_hi, ac[1][k], h1);
-                }
-            };
-            // below the diagonal: the row factor exp(A_t - A_J) and the columns' factors
-            auto scale_off = [&](int J, float at, const f32x4 &dl, const f32x4 &dh) {
-                const int s_lo = 32 * J + g4;
-                const float rf = exp_f(at - acum_s[32 * J + 31]);
-                const f32x4 q_lo = *reinterpret_cast<const f32x4 *>(&q_s[s_lo]);
-                const f32x4 q_hi = *reinterpret_cast<const f32x4 *>(&q_s[s_lo + 16]);
-                V a;
-#pragma unroll
-                for (int ii = 0; ii < 4; ii++) {
-                    a[ii] = static_cast<IT>(dl[ii] * (rf * q_lo[ii]));
-                    a[4 + ii] = static_cast<IT>(dh[ii] * (rf * q_hi[ii]));
-                }
-                return a;
-            };
-            // the diagonal block: exact factor, causal mask
-            auto scale_diag = [&](int J, int tt, float at, const f32x4 &dl, const f32x4 &dh) {
-                const int s_lo = 32 * J + g4;
-                V a;
-#pragma unroll
-                for (int ii = 0; ii < 4; ii++) {
-                    const int s0 = s_lo + ii, s1 = s_lo + 16 + ii;
-                    const float m0 = s0 <= tt ? dl[ii] * (exp_f(at - acum_s[s0]) * dtp_s[s0]) : 0.0f;
-                    const float m1 = s1 <= tt ? dh[ii] * (exp_f(at - acum_s[s1]) * dtp_s[s1]) : 0.0f;
-                    a[ii] = static_cast<IT>(m0);
-                    a[4 + ii] = static_cast<IT>(m1);
-                }
-                return a;
-            };
-            auto xop = [&](int J, int pt) {
-                const int s_lo = 32 * J + g4;
-                const uint2 lo = *reinterpret_cast<const uint2 *>(&Xs[pr + 4 * pt][s_lo]);
-                const uint2 hi = *reinterpret_cast<const uint2 *>(&Xs[pr + 4 * pt][s_lo + 16]);
-                return __builtin_bit_cast(V, (uint4{lo.x, lo.y, hi.x, hi.y}));
-            };
-            const int nj0 = rt0 >> 1, nj1 = rt1 >> 1;  // diagonal blocks (nj0 < nj1)
-            if (has1) {
-                f32x4 dl0, dh0, dl1, dh1;
-                bc2(0, dl0, dh0, dl1, dh1);
-                // blocks 0 .. nj0: both tiles; block J + 1's products are formed
-                // while block J's are scaled and applied
-                for (int J = 0; J <= nj0; J++) {
-                    f32x4 nl0, nh0, nl1, nh1;
-                    if (J < nj0)
-                        bc2(J + 1, nl0, nh0, nl1, nh1);
-                    else
-                        bc1(J + 1, ac[1], nl1, nh1);  // J + 1 <= nj1
-                    const V a0 = J < nj0 ? scale_off(J, at0, dl0, dh0) : scale_diag(J, tt0, at0, dl0, dh0);
-                    const V a1 = scale_off(J, at1, dl1, dh1);
-#pragma unroll
-                    for (int pt = 0; pt < kP / 16; pt++) {
-                        const V xa = xop(J, pt);
-                        y0[pt] = M::run(xa, a0, y0[pt]);
-                        y1[pt] = M::run(xa, a1, y1[pt]);
-                    }
-                    dl0 = nl0;
-                    dh0 = nh0;
-                    dl1 = nl1;
-                    dh1 = nh1;
-                }
-                // blocks nj0 + 1 .. nj1: tile 1
-                for (int J = nj0 + 1; J < nj1; J++) {
-                    f32x4 nl1, nh1;
-                    bc1(J + 1, ac[1], nl1, nh1);
-                    const V a1 = scale_off(J, at1, dl1, dh1);
-#pragma unroll
-                    for (int pt = 0; pt < kP / 16; pt++)
-                        y1[pt] = M::run(xop(J, pt), a1, y1[pt]);
-                    dl1 = nl1;
-                    dh1 = nh1;
-                }
-                const V a1 = scale_diag(nj1, tt1, at1, dl1, dh1);
-#pragma unroll
-                for (int pt = 0; pt < kP / 16; pt++)
-                    y1[pt] = M::run(xop(nj1, pt), a1, y1[pt]);
-            } else {
-                f32x4 dl0, dh0;
-                bc1(0, ac[0], dl0, dh0);
-                for (int J = 0; J < nj0; J++) {
-                    f32x4 nl0, nh0;
-                    bc1(J + 1, ac[0], nl0, nh0);
-                    const V a0 = scale_off(J, at0, dl0, dh0);
-#pragma unroll
-                    for (int pt = 0; pt < kP / 16; pt++)
-                        y0[pt] = M::run(xop(J, pt), a0, y0[pt]);
-                    dl0 = nl0;
-                    dh0 = nh0;
-                }
-                const V a0 = scale_diag(nj0, tt0, at0, dl0, dh0);
-#pragma unroll
-                for (int pt = 0; pt < kP / 16; pt++)
-                    y0[pt] = M::run(xop(nj0, pt), a0, y0[pt]);
-            }
-            // D x, the gate, the store: y[pt][ii] is p = 16 gq + 4 pt + ii of the token
-            auto finish = [&](const f32x4 (&y)[kP / 16], const V (&xv2)[2], const V (&zv2)[2], int tt) {
-                if (tt >= len)
-                    return;
-                const int64_t tok = t0 + tt;
-                V o[2];
-#pragma unroll
-                for (int pt = 0; pt < kP / 16; pt++)
-#pragma unroll
-                    for (int ii = 0; ii < 4; ii++) {
-                        const int e = 4 * pt + ii;  // 0..15
-                        float v = y[pt][ii] + dh * to_f(xv2[e / 8][e % 8]);
-                        if (zs)
-                            v *= silu_f(to_f(zv2[e / 8][e % 8]));
-                        o[e / 8][e % 8] = static_cast<IT>(v);
-                    }
-                IT *orow = outp + tok * sp.out_st + h * sp.out_sh + 16 * gq;
-                *reinterpret_cast<V *>(orow) = o[0];
-                *reinterpret_cast<V *>(orow + 8) = o[1];
-            };
-            finish(y0, xo[0], zo[0], tt0);
-            if (has1)
-                finish(y1, xo[1], zo[1], tt1);
+            for (int J = 0; J < 8; J++)
+                if (J <= nj1)  // uniform; nj1 >= 4
+                    block(J, J == nj1, tt1, at1, cb[8 - J], y);
+            finish(y, xv2, zv2, tt1);
         }
         if (hk + 1 < nh) {  // uniform: the next head's inputs replace this one's
             __syncthreads();
@@ -643,12 +702,13 @@ int launch_ssd_typed(const SsdParams &sp, int state_dtype, void *stream) {
                                    dim3(kStateThreads), args, 0, s);
     if (e != hipSuccess)
         return static_cast<int>(e);
-    const unsigned pass_grid = static_cast<unsigned>(sp.H * ((static_cast<int64_t>(kP) * N + 255) / 256));
+    const unsigned pass_grid =
+        static_cast<unsigned>(sp.H * ((static_cast<int64_t>(kP) * N + kPassThreads * kPassVec - 1) / (kPassThreads * kPassVec)));
     const size_t owner_bytes = sp.intermediate ? 0 : static_cast<size_t>(sp.nchunks) * sizeof(int);
     const void *pass = state_dtype == SSU_F32    ? reinterpret_cast<const void *>(&ssd_state_pass_kernel<float, IT>)
                        : state_dtype == SSU_F16  ? reinterpret_cast<const void *>(&ssd_state_pass_kernel<_Float16, IT>)
                                                  : reinterpret_cast<const void *>(&ssd_state_pass_kernel<__bf16, IT>);
-    e = hipLaunchKernel(pass, dim3(pass_grid), dim3(256), args, owner_bytes, s);
+    e = hipLaunchKernel(pass, dim3(pass_grid), dim3(kPassThreads), args, owner_bytes, s);
     if (e != hipSuccess)
         return static_cast<int>(e);
     const unsigned scan_grid = static_cast<unsigned>(sp.nchunks * (sp.H / sp.hpg) *
