@@ -78,13 +78,22 @@ __device__ __forceinline__ void chunk_range(const SsdParams &sp, int64_t c, int6
 }
 
 // dt' of token t, head h: softplus(dt + dt_bias) (or dt + dt_bias), then the
-// dt_limit clamp
+// dt_limit clamp; the load and the arithmetic apart, so that the load can be
+// issued early
+// (the raw bits: converted at use, so that no wait follows the load)
 template <typename IT>
-__device__ __forceinline__ float processed_dt(const SsdParams &sp, int64_t t, int h) {
+__device__ __forceinline__ uint32_t raw_dt(const SsdParams &sp, int64_t t, int h) {
     const int64_t i = t * sp.dt_st + static_cast<int64_t>(h) * sp.dt_sh;
-    float v = sp.dt_f32 ? static_cast<const float *>(sp.dt)[i] : to_f(static_cast<const IT *>(sp.dt)[i]);
-    if (sp.dt_bias)
-        v += sp.dt_bias[h * sp.bias_sh];
+    return sp.dt_f32 ? static_cast<const uint32_t *>(sp.dt)[i] : static_cast<const uint16_t *>(sp.dt)[i];
+}
+template <typename IT>
+__device__ __forceinline__ float dt_value(const SsdParams &sp, uint32_t bits) {
+    return sp.dt_f32 ? __builtin_bit_cast(float, bits)
+                     : to_f(__builtin_bit_cast(IT, static_cast<uint16_t>(bits)));
+}
+// bias: dt_bias of the head, 0 without one
+__device__ __forceinline__ float processed_dt(const SsdParams &sp, float v, float bias) {
+    v += bias;
     if (sp.softplus)
         v = softplus_f(v);
     v = v < sp.dt_lo ? sp.dt_lo : v;
@@ -99,6 +108,18 @@ __device__ __forceinline__ float wave_inclusive_sum(float v, int lane) {
         v += lane >= off ? u : 0.0f;
     }
     return v;
+}
+
+// Workgroup ids go to the 8 XCDs round robin; consecutive logical ids in
+// groups of 16 are placed on one XCD, so the workgroups of one (chunk, group)
+// read that chunk's B (and C) through one L2.
+__device__ __forceinline__ int32_t xcd_grouped(int32_t id, int32_t n) {
+    constexpr int32_t kXcd = 8, K = 16, block = kXcd * K;
+    const int32_t m = id / block;
+    if ((m + 1) * block > n)
+        return id;
+    const int32_t r = id % block;
+    return m * block + (r % kXcd) * K + r / kXcd;
 }
 
 // ---- stage 1: dt', the decay cumsum, and the chunk's own state
@@ -126,9 +147,10 @@ __global__ __launch_bounds__(kStateThreads) void ssd_chunk_state_kernel(const Ss
 
     const int ngroups = static_cast<int>(sp.H / sp.hpg);
     const int nhb = (sp.hpg + kStateHeads - 1) / kStateHeads;
-    const int64_t c = blockIdx.x / (ngroups * nhb);
-    const int g = (blockIdx.x / nhb) % ngroups;
-    const int hb = blockIdx.x % nhb;
+    const int32_t wg = xcd_grouped(blockIdx.x, gridDim.x);  // a (chunk, group)'s workgroups share an L2
+    const int64_t c = wg / (ngroups * nhb);
+    const int g = (wg / nhb) % ngroups;
+    const int hb = wg % nhb;
     const int h0 = g * sp.hpg + hb * kStateHeads;
     const int nh = sp.hpg - hb * kStateHeads < kStateHeads ? sp.hpg - hb * kStateHeads : kStateHeads;
     const int t = threadIdx.x;
@@ -146,9 +168,25 @@ __global__ __launch_bounds__(kStateThreads) void ssd_chunk_state_kernel(const Ss
         for (int p0 = 0; p0 < kHalfP / 8; p0++)
             xv[p0] = *reinterpret_cast<const V *>(xrow + 8 * p0);
     };
+    // the heads' A and dt_bias, read once (a per-head load in the loop would
+    // be waited on together with the next head's x rows, requested before it)
+    float Ah[kStateHeads], biash[kStateHeads];
+#pragma unroll
+    for (int hk = 0; hk < kStateHeads; hk++) {
+        const int h = hk < nh ? h0 + hk : h0;
+        Ah[hk] = sp.A[h * sp.A_sh];
+        biash[hk] = sp.dt_bias ? sp.dt_bias[h * sp.bias_sh] : 0.0f;
+    }
+    auto pick = [&](const float (&v)[kStateHeads], int hk) {
+        float r = v[0];
+#pragma unroll
+        for (int k = 1; k < kStateHeads; k++)
+            r = hk == k ? v[k] : r;
+        return r;
+    };
     V xv[kHalfP / 8];
     load_x(h0, xv);
-    float dtp = tk < len ? processed_dt<IT>(sp, t0 + tk, h0) : 0.0f;
+    uint32_t dtr = raw_dt<IT>(sp, tok, h0);
     {
         const IT *brow = static_cast<const IT *>(sp.B) + (tok * sp.B_st + g * sp.B_sg) + half * kHalfN;
 #pragma unroll
@@ -167,10 +205,11 @@ __global__ __launch_bounds__(kStateThreads) void ssd_chunk_state_kernel(const Ss
     const int ptile = wv >> 1, nt0 = (wv & 1) * kNT;
     for (int hk = 0; hk < nh; hk++) {
         const int h = h0 + hk;
+        const float dtp = tk < len ? processed_dt(sp, dt_value<IT>(sp, dtr), pick(biash, hk)) : 0.0f;
         // inclusive prefix sum of dt' A over the chunk: within each wave, then
         // the wave totals through LDS (both halves compute the same sums; the
         // first half publishes them)
-        float acum = wave_inclusive_sum(dtp * sp.A[h * sp.A_sh], lane);
+        float acum = wave_inclusive_sum(dtp * pick(Ah, hk), lane);
         if (lane == 63 && half == 0)
             wave_tot[wq] = acum;
         __syncthreads();
@@ -197,7 +236,7 @@ __global__ __launch_bounds__(kStateThreads) void ssd_chunk_state_kernel(const Ss
         __syncthreads();
         if (hk + 1 < nh) {  // the next head's inputs, in flight during the products
             load_x(h + 1, xv);
-            dtp = tk < len ? processed_dt<IT>(sp, t0 + tk, h + 1) : 0.0f;
+            dtr = raw_dt<IT>(sp, tok, h + 1);
         }
 
         // state[p][n] = sum_t Xs[p][t] Bs[n][t]
@@ -329,17 +368,6 @@ __global__ __launch_bounds__(kPassThreads) void ssd_state_pass_kernel(const SsdP
 
 // ---- stage 3: the chunk scan
 //
-// Workgroup ids go to the 8 XCDs round robin; consecutive logical ids in
-// groups of 16 are placed on one XCD, so the heads of one (chunk, group) read
-// that chunk's B and C through one L2.
-__device__ __forceinline__ int32_t xcd_grouped(int32_t id, int32_t n) {
-    constexpr int32_t kXcd = 8, K = 16, block = kXcd * K;
-    const int32_t m = id / block;
-    if ((m + 1) * block > n)
-        return id;
-    const int32_t r = id % block;
-    return m * block + (r % kXcd) * K + r / kXcd;
-}
 
 // y_t = exp(A_t) C_t . S_in + sum_{s<=t} (C_t . B_s) exp(A_t - A_s) dt'_s x_s
 //       + D x_t, gated by silu(z_t);   A = the decay cumsum of the chunk.
@@ -553,22 +581,26 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(const SsdP
     for (int pt = 0; pt < kP / 16; pt++)
         xrow[pt] = dim_row(pr + 4 * pt);
 
+    // D of the workgroup's heads, read once (a per-head load in the loop would
+    // be waited on together with every load issued before it)
+    float Dh[kScanHeads];
+#pragma unroll
+    for (int hk = 0; hk < kScanHeads; hk++)
+        Dh[hk] = sp.D ? sp.D[(hk < nh ? h0 + hk : h0) * sp.D_sh] : 0.0f;
+
     for (int hk = 0; hk < nh; hk++) {
         const int h = h0 + hk;
-        HeadIn next;
-        if (hk + 1 < nh)
-            load_head(h + 1, next);  // in flight during this head
-        const float dh = sp.D ? sp.D[h * sp.D_sh] : 0.0f;
-        // x and z of the lane's token (16 consecutive p), for the output
-        auto load_xz = [&](int tt, V (&xv2)[2], V (&zv2)[2]) {
+        float dh = Dh[0];
+#pragma unroll
+        for (int k = 1; k < kScanHeads; k++)
+            dh = hk == k ? Dh[k] : dh;
+        // z of the lane's token (16 consecutive p), for the gate
+        auto load_z = [&](int tt, V (&zv2)[2]) {
             const int64_t tok = t0 + (tt < len ? tt : len - 1);
-            const IT *xg = static_cast<const IT *>(sp.x) + tok * sp.x_st + h * sp.x_sh + 16 * gq;
             const IT *zg = zs + tok * sp.z_st + h * sp.z_sh + 16 * gq;
 #pragma unroll
-            for (int k = 0; k < 2; k++) {
-                xv2[k] = *reinterpret_cast<const V *>(xg + 8 * k);
+            for (int k = 0; k < 2; k++)
                 zv2[k] = zs ? *reinterpret_cast<const V *>(zg + 8 * k) : V{};
-            }
         };
         // the entering state's contribution, y^T = S_in C^T, scaled by exp(A_t)
         auto init = [&](int tt, float at, f32x4 (&y)[kP / 16]) {
@@ -636,8 +668,9 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(const SsdP
             for (int pt = 0; pt < kP / 16; pt++)
                 y[pt] = M::run(xop(J, pt), a, y[pt]);
         };
-        // D x, the gate, the store: y[pt][ii] is p = 16 gq + 4 pt + ii of the token
-        auto finish = [&](const f32x4 (&y)[kP / 16], const V (&xv2)[2], const V (&zv2)[2], int tt) {
+        // D x (x from its LDS copy: p = 16 gq + e sits at row 4 e + gq), the
+        // gate, the store: y[pt][ii] is p = 16 gq + 4 pt + ii of the token
+        auto finish = [&](const f32x4 (&y)[kP / 16], const V (&zv2)[2], int tt) {
             if (tt >= len)
                 return;
             const int64_t tok = t0 + tt;
@@ -647,7 +680,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(const SsdP
 #pragma unroll
                 for (int ii = 0; ii < 4; ii++) {
                     const int e = 4 * pt + ii;  // 0..15
-                    float v = y[pt][ii] + dh * to_f(xv2[e / 8][e % 8]);
+                    float v = y[pt][ii] + dh * to_f(Xs[4 * e + gq][tt]);
                     if (zs)
                         v *= silu_f(to_f(zv2[e / 8][e % 8]));
                     o[e / 8][e % 8] = static_cast<IT>(v);
@@ -657,11 +690,13 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(const SsdP
             *reinterpret_cast<V *>(orow + 8) = o[1];
         };
 
-        // the two tiles one after the other: one tile's accumulators and
-        // x, z rows are live at a time
+        // the two tiles one after the other: one tile's accumulators and z
+        // row are live at a time. Loads are issued in the order they are
+        // waited on: tile 0's z, then tile 1's, then the next head's inputs
+        // (in flight during tile 1 and until the head's end)
         if (act0) {  // uniform per wave
-            V xv2[2], zv2[2];
-            load_xz(tt0, xv2, zv2);
+            V zv2[2];
+            load_z(tt0, zv2);
             const float at0 = acum_s[tt0];
             f32x4 y[kP / 16];
             init(tt0, at0, y);
@@ -669,11 +704,16 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(const SsdP
             for (int J = 0; J < 4; J++)
                 if (J <= nj0)  // uniform
                     block(J, J == nj0, tt0, at0, cb[J], y);
-            finish(y, xv2, zv2, tt0);
+            finish(y, zv2, tt0);
         }
+        V zv1[2];
+        if (act1)
+            load_z(tt1, zv1);
+        HeadIn next;
+        if (hk + 1 < nh)
+            load_head(h + 1, next);
         if (act1) {
-            V xv2[2], zv2[2];
-            load_xz(tt1, xv2, zv2);
+            const V (&zv2)[2] = zv1;
             const float at1 = acum_s[tt1];
             f32x4 y[kP / 16];
             init(tt1, at1, y);
@@ -681,7 +721,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(const SsdP
             for (int J = 0; J < 8; J++)
                 if (J <= nj1)  // uniform; nj1 >= 4
                     block(J, J == nj1, tt1, at1, cb[8 - J], y);
-            finish(y, xv2, zv2, tt1);
+            finish(y, zv2, tt1);
         }
         if (hk + 1 < nh) {  // uniform: the next head's inputs replace this one's
             __syncthreads();
