@@ -142,8 +142,9 @@ __global__ __launch_bounds__(kStateThreads) void ssd_chunk_state_kernel(const Ss
     using V = typename M::V;
     constexpr int kHalfP = kP / 2, kHalfN = N / 2;  // each half stages half of a token's x and B rows
     __shared__ float wave_tot[kL / 64];
-    __shared__ __attribute__((aligned(16))) IT Xs[kP][kL + kPad];  // (w x)^T: [p][t]
-    __shared__ __attribute__((aligned(16))) IT Bs[N][kL + kPad];   // B^T: [n][t]
+    __shared__ float head_a[kStateHeads], head_bias[kStateHeads];
+    __shared__ __attribute__((aligned(16))) IT Xs[kP][kL + kPad];   // (w x)^T: [p][t]
+    __shared__ __attribute__((aligned(16))) IT Bs[N][kL + kPad];    // B^T: [n][t]
 
     const int ngroups = static_cast<int>(sp.H / sp.hpg);
     const int nhb = (sp.hpg + kStateHeads - 1) / kStateHeads;
@@ -168,22 +169,14 @@ __global__ __launch_bounds__(kStateThreads) void ssd_chunk_state_kernel(const Ss
         for (int p0 = 0; p0 < kHalfP / 8; p0++)
             xv[p0] = *reinterpret_cast<const V *>(xrow + 8 * p0);
     };
-    // the heads' A and dt_bias, read once (a per-head load in the loop would
-    // be waited on together with the next head's x rows, requested before it)
-    float Ah[kStateHeads], biash[kStateHeads];
-#pragma unroll
-    for (int hk = 0; hk < kStateHeads; hk++) {
-        const int h = hk < nh ? h0 + hk : h0;
-        Ah[hk] = sp.A[h * sp.A_sh];
-        biash[hk] = sp.dt_bias ? sp.dt_bias[h * sp.bias_sh] : 0.0f;
+    // the heads' A and dt_bias, read once into LDS (a per-head load in the
+    // loop would be waited on together with the next head's x rows, requested
+    // before it); the first barrier below publishes them
+    if (t < kStateHeads) {
+        const int h = t < nh ? h0 + t : h0;
+        head_a[t] = sp.A[h * sp.A_sh];
+        head_bias[t] = sp.dt_bias ? sp.dt_bias[h * sp.bias_sh] : 0.0f;
     }
-    auto pick = [&](const float (&v)[kStateHeads], int hk) {
-        float r = v[0];
-#pragma unroll
-        for (int k = 1; k < kStateHeads; k++)
-            r = hk == k ? v[k] : r;
-        return r;
-    };
     V xv[kHalfP / 8];
     load_x(h0, xv);
     uint32_t dtr = raw_dt<IT>(sp, tok, h0);
@@ -205,11 +198,13 @@ __global__ __launch_bounds__(kStateThreads) void ssd_chunk_state_kernel(const Ss
     const int ptile = wv >> 1, nt0 = (wv & 1) * kNT;
     for (int hk = 0; hk < nh; hk++) {
         const int h = h0 + hk;
-        const float dtp = tk < len ? processed_dt(sp, dt_value<IT>(sp, dtr), pick(biash, hk)) : 0.0f;
+        if (hk == 0)
+            __syncthreads();  // head_a, head_bias
+        const float dtp = tk < len ? processed_dt(sp, dt_value<IT>(sp, dtr), head_bias[hk]) : 0.0f;
         // inclusive prefix sum of dt' A over the chunk: within each wave, then
         // the wave totals through LDS (both halves compute the same sums; the
         // first half publishes them)
-        float acum = wave_inclusive_sum(dtp * pick(Ah, hk), lane);
+        float acum = wave_inclusive_sum(dtp * head_a[hk], lane);
         if (lane == 63 && half == 0)
             wave_tot[wq] = acum;
         __syncthreads();
@@ -239,7 +234,8 @@ __global__ __launch_bounds__(kStateThreads) void ssd_chunk_state_kernel(const Ss
             dtr = raw_dt<IT>(sp, tok, h + 1);
         }
 
-        // state[p][n] = sum_t Xs[p][t] Bs[n][t]
+        // state^T[n][p] = sum_t Bs[n][t] Xs[p][t]: formed transposed, a lane
+        // ends with 4 consecutive columns n of one row p (16-byte stores)
         f32x4 acc[kNT];
 #pragma unroll
         for (int nt = 0; nt < kNT; nt++)
@@ -249,15 +245,13 @@ __global__ __launch_bounds__(kStateThreads) void ssd_chunk_state_kernel(const Ss
 #pragma unroll
             for (int nt = 0; nt < kNT; nt++) {
                 const V b = *reinterpret_cast<const V *>(&Bs[16 * (nt0 + nt) + r][32 * k + k8]);
-                acc[nt] = M::run(a, b, acc[nt]);
+                acc[nt] = M::run(b, a, acc[nt]);
             }
         }
-        float *dst = sp.ws_state + (c * sp.H + h) * static_cast<int64_t>(kP * N);
+        float *dst = sp.ws_state + (c * sp.H + h) * static_cast<int64_t>(kP * N) + (16 * ptile + r) * N;
 #pragma unroll
         for (int nt = 0; nt < kNT; nt++)
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                dst[(16 * ptile + 4 * (lane >> 4) + i) * N + 16 * (nt0 + nt) + r] = acc[nt][i];
+            *reinterpret_cast<f32x4 *>(dst + 16 * (nt0 + nt) + 4 * (lane >> 4)) = acc[nt];
         __syncthreads();  // Xs and the wave totals are rewritten for the next head
     }
 }
