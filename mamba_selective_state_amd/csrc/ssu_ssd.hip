@@ -127,11 +127,13 @@ __device__ __forceinline__ int32_t xcd_grouped(int32_t id, int32_t n) {
 // One workgroup per (chunk, group, block of kStateHeads heads of the group),
 // 512 lanes in two halves of 256 (lane t % 256 = token of the chunk; each
 // half stages half of the token's x and B rows): B^T is staged in LDS once
-// for the heads; per head, dt' and the cumsum (a wave scan plus the wave
-// totals through LDS), then (w x)^T with w_t = exp(A_end - A_t) dt'_t and
-// the chunk's own state [64 x N] = sum_t (w_t x_t) B_t^T as MFMA tiles (wave
-// w: p tile w / 2, half of the n tiles). The next head's x rows and dt are
-// requested during the current head's products.
+// for the heads, and the heads' dt' and cumsums (wave scans plus the wave
+// totals through LDS) are formed together behind one barrier; then per head
+// (w x)^T with w_t = exp(A_end - A_t) dt'_t goes to one of two LDS buffers
+// and the chunk's own state [64 x N] = sum_t (w_t x_t) B_t^T is formed as
+// MFMA tiles (wave w: p tile w / 2, half of the n tiles): one barrier per
+// head. The next head's x rows are requested during the current head's
+// products.
 
 constexpr int kStateHeads = 4;
 constexpr int kStateThreads = 512;  // two halves of 256 lanes, lane t % 256 = token
@@ -141,10 +143,9 @@ __global__ __launch_bounds__(kStateThreads) void ssd_chunk_state_kernel(const Ss
     using M = Mfma<IT>;
     using V = typename M::V;
     constexpr int kHalfP = kP / 2, kHalfN = N / 2;  // each half stages half of a token's x and B rows
-    __shared__ float wave_tot[kL / 64];
-    __shared__ float head_a[kStateHeads], head_bias[kStateHeads];
-    __shared__ __attribute__((aligned(16))) IT Xs[kP][kL + kPad];   // (w x)^T: [p][t]
-    __shared__ __attribute__((aligned(16))) IT Bs[N][kL + kPad];    // B^T: [n][t]
+    __shared__ float wave_tot[kStateHeads][kL / 64];
+    __shared__ __attribute__((aligned(16))) IT Xs[2][kP][kL + kPad];  // (w x)^T: [p][t], two heads in turn
+    __shared__ __attribute__((aligned(16))) IT Bs[N][kL + kPad];      // B^T: [n][t]
 
     const int ngroups = static_cast<int>(sp.H / sp.hpg);
     const int nhb = (sp.hpg + kStateHeads - 1) / kStateHeads;
@@ -169,26 +170,62 @@ __global__ __launch_bounds__(kStateThreads) void ssd_chunk_state_kernel(const Ss
         for (int p0 = 0; p0 < kHalfP / 8; p0++)
             xv[p0] = *reinterpret_cast<const V *>(xrow + 8 * p0);
     };
-    // the heads' A and dt_bias, read once into LDS (a per-head load in the
-    // loop would be waited on together with the next head's x rows, requested
-    // before it); the first barrier below publishes them
-    if (t < kStateHeads) {
-        const int h = t < nh ? h0 + t : h0;
-        head_a[t] = sp.A[h * sp.A_sh];
-        head_bias[t] = sp.dt_bias ? sp.dt_bias[h * sp.bias_sh] : 0.0f;
+    // loads in the order they are waited on: the heads' A, dt_bias and dt,
+    // then B, then the first head's x row
+    float Ah[kStateHeads], biash[kStateHeads];
+    uint32_t dtr[kStateHeads];
+#pragma unroll
+    for (int hk = 0; hk < kStateHeads; hk++) {
+        const int h = hk < nh ? h0 + hk : h0;
+        Ah[hk] = sp.A[h * sp.A_sh];
+        biash[hk] = sp.dt_bias ? sp.dt_bias[h * sp.bias_sh] : 0.0f;
+        dtr[hk] = raw_dt<IT>(sp, tok, h);
     }
-    V xv[kHalfP / 8];
-    load_x(h0, xv);
-    uint32_t dtr = raw_dt<IT>(sp, tok, h0);
+    V bv[kHalfN / 8];
     {
         const IT *brow = static_cast<const IT *>(sp.B) + (tok * sp.B_st + g * sp.B_sg) + half * kHalfN;
 #pragma unroll
-        for (int n0 = 0; n0 < kHalfN; n0 += 8) {
-            const V v = *reinterpret_cast<const V *>(brow + n0);
+        for (int n0 = 0; n0 < kHalfN / 8; n0++)
+            bv[n0] = *reinterpret_cast<const V *>(brow + 8 * n0);
+    }
+    V xv[kHalfP / 8];
+    load_x(h0, xv);
 #pragma unroll
-            for (int k = 0; k < 8; k++)
-                Bs[half * kHalfN + n0 + k][tk] = tk < len ? v[k] : static_cast<IT>(0.0f);
+    for (int n0 = 0; n0 < kHalfN / 8; n0++)
+#pragma unroll
+        for (int k = 0; k < 8; k++)
+            Bs[half * kHalfN + 8 * n0 + k][tk] = tk < len ? bv[n0][k] : static_cast<IT>(0.0f);
+
+    // every head's dt' and inclusive prefix sum of dt' A over the chunk:
+    // within each wave, then the wave totals through LDS (both halves compute
+    // the same sums; the first half publishes them), one barrier for all heads
+    float dtp[kStateHeads], acum[kStateHeads];
+#pragma unroll
+    for (int hk = 0; hk < kStateHeads; hk++) {
+        dtp[hk] = tk < len ? processed_dt(sp, dt_value<IT>(sp, dtr[hk]), biash[hk]) : 0.0f;
+        acum[hk] = wave_inclusive_sum(dtp[hk] * Ah[hk], lane);
+        if (lane == 63 && half == 0)
+            wave_tot[hk][wq] = acum[hk];
+    }
+    __syncthreads();  // the wave totals, B^T
+    float w[kStateHeads];
+#pragma unroll
+    for (int hk = 0; hk < kStateHeads; hk++) {
+        // the chunk's total, summed in the order of the last lane's cumsum
+        // (padding adds nothing)
+        float total = wave_tot[hk][kL / 64 - 1];
+#pragma unroll
+        for (int k = 0; k < kL / 64; k++) {
+            const float wt = wave_tot[hk][k];
+            acum[hk] += k < wq ? wt : 0.0f;
+            total += k < kL / 64 - 1 ? wt : 0.0f;
         }
+        if (half == 0 && hk < nh) {
+            const int64_t wrow = (c * sp.H + h0 + hk) * kL;
+            sp.ws_dtp[wrow + tk] = dtp[hk];
+            sp.ws_acum[wrow + tk] = acum[hk];
+        }
+        w[hk] = tk < len ? exp_f(total - acum[hk]) * dtp[hk] : 0.0f;
     }
 
     const int r = lane & 15, k8 = 8 * (lane >> 4);
@@ -196,52 +233,32 @@ __global__ __launch_bounds__(kStateThreads) void ssd_chunk_state_kernel(const Ss
     // products: wave wv takes p tile wv / 2 and half of the n tiles
     constexpr int kNT = N / 32;  // n tiles per wave
     const int ptile = wv >> 1, nt0 = (wv & 1) * kNT;
-    for (int hk = 0; hk < nh; hk++) {
-        const int h = h0 + hk;
-        if (hk == 0)
-            __syncthreads();  // head_a, head_bias
-        const float dtp = tk < len ? processed_dt(sp, dt_value<IT>(sp, dtr), head_bias[hk]) : 0.0f;
-        // inclusive prefix sum of dt' A over the chunk: within each wave, then
-        // the wave totals through LDS (both halves compute the same sums; the
-        // first half publishes them)
-        float acum = wave_inclusive_sum(dtp * head_a[hk], lane);
-        if (lane == 63 && half == 0)
-            wave_tot[wq] = acum;
-        __syncthreads();
-        // the chunk's total, summed in the order of the last lane's cumsum
-        // (padding adds nothing)
-        float total = wave_tot[kL / 64 - 1];
 #pragma unroll
-        for (int k = 0; k < kL / 64; k++) {
-            const float wt = wave_tot[k];
-            acum += k < wq ? wt : 0.0f;
-            total += k < kL / 64 - 1 ? wt : 0.0f;
-        }
-        if (half == 0) {
-            const int64_t wrow = (c * sp.H + h) * kL;
-            sp.ws_dtp[wrow + tk] = dtp;
-            sp.ws_acum[wrow + tk] = acum;
-        }
-        const float w = tk < len ? exp_f(total - acum) * dtp : 0.0f;
+    for (int hk = 0; hk < kStateHeads; hk++) {
+        if (hk >= nh)
+            break;  // uniform
+        const int h = h0 + hk;
+        // (w x)^T into this head's buffer: the other one's products may still
+        // run; the barrier of the head before ended the products that read
+        // this buffer
+        IT(*const X)[kL + kPad] = Xs[hk & 1];
 #pragma unroll
         for (int p0 = 0; p0 < kHalfP / 8; p0++)
 #pragma unroll
             for (int k = 0; k < 8; k++)
-                Xs[half * kHalfP + 8 * p0 + k][tk] = static_cast<IT>(to_f(xv[p0][k]) * w);
+                X[half * kHalfP + 8 * p0 + k][tk] = static_cast<IT>(to_f(xv[p0][k]) * w[hk]);
         __syncthreads();
-        if (hk + 1 < nh) {  // the next head's inputs, in flight during the products
+        if (hk + 1 < nh)  // the next head's x row, in flight during the products
             load_x(h + 1, xv);
-            dtr = raw_dt<IT>(sp, tok, h + 1);
-        }
 
-        // state^T[n][p] = sum_t Bs[n][t] Xs[p][t]: formed transposed, a lane
+        // state^T[n][p] = sum_t Bs[n][t] X[p][t]: formed transposed, a lane
         // ends with 4 consecutive columns n of one row p (16-byte stores)
         f32x4 acc[kNT];
 #pragma unroll
         for (int nt = 0; nt < kNT; nt++)
             acc[nt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         for (int k = 0; k < ksteps; k++) {
-            const V a = *reinterpret_cast<const V *>(&Xs[16 * ptile + r][32 * k + k8]);
+            const V a = *reinterpret_cast<const V *>(&X[16 * ptile + r][32 * k + k8]);
 #pragma unroll
             for (int nt = 0; nt < kNT; nt++) {
                 const V b = *reinterpret_cast<const V *>(&Bs[16 * (nt0 + nt) + r][32 * k + k8]);
@@ -252,7 +269,6 @@ __global__ __launch_bounds__(kStateThreads) void ssd_chunk_state_kernel(const Ss
 #pragma unroll
         for (int nt = 0; nt < kNT; nt++)
             *reinterpret_cast<f32x4 *>(dst + 16 * (nt0 + nt) + 4 * (lane >> 4)) = acc[nt];
-        __syncthreads();  // Xs and the wave totals are rewritten for the next head
     }
 }
 
