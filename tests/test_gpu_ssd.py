@@ -130,3 +130,14 @@ def test_ssd_tiny_chunks():
               io="f16", state_dtype="f32")
     check_ssd(c, "ssd tiny chunks")
     check_ssd(c, "ssd tiny chunks, intermediate", intermediate=True)
+
+
+def test_ssd_many_chunks():
+    """More chunks than the state passing stages at a time (1024): 1252
+    chunks of 16 tokens, the second sequence running across the
+    1024-chunk boundary, final and intermediate states."""
+    c = W.ssd(seed=13, lengths=(16000, 3000, 1000, 7), heads=4, dim=64, dstate=64, groups=1, chunk_size=16,
+              io="bf16", state_dtype="f32")
+    assert len(c["seq_idx"]) > 1024 and c["seq_idx"][1023] == c["seq_idx"][1024] == 1
+    check_ssd(c, "ssd 1252 chunks")
+    check_ssd(c, "ssd 1252 chunks, intermediate", intermediate=True)
