@@ -10,7 +10,8 @@
 // below the source, descending when above): every lane loads its words of
 // the chunk, the workgroup waits for all of its loads and meets at a barrier,
 // and only then stores. A chunk's stores never reach source bytes a later
-// chunk still reads, so the result is that of reading the whole source first.
+// chunk still reads, so the result is that of reading the whole source first
+// (a copy of up to 2 chunks is read whole, then written).
 
 #include <hip/hip_runtime.h>
 
@@ -32,6 +33,18 @@ template <> struct WordOf<16> { using T = cu32x4; };
 
 constexpr int kUnroll = 4;  // words per lane per chunk
 
+// The copies' addresses come from pointer tables: as generic pointers their
+// accesses would be flat ones, which count against the LDS counter too (a
+// barrier's LDS wait would then wait for every load in flight). Every
+// address here is device global memory.
+template <typename T> using Global = __attribute__((address_space(1))) T;
+template <typename T> __device__ __forceinline__ Global<T> *global_ptr(void *p) {
+    return (Global<T> *)p;
+}
+template <typename T> __device__ __forceinline__ const Global<T> *global_ptr(const void *p) {
+    return (const Global<T> *)p;
+}
+
 // Widest word (16, 8, 4, 2 or 1 bytes) that divides both addresses and the size.
 __device__ __forceinline__ int word_bytes(uintptr_t dst, uintptr_t src, int64_t size) {
     const uint64_t m = static_cast<uint64_t>(dst | src | static_cast<uintptr_t>(size));
@@ -43,8 +56,8 @@ __device__ __forceinline__ int word_bytes(uintptr_t dst, uintptr_t src, int64_t 
 template <int WB>
 __device__ void copy_tiles(uint8_t *dst, const uint8_t *src, int64_t nwords, int64_t t0, int64_t tstride) {
     using T = typename WordOf<WB>::T;
-    T *d = reinterpret_cast<T *>(dst);
-    const T *s = reinterpret_cast<const T *>(src);
+    Global<T> *d = global_ptr<T>(dst);
+    const Global<T> *s = global_ptr<T>(src);
     const int64_t tile = static_cast<int64_t>(blockDim.x) * kUnroll;
     for (int64_t t = t0; t * tile < nwords; t += tstride) {
         const int64_t base = t * tile + threadIdx.x;
@@ -64,16 +77,42 @@ __device__ void copy_tiles(uint8_t *dst, const uint8_t *src, int64_t nwords, int
     }
 }
 
-// The whole copy by this workgroup, chunk by chunk away from the overlap;
-// each chunk is loaded by every lane, waited for and fenced by a barrier
-// before any lane stores it.
+constexpr int kWholeChunks = 2;  // copies up to this many chunks are loaded whole before any store
+
+// The whole copy by this workgroup. Up to kWholeChunks chunks: every lane
+// loads all of its words, the workgroup waits for them and meets at a
+// barrier, then stores (one round trip). Longer: chunk by chunk away from the
+// overlap, each chunk loaded by every lane, waited for and fenced by a
+// barrier before any lane stores it.
 template <int WB>
 __device__ void copy_ordered(uint8_t *dst, const uint8_t *src, int64_t nwords, bool descending) {
     using T = typename WordOf<WB>::T;
-    T *d = reinterpret_cast<T *>(dst);
-    const T *s = reinterpret_cast<const T *>(src);
+    Global<T> *d = global_ptr<T>(dst);
+    const Global<T> *s = global_ptr<T>(src);
     const int64_t chunk = static_cast<int64_t>(blockDim.x) * kUnroll;
     const int64_t chunks = (nwords + chunk - 1) / chunk;
+    if (chunks <= kWholeChunks) {  // uniform
+        T v[kWholeChunks][kUnroll];
+#pragma unroll
+        for (int c = 0; c < kWholeChunks; c++)
+#pragma unroll
+            for (int u = 0; u < kUnroll; u++) {
+                const int64_t i = c * chunk + u * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+                if (i < nwords)
+                    v[c][u] = s[i];
+            }
+        __builtin_amdgcn_s_waitcnt(0);  // this lane's loads have returned
+        __syncthreads();                // ... and every other lane's
+#pragma unroll
+        for (int c = 0; c < kWholeChunks; c++)
+#pragma unroll
+            for (int u = 0; u < kUnroll; u++) {
+                const int64_t i = c * chunk + u * static_cast<int64_t>(blockDim.x) + threadIdx.x;
+                if (i < nwords)
+                    d[i] = v[c][u];
+            }
+        return;
+    }
     for (int64_t c = 0; c < chunks; c++) {
         const int64_t base = (descending ? chunks - 1 - c : c) * chunk + threadIdx.x;
         T v[kUnroll];

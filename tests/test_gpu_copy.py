@@ -53,6 +53,15 @@ def test_batch_memcpy_rows(direction, shift):
     run_memcpy(W.memmove_rows(rows=128, row_bytes=32 * 1024, shift=shift, direction=direction))
 
 
+@pytest.mark.parametrize("direction", ["left", "right"])
+def test_batch_memcpy_partial_second_chunk(direction):
+    """Overlapping rows of 24 KiB + 48 bytes in 16-byte words: one full
+    chunk of 256 lanes x 4 words and a partial one, read whole before any
+    store."""
+    G.say("[gpu] batch memcpy partial second chunk %s" % direction)
+    run_memcpy(W.memmove_rows(rows=64, row_bytes=24 * 1024 + 48, shift=32, direction=direction))
+
+
 def test_batch_memcpy_large_and_empty():
     """One 8 MiB copy shifted onto itself (many ordered chunks), large disjoint
     copies beyond the max_size hint (tiles loop), and zero / negative sizes."""
