@@ -1,7 +1,7 @@
 // SSD packed variable-length prefill for gfx950 (MATE docs, "Mamba / SSU",
 // section "SSD packed prefill"): the same recurrence as the decode step over
 // every token of a packed batch, computed chunk by chunk. Three launches:
-//   ssd_chunk_state_kernel   per (chunk, group, 4 heads): dt' (softplus,
+//   ssd_chunk_state_kernel   per (chunk, group, 8 heads): dt' (softplus,
 //                            dt_limit), the decay cumsum, and the chunk's own
 //                            state sum_t exp(A_end - A_t) dt'_t x_t B_t^T (MFMA);
 //   ssd_state_pass_kernel    per (head, state slice): walks the chunks in
@@ -135,7 +135,7 @@ __device__ __forceinline__ int32_t xcd_grouped(int32_t id, int32_t n) {
 // head. The next head's x rows are requested during the current head's
 // products.
 
-constexpr int kStateHeads = 4;
+constexpr int kStateHeads = 8;
 constexpr int kStateThreads = 512;  // two halves of 256 lanes, lane t % 256 = token
 
 template <typename IT, int N>

@@ -112,11 +112,13 @@ def test_ssd_full_workload():
     check_ssd(c, "ssd bench workload", heads=[0, 77, 127])
 
 
-@pytest.mark.parametrize("heads,groups", [(6, 1), (12, 4)], ids=["6-per-group", "3-per-group"])
+@pytest.mark.parametrize("heads,groups", [(6, 1), (12, 4), (20, 2)],
+                         ids=["6-per-group", "3-per-group", "10-per-group"])
 def test_ssd_head_blocks(heads, groups):
-    """Heads per group that the kernels' 4-head blocks do not divide (6:
-    a block of 4 and one of 2; 3: one partial block), with intermediate
-    states so every chunk's state is checked."""
+    """Heads per group that the scan's 4-head and the chunk state's 8-head
+    blocks do not divide (6: blocks of 4 + 2 and one partial 8; 3: partial
+    blocks; 10: 4 + 4 + 2 and 8 + 2), with intermediate states so every
+    chunk's state is checked."""
     c = W.ssd(seed=7 + heads, lengths=(300, 17, 129), heads=heads, dim=64, dstate=128, groups=groups,
               chunk_size=128, io="bf16", state_dtype="f32")
     check_ssd(c, "ssd %d heads / %d groups" % (heads, groups))
