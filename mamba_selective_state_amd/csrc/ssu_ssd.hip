@@ -399,7 +399,9 @@ __global__ __launch_bounds__(kPassThreads) void ssd_state_pass_kernel(const SsdP
 //   the lane ends with the 16 consecutive p = 16g .. 16g + 15 of its token
 //   (two 16-byte stores, loads of x and z alike).
 // Dim p is stored at LDS row 4 (p % 16) + p / 16 of x^T and of the entering
-// state, so the 16 rows an operand read touches start 4 banks apart.
+// state: the 16 rows an operand read touches are then consecutive, and with
+// 142-word x^T rows the 16 lanes of an 8-byte read pass hit distinct banks
+// of the 32.
 // Below the diagonal block the decay factors into a row and a column term,
 // exp(A_t - A_s) dt'_s = exp(A_t - A_J) * exp(A_J - A_s) dt'_s with A_J the
 // cumsum at the block's last token; both are at most 1 there (the cumsum
@@ -409,7 +411,7 @@ constexpr int kScanThreads = 512;
 constexpr int kScanTiles = 2;   // 16-token tiles per wave
 constexpr int kScanHeads = 4;   // heads per workgroup
 constexpr int kScanSlots = 9;   // (block, tile) pairs of a wave: (w / 2 + 1) + ((15 - w) / 2 + 1)
-constexpr int kXsRow = kL + 24; // x^T row stride (elements): 140 words, 12 banks past a multiple of 64
+constexpr int kXsRow = kL + 28; // x^T row stride (elements): 142 words, 14 banks past a multiple of 32
 
 __device__ __forceinline__ int dim_row(int p) { return 4 * (p & 15) + (p >> 4); }
 
