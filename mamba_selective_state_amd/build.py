@@ -2,19 +2,21 @@
 with hipcc."""
 import os
 import subprocess
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssu.so")
-SOURCES = [os.path.join(CSRC, "ssu_kernels.hip"), os.path.join(CSRC, "ssu_copy.hip"),
+SOURCES = [os.path.join(CSRC, "ssu_kernels.hip"), os.path.join(CSRC, "ssu_replay.hip"),
+           os.path.join(CSRC, "ssu_copy.hip"),
            os.path.join(CSRC, "ssu_ssd.hip"),
            os.path.join(CSRC, "ssu_api.cpp")]
-HEADERS = [os.path.join(CSRC, "ssu_internal.h"),
+HEADERS = [os.path.join(CSRC, "ssu_internal.h"), os.path.join(CSRC, "ssu_device.h"),
            os.path.join(os.path.dirname(HERE), "include", "ssu.h")]
 
 # Packed-fp32 instructions are switched off for all device code; hipcc -O3
 # still vectorises loads, stores and conversions.
-HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
+HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
                "-fvisibility=hidden"]
 
@@ -25,11 +27,31 @@ def hipcc():
 
 
 def build(out=LIB, extra=()):
-    """Compile the library into `out` (always recompiles); returns `out`."""
-    tmp = out + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-o", tmp, *SOURCES]
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, out)
+    """Compile the library into `out` (always recompiles); returns `out`.
+
+    Each source is compiled to its own object in parallel (no relocatable
+    device code: every translation unit carries its own kernels), then the
+    objects are linked."""
+    tag = "%s.%d" % (os.path.basename(out), os.getpid())
+    objs = [os.path.join(os.path.dirname(out), "_%s_%s.o" % (os.path.basename(src), tag))
+            for src in SOURCES]
+
+    def compile_one(i):
+        subprocess.run([hipcc(), *HIPCC_FLAGS, *extra, "-c", "-o", objs[i], SOURCES[i]],
+                       check=True)
+
+    try:
+        jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", "4"))))
+        with ThreadPoolExecutor(jobs) as pool:
+            list(pool.map(compile_one, range(len(SOURCES))))
+        tmp = out + ".tmp%d" % os.getpid()
+        subprocess.run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs],
+                       check=True)
+        os.replace(tmp, out)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     return out
 
 
