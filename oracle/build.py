@@ -19,7 +19,7 @@ CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
 def build(src=SRC, out=LIB, extra=()):
     """Compile `src` into the shared library `out`; returns `out`."""
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = ["gcc", *CFLAGS, *extra, "-o", tmp, src, "-lm"]
+    cmd = ["gcc", *CFLAGS, *extra, "-o", tmp, src, "-lm", "-lpthread"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out

@@ -59,10 +59,73 @@
  * convention itself is parity unpinned.
  */
 #include <math.h>
+#include <pthread.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
+
+/* ---- sequences in parallel
+ *
+ * Sequences are independent: every function below that loops over them has
+ * already refused inputs where two sequences share a slot, so each sequence
+ * reads only the input pool and its own inputs and writes only its own
+ * slots, buffer entries and output rows. Running them on several threads
+ * therefore gives the same bytes as one thread (the CPU suite checks it).
+ * The thread count is process-wide, 1 unless set. */
+static int g_threads = 1;
+
+void oracle_set_threads(int n) { g_threads = n < 1 ? 1 : n; }
+int oracle_get_threads(void) { return g_threads; }
+
+typedef void (*oracle_seq_fn)(const void *args, int64_t b, void *scratch);
+typedef struct {
+    const void *args;
+    oracle_seq_fn fn;
+    int64_t nseq, first, step;
+    size_t scratch_bytes;
+} oracle_job;
+
+static void *oracle_worker(void *p)
+{
+    const oracle_job *j = (const oracle_job *)p;
+    void *scratch = malloc(j->scratch_bytes ? j->scratch_bytes : 1);
+    for (int64_t b = j->first; b < j->nseq; b += j->step)
+        j->fn(j->args, b, scratch);
+    free(scratch);
+    return NULL;
+}
+
+/* fn(args, b, scratch) for b = 0..nseq-1, sequence b on thread b mod n */
+static void for_each_sequence(const void *args, oracle_seq_fn fn, int64_t nseq, size_t scratch_bytes)
+{
+    int n = g_threads;
+    if (n > nseq)
+        n = nseq < 1 ? 1 : (int)nseq;
+    oracle_job *jobs = (oracle_job *)malloc((size_t)n * sizeof(oracle_job));
+    pthread_t *tid = (pthread_t *)malloc((size_t)n * sizeof(pthread_t));
+    int started = 0;
+    for (int i = 0; i < n; i++) {
+        jobs[i].args = args;
+        jobs[i].fn = fn;
+        jobs[i].nseq = nseq;
+        jobs[i].first = i;
+        jobs[i].step = n;
+        jobs[i].scratch_bytes = scratch_bytes;
+    }
+    if (n > 1)
+        for (; started < n - 1; started++)
+            if (pthread_create(&tid[started], NULL, oracle_worker, &jobs[started + 1]))
+                break;
+    /* thread 0 is this one; a worker that could not start runs here too */
+    oracle_worker(&jobs[0]);
+    for (int i = started + 1; i < n; i++)
+        oracle_worker(&jobs[i]);
+    for (int i = 0; i < started; i++)
+        pthread_join(tid[i], NULL);
+    free(jobs);
+    free(tid);
+}
 
 enum { OR_F32 = 0, OR_F16 = 1, OR_BF16 = 2 };
 enum { OR_ONE_TOKEN = 0, OR_DENSE = 1, OR_CU = 2 };
@@ -393,23 +456,21 @@ static int check_inputs(const oracle_args *a, char *err, int errlen)
 
 /* ---- the update */
 
-int oracle_ssu(const oracle_args *a, char *err, int errlen)
+/* sequence b of the update; S: scratch of P * N floats */
+static void ssu_sequence(const void *args, int64_t b, void *scratch)
 {
-    if (check_inputs(a, err, errlen))
-        return 1;
+    const oracle_args *a = (const oracle_args *)args;
     const int64_t H = a->H, P = a->P, N = a->N, G = a->G;
     const int64_t heads_per_group = H / G;
     const int64_t tile = P * N;
-    float *S = (float *)malloc((size_t)tile * sizeof(float));
-    const int64_t nseq = num_seqs(a);
-
-    for (int64_t b = 0; b < nseq; b++) {
+    float *S = (float *)scratch;
+    {
         int64_t bos, len;
         seq_span(a, b, &bos, &len);
         if (a->read_slot)
             a->read_slot[b] = INT64_MIN;
         if (len == 0)
-            continue; /* empty sequences are skipped */
+            return; /* empty sequences are skipped */
         int64_t rslot;
         read_slot_of(a, b, bos, &rslot);
         if (a->read_slot)
@@ -468,7 +529,13 @@ int oracle_ssu(const oracle_args *a, char *err, int errlen)
             }
         }
     }
-    free(S);
+}
+
+int oracle_ssu(const oracle_args *a, char *err, int errlen)
+{
+    if (check_inputs(a, err, errlen))
+        return 1;
+    for_each_sequence(a, ssu_sequence, num_seqs(a), (size_t)(a->P * a->N) * sizeof(float));
     return 0;
 }
 
@@ -624,11 +691,14 @@ static void copy_elem(void *dst, const void *src, int32_t dtype, int64_t di, int
         ((uint16_t *)dst)[di] = ((const uint16_t *)src)[si];
 }
 
+static void replay_sequence(const void *args, int64_t b, void *scratch);
+static void replay_spec_sequence(const void *args, int64_t b, void *scratch);
+
 int oracle_replay(const oracle_replay_args *ra, char *err, int errlen)
 {
     const oracle_args *a = &ra->base;
     const int64_t H = a->H, P = a->P, N = a->N, G = a->G, L = ra->L;
-    const int64_t per_group = H / G, tile = P * N;
+    const int64_t tile = P * N;
     if (a->layout != OR_ONE_TOKEN || a->wtab.data || a->acc || L < 1 || H % G) {
         set_err(err, errlen, "replay takes one token per sequence, no destination table, L >= 1%lld%lld", 0, 0);
         return 1;
@@ -642,7 +712,6 @@ int oracle_replay(const oracle_replay_args *ra, char *err, int errlen)
         return 1;
     }
     const int64_t nseq = a->R;
-    const int64_t dtw = a->dt_per_head ? 1 : P; /* dt values per (step, head) */
     /* slots in range, at most one sequence per slot, 0 <= h < L */
     for (int64_t b = 0; b < nseq; b++) {
         const int64_t s = a->rtab.data ? a->rtab.data[b] : b;
@@ -663,11 +732,24 @@ int oracle_replay(const oracle_replay_args *ra, char *err, int errlen)
                 return 1;
             }
     }
-    float *S = (float *)malloc((size_t)tile * sizeof(float));
-    float *alpha = (float *)malloc((size_t)L * sizeof(float));
-    float *dtp = (float *)malloc((size_t)L * sizeof(float));
-    float *xs = (float *)malloc((size_t)L * sizeof(float));
-    for (int64_t b = 0; b < nseq; b++) {
+    for_each_sequence(ra, replay_sequence, nseq, (size_t)(tile + 3 * L) * sizeof(float));
+    return 0;
+}
+
+/* sequence b of the replay step; scratch: the tile, then alpha, dt' and x
+ * of up to L steps */
+static void replay_sequence(const void *args, int64_t b, void *scratch)
+{
+    const oracle_replay_args *ra = (const oracle_replay_args *)args;
+    const oracle_args *a = &ra->base;
+    const int64_t H = a->H, P = a->P, N = a->N, G = a->G, L = ra->L;
+    const int64_t per_group = H / G, tile = P * N;
+    const int64_t dtw = a->dt_per_head ? 1 : P; /* dt values per (step, head) */
+    float *S = (float *)scratch;
+    float *alpha = S + tile;
+    float *dtp = alpha + L;
+    float *xs = dtp + L;
+    {
         const int64_t s = a->rtab.data ? a->rtab.data[b] : b;
         const int pad = s == a->pad;
         const int64_t h = pad ? 0 : ra->buf_len[b]; /* R19 */
@@ -773,11 +855,6 @@ int oracle_replay(const oracle_replay_args *ra, char *err, int errlen)
 #undef RB
         }
     }
-    free(S);
-    free(alpha);
-    free(dtp);
-    free(xs);
-    return 0;
 }
 
 /* ---- ReplaySSM speculative step: T draft tokens per sequence
@@ -813,7 +890,7 @@ int oracle_replay_spec(const oracle_replay_args *ra, char *err, int errlen)
 {
     const oracle_args *a = &ra->base;
     const int64_t H = a->H, P = a->P, N = a->N, G = a->G, L = ra->L, T = a->steps;
-    const int64_t per_group = H / G, tile = P * N;
+    const int64_t tile = P * N;
     if (a->layout != OR_DENSE || T < 1 || T > L || a->R % T || a->wtab.data || a->acc || H % G) {
         set_err(err, errlen, "speculative replay takes [batch, T, ...] inputs with 1 <= T <= L%lld%lld", 0, 0);
         return 1;
@@ -827,7 +904,6 @@ int oracle_replay_spec(const oracle_replay_args *ra, char *err, int errlen)
         return 1;
     }
     const int64_t nseq = a->R / T;
-    const int64_t dtw = a->dt_per_head ? 1 : P;
     for (int64_t b = 0; b < nseq; b++) {
         const int64_t s = a->rtab.data ? a->rtab.data[b] : b;
         const int64_t h = ra->buf_len[b];
@@ -847,11 +923,24 @@ int oracle_replay_spec(const oracle_replay_args *ra, char *err, int errlen)
                 return 1;
             }
     }
-    float *S = (float *)malloc((size_t)tile * sizeof(float));
-    float *alpha = (float *)malloc((size_t)(L + T) * sizeof(float));
-    float *dtp = (float *)malloc((size_t)(L + T) * sizeof(float));
-    float *xs = (float *)malloc((size_t)(L + T) * sizeof(float));
-    for (int64_t b = 0; b < nseq; b++) {
+    for_each_sequence(ra, replay_spec_sequence, nseq, (size_t)(tile + 3 * (L + T)) * sizeof(float));
+    return 0;
+}
+
+/* sequence b of the speculative step; scratch: the tile, then alpha, dt'
+ * and x of up to L + T steps */
+static void replay_spec_sequence(const void *args, int64_t b, void *scratch)
+{
+    const oracle_replay_args *ra = (const oracle_replay_args *)args;
+    const oracle_args *a = &ra->base;
+    const int64_t H = a->H, P = a->P, N = a->N, G = a->G, L = ra->L, T = a->steps;
+    const int64_t per_group = H / G, tile = P * N;
+    const int64_t dtw = a->dt_per_head ? 1 : P;
+    float *S = (float *)scratch;
+    float *alpha = S + tile;
+    float *dtp = alpha + (L + T);
+    float *xs = dtp + (L + T);
+    {
         const int64_t s = a->rtab.data ? a->rtab.data[b] : b;
         const int pad = s == a->pad;
         const int64_t h = pad ? 0 : ra->buf_len[b]; /* R23 */
@@ -948,11 +1037,6 @@ int oracle_replay_spec(const oracle_replay_args *ra, char *err, int errlen)
 #undef DC
         }
     }
-    free(S);
-    free(alpha);
-    free(dtp);
-    free(xs);
-    return 0;
 }
 
 /* ---- memmove-safe Mamba state copies

@@ -83,6 +83,18 @@ class Oracle:
         self.lib.oracle_bf16_to_f32.restype = ctypes.c_float
         self.lib.oracle_softplus.argtypes = [ctypes.c_float]
         self.lib.oracle_softplus.restype = ctypes.c_float
+        self.lib.oracle_set_threads.argtypes = [ctypes.c_int]
+        self.lib.oracle_set_threads.restype = None
+        self.lib.oracle_get_threads.argtypes = []
+        self.lib.oracle_get_threads.restype = ctypes.c_int
+
+    def set_threads(self, n):
+        """Threads over sequences for every later call (1: serial); the
+        result is byte-identical for any count."""
+        self.lib.oracle_set_threads(int(n))
+
+    def threads(self):
+        return self.lib.oracle_get_threads()
 
     # scalar helpers, exported for the pins
     def f32_to_f16(self, v):

@@ -1064,29 +1064,72 @@ def pin_e4m3_codec(orc):
 
 
 def pin_mx8_blocks(orc):
-    """MXFP8 blocks (R30): the scale exponent is floor(log2 max|x|) - 8, a
-    block of zeros gets byte 1 and zero codes, the decoded block errs by at
-    most half an E4M3 step (1/16 relative, 2^-10 of the scale in the
-    subnormal range) except clipped maxima, which decode to +-448 x scale,
-    and an already decoded block is a fixed point."""
+    """MXFP8 blocks (R30) against the OCP MX definition, with the formats
+    decoded by a library (PyTorch's float8_e8m0fnu and float8_e4m3fn): the
+    scale byte decodes to X = 2^k with the block's largest magnitude in
+    [2^emax, 2^(emax+1)) X, emax being the exponent of E4M3's largest finite
+    value (8); so the largest code of every block sits in E4M3's top binade
+    (clipped to its largest value above it). Away from the exponent clamp,
+    every unclipped element decodes within half an E4M3 step (1/16 relative,
+    2^-10 X below the normal range), and an already decoded block is a fixed
+    point. A block of zeros has zero codes (and byte 1, k = -126)."""
+    import torch
     from oracle import ssu_oracle
     rng = np.random.default_rng(4)
     x = (rng.standard_normal((64, 32)) * np.exp(rng.uniform(-12, 12, (64, 1)))).astype(np.float32)
     x[3] = 0.0
+    x[5] *= np.float32(1e-38)                      # scale exponent clamped at -126
     codes, scales = ssu_oracle.mx8_quantize(x, orc)
-    amax = np.abs(x).max(axis=1)
-    k = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1))) - 8, -126)
-    assert np.array_equal(scales[:, 0].astype(int) - 127, k.astype(int))
+    X = torch.from_numpy(scales[:, 0].copy()).view(torch.float8_e8m0fnu).double().numpy()
+    e4 = torch.from_numpy(codes.reshape(-1).copy()).view(torch.float8_e4m3fn).double().numpy()
+    e4 = e4.reshape(codes.shape)
+    fmax = float(torch.finfo(torch.float8_e4m3fn).max)
+    emax = math.floor(math.log2(fmax))
+    amax = np.abs(x).max(axis=1).astype(np.float64)
+    live = (amax > 0) & (np.arange(64) != 5)
+    ratio = amax[live] / X[live]
+    assert np.all(ratio >= 2.0 ** emax) and np.all(ratio < 2.0 ** (emax + 1)), ratio
+    top = np.abs(e4[live]).max(axis=1)
+    assert np.all((top >= 2.0 ** emax) & (top <= fmax)), top
     assert scales[3, 0] == 1 and not codes[3].any()
-    deq = ssu_oracle.mx8_dequantize(codes, scales, orc)
-    sc = np.exp2(k)[:, None]
-    clipped = np.abs(x) / sc >= 464
-    assert np.all(np.abs(deq[clipped]) == (448 * np.broadcast_to(sc, x.shape))[clipped])
+    assert scales[5, 0] == 1                     # 2^-126, the smallest scale R30 allows
+    deq = ssu_oracle.mx8_dequantize(codes, scales, orc).astype(np.float64)
+    assert np.array_equal(deq, e4 * X[:, None])  # decode = E4M3 value x E8M0 scale
+    sc = np.broadcast_to(X[:, None], x.shape)
+    clipped = np.abs(x) / sc >= fmax + 16        # beyond the rounding edge (464)
+    assert np.all(np.abs(deq[clipped]) == (fmax * sc)[clipped])
     err = np.abs(deq - x)
-    bound = np.maximum(np.abs(x) / 16, np.broadcast_to(sc, x.shape) * 2.0 ** -10)
+    bound = np.maximum(np.abs(x) / 16, sc * 2.0 ** -10)
     assert np.all(err[~clipped] <= bound[~clipped])
-    c2, s2 = ssu_oracle.mx8_quantize(deq, orc)
-    assert np.array_equal(ssu_oracle.mx8_dequantize(c2, s2, orc), deq)
+    c2, s2 = ssu_oracle.mx8_quantize(deq.astype(np.float32), orc)
+    assert np.array_equal(ssu_oracle.mx8_dequantize(c2, s2, orc), deq.astype(np.float32))
+
+
+def pin_threads_byte_identical(orc):
+    """Sequences are independent (the oracle refuses shared slots), so the
+    oracle threaded over sequences gives the serial result byte for byte:
+    the update on every sequence layout, the replay step and the speculative
+    step."""
+    from oracle import ssu_oracle
+    cases = [("ssu", small("varlen", nseq=13, heads=4, dim=8, dstate=16)),
+             ("ssu", small("mtp", nseq=7, steps=3, heads=4, dim=8, dstate=16, groups=2)),
+             ("ssu", small("decode", batch=9, heads=4, dim=8, dstate=16, groups=2, slots=12)),
+             ("replay", _replay_case(4, [0, 3, 1, 2, 3, 0, 2], batch=7, slots=9)),
+             ("spec", _spec_case(8, 2, [0, 5, 7, 8, 2, 6], batch=6, slots=8))]
+    before = orc.threads()
+    try:
+        for kind, c in cases:
+            fn = {"ssu": ssu_oracle.run, "replay": ssu_oracle.run_replay,
+                  "spec": ssu_oracle.run_replay_spec}[kind]
+            orc.set_threads(1)
+            one = fn(c, orc)
+            for n in (3, 8):
+                orc.set_threads(n)
+                many = fn(c, orc)
+                for k in one:
+                    assert np.array_equal(np.asarray(one[k]), np.asarray(many[k])), (kind, n, k)
+    finally:
+        orc.set_threads(before)
 
 
 def _lp_case(L, buf_len, **kw):
@@ -1145,4 +1188,4 @@ ALL = [pin_golden_mate_examples, pin_f16_decode_exhaustive, pin_f16_encode, pin_
        pin_memmove_matches_snapshot, pin_conv_shift_matches_snapshot,
        pin_ssd_matches_chunked_float64, pin_ssd_equals_decode_chain, pin_ssd_chunking_invariance,
        pin_ssd_seq_idx_authority, pin_ssd_dt_limit_zero, pin_e4m3_codec, pin_mx8_blocks,
-       pin_replay_read_copy]
+       pin_replay_read_copy, pin_threads_byte_identical]

@@ -96,6 +96,7 @@ MUTANTS = [
      "const float q = floorf(ldexpf(a, 9));"),
     ("e4m3_decode_bias", "ldexpf(1.0f + (float)m / 8.0f, e - 7)", "ldexpf(1.0f + (float)m / 8.0f, e - 8)"),
     ("mx8_scale_off_by_one", "k = (ex - 1) - 8; /* R30 */", "k = (ex - 1) - 7;"),
+    ("mx8_scale_off_by_one_up", "k = (ex - 1) - 8; /* R30 */", "k = (ex - 1) - 9;"),
     ("lp_read_at_fold", "const int from_copy = ra->lp_in && h + 1 != L && !pad;",
      "const int from_copy = ra->lp_in && !pad;"),
     ("lp_not_rewritten", "if (ra->lp_out) /* R32: the fold rewrites the read copy */", "if (0)"),
