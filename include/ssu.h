@@ -228,7 +228,10 @@ SSU_API ssu_status_t ssu_replay_update(const ssu_replay_args_t *args, void *stre
  * outside for a slot other than the pad id makes that sequence's y NaN and
  * writes nothing). The pad id reads a zero checkpoint, has no buffer and
  * writes nothing; disable_state_update writes neither checkpoint nor buffer.
- * Same error, stream and allocation conventions as ssu_update. */
+ * Enqueues two kernels on `stream`: the step, then the append of the drafts'
+ * B rows and per-head dt, which a folding sequence's group-mates still read
+ * while the step runs. Otherwise the same error, stream and allocation
+ * conventions as ssu_update. */
 SSU_API ssu_status_t ssu_replay_spec_update(const ssu_replay_args_t *args, void *stream);
 
 /* ---- ReplaySSM with a low-precision read copy (ReplaySSM article, lpnh.cn,

@@ -1022,8 +1022,15 @@ static ssu_status_t replay_common(const ssu_replay_args_t *ra, bool spec, void *
     const int64_t grid = pr.nseq * pr.H * geo.dim_tiles;
     if (grid > INT32_MAX)
         return fail(SSU_ERR_NOT_IMPLEMENTED, "grid too large");
-    const int e = ssu::launch_replay(k, p, rp, static_cast<unsigned>(grid),
-                                     static_cast<unsigned>(geo.block), stream);
+    if (spec && pr.nseq * T > INT32_MAX)
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "batch * T too large");
+    int e = ssu::launch_replay(k, p, rp, static_cast<unsigned>(grid),
+                               static_cast<unsigned>(geo.block), stream);
+    // the speculative step's shared appends run after the step (same stream)
+    if (e == 0 && spec)
+        e = ssu::launch_replay_spec_append(p, rp, static_cast<int>(elem_bytes(pr.io)),
+                                           static_cast<int>(elem_bytes(pr.dt_dtype)),
+                                           static_cast<unsigned>(pr.nseq * T), stream);
     if (e != 0)
         return fail(SSU_ERR_HIP, "kernel launch failed: %s", ssu::hip_error_string(e));
     g_error.clear();

@@ -211,6 +211,12 @@ bool find_replay_lp_kernel(int io_dtype, int dstate, KernelRef *out);
 int launch_mx8_quantize(const float *src, uint8_t *codes, uint8_t *scales, int64_t nblocks, void *stream);
 int launch_replay(const KernelRef &k, const Params &p, const ReplayParams &rp, unsigned grid,
                   unsigned block, void *stream);
+// The speculative step's second launch: the drafts' B rows and per-head dt
+// appended once the step's kernel has ended. One workgroup per (sequence,
+// draft): grid = batch * T.
+constexpr int kSpecAppendThreads = 256;
+int launch_replay_spec_append(const Params &p, const ReplayParams &rp, int io_bytes, int dt_bytes,
+                              unsigned grid, void *stream);
 
 // Loads the kernel's code object on the current device and reports its
 // registers; returns the hipError_t value as int.

@@ -491,8 +491,20 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes, replay_waves_per_eu(sizeof(S
 // ssu_replay_kernel, every run keeps one (R, G) pair per draft of the group,
 // updated only at steps that draft can see (the causal mask), and each
 // B_j . C_t is formed once per DPP row and draft. The drafts' raw inputs go
-// to entries w .. w+T-1. An entry count outside [0, L] (not for the pad id)
-// makes the sequence's y NaN and writes nothing.
+// to entries w .. w+T-1: x and a per-dim dt here, by the lane that owns the
+// dim row; B and a per-head dt by ssu_replay_spec_append_kernel, launched
+// after this kernel on the same stream. An entry count outside [0, L] (not
+// for the pad id) makes the sequence's y NaN and writes nothing.
+//
+// Ordering: a fold reads committed entries 0..h-1 and its drafts go to
+// entries 0..T-1, so a folding sequence's appends overwrite entries its fold
+// reads. An entry's B row is read by every dim tile of every head of the
+// group and a per-head dt by every dim tile of the head, across workgroups
+// that run in no fixed order, so those two are written only once this
+// launch has ended. x and a per-dim dt of row d are read (fold) and written
+// (append) by the one lane that owns row d, in that order; other lanes read
+// no buffer row they do not own. A sequence that does not fold reads entries
+// below w and writes entries w and above.
 constexpr int kSpecGroup = 4;
 
 template <typename ST, typename IT, int N>
@@ -623,8 +635,11 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes, replay_spec_waves_per_eu(siz
 #pragma unroll
             for (int c = 0; c < NCH; c++)
                 in.b[c] = load_words<IT, IVEC>(entry_B(j) + c * kLanesPerRow * IVEC);
-            in.x = *reinterpret_cast<const Bits *>(entry_x(j, d_fetch));
-            const unsigned char *dp = entry_dt_p(j, d_fetch);
+            // a lane that owns no row reads the first draft's x and dt (read
+            // only, unused) rather than a buffer row another lane appends to
+            in.x = *reinterpret_cast<const Bits *>(owner ? entry_x(j, d_own) : draft_x(0, 0));
+            const unsigned char *dp =
+                owner || rp.dt_per_head ? entry_dt_p(j, owner ? d_own : 0) : draft_dt_p(0, 0);
             in.dt_lo = *reinterpret_cast<const uint16_t *>(dp);
             in.dt_hi = *reinterpret_cast<const uint16_t *>(dp + (dt_f32 ? 2 : 0));
         };
@@ -883,35 +898,64 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes, replay_spec_waves_per_eu(siz
                 ys[row(t0 + i) * p.out_sr + h * p.out_sh + d_own] = narrow<IT>(bad ? __builtin_nanf("") : y);
             }
         }
-        // append the group's drafts at entries w + t
-        if (write) {
+        // append the group's drafts at entries w + t: the owner rows' x and
+        // per-dim dt (B and a per-head dt: ssu_replay_spec_append_kernel)
+        if (write && owner) {
 #pragma unroll
             for (int i = 0; i < TG; i++) {
                 if (t0 + i >= T)
                     break;
                 const int64_t e = sl + w + t0 + i;
-                auto put_dt = [&](unsigned char *dst) {
+                *reinterpret_cast<Bits *>(bxs + (e * H + h) * P + d_own) = xo[i];
+                if (!rp.dt_per_head) {
+                    unsigned char *dst = bdts + ((e * H + h) * P + d_own) * dt_bytes;
                     if (dt_f32)
                         *reinterpret_cast<uint32_t *>(dst) = uint32_t(dlo[i]) | (uint32_t(dhi[i]) << 16);
                     else
                         *reinterpret_cast<uint16_t *>(dst) = dlo[i];
-                };
-                if (owner) {
-                    *reinterpret_cast<Bits *>(bxs + (e * H + h) * P + d_own) = xo[i];
-                    if (!rp.dt_per_head)
-                        put_dt(bdts + ((e * H + h) * P + d_own) * dt_bytes);
-                }
-                if (rp.dt_per_head && tile == 0 && threadIdx.x == 0)
-                    put_dt(bdts + (e * H + h) * dt_bytes);  // lane 0 owns a row; dt is the head's
-                if (h % p.heads_per_group == 0 && tile == 0 && wave == 0 && rsub == 0) {
-                    IT *dst = bBs + (e * rp.G + g) * N + col * IVEC;
-#pragma unroll
-                    for (int c = 0; c < NCH; c++)
-                        store_words<IT, IVEC>(dst + c * kLanesPerRow * IVEC,
-                                              load_words<IT, IVEC>(draft_B(t0 + i) + c * kLanesPerRow * IVEC));
                 }
             }
         }
+    }
+}
+
+// The speculative step's appends that other workgroups of the step read:
+// the drafts' B rows (every head of a group) and a per-head dt (every dim
+// tile of a head), written to entries w .. w+T-1 after the step's kernel has
+// ended (same stream). One workgroup per (sequence, draft); the sequence's
+// slot, pointer, fold decision and write rule are those of the step.
+// IO_BYTES / DT_BYTES: element sizes of the x dtype and the dt dtype.
+template <int IO_BYTES, int DT_BYTES>
+__global__ __launch_bounds__(kSpecAppendThreads) void ssu_replay_spec_append_kernel(const Params p,
+                                                                                   const ReplayParams rp) {
+    using IOW = std::conditional_t<IO_BYTES == 2, uint16_t, uint32_t>;
+    using DTW = std::conditional_t<DT_BYTES == 2, uint16_t, uint32_t>;
+    const int32_t T = p.steps;
+    const int32_t b = blockIdx.x / T;
+    const int32_t t = blockIdx.x % T;
+    const int flags = p.flags;
+    const int64_t s = p.rtab ? load_index(p.rtab, flags & kReadI64, b * p.r_s0) : b;
+    if (s == p.pad || (flags & kDisable))
+        return;
+    const int64_t h_in = load_index(rp.buf_len, rp.len_i64, b * rp.len_s);
+    if (h_in < 0 || h_in > rp.L)
+        return;
+    const int32_t hc = static_cast<int32_t>(h_in);
+    const int32_t w = hc + 2 * T > rp.L ? 0 : hc;
+    const int64_t e = s * rp.L + w + t;  // the buffer entry
+    const int32_t r = b * T + t;         // the draft's row
+    const int32_t N = p.P == 0 ? 0 : static_cast<int32_t>(p.slot_stride / (static_cast<int64_t>(p.H) * p.P));
+    const IOW *const Bs = static_cast<const IOW *>(p.B);
+    IOW *const bB = static_cast<IOW *>(rp.buf_B) + e * rp.G * N;
+    for (int32_t i = threadIdx.x; i < rp.G * N; i += blockDim.x) {
+        const int32_t g = i / N, n = i - g * N;
+        bB[i] = Bs[r * p.B_sr + g * p.B_sg + n];
+    }
+    if (rp.dt_per_head) {
+        const DTW *const dts = static_cast<const DTW *>(p.dt);
+        DTW *const bdt = static_cast<DTW *>(rp.buf_dt) + e * p.H;
+        for (int32_t h = threadIdx.x; h < p.H; h += blockDim.x)
+            bdt[h] = dts[r * p.dt_sr + h * p.dt_sh];
     }
 }
 
@@ -1026,6 +1070,19 @@ int launch_replay(const KernelRef &k, const Params &p, const ReplayParams &rp, u
     ReplayParams rc = rp;
     void *args[] = {&pc, &rc};
     return static_cast<int>(hipLaunchKernel(k.fn, dim3(grid), dim3(block), args, 0,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int launch_replay_spec_append(const Params &p, const ReplayParams &rp, int io_bytes, int dt_bytes,
+                              unsigned grid, void *stream) {
+    const void *fn = io_bytes == 2 ? (dt_bytes == 2 ? reinterpret_cast<const void *>(&ssu_replay_spec_append_kernel<2, 2>)
+                                                    : reinterpret_cast<const void *>(&ssu_replay_spec_append_kernel<2, 4>))
+                                   : (dt_bytes == 2 ? reinterpret_cast<const void *>(&ssu_replay_spec_append_kernel<4, 2>)
+                                                    : reinterpret_cast<const void *>(&ssu_replay_spec_append_kernel<4, 4>));
+    Params pc = p;
+    ReplayParams rc = rp;
+    void *args[] = {&pc, &rc};
+    return static_cast<int>(hipLaunchKernel(fn, dim3(grid), dim3(kSpecAppendThreads), args, 0,
                                             static_cast<hipStream_t>(stream)));
 }
 

@@ -106,34 +106,33 @@ def test_replay_spec_out_of_range_counts():
 
 
 def test_replay_spec_full_workload():
-    """The speculative benchmark workload (batch 512, T = 4, L = 16):
-    untouched pool slots and buffer entries byte-identical, sampled
-    sequences against the oracle."""
+    """The speculative benchmark workload (batch 512, T = 4, L = 16): every
+    sequence, folding or not, against the oracle's whole step (pool, y and
+    the three buffers bit for bit)."""
     c = W.replay_spec()
-    T, L = np.shape(c["x"])[1], c["L"]
+    G.say("[gpu] replay spec full: oracle")
+    ref = G.oracle_replay(c)
     G.say("[gpu] replay spec full: launching")
-    d = G.device_replay(c)
-    snap = d["state"].clone()
-    bsnap = {k: d[k].clone() for k in ("buf_x", "buf_dt", "buf_B")}
-    got = G.run_gpu_replay(c, d=d)
-    tab = np.asarray(c["state_batch_indices"])
-    blen = np.asarray(c["buf_len"])
-    fold = blen + 2 * T > L
-    written = np.zeros(c["state"].shape[0], bool)
-    written[tab[fold]] = True
-    idx_u = torch.from_numpy(np.flatnonzero(~written)).to("cuda:0")
-    assert torch.equal(d["state"][idx_u], snap[idx_u])
-    for k in ("buf_x", "buf_dt", "buf_B"):
-        mask = torch.ones(d[k].shape[:2], dtype=torch.bool, device="cuda:0")
-        for b in range(len(tab)):
-            w = 0 if fold[b] else int(blen[b])
-            mask[int(tab[b]), w:w + T] = False
-        assert torch.equal(d[k][mask], bsnap[k][mask]), k
-    seqs = sorted(set([0, 511] + list(np.flatnonzero(fold)[:3]) + list(np.flatnonzero(~fold)[:3])))
-    sub, used = G.replay_subcase(c, seqs)
-    ref = G.oracle_replay(sub)
-    sub_got = {"y": got["y"][seqs], "state": got["state"][used]}
-    for k in ("buf_x", "buf_dt", "buf_B"):
-        sub_got[k] = got[k][used]
-    stats = G.compare_replay(sub, sub_got, ref, "replay spec full")
+    got = G.run_gpu_replay(c)
+    stats = G.compare_replay(c, got, ref, "replay spec full")
     G.say("[gpu] replay spec full: ok %s" % {k: "%.3g" % v for k, v in stats.items()})
+
+
+@pytest.mark.parametrize("dt_per_head", [False, True])
+def test_replay_spec_fold_across_workgroups(dt_per_head):
+    """Every sequence folds while its drafts go to the entries the folds read
+    (h = 6, T = 4, L = 8: entries 0..5 read, 0..3 written), 64 heads share
+    one group's B rows and a per-head dt is shared by a head's dim tiles, on
+    a grid far larger than what can be resident at once (512 x 64 x dim
+    tiles). Every folded checkpoint, y and buffer entry against the oracle:
+    a fold that saw a draft's B or dt would differ."""
+    c = W.replay_spec(seed=61, batch=512, T=4, heads=64, dim=64, dstate=128, groups=1,
+                      slots=520, L=8, buf_len=6, dt_per_head=dt_per_head)
+    G.say("[gpu] replay spec fold across workgroups (per-head dt %s): oracle" % dt_per_head)
+    ref = G.oracle_replay(c)
+    assert ref["written"].sum() == 512
+    G.say("[gpu] replay spec fold across workgroups: launching")
+    got = G.run_gpu_replay(c)
+    stats = G.compare_replay(c, got, ref, "replay spec fold across workgroups")
+    G.say("[gpu] replay spec fold across workgroups: ok %s"
+          % {k: "%.3g" % v for k, v in stats.items()})
