@@ -373,6 +373,21 @@ SSU_API int64_t ssu_ssd_workspace_bytes(int64_t heads, int64_t dim, int64_t dsta
 SSU_API ssu_status_t ssu_ssd_prefill(const ssu_ssd_args_t *args, void *workspace, int64_t workspace_bytes,
                                      void *stream);
 
+/* ---- SSD prefill that allocates nothing and takes no workspace argument.
+ * For callers that cannot allocate device memory or pass one: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * arguments, kernels and results as ssu_ssd_prefill; its workspace is a
+ * device array of SSU_SSD_SCRATCH_BYTES inside the library, one per GPU,
+ * held from the library's load until the process ends (its address on a
+ * GPU is looked up on the first call made with that GPU current). A call
+ * whose workspace (ssu_ssd_workspace_bytes) exceeds that size fails with
+ * SSU_ERR_VALUE before anything is enqueued. `stream` must belong to the
+ * current device. Every call on one GPU uses the same array: calls that
+ * overlap on one GPU (other streams, other threads) race on it; calls on one
+ * stream are ordered. Nothing in the array needs clearing between calls. */
+#define SSU_SSD_SCRATCH_BYTES (64ll << 20)
+SSU_API ssu_status_t ssu_ssd_prefill_noalloc(const ssu_ssd_args_t *args, void *stream);
+
 /* Message of the last failing call on this thread ("" if none). The pointer
  * stays valid until the next call on the same thread. */
 SSU_API const char *ssu_last_error(void);

@@ -9,7 +9,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libssu.so")
 SOURCES = [os.path.join(CSRC, "ssu_kernels.hip"), os.path.join(CSRC, "ssu_replay.hip"),
            os.path.join(CSRC, "ssu_copy.hip"),
-           os.path.join(CSRC, "ssu_ssd.hip"),
+           os.path.join(CSRC, "ssu_ssd.hip"), os.path.join(CSRC, "ssu_noalloc.hip"),
            os.path.join(CSRC, "ssu_api.cpp")]
 HEADERS = [os.path.join(CSRC, "ssu_internal.h"), os.path.join(CSRC, "ssu_device.h"),
            os.path.join(os.path.dirname(HERE), "include", "ssu.h")]

@@ -32,6 +32,15 @@ ssu_status_t fail(ssu_status_t st, const char *fmt, ...) {
     return st;
 }
 
+}  // namespace
+
+ssu_status_t ssu::report_error(ssu_status_t st, const char *msg) {
+    g_error = msg;
+    return st;
+}
+
+namespace {
+
 bool is_float(int d) { return d == SSU_F32 || d == SSU_F16 || d == SSU_BF16; }
 bool is_index(int d) { return d == SSU_I32 || d == SSU_I64; }
 int64_t elem_bytes(int d) {

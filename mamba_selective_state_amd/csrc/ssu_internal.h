@@ -4,7 +4,12 @@
 
 #include <stdint.h>
 
+#include "../../include/ssu.h"
+
 namespace ssu {
+
+// Sets the thread's last-error message (ssu_last_error) and returns `st`.
+ssu_status_t report_error(ssu_status_t st, const char *msg);
 
 // How rows are grouped into sequences.
 enum Layout : int32_t {

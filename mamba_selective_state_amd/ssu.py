@@ -81,7 +81,8 @@ class SsuPlanInfo(ctypes.Structure):
 
 EXPORTS = ("ssu_plan", "ssu_update", "ssu_replay_update", "ssu_replay_spec_update",
            "ssu_replay_lp_update", "ssu_mx8_quantize", "ssu_batch_memcpy", "ssu_conv_state_shift", "ssu_ssd_workspace_bytes", "ssu_ssd_prefill",
-           "ssu_last_error", "ssu_abi_version")
+           "ssu_ssd_prefill_noalloc", "ssu_last_error", "ssu_abi_version")
+SSD_SCRATCH_BYTES = 64 << 20  # SSU_SSD_SCRATCH_BYTES
 
 
 def load_library(path=None):
@@ -113,6 +114,8 @@ def load_library(path=None):
     lib.ssu_ssd_prefill.argtypes = [ctypes.POINTER(SsuSsdArgs), ctypes.c_void_p, ctypes.c_int64,
                                     ctypes.c_void_p]
     lib.ssu_ssd_prefill.restype = ctypes.c_int
+    lib.ssu_ssd_prefill_noalloc.argtypes = [ctypes.POINTER(SsuSsdArgs), ctypes.c_void_p]
+    lib.ssu_ssd_prefill_noalloc.restype = ctypes.c_int
     lib.ssu_last_error.argtypes = []
     lib.ssu_last_error.restype = ctypes.c_char_p
     lib.ssu_abi_version.argtypes = []
@@ -479,6 +482,17 @@ def ssu_ssd_prefill(args, workspace, workspace_bytes, stream=None):
         _raise(st, "ssu_ssd_prefill")
 
 
+def ssu_ssd_prefill_noalloc(args, stream=None):
+    """Enqueue an SSD prefill whose workspace is the library's own device
+    array (include/ssu.h ssu_ssd_prefill_noalloc): nothing is allocated;
+    calls whose workspace exceeds SSD_SCRATCH_BYTES raise ValueError."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    st = _lib.ssu_ssd_prefill_noalloc(ctypes.byref(args), ctypes.c_void_p(stream))
+    if st != OK:
+        _raise(st, "ssu_ssd_prefill_noalloc")
+
+
 def ssd_workspace(device, nbytes):
     """The cached workspace of `device`, grown to at least `nbytes` (a call
     of an already seen size allocates nothing)."""
@@ -487,6 +501,29 @@ def ssd_workspace(device, nbytes):
         ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _ssd_workspaces[device] = ws
     return ws
+
+
+def make_ssd_args(x, dt, A, B, C, chunk_size, cu_seqlens, cu_chunk_seqlens, last_chunk_indices,
+                  seq_idx, out, states, D=None, z=None, dt_bias=None, dt_softplus=False,
+                  dt_limit=(0.0, float("inf")), initial_states=None,
+                  return_intermediate_states=False, checkpoint=False):
+    """An SsuSsdArgs for ssu_ssd_prefill / ssu_ssd_prefill_noalloc (out and
+    states given)."""
+    dev = x.device
+    a = SsuSsdArgs()
+    for k, v in (("x", x), ("dt", dt), ("A", A), ("B", B), ("C", C), ("D", D), ("z", z),
+                 ("dt_bias", dt_bias), ("cu_seqlens", cu_seqlens),
+                 ("cu_chunk_seqlens", cu_chunk_seqlens), ("last_chunk_indices", last_chunk_indices),
+                 ("seq_idx", seq_idx), ("initial_states", initial_states), ("out", out),
+                 ("states", states)):
+        setattr(a, k, tensor_desc(v, dev))
+    a.chunk_size = int(chunk_size)
+    a.dt_softplus = int(bool(dt_softplus))
+    a.return_intermediate_states = int(bool(return_intermediate_states))
+    a.dt_limit_lo, a.dt_limit_hi = float(dt_limit[0]), float(dt_limit[1])
+    if checkpoint:
+        a.unsupported |= OPT_SSD_CHECKPOINT
+    return a
 
 
 def ssd_combined_fwd_varlen(x, dt, A, B, C, chunk_size, cu_seqlens, cu_chunk_seqlens,
@@ -509,20 +546,15 @@ def ssd_combined_fwd_varlen(x, dt, A, B, C, chunk_size, cu_seqlens, cu_chunk_seq
     states = torch.empty((rows, x.shape[1], x.shape[2], B.shape[2]), dtype=state_dtype, device=dev)
     if out is None:
         out = torch.empty_like(x)
-    a = SsuSsdArgs()
-    for k, v in (("x", x), ("dt", dt), ("A", A), ("B", B), ("C", C), ("D", D), ("z", z),
-                 ("dt_bias", dt_bias), ("cu_seqlens", cu_seqlens),
-                 ("cu_chunk_seqlens", cu_chunk_seqlens), ("last_chunk_indices", last_chunk_indices),
-                 ("seq_idx", seq_idx), ("initial_states", initial_states), ("out", out),
-                 ("states", states)):
-        setattr(a, k, tensor_desc(v, dev))
-    a.chunk_size = int(chunk_size)
-    a.dt_softplus = int(bool(dt_softplus))
-    a.return_intermediate_states = int(bool(return_intermediate_states))
-    a.dt_limit_lo, a.dt_limit_hi = float(dt_limit[0]), float(dt_limit[1])
-    if any(v is not None for v in (checkpoint_token_indices, checkpoint_state_slots, checkpoint_states)):
-        a.unsupported |= OPT_SSD_CHECKPOINT
+    a = make_ssd_args(x, dt, A, B, C, chunk_size, cu_seqlens, cu_chunk_seqlens, last_chunk_indices,
+                      seq_idx, out, states, D=D, z=z, dt_bias=dt_bias, dt_softplus=dt_softplus,
+                      dt_limit=dt_limit, initial_states=initial_states,
+                      return_intermediate_states=return_intermediate_states,
+                      checkpoint=any(v is not None for v in (checkpoint_token_indices,
+                                                             checkpoint_state_slots,
+                                                             checkpoint_states)))
+    stream = torch.cuda.current_stream(dev).cuda_stream
     nbytes = ssu_ssd_workspace_bytes(x.shape[1], x.shape[2], B.shape[2], max(nchunks, 0))
     ws = ssd_workspace(dev, nbytes)
-    ssu_ssd_prefill(a, ws.data_ptr(), ws.numel(), torch.cuda.current_stream(dev).cuda_stream)
+    ssu_ssd_prefill(a, ws.data_ptr(), ws.numel(), stream)
     return states

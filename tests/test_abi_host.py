@@ -630,3 +630,16 @@ def test_ssd_errors():
     a.cu_chunk_seqlens = S.SsuTensor()
     st, msg = ssd(a)
     assert st == S.ERR_VALUE and "cu_chunk_seqlens" in msg
+
+
+def test_ssd_noalloc_rejects_oversized_and_null():
+    """The allocation-free prefill refuses, before any device call, a call
+    whose workspace exceeds the library's array, naming both sizes."""
+    assert S._lib.ssu_ssd_prefill_noalloc(None, None) == S.ERR_VALUE
+    assert "NULL" in S.ssu_last_error()
+    a = ssd_args(T=16, H=128, nchunks=200, batch=1)
+    need = S.ssu_ssd_workspace_bytes(128, 64, 128, 200)
+    assert need > S.SSD_SCRATCH_BYTES
+    st = S._lib.ssu_ssd_prefill_noalloc(ctypes.byref(a), None)
+    msg = S.ssu_last_error()
+    assert st == S.ERR_VALUE and str(need) in msg and str(S.SSD_SCRATCH_BYTES) in msg, msg
