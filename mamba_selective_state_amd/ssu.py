@@ -493,13 +493,17 @@ def ssu_ssd_prefill_noalloc(args, stream=None):
         _raise(st, "ssu_ssd_prefill_noalloc")
 
 
-def ssd_workspace(device, nbytes):
-    """The cached workspace of `device`, grown to at least `nbytes` (a call
-    of an already seen size allocates nothing)."""
-    ws = _ssd_workspaces.get(device)
+def ssd_workspace(device, stream, nbytes):
+    """The cached workspace of (`device`, `stream`), grown to at least
+    `nbytes` (a call of an already seen size allocates nothing). One per
+    stream: calls on one stream are ordered, so they can share it; a grown
+    workspace is allocated on that stream, so the caching allocator hands
+    the old one's memory out again only behind the kernels that used it."""
+    key = (device, stream)
+    ws = _ssd_workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
-        _ssd_workspaces[device] = ws
+        _ssd_workspaces[key] = ws
     return ws
 
 
@@ -555,6 +559,6 @@ def ssd_combined_fwd_varlen(x, dt, A, B, C, chunk_size, cu_seqlens, cu_chunk_seq
                                                              checkpoint_states)))
     stream = torch.cuda.current_stream(dev).cuda_stream
     nbytes = ssu_ssd_workspace_bytes(x.shape[1], x.shape[2], B.shape[2], max(nchunks, 0))
-    ws = ssd_workspace(dev, nbytes)
+    ws = ssd_workspace(dev, stream, nbytes)
     ssu_ssd_prefill(a, ws.data_ptr(), ws.numel(), stream)
     return states
