@@ -16,10 +16,17 @@ Prints ONE JSON line:
              by a plain copy of known size) when they were taken on the
              current kernel source, else null
   cpu_baseline  the CPU oracle timed on this host on the same workload
+Timing: every timed call is bracketed by its own pair of HIP events on the
+launch stream; kernel_us is their median (kernel_us_mean their mean), and
+roofline.achieved uses the median.
+  ceiling    the same bytes moved by the runtime's device-to-device copy and
+             by an in-place read-modify-write stream (libssu_ceiling.so):
+             what this part sustains for a plain stream of that size
 Options: --config {decode, decode_pad, mtp, varlen, varlen_disable, varlen_nodst, replay,
-replay_spec, replay_lp, spec_snapshots, tiny, conv_shift_sd, conv_shift_ds, memcpy_left, ssd},
---no-cpu-baseline, --calib-copy (also runs a plain device copy of the state's
-size, the calibration kernel for the counters).
+replay_spec, replay_lp, spec_snapshots, tiny, conv_shift_sd, conv_shift_ds, memcpy_left, ssd,
+ceiling}, --no-cpu-baseline, --calib-copy (also runs a plain device copy of the
+state's size, the calibration kernel for the counters). --config ceiling
+measures the streaming ceilings alone (1 GiB buffers, every pattern).
 """
 import argparse
 import hashlib
@@ -37,8 +44,26 @@ sys.path.insert(0, ROOT)
 METRIC = "SSU decode achieved HBM GB/s (% of peak) and token-head updates/s"
 HBM_PEAK_GBS = 8000.0
 COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "mamba_selective_state_amd", "csrc", f)
-                  for f in ("ssu_kernels.hip", "ssu_copy.hip", "ssu_ssd.hip", "ssu_internal.h")]
+CSRC = os.path.join(ROOT, "mamba_selective_state_amd", "csrc")
+# The sources each workload's kernels are built from: a counter reading is
+# used only while these are unchanged.
+_COMMON = ("ssu_internal.h",)
+KERNEL_SOURCES = {
+    "decode": ("ssu_kernels.hip", "ssu_device.h") + _COMMON,
+    "replay": ("ssu_replay.hip", "ssu_device.h") + _COMMON,
+    "copy": ("ssu_copy.hip",) + _COMMON,
+    "ssd": ("ssu_ssd.hip",) + _COMMON,
+}
+
+
+def source_family(config):
+    if config in ("replay", "replay_spec", "replay_lp"):
+        return "replay"
+    if config in ("conv_shift_sd", "conv_shift_ds", "memcpy_left"):
+        return "copy"
+    if config == "ssd":
+        return "ssd"
+    return "decode"
 
 DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 / f16 matrix peak of MI355X
@@ -209,15 +234,179 @@ def replay_algorithmic_bytes(case, lp=False):
     return int(total + R * row + vec + idx), int(R * H)
 
 
+# ---------------------------------------------------------------- timing
+
+def time_calls(launch, stream, steps, warmup):
+    """Warm up, then `steps` calls, each between its own pair of HIP events
+    on `stream` (the stream the library launches on), the whole bracketed by
+    device synchronisation. Returns (per-call ms list, wall s)."""
+    import torch
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize(stream.device)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        launch()
+        b.record(stream)
+    torch.cuda.synchronize(stream.device)
+    wall = time.perf_counter() - t0
+    return [a.elapsed_time(b) for a, b in ev], wall
+
+
+def kernel_times(ms):
+    """(median, mean) of per-call durations, in ms."""
+    return statistics.median(ms), statistics.fmean(ms)
+
+
+_ceiling_lib = None
+
+
+def ceiling_lib():
+    global _ceiling_lib
+    if _ceiling_lib is None:
+        import ctypes
+        from mamba_selective_state_amd import build as B
+        if not os.path.exists(B.CEILING_LIB):
+            raise SystemExit("libssu_ceiling.so is not built (run mamba_selective_state_amd/build.py)")
+        lib = ctypes.CDLL(B.CEILING_LIB)
+        lib.ssu_ceiling_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, ctypes.c_void_p]
+        lib.ssu_ceiling_run.restype = ctypes.c_int
+        _ceiling_lib = lib
+    return _ceiling_lib
+
+
+CEILING_KINDS = {"rmw": 0, "copy": 1, "write": 2, "read": 3}
+# launch shapes tried for each pattern: (lanes per workgroup, 16-byte words
+# per lane per pass, grid: "pass" = one workgroup per pass-sized piece, or a
+# fixed count walking the buffer grid-stride)
+CEILING_SHAPES = ((64, 8, "pass"), (64, 4, "pass"), (256, 4, "pass"), (256, 8, "pass"),
+                  (256, 4, 2048), (256, 8, 4096))
+
+
+def stream_ceiling(dev, kind, nbytes, nt=True, reps=10, shapes=CEILING_SHAPES):
+    """Best GB/s of one ceiling pattern over a buffer of `nbytes` (bytes
+    moved per call: read + written) among the launch shapes, median of `reps`
+    calls each; returns (GB/s, shape)."""
+    import torch
+    lib = ceiling_lib()
+    nbytes = nbytes // 16 * 16
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    b = a if kind in ("rmw", "read") else torch.empty_like(a)
+    stream = torch.cuda.current_stream(dev)
+    moved = nbytes * (2 if kind in ("rmw", "copy") else 1)
+    best = (0.0, None)
+    for threads, words, grid in shapes:
+        if grid == "pass":
+            grid = (nbytes // 16 + threads * words - 1) // (threads * words)
+        sink = torch.empty(grid, dtype=torch.float32, device=dev)
+
+        def launch():
+            e = lib.ssu_ceiling_run(CEILING_KINDS[kind], int(nt), a.data_ptr(), b.data_ptr(), nbytes,
+                                    sink.data_ptr(), grid, threads, words, stream.cuda_stream)
+            if e:
+                raise RuntimeError("ceiling kernel launch failed: %d" % e)
+
+        ms, _ = time_calls(launch, stream, reps, 3)
+        gbs = moved / (statistics.median(ms) * 1e-3) / 1e9
+        if gbs > best[0]:
+            best = (gbs, "%d lanes x %d words, grid %d" % (threads, words, grid))
+    return best
+
+
+def copy_ceiling(dev, nbytes, reps=10):
+    """GB/s of the runtime's device-to-device copy (hipMemcpyAsync) moving
+    `nbytes` (half read, half written), median of `reps` calls."""
+    import torch
+    half = nbytes // 2 // 16 * 16
+    src = torch.empty(half // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream(dev)
+    ms, _ = time_calls(lambda: dst.copy_(src), stream, reps, 3)
+    return 2 * half / (statistics.median(ms) * 1e-3) / 1e9
+
+
+def ceiling_fields(dev, nbytes):
+    """The streaming ceilings for `nbytes` moved (reported beside a result)."""
+    return {"bytes": int(nbytes),
+            "d2d_copy_gbs": round(copy_ceiling(dev, nbytes), 1),
+            "rmw_nt_gbs": round(stream_ceiling(dev, "rmw", nbytes // 2)[0], 1),
+            "note": "the same bytes through hipMemcpyAsync device-to-device and through an "
+                    "in-place 16-byte non-temporal read-modify-write stream (libssu_ceiling.so)"}
+
+
+def ceiling_bench(args):
+    """--config ceiling: every streaming pattern over 1 GiB buffers."""
+    import torch
+    dev = torch.device("cuda", 0)
+    size = 1 << 30
+    res, shapes = {}, {}
+    for kind in ("rmw", "copy", "write", "read"):
+        for nt in (True, False):
+            key = "%s_%s" % (kind, "nt" if nt else "plain")
+            gbs, shape = stream_ceiling(dev, kind, size, nt)
+            res[key], shapes[key] = round(gbs, 1), shape
+    res["d2d_copy_runtime"] = round(copy_ceiling(dev, 2 * size), 1)
+    best = max(res.values())
+    result = {"metric": "HBM streaming ceilings (GB/s moved, read + written)", "value": best,
+              "unit": "GB/s", "n_gpus": 1, "steps": 10, "warmup": 3, "ms_per_step": None,
+              "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8",
+              "data": "synthetic",
+              "config": {"workload": "ceiling: 1 GiB buffers, 16-byte accesses, the best of %d "
+                                     "launch shapes per pattern; rmw = in place p = 0.5 p + 1, "
+                                     "copy, write-only, read-only; nt = non-temporal hint"
+                                     % len(CEILING_SHAPES)},
+              "patterns_gbs": res, "best_shapes": shapes,
+              "pct_of_hbm_peak": {k: round(100 * v / HBM_PEAK_GBS, 1) for k, v in res.items()}}
+    print(json.dumps(result), flush=True)
+
+
+def oracle_threads():
+    """Threads for the threaded oracle leg: the cores this process may run
+    on, at most the 16 host cores of a one-GPU share."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def timed_oracle(run, case, reps, threads):
+    """Median wall time of `reps` oracle calls on `threads` threads, and the
+    last result."""
+    from oracle import ssu_oracle
+    orc = ssu_oracle.default()
+    before = orc.threads()
+    orc.set_threads(threads)
+    try:
+        times, res = [], None
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            res = run(case)
+            times.append(time.perf_counter() - t0)
+    finally:
+        orc.set_threads(before)
+    return statistics.median(times), res
+
+
+def same_result(a, b):
+    return all(np.array_equal(np.asarray(a[k]), np.asarray(b[k])) for k in a)
+
+
 COPY_CONFIGS = ("conv_shift_sd", "conv_shift_ds", "memcpy_left")
 
 
 def ssd_algorithmic(case):
     """Bytes the prefill must move (inputs read once, y and the returned
     states written once) and the chunked algorithm's matrix flops: per chunk
-    of L tokens and head, the chunk state 2 L P N, C.B^T over the causal half
-    L (L + 1) N, its product with x L (L + 1) P, and the entering state read
-    out 2 L N P. Returns (bytes, flops)."""
+    of L tokens and head, the chunk state 2 L P N, the masked C.B^T's product
+    with x L (L + 1) P and the entering state read out 2 L N P; per chunk and
+    group (C.B^T does not depend on the head) C.B^T over the causal half
+    L (L + 1) N. Returns (bytes, flops)."""
     T, H, P = np.shape(case["x"])
     G, N = np.shape(case["B"])[1:]
     io = DTYPE_BYTES[case["io_dtype"]]
@@ -230,7 +419,7 @@ def ssd_algorithmic(case):
     flops = 0
     for L in np.diff(cu):
         L = int(L)
-        flops += H * (2 * L * P * N + L * (L + 1) * N + L * (L + 1) * P + 2 * L * N * P)
+        flops += H * (2 * L * P * N + L * (L + 1) * P + 2 * L * N * P) + G * L * (L + 1) * N
     return int(nbytes), int(flops)
 
 
@@ -254,18 +443,8 @@ def ssd_bench_run(args, case, desc):
             dt_softplus=case["dt_softplus"], dt_limit=case["dt_limit"], initial_states=init,
             state_dtype=TORCH[sd])
     stream = torch.cuda.current_stream(d)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize(d)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize(d)
-    wall = time.perf_counter() - t0
-    event_ms = start.elapsed_time(end) / args.steps
+    per_call, wall = time_calls(step, stream, args.steps, args.warmup)
+    event_ms, mean_ms = kernel_times(per_call)
     if args.calib_copy:
         src_c = torch.empty((1 << 30) // 4, dtype=torch.float32, device=d).fill_(1.0)
         dst_c = torch.empty_like(src_c)
@@ -294,25 +473,56 @@ def ssd_bench_run(args, case, desc):
                      "frac": round(gbs / HBM_PEAK_GBS if hbm_bound else tflops / MFMA_BF16_PEAK_TFLOPS, 5),
                      "traffic": traffic_from_counters("ssd"),
                      "kernel_us": round(event_ms * 1e3, 2),
+                     "kernel_us_mean": round(mean_ms * 1e3, 2),
                      "intensity_flop_per_byte": round(flops / nbytes, 1),
                      "ridge_flop_per_byte": round(MFMA_BF16_PEAK_TFLOPS * 1e3 / HBM_PEAK_GBS, 1),
                      "mfma_tflops": round(tflops, 3), "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 5),
-                     "note": "the three launches of one call timed together"},
+                     "note": "the launches of one call timed together"},
+        "ceiling": ceiling_fields(d, nbytes),
     }
     if not args.no_cpu_baseline:
-        from oracle import ssu_oracle
-        import workloads as W
-        heads = [0, 64]
-        sub = W.ssd_heads(case, heads)
-        t1 = time.perf_counter()
-        ssu_oracle.run_ssd(sub)
-        tm = (time.perf_counter() - t1) * np.shape(case["x"])[1] / len(heads)
-        result["cpu_baseline"] = {"value": round(flops / tm / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
-                                  "kind": "oracle",
-                                  "sample": "2 of the 128 heads (heads are independent), scaled to all "
-                                            "heads: %.1f s per call; single-threaded token-by-token C oracle"
-                                            % tm}
+        result["cpu_baseline"] = ssd_cpu_baseline(case, flops)
     print(json.dumps(result), flush=True)
+
+
+def ssd_cpu_baseline(case, flops):
+    """The SSD oracle on sampled heads (heads are independent): one head pair
+    on one thread, then one head pair per thread on `threads` threads at once
+    (the oracle's C call runs without the interpreter lock), each scaled to
+    all heads; the threads' first pair must equal the serial run byte for
+    byte."""
+    import threading
+    from oracle import ssu_oracle
+    import workloads as W
+    H = np.shape(case["x"])[1]
+    threads = oracle_threads()
+    pairs = [[(2 * i) % H, (2 * i + 64) % H] for i in range(threads)]
+    subs = [W.ssd_heads(case, hp) for hp in pairs]
+    t1 = time.perf_counter()
+    serial = ssu_oracle.run_ssd(subs[0])
+    t_serial = (time.perf_counter() - t1) * H / 2
+    results = [None] * threads
+
+    def work(i):
+        results[i] = ssu_oracle.run_ssd(subs[i])
+
+    workers = [threading.Thread(target=work, args=(i,)) for i in range(threads)]
+    t1 = time.perf_counter()
+    for w in workers:
+        w.start()
+    for w in workers:
+        w.join()
+    t_threads = (time.perf_counter() - t1) * H / (2 * threads)
+    identical = same_result(serial, results[0])
+    assert identical, "the threaded SSD oracle differs from the serial one"
+    return {"value": round(flops / t_threads / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "nproc": os.cpu_count(),
+            "serial_value": round(flops / t_serial / 1e12, 6),
+            "identical_to_serial": bool(identical),
+            "sample": "head pairs (heads are independent): one pair on one thread (%.1f s per call "
+                      "scaled to all %d heads), then %d pairs on %d threads at once (%.1f s per "
+                      "call scaled); token-by-token C oracle" % (t_serial, H, threads, threads,
+                                                                 t_threads)}
 
 
 def copy_algorithmic_bytes(case):
@@ -354,18 +564,8 @@ def copy_bench(args, name, case, desc):
         kernel = "batch_memcpy_kernel"
     stream = torch.cuda.current_stream(dev)
     handle = stream.cuda_stream
-    for _ in range(args.warmup):
-        launch(handle)
-    torch.cuda.synchronize(dev)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        launch(handle)
-    end.record(stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
-    event_ms = start.elapsed_time(end) / args.steps
+    per_call, wall = time_calls(lambda: launch(handle), stream, args.steps, args.warmup)
+    event_ms, mean_ms = kernel_times(per_call)
     if args.calib_copy:
         nbytes = 1 << 30
         src_c = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -386,7 +586,8 @@ def copy_bench(args, name, case, desc):
         "pct_of_hbm_peak": round(100.0 * achieved / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_counters(name),
-                     "kernel_us": round(event_ms * 1e3, 2)},
+                     "kernel_us": round(event_ms * 1e3, 2), "kernel_us_mean": round(mean_ms * 1e3, 2)},
+        "ceiling": ceiling_fields(dev, alg_bytes),
     }
     if not args.no_cpu_baseline:
         from oracle import ssu_oracle
@@ -503,26 +704,30 @@ def tiny_bench(args):
     print(json.dumps(result), flush=True)
 
 
-def kernel_source_hash():
+def kernel_source_hash(config):
+    """sha256 over the sources the workload's kernels are built from."""
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        h.update(open(p, "rb").read())
+    for f in KERNEL_SOURCES[source_family(config)]:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()
 
 
 def traffic_from_counters(config):
     """HBM bytes per launch from the committed counter summary, or None when
-    it is missing, for another workload, or taken on another kernel source."""
+    it is missing, for another workload, or taken on other kernel sources."""
     if not os.path.exists(COUNTERS):
         return None
     c = json.load(open(COUNTERS))
     entry = c.get("workloads", {}).get(config)
-    if not entry or c.get("kernel_source_sha256") != kernel_source_hash():
+    if not entry or entry.get("kernel_source_sha256") != kernel_source_hash(config):
         return None
     return entry.get("hbm_bytes_per_dispatch")
 
 
 def cpu_baseline(case, alg_bytes, updates, reps, lp=False):
+    """The oracle on the whole workload: median of `reps` calls on one
+    thread, then on oracle_threads() threads over sequences; the two results
+    must be byte-identical."""
     from oracle import ssu_oracle
     ssu_oracle.default()
     if "buf_len" in case:
@@ -533,16 +738,19 @@ def cpu_baseline(case, alg_bytes, updates, reps, lp=False):
                 np.asarray(case["state"], np.float32))
     else:
         run = ssu_oracle.run
-    times = []
-    for _ in range(reps):
-        t0 = time.perf_counter()
-        run(case)
-        times.append(time.perf_counter() - t0)
-    t = statistics.median(times)
-    return {"value": round(alg_bytes / t / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "updates_per_s": round(updates / t, 1),
-            "sample": "the whole workload, one call per repetition, median of %d (%.2f s each); "
-                      "single-threaded plain-C fp32 oracle incl. its NumPy wrapper" % (reps, t)}
+    threads = oracle_threads()
+    t1, r1 = timed_oracle(run, case, reps, 1)
+    tn, rn = timed_oracle(run, case, reps, threads)
+    identical = same_result(r1, rn)
+    assert identical, "the threaded oracle differs from the serial one"
+    return {"value": round(alg_bytes / tn / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "updates_per_s": round(updates / tn, 1), "nproc": os.cpu_count(),
+            "serial_value": round(alg_bytes / t1 / 1e9, 4),
+            "serial_updates_per_s": round(updates / t1, 1),
+            "identical_to_serial": bool(identical),
+            "sample": "the whole workload, one call per repetition, median of %d: %.2f s on %d "
+                      "threads over sequences, %.2f s on one thread; plain-C fp32 oracle incl. "
+                      "its NumPy wrapper" % (reps, tn, threads, t1)}
 
 
 def main():
@@ -552,7 +760,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=4)
+    ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--calib-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -561,6 +769,12 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.config == "ceiling":
+        import torch
+        if not torch.cuda.is_available():
+            raise SystemExit("bench.py needs a GPU")
+        ceiling_bench(args)
+        return
     if args.config == "ssd":
         import torch
         if not torch.cuda.is_available():
@@ -638,20 +852,11 @@ def main():
     stream = torch.cuda.current_stream(dev)
     handle = stream.cuda_stream
 
-    for _ in range(args.warmup):
-        launch(args_c, handle)
-    torch.cuda.synchronize(dev)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        launch(args_c, handle)
-    end.record(stream)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
-    event_ms = start.elapsed_time(end) / args.steps
-    print("[bench] %d steps: %.1f us per launch (events), %.1f us per step (wall)"
-          % (args.steps, event_ms * 1e3, wall / args.steps * 1e6), file=sys.stderr, flush=True)
+    per_call, wall = time_calls(lambda: launch(args_c, handle), stream, args.steps, args.warmup)
+    event_ms, mean_ms = kernel_times(per_call)
+    print("[bench] %d steps: %.1f us per call (median of events; mean %.1f), %.1f us per step "
+          "(wall)" % (args.steps, event_ms * 1e3, mean_ms * 1e3, wall / args.steps * 1e6),
+          file=sys.stderr, flush=True)
 
     if args.calib_copy:
         nbytes = int(np.prod(np.shape(case["state"]))) * DTYPE_BYTES[case["state_dtype"]] // 2
@@ -684,8 +889,13 @@ def main():
         "token_head_updates_per_s": round(updates * args.steps / wall, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel_us": round(event_ms * 1e3, 2)},
+                     "traffic": traffic, "kernel_us": round(event_ms * 1e3, 2),
+                     "kernel_us_mean": round(mean_ms * 1e3, 2)},
+        "ceiling": ceiling_fields(dev, alg_bytes),
     }
+    if args.config == "replay_spec":
+        result["roofline"]["note"] = ("each call is the step and the append of the drafts' B "
+                                      "rows and per-head dt, timed together")
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(case, alg_bytes, updates, args.cpu_reps, lp)
