@@ -878,7 +878,11 @@ ssu_status_t ssu_update(const ssu_args_t *a, void *stream) {
     if (pr.empty)
         return g_error.clear(), SSU_OK;
     ssu::KernelRef k;
-    if (!ssu::find_kernel(pr.state_dtype, pr.io, static_cast<int>(pr.N), pr.multi, &k))
+    // with disable_state_update nothing is stored: the multi-token path's
+    // output-only variant where it applies
+    const bool yonly = pr.multi && (pr.p.flags & ssu::kDisable) &&
+                       ssu::find_yonly_kernel(pr.state_dtype, pr.io, static_cast<int>(pr.N), &k);
+    if (!yonly && !ssu::find_kernel(pr.state_dtype, pr.io, static_cast<int>(pr.N), pr.multi, &k))
         return fail(SSU_ERR_NOT_IMPLEMENTED, "no kernel for state %s / io %s / dstate %lld",
                     dtype_str(pr.state_dtype), dtype_str(pr.io), (long long)pr.N);
     const int e = ssu::launch(k, pr.p, static_cast<unsigned>(pr.grid),

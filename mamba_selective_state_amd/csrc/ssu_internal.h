@@ -156,6 +156,9 @@ struct KernelRef {
 
 // Returns false if no variant exists for the combination.
 bool find_kernel(int state_dtype, int io_dtype, int dstate, bool multi, KernelRef *out);
+// The multi-token kernel's output-only variant for disable_state_update;
+// false where it does not apply (16-bit state with fp32 outputs).
+bool find_yonly_kernel(int state_dtype, int io_dtype, int dstate, KernelRef *out);
 
 // "ssu_onetoken_<state>_<io>_n<dstate>" or "ssu_packed_...".
 void kernel_name(int state_dtype, int io_dtype, int dstate, bool multi, char *buf, int len);

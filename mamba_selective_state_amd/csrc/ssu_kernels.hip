@@ -32,9 +32,26 @@
 namespace ssu {
 namespace {
 
-template <typename ST, typename IT, int N, bool MULTI>
+// Output-only variant of the multi-token kernel (YONLY), for
+// disable_state_update: nothing is stored, so a sequence of at most kYMax
+// tokens gets each y_t from the read tile and the unrolled window (ReplaySSM
+// article, section "核心做法"):
+//   y_t = (prod_{i<=t} a_i)(S_0 . C_t) + sum_{j<=t} (prod_{j<i<=t} a_i) dt'_j x_j (B_j . C_t) + D x_t,
+// gated: one multiply-add per state element and token in place of the
+// update, the readout and the rounding of the carried state. The carry is
+// therefore not rounded to the state dtype between tokens, which moves y by
+// far less than the tolerance of 16-bit outputs; the variant is used with
+// fp32 outputs only for fp32 state, where nothing is rounded. Each DPP row
+// forms the dots B_j . C_t with j = its row (mod 4) from the sequence's B
+// rows kept in LDS and hands them to the row owners through LDS (a workgroup
+// is one wave, whose LDS accesses complete in order). Longer sequences take
+// the update path.
+constexpr int kYMax = 8;
+
+template <typename ST, typename IT, int N, bool MULTI, bool YONLY = false>
 __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
                              MULTI ? SSU_WAVES_PER_EU_MULTI : SSU_WAVES_PER_EU) void ssu_kernel(const Params p) {
+    static_assert(!YONLY || MULTI, "the output-only path is a multi-token path");
     constexpr int E = N / kLanesPerRow;  // state elements per lane per row
     constexpr int VEC = (16 / (int)sizeof(ST)) < E ? (16 / (int)sizeof(ST)) : E;
     constexpr int NCH = E / VEC;         // accesses per lane per row
@@ -236,6 +253,100 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
         }
     };
 
+    if constexpr (YONLY) {
+        if (len <= kYMax) {  // uniform
+            __shared__ __attribute__((aligned(16))) IT Bl[kYMax][N];  // B rows of the tokens
+            __shared__ float Wl[kYMax][kYMax];                        // Wl[j][t] = B_j . C_t
+            Inputs yin[2];
+            fetch(0, yin[0]);
+            float av[kYMax], dxv[kYMax];  // the own row's decay and dt' x per token
+            float G = 1.0f;               // prod of the decays so far
+#pragma unroll
+            for (int t = 0; t < kYMax; t++) {
+                if (t >= len)
+                    break;  // uniform
+                __builtin_amdgcn_sched_barrier(0);
+                fetch(t + 1 < len ? t + 1 : len - 1, yin[(t + 1) & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                const Inputs &in = yin[t & 1];
+                const int32_t r = first_row + t;
+                float Cv[E];
+#pragma unroll
+                for (int c = 0; c < NCH; c++)
+#pragma unroll
+                    for (int k = 0; k < IVEC; k++)
+                        Cv[c * IVEC + k] = word_elem(in.c[c], k);
+                if (rsub == 0) {
+#pragma unroll
+                    for (int c = 0; c < NCH; c++)
+                        store_words<IT, IVEC>(&Bl[t][c * kLanesPerRow * IVEC + col * IVEC], in.b[c]);
+                }
+                // scalars of the lane's own row
+                const float xv = from_bits<IT>(in.x);
+                const float zv = from_bits<IT>(in.z);
+                const float dtv = dt_f32 ? __uint_as_float(uint32_t(in.dt_lo) | (uint32_t(in.dt_hi) << 16))
+                                         : from_bits<IT>(in.dt_lo);
+                float v = dtv + bias_h;
+                if (flags & kSoftplus)
+                    v = softplus(v);
+                av[t] = exp_hw(v * a_h);
+                dxv[t] = v * xv;
+                G *= av[t];
+                // u = S_0 . C_t of the own row
+                float usum = 0.0f;
+                for_passes<0, PASSES>([&](auto qc) {
+                    constexpr int q = decltype(qc)::value;
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int c = 0; c < NCH; c++)
+#pragma unroll
+                        for (int k = 0; k < VEC; k++)
+                            acc = fmaf(widen(S[q][c].v[k]), Cv[c * VEC + k], acc);
+                    const float sum = row16_sum(acc);
+                    usum = col == q ? sum : usum;
+                });
+                // B_j . C_t for j = rsub, rsub + 4, ... up to t (rows past t
+                // repeat token t and write nothing)
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+                for (int jj = 0; jj < kYMax; jj += kRowsPerPass) {
+                    if (jj > t)
+                        break;  // uniform
+                    const int j = jj + rsub;
+                    const int jr = j <= t ? j : t;
+                    float part = 0.0f;
+#pragma unroll
+                    for (int c = 0; c < NCH; c++) {
+                        const RawWords<IT, IVEC> bw =
+                            *reinterpret_cast<const RawWords<IT, IVEC> *>(&Bl[jr][c * kLanesPerRow * IVEC + col * IVEC]);
+#pragma unroll
+                        for (int k = 0; k < IVEC; k++)
+                            part = fmaf(word_elem(bw, k), Cv[c * IVEC + k], part);
+                    }
+                    const float dot = row16_sum(part);
+                    if (col == 0 && j <= t)
+                        Wl[j][t] = dot;
+                }
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                // the window of the own row, Horner over j
+                float R = 0.0f;
+#pragma unroll
+                for (int j = 0; j < kYMax; j++) {
+                    if (j > t)
+                        break;
+                    R = fmaf(R, av[j], dxv[j] * Wl[j][t]);
+                }
+                if (owner) {
+                    float y = fmaf(G, usum, R) + d_h * xv;
+                    if (zs)
+                        y *= silu(zv);
+                    ys[r * p.out_sr + h * p.out_sh + d_own] = narrow<IT>(y);
+                }
+            }
+            return;
+        }
+    }
+
     // Tokens alternate between two input buffers: the next token's inputs are
     // requested before the current token's stores, and no register copy joins
     // the two, so waiting for one buffer never waits for the other or for the
@@ -282,6 +393,23 @@ bool pick_n(int n, KernelRef *k) {
     return false;
 }
 
+template <typename ST, typename IT>
+bool pick_yonly_n(int n, KernelRef *k) {
+    switch (n) {
+#define SSU_CASE(NN)                                                                     \
+    case NN:                                                                             \
+        k->fn = reinterpret_cast<const void *>(&ssu_kernel<ST, IT, NN, true, true>);    \
+        return true;
+        SSU_CASE(16)
+        SSU_CASE(32)
+        SSU_CASE(64)
+        SSU_CASE(128)
+        SSU_CASE(256)
+#undef SSU_CASE
+    }
+    return false;
+}
+
 template <typename ST>
 bool pick_io(int io, int n, bool multi, KernelRef *k) {
     switch (io) {
@@ -308,6 +436,27 @@ bool find_kernel(int state_dtype, int io_dtype, int dstate, bool multi, KernelRe
     case SSU_F32: return pick_io<float>(io_dtype, dstate, multi, out);
     case SSU_F16: return pick_io<_Float16>(io_dtype, dstate, multi, out);
     case SSU_BF16: return pick_io<__bf16>(io_dtype, dstate, multi, out);
+    }
+    return false;
+}
+
+bool find_yonly_kernel(int state_dtype, int io_dtype, int dstate, KernelRef *out) {
+    // the carry is not rounded between tokens: with fp32 outputs only for
+    // fp32 state
+    switch (state_dtype) {
+    case SSU_F32:
+        return io_dtype == SSU_F32    ? pick_yonly_n<float, float>(dstate, out)
+               : io_dtype == SSU_F16  ? pick_yonly_n<float, _Float16>(dstate, out)
+               : io_dtype == SSU_BF16 ? pick_yonly_n<float, __bf16>(dstate, out)
+                                      : false;
+    case SSU_F16:
+        return io_dtype == SSU_F16    ? pick_yonly_n<_Float16, _Float16>(dstate, out)
+               : io_dtype == SSU_BF16 ? pick_yonly_n<_Float16, __bf16>(dstate, out)
+                                      : false;
+    case SSU_BF16:
+        return io_dtype == SSU_F16    ? pick_yonly_n<__bf16, _Float16>(dstate, out)
+               : io_dtype == SSU_BF16 ? pick_yonly_n<__bf16, __bf16>(dstate, out)
+                                      : false;
     }
     return false;
 }
