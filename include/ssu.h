@@ -373,6 +373,31 @@ SSU_API int64_t ssu_ssd_workspace_bytes(int64_t heads, int64_t dim, int64_t dsta
 SSU_API ssu_status_t ssu_ssd_prefill(const ssu_ssd_args_t *args, void *workspace, int64_t workspace_bytes,
                                      void *stream);
 
+/* ---- SSD prewarm (MATE docs, "Mamba / SSU", the API entry of
+ * prewarm_ssd_combined_fwd_varlen): validate one prefill configuration --
+ * the shape parameters, the dtypes and chunk_size; token and chunk counts
+ * are runtime sizes -- and load its kernels onto the current device, before
+ * any graph capture, so a later ssu_ssd_prefill of that configuration has
+ * no first-use cost. block_M is accepted and ignored (the gfx950 kernels fix
+ * their own tiling). Idempotent and thread-safe; info may be NULL. Errors:
+ * SSU_ERR_VALUE (bad shape or dtype), SSU_ERR_NOT_IMPLEMENTED (a supported
+ * set is left: head dim 64, dstate 64 or 128, chunk_size <= 256, x bf16 or
+ * f16), SSU_ERR_HIP (loading failed). */
+typedef struct {
+    int32_t heads, groups, dim, dstate, chunk_size;
+    int32_t io_dtype, state_dtype, dt_dtype; /* ssu_dtype_t */
+    int32_t block_M;
+} ssu_ssd_plan_desc_t;
+
+typedef struct {
+    int32_t launches;            /* kernels one prefill call enqueues */
+    char kernels[3][64];         /* their names, in launch order */
+    int32_t vgprs[3];            /* their registers per lane */
+    int64_t workspace_bytes_per_chunk; /* ssu_ssd_workspace_bytes(heads, dim, dstate, 1) */
+} ssu_ssd_plan_info_t;
+
+SSU_API ssu_status_t ssu_ssd_plan(const ssu_ssd_plan_desc_t *desc, ssu_ssd_plan_info_t *info);
+
 /* ---- SSD prefill that allocates nothing and takes no workspace argument.
  * For callers that cannot allocate device memory or pass one: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc. Same

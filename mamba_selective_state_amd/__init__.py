@@ -7,7 +7,8 @@ from .ssu import (LIBRARY_PATH, SsuArgs, SsuConvShiftArgs, SsuError, SsuReplayAr
                   SsuSsdArgs, mx8_quantize, replay_lp_selective_state_update,
                   ssu_mx8_quantize, ssu_replay_lp_update, make_replay_lp_args,
                   batch_memcpy, ssd_combined_fwd_varlen, ssu_ssd_prefill, ssu_ssd_workspace_bytes,
-                  ssu_ssd_prefill_noalloc, make_ssd_args, SSD_SCRATCH_BYTES,
+                  ssu_ssd_prefill_noalloc, make_ssd_args, SSD_SCRATCH_BYTES, ssu_ssd_plan,
+                  prewarm_ssd_combined_fwd_varlen, SsuSsdPlanDesc,
                   conv_state_shift, make_args, make_conv_shift_args, make_replay_args,
                   prewarm_selective_state_update, replay_selective_state_update,
                   replay_spec_selective_state_update, selective_state_update, ssu_abi_version,
@@ -21,6 +22,7 @@ __all__ = ["selective_state_update", "prewarm_selective_state_update",
            "SsuError", "LIBRARY_PATH", "batch_memcpy", "conv_state_shift", "ssu_batch_memcpy",
            "ssu_conv_state_shift", "make_conv_shift_args", "SsuConvShiftArgs",
            "ssd_combined_fwd_varlen", "ssu_ssd_prefill", "ssu_ssd_workspace_bytes", "SsuSsdArgs",
-           "ssu_ssd_prefill_noalloc", "make_ssd_args", "SSD_SCRATCH_BYTES",
+           "ssu_ssd_prefill_noalloc", "make_ssd_args", "SSD_SCRATCH_BYTES", "ssu_ssd_plan",
+           "prewarm_ssd_combined_fwd_varlen", "SsuSsdPlanDesc",
            "replay_lp_selective_state_update", "ssu_replay_lp_update", "make_replay_lp_args",
            "SsuReplayLpArgs", "mx8_quantize", "ssu_mx8_quantize"]

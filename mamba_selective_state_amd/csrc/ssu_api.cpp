@@ -639,6 +639,43 @@ static bool contiguous4(const ssu_tensor_t &t) {
            t.stride[1] == t.size[2] * t.size[3] && t.stride[0] == t.size[1] * t.size[2] * t.size[3];
 }
 
+ssu_status_t ssu_ssd_plan(const ssu_ssd_plan_desc_t *d, ssu_ssd_plan_info_t *info) {
+    if (!d)
+        return fail(SSU_ERR_VALUE, "ssu_ssd_plan: desc is NULL");
+    if (d->heads <= 0 || d->groups <= 0 || d->dim <= 0 || d->dstate <= 0)
+        return fail(SSU_ERR_VALUE, "heads, groups, dim and dstate must be positive");
+    if (d->heads % d->groups != 0)
+        return fail(SSU_ERR_VALUE, "heads (%d) must be divisible by groups (%d)", d->heads, d->groups);
+    if (d->io_dtype != SSU_BF16 && d->io_dtype != SSU_F16)
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "SSD prefill takes bf16 or f16 x, got %s", dtype_str(d->io_dtype));
+    if (!is_float(d->state_dtype))
+        return fail(SSU_ERR_VALUE, "state_dtype must be f32, f16 or bf16");
+    if (d->dt_dtype != SSU_F32 && d->dt_dtype != d->io_dtype)
+        return fail(SSU_ERR_VALUE, "dt_dtype must be f32 or the x dtype");
+    if (d->dim != ssu::kSsdDim)
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "SSD prefill supports head dim %d, got %d", ssu::kSsdDim, d->dim);
+    if (d->dstate != 64 && d->dstate != 128)
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "SSD prefill supports dstate 64 or 128, got %d", d->dstate);
+    if (d->chunk_size < 1 || d->chunk_size > ssu::kSsdMaxChunk)
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "chunk_size must be 1..%d, got %d", ssu::kSsdMaxChunk, d->chunk_size);
+    const char *names[3] = {"", "", ""};
+    int vgprs[3] = {0, 0, 0};
+    const int e = ssu::ssd_kernel_attributes(d->io_dtype, d->state_dtype, d->dstate, names, vgprs);
+    if (e != 0)
+        return fail(SSU_ERR_HIP, "loading the SSD kernels failed: %s", ssu::hip_error_string(e));
+    if (info) {
+        memset(info, 0, sizeof *info);
+        info->launches = 3;
+        for (int i = 0; i < 3; i++) {
+            snprintf(info->kernels[i], sizeof info->kernels[i], "%s", names[i]);
+            info->vgprs[i] = vgprs[i];
+        }
+        info->workspace_bytes_per_chunk = ssu_ssd_workspace_bytes(d->heads, d->dim, d->dstate, 1);
+    }
+    g_error.clear();
+    return SSU_OK;
+}
+
 ssu_status_t ssu_ssd_prefill(const ssu_ssd_args_t *a, void *workspace, int64_t workspace_bytes, void *stream) {
     if (!a)
         return fail(SSU_ERR_VALUE, "ssu_ssd_prefill: args is NULL");

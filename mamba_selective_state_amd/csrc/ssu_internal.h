@@ -210,6 +210,10 @@ struct SsdParams {
     float dt_lo, dt_hi;
 };
 int launch_ssd(const SsdParams &sp, int io_dtype, int state_dtype, void *stream);
+// Loads the prefill's three kernels for (io dtype, state dtype, dstate) on
+// the current device; fills their names (launch order) and registers.
+// Returns the hipError_t value as int.
+int ssd_kernel_attributes(int io_dtype, int state_dtype, int dstate, const char *names[3], int vgprs[3]);
 int launch_conv_shift(const ConvParams &cv, bool dim_major, unsigned grid, void *stream);
 
 bool find_replay_kernel(int state_dtype, int io_dtype, int dstate, bool spec, KernelRef *out);

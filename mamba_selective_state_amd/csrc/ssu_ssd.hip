@@ -770,7 +770,36 @@ int launch_ssd_typed(const SsdParams &sp, int state_dtype, void *stream) {
     return static_cast<int>(e);
 }
 
+template <typename IT, int N>
+int attributes_typed(int state_dtype, const char *names[3], int vgprs[3]) {
+    const void *fns[3] = {
+        reinterpret_cast<const void *>(&ssd_chunk_state_kernel<IT, N>),
+        state_dtype == SSU_F32   ? reinterpret_cast<const void *>(&ssd_state_pass_kernel<float, IT>)
+        : state_dtype == SSU_F16 ? reinterpret_cast<const void *>(&ssd_state_pass_kernel<_Float16, IT>)
+                                 : reinterpret_cast<const void *>(&ssd_state_pass_kernel<__bf16, IT>),
+        reinterpret_cast<const void *>(&ssd_chunk_scan_kernel<IT, N>)};
+    names[0] = "ssd_chunk_state_kernel";
+    names[1] = "ssd_state_pass_kernel";
+    names[2] = "ssd_chunk_scan_kernel";
+    for (int i = 0; i < 3; i++) {
+        hipFuncAttributes attr;
+        const hipError_t e = hipFuncGetAttributes(&attr, fns[i]);
+        if (e != hipSuccess)
+            return static_cast<int>(e);
+        vgprs[i] = attr.numRegs;
+    }
+    return 0;
+}
+
 }  // namespace
+
+int ssd_kernel_attributes(int io_dtype, int state_dtype, int dstate, const char *names[3], int vgprs[3]) {
+    if (io_dtype == SSU_BF16)
+        return dstate == 64 ? attributes_typed<__bf16, 64>(state_dtype, names, vgprs)
+                            : attributes_typed<__bf16, 128>(state_dtype, names, vgprs);
+    return dstate == 64 ? attributes_typed<_Float16, 64>(state_dtype, names, vgprs)
+                        : attributes_typed<_Float16, 128>(state_dtype, names, vgprs);
+}
 
 int launch_ssd(const SsdParams &sp, int io_dtype, int state_dtype, void *stream) {
     if (io_dtype == SSU_BF16)

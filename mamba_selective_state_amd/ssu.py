@@ -67,6 +67,17 @@ class SsuSsdArgs(ctypes.Structure):
 OPT_SSD_CHECKPOINT = 64
 
 
+class SsuSsdPlanDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("heads", "groups", "dim", "dstate", "chunk_size", "io_dtype", "state_dtype",
+                 "dt_dtype", "block_M")]
+
+
+class SsuSsdPlanInfo(ctypes.Structure):
+    _fields_ = [("launches", ctypes.c_int32), ("kernels", (ctypes.c_char * 64) * 3),
+                ("vgprs", ctypes.c_int32 * 3), ("workspace_bytes_per_chunk", ctypes.c_int64)]
+
+
 class SsuPlanDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("state_dtype", "io_dtype", "dt_dtype", "slot_dtype", "meta_dtype", "heads",
@@ -81,7 +92,7 @@ class SsuPlanInfo(ctypes.Structure):
 
 EXPORTS = ("ssu_plan", "ssu_update", "ssu_replay_update", "ssu_replay_spec_update",
            "ssu_replay_lp_update", "ssu_mx8_quantize", "ssu_batch_memcpy", "ssu_conv_state_shift", "ssu_ssd_workspace_bytes", "ssu_ssd_prefill",
-           "ssu_ssd_prefill_noalloc", "ssu_last_error", "ssu_abi_version")
+           "ssu_ssd_prefill_noalloc", "ssu_ssd_plan", "ssu_last_error", "ssu_abi_version")
 SSD_SCRATCH_BYTES = 64 << 20  # SSU_SSD_SCRATCH_BYTES
 
 
@@ -114,6 +125,8 @@ def load_library(path=None):
     lib.ssu_ssd_prefill.argtypes = [ctypes.POINTER(SsuSsdArgs), ctypes.c_void_p, ctypes.c_int64,
                                     ctypes.c_void_p]
     lib.ssu_ssd_prefill.restype = ctypes.c_int
+    lib.ssu_ssd_plan.argtypes = [ctypes.POINTER(SsuSsdPlanDesc), ctypes.POINTER(SsuSsdPlanInfo)]
+    lib.ssu_ssd_plan.restype = ctypes.c_int
     lib.ssu_ssd_prefill_noalloc.argtypes = [ctypes.POINTER(SsuSsdArgs), ctypes.c_void_p]
     lib.ssu_ssd_prefill_noalloc.restype = ctypes.c_int
     lib.ssu_last_error.argtypes = []
@@ -480,6 +493,35 @@ def ssu_ssd_prefill(args, workspace, workspace_bytes, stream=None):
                               ctypes.c_void_p(stream))
     if st != OK:
         _raise(st, "ssu_ssd_prefill")
+
+
+def ssu_ssd_plan(desc):
+    """Validate an SSD prefill configuration and load its kernels
+    (include/ssu.h ssu_ssd_plan); returns what was loaded."""
+    info = SsuSsdPlanInfo()
+    st = _lib.ssu_ssd_plan(ctypes.byref(desc), ctypes.byref(info))
+    if st != OK:
+        _raise(st, "ssu_ssd_plan")
+    return {"launches": info.launches,
+            "kernels": [info.kernels[i].value.decode() for i in range(info.launches)],
+            "vgprs": [info.vgprs[i] for i in range(info.launches)],
+            "workspace_bytes_per_chunk": info.workspace_bytes_per_chunk}
+
+
+def prewarm_ssd_combined_fwd_varlen(heads, groups, dim, dstate, chunk_size, io_dtype=torch.bfloat16,
+                                    state_dtype=torch.bfloat16, dt_dtype=torch.float32, block_M=32):
+    """Validate one SSD prefill configuration and load its kernels on the
+    current device, before any graph capture (MATE
+    prewarm_ssd_combined_fwd_varlen; block_M is accepted and ignored: the
+    gfx950 kernels fix their own tiling). Token and chunk counts are runtime
+    sizes. Returns what was loaded."""
+    d = SsuSsdPlanDesc()
+    d.heads, d.groups, d.dim, d.dstate, d.chunk_size = heads, groups, dim, dstate, chunk_size
+    d.io_dtype = _TORCH_DTYPES[io_dtype]
+    d.state_dtype = _TORCH_DTYPES[state_dtype]
+    d.dt_dtype = _TORCH_DTYPES[dt_dtype]
+    d.block_M = block_M
+    return ssu_ssd_plan(d)
 
 
 def ssu_ssd_prefill_noalloc(args, stream=None):

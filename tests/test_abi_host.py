@@ -41,7 +41,8 @@ def test_struct_layout_matches_header(tmp_path):
                "ssu_plan_desc_t": S.SsuPlanDesc, "ssu_plan_info_t": S.SsuPlanInfo,
                "ssu_replay_args_t": S.SsuReplayArgs, "ssu_replay_lp_args_t": S.SsuReplayLpArgs,
                "ssu_conv_shift_args_t": S.SsuConvShiftArgs,
-               "ssu_ssd_args_t": S.SsuSsdArgs}
+               "ssu_ssd_args_t": S.SsuSsdArgs, "ssu_ssd_plan_desc_t": S.SsuSsdPlanDesc,
+               "ssu_ssd_plan_info_t": S.SsuSsdPlanInfo}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "ssu.h"', "int main(void) {"]
     for cname, cls in structs.items():
         lines.append('printf("%s SIZEOF %%zu\\n", sizeof(%s));' % (cname, cname))
@@ -643,3 +644,29 @@ def test_ssd_noalloc_rejects_oversized_and_null():
     st = S._lib.ssu_ssd_prefill_noalloc(ctypes.byref(a), None)
     msg = S.ssu_last_error()
     assert st == S.ERR_VALUE and str(need) in msg and str(S.SSD_SCRATCH_BYTES) in msg, msg
+
+
+def test_ssd_plan_validation():
+    """The SSD prewarm refuses, before loading anything, configurations the
+    prefill does not take, naming the rule or the capability."""
+    def plan(**kw):
+        d = S.SsuSsdPlanDesc()
+        base = dict(heads=8, groups=2, dim=64, dstate=128, chunk_size=256, io_dtype=S.BF16,
+                    state_dtype=S.F32, dt_dtype=S.F32, block_M=32)
+        base.update(kw)
+        for k, v in base.items():
+            setattr(d, k, v)
+        info = S.SsuSsdPlanInfo()
+        return S._lib.ssu_ssd_plan(ctypes.byref(d), ctypes.byref(info)), S.ssu_last_error()
+
+    assert S._lib.ssu_ssd_plan(None, None) == S.ERR_VALUE
+    for kw, status, word in ((dict(heads=6, groups=4), S.ERR_VALUE, "divisible"),
+                             (dict(heads=0), S.ERR_VALUE, "positive"),
+                             (dict(io_dtype=S.F32), S.ERR_NOT_IMPLEMENTED, "bf16 or f16"),
+                             (dict(state_dtype=S.I32), S.ERR_VALUE, "state_dtype"),
+                             (dict(dt_dtype=S.F16), S.ERR_VALUE, "dt_dtype"),
+                             (dict(dim=128), S.ERR_NOT_IMPLEMENTED, "head dim"),
+                             (dict(dstate=256), S.ERR_NOT_IMPLEMENTED, "dstate"),
+                             (dict(chunk_size=512), S.ERR_NOT_IMPLEMENTED, "chunk_size")):
+        st, msg = plan(**kw)
+        assert st == status and word in msg, (kw, st, msg)

@@ -6,8 +6,9 @@ that is scaled before a product (w_t x_t in the chunk states, the masked
 and scaled C.B^T in the scan, the entering state read out by C) is rounded to the x
 dtype: 2^-9 relative per operand, summed over at most chunk_size + dstate
 terms of random sign. y and the returned states are compared at
-3e-2 x max|ref| (the 16-bit tolerance of the decode path with headroom for
-the extra operand rounding), on every element.
+2e-2 x max|ref| (the 16-bit tolerance of the decode path), on every
+element; the largest error over max|ref| observed on MI355X is 0.0054 for y
+and 0.0032 for the states (each case prints its own).
 """
 import numpy as np
 import pytest
@@ -18,7 +19,7 @@ import workloads as W
 from oracle import ssu_oracle
 
 pytestmark = pytest.mark.gpu
-TOL = 3e-2
+TOL = 2e-2
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -143,3 +144,55 @@ def test_ssd_many_chunks():
     assert len(c["seq_idx"]) > 1024 and c["seq_idx"][1023] == c["seq_idx"][1024] == 1
     check_ssd(c, "ssd 1252 chunks")
     check_ssd(c, "ssd 1252 chunks, intermediate", intermediate=True)
+
+
+def test_ssd_prewarm_then_graph_replay():
+    """The prewarm loads the three kernels for a configuration; a prefill
+    captured in a HIP graph afterwards replays to the eager result, every
+    replay (eager work and synchronisation in between), and matches the
+    oracle."""
+    info = G.ssu.prewarm_ssd_combined_fwd_varlen(8, 2, 64, 128, 128, io_dtype=torch.bfloat16,
+                                                 state_dtype=torch.float32, dt_dtype=torch.float32)
+    assert info["launches"] == 3 and all(v > 0 for v in info["vgprs"])
+    assert info["kernels"] == ["ssd_chunk_state_kernel", "ssd_state_pass_kernel", "ssd_chunk_scan_kernel"]
+    c = W.ssd(seed=31, lengths=(300, 17, 129), heads=8, dim=64, dstate=128, groups=2, chunk_size=128,
+              io="bf16", state_dtype="f32", initial_states=True)
+    ref = ssu_oracle.run_ssd(c)
+    dev = "cuda:0"
+    d = {k: G.dev(c[k], "bf16", dev) for k in ("x", "B", "C", "z")}
+    dt = G.dev(c["dt"], c["dt_dtype"], dev)
+    idx = {k: torch.from_numpy(np.asarray(c[k])).to(dev)
+           for k in ("cu_seqlens", "cu_chunk_seqlens", "last_chunk_indices", "seq_idx")}
+    init = G.dev(c["initial_states"], "f32", dev)
+    A, D, bias = (torch.from_numpy(c[k]).to(dev) for k in ("A", "D", "dt_bias"))
+    nchunks = len(c["seq_idx"])
+    out = torch.empty_like(d["x"])
+    states = torch.empty((len(c["last_chunk_indices"]), 8, 64, 128), dtype=torch.float32, device=dev)
+    ws = torch.empty(G.ssu.ssu_ssd_workspace_bytes(8, 64, 128, nchunks), dtype=torch.uint8, device=dev)
+    a = G.ssu.make_ssd_args(d["x"], dt, A, d["B"], d["C"], c["chunk_size"], idx["cu_seqlens"],
+                            idx["cu_chunk_seqlens"], idx["last_chunk_indices"], idx["seq_idx"], out,
+                            states, D=D, z=d["z"], dt_bias=bias, dt_softplus=c["dt_softplus"],
+                            dt_limit=c["dt_limit"], initial_states=init)
+    G.say("[gpu] ssd graph: eager")
+    G.ssu.ssu_ssd_prefill(a, ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    y_eager, s_eager = G.host(out, "bf16"), G.host(states, "f32")
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    G.say("[gpu] ssd graph: capturing")
+    with torch.cuda.graph(g, stream=stream):
+        G.ssu.ssu_ssd_prefill(a, ws.data_ptr(), ws.numel(), torch.cuda.current_stream().cuda_stream)
+    for i in range(3):
+        out.fill_(float("nan"))
+        states.fill_(float("nan"))
+        ws.fill_(255)  # the workspace holds nothing a call reads before writing it
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(G.host(out, "bf16"), y_eager), i
+        assert np.array_equal(G.host(states, "f32"), s_eager), i
+    ry = G.brute64.to_f64(ref["y"], "bf16")
+    assert np.abs(G.brute64.to_f64(y_eager, "bf16") - ry).max() <= TOL * np.abs(ry).max()
+    rs = ref["states"].astype(np.float64)
+    assert np.abs(s_eager.astype(np.float64) - rs).max() <= TOL * np.abs(rs).max()
+    G.say("[gpu] ssd graph: 3 replays identical to the eager call")
