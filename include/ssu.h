@@ -338,7 +338,8 @@ SSU_API ssu_status_t ssu_conv_state_shift(const ssu_conv_shift_args_t *args, voi
  * every sequence b, or the state after every chunk when
  * return_intermediate_states is set. The products run on bf16 / f16 matrix
  * cores (the x dtype) with fp32 accumulation.
- * Supported: head dim 64, dstate 64 or 128, chunk_size <= 256, x bf16 or f16,
+ * Supported: head dims that are multiples of 64, dstate 64 or 128,
+ * chunk_size <= 256, x bf16 or f16,
  * states f32 / f16 / bf16. A chunk whose cu_chunk_seqlens entries are out of
  * range or longer than chunk_size is taken as empty (checked on the device). */
 typedef struct {
@@ -381,8 +382,8 @@ SSU_API ssu_status_t ssu_ssd_prefill(const ssu_ssd_args_t *args, void *workspace
  * no first-use cost. block_M is accepted and ignored (the gfx950 kernels fix
  * their own tiling). Idempotent and thread-safe; info may be NULL. Errors:
  * SSU_ERR_VALUE (bad shape or dtype), SSU_ERR_NOT_IMPLEMENTED (a supported
- * set is left: head dim 64, dstate 64 or 128, chunk_size <= 256, x bf16 or
- * f16), SSU_ERR_HIP (loading failed). */
+ * set is left: head dims a multiple of 64, dstate 64 or 128, chunk_size <=
+ * 256, x bf16 or f16), SSU_ERR_HIP (loading failed). */
 typedef struct {
     int32_t heads, groups, dim, dstate, chunk_size;
     int32_t io_dtype, state_dtype, dt_dtype; /* ssu_dtype_t */

@@ -600,7 +600,8 @@ ssu_status_t ssu_batch_memcpy(const ssu_tensor_t *src_ptrs, const ssu_tensor_t *
 static int64_t ssd_ws_parts(int64_t H, int64_t P, int64_t N, int64_t nchunks, int64_t *rows_bytes,
                             int64_t *state_bytes = nullptr) {
     auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
-    *rows_bytes = up(nchunks * H * ssu::kSsdMaxChunk * 4);
+    const int64_t parts = (P + ssu::kSsdDim - 1) / ssu::kSsdDim;  // kSsdDim-wide parts of a head
+    *rows_bytes = up(nchunks * H * parts * ssu::kSsdMaxChunk * 4);
     const int64_t sb = up(nchunks * H * P * N * 4);
     if (state_bytes)
         *state_bytes = sb;
@@ -652,8 +653,9 @@ ssu_status_t ssu_ssd_plan(const ssu_ssd_plan_desc_t *d, ssu_ssd_plan_info_t *inf
         return fail(SSU_ERR_VALUE, "state_dtype must be f32, f16 or bf16");
     if (d->dt_dtype != SSU_F32 && d->dt_dtype != d->io_dtype)
         return fail(SSU_ERR_VALUE, "dt_dtype must be f32 or the x dtype");
-    if (d->dim != ssu::kSsdDim)
-        return fail(SSU_ERR_NOT_IMPLEMENTED, "SSD prefill supports head dim %d, got %d", ssu::kSsdDim, d->dim);
+    if (d->dim % ssu::kSsdDim != 0)
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "SSD prefill supports head dims that are multiples of %d, got %d",
+                    ssu::kSsdDim, d->dim);
     if (d->dstate != 64 && d->dstate != 128)
         return fail(SSU_ERR_NOT_IMPLEMENTED, "SSD prefill supports dstate 64 or 128, got %d", d->dstate);
     if (d->chunk_size < 1 || d->chunk_size > ssu::kSsdMaxChunk)
@@ -690,9 +692,9 @@ ssu_status_t ssu_ssd_prefill(const ssu_ssd_args_t *a, void *workspace, int64_t w
     if (x.dtype != SSU_BF16 && x.dtype != SSU_F16)
         return fail(SSU_ERR_NOT_IMPLEMENTED, "SSD prefill takes bf16 or f16 x, got %s", dtype_str(x.dtype));
     const int64_t T = x.size[0], H = x.size[1], P = x.size[2];
-    if (P != ssu::kSsdDim)
-        return fail(SSU_ERR_NOT_IMPLEMENTED, "SSD prefill supports head dim %d, got %lld", ssu::kSsdDim,
-                    (long long)P);
+    if (P <= 0 || P % ssu::kSsdDim != 0)
+        return fail(SSU_ERR_NOT_IMPLEMENTED, "SSD prefill supports head dims that are multiples of %d, got %lld",
+                    ssu::kSsdDim, (long long)P);
     ssu::SsdParams sp;
     memset(&sp, 0, sizeof sp);
     ssu_status_t s;
@@ -772,7 +774,8 @@ ssu_status_t ssu_ssd_prefill(const ssu_ssd_args_t *a, void *workspace, int64_t w
         return g_error.clear(), SSU_OK;
     if (!a->return_intermediate_states && nchunks > 16384)
         return fail(SSU_ERR_NOT_IMPLEMENTED, "more than 16384 chunks");
-    if (nchunks * H > INT32_MAX)
+    const int64_t hsplit = P / ssu::kSsdDim;
+    if (nchunks * H * hsplit > INT32_MAX / 8)
         return fail(SSU_ERR_NOT_IMPLEMENTED, "grid too large");
     int64_t rows_bytes, state_bytes;
     const int64_t need = ssd_ws_parts(H, P, N, nchunks, &rows_bytes, &state_bytes);
@@ -791,12 +794,13 @@ ssu_status_t ssu_ssd_prefill(const ssu_ssd_args_t *a, void *workspace, int64_t w
     sp.out = const_cast<void *>(a->out.data);
     sp.states = const_cast<void *>(st.data);
     sp.T = T;
-    sp.H = H;
+    sp.H = H * hsplit;  // the kernels see heads of dim kSsdDim
+    sp.hsplit = static_cast<int32_t>(hsplit);
     sp.N = N;
     sp.nchunks = nchunks;
     sp.batch = batch;
     sp.chunk_size = a->chunk_size;
-    sp.hpg = static_cast<int32_t>(H / G);
+    sp.hpg = static_cast<int32_t>(H / G * hsplit);
     sp.dt_f32 = dt.dtype == SSU_F32;
     sp.softplus = a->dt_softplus != 0;
     sp.intermediate = a->return_intermediate_states != 0;

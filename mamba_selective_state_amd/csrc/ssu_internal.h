@@ -207,6 +207,7 @@ struct SsdParams {
     int64_t cu_chunk_s, seq_idx_s, last_chunk_s;
     int32_t cu_chunk_i64, seq_idx_i64, last_chunk_i64;
     int32_t hpg, dt_f32, softplus, intermediate;
+    int32_t hsplit;  // kSsdDim-wide parts per head: H and hpg count the parts
     float dt_lo, dt_hi;
 };
 int launch_ssd(const SsdParams &sp, int io_dtype, int state_dtype, void *stream);

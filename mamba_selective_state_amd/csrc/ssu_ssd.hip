@@ -14,7 +14,9 @@
 //                            silu(z_t) (MFMA).
 // MFMA operands are bf16 / f16 (the x dtype): 16x16x32 tiles with fp32
 // accumulation; the scaled operands (w_t x_t, the scaled C.B^T, the entering
-// state) are rounded to the x dtype before they enter a product.
+// state) are rounded to the x dtype before they enter a product. Every
+// kernel works on heads of dim 64; wider heads (a multiple of 64) are split
+// into several of those (head_off).
 
 #include <hip/hip_runtime.h>
 
@@ -65,6 +67,16 @@ __device__ __forceinline__ float to_f(T v) { return static_cast<float>(v); }
 
 __device__ __forceinline__ int64_t idx_at(const void *base, bool i64, int64_t i) {
     return i64 ? static_cast<const int64_t *>(base)[i] : static_cast<int64_t>(static_cast<const int32_t *>(base)[i]);
+}
+
+// A head of dim kP * hsplit runs as hsplit heads of dim kP ("virtual"
+// heads, numbered hsplit * head + part): each part is dims part * kP .. of
+// the head's rows of x, z and out, and takes the head's dt, A, D, dt_bias
+// (the recurrence never mixes dim rows); the contiguous state and workspace
+// layouts [.., heads, dim, dstate] are the same memory as [.., virtual
+// heads, kP, dstate]. Element offset of virtual head v in a row of x, z or out:
+__device__ __forceinline__ int64_t head_off(const SsdParams &sp, int v, int64_t head_stride) {
+    return static_cast<int64_t>(v / sp.hsplit) * head_stride + static_cast<int64_t>(v % sp.hsplit) * kP;
 }
 
 // Token range of chunk c; an inconsistent entry (outside the tokens, or
@@ -165,7 +177,7 @@ __global__ __launch_bounds__(kStateThreads) void ssd_chunk_state_kernel(const Ss
     const int64_t tok = tk < len ? t0 + tk : 0;
 
     auto load_x = [&](int h, V (&xv)[kHalfP / 8]) {
-        const IT *xrow = static_cast<const IT *>(sp.x) + (tok * sp.x_st + h * sp.x_sh) + half * kHalfP;
+        const IT *xrow = static_cast<const IT *>(sp.x) + (tok * sp.x_st + head_off(sp, h, sp.x_sh)) + half * kHalfP;
 #pragma unroll
         for (int p0 = 0; p0 < kHalfP / 8; p0++)
             xv[p0] = *reinterpret_cast<const V *>(xrow + 8 * p0);
@@ -177,9 +189,9 @@ __global__ __launch_bounds__(kStateThreads) void ssd_chunk_state_kernel(const Ss
 #pragma unroll
     for (int hk = 0; hk < kStateHeads; hk++) {
         const int h = hk < nh ? h0 + hk : h0;
-        Ah[hk] = sp.A[h * sp.A_sh];
-        biash[hk] = sp.dt_bias ? sp.dt_bias[h * sp.bias_sh] : 0.0f;
-        dtr[hk] = raw_dt<IT>(sp, tok, h);
+        Ah[hk] = sp.A[(h / sp.hsplit) * sp.A_sh];
+        biash[hk] = sp.dt_bias ? sp.dt_bias[(h / sp.hsplit) * sp.bias_sh] : 0.0f;
+        dtr[hk] = raw_dt<IT>(sp, tok, h / sp.hsplit);
     }
     V bv[kHalfN / 8];
     {
@@ -466,7 +478,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(const SsdP
     };
     const int pc = 8 * (t & 7);
     auto load_head = [&](int h, HeadIn &in) {
-        const IT *xs = static_cast<const IT *>(sp.x) + h * sp.x_sh + pc;
+        const IT *xs = static_cast<const IT *>(sp.x) + head_off(sp, h, sp.x_sh) + pc;
 #pragma unroll
         for (int u = 0; u < 2; u++)
 #pragma unroll
@@ -598,7 +610,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(const SsdP
     float Dh[kScanHeads];
 #pragma unroll
     for (int hk = 0; hk < kScanHeads; hk++)
-        Dh[hk] = sp.D ? sp.D[(hk < nh ? h0 + hk : h0) * sp.D_sh] : 0.0f;
+        Dh[hk] = sp.D ? sp.D[((hk < nh ? h0 + hk : h0) / sp.hsplit) * sp.D_sh] : 0.0f;
 
     for (int hk = 0; hk < nh; hk++) {
         const int h = h0 + hk;
@@ -609,7 +621,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(const SsdP
         // z of the lane's token (16 consecutive p), for the gate
         auto load_z = [&](int tt, V (&zv2)[2]) {
             const int64_t tok = t0 + (tt < len ? tt : len - 1);
-            const IT *zg = zs + tok * sp.z_st + h * sp.z_sh + 16 * gq;
+            const IT *zg = zs + tok * sp.z_st + head_off(sp, h, sp.z_sh) + 16 * gq;
 #pragma unroll
             for (int k = 0; k < 2; k++)
                 zv2[k] = zs ? *reinterpret_cast<const V *>(zg + 8 * k) : V{};
@@ -697,7 +709,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(const SsdP
                         v *= silu_f(to_f(zv2[e / 8][e % 8]));
                     o[e / 8][e % 8] = static_cast<IT>(v);
                 }
-            IT *orow = outp + tok * sp.out_st + h * sp.out_sh + 16 * gq;
+            IT *orow = outp + tok * sp.out_st + head_off(sp, h, sp.out_sh) + 16 * gq;
             *reinterpret_cast<V *>(orow) = o[0];
             *reinterpret_cast<V *>(orow + 8) = o[1];
         };

@@ -665,7 +665,7 @@ def test_ssd_plan_validation():
                              (dict(io_dtype=S.F32), S.ERR_NOT_IMPLEMENTED, "bf16 or f16"),
                              (dict(state_dtype=S.I32), S.ERR_VALUE, "state_dtype"),
                              (dict(dt_dtype=S.F16), S.ERR_VALUE, "dt_dtype"),
-                             (dict(dim=128), S.ERR_NOT_IMPLEMENTED, "head dim"),
+                             (dict(dim=96), S.ERR_NOT_IMPLEMENTED, "head dim"),
                              (dict(dstate=256), S.ERR_NOT_IMPLEMENTED, "dstate"),
                              (dict(chunk_size=512), S.ERR_NOT_IMPLEMENTED, "chunk_size")):
         st, msg = plan(**kw)

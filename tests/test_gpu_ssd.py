@@ -126,6 +126,17 @@ def test_ssd_head_blocks(heads, groups):
     check_ssd(c, "ssd %d heads / %d groups, intermediate" % (heads, groups), intermediate=True)
 
 
+@pytest.mark.parametrize("dim,heads,groups,N", [(128, 4, 2, 128), (192, 3, 1, 64), (256, 2, 2, 128)],
+                         ids=["dim128", "dim192-3heads", "dim256"])
+def test_ssd_wide_heads(dim, heads, groups, N):
+    """Head dims that are multiples of 64 (each head runs as dim / 64 parts
+    sharing its dt, A, D and group), with initial and intermediate states."""
+    c = W.ssd(seed=dim + heads, lengths=(300, 17, 129), heads=heads, dim=dim, dstate=N, groups=groups,
+              chunk_size=128, io="bf16", state_dtype="f32", initial_states=True)
+    check_ssd(c, "ssd dim %d, %d heads / %d groups" % (dim, heads, groups))
+    check_ssd(c, "ssd dim %d, intermediate" % dim, intermediate=True)
+
+
 def test_ssd_tiny_chunks():
     """Seventeen sequences of 1..17 tokens at chunk size 16: every chunk is
     shorter than a 32-token block and most are ragged 16-row tiles."""
