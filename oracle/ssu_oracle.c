@@ -622,6 +622,80 @@ float oracle_mx8_value(uint8_t code, uint8_t scale)
     return ldexpf(oracle_e4m3_decode(code), (int)scale - 127);
 }
 
+/* ---- MXFP4 (E2M1) block format: a 4-bit read copy
+ *
+ * The same read copy as MXFP8 above with 4-bit elements (the ReplaySSM
+ * article measures a 4-bit copy; OCP Microscaling v1.0's MXFP4 is the 4-bit
+ * format with power-of-two block scales): blocks of 32 consecutive dstate
+ * elements share an E8M0 scale, elements are FP4 E2M1 (1 sign, 2 exponent
+ * bits with bias 1, 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6;
+ * no infinities, no NaN).
+ *
+ * Readings:
+ *  R33 two elements per byte: element 2i in the low nibble, 2i+1 in the high
+ *      nibble; a copy row of dstate values takes dstate / 2 bytes;
+ *  R34 block scale exponent = floor(log2(max |x|)) - 2 (2 = the exponent of
+ *      E2M1's largest power of two, so the largest element lands in [4, 8)),
+ *      clamped to [-126, 127], -126 for a block of zeros (as R30); elements
+ *      x / 2^exponent rounded to nearest, ties to the even code, in E2M1;
+ *      magnitudes above 6 saturate to 6; a NaN element gets code 0 (E2M1
+ *      has no NaN; checkpoints are finite).
+ */
+float oracle_e2m1_decode(uint8_t nib)
+{
+    const int s = (nib >> 3) & 1, e = (nib >> 1) & 3, m = nib & 1;
+    const float mag = e == 0 ? 0.5f * (float)m : ldexpf(1.0f + 0.5f * (float)m, e - 1);
+    return s ? -mag : mag;
+}
+
+uint8_t oracle_e2m1_encode(float v)
+{
+    if (isnan(v))
+        return 0; /* R34 */
+    const uint8_t sign = signbit(v) ? 8 : 0;
+    const float a = fabsf(v);
+    if (a >= 6.0f)
+        return sign | 7; /* R34: saturate */
+    int code;
+    if (a < 2.0f) /* 0, 0.5, 1, 1.5, 2: codes 0..4, steps of 0.5 */
+        code = (int)nearbyintf(a * 2.0f);
+    else if (a < 4.0f) /* 2, 3, 4: codes 4, 5, 6 */
+        code = 4 + ((int)nearbyintf(a) - 2);
+    else /* 4, 6: codes 6, 7 */
+        code = 6 + ((int)nearbyintf(a * 0.5f) - 2);
+    return sign | (uint8_t)code;
+}
+
+/* one block of 32 values -> 16 bytes of codes and the scale byte */
+void oracle_mx4_block(const float *x, uint8_t *codes, uint8_t *scale)
+{
+    float amax = 0.0f;
+    for (int i = 0; i < 32; i++)
+        if (fabsf(x[i]) > amax)
+            amax = fabsf(x[i]);
+    int k = -126;
+    if (amax > 0.0f) {
+        int ex;
+        frexpf(amax, &ex);
+        k = (ex - 1) - 2; /* R34 */
+        if (k < -126)
+            k = -126;
+        if (k > 127)
+            k = 127;
+    }
+    *scale = (uint8_t)(k + 127);
+    for (int i = 0; i < 16; i++)
+        codes[i] = (uint8_t)(oracle_e2m1_encode(ldexpf(x[2 * i], -k)) |
+                             (oracle_e2m1_encode(ldexpf(x[2 * i + 1], -k)) << 4)); /* R33 */
+}
+
+/* element i of a row of codes (R33), times its block scale */
+float oracle_mx4_value(const uint8_t *codes, int64_t i, uint8_t scale)
+{
+    const uint8_t nib = (uint8_t)((codes[i / 2] >> (4 * (i & 1))) & 15);
+    return ldexpf(oracle_e2m1_decode(nib), (int)scale - 127);
+}
+
 /* ---- ReplaySSM decode: checkpoint plus input buffer
  *
  * ReplaySSM article (lpnh.cn), section "核心做法" (core method) and its
@@ -670,6 +744,7 @@ typedef struct {
      * codes [slots, H, P, N], scales [slots, H, P, N / 32] */
     const uint8_t *lp_in, *lps_in;
     uint8_t *lp_out, *lps_out;
+    int32_t lp_bits; /* 8: MXFP8 codes [slots, H, P, N]; 4: MXFP4 codes [slots, H, P, N / 2] */
 } oracle_replay_args;
 
 /* dt' of one buffered or current step, one dim row */
@@ -766,11 +841,13 @@ static void replay_sequence(const void *args, int64_t b, void *scratch)
                           : load_as_f32(a->B, a->io_dtype, (b * G + g) * N + (n)))
             /* R32: an output-only step reads the read copy when there is one */
             const int from_copy = ra->lp_in && h + 1 != L && !pad;
-            for (int64_t e = 0; e < tile; e++)
-                S[e] = pad ? 0.0f
-                           : from_copy ? oracle_mx8_value(ra->lp_in[(s * H + hd) * tile + e],
-                                                          ra->lps_in[((s * H + hd) * tile + e) / 32])
-                                       : load_as_f32(a->pool_in, a->state_dtype, (s * H + hd) * tile + e);
+            for (int64_t e = 0; e < tile; e++) {
+                const int64_t at = (s * H + hd) * tile + e; /* element of the pool */
+                S[e] = pad         ? 0.0f
+                       : !from_copy ? load_as_f32(a->pool_in, a->state_dtype, at)
+                       : ra->lp_bits == 4 ? oracle_mx4_value(ra->lp_in, at, ra->lps_in[at / 32])
+                                          : oracle_mx8_value(ra->lp_in[at], ra->lps_in[at / 32]);
+            }
             if (h + 1 == L) {
                 /* flush: fold the buffered steps and the current one into the
                  * checkpoint, one plain update after the other */
@@ -803,9 +880,13 @@ static void replay_sequence(const void *args, int64_t b, void *scratch)
                     if (a->written)
                         a->written[s] = 1;
                     if (ra->lp_out) /* R32: the fold rewrites the read copy */
-                        for (int64_t e = 0; e < tile; e += 32)
-                            oracle_mx8_block(S + e, ra->lp_out + (s * H + hd) * tile + e,
-                                             ra->lps_out + ((s * H + hd) * tile + e) / 32);
+                        for (int64_t e = 0; e < tile; e += 32) {
+                            const int64_t at = (s * H + hd) * tile + e;
+                            if (ra->lp_bits == 4)
+                                oracle_mx4_block(S + e, ra->lp_out + at / 2, ra->lps_out + at / 32);
+                            else
+                                oracle_mx8_block(S + e, ra->lp_out + at, ra->lps_out + at / 32);
+                        }
                 }
             } else {
                 /* output-only: y from the checkpoint and the buffer */
@@ -1250,6 +1331,18 @@ void oracle_mx8_quantize(const float *x, int64_t nblocks, uint8_t *codes, uint8_
 {
     for (int64_t b = 0; b < nblocks; b++)
         oracle_mx8_block(x + 32 * b, codes + 32 * b, scales + b);
+}
+
+void oracle_mx4_quantize(const float *x, int64_t nblocks, uint8_t *codes, uint8_t *scales)
+{
+    for (int64_t b = 0; b < nblocks; b++)
+        oracle_mx4_block(x + 32 * b, codes + 16 * b, scales + b);
+}
+
+void oracle_mx4_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t nblocks, float *x)
+{
+    for (int64_t i = 0; i < nblocks * 32; i++)
+        x[i] = oracle_mx4_value(codes, i, scales[i / 32]);
 }
 
 void oracle_mx8_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t nblocks, float *x)

@@ -249,11 +249,15 @@ class _ReplayArgs(ctypes.Structure):
                 ("bB_in", ctypes.c_void_p), ("bB_out", ctypes.c_void_p),
                 ("buf_len", ctypes.c_void_p),
                 ("lp_in", ctypes.c_void_p), ("lps_in", ctypes.c_void_p),
-                ("lp_out", ctypes.c_void_p), ("lps_out", ctypes.c_void_p)]
+                ("lp_out", ctypes.c_void_p), ("lps_out", ctypes.c_void_p),
+                ("lp_bits", ctypes.c_int32)]
 
 
 def run_replay(case, oracle=None):
-    """ReplaySSM decode step (oracle_replay in ssu_oracle.c). The case holds
+    """ReplaySSM decode step (oracle_replay in ssu_oracle.c). With "lp" and
+    "lp_scale" the output-only steps read that copy of the checkpoint pool:
+    MXFP8 codes [slots, H, P, N], or with lp_format "mx4" MXFP4 codes
+    [slots, H, P, N / 2]; scales [slots, H, P, N / 32]. The case holds
     the one-token update's inputs (state = checkpoint pool, a 1-D slot table
     or none, no destination table) plus
       L         buffer length
@@ -351,7 +355,10 @@ def _run_replay(case, oracle, spec):
     if lp is not None:
         lp = np.ascontiguousarray(lp, dtype=np.uint8)
         lps = np.ascontiguousarray(case["lp_scale"], dtype=np.uint8)
-        if lp.shape != state.shape or lps.shape != state.shape[:3] + (N // 32,):
+        mx4 = case.get("lp_format", "mx8") == "mx4"
+        args.lp_bits = 4 if mx4 else 8
+        want = state.shape[:3] + (N // 2,) if mx4 else state.shape
+        if lp.shape != want or lps.shape != state.shape[:3] + (N // 32,):
             raise OracleError("read copy shapes do not match the pool")
         out_lp = {"lp": lp.copy(), "lp_scale": lps.copy()}
         args.lp_in, args.lps_in = _ptr(lp), _ptr(lps)
@@ -543,3 +550,57 @@ def e4m3_decode(b, oracle=None):
     lib = (oracle or default()).lib
     _mx8_fns(lib)
     return float(lib.oracle_e4m3_decode(int(b)))
+
+
+# ---------------------------------------------------------------- MXFP4 copies
+
+def _mx4_fns(lib):
+    if not hasattr(lib, "_mx4_ready"):
+        lib.oracle_mx4_quantize.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                            ctypes.c_void_p]
+        lib.oracle_mx4_quantize.restype = None
+        lib.oracle_mx4_dequantize.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                              ctypes.c_void_p]
+        lib.oracle_mx4_dequantize.restype = None
+        lib.oracle_e2m1_encode.argtypes = [ctypes.c_float]
+        lib.oracle_e2m1_encode.restype = ctypes.c_uint8
+        lib.oracle_e2m1_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_e2m1_decode.restype = ctypes.c_float
+        lib._mx4_ready = True
+
+
+def mx4_quantize(x, oracle=None):
+    """MXFP4 (E2M1, blocks of 32 along the last axis, two codes a byte, the
+    even element in the low nibble) of a float32 array: returns (codes uint8
+    [..., last / 2], scales uint8 [..., last / 32])."""
+    lib = (oracle or default()).lib
+    _mx4_fns(lib)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if x.shape[-1] % 32:
+        raise OracleError("the last axis must be a multiple of 32")
+    codes = np.zeros(x.shape[:-1] + (x.shape[-1] // 2,), np.uint8)
+    scales = np.zeros(x.shape[:-1] + (x.shape[-1] // 32,), np.uint8)
+    lib.oracle_mx4_quantize(x.ctypes.data, x.size // 32, codes.ctypes.data, scales.ctypes.data)
+    return codes, scales
+
+
+def mx4_dequantize(codes, scales, oracle=None):
+    lib = (oracle or default()).lib
+    _mx4_fns(lib)
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    x = np.zeros(codes.shape[:-1] + (codes.shape[-1] * 2,), np.float32)
+    lib.oracle_mx4_dequantize(codes.ctypes.data, scales.ctypes.data, codes.size // 16, x.ctypes.data)
+    return x
+
+
+def e2m1_encode(v, oracle=None):
+    lib = (oracle or default()).lib
+    _mx4_fns(lib)
+    return int(lib.oracle_e2m1_encode(float(v)))
+
+
+def e2m1_decode(nib, oracle=None):
+    lib = (oracle or default()).lib
+    _mx4_fns(lib)
+    return float(lib.oracle_e2m1_decode(int(nib)))

@@ -1105,6 +1105,113 @@ def pin_mx8_blocks(orc):
     assert np.array_equal(ssu_oracle.mx8_dequantize(c2, s2, orc), deq.astype(np.float32))
 
 
+# ---------------------------------------------------- MXFP4 read copy (R33, R34)
+
+# FP4 E2M1 magnitudes as the OCP Microscaling v1.0 specification tabulates
+# them (codes 0..7; codes 8..15 are their negatives)
+E2M1_TABLE = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def pin_e2m1_codec(orc):
+    """FP4 E2M1 (R34): the 16 codes decode to the OCP table (and each value is
+    exact in PyTorch's float8_e4m3fn, a library check of the literals); every
+    code round-trips; encoding any value below 6 gives the table's nearest
+    value, ties to the even code (brute force over the table); values of 6
+    and above saturate to 6."""
+    import torch
+    from oracle import ssu_oracle
+    want = list(E2M1_TABLE) + [-v for v in E2M1_TABLE]
+    got = [ssu_oracle.e2m1_decode(c, orc) for c in range(16)]
+    assert got == want and all(math.copysign(1, g) == (-1 if c >= 8 else 1) for c, g in enumerate(got))
+    t = torch.tensor(want, dtype=torch.float32)
+    assert torch.equal(t.to(torch.float8_e4m3fn).float(), t)
+    for c in range(16):
+        assert ssu_oracle.e2m1_encode(got[c], orc) == c, c
+    rng = np.random.default_rng(5)
+    mags = np.asarray(E2M1_TABLE)
+    mids = (mags[:-1] + mags[1:]) / 2
+    probes = np.concatenate([mids, np.nextafter(mids, 0), np.nextafter(mids, 10),
+                             rng.uniform(0, 6, 3000)]).astype(np.float32)
+    for v in probes:
+        d = np.abs(mags - float(v))
+        best = np.flatnonzero(d == d.min())
+        code = int(best[0]) if len(best) == 1 else int(best[best % 2 == 0][0])  # ties: the even code
+        assert ssu_oracle.e2m1_encode(float(v), orc) == code, v
+        assert ssu_oracle.e2m1_encode(-float(v), orc) == code | 8, v
+    for v in (6.0, 6.5, 7.0, 1e30):
+        assert ssu_oracle.e2m1_encode(v, orc) == 7 and ssu_oracle.e2m1_encode(-v, orc) == 15, v
+
+
+def pin_mx4_blocks(orc):
+    """MXFP4 blocks (R33, R34) against the OCP MX definition with the scale
+    decoded by PyTorch's float8_e8m0fnu: max |x| / X lies in
+    [2^emax, 2^(emax+1)), emax = 2 being the exponent of E2M1's largest
+    value (6); every block's largest code sits in E2M1's top binade [4, 6];
+    unclipped elements decode within half a step (|x| / 4, X / 4 below 1 X),
+    clipped ones to 6 X; element 2i is the low nibble of byte i; a decoded
+    block is a fixed point; a block of zeros has zero codes."""
+    import torch
+    from oracle import ssu_oracle
+    rng = np.random.default_rng(6)
+    x = (rng.standard_normal((64, 32)) * np.exp(rng.uniform(-12, 12, (64, 1)))).astype(np.float32)
+    x[3] = 0.0
+    x[7, :] = 0.0
+    x[7, 0] = 5.0
+    codes, scales = ssu_oracle.mx4_quantize(x, orc)
+    assert codes.shape == (64, 16) and scales.shape == (64, 1)
+    X = torch.from_numpy(scales[:, 0].copy()).view(torch.float8_e8m0fnu).double().numpy()
+    emax = math.floor(math.log2(max(E2M1_TABLE)))
+    amax = np.abs(x).max(axis=1).astype(np.float64)
+    live = amax > 0
+    ratio = amax[live] / X[live]
+    assert np.all(ratio >= 2.0 ** emax) and np.all(ratio < 2.0 ** (emax + 1)), ratio
+    nib = np.stack([codes & 15, codes >> 4], axis=-1).reshape(64, 32)  # element 2i low, 2i + 1 high
+    vals = np.where(nib >= 8, -1.0, 1.0) * np.asarray(E2M1_TABLE)[nib & 7]
+    top = np.abs(vals[live]).max(axis=1)
+    assert np.all((top >= 4.0) & (top <= 6.0)), top
+    assert not codes[3].any() and scales[3, 0] == 1
+    assert codes[7, 0] == ssu_oracle.e2m1_encode(5.0 / X[7], orc)  # the low nibble of byte 0
+    deq = ssu_oracle.mx4_dequantize(codes, scales, orc).astype(np.float64)
+    assert np.array_equal(deq, vals * X[:, None])
+    sc = np.broadcast_to(X[:, None], x.shape)
+    clipped = np.abs(x) / sc >= 6.0
+    assert np.all(np.abs(deq[clipped]) == (6.0 * sc)[clipped])
+    err = np.abs(deq - x)
+    bound = np.maximum(np.abs(x) / 4, sc / 4)
+    assert np.all(err[~clipped] <= bound[~clipped])
+    c2, s2 = ssu_oracle.mx4_quantize(deq.astype(np.float32), orc)
+    assert np.array_equal(ssu_oracle.mx4_dequantize(c2, s2, orc), deq.astype(np.float32))
+
+
+def pin_replay_read_copy_mx4(orc):
+    """ReplaySSM with an MXFP4 read copy (R32 with R33, R34): an output-only
+    step equals the plain replay step run on the copy's decoded values; a
+    fold ignores the copy, matches the plain step bit for bit and rewrites
+    exactly the folded slot's copy."""
+    from oracle import ssu_oracle
+    c = _replay_case(6, [0, 5, 3, 5], sd="f32", io="bf16", dstate=64)  # sequences 1 and 3 fold
+    c["lp"], c["lp_scale"] = ssu_oracle.mx4_quantize(np.asarray(c["state"], np.float32) * np.float32(1.7), orc)
+    c["lp_format"] = "mx4"
+    r = ssu_oracle.run_replay(c, orc)
+    plain_c = {k: v for k, v in c.items() if not k.startswith("lp")}
+    deq = ssu_oracle.mx4_dequantize(c["lp"], c["lp_scale"], orc)
+    plain_deq = ssu_oracle.run_replay(dict(plain_c, state=deq), orc)
+    plain = ssu_oracle.run_replay(plain_c, orc)
+    tab = c["state_batch_indices"]
+    for b in (0, 2):
+        assert np.array_equal(r["y"][b], plain_deq["y"][b]), b
+    for b in (1, 3):
+        assert np.array_equal(r["y"][b], plain["y"][b]), b
+    assert np.array_equal(r["state"], plain["state"])
+    for b in range(4):
+        s = tab[b]
+        if b in (1, 3):
+            qc, qs = ssu_oracle.mx4_quantize(plain["state"][s], orc)
+            assert np.array_equal(r["lp"][s], qc) and np.array_equal(r["lp_scale"][s], qs), b
+        else:
+            assert np.array_equal(r["lp"][s], c["lp"][s]), b
+
+
 def pin_threads_byte_identical(orc):
     """Sequences are independent (the oracle refuses shared slots), so the
     oracle threaded over sequences gives the serial result byte for byte:
@@ -1188,4 +1295,5 @@ ALL = [pin_golden_mate_examples, pin_f16_decode_exhaustive, pin_f16_encode, pin_
        pin_memmove_matches_snapshot, pin_conv_shift_matches_snapshot,
        pin_ssd_matches_chunked_float64, pin_ssd_equals_decode_chain, pin_ssd_chunking_invariance,
        pin_ssd_seq_idx_authority, pin_ssd_dt_limit_zero, pin_e4m3_codec, pin_mx8_blocks,
-       pin_replay_read_copy, pin_threads_byte_identical]
+       pin_replay_read_copy, pin_e2m1_codec, pin_mx4_blocks, pin_replay_read_copy_mx4,
+       pin_threads_byte_identical]

@@ -97,6 +97,15 @@ MUTANTS = [
     ("e4m3_decode_bias", "ldexpf(1.0f + (float)m / 8.0f, e - 7)", "ldexpf(1.0f + (float)m / 8.0f, e - 8)"),
     ("mx8_scale_off_by_one", "k = (ex - 1) - 8; /* R30 */", "k = (ex - 1) - 7;"),
     ("mx8_scale_off_by_one_up", "k = (ex - 1) - 8; /* R30 */", "k = (ex - 1) - 9;"),
+    ("mx4_scale_off_by_one", "k = (ex - 1) - 2; /* R34 */", "k = (ex - 1) - 1;"),
+    ("mx4_scale_off_by_one_up", "k = (ex - 1) - 2; /* R34 */", "k = (ex - 1) - 3;"),
+    ("e2m1_ties_away", "code = (int)nearbyintf(a * 2.0f);", "code = (int)floorf(a * 2.0f + 0.5f);"),
+    ("e2m1_no_saturation", "return sign | 7; /* R34: saturate */", "return sign | 6;"),
+    ("mx4_nibbles_swapped", "(oracle_e2m1_encode(ldexpf(x[2 * i + 1], -k)) << 4)); /* R33 */",
+     "(oracle_e2m1_encode(ldexpf(x[2 * i + 1], -k)) >> 0)) ^ 0; /* R33 */"),
+    ("e2m1_decode_bias", "ldexpf(1.0f + 0.5f * (float)m, e - 1)", "ldexpf(1.0f + 0.5f * (float)m, e)"),
+    ("mx4_read_as_mx8", "                       : ra->lp_bits == 4 ? oracle_mx4_value(",
+     "                       : ra->lp_bits == 5 ? oracle_mx4_value("),
     ("lp_read_at_fold", "const int from_copy = ra->lp_in && h + 1 != L && !pad;",
      "const int from_copy = ra->lp_in && !pad;"),
     ("lp_not_rewritten", "if (ra->lp_out) /* R32: the fold rewrites the read copy */", "if (0)"),
