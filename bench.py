@@ -23,7 +23,7 @@ roofline.achieved uses the median.
              by an in-place read-modify-write stream (libssu_ceiling.so):
              what this part sustains for a plain stream of that size
 Options: --config {decode, decode_pad, mtp, varlen, varlen_disable, varlen_nodst, replay,
-replay_spec, replay_lp, spec_snapshots, tiny, conv_shift_sd, conv_shift_ds, memcpy_left, ssd,
+replay_spec, replay_lp, replay_mx4, spec_snapshots, tiny, conv_shift_sd, conv_shift_ds, memcpy_left, ssd,
 ceiling}, --no-cpu-baseline, --calib-copy (also runs a plain device copy of the
 state's size, the calibration kernel for the counters). --config ceiling
 measures the streaming ceilings alone (1 GiB buffers, every pattern).
@@ -56,8 +56,13 @@ KERNEL_SOURCES = {
 }
 
 
+REPLAY_CONFIGS = ("replay", "replay_spec", "replay_lp", "replay_mx4")
+# the read copy's format of a replay workload
+COPY_FORMAT = {"replay_lp": "mx8", "replay_mx4": "mx4"}
+
+
 def source_family(config):
-    if config in ("replay", "replay_spec", "replay_lp"):
+    if config in REPLAY_CONFIGS:
         return "replay"
     if config in ("conv_shift_sd", "conv_shift_ds", "memcpy_left"):
         return "copy"
@@ -90,6 +95,11 @@ def workload(name):
         return W.replay(), ("replay_lp: the replay workload with an MXFP8 read copy of the fp32 "
                             "checkpoint (E4M3 codes, one E8M0 scale per 32 values): output-only "
                             "steps read the copy, folds store the checkpoint and rewrite the copy")
+    if name == "replay_mx4":
+        return W.replay(), ("replay_mx4: the replay workload with an MXFP4 read copy of the fp32 "
+                            "checkpoint (E2M1 codes two a byte, one E8M0 scale per 32 values): "
+                            "output-only steps read the copy, folds store the checkpoint and "
+                            "rewrite the copy")
     if name == "replay_spec":
         return W.replay_spec(), ("replay_spec: ReplaySSM speculative step, batch 512 x T = 4 draft "
                                  "tokens, heads 128, dim 64, dstate 128, groups 8, fp32 "
@@ -186,16 +196,16 @@ def algorithmic_bytes(case):
     return int(total), int(R * H)
 
 
-def replay_algorithmic_bytes(case, lp=False):
+def replay_algorithmic_bytes(case, lp=None):
     """Minimal bytes of one ReplaySSM step: each live sequence reads its
     checkpoint tile and its h committed entries; a folding sequence writes its
     checkpoint; the step's tokens are appended (one entry per token, or none
     for a one-token fold); plus the step's inputs and y, and per-head vectors
     and tables, as for the plain update. One-token steps fold at h + 1 = L,
-    speculative steps (x [batch, T, ...]) at h + 2T > L. With the MXFP8 read
-    copy (lp) an output-only step reads the copy (1 + 1/32 bytes a value) in
-    place of the tile, and a fold also writes the copy. Returns (bytes,
-    token-head updates)."""
+    speculative steps (x [batch, T, ...]) at h + 2T > L. With a read copy
+    (lp "mx8": 1 + 1/32 bytes a value; "mx4": 1/2 + 1/32) an output-only step
+    reads the copy in place of the tile, and a fold also writes the copy.
+    Returns (bytes, token-head updates)."""
     slots, H, P, N = np.shape(case["state"])
     sb = DTYPE_BYTES[case["state_dtype"]]
     io = DTYPE_BYTES[case["io_dtype"]]
@@ -208,7 +218,7 @@ def replay_algorithmic_bytes(case, lp=False):
     per_head = np.ndim(case["buf_dt"]) == 3
     entry = H * P * io + (H if per_head else H * P) * dtb + G * N * io
     tile = H * P * N * sb
-    copy = H * P * N + H * P * N // 32
+    copy = H * P * N // (2 if lp == "mx4" else 1) + H * P * N // 32
     pad = int(case.get("pad_slot_id", -1))
     tab = case.get("state_batch_indices")
     total = 0
@@ -724,7 +734,7 @@ def traffic_from_counters(config):
     return entry.get("hbm_bytes_per_dispatch")
 
 
-def cpu_baseline(case, alg_bytes, updates, reps, lp=False):
+def cpu_baseline(case, alg_bytes, updates, reps, lp=None):
     """The oracle on the whole workload: median of `reps` calls on one
     thread, then on oracle_threads() threads over sequences; the two results
     must be byte-identical."""
@@ -733,9 +743,9 @@ def cpu_baseline(case, alg_bytes, updates, reps, lp=False):
     if "buf_len" in case:
         run = ssu_oracle.run_replay_spec if np.ndim(case["x"]) == 4 else ssu_oracle.run_replay
         if lp:
-            case = dict(case)
-            case["lp"], case["lp_scale"] = ssu_oracle.mx8_quantize(
-                np.asarray(case["state"], np.float32))
+            case = dict(case, lp_format=lp)
+            quantize = ssu_oracle.mx4_quantize if lp == "mx4" else ssu_oracle.mx8_quantize
+            case["lp"], case["lp_scale"] = quantize(np.asarray(case["state"], np.float32))
     else:
         run = ssu_oracle.run
     threads = oracle_threads()
@@ -804,8 +814,8 @@ def main():
         raise SystemExit("bench.py needs a GPU")
     dev = torch.device("cuda", 0)
     case, desc = workload(args.config)
-    is_replay = args.config in ("replay", "replay_spec", "replay_lp")
-    lp = args.config == "replay_lp"
+    is_replay = args.config in REPLAY_CONFIGS
+    lp = COPY_FORMAT.get(args.config)
     alg_bytes, updates = replay_algorithmic_bytes(case, lp) if is_replay else \
         algorithmic_bytes(case)
     print("[bench] %s: %.3f GB per step" % (args.config, alg_bytes / 1e9), file=sys.stderr,
@@ -823,13 +833,14 @@ def main():
         if lp:
             # the read copy is resident state like the checkpoint: made once,
             # on the GPU, before the timed steps
-            d["lp"], d["lp_scale"] = ssu.mx8_quantize(d["state"])
+            quantize = ssu.mx4_quantize if lp == "mx4" else ssu.mx8_quantize
+            d["lp"], d["lp_scale"] = quantize(d["state"])
             args_c = ssu.make_replay_lp_args(
                 d["state"], d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["buf_x"],
                 d["buf_dt"], d["buf_B"], d["buf_len"], d["lp"], d["lp_scale"], d["z"],
                 d["dt_bias"], case.get("dt_softplus", False), d["state_batch_indices"],
                 case.get("pad_slot_id", -1), out, case.get("disable_state_update", False))
-            launch = ssu.ssu_replay_lp_update
+            launch = ssu.ssu_replay_mx4_update if lp == "mx4" else ssu.ssu_replay_lp_update
     else:
         args_c = ssu.make_args(d["state"], d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"],
                                d["z"], d["dt_bias"], case.get("dt_softplus", False),

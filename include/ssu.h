@@ -266,7 +266,7 @@ SSU_API ssu_status_t ssu_mx8_quantize(const ssu_tensor_t *src, const ssu_tensor_
  * disable_state_update writes neither checkpoint, copy nor buffer.
  * base: as for ssu_replay_update, with an f32 state pool whose [heads, dim,
  * dstate] part is contiguous, and dstate a multiple of 32.
- *   lp        [slots, heads, dim, dstate] u8, contiguous, 4-byte aligned (device)
+ *   lp        [slots, heads, dim, dstate] u8, contiguous, 16-byte aligned (device)
  *   lp_scale  [slots, heads, dim, dstate / 32] u8, contiguous, 8-byte aligned (device)
  * The caller keeps the copy in step with the checkpoint (ssu_mx8_quantize
  * of the pool makes a first copy). Same error, stream and allocation
@@ -277,6 +277,34 @@ typedef struct {
 } ssu_replay_lp_args_t;
 
 SSU_API ssu_status_t ssu_replay_lp_update(const ssu_replay_lp_args_t *args, void *stream);
+
+/* The same read copy in MXFP4 (OCP Microscaling v1.0, FP4 with E2M1
+ * elements), a quarter of the fp32 checkpoint's bytes plus the scales:
+ * blocks of 32 consecutive dstate values with one E8M0 scale byte
+ * X = 2^(e - 127), e - 127 = floor(log2 max|v|) - 2 clamped to [-126, 127]
+ * (-126 for an all-zero block); each element is v / X rounded to nearest
+ * even among the E2M1 values 0, 0.5, 1, 1.5, 2, 3, 4, 6 (sign in bit 3),
+ * saturating to +-6. Two elements a byte, the even-indexed one in the low
+ * nibble. A value decodes as code * X. */
+
+/* Quantize fp32 values to MXFP4:
+ *   src     [n] f32 (device), n a multiple of 32, 16-byte aligned; blocks
+ *           are consecutive runs of 32 values
+ *   codes   [n / 2] u8 (device), 4-byte aligned: E2M1 code pairs
+ *   scales  [n / 32] u8 (device): E8M0 scale bytes
+ * A NaN element becomes code 0 and does not count toward the block's
+ * largest magnitude; a block holding an infinity has no defined scale and
+ * its bytes are unspecified (a checkpoint is finite). Otherwise as
+ * ssu_mx8_quantize. */
+SSU_API ssu_status_t ssu_mx4_quantize(const ssu_tensor_t *src, const ssu_tensor_t *codes,
+                                      const ssu_tensor_t *scales, void *stream);
+
+/* ssu_replay_lp_update with the MXFP4 copy:
+ *   lp        [slots, heads, dim, dstate / 2] u8, contiguous, 16-byte aligned (device)
+ *   lp_scale  [slots, heads, dim, dstate / 32] u8, contiguous, 8-byte aligned (device)
+ * Everything else as ssu_replay_lp_update (ssu_mx4_quantize of the pool
+ * makes a first copy). */
+SSU_API ssu_status_t ssu_replay_mx4_update(const ssu_replay_lp_args_t *args, void *stream);
 
 /* ---- memmove-safe Mamba state copies (vLLM PR #50729 digest, prhub:
  * sections "实现拆解" and "关键源码片段"). Speculative decoding shifts a

@@ -6,6 +6,8 @@ libssu.so); this package is its Python binding.
 from .ssu import (LIBRARY_PATH, SsuArgs, SsuConvShiftArgs, SsuError, SsuReplayArgs, SsuReplayLpArgs,
                   SsuSsdArgs, mx8_quantize, replay_lp_selective_state_update,
                   ssu_mx8_quantize, ssu_replay_lp_update, make_replay_lp_args,
+                  mx4_quantize, replay_mx4_selective_state_update, ssu_mx4_quantize,
+                  ssu_replay_mx4_update,
                   batch_memcpy, ssd_combined_fwd_varlen, ssu_ssd_prefill, ssu_ssd_workspace_bytes,
                   ssu_ssd_prefill_noalloc, make_ssd_args, SSD_SCRATCH_BYTES, ssu_ssd_plan,
                   prewarm_ssd_combined_fwd_varlen, SsuSsdPlanDesc,
@@ -25,4 +27,5 @@ __all__ = ["selective_state_update", "prewarm_selective_state_update",
            "ssu_ssd_prefill_noalloc", "make_ssd_args", "SSD_SCRATCH_BYTES", "ssu_ssd_plan",
            "prewarm_ssd_combined_fwd_varlen", "SsuSsdPlanDesc",
            "replay_lp_selective_state_update", "ssu_replay_lp_update", "make_replay_lp_args",
-           "SsuReplayLpArgs", "mx8_quantize", "ssu_mx8_quantize"]
+           "SsuReplayLpArgs", "mx8_quantize", "ssu_mx8_quantize", "mx4_quantize",
+           "replay_mx4_selective_state_update", "ssu_mx4_quantize", "ssu_replay_mx4_update"]

@@ -936,9 +936,12 @@ ssu_status_t ssu_update(const ssu_args_t *a, void *stream) {
 
 // Both ReplaySSM entry points: validate, then launch the one-token or the
 // speculative kernel.
+// lp_bits: the read copy's format for the LP entry points (8 MXFP8, 4 MXFP4).
 static ssu_status_t replay_common(const ssu_replay_args_t *ra, bool spec, void *stream,
-                                  const ssu_replay_lp_args_t *lpa = nullptr) {
-    const char *fn = lpa ? "ssu_replay_lp_update" : spec ? "ssu_replay_spec_update" : "ssu_replay_update";
+                                  const ssu_replay_lp_args_t *lpa = nullptr, int lp_bits = 8) {
+    const char *fn = lpa ? (lp_bits == 4 ? "ssu_replay_mx4_update" : "ssu_replay_lp_update")
+                     : spec ? "ssu_replay_spec_update"
+                            : "ssu_replay_update";
     if (!ra)
         return fail(SSU_ERR_VALUE, "%s: args is NULL", fn);
     const ssu_args_t *a = &ra->base;
@@ -1016,17 +1019,19 @@ static ssu_status_t replay_common(const ssu_replay_args_t *ra, bool spec, void *
         SSU_OK)
         return s;
     if (lpa) {
-        // the copy mirrors the pool's [slots, heads, dim, dstate], one byte a value
+        // the copy mirrors the pool's [slots, heads, dim, dstate], one byte a
+        // value (MXFP8) or two values a byte (MXFP4)
+        const char *fmt = lp_bits == 4 ? "MXFP4" : "MXFP8";
         if (pr.state_dtype != SSU_F32)
-            return fail(SSU_ERR_NOT_IMPLEMENTED, "the MXFP8 read copy needs an f32 checkpoint");
+            return fail(SSU_ERR_NOT_IMPLEMENTED, "the %s read copy needs an f32 checkpoint", fmt);
         if (pr.N % 32 != 0)
-            return fail(SSU_ERR_VALUE, "the MXFP8 read copy needs dstate a multiple of 32");
+            return fail(SSU_ERR_VALUE, "the %s read copy needs dstate a multiple of 32", fmt);
         const ssu_tensor_t &lp = lpa->lp, &lps = lpa->lp_scale;
         if (!present(lp) || !present(lps))
             return fail(SSU_ERR_VALUE, "lp and lp_scale are required");
         if (lp.dtype != SSU_U8 || lps.dtype != SSU_U8)
             return fail(SSU_ERR_VALUE, "lp and lp_scale must be u8");
-        const int64_t want_lp[4] = {pr.slots, pr.H, pr.P, pr.N};
+        const int64_t want_lp[4] = {pr.slots, pr.H, pr.P, lp_bits == 4 ? pr.N / 2 : pr.N};
         const int64_t want_sc[4] = {pr.slots, pr.H, pr.P, pr.N / 32};
         const ssu_tensor_t *ts[2] = {&lp, &lps};
         const int64_t *wants[2] = {want_lp, want_sc};
@@ -1037,15 +1042,16 @@ static ssu_status_t replay_common(const ssu_replay_args_t *ra, bool spec, void *
             int64_t want = 1;
             for (int j = 3; j >= 0; j--) {
                 if (t->size[j] != wants[i][j])
-                    return fail(SSU_ERR_VALUE, i ? "lp_scale must be [slots, heads, dim, dstate / 32]"
-                                                 : "lp must be [slots, heads, dim, dstate]");
+                    return fail(SSU_ERR_VALUE, i                ? "lp_scale must be [slots, heads, dim, dstate / 32]"
+                                               : lp_bits == 4 ? "lp must be [slots, heads, dim, dstate / 2]"
+                                                              : "lp must be [slots, heads, dim, dstate]");
                 if (t->stride[j] != want && t->size[j] != 1)
                     return fail(SSU_ERR_VALUE, "lp and lp_scale must be contiguous");
                 want *= t->size[j];
             }
         }
-        if (!aligned(lp.data, 4) || !aligned(lps.data, 8))
-            return fail(SSU_ERR_VALUE, "lp must be 4-byte and lp_scale 8-byte aligned");
+        if (!aligned(lp.data, 16) || !aligned(lps.data, 8))
+            return fail(SSU_ERR_VALUE, "lp must be 16-byte and lp_scale 8-byte aligned");
         rp.lp = static_cast<uint8_t *>(const_cast<void *>(lp.data));
         rp.lp_scale = static_cast<uint8_t *>(const_cast<void *>(lps.data));
     }
@@ -1065,21 +1071,34 @@ static ssu_status_t replay_common(const ssu_replay_args_t *ra, bool spec, void *
     rp.G = static_cast<int32_t>(pr.G);
 
     ssu::KernelRef k;
-    if (lpa ? !ssu::find_replay_lp_kernel(pr.io, static_cast<int>(pr.N), &k)
+    if (lpa ? !ssu::find_replay_lp_kernel(pr.io, static_cast<int>(pr.N), lp_bits, &k)
             : !ssu::find_replay_kernel(pr.state_dtype, pr.io, static_cast<int>(pr.N), spec, &k))
         return fail(SSU_ERR_NOT_IMPLEMENTED, "no replay kernel for state %s / io %s / dstate %lld",
                     dtype_str(pr.state_dtype), dtype_str(pr.io), (long long)pr.N);
-    const Geometry geo = geometry(pr.P, pr.N, pr.state_dtype, ssu::kTileReplay);
     ssu::Params p = pr.p;
-    p.dim_tiles = geo.dim_tiles;
-    p.rows_per_block = geo.rows_per_block;
-    const int64_t grid = pr.nseq * pr.H * geo.dim_tiles;
+    int64_t grid, block;
+    if (spec) {
+        const Geometry geo = geometry(pr.P, pr.N, pr.state_dtype, ssu::kTileReplay);
+        p.dim_tiles = geo.dim_tiles;
+        p.rows_per_block = geo.rows_per_block;
+        grid = pr.nseq * pr.H * geo.dim_tiles;
+        block = geo.block;
+    } else {
+        // one wave per kReplayRows dim rows of a (sequence, head)
+        p.dim_tiles = static_cast<int32_t>((pr.P + ssu::kReplayRows - 1) / ssu::kReplayRows);
+        p.rows_per_block = ssu::kReplayRows;
+        const int64_t waves = pr.nseq * pr.H * p.dim_tiles;
+        if (waves > INT32_MAX)
+            return fail(SSU_ERR_NOT_IMPLEMENTED, "grid too large");
+        grid = (waves + ssu::kReplayWaves - 1) / ssu::kReplayWaves;
+        block = ssu::kReplayWaves * ssu::kWaveLanes;
+    }
     if (grid > INT32_MAX)
         return fail(SSU_ERR_NOT_IMPLEMENTED, "grid too large");
     if (spec && pr.nseq * T > INT32_MAX)
         return fail(SSU_ERR_NOT_IMPLEMENTED, "batch * T too large");
-    int e = ssu::launch_replay(k, p, rp, static_cast<unsigned>(grid),
-                               static_cast<unsigned>(geo.block), stream);
+    int e = ssu::launch_replay(k, p, rp, static_cast<unsigned>(grid), static_cast<unsigned>(block),
+                               stream);
     // the speculative step's shared appends run after the step (same stream)
     if (e == 0 && spec)
         e = ssu::launch_replay_spec_append(p, rp, static_cast<int>(elem_bytes(pr.io)),
@@ -1102,7 +1121,13 @@ ssu_status_t ssu_replay_spec_update(const ssu_replay_args_t *ra, void *stream) {
 ssu_status_t ssu_replay_lp_update(const ssu_replay_lp_args_t *la, void *stream) {
     if (!la)
         return fail(SSU_ERR_VALUE, "ssu_replay_lp_update: args is NULL");
-    return replay_common(&la->base, false, stream, la);
+    return replay_common(&la->base, false, stream, la, 8);
+}
+
+ssu_status_t ssu_replay_mx4_update(const ssu_replay_lp_args_t *la, void *stream) {
+    if (!la)
+        return fail(SSU_ERR_VALUE, "ssu_replay_mx4_update: args is NULL");
+    return replay_common(&la->base, false, stream, la, 4);
 }
 
 // a contiguous tensor of `dtype` read as flat; returns its element count or -1
@@ -1118,32 +1143,46 @@ static int64_t flat_count(const ssu_tensor_t &t, int dtype) {
     return want;
 }
 
-ssu_status_t ssu_mx8_quantize(const ssu_tensor_t *src, const ssu_tensor_t *codes,
-                              const ssu_tensor_t *scales, void *stream) {
+// MXFP8 (bits 8) or MXFP4 (bits 4) quantization of a flat fp32 tensor.
+static ssu_status_t mx_quantize(const char *fn, int bits, const ssu_tensor_t *src,
+                                const ssu_tensor_t *codes, const ssu_tensor_t *scales, void *stream) {
     if (!src || !codes || !scales)
-        return fail(SSU_ERR_VALUE, "ssu_mx8_quantize: a tensor is NULL");
+        return fail(SSU_ERR_VALUE, "%s: a tensor is NULL", fn);
     const int64_t n = flat_count(*src, SSU_F32);
     if (n < 0)
         return fail(SSU_ERR_VALUE, "src must be a contiguous f32 tensor");
     if (n % 32 != 0)
         return fail(SSU_ERR_VALUE, "src holds %lld values, not a multiple of 32", (long long)n);
-    if (flat_count(*codes, SSU_U8) != n)
-        return fail(SSU_ERR_VALUE, "codes must be a contiguous u8 tensor of %lld values", (long long)n);
+    const int64_t ncodes = bits == 4 ? n / 2 : n;
+    if (flat_count(*codes, SSU_U8) != ncodes)
+        return fail(SSU_ERR_VALUE, "codes must be a contiguous u8 tensor of %lld bytes", (long long)ncodes);
     if (flat_count(*scales, SSU_U8) != n / 32)
         return fail(SSU_ERR_VALUE, "scales must be a contiguous u8 tensor of %lld values",
                     (long long)(n / 32));
     if (n == 0)
         return g_error.clear(), SSU_OK;
-    if (!aligned(src->data, 16) || !aligned(codes->data, 8))
-        return fail(SSU_ERR_VALUE, "src must be 16-byte and codes 8-byte aligned");
-    const int e = ssu::launch_mx8_quantize(static_cast<const float *>(src->data),
-                                           static_cast<uint8_t *>(const_cast<void *>(codes->data)),
-                                           static_cast<uint8_t *>(const_cast<void *>(scales->data)),
-                                           n / 32, stream);
+    if (!aligned(src->data, 16) || !aligned(codes->data, bits == 4 ? 4 : 8))
+        return fail(SSU_ERR_VALUE, bits == 4 ? "src must be 16-byte and codes 4-byte aligned"
+                                             : "src must be 16-byte and codes 8-byte aligned");
+    const float *sp = static_cast<const float *>(src->data);
+    uint8_t *cp = static_cast<uint8_t *>(const_cast<void *>(codes->data));
+    uint8_t *scp = static_cast<uint8_t *>(const_cast<void *>(scales->data));
+    const int e = bits == 4 ? ssu::launch_mx4_quantize(sp, cp, scp, n / 32, stream)
+                            : ssu::launch_mx8_quantize(sp, cp, scp, n / 32, stream);
     if (e != 0)
         return fail(SSU_ERR_HIP, "kernel launch failed: %s", ssu::hip_error_string(e));
     g_error.clear();
     return SSU_OK;
+}
+
+ssu_status_t ssu_mx8_quantize(const ssu_tensor_t *src, const ssu_tensor_t *codes,
+                              const ssu_tensor_t *scales, void *stream) {
+    return mx_quantize("ssu_mx8_quantize", 8, src, codes, scales, stream);
+}
+
+ssu_status_t ssu_mx4_quantize(const ssu_tensor_t *src, const ssu_tensor_t *codes,
+                              const ssu_tensor_t *scales, void *stream) {
+    return mx_quantize("ssu_mx4_quantize", 4, src, codes, scales, stream);
 }
 
 }  // extern "C"

@@ -1,7 +1,8 @@
 // Device helpers shared by the gfx950 kernels of libssu (ssu_kernels.hip and
 // ssu_replay.hip): element conversions, 16-byte state accesses, DPP row
 // reductions and broadcasts, the per-row transcendentals, the XCD-aware
-// workgroup order, slot-table reads, raw input words and the MXFP8 codec.
+// workgroup order, slot-table reads, raw input words and the MXFP8 and
+// MXFP4 codecs.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -311,6 +312,46 @@ __device__ __forceinline__ int mx8_exponent(float amax) {
     if (ex == 0)
         return -126;  // zero or subnormal
     const int k = ex - 127 - 8;
+    return k < -126 ? -126 : (k > 127 ? 127 : k);
+}
+
+// MXFP4 (OCP Microscaling, FP4 E2M1 elements two a byte -- the even
+// element in the low nibble -- and an E8M0 scale per 32 values) for the
+// checkpoint's 4-bit read copy. A block's scale is 2^k with k =
+// floor(log2 max|x|) - 2 clamped to [-126, 127] (-126 for a block of zeros);
+// elements x 2^-k round to nearest even in E2M1 and saturate at 6.
+
+// The two E2M1 elements of byte BYTE of `codes`, times the scale (the
+// conversion unit decodes the low nibble first and applies the power-of-two
+// scale exactly).
+template <int BYTE>
+__device__ __forceinline__ float2 e2m1_pair(uint32_t codes, float scale) {
+    const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, scale, BYTE);
+    return float2{v[0], v[1]};
+}
+
+// E2M1 codes of v[0..3] / 2^k in the low 16 bits: byte 0 holds v[0] (low
+// nibble) and v[1], byte 1 v[2] and v[3]. The conversion unit divides by the
+// power-of-two scale, rounds to nearest even and saturates at 6 (checked on
+// the device at scale exponents from -126 to 127 against a plain E2M1
+// rounding); it gives a NaN input the code of 6, which is set to 0 here.
+__device__ __forceinline__ uint32_t e2m1_codes4(const float v[4], int k) {
+    const float X = __uint_as_float(static_cast<uint32_t>(k + 127) << 23);
+    uint32_t r = 0;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[0], v[1], X, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[2], v[3], X, 1);
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        r = v[i] != v[i] ? r & ~(0xFu << (4 * i)) : r;
+    return r & 0xFFFFu;
+}
+
+// scale exponent of an MXFP4 block from its largest magnitude
+__device__ __forceinline__ int mx4_exponent(float amax) {
+    const int ex = static_cast<int>((__float_as_uint(amax) >> 23) & 0xFFu);
+    if (ex == 0)
+        return -126;  // zero or subnormal
+    const int k = ex - 127 - 2;
     return k < -126 ? -126 : (k > 127 ? 127 : k);
 }
 

@@ -45,22 +45,29 @@ constexpr int kMaxWaves = SSU_MAX_WAVES;
 #ifndef SSU_WAVES_PER_EU
 #define SSU_WAVES_PER_EU 1
 #endif
-// The replay kernel: fp32 state with dstate <= 128 fits 4 waves per SIMD
-// without spills; the other tiles need more registers for the fold path.
-// Its output-only path requests the inputs of the first SSU_REPLAY_PREFETCH
-// steps of every run before the checkpoint tile.
+// The one-token replay kernel: workgroups of kReplayWaves independent waves,
+// each on kReplayRows dim rows of one (sequence, head), and the waves per
+// SIMD its register allocation must allow.
+constexpr int kReplayRows = 64;
+constexpr int kReplayWaves = 4;
 #ifndef SSU_WAVES_PER_EU_REPLAY
 #define SSU_WAVES_PER_EU_REPLAY 4
 #endif
-#ifndef SSU_WAVES_PER_EU_REPLAY_WIDE
-#define SSU_WAVES_PER_EU_REPLAY_WIDE 3
+constexpr int replay_waves_per_eu() { return SSU_WAVES_PER_EU_REPLAY; }
+// Slices in flight per wave: of the fold, of the output-only read's MXFP8
+// and MXFP4 copies, and 32-bit words of its checkpoint slices.
+#ifndef SSU_REPLAY_COPY8_DEPTH
+#define SSU_REPLAY_COPY8_DEPTH 4
 #endif
-#ifndef SSU_REPLAY_PREFETCH
-#define SSU_REPLAY_PREFETCH 4
+#ifndef SSU_REPLAY_COPY4_DEPTH
+#define SSU_REPLAY_COPY4_DEPTH 4
 #endif
-constexpr int replay_waves_per_eu(int state_bytes, int dstate) {
-    return state_bytes == 4 && dstate <= 128 ? SSU_WAVES_PER_EU_REPLAY : SSU_WAVES_PER_EU_REPLAY_WIDE;
-}
+#ifndef SSU_REPLAY_FOLD_DEPTH
+#define SSU_REPLAY_FOLD_DEPTH 4
+#endif
+#ifndef SSU_REPLAY_CKPT_WORDS
+#define SSU_REPLAY_CKPT_WORDS 32
+#endif
 // The speculative replay kernel also holds a group of drafts' C and their
 // per-draft accumulators.
 constexpr int replay_spec_waves_per_eu(int state_bytes, int dstate) {
@@ -143,8 +150,9 @@ struct ReplayParams {
     int32_t len_i64;    // buf_len is i64
     int32_t dt_per_head;  // buf_dt is [slots, L, H]
     int32_t G;
-    // MXFP8 read copy of the checkpoint pool (LP kernels): E4M3 codes
-    // [slots, H, P, N] and E8M0 scales [slots, H, P, N / 32]
+    // read copy of the checkpoint pool (LP kernels): E4M3 codes
+    // [slots, H, P, N] (MXFP8) or E2M1 codes [slots, H, P, N / 2] (MXFP4),
+    // and E8M0 scales [slots, H, P, N / 32]
     uint8_t *lp;
     uint8_t *lp_scale;
 };
@@ -218,10 +226,12 @@ int ssd_kernel_attributes(int io_dtype, int state_dtype, int dstate, const char 
 int launch_conv_shift(const ConvParams &cv, bool dim_major, unsigned grid, void *stream);
 
 bool find_replay_kernel(int state_dtype, int io_dtype, int dstate, bool spec, KernelRef *out);
-// The one-token replay kernel with an MXFP8 read copy (fp32 checkpoints).
-bool find_replay_lp_kernel(int io_dtype, int dstate, KernelRef *out);
-// MXFP8 quantization of `nblocks` blocks of 32 fp32 values.
+// The one-token replay kernel with an MXFP8 (bits 8) or MXFP4 (bits 4) read
+// copy (fp32 checkpoints).
+bool find_replay_lp_kernel(int io_dtype, int dstate, int bits, KernelRef *out);
+// MXFP8 / MXFP4 quantization of `nblocks` blocks of 32 fp32 values.
 int launch_mx8_quantize(const float *src, uint8_t *codes, uint8_t *scales, int64_t nblocks, void *stream);
+int launch_mx4_quantize(const float *src, uint8_t *codes, uint8_t *scales, int64_t nblocks, void *stream);
 int launch_replay(const KernelRef &k, const Params &p, const ReplayParams &rp, unsigned grid,
                   unsigned block, void *stream);
 // The speculative step's second launch: the drafts' B rows and per-head dt

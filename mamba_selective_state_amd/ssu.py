@@ -91,7 +91,8 @@ class SsuPlanInfo(ctypes.Structure):
 
 
 EXPORTS = ("ssu_plan", "ssu_update", "ssu_replay_update", "ssu_replay_spec_update",
-           "ssu_replay_lp_update", "ssu_mx8_quantize", "ssu_batch_memcpy", "ssu_conv_state_shift", "ssu_ssd_workspace_bytes", "ssu_ssd_prefill",
+           "ssu_replay_lp_update", "ssu_mx8_quantize", "ssu_replay_mx4_update", "ssu_mx4_quantize",
+           "ssu_batch_memcpy", "ssu_conv_state_shift", "ssu_ssd_workspace_bytes", "ssu_ssd_prefill",
            "ssu_ssd_prefill_noalloc", "ssu_ssd_plan", "ssu_last_error", "ssu_abi_version")
 SSD_SCRATCH_BYTES = 64 << 20  # SSU_SSD_SCRATCH_BYTES
 
@@ -115,6 +116,10 @@ def load_library(path=None):
     lib.ssu_replay_lp_update.restype = ctypes.c_int
     lib.ssu_mx8_quantize.argtypes = [ctypes.POINTER(SsuTensor)] * 3 + [ctypes.c_void_p]
     lib.ssu_mx8_quantize.restype = ctypes.c_int
+    lib.ssu_replay_mx4_update.argtypes = [ctypes.POINTER(SsuReplayLpArgs), ctypes.c_void_p]
+    lib.ssu_replay_mx4_update.restype = ctypes.c_int
+    lib.ssu_mx4_quantize.argtypes = [ctypes.POINTER(SsuTensor)] * 3 + [ctypes.c_void_p]
+    lib.ssu_mx4_quantize.restype = ctypes.c_int
     lib.ssu_batch_memcpy.argtypes = [ctypes.POINTER(SsuTensor)] * 3 + [ctypes.c_int64,
                                                                        ctypes.c_void_p]
     lib.ssu_batch_memcpy.restype = ctypes.c_int
@@ -208,6 +213,27 @@ def ssu_mx8_quantize(src, codes, scales, stream=None):
                                ctypes.c_void_p(stream))
     if st != OK:
         _raise(st, "ssu_mx8_quantize")
+
+
+def ssu_replay_mx4_update(args, stream=None):
+    """Enqueue one ReplaySSM decode step with the MXFP4 read copy (include/ssu.h
+    ssu_replay_mx4_update)."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    st = _lib.ssu_replay_mx4_update(ctypes.byref(args), ctypes.c_void_p(stream))
+    if st != OK:
+        _raise(st, "ssu_replay_mx4_update")
+
+
+def ssu_mx4_quantize(src, codes, scales, stream=None):
+    """Enqueue an MXFP4 quantization (include/ssu.h ssu_mx4_quantize); the
+    arguments are SsuTensor descriptors."""
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    st = _lib.ssu_mx4_quantize(ctypes.byref(src), ctypes.byref(codes), ctypes.byref(scales),
+                               ctypes.c_void_p(stream))
+    if st != OK:
+        _raise(st, "ssu_mx4_quantize")
 
 
 def ssu_plan(desc):
@@ -378,7 +404,8 @@ def replay_spec_selective_state_update(state, x, dt, A, B, C, D, buf_x, buf_dt, 
 def make_replay_lp_args(state, x, dt, A, B, C, D, buf_x, buf_dt, buf_B, buf_len, lp, lp_scale,
                         z=None, dt_bias=None, dt_softplus=False, state_batch_indices=None,
                         pad_slot_id=-1, out=None, disable_state_update=False):
-    """SsuReplayLpArgs for ssu_replay_lp_update; `out` must be given."""
+    """SsuReplayLpArgs for ssu_replay_lp_update or ssu_replay_mx4_update;
+    `out` must be given."""
     r = SsuReplayLpArgs()
     r.base = make_replay_args(state, x, dt, A, B, C, D, buf_x, buf_dt, buf_B, buf_len, z, dt_bias,
                               dt_softplus, state_batch_indices, pad_slot_id, out,
@@ -406,6 +433,23 @@ def replay_lp_selective_state_update(state, x, dt, A, B, C, D, buf_x, buf_dt, bu
     return out
 
 
+def replay_mx4_selective_state_update(state, x, dt, A, B, C, D, buf_x, buf_dt, buf_B, buf_len, lp,
+                                      lp_scale, z=None, dt_bias=None, dt_softplus=False,
+                                      state_batch_indices=None, pad_slot_id=-1, out=None,
+                                      disable_state_update=False):
+    """replay_lp_selective_state_update with an MXFP4 copy (OCP MX v1.0
+    MXFP4, E2M1 elements): lp holds two codes a byte, the even-indexed value
+    in the low nibble ([slots, heads, dim, dstate / 2]); lp_scale as for
+    MXFP8. Returns y."""
+    if out is None:
+        out = torch.empty(x.shape, dtype=x.dtype, device=x.device)
+    args = make_replay_lp_args(state, x, dt, A, B, C, D, buf_x, buf_dt, buf_B, buf_len, lp,
+                               lp_scale, z, dt_bias, dt_softplus, state_batch_indices,
+                               pad_slot_id, out, disable_state_update)
+    ssu_replay_mx4_update(args, torch.cuda.current_stream(state.device).cuda_stream)
+    return out
+
+
 def mx8_quantize(src, codes=None, scales=None):
     """MXFP8 (E4M3 elements, an E8M0 scale per 32 consecutive values) of a
     contiguous float32 CUDA tensor whose size is a multiple of 32; the codes
@@ -418,6 +462,24 @@ def mx8_quantize(src, codes=None, scales=None):
         scales = torch.empty(shape, dtype=torch.uint8, device=src.device)
     dev = src.device
     ssu_mx8_quantize(tensor_desc(src, dev), tensor_desc(codes, dev), tensor_desc(scales, dev),
+                     torch.cuda.current_stream(dev).cuda_stream)
+    return codes, scales
+
+
+def mx4_quantize(src, codes=None, scales=None):
+    """MXFP4 (E2M1 elements two a byte, an E8M0 scale per 32 consecutive
+    values) of a contiguous float32 CUDA tensor whose size is a multiple of
+    32; the codes take src's shape with the last dimension / 2, the scales
+    with it / 32. Returns (codes, scales)."""
+    last = src.shape[-1] if src.dim() else 0
+    if codes is None:
+        shape = tuple(src.shape[:-1]) + (last // 2,) if src.dim() else (0,)
+        codes = torch.empty(shape, dtype=torch.uint8, device=src.device)
+    if scales is None:
+        shape = tuple(src.shape[:-1]) + (last // 32,) if src.dim() else (0,)
+        scales = torch.empty(shape, dtype=torch.uint8, device=src.device)
+    dev = src.device
+    ssu_mx4_quantize(tensor_desc(src, dev), tensor_desc(codes, dev), tensor_desc(scales, dev),
                      torch.cuda.current_stream(dev).cuda_stream)
     return codes, scales
 

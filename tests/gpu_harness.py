@@ -302,13 +302,20 @@ def replay_subcase(case, seqs):
     return sub, used
 
 
-# ---------------------------------------------------------------- MXFP8 read copy
+# ---------------------------------------------------------------- MX read copies
 
-def with_copy(case, source=None):
-    """The case with an MXFP8 read copy of `source` (default: its own pool),
-    made by the oracle's quantizer."""
-    c = dict(case)
-    c["lp"], c["lp_scale"] = ssu_oracle.mx8_quantize(
+def quantizers(case):
+    """The oracle's (quantize, dequantize) pair for the case's copy format."""
+    if case.get("lp_format", "mx8") == "mx4":
+        return ssu_oracle.mx4_quantize, ssu_oracle.mx4_dequantize
+    return ssu_oracle.mx8_quantize, ssu_oracle.mx8_dequantize
+
+
+def with_copy(case, source=None, fmt="mx8"):
+    """The case with an MXFP8 (fmt "mx8") or MXFP4 ("mx4") read copy of
+    `source` (default: its own pool), made by the oracle's quantizer."""
+    c = dict(case, lp_format=fmt)
+    c["lp"], c["lp_scale"] = quantizers(c)[0](
         np.asarray(case["state"] if source is None else source, np.float32))
     return c
 
@@ -327,7 +334,9 @@ def run_gpu_replay_lp(case, d=None, device="cuda:0"):
         d = device_replay_lp(case, device)
     o = torch.full(np.shape(case["x"]), float("nan"), dtype=TORCH[case["io_dtype"]],
                    device=device)
-    y = ssu.replay_lp_selective_state_update(
+    step = (ssu.replay_mx4_selective_state_update if case.get("lp_format") == "mx4"
+            else ssu.replay_lp_selective_state_update)
+    y = step(
         d["state"], d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["buf_x"], d["buf_dt"],
         d["buf_B"], d["buf_len"], d["lp"], d["lp_scale"], z=d["z"], dt_bias=d["dt_bias"],
         dt_softplus=case.get("dt_softplus", False), state_batch_indices=d["state_batch_indices"],
@@ -345,23 +354,31 @@ def compare_copy(case, got, ref, name=""):
     """The read copy: slots the oracle does not write keep their bytes; a
     written slot's copy is, byte for byte, the quantization of the state the
     GPU stored (the codes are decided on the same fp32 values), and within one
-    E4M3 step of the oracle's copy (its state differs by rounding order)."""
+    element step of the oracle's copy (its state differs by rounding order)."""
     written = ref["written"]
     for k in ("lp", "lp_scale"):
         assert np.array_equal(got[k][~written], np.asarray(case[k])[~written]), \
             "%s: %s of a slot the oracle leaves alone changed" % (name, k)
     if not written.any():
         return 0
-    codes, scales = ssu_oracle.mx8_quantize(got["state"][written])
+    quantize, dequantize = quantizers(case)
+    codes, scales = quantize(got["state"][written])
     assert np.array_equal(got["lp_scale"][written], scales), "%s: scale bytes" % name
     assert np.array_equal(got["lp"][written], codes), "%s: code bytes" % name
-    g = ssu_oracle.mx8_dequantize(got["lp"][written], got["lp_scale"][written]).astype(np.float64)
-    r = ssu_oracle.mx8_dequantize(ref["lp"][written], ref["lp_scale"][written]).astype(np.float64)
+    g = dequantize(got["lp"][written], got["lp_scale"][written]).astype(np.float64)
+    r = dequantize(ref["lp"][written], ref["lp_scale"][written]).astype(np.float64)
     # the block scale X = 2^(byte - 127) of every element
     sc = np.repeat(np.ldexp(1.0, ref["lp_scale"][written].astype(np.int64) - 127), 32, axis=-1)
-    # one E4M3 step: |v| / 8 for a normal value, 2^-9 X for a subnormal
-    assert (np.abs(g - r) <= np.abs(r) / 8 + sc * 2.0 ** -9 * 1.0001).all(), \
-        "%s: copy more than one E4M3 step from the oracle's" % name
+    if case.get("lp_format") == "mx4":
+        # one E2M1 step: at most |v| / 2 for a normal value, X / 2 below 1;
+        # a block whose largest value crossed a power of two between the two
+        # states takes the other scale: X more
+        assert (np.abs(g - r) <= np.abs(r) / 2 + sc * 1.5001).all(), \
+            "%s: copy more than one E2M1 step from the oracle's" % name
+    else:
+        # one E4M3 step: |v| / 8 for a normal value, 2^-9 X for a subnormal
+        assert (np.abs(g - r) <= np.abs(r) / 8 + sc * 2.0 ** -9 * 1.0001).all(), \
+            "%s: copy more than one E4M3 step from the oracle's" % name
     return int((got["lp"][written] != ref["lp"][written]).sum())
 
 

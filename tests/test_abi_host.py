@@ -496,10 +496,11 @@ def test_replay_lp_errors():
     r.lp = tdesc((8, 8, 16, 128), S.U8, strides=(8 * 16 * 128, 16 * 128, 1, 16))
     st, msg = replay_lp(r)
     assert st == S.ERR_VALUE and "contiguous" in msg
-    r = replay_lp_args()
-    r.lp = tdesc((8, 8, 16, 128), S.U8, ptr=FAKE + 2)
-    st, msg = replay_lp(r)
-    assert st == S.ERR_VALUE and "aligned" in msg
+    for off in (2, 8):  # the copy is read 16 bytes at a time
+        r = replay_lp_args()
+        r.lp = tdesc((8, 8, 16, 128), S.U8, ptr=FAKE + off)
+        st, msg = replay_lp(r)
+        assert st == S.ERR_VALUE and "16-byte" in msg
     # the replay checks still apply
     r = replay_lp_args()
     r.base.buf_len = S.SsuTensor()
@@ -529,6 +530,70 @@ def test_mx8_quantize_empty_and_errors():
     assert st == S.ERR_VALUE and "contiguous" in msg
     st, msg = quantize(tdesc((64,), S.F32, ptr=FAKE + 4), tdesc((64,), S.U8), tdesc((2,), S.U8))
     assert st == S.ERR_VALUE and "aligned" in msg
+
+
+# ---------------------------------------------------------------- MXFP4 read copy
+
+
+def replay_mx4(r):
+    st = S._lib.ssu_replay_mx4_update(ctypes.byref(r), None)
+    return st, S.ssu_last_error()
+
+
+def replay_mx4_args(**kw):
+    r = replay_lp_args(**kw)
+    slots, H, P, N = (r.lp.size[i] for i in range(4))
+    r.lp = tdesc((slots, H, P, N // 2), S.U8)
+    return r
+
+
+def test_replay_mx4_empty_is_ok_without_launch():
+    assert replay_mx4(replay_mx4_args()) == (S.OK, "")
+    # the MXFP8 entry point takes the full-width copy only
+    st, msg = replay_lp(replay_mx4_args())
+    assert st == S.ERR_VALUE and "lp must be [slots, heads, dim, dstate]" in msg
+
+
+def test_replay_mx4_errors():
+    assert S._lib.ssu_replay_mx4_update(None, None) == S.ERR_VALUE
+    st, msg = replay_mx4(replay_mx4_args(sd=S.BF16))
+    assert st == S.ERR_NOT_IMPLEMENTED and "MXFP4" in msg and "f32" in msg
+    st, msg = replay_mx4(replay_mx4_args(N=16))
+    assert st == S.ERR_VALUE and "multiple of 32" in msg
+    r = replay_mx4_args()
+    r.lp = tdesc((8, 8, 16, 128), S.U8)  # the MXFP8 width
+    st, msg = replay_mx4(r)
+    assert st == S.ERR_VALUE and "dstate / 2" in msg
+    r = replay_mx4_args()
+    r.lp_scale = tdesc((8, 8, 16, 8), S.U8)
+    st, msg = replay_mx4(r)
+    assert st == S.ERR_VALUE and "lp_scale must be" in msg
+    r = replay_mx4_args()
+    r.lp = tdesc((8, 8, 16, 64), S.U8, strides=(8 * 16 * 64, 16 * 64, 1, 16))
+    st, msg = replay_mx4(r)
+    assert st == S.ERR_VALUE and "contiguous" in msg
+    r = replay_mx4_args()
+    r.lp = tdesc((8, 8, 16, 64), S.U8, ptr=FAKE + 2)
+    st, msg = replay_mx4(r)
+    assert st == S.ERR_VALUE and "aligned" in msg
+
+
+def quantize4(src, codes, scales):
+    st = S._lib.ssu_mx4_quantize(ctypes.byref(src), ctypes.byref(codes), ctypes.byref(scales), None)
+    return st, S.ssu_last_error()
+
+
+def test_mx4_quantize_empty_and_errors():
+    assert quantize4(tdesc((0,), S.F32), tdesc((0,), S.U8), tdesc((0,), S.U8)) == (S.OK, "")
+    assert S._lib.ssu_mx4_quantize(None, None, None, None) == S.ERR_VALUE
+    st, msg = quantize4(tdesc((48,), S.F32), tdesc((24,), S.U8), tdesc((1,), S.U8))
+    assert st == S.ERR_VALUE and "multiple of 32" in msg
+    st, msg = quantize4(tdesc((64,), S.F32), tdesc((64,), S.U8), tdesc((2,), S.U8))
+    assert st == S.ERR_VALUE and "codes" in msg and "32 bytes" in msg
+    st, msg = quantize4(tdesc((64,), S.F32), tdesc((32,), S.U8), tdesc((3,), S.U8))
+    assert st == S.ERR_VALUE and "scales" in msg
+    st, msg = quantize4(tdesc((64,), S.F32), tdesc((32,), S.U8, ptr=FAKE + 2), tdesc((2,), S.U8))
+    assert st == S.ERR_VALUE and "4-byte" in msg
 
 
 def test_conv_state_shift_empty_and_errors():

@@ -49,8 +49,11 @@ def test_replay_small(sd, io, L, per_head, N, P):
 
 
 def test_replay_L1_equals_plain_kernel():
-    """L = 1: the replay kernel's step equals the plain one-token kernel bit
-    for bit (y and pool)."""
+    """L = 1: every step is a fill of one step, whose state update is the
+    plain one-token kernel's arithmetic: the pools agree bit for bit. y is the
+    same dot product S . C summed in another order (4 values a lane over 32
+    lanes against 8 over 16), so the two bf16 outputs are at most one
+    rounding apart."""
     for sd in ("f32", "bf16"):
         c = W.replay(seed=7, batch=32, heads=16, dim=64, dstate=128, groups=4, slots=48, L=1,
                      state_dtype=sd, buf_len=0)
@@ -58,7 +61,11 @@ def test_replay_L1_equals_plain_kernel():
         got = G.run_gpu_replay(c)
         plain = {k: v for k, v in c.items() if not k.startswith("buf") and k != "L"}
         y, s = G.run_gpu(plain)
-        assert np.array_equal(got["y"], y) and np.array_equal(got["state"], s), sd
+        assert np.array_equal(got["state"], s), sd
+        gy = G.brute64.to_f64(got["y"], c["io_dtype"])
+        py = G.brute64.to_f64(y, c["io_dtype"])
+        # one bf16 step (8 significant bits) of the larger magnitude
+        assert (np.abs(gy - py) <= np.maximum(np.abs(gy), np.abs(py)) * 2.0 ** -7).all(), sd
 
 
 def test_replay_window_equals_chain():
