@@ -1086,6 +1086,8 @@ static ssu_status_t replay_common(const ssu_replay_args_t *ra, bool spec, void *
     } else {
         // one wave per kReplayRows dim rows of a (sequence, head)
         p.dim_tiles = static_cast<int32_t>((pr.P + ssu::kReplayRows - 1) / ssu::kReplayRows);
+        if (pr.nseq <= ssu::kReplayScanMax && rp.L > 1)
+            p.flags |= ssu::kFillFirst;
         p.rows_per_block = ssu::kReplayRows;
         const int64_t waves = pr.nseq * pr.H * p.dim_tiles;
         if (waves > INT32_MAX)

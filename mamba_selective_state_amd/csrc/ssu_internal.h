@@ -27,7 +27,8 @@ enum Flags : int32_t {
     kWrite2D = 1 << 5,
     kWriteI64 = 1 << 6,
     kCuI64 = 1 << 7,
-    kAccI64 = 1 << 8
+    kAccI64 = 1 << 8,
+    kFillFirst = 1 << 9  // replay: sequences that fill their buffer are taken first
 };
 
 // Geometry of one workgroup: 16 lanes share a dim row (one DPP row), so a
@@ -50,17 +51,24 @@ constexpr int kMaxWaves = SSU_MAX_WAVES;
 // SIMD its register allocation must allow.
 constexpr int kReplayRows = 64;
 constexpr int kReplayWaves = 4;
+// Batches up to this size take the filling sequences first (each wave scans
+// the buffer counts of the whole batch).
+constexpr int kReplayScanMax = 512;
 #ifndef SSU_WAVES_PER_EU_REPLAY
 #define SSU_WAVES_PER_EU_REPLAY 4
 #endif
 constexpr int replay_waves_per_eu() { return SSU_WAVES_PER_EU_REPLAY; }
-// Slices in flight per wave: of the fold, of the output-only read's MXFP8
-// and MXFP4 copies, and 32-bit words of its checkpoint slices.
+// Window steps per round of the output-only path; slices in flight per
+// wave: of the fold, of the output-only read's MXFP8 and MXFP4 copies, and
+// 32-bit words of its checkpoint slices.
 #ifndef SSU_REPLAY_COPY8_DEPTH
 #define SSU_REPLAY_COPY8_DEPTH 4
 #endif
 #ifndef SSU_REPLAY_COPY4_DEPTH
 #define SSU_REPLAY_COPY4_DEPTH 4
+#endif
+#ifndef SSU_REPLAY_WIN
+#define SSU_REPLAY_WIN 8
 #endif
 #ifndef SSU_REPLAY_FOLD_DEPTH
 #define SSU_REPLAY_FOLD_DEPTH 4

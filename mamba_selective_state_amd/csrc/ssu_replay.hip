@@ -30,7 +30,7 @@ namespace {
 // and writes nothing. LPF: the read copy's format -- 0 none, 8 MXFP8 (a byte
 // a value), 4 MXFP4 (two values a byte); a copy is read in place of the
 // checkpoint by output-only steps that are not a fill of the buffer.
-constexpr int kReplayWin = 8;   // window steps per round of the output-only path
+constexpr int kReplayWin = SSU_REPLAY_WIN;  // window steps per round of the output-only path
 constexpr int kReplayTab = 36;  // floats per row of the fold table (a_0 .. a_15, dt'x_0 .. dt'x_15; 16-byte rows)
 
 // Sum over aligned groups of L lanes (1 .. 64), in every lane of the group.
@@ -100,10 +100,60 @@ __global__ __launch_bounds__(kReplayWaves *kWaveLanes, replay_waves_per_eu()) vo
 
     const int lane = threadIdx.x & (kWaveLanes - 1);
     const int wave = threadIdx.x / kWaveLanes;
-    const int32_t item =
+    int32_t item =
         __builtin_amdgcn_readfirstlane(xcd_clustered_index(blockIdx.x, gridDim.x) * kReplayWaves + wave);
     if (item >= p.nseq * p.H * p.dim_tiles)
         return;  // the last workgroup's spare waves
+    if (p.flags & kFillFirst) {
+        // Any order of the (sequence, head, rows) items is correct. A fill
+        // moves several times a step's bytes, so the sequences whose step
+        // fills the buffer (buf_len + 1 == L) are taken first, then the
+        // others, each in batch order: no long wave starts last.
+        constexpr int kBlocks = kReplayScanMax / kWaveLanes;
+        const int32_t per = p.H * p.dim_tiles;
+        uint32_t bits = 0;  // bit m: sequence 64 m + lane fills
+#pragma unroll
+        for (int m = 0; m < kBlocks; m++) {
+            const int32_t bm = m * kWaveLanes + lane;
+            if (m * kWaveLanes < p.nseq && bm < p.nseq)
+                bits |= static_cast<uint32_t>(load_index(rp.buf_len, rp.len_i64, bm * rp.len_s) + 1 == rp.L) << m;
+        }
+        int32_t fills = 0;
+#pragma unroll
+        for (int m = 0; m < kBlocks; m++)
+            fills += __popcll(__ballot((bits >> m) & 1u));
+        const bool take_fill = item < fills * per;
+        int32_t k = take_fill ? item / per : (item - fills * per) / per;  // rank in its kind
+        int32_t bsel = 0;
+        bool found = false;
+#pragma unroll
+        for (int m = 0; m < kBlocks; m++) {
+            const int32_t live = p.nseq - m * kWaveLanes;  // sequences in block m
+            if (live <= 0 || found)
+                continue;
+            uint64_t mask = __ballot((bits >> m) & 1u);
+            if (!take_fill)
+                mask = ~mask & (live >= kWaveLanes ? ~0ull : (1ull << live) - 1);
+            const int32_t c = __popcll(mask);
+            if (k < c) {
+                // position of the k-th set bit
+                int pos = 0;
+#pragma unroll
+                for (int w = 32; w >= 1; w >>= 1) {
+                    const int32_t lo = __popcll((mask >> pos) & ((1ull << w) - 1));
+                    if (k >= lo) {
+                        k -= lo;
+                        pos += w;
+                    }
+                }
+                bsel = m * kWaveLanes + pos;
+                found = true;
+            } else {
+                k -= c;
+            }
+        }
+        item = __builtin_amdgcn_readfirstlane(bsel * per + item % per);
+    }
     const int chunk = item % p.dim_tiles;
     const int32_t sh = item / p.dim_tiles;
     const int h = sh % p.H;

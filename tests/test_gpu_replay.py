@@ -48,6 +48,21 @@ def test_replay_small(sd, io, L, per_head, N, P):
     G.check_replay(c, "replay %s %s L=%d" % (sd, io, L))
 
 
+@pytest.mark.parametrize("batch", [100, 513])
+def test_replay_fill_order(batch):
+    """Sequences that fill their buffer are taken first when the batch is at
+    most 512 (a scan of every count), in batch order otherwise: a batch over
+    several 64-sequence blocks with a partial last one, and one past the
+    scan's limit, each with fills scattered through it."""
+    L = 6
+    c = W.replay(seed=30 + batch, batch=batch, heads=4, dim=64, dstate=64, groups=2,
+                 slots=batch + 8, L=L)
+    rng = np.random.default_rng(batch)
+    c["buf_len"][:] = rng.integers(0, L, batch)
+    c["buf_len"][rng.random(batch) < 0.2] = L - 1
+    G.check_replay(c, "replay fill order, batch %d" % batch)
+
+
 def test_replay_L1_equals_plain_kernel():
     """L = 1: every step is a fill of one step, whose state update is the
     plain one-token kernel's arithmetic: the pools agree bit for bit. y is the
