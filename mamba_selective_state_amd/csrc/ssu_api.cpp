@@ -926,8 +926,18 @@ ssu_status_t ssu_update(const ssu_args_t *a, void *stream) {
     if (!yonly && !ssu::find_kernel(pr.state_dtype, pr.io, static_cast<int>(pr.N), pr.multi, &k))
         return fail(SSU_ERR_NOT_IMPLEMENTED, "no kernel for state %s / io %s / dstate %lld",
                     dtype_str(pr.state_dtype), dtype_str(pr.io), (long long)pr.N);
-    const int e = ssu::launch(k, pr.p, static_cast<unsigned>(pr.grid),
-                              static_cast<unsigned>(pr.geo.block), stream);
+    ssu::Params p = pr.p;
+    Geometry geo = pr.geo;
+    int64_t grid = pr.grid;
+    if (yonly) {  // the output-only variant's own tile
+        geo = geometry(pr.P, pr.N, pr.state_dtype, ssu::kTileYonly);
+        p.dim_tiles = geo.dim_tiles;
+        p.rows_per_block = geo.rows_per_block;
+        grid = pr.nseq * pr.H * geo.dim_tiles;
+        if (grid > INT32_MAX)
+            return fail(SSU_ERR_NOT_IMPLEMENTED, "grid of %lld workgroups is too large", (long long)grid);
+    }
+    const int e = ssu::launch(k, p, static_cast<unsigned>(grid), static_cast<unsigned>(geo.block), stream);
     if (e != 0)
         return fail(SSU_ERR_HIP, "kernel launch failed: %s", ssu::hip_error_string(e));
     g_error.clear();

@@ -98,11 +98,17 @@ constexpr int replay_spec_waves_per_eu(int state_bytes, int dstate) {
 #ifndef SSU_LANE_BYTES_REPLAY
 #define SSU_LANE_BYTES_REPLAY 128
 #endif
-enum TileKind { kTileOneToken = 0, kTileMulti = 1, kTileReplay = 2 };
+// the multi-token kernel's output-only variant, which also holds its tokens'
+// per-row inputs
+#ifndef SSU_LANE_BYTES_YONLY
+#define SSU_LANE_BYTES_YONLY 128
+#endif
+enum TileKind { kTileOneToken = 0, kTileMulti = 1, kTileReplay = 2, kTileYonly = 3 };
 constexpr int passes_for(int dstate, int state_bytes, int kind) {
     const int per_row = (dstate / kLanesPerRow) * state_bytes;
     const int budget = kind == kTileMulti    ? SSU_LANE_BYTES_MULTI
                        : kind == kTileReplay ? SSU_LANE_BYTES_REPLAY
+                       : kind == kTileYonly  ? SSU_LANE_BYTES_YONLY
                                              : SSU_LANE_BYTES;
     const int rows = budget / per_row;
     return rows < 1 ? 1 : (rows > 8 ? 8 : rows);

@@ -41,12 +41,14 @@ namespace {
 // update, the readout and the rounding of the carried state. The carry is
 // therefore not rounded to the state dtype between tokens, which moves y by
 // far less than the tolerance of 16-bit outputs; the variant is used with
-// fp32 outputs only for fp32 state, where nothing is rounded. Each DPP row
-// forms the dots B_j . C_t with j = its row (mod 4) from the sequence's B
-// rows kept in LDS and hands them to the row owners through LDS (a workgroup
-// is one wave, whose LDS accesses complete in order). Longer sequences take
-// the update path.
+// fp32 outputs only for fp32 state, where nothing is rounded. All the
+// tokens' inputs are requested at once, with the tile: their B and C rows go
+// to LDS, the own row's x, z and dt to registers. Each DPP row forms the dots
+// B_j . C_t with j = its row (mod 4) and hands them to the row owners through
+// LDS (a workgroup is one wave, whose LDS accesses complete in order).
+// Longer sequences take the update path.
 constexpr int kYMax = 8;
+constexpr int kYRound = 4;  // tokens whose per-row inputs are requested together
 
 template <typename ST, typename IT, int N, bool MULTI, bool YONLY = false>
 __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
@@ -55,7 +57,7 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
     constexpr int E = N / kLanesPerRow;  // state elements per lane per row
     constexpr int VEC = (16 / (int)sizeof(ST)) < E ? (16 / (int)sizeof(ST)) : E;
     constexpr int NCH = E / VEC;         // accesses per lane per row
-    constexpr int PASSES = passes_for(N, sizeof(ST), MULTI ? kTileMulti : kTileOneToken);
+    constexpr int PASSES = passes_for(N, sizeof(ST), YONLY ? kTileYonly : MULTI ? kTileMulti : kTileOneToken);
     constexpr int IVEC = VEC;            // B / C are read with the same column split
     static_assert(E * kLanesPerRow == N && NCH * VEC == E, "dstate split");
     static_assert(PASSES <= kLanesPerRow, "one scalar-owning lane per pass");
@@ -256,36 +258,79 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
     if constexpr (YONLY) {
         if (len <= kYMax) {  // uniform
             __shared__ __attribute__((aligned(16))) IT Bl[kYMax][N];  // B rows of the tokens
+            __shared__ __attribute__((aligned(16))) IT Cl[kYMax][N];  // C rows of the tokens
             __shared__ float Wl[kYMax][kYMax];                        // Wl[j][t] = B_j . C_t
-            Inputs yin[2];
-            fetch(0, yin[0]);
+            // Every token's inputs in one round of loads, in flight with the
+            // tile: DPP row rsub copies the B and C rows of tokens rsub,
+            // rsub + 4 into LDS (tokens past the last reload the last), and
+            // the own row's x, z and dt of each token go to registers.
+            constexpr int kRounds = kYMax / kRowsPerPass;
+            RawWords<IT, IVEC> bst[kRounds][NCH], cst[kRounds][NCH];
+#pragma unroll
+            for (int i = 0; i < kRounds; i++) {
+                const int j = rsub + i * kRowsPerPass;
+                const int32_t r = first_row + (j < len ? j : len - 1);
+                const IT *bsrc = Bs + (r * p.B_sr + g * p.B_sg + col * IVEC);
+                const IT *csrc = Cs + (r * p.C_sr + g * p.C_sg + col * IVEC);
+#pragma unroll
+                for (int c = 0; c < NCH; c++) {
+                    bst[i][c] = load_words<IT, IVEC>(bsrc + c * kLanesPerRow * IVEC);
+                    cst[i][c] = load_words<IT, IVEC>(csrc + c * kLanesPerRow * IVEC);
+                }
+            }
+            // the own row's x, z and dt, kYRound tokens at a time (the first
+            // round now, the next when its first token comes)
+            typename Inputs::Bits xb[kYRound], zb[kYRound];
+            uint16_t dlo[kYRound], dhi[kYRound];
+            auto fetch_round = [&](int t0) {
+#pragma unroll
+                for (int u = 0; u < kYRound; u++) {
+                    const int32_t r = first_row + (t0 + u < len ? t0 + u : len - 1);
+                    xb[u] = *reinterpret_cast<const typename Inputs::Bits *>(xs + (r * p.x_sr + h * p.x_sh + d_fetch));
+                    zb[u] = *reinterpret_cast<const typename Inputs::Bits *>(zsrc + (r * z_sr + h * z_sh + d_fetch));
+                    const unsigned char *dp =
+                        dts + static_cast<int64_t>(r * p.dt_sr + h * p.dt_sh + d_fetch * p.dt_sp) * dt_bytes;
+                    dlo[u] = *reinterpret_cast<const uint16_t *>(dp);
+                    dhi[u] = *reinterpret_cast<const uint16_t *>(dp + (dt_f32 ? 2 : 0));
+                }
+            };
+            fetch_round(0);
+#pragma unroll
+            for (int i = 0; i < kRounds; i++) {
+                const int j = rsub + i * kRowsPerPass;
+                if (j < len) {
+#pragma unroll
+                    for (int c = 0; c < NCH; c++) {
+                        store_words<IT, IVEC>(&Bl[j][c * kLanesPerRow * IVEC + col * IVEC], bst[i][c]);
+                        store_words<IT, IVEC>(&Cl[j][c * kLanesPerRow * IVEC + col * IVEC], cst[i][c]);
+                    }
+                }
+            }
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
             float av[kYMax], dxv[kYMax];  // the own row's decay and dt' x per token
             float G = 1.0f;               // prod of the decays so far
 #pragma unroll
             for (int t = 0; t < kYMax; t++) {
                 if (t >= len)
                     break;  // uniform
-                __builtin_amdgcn_sched_barrier(0);
-                fetch(t + 1 < len ? t + 1 : len - 1, yin[(t + 1) & 1]);
-                __builtin_amdgcn_sched_barrier(0);
-                const Inputs &in = yin[t & 1];
+                if (t > 0 && t % kYRound == 0)
+                    fetch_round(t);
+                const int u = t % kYRound;
                 const int32_t r = first_row + t;
                 float Cv[E];
 #pragma unroll
-                for (int c = 0; c < NCH; c++)
+                for (int c = 0; c < NCH; c++) {
+                    const RawWords<IT, IVEC> cw =
+                        *reinterpret_cast<const RawWords<IT, IVEC> *>(&Cl[t][c * kLanesPerRow * IVEC + col * IVEC]);
 #pragma unroll
                     for (int k = 0; k < IVEC; k++)
-                        Cv[c * IVEC + k] = word_elem(in.c[c], k);
-                if (rsub == 0) {
-#pragma unroll
-                    for (int c = 0; c < NCH; c++)
-                        store_words<IT, IVEC>(&Bl[t][c * kLanesPerRow * IVEC + col * IVEC], in.b[c]);
+                        Cv[c * IVEC + k] = word_elem(cw, k);
                 }
                 // scalars of the lane's own row
-                const float xv = from_bits<IT>(in.x);
-                const float zv = from_bits<IT>(in.z);
-                const float dtv = dt_f32 ? __uint_as_float(uint32_t(in.dt_lo) | (uint32_t(in.dt_hi) << 16))
-                                         : from_bits<IT>(in.dt_lo);
+                const float xv = from_bits<IT>(xb[u]);
+                const float zv = from_bits<IT>(zb[u]);
+                const float dtv = dt_f32 ? __uint_as_float(uint32_t(dlo[u]) | (uint32_t(dhi[u]) << 16))
+                                         : from_bits<IT>(dlo[u]);
                 float v = dtv + bias_h;
                 if (flags & kSoftplus)
                     v = softplus(v);
