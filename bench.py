@@ -19,6 +19,8 @@ Prints ONE JSON line:
 Timing: every timed call is bracketed by its own pair of HIP events on the
 launch stream; kernel_us is their median (kernel_us_mean their mean), and
 roofline.achieved uses the median.
+  line_granular  (dim-major shift) the same call against the minimal bytes at
+             cache-line granularity: its rows are shorter than a line
   ceiling    the same bytes moved by the runtime's device-to-device copy and
              by an in-place read-modify-write stream (libssu_ceiling.so):
              what this part sustains for a plain stream of that size
@@ -548,6 +550,19 @@ def copy_algorithmic_bytes(case):
     return int(2 * np.sum(np.maximum(sizes, 0)) + 3 * 8 * len(sizes)), len(sizes)
 
 
+def copy_line_bytes(case):
+    """Minimal HBM bytes at cache-line granularity (128 B): the dim-major
+    shift moves (W - bias) elements of rows only W elements long (8 bytes at
+    width 4, fp16), so every line of the source block is read and every line
+    of the destination block written; the other copies move whole lines (the
+    byte-exact count). Returns bytes per step."""
+    if "pool" in case and case["layout"] == "DS":
+        pool = case["pool"]
+        block = pool.shape[1] * pool.shape[2] * pool.itemsize
+        return 2 * block * len(case["bias"]) + 3 * 8 * len(case["bias"])
+    return copy_algorithmic_bytes(case)[0]
+
+
 def copy_bench(args, name, case, desc):
     """bench.py for the state copies: one step is one call over the workload."""
     import torch
@@ -599,6 +614,11 @@ def copy_bench(args, name, case, desc):
                      "kernel_us": round(event_ms * 1e3, 2), "kernel_us_mean": round(mean_ms * 1e3, 2)},
         "ceiling": ceiling_fields(dev, alg_bytes),
     }
+    line = copy_line_bytes(case)
+    if line != alg_bytes:
+        result["line_granular"] = {"bytes_per_step": line,
+                                   "achieved": round(line / (event_ms * 1e-3) / 1e9, 2),
+                                   "frac": round(line / (event_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     if not args.no_cpu_baseline:
         from oracle import ssu_oracle
         times = []
