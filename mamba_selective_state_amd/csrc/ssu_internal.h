@@ -84,6 +84,10 @@ constexpr int replay_spec_waves_per_eu(int state_bytes, int dstate) {
 #ifndef SSU_WAVES_PER_EU_MULTI
 #define SSU_WAVES_PER_EU_MULTI 4
 #endif
+// the multi-token kernel's output-only variant on the matrix cores
+#ifndef SSU_WAVES_PER_EU_YMFMA
+#define SSU_WAVES_PER_EU_YMFMA 4
+#endif
 
 // Passes (dim rows per lane): enough rows that each lane keeps about
 // `lane_bytes` of state in flight (dstate/16 elements per row, in the state

@@ -48,11 +48,38 @@ namespace {
 // LDS (a workgroup is one wave, whose LDS accesses complete in order).
 // Longer sequences take the update path.
 constexpr int kYMax = 8;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// D += A B on a 16 x 16 x 32 tile: A row m = lane % 16 with k = 8 (lane / 16)
+// .. +7, B column n = lane % 16 with the same k, D[4 (lane / 16) + i][lane % 16]
+// in register i.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x32(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
 constexpr int kYRound = 4;  // tokens whose per-row inputs are requested together
+
+// The output-only variant forms every S_0 . C_t on the matrix cores where
+// the products are exact in an MFMA input type: a bf16 state with bf16 C, an
+// fp16 state with fp16 C, or with bf16 C taken into fp16 by a power-of-two
+// scale per token (bf16's 8 significant bits fit fp16's 11).
+template <typename ST, typename IT, int N, bool YONLY>
+constexpr bool yonly_mfma() {
+    return YONLY && N % 32 == 0 && (kRowsPerPass * passes_for(N, sizeof(ST), kTileYonly)) % 16 == 0 &&
+           ((std::is_same_v<ST, __bf16> && std::is_same_v<IT, __bf16>) ||
+            (std::is_same_v<ST, _Float16> && !std::is_same_v<IT, float>));
+}
 
 template <typename ST, typename IT, int N, bool MULTI, bool YONLY = false>
 __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
-                             MULTI ? SSU_WAVES_PER_EU_MULTI : SSU_WAVES_PER_EU) void ssu_kernel(const Params p) {
+                             (yonly_mfma<ST, IT, N, YONLY>() ? SSU_WAVES_PER_EU_YMFMA
+                              : MULTI                         ? SSU_WAVES_PER_EU_MULTI
+                                                              : SSU_WAVES_PER_EU)) void ssu_kernel(const Params p) {
     static_assert(!YONLY || MULTI, "the output-only path is a multi-token path");
     constexpr int E = N / kLanesPerRow;  // state elements per lane per row
     constexpr int VEC = (16 / (int)sizeof(ST)) < E ? (16 / (int)sizeof(ST)) : E;
@@ -63,6 +90,8 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
     static_assert(PASSES <= kLanesPerRow, "one scalar-owning lane per pass");
     using SPack = Pack<ST, VEC>;
     using Inputs = TokenInputs<IT, NCH, IVEC>;
+    constexpr int kRowsWave = kRowsPerPass * PASSES;
+    constexpr bool YMFMA = yonly_mfma<ST, IT, N, YONLY>();
 
     const int lane = threadIdx.x & (kWaveLanes - 1);
     const int wave = threadIdx.x / kWaveLanes;
@@ -117,21 +146,27 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
     SPack S[PASSES][NCH];
     const bool read_pad = rslot == p.pad;
     const ST *const rbase = pool + rslot * p.slot_stride + tile_off;
+    auto load_tile = [&]() {
 #pragma unroll
-    for (int q = 0; q < PASSES; q++) {
-        const int d = dw + q * kRowsPerPass + rsub;
+        for (int q = 0; q < PASSES; q++) {
+            const int d = dw + q * kRowsPerPass + rsub;
 #pragma unroll
-        for (int c = 0; c < NCH; c++) {
-            if (!read_pad && d < p.P) {
-                S[q][c] = load_state(reinterpret_cast<const SPack *>(
-                    rbase + static_cast<int64_t>(d) * N + c * kLanesPerRow * VEC + col * VEC));
-            } else {
+            for (int c = 0; c < NCH; c++) {
+                if (!read_pad && d < p.P) {
+                    S[q][c] = load_state(reinterpret_cast<const SPack *>(
+                        rbase + static_cast<int64_t>(d) * N + c * kLanesPerRow * VEC + col * VEC));
+                } else {
 #pragma unroll
-                for (int k = 0; k < VEC; k++)
-                    S[q][c].v[k] = narrow<ST>(0.0f);
+                    for (int k = 0; k < VEC; k++)
+                        S[q][c].v[k] = narrow<ST>(0.0f);
+                }
             }
         }
-    }
+    };
+    // (the output-only variant on the matrix cores reads the tile in its own
+    // layout, and this one only for a sequence too long for it)
+    if constexpr (!YMFMA)
+        load_tile();
 
     const float a_h = p.A[h * p.A_sh];
     const float d_h = p.D ? p.D[h * p.D_sh] : 0.0f;
@@ -260,6 +295,24 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
             __shared__ __attribute__((aligned(16))) IT Bl[kYMax][N];  // B rows of the tokens
             __shared__ __attribute__((aligned(16))) IT Cl[kYMax][N];  // C rows of the tokens
             __shared__ float Wl[kYMax][kYMax];                        // Wl[j][t] = B_j . C_t
+            // (matrix cores) the tile as A operands: lane l takes row
+            // 16 mt + l % 16 and columns 32 kb + 8 (l / 16) .. +7 (16 bytes);
+            // rows past the dim and the pad id read a valid row, then zeros
+            constexpr int MT = YMFMA ? kRowsWave / 16 : 1, KB = YMFMA ? N / 32 : 1;
+            using MV = std::conditional_t<std::is_same_v<ST, __bf16>, bf16x8, f16x8>;
+            u32x4 sa[MT][KB];
+            if constexpr (YMFMA) {
+                const ST *abase = read_pad ? pool + tile_off : rbase;
+#pragma unroll
+                for (int mt = 0; mt < MT; mt++) {
+                    const int d = dw + 16 * mt + (lane & 15);
+                    const int dl = d < p.P ? d : p.P - 1;
+#pragma unroll
+                    for (int kb = 0; kb < KB; kb++)
+                        sa[mt][kb] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                            abase + static_cast<int64_t>(dl) * N + 32 * kb + 8 * (lane >> 4)));
+                }
+            }
             // Every token's inputs in one round of loads, in flight with the
             // tile: DPP row rsub copies the B and C rows of tokens rsub,
             // rsub + 4 into LDS (tokens past the last reload the last), and
@@ -278,13 +331,15 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
                     cst[i][c] = load_words<IT, IVEC>(csrc + c * kLanesPerRow * IVEC);
                 }
             }
-            // the own row's x, z and dt, kYRound tokens at a time (the first
-            // round now, the next when its first token comes)
-            typename Inputs::Bits xb[kYRound], zb[kYRound];
-            uint16_t dlo[kYRound], dhi[kYRound];
+            // the own row's x, z and dt, kRound tokens at a time (the first
+            // round now, the next when its first token comes; one round of 8
+            // was not faster on the matrix-core variant)
+            constexpr int kRound = kYRound;
+            typename Inputs::Bits xb[kRound], zb[kRound];
+            uint16_t dlo[kRound], dhi[kRound];
             auto fetch_round = [&](int t0) {
 #pragma unroll
-                for (int u = 0; u < kYRound; u++) {
+                for (int u = 0; u < kRound; u++) {
                     const int32_t r = first_row + (t0 + u < len ? t0 + u : len - 1);
                     xb[u] = *reinterpret_cast<const typename Inputs::Bits *>(xs + (r * p.x_sr + h * p.x_sh + d_fetch));
                     zb[u] = *reinterpret_cast<const typename Inputs::Bits *>(zsrc + (r * z_sr + h * z_sh + d_fetch));
@@ -307,24 +362,110 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
                 }
             }
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            // u_t = S_0 . C_t of every row of the wave and token, on the matrix cores
+            __shared__ float Ul[YMFMA ? kRowsWave : 1][kYMax];
+            if constexpr (YMFMA) {
+                // bf16 C into fp16: token j scaled by 2^-e_j, e_j = floor(log2 max |C_j|) - 14,
+                // so its values down to 2^-28 of the largest are exact fp16 normals
+                constexpr bool kScaled = std::is_same_v<ST, _Float16> && std::is_same_v<IT, __bf16>;
+                // (and B the same way, for W = B C^T)
+                __shared__ int El[2][kYMax];
+                if constexpr (kScaled) {
+#pragma unroll
+                    for (int i = 0; i < kRounds; i++) {
+                        float mc = 0.0f, mb = 0.0f;
+#pragma unroll
+                        for (int c = 0; c < NCH; c++)
+#pragma unroll
+                            for (int k = 0; k < IVEC; k++) {
+                                mc = fmaxf(mc, fabsf(word_elem(cst[i][c], k)));
+                                mb = fmaxf(mb, fabsf(word_elem(bst[i][c], k)));
+                            }
+                        mc = group_max<16>(mc);
+                        mb = group_max<16>(mb);
+                        const int j = rsub + i * kRowsPerPass;
+                        auto expo = [](float m) {
+                            const int ex = static_cast<int>((__float_as_uint(m) >> 23) & 0xFFu);
+                            return m == 0.0f ? 0 : (ex == 0 ? -126 : ex - 127) - 14;
+                        };
+                        if (col == 0 && j < len) {
+                            El[0][j] = expo(mc);
+                            El[1][j] = expo(mb);
+                        }
+                    }
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+                }
+                // one token a lane: the B operand's column (C_n) and the W
+                // product's A row (B_n)
+                const int n = lane & 15;
+                const int nr = n < len ? n : len - 1;
+                const int ec = kScaled ? El[0][nr] : 0, eb = kScaled ? El[1][nr] : 0;
+                auto operand = [&](const IT *src, int e) {
+                    const u32x4 w = *reinterpret_cast<const u32x4 *>(src);
+                    MV v;
+                    if constexpr (kScaled) {
+                        const bf16x8 x = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+                        for (int k = 0; k < 8; k++)
+                            v[k] = static_cast<_Float16>(ldexpf(static_cast<float>(x[k]), -e));
+                    } else {
+                        v = __builtin_bit_cast(MV, w);
+                    }
+                    return n < len ? v : MV{};
+                };
+                f32x4 D[MT], Dw = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int mt = 0; mt < MT; mt++)
+                    D[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int kb = 0; kb < KB; kb++) {
+                    const MV bv = operand(&Cl[nr][32 * kb + 8 * (lane >> 4)], ec);
+#pragma unroll
+                    for (int mt = 0; mt < MT; mt++) {
+                        const bool live = !read_pad && dw + 16 * mt + (lane & 15) < p.P;
+                        const u32x4 a = live ? sa[mt][kb] : u32x4{0u, 0u, 0u, 0u};
+                        D[mt] = mfma16x16x32(__builtin_bit_cast(MV, a), bv, D[mt]);
+                    }
+                    Dw = mfma16x16x32(operand(&Bl[nr][32 * kb + 8 * (lane >> 4)], eb), bv, Dw);
+                }
+                if (n < kYMax) {
+#pragma unroll
+                    for (int mt = 0; mt < MT; mt++)
+#pragma unroll
+                        for (int i = 0; i < 4; i++)
+                            Ul[16 * mt + 4 * (lane >> 4) + i][n] = ldexpf(D[mt][i], ec);
+                    // Dw[i] = W[j][n] with j = 4 (lane / 16) + i, scaled by 2^-(eb_j + ec_n)
+                    if ((lane >> 4) < kYMax / 4) {
+#pragma unroll
+                        for (int i = 0; i < 4; i++) {
+                            const int j = 4 * (lane >> 4) + i;
+                            const int ebj = kScaled ? El[1][j < len ? j : len - 1] : 0;
+                            Wl[j][n] = ldexpf(Dw[i], ec + ebj);
+                        }
+                    }
+                }
+                __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            }
             float av[kYMax], dxv[kYMax];  // the own row's decay and dt' x per token
             float G = 1.0f;               // prod of the decays so far
 #pragma unroll
             for (int t = 0; t < kYMax; t++) {
                 if (t >= len)
                     break;  // uniform
-                if (t > 0 && t % kYRound == 0)
+                if (t > 0 && t % kRound == 0)
                     fetch_round(t);
-                const int u = t % kYRound;
+                const int u = t % kRound;
                 const int32_t r = first_row + t;
                 float Cv[E];
+                if constexpr (!YMFMA) {
 #pragma unroll
-                for (int c = 0; c < NCH; c++) {
-                    const RawWords<IT, IVEC> cw =
-                        *reinterpret_cast<const RawWords<IT, IVEC> *>(&Cl[t][c * kLanesPerRow * IVEC + col * IVEC]);
+                    for (int c = 0; c < NCH; c++) {
+                        const RawWords<IT, IVEC> cw =
+                            *reinterpret_cast<const RawWords<IT, IVEC> *>(&Cl[t][c * kLanesPerRow * IVEC + col * IVEC]);
 #pragma unroll
-                    for (int k = 0; k < IVEC; k++)
-                        Cv[c * IVEC + k] = word_elem(cw, k);
+                        for (int k = 0; k < IVEC; k++)
+                            Cv[c * IVEC + k] = word_elem(cw, k);
+                    }
                 }
                 // scalars of the lane's own row
                 const float xv = from_bits<IT>(xb[u]);
@@ -339,22 +480,28 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
                 G *= av[t];
                 // u = S_0 . C_t of the own row
                 float usum = 0.0f;
-                for_passes<0, PASSES>([&](auto qc) {
-                    constexpr int q = decltype(qc)::value;
-                    float acc = 0.0f;
+                if constexpr (YMFMA) {
+                    const int lr = d_own - dw;  // < kRowsWave for an owner
+                    usum = Ul[lr < kRowsWave ? lr : kRowsWave - 1][t];
+                } else {
+                    for_passes<0, PASSES>([&](auto qc) {
+                        constexpr int q = decltype(qc)::value;
+                        float acc = 0.0f;
 #pragma unroll
-                    for (int c = 0; c < NCH; c++)
+                        for (int c = 0; c < NCH; c++)
 #pragma unroll
-                        for (int k = 0; k < VEC; k++)
-                            acc = fmaf(widen(S[q][c].v[k]), Cv[c * VEC + k], acc);
-                    const float sum = row16_sum(acc);
-                    usum = col == q ? sum : usum;
-                });
+                            for (int k = 0; k < VEC; k++)
+                                acc = fmaf(widen(S[q][c].v[k]), Cv[c * VEC + k], acc);
+                        const float sum = row16_sum(acc);
+                        usum = col == q ? sum : usum;
+                    });
+                }
                 // B_j . C_t for j = rsub, rsub + 4, ... up to t (rows past t
-                // repeat token t and write nothing)
+                // repeat token t and write nothing); on the matrix cores, all
+                // of them before the loop
                 __atomic_signal_fence(__ATOMIC_SEQ_CST);
 #pragma unroll
-                for (int jj = 0; jj < kYMax; jj += kRowsPerPass) {
+                for (int jj = 0; jj < (YMFMA ? 0 : kYMax); jj += kRowsPerPass) {
                     if (jj > t)
                         break;  // uniform
                     const int j = jj + rsub;
@@ -390,6 +537,19 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
             }
             return;
         }
+    }
+
+    if constexpr (YMFMA) {
+        // a sequence longer than kYMax: the update path without stores, one
+        // token at a time (the double-buffered loop below would set this
+        // kernel's registers for a case its callers rarely reach)
+        load_tile();
+        for (int32_t t = 0; t < len; t++) {
+            Inputs in;
+            fetch(t, in);
+            process(t, in);
+        }
+        return;
     }
 
     // Tokens alternate between two input buffers: the next token's inputs are

@@ -100,6 +100,39 @@ def test_varlen(mode):
     G.check(c, "varlen %s" % mode)
 
 
+YONLY_CASES = [
+    # (state, io, dstate, dim): the output-only variant (disable_state_update) on
+    # the matrix cores (f16 state with f16 or bf16 io, bf16 with bf16) and on
+    # the VALU (the rest)
+    ("f16", "bf16", 128, 64), ("f16", "bf16", 32, 40), ("f16", "bf16", 256, 64),
+    ("f16", "f16", 64, 64), ("bf16", "bf16", 128, 28), ("bf16", "bf16", 256, 64),
+    ("bf16", "f16", 128, 64), ("f32", "bf16", 128, 64), ("f32", "f32", 64, 36),
+]
+
+
+@pytest.mark.parametrize("sd,io,N,P", YONLY_CASES, ids=["%s-%s-n%d-p%d" % c for c in YONLY_CASES])
+def test_varlen_disable_variants(sd, io, N, P):
+    """Lengths 0..12: sequences of at most 8 tokens take the output-only
+    path, longer ones the update path without stores."""
+    rng = np.random.default_rng(N + P)
+    lengths = rng.integers(0, 13, 24)
+    lengths[:3] = [8, 9, 1]
+    c = W.varlen(seed=11, nseq=24, heads=4, dim=P, dstate=N, groups=2, state_dtype=sd, io=io,
+                 disable=True, lengths=lengths)
+    G.check(c, "varlen disable %s %s n%d p%d" % (sd, io, N, P))
+
+
+@pytest.mark.parametrize("pad", [0, -1])
+@pytest.mark.parametrize("sd", ["f32", "f16", "bf16"])
+def test_mtp_disable(sd, pad):
+    """MTP with disable_state_update: reads at the accepted count, the pad
+    id read as zeros, nothing stored."""
+    c = W.mtp(nseq=6, steps=7, heads=16, dim=64, dstate=128, groups=4, state_dtype=sd,
+              pad_slot_id=pad)
+    c["disable_state_update"] = True
+    G.check(c, "mtp disable %s pad=%d" % (sd, pad))
+
+
 def test_varlen_f32_ragged():
     c = W.varlen(seed=9, nseq=30, heads=4, dim=28, dstate=64, groups=2, state_dtype="f32",
                  io="f32")
