@@ -475,7 +475,7 @@ def ssd_bench_run(args, case, desc):
         "ms_per_step": round(wall / args.steps * 1e3, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": desc, "flops_per_step": flops, "bytes_per_step": nbytes,
-                   "kernels": "ssd_chunk_state_kernel, ssd_state_pass_kernel, ssd_chunk_scan_kernel"},
+                   "kernels": "ssd_prep_kernel, ssd_fused_kernel"},
         "tokens_per_s": round(np.shape(case["x"])[0] * args.steps / wall, 1),
         "hbm_gbs_algorithmic": round(nbytes / (event_ms * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm" if hbm_bound else "mfma",

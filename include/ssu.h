@@ -395,10 +395,13 @@ typedef struct {
 /* Bytes of device workspace ssu_ssd_prefill needs for `nchunks` chunks. */
 SSU_API int64_t ssu_ssd_workspace_bytes(int64_t heads, int64_t dim, int64_t dstate, int64_t nchunks);
 
-/* Three kernels on `stream` (none when there are no chunks); asynchronous;
+/* Two kernels on `stream` (none when there are no chunks); asynchronous;
  * allocates nothing: the caller passes `workspace` (DEVICE memory, 256-byte
  * aligned, at least ssu_ssd_workspace_bytes) and keeps it for the call's
- * duration. Errors as for ssu_update. */
+ * duration. The workspace carries each chunk's state to the next chunk of
+ * its sequence and the words that order that hand-over; the call clears
+ * them itself, so the workspace needs no clearing, but two calls that
+ * overlap (other streams) must not share one. Errors as for ssu_update. */
 SSU_API ssu_status_t ssu_ssd_prefill(const ssu_ssd_args_t *args, void *workspace, int64_t workspace_bytes,
                                      void *stream);
 

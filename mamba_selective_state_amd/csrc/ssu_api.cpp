@@ -594,25 +594,28 @@ ssu_status_t ssu_batch_memcpy(const ssu_tensor_t *src_ptrs, const ssu_tensor_t *
 
 // ---- SSD packed prefill
 
-// Workspace: dt' and the cumsum [nchunks, H, 256] f32, each chunk's own
-// state [nchunks, H, P, N] f32, each chunk's entering state in the x dtype
-// (2 bytes), each part 256-byte aligned.
-static int64_t ssd_ws_parts(int64_t H, int64_t P, int64_t N, int64_t nchunks, int64_t *rows_bytes,
-                            int64_t *state_bytes = nullptr) {
+// Workspace: the state each chunk leaves to the next [nchunks, H, P, N] f32,
+// the chain flags [nchunks, H * P / kSsdDim] and the chunk-to-sequence map
+// [nchunks] (int32), the 8 ticket counters; each part 256-byte aligned.
+struct SsdWorkspace {
+    int64_t state, flags, owner, tickets, total;  // byte offsets and the total
+};
+static SsdWorkspace ssd_ws_parts(int64_t H, int64_t P, int64_t N, int64_t nchunks) {
     auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
     const int64_t parts = (P + ssu::kSsdDim - 1) / ssu::kSsdDim;  // kSsdDim-wide parts of a head
-    *rows_bytes = up(nchunks * H * parts * ssu::kSsdMaxChunk * 4);
-    const int64_t sb = up(nchunks * H * P * N * 4);
-    if (state_bytes)
-        *state_bytes = sb;
-    return 2 * *rows_bytes + sb + up(nchunks * H * P * N * 2);
+    SsdWorkspace w;
+    w.state = 0;
+    w.flags = up(nchunks * H * P * N * 4);
+    w.owner = w.flags + up(nchunks * H * parts * 4);
+    w.tickets = w.owner + up(nchunks * 4);
+    w.total = w.tickets + 256;
+    return w;
 }
 
 int64_t ssu_ssd_workspace_bytes(int64_t heads, int64_t dim, int64_t dstate, int64_t nchunks) {
     if (heads < 0 || dim < 0 || dstate < 0 || nchunks < 0)
         return -1;
-    int64_t rows;
-    return ssd_ws_parts(heads, dim, dstate, nchunks, &rows);
+    return ssd_ws_parts(heads, dim, dstate, nchunks).total;
 }
 
 // A [rows, a, b] tensor with unit stride on the last axis; returns its row
@@ -660,15 +663,15 @@ ssu_status_t ssu_ssd_plan(const ssu_ssd_plan_desc_t *d, ssu_ssd_plan_info_t *inf
         return fail(SSU_ERR_NOT_IMPLEMENTED, "SSD prefill supports dstate 64 or 128, got %d", d->dstate);
     if (d->chunk_size < 1 || d->chunk_size > ssu::kSsdMaxChunk)
         return fail(SSU_ERR_NOT_IMPLEMENTED, "chunk_size must be 1..%d, got %d", ssu::kSsdMaxChunk, d->chunk_size);
-    const char *names[3] = {"", "", ""};
-    int vgprs[3] = {0, 0, 0};
+    const char *names[2] = {"", ""};
+    int vgprs[2] = {0, 0};
     const int e = ssu::ssd_kernel_attributes(d->io_dtype, d->state_dtype, d->dstate, names, vgprs);
     if (e != 0)
         return fail(SSU_ERR_HIP, "loading the SSD kernels failed: %s", ssu::hip_error_string(e));
     if (info) {
         memset(info, 0, sizeof *info);
-        info->launches = 3;
-        for (int i = 0; i < 3; i++) {
+        info->launches = 2;
+        for (int i = 0; i < 2; i++) {
             snprintf(info->kernels[i], sizeof info->kernels[i], "%s", names[i]);
             info->vgprs[i] = vgprs[i];
         }
@@ -772,20 +775,17 @@ ssu_status_t ssu_ssd_prefill(const ssu_ssd_args_t *a, void *workspace, int64_t w
     }
     if (nchunks == 0 || T == 0 || H == 0)
         return g_error.clear(), SSU_OK;
-    if (!a->return_intermediate_states && nchunks > 16384)
-        return fail(SSU_ERR_NOT_IMPLEMENTED, "more than 16384 chunks");
     const int64_t hsplit = P / ssu::kSsdDim;
     if (nchunks * H * hsplit > INT32_MAX / 8)
         return fail(SSU_ERR_NOT_IMPLEMENTED, "grid too large");
-    int64_t rows_bytes, state_bytes;
-    const int64_t need = ssd_ws_parts(H, P, N, nchunks, &rows_bytes, &state_bytes);
-    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
-        return fail(SSU_ERR_VALUE, "workspace must be 256-byte aligned with at least %lld bytes", (long long)need);
+    const SsdWorkspace wp = ssd_ws_parts(H, P, N, nchunks);
+    if (!workspace || workspace_bytes < wp.total || !aligned(workspace, 256))
+        return fail(SSU_ERR_VALUE, "workspace must be 256-byte aligned with at least %lld bytes", (long long)wp.total);
     char *ws = static_cast<char *>(workspace);
-    sp.ws_dtp = reinterpret_cast<float *>(ws);
-    sp.ws_acum = reinterpret_cast<float *>(ws + rows_bytes);
-    sp.ws_state = reinterpret_cast<float *>(ws + 2 * rows_bytes);
-    sp.ws_sin = ws + 2 * rows_bytes + state_bytes;
+    sp.ws_state = reinterpret_cast<float *>(ws + wp.state);
+    sp.ws_flags = reinterpret_cast<int *>(ws + wp.flags);
+    sp.ws_owner = reinterpret_cast<int *>(ws + wp.owner);
+    sp.ws_tickets = reinterpret_cast<int *>(ws + wp.tickets);
     sp.x = x.data;
     sp.dt = dt.data;
     sp.B = a->B.data;
@@ -801,6 +801,9 @@ ssu_status_t ssu_ssd_prefill(const ssu_ssd_args_t *a, void *workspace, int64_t w
     sp.batch = batch;
     sp.chunk_size = a->chunk_size;
     sp.hpg = static_cast<int32_t>(H / G * hsplit);
+    sp.nhb = (sp.hpg + 3) / 4;                                      // blocks of 4 heads
+    const int64_t nstream = G * sp.nhb;
+    sp.streams_per_xcd = static_cast<int32_t>((nstream + 7) / 8);   // streams per virtual XCD
     sp.dt_f32 = dt.dtype == SSU_F32;
     sp.softplus = a->dt_softplus != 0;
     sp.intermediate = a->return_intermediate_states != 0;

@@ -225,8 +225,10 @@ struct SsdParams {
     const void *init;
     const float *A, *D, *dt_bias;
     const void *cu_chunk, *seq_idx, *last_chunk;
-    float *ws_dtp, *ws_acum, *ws_state;
-    void *ws_sin;  // entering states [nchunks, H, P, N] in the x dtype
+    float *ws_state;  // the state each chunk leaves to the next [nchunks, H, P, N] (fp32)
+    int *ws_flags;    // [nchunks, H]: 1 once ws_state of (chunk, head) is published
+    int *ws_tickets;  // [8]: start-order counters, one per virtual XCD
+    int *ws_owner;    // [nchunks]: the sequence whose returned state the chunk gives, or -1
     int64_t T, H, N, nchunks, batch, chunk_size;
     int64_t x_st, x_sh, dt_st, dt_sh, B_st, B_sg, C_st, C_sg, z_st, z_sh, out_st, out_sh;
     int64_t A_sh, D_sh, bias_sh;
@@ -234,13 +236,15 @@ struct SsdParams {
     int32_t cu_chunk_i64, seq_idx_i64, last_chunk_i64;
     int32_t hpg, dt_f32, softplus, intermediate;
     int32_t hsplit;  // kSsdDim-wide parts per head: H and hpg count the parts
+    int32_t nhb;              // blocks of 4 heads per group
+    int32_t streams_per_xcd;  // (group, block) streams per virtual XCD
     float dt_lo, dt_hi;
 };
 int launch_ssd(const SsdParams &sp, int io_dtype, int state_dtype, void *stream);
-// Loads the prefill's three kernels for (io dtype, state dtype, dstate) on
+// Loads the prefill's two kernels for (io dtype, state dtype, dstate) on
 // the current device; fills their names (launch order) and registers.
 // Returns the hipError_t value as int.
-int ssd_kernel_attributes(int io_dtype, int state_dtype, int dstate, const char *names[3], int vgprs[3]);
+int ssd_kernel_attributes(int io_dtype, int state_dtype, int dstate, const char *names[2], int vgprs[2]);
 int launch_conv_shift(const ConvParams &cv, bool dim_major, unsigned grid, void *stream);
 
 bool find_replay_kernel(int state_dtype, int io_dtype, int dstate, bool spec, KernelRef *out);

@@ -147,9 +147,8 @@ def test_ssd_tiny_chunks():
 
 
 def test_ssd_many_chunks():
-    """More chunks than the state passing stages at a time (1024): 1252
-    chunks of 16 tokens, the second sequence running across the
-    1024-chunk boundary, final and intermediate states."""
+    """A long chain: 1252 chunks of 16 tokens, the first sequence's state
+    handed through 1000 of them, final and intermediate states."""
     c = W.ssd(seed=13, lengths=(16000, 3000, 1000, 7), heads=4, dim=64, dstate=64, groups=1, chunk_size=16,
               io="bf16", state_dtype="f32")
     assert len(c["seq_idx"]) > 1024 and c["seq_idx"][1023] == c["seq_idx"][1024] == 1
@@ -158,14 +157,14 @@ def test_ssd_many_chunks():
 
 
 def test_ssd_prewarm_then_graph_replay():
-    """The prewarm loads the three kernels for a configuration; a prefill
+    """The prewarm loads the two kernels for a configuration; a prefill
     captured in a HIP graph afterwards replays to the eager result, every
     replay (eager work and synchronisation in between), and matches the
     oracle."""
     info = G.ssu.prewarm_ssd_combined_fwd_varlen(8, 2, 64, 128, 128, io_dtype=torch.bfloat16,
                                                  state_dtype=torch.float32, dt_dtype=torch.float32)
-    assert info["launches"] == 3 and all(v > 0 for v in info["vgprs"])
-    assert info["kernels"] == ["ssd_chunk_state_kernel", "ssd_state_pass_kernel", "ssd_chunk_scan_kernel"]
+    assert info["launches"] == 2 and all(v > 0 for v in info["vgprs"])
+    assert info["kernels"] == ["ssd_prep_kernel", "ssd_fused_kernel"]
     c = W.ssd(seed=31, lengths=(300, 17, 129), heads=8, dim=64, dstate=128, groups=2, chunk_size=128,
               io="bf16", state_dtype="f32", initial_states=True)
     ref = ssu_oracle.run_ssd(c)
