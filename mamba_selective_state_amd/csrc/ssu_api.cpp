@@ -801,7 +801,7 @@ ssu_status_t ssu_ssd_prefill(const ssu_ssd_args_t *a, void *workspace, int64_t w
     sp.batch = batch;
     sp.chunk_size = a->chunk_size;
     sp.hpg = static_cast<int32_t>(H / G * hsplit);
-    sp.nhb = (sp.hpg + 3) / 4;                                      // blocks of 4 heads
+    sp.nhb = (sp.hpg + ssu::kSsdHeads - 1) / ssu::kSsdHeads;        // blocks of heads
     const int64_t nstream = G * sp.nhb;
     sp.streams_per_xcd = static_cast<int32_t>((nstream + 7) / 8);   // streams per virtual XCD
     sp.dt_f32 = dt.dtype == SSU_F32;

@@ -219,6 +219,12 @@ int launch_batch_memcpy(const CopyParams &cp, unsigned grid, void *stream);
 // [chunk, head, token] and one fp32 state per [chunk, head]).
 constexpr int kSsdDim = 64;
 constexpr int kSsdMaxChunk = 256;
+// Heads per workgroup of the fused prefill kernel (the host derives the
+// grid from it)
+#ifndef SSU_SSD_HEADS
+#define SSU_SSD_HEADS 4
+#endif
+constexpr int kSsdHeads = SSU_SSD_HEADS;
 struct SsdParams {
     const void *x, *dt, *B, *C, *z;
     void *out, *states;
@@ -236,7 +242,7 @@ struct SsdParams {
     int32_t cu_chunk_i64, seq_idx_i64, last_chunk_i64;
     int32_t hpg, dt_f32, softplus, intermediate;
     int32_t hsplit;  // kSsdDim-wide parts per head: H and hpg count the parts
-    int32_t nhb;              // blocks of 4 heads per group
+    int32_t nhb;              // blocks of kSsdHeads heads per group
     int32_t streams_per_xcd;  // (group, block) streams per virtual XCD
     float dt_lo, dt_hi;
 };

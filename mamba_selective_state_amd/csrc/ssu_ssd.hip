@@ -227,13 +227,20 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(const SsdParams 
 // does not increase). The diagonal block takes the exact factor per element
 // under the causal mask.
 constexpr int kFThreads = 512;
-constexpr int kFHeads = 4;      // heads per workgroup
+constexpr int kFHeads = kSsdHeads;  // heads per workgroup
+constexpr int kHPL = kFHeads > 1 ? kFHeads / 2 : 1;  // heads whose dt' a lane forms (two halves of 256 lanes)
+// head j of the lane's heads; with one head both halves form it (and store the same values)
+__device__ __forceinline__ int lane_head(int half, int j) { return kFHeads > 1 ? kHPL * half + j : 0; }
 constexpr int kFTiles = 2;      // 16-token tiles per wave
 constexpr int kFSlots = 9;      // (block, tile) pairs of a wave: (w / 2 + 1) + ((15 - w) / 2 + 1)
 constexpr int kXsRow = kL + 28; // x^T row stride (elements): 142 words
 constexpr int kBtRow = kL + 4;  // B^T row stride (elements): 130 words
 
 __device__ __forceinline__ int dim_row(int p) { return 4 * (p & 15) + (p >> 4); }
+// Row of dim p in the entering state's LDS copy: 16 pt + r for p = 16 (r / 4)
+// + r % 4 + 4 pt, so that the 16 rows of an operand read are in MFMA-row
+// order (16-byte reads by 8 lanes hit distinct banks with 68-word rows)
+__device__ __forceinline__ int sin_row(int p) { return 16 * ((p >> 2) & 3) + 4 * (p >> 4) + (p & 3); }
 
 template <typename T> struct alignas(4 * sizeof(T)) Vec4 { T v[4]; };  // one 8- or 16-byte access
 
@@ -303,20 +310,17 @@ __global__ __launch_bounds__(kFThreads) void ssd_fused_kernel(const SsdParams sp
     auto row_tok = [&](int i) -> int64_t { return len == 0 ? 0 : t0 + (i < len ? i : len - 1); };
 
     // ---- 1. loads in the order they are waited on: dt, B, the first head's x, C
-    float Ah[kFHeads], biash[kFHeads], Dh[kFHeads];
+    // the wave's heads kHPL half + j (uniform per wave), token t % 256
+    const int tk = t & (kL - 1), half = wv >> 2, wq = wv & 3;
+    float Ah[kHPL], biash[kHPL];
+    uint32_t dtr[kHPL];
 #pragma unroll
-    for (int hk = 0; hk < kFHeads; hk++) {
+    for (int j = 0; j < kHPL; j++) {
+        const int hk = lane_head(half, j);
         const int hh = (hk < nh ? h0 + hk : h0) / sp.hsplit;
-        Ah[hk] = sp.A[hh * sp.A_sh];
-        biash[hk] = sp.dt_bias ? sp.dt_bias[hh * sp.bias_sh] : 0.0f;
-        Dh[hk] = sp.D ? sp.D[hh * sp.D_sh] : 0.0f;
-    }
-    const int tk = t & (kL - 1), half = wv >> 2, wq = wv & 3;  // token, heads 2 half + {0, 1}, wave in the half
-    uint32_t dtr[2];
-#pragma unroll
-    for (int j = 0; j < 2; j++) {
-        const int hk = 2 * half + j;
-        dtr[j] = raw_dt<IT>(sp, tk < len ? t0 + tk : 0, (hk < nh ? h0 + hk : h0) / sp.hsplit);
+        Ah[j] = sp.A[hh * sp.A_sh];
+        biash[j] = sp.dt_bias ? sp.dt_bias[hh * sp.bias_sh] : 0.0f;
+        dtr[j] = raw_dt<IT>(sp, tk < len ? t0 + tk : 0, hh);
     }
     V bv[kBItems][2];
     {
@@ -381,12 +385,12 @@ __global__ __launch_bounds__(kFThreads) void ssd_fused_kernel(const SsdParams sp
     }
     // dt' and the inclusive prefix sum of dt' A of the lane's two heads:
     // within each wave, then the wave totals through LDS
-    float dtp2[2], acum2[2];
+    float dtp2[kHPL], acum2[kHPL];
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-        const int hk = 2 * half + j;
-        dtp2[j] = tk < len ? processed_dt(sp, dt_value<IT>(sp, dtr[j]), biash[hk]) : 0.0f;
-        acum2[j] = wave_inclusive_sum(dtp2[j] * Ah[hk], lane);
+    for (int j = 0; j < kHPL; j++) {
+        const int hk = lane_head(half, j);
+        dtp2[j] = tk < len ? processed_dt(sp, dt_value<IT>(sp, dtr[j]), biash[j]) : 0.0f;
+        acum2[j] = wave_inclusive_sum(dtp2[j] * Ah[j], lane);
         if (lane == 63)
             wave_tot[hk][wq] = acum2[j];
     }
@@ -394,8 +398,8 @@ __global__ __launch_bounds__(kFThreads) void ssd_fused_kernel(const SsdParams sp
 
     // ---- 2. the per-head factors, and C.B^T
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-        const int hk = 2 * half + j;
+    for (int j = 0; j < kHPL; j++) {
+        const int hk = lane_head(half, j);
         // the chunk's total, summed in the order of the last token's cumsum
         // (padding adds nothing)
         float a = acum2[j];
@@ -481,10 +485,7 @@ __global__ __launch_bounds__(kFThreads) void ssd_fused_kernel(const SsdParams sp
 
     for (int hk = 0; hk < nh; hk++) {
         const int h = h0 + hk;
-        float dh = Dh[0];
-#pragma unroll
-        for (int k = 1; k < kFHeads; k++)
-            dh = hk == k ? Dh[k] : dh;
+        const float dh = sp.D ? sp.D[(h / sp.hsplit) * sp.D_sh] : 0.0f;
         const float *acum_h = acum_s[hk];
         const float *dtp_h = dtp_s[hk];
         const float *q_h = q_s[hk];
@@ -680,7 +681,7 @@ __global__ __launch_bounds__(kFThreads) void ssd_fused_kernel(const SsdParams sp
 #pragma unroll
             for (int i = 0; i < 4; i++)
                 sv.v[i] = static_cast<IT>(sin[nt][i]);
-            *reinterpret_cast<Vec4<IT> *>(&Sin[dim_row(p_own)][16 * (ntb + nt) + g4]) = sv;
+            *reinterpret_cast<Vec4<IT> *>(&Sin[sin_row(p_own)][16 * (ntb + nt) + g4]) = sv;
         }
         if (feeds)
             __builtin_amdgcn_s_waitcnt(kWaitStores);  // the state's stores are complete
@@ -688,19 +689,30 @@ __global__ __launch_bounds__(kFThreads) void ssd_fused_kernel(const SsdParams sp
         if (feeds && t == 0)
             __hip_atomic_store(sp.ws_flags + c * sp.H + h, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-        // the entering state's part, y^T += exp(A_t) S_in C^T; the gate; the store
-        auto finish = [&](int tt, const V (&acv)[KN], const V (&zv2)[2], f32x4 (&y)[kP / 16]) {
-            const float rs = exp_f(acum_h[tt]);
+        // the entering state's part, y^T += exp(A_t) S_in C^T, both tiles
+        // from one read of each operand of S_in
+        {
+            const float rs0 = exp_f(acum_h[tt0]), rs1 = exp_f(acum_h[tt1]);
 #pragma unroll
             for (int pt = 0; pt < kP / 16; pt++) {
-                f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+                f32x4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                for (int k = 0; k < KN; k++)
-                    acc = M::run(*reinterpret_cast<const V *>(&Sin[xrow[pt]][32 * k + k8]), acv[k], acc);
+                for (int k = 0; k < KN; k++) {
+                    const V sa = *reinterpret_cast<const V *>(&Sin[16 * pt + r][32 * k + k8]);
+                    if (act0)
+                        acc0 = M::run(sa, ac[0][k], acc0);
+                    if (act1)
+                        acc1 = M::run(sa, ac[1][k], acc1);
+                }
 #pragma unroll
-                for (int ii = 0; ii < 4; ii++)
-                    y[pt][ii] = fmaf(rs, acc[ii], y[pt][ii]);
+                for (int ii = 0; ii < 4; ii++) {
+                    y0[pt][ii] = fmaf(rs0, acc0[ii], y0[pt][ii]);
+                    y1[pt][ii] = fmaf(rs1, acc1[ii], y1[pt][ii]);
+                }
             }
+        }
+        // the gate and the store: y[pt][ii] is p = 16 gq + 4 pt + ii of the token
+        auto finish = [&](int tt, const V (&zv2)[2], const f32x4 (&y)[kP / 16]) {
             if (tt >= len)
                 return;
             V o[2];
@@ -719,9 +731,9 @@ __global__ __launch_bounds__(kFThreads) void ssd_fused_kernel(const SsdParams sp
             *reinterpret_cast<V *>(orow + 8) = o[1];
         };
         if (act0)
-            finish(tt0, ac[0], zv0, y0);
+            finish(tt0, zv0, y0);
         if (act1)
-            finish(tt1, ac[1], zv1, y1);
+            finish(tt1, zv1, y1);
     }
 }
 
