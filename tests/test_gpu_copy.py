@@ -153,3 +153,29 @@ def test_conv_shift_full_workload(config):
     G.say("[gpu] %s full: launching" % config)
     run_shift(c, repeat=2)
     G.say("[gpu] %s full: ok" % config)
+
+
+def test_temporal_state_copy():
+    """Temporal (SSM) state copies of a speculative step (vLLM PR #50729
+    digest, "功能与动机" and the temporal-copy test it names): each sequence
+    b holds its per-position states in blocks bt[b, 0..K-1] of a pool of
+    [heads, dim, dstate] fp32 states; after acceptance, the state of the
+    last accepted position bt[b, bias] moves whole into bt[b, 0] (bias =
+    accepted - 1, copies only for bias >= 1, biases up to K - 1 >= 2). The
+    reading: whole-block copies between distinct blocks, which the batched
+    copy serves (no layout-aware kernel of its own); checked against the
+    snapshot's slices and the oracle, 10 repetitions."""
+    rng = np.random.default_rng(77)
+    batch, K, heads, dim, dstate = 24, 4, 8, 64, 128
+    block = heads * dim * dstate * 4
+    slots = batch * K + 8
+    perm = rng.permutation(slots)[:batch * K].reshape(batch, K)
+    bias = rng.integers(0, K, batch)
+    bias[:3] = [0, 2, K - 1]
+    pool = rng.standard_normal(slots * heads * dim * dstate).astype(np.float32).view(np.uint8)
+    src = [int(perm[b, bias[b]]) * block for b in range(batch) if bias[b] >= 1]
+    dst = [int(perm[b, 0]) * block for b in range(batch) if bias[b] >= 1]
+    c = {"buf": pool.copy(), "src_off": np.asarray(src, np.int64), "dst_off": np.asarray(dst, np.int64),
+         "sizes": np.full(len(src), block, np.int64)}
+    G.say("[gpu] temporal state copy: %d blocks of %d bytes" % (len(src), block))
+    run_memcpy(c, max_size=block)
