@@ -193,7 +193,7 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(const SsdParams 
 // One workgroup of 8 waves per (chunk, group, block of kFHeads heads of the
 // group). Phases:
 //  1. loads: B rows (lane items: a pair of rows, one 16-byte piece), the C
-//     row of each of the lane's two tokens, dt of two heads for token
+//     row of each of the lane's two tokens, dt of the lane's heads for token
 //     t % 256, the first head's x; dt' and the cumsums of all heads (wave
 //     scans, the wave totals through LDS); B rows and x^T to LDS.
 //  2. C.B^T: rows t in 16-row tiles (wave w takes tiles w and 15 - w: equal
@@ -217,10 +217,10 @@ __global__ __launch_bounds__(kPrepThreads) void ssd_prep_kernel(const SsdParams 
 //   (two 16-byte stores, loads of z alike).
 // The own state uses the same k order over tokens and the same p map (its
 // MFMA column r is p = 16 (r / 4) + r % 4 + 4 pt).
-// Dim p is stored at LDS row 4 (p % 16) + p / 16 of x^T and of the entering
-// state: the 16 rows an operand read touches are then consecutive; with
-// 142-word x^T rows and 130-word B^T rows the 16 lanes of an 8-byte read
-// pass hit distinct banks of the 32.
+// Dim p is stored at LDS row 4 (p % 16) + p / 16 of x^T (the entering state
+// in MFMA-row order, sin_row): the 16 rows an operand read touches are then
+// consecutive; with 142-word x^T rows and 130-word B^T rows the 16 lanes of
+// an 8-byte read pass hit distinct banks of the 32.
 // Below the diagonal block the decay factors into a row and a column term,
 // exp(A_t - A_s) dt'_s = exp(A_t - A_J) * exp(A_J - A_s) dt'_s with A_J the
 // cumsum at the block's last token; both are at most 1 there (the cumsum
