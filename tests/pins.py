@@ -994,6 +994,34 @@ def pin_ssd_chunking_invariance(orc):
         assert np.array_equal(o["y"], outs[0]["y"]) and np.array_equal(o["states"], outs[0]["states"])
 
 
+def pin_ssd_empty_chunks(orc):
+    """A chunk of zero tokens (cu_chunk_seqlens repeating an entry) changes
+    nothing, inside a sequence, opening one or ending one: outputs and final
+    states equal the case without them bit for bit, and the empty chunk's
+    own intermediate state is the state before it."""
+    from oracle import ssu_oracle
+    c = _ssd_case(lengths=(40, 30), initial_states=True)
+    cu, seq = np.asarray(c["cu_chunk_seqlens"]), np.asarray(c["seq_idx"])
+    out = []
+    first1 = int(np.argmax(seq == 1))
+    for k in range(len(seq)):
+        if k == first1:
+            out.append((int(cu[k]), int(cu[k]), 1))          # opens sequence 1
+        out.append((int(cu[k]), int(cu[k + 1]), int(seq[k])))
+        if k == 0:
+            out.append((int(cu[1]), int(cu[1]), int(seq[0])))  # inside sequence 0
+    out.append((int(cu[-1]), int(cu[-1]), int(seq[-1])))        # ends the last sequence
+    e = dict(c, cu_chunk_seqlens=np.asarray([0] + [q[1] for q in out], np.int64),
+             seq_idx=np.asarray([q[2] for q in out], np.int64),
+             last_chunk_indices=np.asarray([max(k for k, q in enumerate(out) if q[2] == b) for b in (0, 1)],
+                                           np.int64))
+    r0 = ssu_oracle.run_ssd(c, orc)
+    r = ssu_oracle.run_ssd(e, orc)
+    assert np.array_equal(r["y"], r0["y"]) and np.array_equal(r["states"], r0["states"])
+    # the empty chunk inside sequence 0 (chunk 1) passes chunk 0's state on
+    assert np.array_equal(r["chunk_states"][1], r["chunk_states"][0])
+
+
 def pin_ssd_seq_idx_authority(orc):
     """seq_idx decides where a sequence opens: relabelling the second
     sequence's chunks as the first's makes them continue its state (the same
@@ -1294,6 +1322,6 @@ ALL = [pin_golden_mate_examples, pin_f16_decode_exhaustive, pin_f16_encode, pin_
        pin_replay_spec_fold_boundary, pin_replay_spec_pad_and_disable, pin_replay_spec_brute_force,
        pin_memmove_matches_snapshot, pin_conv_shift_matches_snapshot,
        pin_ssd_matches_chunked_float64, pin_ssd_equals_decode_chain, pin_ssd_chunking_invariance,
-       pin_ssd_seq_idx_authority, pin_ssd_dt_limit_zero, pin_e4m3_codec, pin_mx8_blocks,
+       pin_ssd_seq_idx_authority, pin_ssd_empty_chunks, pin_ssd_dt_limit_zero, pin_e4m3_codec, pin_mx8_blocks,
        pin_replay_read_copy, pin_e2m1_codec, pin_mx4_blocks, pin_replay_read_copy_mx4,
        pin_threads_byte_identical]
