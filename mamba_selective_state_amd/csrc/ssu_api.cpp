@@ -933,7 +933,7 @@ ssu_status_t ssu_update(const ssu_args_t *a, void *stream) {
     Geometry geo = pr.geo;
     int64_t grid = pr.grid;
     if (yonly) {  // the output-only variant's own tile
-        geo = geometry(pr.P, pr.N, pr.state_dtype, ssu::kTileYonly);
+        geo = geometry(pr.P, pr.N, pr.state_dtype, k.tile);
         p.dim_tiles = geo.dim_tiles;
         p.rows_per_block = geo.rows_per_block;
         grid = pr.nseq * pr.H * geo.dim_tiles;

@@ -84,15 +84,22 @@ constexpr int replay_spec_waves_per_eu(int state_bytes, int dstate) {
 #ifndef SSU_WAVES_PER_EU_MULTI
 #define SSU_WAVES_PER_EU_MULTI 4
 #endif
-// the multi-token kernel's output-only variant on the matrix cores
+// the multi-token kernel's output-only variant on the matrix cores: its
+// 64-row tiles need more registers than 4 waves leave (3 waves), its 32-row
+// tiles fit 4
 #ifndef SSU_WAVES_PER_EU_YMFMA
-#define SSU_WAVES_PER_EU_YMFMA 4
+#define SSU_WAVES_PER_EU_YMFMA 3
+#endif
+#ifndef SSU_WAVES_PER_EU_YMFMA_32
+#define SSU_WAVES_PER_EU_YMFMA_32 4
 #endif
 
 // Passes (dim rows per lane): enough rows that each lane keeps about
 // `lane_bytes` of state in flight (dstate/16 elements per row, in the state
 // dtype), between 1 and 8 rows (separate budgets for the one-token and the
-// multi-token kernel, which also holds the next token's inputs).
+// multi-token kernel, which also holds the next token's inputs); up to 16
+// for the output-only variant on the matrix cores, whose wave shares its
+// tokens' B and C rows and their products over all of its rows.
 #ifndef SSU_LANE_BYTES
 #define SSU_LANE_BYTES 128
 #endif
@@ -107,15 +114,20 @@ constexpr int replay_spec_waves_per_eu(int state_bytes, int dstate) {
 #ifndef SSU_LANE_BYTES_YONLY
 #define SSU_LANE_BYTES_YONLY 128
 #endif
-enum TileKind { kTileOneToken = 0, kTileMulti = 1, kTileReplay = 2, kTileYonly = 3 };
+#ifndef SSU_LANE_BYTES_YMFMA
+#define SSU_LANE_BYTES_YMFMA 256
+#endif
+enum TileKind { kTileOneToken = 0, kTileMulti = 1, kTileReplay = 2, kTileYonly = 3, kTileYonlyMfma = 4 };
 constexpr int passes_for(int dstate, int state_bytes, int kind) {
     const int per_row = (dstate / kLanesPerRow) * state_bytes;
-    const int budget = kind == kTileMulti    ? SSU_LANE_BYTES_MULTI
-                       : kind == kTileReplay ? SSU_LANE_BYTES_REPLAY
-                       : kind == kTileYonly  ? SSU_LANE_BYTES_YONLY
-                                             : SSU_LANE_BYTES;
+    const int budget = kind == kTileMulti       ? SSU_LANE_BYTES_MULTI
+                       : kind == kTileReplay    ? SSU_LANE_BYTES_REPLAY
+                       : kind == kTileYonly     ? SSU_LANE_BYTES_YONLY
+                       : kind == kTileYonlyMfma ? SSU_LANE_BYTES_YMFMA
+                                                : SSU_LANE_BYTES;
+    const int cap = kind == kTileYonlyMfma ? 16 : 8;
     const int rows = budget / per_row;
-    return rows < 1 ? 1 : (rows > 8 ? 8 : rows);
+    return rows < 1 ? 1 : (rows > cap ? cap : rows);
 }
 
 // Kernel arguments. Strides are in elements. The pool is contiguous
@@ -178,12 +190,14 @@ struct ReplayParams {
 // Selected kernel variant for (state dtype, io dtype, dstate, multi-token).
 struct KernelRef {
     const void *fn;
+    int tile = kTileOneToken;  // TileKind of its dim tile (set by find_yonly_kernel)
 };
 
 // Returns false if no variant exists for the combination.
 bool find_kernel(int state_dtype, int io_dtype, int dstate, bool multi, KernelRef *out);
 // The multi-token kernel's output-only variant for disable_state_update;
-// false where it does not apply (16-bit state with fp32 outputs).
+// false where it does not apply (16-bit state with fp32 outputs). Sets
+// out->tile to kTileYonlyMfma for the matrix-core form, else kTileYonly.
 bool find_yonly_kernel(int state_dtype, int io_dtype, int dstate, KernelRef *out);
 
 // "ssu_onetoken_<state>_<io>_n<dstate>" or "ssu_packed_...".

@@ -70,21 +70,30 @@ constexpr int kYRound = 4;  // tokens whose per-row inputs are requested togethe
 // scale per token (bf16's 8 significant bits fit fp16's 11).
 template <typename ST, typename IT, int N, bool YONLY>
 constexpr bool yonly_mfma() {
-    return YONLY && N % 32 == 0 && (kRowsPerPass * passes_for(N, sizeof(ST), kTileYonly)) % 16 == 0 &&
+    return YONLY && N % 32 == 0 && (kRowsPerPass * passes_for(N, sizeof(ST), kTileYonlyMfma)) % 16 == 0 &&
            ((std::is_same_v<ST, __bf16> && std::is_same_v<IT, __bf16>) ||
             (std::is_same_v<ST, _Float16> && !std::is_same_v<IT, float>));
+}
+template <typename ST, int N>
+constexpr int yonly_mfma_waves_per_eu() {
+    return kRowsPerPass * passes_for(N, sizeof(ST), kTileYonlyMfma) > 32 ? SSU_WAVES_PER_EU_YMFMA
+                                                                         : SSU_WAVES_PER_EU_YMFMA_32;
 }
 
 template <typename ST, typename IT, int N, bool MULTI, bool YONLY = false>
 __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
-                             (yonly_mfma<ST, IT, N, YONLY>() ? SSU_WAVES_PER_EU_YMFMA
+                             (yonly_mfma<ST, IT, N, YONLY>() ? yonly_mfma_waves_per_eu<ST, N>()
                               : MULTI                         ? SSU_WAVES_PER_EU_MULTI
                                                               : SSU_WAVES_PER_EU)) void ssu_kernel(const Params p) {
     static_assert(!YONLY || MULTI, "the output-only path is a multi-token path");
     constexpr int E = N / kLanesPerRow;  // state elements per lane per row
     constexpr int VEC = (16 / (int)sizeof(ST)) < E ? (16 / (int)sizeof(ST)) : E;
     constexpr int NCH = E / VEC;         // accesses per lane per row
-    constexpr int PASSES = passes_for(N, sizeof(ST), YONLY ? kTileYonly : MULTI ? kTileMulti : kTileOneToken);
+    constexpr int PASSES = passes_for(N, sizeof(ST),
+                                      yonly_mfma<ST, IT, N, YONLY>() ? kTileYonlyMfma
+                                      : YONLY                         ? kTileYonly
+                                      : MULTI                         ? kTileMulti
+                                                                      : kTileOneToken);
     constexpr int IVEC = VEC;            // B / C are read with the same column split
     static_assert(E * kLanesPerRow == N && NCH * VEC == E, "dstate split");
     static_assert(PASSES <= kLanesPerRow, "one scalar-owning lane per pass");
@@ -604,6 +613,7 @@ bool pick_yonly_n(int n, KernelRef *k) {
 #define SSU_CASE(NN)                                                                     \
     case NN:                                                                             \
         k->fn = reinterpret_cast<const void *>(&ssu_kernel<ST, IT, NN, true, true>);    \
+        k->tile = yonly_mfma<ST, IT, NN, true>() ? kTileYonlyMfma : kTileYonly;           \
         return true;
         SSU_CASE(16)
         SSU_CASE(32)
