@@ -98,8 +98,10 @@ constexpr int replay_spec_waves_per_eu(int state_bytes, int dstate) {
 // `lane_bytes` of state in flight (dstate/16 elements per row, in the state
 // dtype), between 1 and 8 rows (separate budgets for the one-token and the
 // multi-token kernel, which also holds the next token's inputs); up to 16
-// for the output-only variant on the matrix cores, whose wave shares its
-// tokens' B and C rows and their products over all of its rows.
+// for the output-only variant on the matrix cores up to dstate 128, whose
+// wave shares its tokens' B and C rows and their products over all of its
+// rows (a larger dstate keeps the 16-row tile its A operands fit in at 4
+// waves per SIMD).
 #ifndef SSU_LANE_BYTES
 #define SSU_LANE_BYTES 128
 #endif
@@ -123,7 +125,7 @@ constexpr int passes_for(int dstate, int state_bytes, int kind) {
     const int budget = kind == kTileMulti       ? SSU_LANE_BYTES_MULTI
                        : kind == kTileReplay    ? SSU_LANE_BYTES_REPLAY
                        : kind == kTileYonly     ? SSU_LANE_BYTES_YONLY
-                       : kind == kTileYonlyMfma ? SSU_LANE_BYTES_YMFMA
+                       : kind == kTileYonlyMfma ? (dstate <= 128 ? SSU_LANE_BYTES_YMFMA : SSU_LANE_BYTES_YONLY)
                                                 : SSU_LANE_BYTES;
     const int cap = kind == kTileYonlyMfma ? 16 : 8;
     const int rows = budget / per_row;

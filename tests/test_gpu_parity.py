@@ -122,6 +122,19 @@ def test_varlen_disable_variants(sd, io, N, P):
     G.check(c, "varlen disable %s %s n%d p%d" % (sd, io, N, P))
 
 
+@pytest.mark.parametrize("groups,P", [(1, 64), (2, 40), (8, 64)])
+def test_varlen_disable_groups(groups, P):
+    """The matrix-core output-only variant with 8 heads in one group, in two
+    groups, and one head per group; lengths 0..12 (the longer sequences take
+    the update path without stores)."""
+    rng = np.random.default_rng(5 + groups)
+    lengths = rng.integers(0, 13, 20)
+    lengths[:3] = [12, 8, 0]
+    c = W.varlen(seed=13 + groups, nseq=20, heads=8, dim=P, dstate=128, groups=groups,
+                 state_dtype="f16", io="bf16", disable=True, lengths=lengths)
+    G.check(c, "varlen disable heads g%d p%d" % (groups, P))
+
+
 @pytest.mark.parametrize("pad", [0, -1])
 @pytest.mark.parametrize("sd", ["f32", "f16", "bf16"])
 def test_mtp_disable(sd, pad):
