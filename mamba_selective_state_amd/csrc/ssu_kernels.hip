@@ -301,8 +301,11 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
 
     if constexpr (YONLY) {
         if (len <= kYMax) {  // uniform
-            __shared__ __attribute__((aligned(16))) IT Bl[kYMax][N];  // B rows of the tokens
-            __shared__ __attribute__((aligned(16))) IT Cl[kYMax][N];  // C rows of the tokens
+            // (rows padded by 16 bytes, and Ul's by a word: the tokens' rows,
+            // read by one 16-byte operand load each, and the wave's 64 rows
+            // of Ul, read column-wise, fall in distinct banks)
+            __shared__ __attribute__((aligned(16))) IT Bl[kYMax][N + 8];  // B rows of the tokens
+            __shared__ __attribute__((aligned(16))) IT Cl[kYMax][N + 8];  // C rows of the tokens
             __shared__ float Wl[kYMax][kYMax];                        // Wl[j][t] = B_j . C_t
             // (matrix cores) the tile as A operands: lane l takes row
             // 16 mt + l % 16 and columns 32 kb + 8 (l / 16) .. +7 (16 bytes);
@@ -372,7 +375,7 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
             }
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             // u_t = S_0 . C_t of every row of the wave and token, on the matrix cores
-            __shared__ float Ul[YMFMA ? kRowsWave : 1][kYMax];
+            __shared__ float Ul[YMFMA ? kRowsWave : 1][kYMax + 1];
             if constexpr (YMFMA) {
                 // bf16 C into fp16: token j scaled by 2^-e_j, e_j = floor(log2 max |C_j|) - 14,
                 // so its values down to 2^-28 of the largest are exact fp16 normals
