@@ -90,6 +90,12 @@ constexpr int replay_spec_waves_per_eu(int state_bytes, int dstate) {
 #ifndef SSU_WAVES_PER_EU_YMFMA
 #define SSU_WAVES_PER_EU_YMFMA 3
 #endif
+// its VALU form with a 16-bit state (it spills at 4 waves: 159 against 191 us
+// with bf16 state and fp16 outputs); with an fp32 state the spilling 4-wave
+// build was the faster one (95 against 101 us on MTP)
+#ifndef SSU_WAVES_PER_EU_YVALU16
+#define SSU_WAVES_PER_EU_YVALU16 3
+#endif
 #ifndef SSU_WAVES_PER_EU_YMFMA_32
 #define SSU_WAVES_PER_EU_YMFMA_32 4
 #endif

@@ -83,6 +83,7 @@ constexpr int yonly_mfma_waves_per_eu() {
 template <typename ST, typename IT, int N, bool MULTI, bool YONLY = false>
 __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
                              (yonly_mfma<ST, IT, N, YONLY>() ? yonly_mfma_waves_per_eu<ST, N>()
+                              : YONLY && sizeof(ST) == 2      ? SSU_WAVES_PER_EU_YVALU16
                               : MULTI                         ? SSU_WAVES_PER_EU_MULTI
                                                               : SSU_WAVES_PER_EU)) void ssu_kernel(const Params p) {
     static_assert(!YONLY || MULTI, "the output-only path is a multi-token path");
