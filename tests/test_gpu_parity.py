@@ -107,6 +107,8 @@ YONLY_CASES = [
     ("f16", "bf16", 128, 64), ("f16", "bf16", 32, 40), ("f16", "bf16", 256, 64),
     ("f16", "f16", 64, 64), ("bf16", "bf16", 128, 28), ("bf16", "bf16", 256, 64),
     ("bf16", "f16", 128, 64), ("f32", "bf16", 128, 64), ("f32", "f32", 64, 36),
+    # two 64-row tiles per head on the matrix cores, the second partial or whole
+    ("f16", "bf16", 128, 96), ("bf16", "bf16", 64, 128),
 ]
 
 
