@@ -314,16 +314,30 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
             constexpr int MT = YMFMA ? kRowsWave / 16 : 1, KB = YMFMA ? N / 32 : 1;
             using MV = std::conditional_t<std::is_same_v<ST, __bf16>, bf16x8, f16x8>;
             u32x4 sa[MT][KB];
+            constexpr int kCpr = YMFMA ? N * (int)sizeof(ST) / 16 : 1;  // 16-byte pieces of a row
+            static_assert(!YMFMA || kCpr == 4 * KB, "a row is KB operand columns of 4 pieces");
+            // (64-row tiles; a one-tile wave reads in operand order, as its
+            // LDS copy would cost it a wave per SIMD)
+            constexpr bool kReorder = YMFMA && MT > 1;
             if constexpr (YMFMA) {
+                // read in whole contiguous KiB: load (mt, kb) gives lane l the
+                // 16-byte piece c = 64 (KB mt + kb) + l of the wave's rows
+                // (row c / kCpr, piece c % kCpr), and the 16-row tile mt is
+                // put in operand order through LDS before its products (an
+                // operand-order read touches 16 rows x 64 bytes per load
+                // instruction, which was 15% slower)
                 const ST *abase = read_pad ? pool + tile_off : rbase;
 #pragma unroll
                 for (int mt = 0; mt < MT; mt++) {
-                    const int d = dw + 16 * mt + (lane & 15);
-                    const int dl = d < p.P ? d : p.P - 1;
 #pragma unroll
-                    for (int kb = 0; kb < KB; kb++)
+                    for (int kb = 0; kb < KB; kb++) {
+                        const int c = 64 * (KB * mt + kb) + lane;
+                        const int d = dw + (kReorder ? c / kCpr : 16 * mt + (lane & 15));
+                        const int dl = d < p.P ? d : p.P - 1;
+                        const int piece = kReorder ? c % kCpr : 4 * kb + (lane >> 4);
                         sa[mt][kb] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-                            abase + static_cast<int64_t>(dl) * N + 32 * kb + 8 * (lane >> 4)));
+                            abase + static_cast<int64_t>(dl) * N + 8 * piece));
+                    }
                 }
             }
             // Every token's inputs in one round of loads, in flight with the
@@ -427,19 +441,44 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
                     return n < len ? v : MV{};
                 };
                 f32x4 D[MT], Dw = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                // the C operands, kept for the tiles when there are several
+                MV bvs[MT > 1 ? KB : 1];
+                auto c_op = [&](int kb) { return operand(&Cl[nr][32 * kb + 8 * (lane >> 4)], ec); };
+                auto b_op = [&](int kb) { return operand(&Bl[nr][32 * kb + 8 * (lane >> 4)], eb); };
+                if constexpr (MT > 1) {
 #pragma unroll
-                for (int mt = 0; mt < MT; mt++)
+                    for (int kb = 0; kb < KB; kb++) {
+                        bvs[kb] = c_op(kb);
+                        Dw = mfma16x16x32(b_op(kb), bvs[kb], Dw);
+                    }
+                }
+                // the 16-row tile mt in operand order: lane l takes row l % 16
+                // and piece 4 kb + l / 16 (rows padded by a piece: the 16
+                // lanes of a pass hit distinct banks both ways)
+                __shared__ __attribute__((aligned(16))) u32x4 Tl[kReorder ? 16 : 1][kReorder ? kCpr + 1 : 1];
+#pragma unroll
+                for (int mt = 0; mt < MT; mt++) {
+                    if constexpr (kReorder) {
+#pragma unroll
+                        for (int kb = 0; kb < KB; kb++) {
+                            const int c = 64 * kb + lane;
+                            Tl[c / kCpr][c % kCpr] = sa[mt][kb];
+                        }
+                    }
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
                     D[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                    const bool live = !read_pad && dw + 16 * mt + (lane & 15) < p.P;
 #pragma unroll
-                for (int kb = 0; kb < KB; kb++) {
-                    const MV bv = operand(&Cl[nr][32 * kb + 8 * (lane >> 4)], ec);
-#pragma unroll
-                    for (int mt = 0; mt < MT; mt++) {
-                        const bool live = !read_pad && dw + 16 * mt + (lane & 15) < p.P;
-                        const u32x4 a = live ? sa[mt][kb] : u32x4{0u, 0u, 0u, 0u};
+                    for (int kb = 0; kb < KB; kb++) {
+                        const MV bv = MT > 1 ? bvs[MT > 1 ? kb : 0] : c_op(kb);
+                        if constexpr (MT == 1)
+                            Dw = mfma16x16x32(b_op(kb), bv, Dw);
+                        const u32x4 t = kReorder ? Tl[kReorder ? lane & 15 : 0][kReorder ? 4 * kb + (lane >> 4) : 0]
+                                                 : sa[mt][kb];
+                        const u32x4 a = live ? t : u32x4{0u, 0u, 0u, 0u};
                         D[mt] = mfma16x16x32(__builtin_bit_cast(MV, a), bv, D[mt]);
                     }
-                    Dw = mfma16x16x32(operand(&Bl[nr][32 * kb + 8 * (lane >> 4)], eb), bv, Dw);
+                    __atomic_signal_fence(__ATOMIC_SEQ_CST);
                 }
                 if (n < kYMax) {
 #pragma unroll
