@@ -633,6 +633,13 @@ __global__ __launch_bounds__(kFThreads) void ssd_fused_kernel(const SsdParams sp
         __syncthreads();  // the flag is seen; every wave is done with x^T and the entering state's LDS copy
         if (hk + 1 < nh)
             store_x(nx);
+        // The chain's fp32 state is kept in the workspace in the lanes' own
+        // order (16 bytes of lane l of wave w at (w KNT + nt) 64 + l): the
+        // next chunk's lanes hold the same (p, n) and read it back, each
+        // load or store instruction covering 1 KiB (in [p][n] order one
+        // covered 16 rows x 64 bytes, 5% slower over the prefill).
+        static_assert(kFThreads / 64 * KNT * 64 * 16 == PN * 4, "the lanes' order covers the state");
+        const uint32_t chain_off = static_cast<uint32_t>(wv * KNT * 64 + lane) * 16;
         f32x4 sin[KNT];
         if (!opens) {
             const __amdgpu_buffer_rsrc_t src =
@@ -641,7 +648,7 @@ __global__ __launch_bounds__(kFThreads) void ssd_fused_kernel(const SsdParams sp
             for (int nt = 0; nt < KNT; nt++)
                 sin[nt] = __builtin_bit_cast(
                     f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                               src, (p_own * N + 16 * (ntb + nt) + g4) * 4, 0, kDeviceScope));
+                               src, chain_off + nt * 64 * 16, 0, kDeviceScope));
         } else if (has_init) {
             const ST *ip = init + (seq * sp.H + h) * PN + p_own * N + g4;
 #pragma unroll
@@ -668,7 +675,7 @@ __global__ __launch_bounds__(kFThreads) void ssd_fused_kernel(const SsdParams sp
 #pragma unroll
             for (int nt = 0; nt < KNT; nt++)
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, so[nt]), dst,
-                                                       (p_own * N + 16 * (ntb + nt) + g4) * 4, 0, kDeviceScope);
+                                                       chain_off + nt * 64 * 16, 0, kDeviceScope);
         }
         if (sp.intermediate || owner >= 0) {
             ST *dst = outs + ((sp.intermediate ? c : owner) * sp.H + h) * PN + p_own * N + g4;
