@@ -470,11 +470,18 @@ __global__ __launch_bounds__(kMaxWaves *kWaveLanes,
                     const bool live = !read_pad && dw + 16 * mt + (lane & 15) < p.P;
 #pragma unroll
                     for (int kb = 0; kb < KB; kb++) {
-                        const MV bv = MT > 1 ? bvs[MT > 1 ? kb : 0] : c_op(kb);
-                        if constexpr (MT == 1)
+                        MV bv;
+                        if constexpr (MT > 1) {
+                            bv = bvs[kb];
+                        } else {
+                            bv = c_op(kb);
                             Dw = mfma16x16x32(b_op(kb), bv, Dw);
-                        const u32x4 t = kReorder ? Tl[kReorder ? lane & 15 : 0][kReorder ? 4 * kb + (lane >> 4) : 0]
-                                                 : sa[mt][kb];
+                        }
+                        u32x4 t;
+                        if constexpr (kReorder)
+                            t = Tl[lane & 15][4 * kb + (lane >> 4)];
+                        else
+                            t = sa[mt][kb];
                         const u32x4 a = live ? t : u32x4{0u, 0u, 0u, 0u};
                         D[mt] = mfma16x16x32(__builtin_bit_cast(MV, a), bv, D[mt]);
                     }
