@@ -879,7 +879,8 @@ def main():
         else torch.int32,
         packed=x.ndim == 4 or case.get("cu_seqlens") is not None
         or case.get("num_accepted_tokens") is not None,
-        dt_dtype=TORCH[case.get("dt_dtype", case["io_dtype"])])
+        dt_dtype=TORCH[case.get("dt_dtype", case["io_dtype"])],
+        disable_state_update=case.get("disable_state_update", False))
     stream = torch.cuda.current_stream(dev)
     handle = stream.cuda_stream
 

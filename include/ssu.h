@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SSU_ABI_VERSION 3
+#define SSU_ABI_VERSION 4
 
 #ifndef SSU_API
 #define SSU_API __attribute__((visibility("default")))
@@ -138,16 +138,21 @@ typedef struct {
  * prewarm_selective_state_update). dt_dim is 1 for one dt value per head,
  * else dim. packed selects the multi-token kernel (cu_seqlens, dense
  * [batch, steps, ...], or num_accepted_tokens); slot_dtype and meta_dtype are
- * accepted for compatibility (both index widths run in the same kernels). */
+ * accepted for compatibility (both index widths run in the same kernels).
+ * disable_state_update (nonzero) with packed selects the output-only variant
+ * those calls take where one exists for the dtypes (as ssu_update does), and
+ * reports its tiling. */
 typedef struct {
     int32_t state_dtype, io_dtype, dt_dtype, slot_dtype, meta_dtype; /* ssu_dtype_t */
     int32_t heads, dim, dstate, groups, dt_dim, packed;
     int64_t max_rows; /* informational; 0 if unknown */
+    int32_t disable_state_update;
 } ssu_plan_desc_t;
 
 /* What ssu_plan selected (for logging and tests). */
 typedef struct {
-    char kernel[64];       /* name of the selected kernel variant */
+    char kernel[64];       /* name of the selected kernel variant ("ssu_onetoken_...",
+                              "ssu_packed_..." or "ssu_packed_output_only_...") */
     int32_t block_threads; /* threads per workgroup */
     int32_t rows_per_block;/* dim rows one workgroup covers */
     int32_t blocks_per_seq_head; /* workgroups per (sequence, head) */

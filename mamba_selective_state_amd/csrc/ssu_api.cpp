@@ -892,7 +892,11 @@ ssu_status_t ssu_plan(const ssu_plan_desc_t *desc, ssu_plan_info_t *info) {
         return fail(SSU_ERR_VALUE, "dt_dim must be 1 or dim");
     ssu::KernelRef k;
     const bool multi = desc->packed != 0;
-    if (!ssu::find_kernel(desc->state_dtype, desc->io_dtype, desc->dstate, multi, &k))
+    // packed calls with disable_state_update take the output-only variant
+    // where one exists (the choice ssu_update makes)
+    const bool yonly = multi && desc->disable_state_update &&
+                       ssu::find_yonly_kernel(desc->state_dtype, desc->io_dtype, desc->dstate, &k);
+    if (!yonly && !ssu::find_kernel(desc->state_dtype, desc->io_dtype, desc->dstate, multi, &k))
         return fail(SSU_ERR_NOT_IMPLEMENTED, "no kernel for this dtype combination");
     int vgprs = 0, sgprs = 0;
     const int e = ssu::kernel_attributes(k, &vgprs, &sgprs);
@@ -900,10 +904,14 @@ ssu_status_t ssu_plan(const ssu_plan_desc_t *desc, ssu_plan_info_t *info) {
         return fail(SSU_ERR_HIP, "loading the kernel failed: %s", ssu::hip_error_string(e));
     if (info) {
         const Geometry g = geometry(desc->dim, desc->dstate, desc->state_dtype,
-                                    multi ? ssu::kTileMulti : ssu::kTileOneToken);
+                                    yonly ? k.tile : multi ? ssu::kTileMulti : ssu::kTileOneToken);
         memset(info, 0, sizeof *info);
-        ssu::kernel_name(desc->state_dtype, desc->io_dtype, desc->dstate, multi, info->kernel,
-                         sizeof info->kernel);
+        if (yonly)
+            snprintf(info->kernel, sizeof info->kernel, "ssu_packed_output_only_%s_%s_n%d",
+                     dtype_str(desc->state_dtype), dtype_str(desc->io_dtype), desc->dstate);
+        else
+            ssu::kernel_name(desc->state_dtype, desc->io_dtype, desc->dstate, multi, info->kernel,
+                             sizeof info->kernel);
         info->block_threads = g.block;
         info->rows_per_block = g.rows_per_block;
         info->blocks_per_seq_head = g.dim_tiles;

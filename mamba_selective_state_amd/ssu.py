@@ -81,7 +81,8 @@ class SsuSsdPlanInfo(ctypes.Structure):
 class SsuPlanDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("state_dtype", "io_dtype", "dt_dtype", "slot_dtype", "meta_dtype", "heads",
-                 "dim", "dstate", "groups", "dt_dim", "packed")] + [("max_rows", ctypes.c_int64)]
+                 "dim", "dstate", "groups", "dt_dim", "packed")] + [("max_rows", ctypes.c_int64),
+                                                                     ("disable_state_update", ctypes.c_int32)]
 
 
 class SsuPlanInfo(ctypes.Structure):
@@ -330,11 +331,13 @@ def selective_state_update(state, x, dt, A, B, C, D, z=None, dt_bias=None, dt_so
 
 def prewarm_selective_state_update(*, state_dtype, io_dtype, batch, heads, dim, dstate, groups,
                                    slot_dtype, rows_per_cta=4, lanes_per_row=32, packed=False,
-                                   meta_dtype=torch.int32, dt_dim=None, dt_dtype=None):
+                                   meta_dtype=torch.int32, dt_dim=None, dt_dtype=None,
+                                   disable_state_update=False):
     """Validate and load the kernel one configuration uses, before any graph
     capture (MATE prewarm_selective_state_update; rows_per_cta and
     lanes_per_row are accepted and ignored: the gfx950 kernels fix their own
-    tiling). Returns the selection."""
+    tiling). With packed and disable_state_update it selects the output-only
+    variant such calls take. Returns the selection."""
     desc = SsuPlanDesc()
     desc.state_dtype = _TORCH_DTYPES[state_dtype]
     desc.io_dtype = _TORCH_DTYPES[io_dtype]
@@ -345,6 +348,7 @@ def prewarm_selective_state_update(*, state_dtype, io_dtype, batch, heads, dim, 
     desc.dt_dim = dim if dt_dim is None else dt_dim
     desc.packed = int(bool(packed))
     desc.max_rows = batch
+    desc.disable_state_update = int(bool(disable_state_update))
     return ssu_plan(desc)
 
 

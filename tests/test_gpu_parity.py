@@ -244,6 +244,27 @@ def test_alias_repeat10(kind):
     G.say("[gpu] %s: 10 repeats identical" % kind)
 
 
+def test_prewarm_output_only():
+    """With packed and disable_state_update, prewarm selects the variant such
+    calls take and reports its tiling: the matrix-core form's 64-row tiles
+    (fp16 state, bf16 io, dstate 128), the VALU form's 16-row tiles (fp32
+    state); a 16-bit state with fp32 outputs has no output-only variant and
+    keeps the update kernel."""
+    def pre(sd, io, disable):
+        return G.ssu.prewarm_selective_state_update(
+            state_dtype=sd, io_dtype=io, batch=512, heads=64, dim=64, dstate=128, groups=1,
+            slot_dtype=torch.int32, packed=True, disable_state_update=disable)
+    info = pre(torch.float16, torch.bfloat16, True)
+    assert info["kernel"] == "ssu_packed_output_only_f16_bf16_n128"
+    assert (info["block_threads"], info["rows_per_block"], info["blocks_per_seq_head"]) == (64, 64, 1)
+    info = pre(torch.float32, torch.bfloat16, True)
+    assert info["kernel"] == "ssu_packed_output_only_f32_bf16_n128"
+    assert (info["rows_per_block"], info["blocks_per_seq_head"]) == (16, 4)
+    info = pre(torch.float16, torch.float32, True)
+    assert info["kernel"] == "ssu_packed_f16_f32_n128"
+    assert pre(torch.float16, torch.bfloat16, False)["kernel"] == "ssu_packed_f16_bf16_n128"
+
+
 def test_prewarm_and_graph_replay():
     """prewarm selects and loads the kernel; the update captured in a HIP
     graph replays to the eager result (read and write slots differ, so each
