@@ -85,8 +85,9 @@ constexpr int replay_spec_waves_per_eu(int state_bytes, int dstate) {
 #define SSU_WAVES_PER_EU_MULTI 4
 #endif
 // the multi-token kernel's output-only variant on the matrix cores: its
-// 64-row tiles need more registers than 4 waves leave (3 waves), its 32-row
-// tiles fit 4
+// 64-row tiles (dstate up to 128) need more registers than 4 waves leave
+// (3 waves); its tiles of 32 rows or fewer (dstate 256: 16) fit 4
+// (SSU_WAVES_PER_EU_YMFMA_32)
 #ifndef SSU_WAVES_PER_EU_YMFMA
 #define SSU_WAVES_PER_EU_YMFMA 3
 #endif
