@@ -142,12 +142,12 @@ def test_ssd_full_workload():
     check_ssd(c, "ssd bench workload", heads=[0, 77, 127])
 
 
-@pytest.mark.parametrize("heads,groups", [(6, 1), (12, 4), (20, 2)],
-                         ids=["6-per-group", "3-per-group", "10-per-group"])
+@pytest.mark.parametrize("heads,groups", [(6, 1), (12, 4), (20, 2), (18, 1)],
+                         ids=["6-per-group", "3-per-group", "10-per-group", "18-per-group"])
 def test_ssd_head_blocks(heads, groups):
-    """Heads per group that the fused kernel's 4-head blocks do not divide
-    (6: 4 + 2; 3: one partial block; 10: 4 + 4 + 2), so the (group, head
-    block) streams come in counts that do not fill the 8 virtual XCDs
+    """Heads per group that the fused kernel's 8-head blocks do not divide
+    (6 and 3: one partial block; 10: 8 + 2; 18: 8 + 8 + 2), so the (group,
+    head block) streams come in counts that do not fill the 8 virtual XCDs
     evenly, with intermediate states so every chunk's state is checked."""
     c = W.ssd(seed=7 + heads, lengths=(300, 17, 129), heads=heads, dim=64, dstate=128, groups=groups,
               chunk_size=128, io="bf16", state_dtype="f32")
